@@ -1,0 +1,218 @@
+"""numpy fp64 oracle of the com.microsoft PagedAttention operator (SEPARATE K/V).
+
+Test infrastructure: imported only by the test suite, the package entry file's
+smoke check and the benchmark's CPU-baseline leg.  Nothing here is shared with
+the HIP library.
+
+What the operator computes (model-card README "com.microsoft.PagedAttention",
+sections Description, Inputs, Outputs, Attributes, Type constraints): the
+step's keys and values are written into the block caches, then every packed
+query row attends, causally, to its sequence's history read back through
+block_table.  Grouped-query heads share a key/value head; scale 0 means
+1/sqrt(head_size); only is_causal=1 exists.
+
+Readings taken where the pages leave a step open (each is listed with its
+reason in the design notes of the repository):
+  * Everything is read back from the cache *after* the writes, through
+    block_table, including the step's own positions; a token whose slot is -1
+    sees whatever the cache already held at its position (README,
+    Description: "scattered into the cache, then attended"; Inputs,
+    slot_mapping: block_table "defines the read path").
+  * Query head h uses key/value head h // (H/Hkv) (contiguous groups): in the
+    Qwen3-8B example of "WS2 CP-Aware Attention Contract" one rank owns query
+    heads 0-15 together with KV heads 0-3 only.
+  * Causal alignment is bottom-right: new row i of sequence b sits at logical
+    position past_b + i and sees keys 0..past_b+i ("WS2 ...", Scope and
+    Mode-Specific Metadata: chunked prefill / decode have query lengths
+    shorter than their KV context, one causal offset per packed sequence).
+  * Packed rows are [Q | K | V], each head-major [heads, D].
+  * Slot writes are applied in token order (two tokens naming one slot is
+    outside the contract, so the order only makes the oracle definite).
+
+All floating point is fp64; the caches returned are fp16 with their bits
+copied, never converted.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+
+def resolve_call(query: np.ndarray, key: Optional[np.ndarray], value: Optional[np.ndarray],
+                 num_heads: int, kv_num_heads: int, scale: float):
+    """Split the query input and fix head_size and scale.
+
+    README, Inputs (query, key, value) and Attributes (scale): query is
+    [N, H*D], or [N, (H+2*Hkv)*D] carrying [Q|K|V] when key and value are both
+    absent; scale == 0 selects 1/sqrt(D).  Returns (Q, K, V, D, scale) with Q
+    [N, H, D], K and V [N, Hkv, D], still fp16.
+    """
+    if (key is None) != (value is None):
+        raise ValueError("key and value must be given together")
+    H, Hkv = int(num_heads), int(kv_num_heads)
+    if H <= 0 or Hkv <= 0 or H % Hkv:
+        raise ValueError("num_heads must be a positive multiple of kv_num_heads")
+    N, width = query.shape
+    if key is None:
+        if width % (H + 2 * Hkv):
+            raise ValueError("packed query width is not (H+2*Hkv)*D")
+        D = width // (H + 2 * Hkv)
+        Q = query[:, :H * D]
+        K = query[:, H * D:(H + Hkv) * D]
+        V = query[:, (H + Hkv) * D:]
+    else:
+        if width % H:
+            raise ValueError("query width is not H*D")
+        D = width // H
+        Q, K, V = query, key, value
+        if K.shape != (N, Hkv * D) or V.shape != (N, Hkv * D):
+            raise ValueError("key/value must be [N, Hkv*D]")
+    s = 1.0 / math.sqrt(D) if scale == 0 else float(scale)
+    return (Q.reshape(N, H, D), K.reshape(N, Hkv, D), V.reshape(N, Hkv, D), D, s)
+
+
+def scatter_kv(key_cache: np.ndarray, value_cache: np.ndarray, K: np.ndarray, V: np.ndarray,
+               cum: np.ndarray, past: np.ndarray, block_table: np.ndarray,
+               slot_mapping: Optional[np.ndarray]):
+    """Write each new token's K/V rows into copies of the caches.
+
+    README, Inputs (slot_mapping): token t goes to flat slot
+    block_id*block_size + offset; -1 suppresses the write; without
+    slot_mapping the slot follows from past_seqlens (token i of sequence b is
+    at position past_b + i, found through block_table).  The copy is bit
+    exact: fp16 in, fp16 out.
+    """
+    kc = key_cache.copy()
+    vc = value_cache.copy()
+    NB, bs, Hkv, D = kc.shape
+    kslots = kc.reshape(NB * bs, Hkv, D)
+    vslots = vc.reshape(NB * bs, Hkv, D)
+    for b in range(past.shape[0]):
+        for i in range(int(cum[b + 1]) - int(cum[b])):
+            t = int(cum[b]) + i
+            if slot_mapping is not None:
+                slot = int(slot_mapping[t])
+            else:
+                pos = int(past[b]) + i
+                slot = int(block_table[b, pos // bs]) * bs + pos % bs
+            if slot >= 0:
+                kslots[slot] = K[t]
+                vslots[slot] = V[t]
+    return kc, vc
+
+
+def gather_history(kc: np.ndarray, vc: np.ndarray, block_table: np.ndarray, b: int,
+                   length: int):
+    """Contiguous fp64 copies [length, Hkv, D] of sequence b's positions
+    0..length-1, each read at slot block_table[b, j // bs]*bs + j % bs
+    (README, Inputs: block_table maps a sequence's logical blocks to
+    physical blocks and defines the read path)."""
+    NB, bs, Hkv, D = kc.shape
+    j = np.arange(int(length), dtype=np.int64)
+    idx = block_table[b, j // bs].astype(np.int64) * bs + j % bs
+    Kb = kc.reshape(NB * bs, Hkv, D)[idx].astype(np.float64)
+    Vb = vc.reshape(NB * bs, Hkv, D)[idx].astype(np.float64)
+    return Kb, Vb
+
+
+def attend_sequence(Qb: np.ndarray, Kb: np.ndarray, Vb: np.ndarray, past_b: int,
+                    scale: float, rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Causal grouped-query softmax attention of one sequence, brute force.
+
+    Qb [q, H, D], Kb/Vb [L, Hkv, D] (fp64, L = past_b + q).  For head h with
+    kv head k = h // (H/Hkv): S = scale * Q_h K_k^T, entries with key
+    position j > past_b + i set to -inf, P = softmax over keys, O = P V_k.
+    ``rows`` restricts the work to those new-token rows (others are NaN).
+    Returns [q, H, D] fp64.
+    """
+    q, H, D = Qb.shape
+    L, Hkv, _ = Kb.shape
+    G = H // Hkv
+    sel = np.arange(q) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.full((q, H, D), np.nan)
+    if sel.size == 0:
+        return out
+    pos = int(past_b) + sel
+    masked = np.arange(L)[None, :] > pos[:, None]
+    for h in range(H):
+        k = h // G
+        S = scale * (Qb[sel, h, :] @ Kb[:, k, :].T)
+        S[masked] = -np.inf
+        S = S - S.max(axis=1, keepdims=True)
+        P = np.exp(S)
+        P /= P.sum(axis=1, keepdims=True)
+        out[sel, h, :] = P @ Vb[:, k, :]
+    return out
+
+
+def paged_attention(query, key, value, key_cache, value_cache, cum, past, block_table,
+                    slot_mapping=None, *, num_heads: int, kv_num_heads: int,
+                    scale: float = 0.0, is_causal: int = 1, rows=None):
+    """The whole operator: returns (output fp64 [N, H*D], key_cache', value_cache').
+
+    README, Description/Outputs: the caches are updated (here: copies are
+    returned) and output holds one row of H*D values per packed token.
+    ``rows``: optional sorted token indices to compute (others are NaN), so
+    that full-size workloads can be checked on a sample.
+    """
+    if int(is_causal) != 1:
+        raise ValueError("only is_causal=1 is defined")
+    Q, K, V, D, s = resolve_call(query, key, value, num_heads, kv_num_heads, scale)
+    cum = np.asarray(cum, dtype=np.int64)
+    past = np.asarray(past, dtype=np.int64)
+    N = Q.shape[0]
+    if cum[0] != 0 or cum[-1] != N or np.any(np.diff(cum) < 0):
+        raise ValueError("cumulative_sequence_length must run from 0 to N")
+    kc, vc = scatter_kv(key_cache, value_cache, K, V, cum, past, block_table, slot_mapping)
+    out = np.full((N, num_heads, D), np.nan)
+    want = None if rows is None else np.zeros(N, dtype=bool)
+    if want is not None:
+        want[np.asarray(rows, dtype=np.int64)] = True
+    for b in range(past.shape[0]):
+        t0, t1 = int(cum[b]), int(cum[b + 1])
+        if t1 == t0:
+            continue
+        local = None
+        if want is not None:
+            local = np.nonzero(want[t0:t1])[0]
+            if local.size == 0:
+                continue
+        L = int(past[b]) + (t1 - t0)
+        Kb, Vb = gather_history(kc, vc, block_table, b, L)
+        Qb = Q[t0:t1].astype(np.float64)
+        out[t0:t1] = attend_sequence(Qb, Kb, Vb, int(past[b]), s, rows=local)
+    return out.reshape(N, num_heads * D), kc, vc
+
+
+def partial_state(q_row: np.ndarray, Kk: np.ndarray, Vk: np.ndarray, scale: float,
+                  keys: Sequence[int]):
+    """Partial attention state of one query row and head over a key subset.
+
+    "WS2 CP-Aware Attention Contract", Reduction Semantics: a partial state is
+    (out, attention-domain lse).  Here out = sum_j softmax_J(s)_j v_j and
+    lse = log sum_{j in J} exp(s_j) with s_j = scale <q, k_j>, natural log,
+    fp64.  q_row [D], Kk/Vk [L, D].
+    """
+    J = np.asarray(keys, dtype=np.int64)
+    s = scale * (Kk[J] @ q_row)
+    m = s.max()
+    w = np.exp(s - m)
+    return (w @ Vk[J]) / w.sum(), m + math.log(w.sum())
+
+
+def merge_partials(outs: Sequence[np.ndarray], lses: Sequence[float]) -> np.ndarray:
+    """Fixed-order merge of partial states ("WS2 CP-Aware Attention Contract",
+    Reduction Semantics: online-softmax merge by lse, fp32-or-wider
+    accumulation, fixed global block order, downcast only at the final write).
+    out = sum_s e^{lse_s - M} out_s / sum_s e^{lse_s - M}, M = max_s lse_s,
+    summed in the given order."""
+    M = max(lses)
+    num = np.zeros_like(np.asarray(outs[0], dtype=np.float64))
+    den = 0.0
+    for o, l in zip(outs, lses):
+        w = math.exp(l - M)
+        num = num + w * np.asarray(o, dtype=np.float64)
+        den += w
+    return num / den

@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged KV-cache attention path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pa_paged_attention() call (cache scatter, planning, split-KV
+decode, split merge, MFMA prefill) on one synthetic batch whose inputs are
+already resident in HBM.  The headline workload is pure_decode: 64 single-token
+decodes over 512-4096 cached tokens, 32/8 heads, head_size 128, block_size 16.
+The run prints ONE JSON line on stdout; progress goes to stderr.
+
+Measured:
+  value         decode KV-read GB/s of the whole step (logical history bytes
+                sum_b L_b * 2 * Hkv * D * 2 / step time)
+  roofline      the dominant kernel's algorithmic bytes (or flops) per launch
+                over its average duration, timed with HIP events the library
+                records on its own stream around each launch
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
+                workload, in the same unit
+  also          the other workloads' step times, TFLOP/s, GB/s, tokens/s
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode KV-read GB/s (% HBM peak); prefill TFLOP/s (% MFMA peak); tokens/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
+KERNEL_SRC = {"decode": "pa_decode.hip", "prefill": "pa_prefill.hip",
+              "merge": "pa_decode.hip", "scatter_plan": "pa_scatter.hip"}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash(kernel: str) -> str:
+    path = os.path.join(ROOT, "paged_kv_varlen_amd", "csrc", KERNEL_SRC[kernel])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, or None
+    when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Runner:
+    """Device copies of one batch plus the preallocated output and workspace."""
+
+    def __init__(self, batch, torch, pa):
+        self.torch, self.pa, self.b = torch, pa, batch
+        dev = "cuda:0"
+        to = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        self.q, self.k, self.v = to(batch.query), to(batch.key), to(batch.value)
+        self.kc, self.vc = to(batch.key_cache), to(batch.value_cache)
+        self.cum, self.past = to(batch.cum), to(batch.past)
+        self.table, self.slots = to(batch.block_table), to(batch.slot_mapping)
+        D = batch.head_size
+        self.out = torch.empty((batch.num_tokens, batch.num_heads * D), dtype=torch.float16,
+                               device=dev)
+        args = pa.make_args(self.q, self.k, self.v, self.kc, self.vc, self.cum, self.past,
+                            self.table, self.slots, self.out, num_heads=batch.num_heads,
+                            kv_num_heads=batch.kv_num_heads, scale=batch.scale)
+        self.ws = torch.empty(max(1, pa.workspace_bytes(args)), dtype=torch.uint8, device=dev)
+
+    def step(self, events=None):
+        b = self.b
+        self.pa.paged_attention(self.q, self.k, self.v, self.kc, self.vc, self.cum, self.past,
+                                self.table, self.slots, num_heads=b.num_heads,
+                                kv_num_heads=b.kv_num_heads, scale=b.scale, output=self.out,
+                                workspace=self.ws, kernel_events=events)
+
+
+def time_workload(name: str, steps: int, warmup: int, seed: int, torch, pa, W):
+    t_gen = time.perf_counter()
+    b = W.workload(name, seed)
+    work = W.work(b)
+    log(f"[bench] {name}: generated in {time.perf_counter() - t_gen:.1f}s "
+        f"(N={b.num_tokens}, B={b.batch_size}, KV {work['kv_hist_bytes'] / 1e9:.3f} GB, "
+        f"{work['flops'] / 1e12:.3f} TFLOP)")
+    r = Runner(b, torch, pa)
+    for _ in range(warmup):
+        r.step()
+    torch.cuda.synchronize()
+
+    # phase A: the timed region (steps back to back, no per-kernel events)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        r.step()
+    end.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3 / steps
+    ms = start.elapsed_time(end) / steps
+
+    # phase B: same steps with the library recording events around each kernel
+    nk = len(pa.KERNELS)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nk)] for _ in range(steps)]
+    for row in evs:  # create the underlying HIP events
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    for k in range(steps):
+        r.step(evs[k])
+    torch.cuda.synchronize()
+    kernel_ms = {kname: float(np.mean([evs[s][2 * i].elapsed_time(evs[s][2 * i + 1])
+                                       for s in range(steps)]))
+                 for i, kname in enumerate(pa.KERNELS)}
+    log(f"[bench] {name}: {ms * 1e3:.1f} us/step (wall {wall_ms * 1e3:.1f}), kernels "
+        + ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in kernel_ms.items()))
+    del r
+    torch.cuda.empty_cache()
+    return b, work, ms, wall_ms, kernel_ms
+
+
+def summarize(name, b, work, ms, kernel_ms):
+    s = ms / 1e3
+    out = {
+        "workload": name,
+        "ms_per_step": round(ms, 5),
+        "tokens_per_s": round(work["tokens"] / s, 1),
+        "kv_tokens_per_s": round(work["kv_tokens"] / s, 1),
+        "kv_read_GBps": round(work["kv_hist_bytes"] / s / 1e9, 2),
+        "alg_TFLOPps": round(work["flops"] / s / 1e12, 3),
+        "kernel_us": {k: round(v * 1e3, 2) for k, v in kernel_ms.items()},
+    }
+    if "kv_unique_bytes" in work:
+        out["kv_unique_read_GBps"] = round(work["kv_unique_bytes"] / s / 1e9, 2)
+    return out
+
+
+def roofline(name, work, kernel_ms):
+    """Dominant kernel: decode (bytes) unless prefill flops dominate."""
+    dec_t, pf_t = kernel_ms["decode"] / 1e3, kernel_ms["prefill"] / 1e3
+    if work["prefill_flops"] > 0 and pf_t >= dec_t:
+        achieved = work["prefill_flops"] / pf_t / 1e12
+        traffic = measured_traffic("prefill", name)
+        return {"kernel": "prefill", "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic,
+                "kernel_us": round(kernel_ms["prefill"] * 1e3, 2),
+                "work_per_launch": work["prefill_flops"]}
+    achieved = work["decode_kv_hist_bytes"] / dec_t / 1e9
+    traffic = measured_traffic("decode", name)
+    return {"kernel": "decode", "bound": "hbm", "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic, "kernel_us": round(kernel_ms["decode"] * 1e3, 2),
+            "work_per_launch": work["decode_kv_hist_bytes"]}
+
+
+def sub_batch(b, seqs, W):
+    """The sequences ``seqs`` of batch b as a batch of their own (same caches)."""
+    rows = np.concatenate([np.arange(b.cum[i], b.cum[i + 1]) for i in seqs]).astype(np.int64)
+    pick = lambda x: None if x is None else x[rows]
+    return W.Batch(name=b.name, seed=b.seed, query=b.query[rows], key=pick(b.key),
+                   value=pick(b.value), key_cache=b.key_cache, value_cache=b.value_cache,
+                   cum=W.cum_from_lens(b.q_lens[seqs]), past=b.past[seqs],
+                   block_table=b.block_table[seqs], slot_mapping=pick(b.slot_mapping),
+                   num_heads=b.num_heads, kv_num_heads=b.kv_num_heads, head_size=b.head_size,
+                   block_size=b.block_size, scale=b.scale)
+
+
+def cpu_baseline(b, W, target_s: float):
+    """Time the oracle on the first k sequences, k sized for ~target_s seconds."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+
+    def run(k):
+        sb = sub_batch(b, np.arange(k), W)
+        t = time.perf_counter()
+        oracle.paged_attention(sb.query, sb.key, sb.value, sb.key_cache, sb.value_cache, sb.cum,
+                               sb.past, sb.block_table, sb.slot_mapping, num_heads=sb.num_heads,
+                               kv_num_heads=sb.kv_num_heads, scale=sb.scale)
+        return time.perf_counter() - t, W.work(sb)
+
+    t1, _ = run(1)
+    k = int(min(b.batch_size, max(1, target_s / max(t1, 1e-3))))
+    t, work = run(k)
+    log(f"[bench] cpu oracle: {k} of {b.batch_size} sequences in {t:.1f}s ({threads} BLAS threads)")
+    return {"value": round(work["kv_hist_bytes"] / t / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"first {k} of {b.batch_size} sequences of {b.name} seed {b.seed} "
+                      f"(numpy fp64 oracle incl. its cache copies; {t:.1f} s wall)",
+            "seconds": round(t, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="pure_decode")
+    ap.add_argument("--also", default="mixed,long_prefill",
+                    help="comma list of other workloads to time (empty for none)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU mode in this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_varlen_amd as pa
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    pa.library()  # fail loudly if the HIP library is missing
+
+    b, work, ms, wall_ms, kms = time_workload(args.workload, args.steps, args.warmup, args.seed,
+                                              torch, pa, W)
+    head = summarize(args.workload, b, work, ms, kms)
+    also = []
+    for name in [x for x in args.also.split(",") if x and x != args.workload]:
+        ob, owork, oms, _, okms = time_workload(name, args.steps, args.warmup, args.seed, torch,
+                                                pa, W)
+        entry = summarize(name, ob, owork, oms, okms)
+        entry["roofline"] = roofline(name, owork, okms)
+        also.append(entry)
+        del ob
+
+    line = {
+        "metric": METRIC,
+        "value": round(work["decode_kv_hist_bytes"] / (ms / 1e3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "seed": args.seed, "batch": b.batch_size,
+                   "num_tokens": b.num_tokens, "num_heads": b.num_heads,
+                   "kv_num_heads": b.kv_num_heads, "head_size": b.head_size,
+                   "block_size": b.block_size, "num_blocks": b.num_blocks,
+                   "kv_hist_bytes": work["kv_hist_bytes"], "wall_ms_per_step": round(wall_ms, 5)},
+        "roofline": roofline(args.workload, work, kms),
+        "tokens_per_s": head["tokens_per_s"],
+        "kernel_us": head["kernel_us"],
+        "also": also,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(b, W, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,180 @@
+/*
+ * pagedattn.h - C ABI of the MI355X (gfx950) paged KV-cache attention library.
+ *
+ * One compute entry point, pa_paged_attention(), implements the
+ * com.microsoft PagedAttention operator in its SEPARATE key/value cache
+ * layout as the model-card README "com.microsoft.PagedAttention" defines it
+ * (sections Description, Inputs, Outputs, Attributes, Type constraints):
+ *
+ *   1. the step's keys and values are written ("scattered") into the block
+ *      caches, in place, at slot_mapping[t] when given (-1 = no write), else
+ *      at the slot that past_seqlens and block_table give token t;
+ *   2. every packed query row then attends, causally and with grouped-query
+ *      heads, to its sequence's history read back from the caches through
+ *      block_table, which defines the read path.
+ *
+ * Readings of points the pages leave open (stated once here, applied by every
+ * kernel):
+ *   - query head h uses key/value head h / (num_heads / kv_num_heads)
+ *     (contiguous groups; the Qwen3-8B example of "WS2 CP-Aware Attention
+ *     Contract" has one rank own query heads 0-15 with KV heads 0-3);
+ *   - new row i of sequence b is at logical position past_seqlens[b] + i and
+ *     sees keys 0 .. past_seqlens[b] + i (bottom-right causal offset, "WS2
+ *     CP-Aware Attention Contract", Mode-Specific Metadata);
+ *   - everything is read from the cache after the writes, so a token whose
+ *     slot is -1 sees the old cache content at its own position;
+ *   - a packed query row is [Q | K | V], each head-major [heads, head_size].
+ *
+ * Memory ownership: every pointer is caller-owned.  The library never
+ * allocates, frees or keeps a pointer after the call returns.  Device
+ * pointers must point to memory of the current HIP device.
+ *
+ * Ordering: the call is asynchronous on the given HIP stream.  It performs no
+ * host<->device copy and no synchronisation (except under the environment
+ * variable PA_DEBUG_CHECKS=1, see pa_paged_attention), so it may be captured
+ * into a HIP graph.  Within one call the cache writes precede every cache
+ * read.  Two calls that share caches or a workspace must be ordered by the
+ * caller (same stream, or events).
+ *
+ * The header is plain C99 and includes no HIP header: streams are passed as
+ * void* (a hipStream_t; NULL = the default stream).
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+/* Result codes.  Every host-checkable fault returns one of these before any
+ * device work is enqueued (typed errors, as the acceptance criteria of "Add
+ * Qwen3.8 packed hybrid PagedAttention export for ORT GenAI Engine" ask for
+ * unsupported dtype/cache combinations). */
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL_ARG = 1,     /* a required pointer is NULL                          */
+  PA_ERR_SHAPE = 2,        /* sizes inconsistent with each other                  */
+  PA_ERR_UNSUPPORTED = 3,  /* valid for the operator, not supported by the kernels */
+  PA_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than pa_workspace_bytes() */
+  PA_ERR_ALIGNMENT = 5,    /* a tensor pointer is not 16-byte aligned             */
+  PA_ERR_ABI = 6,          /* args->struct_size does not match this library      */
+  PA_ERR_METADATA = 7,     /* PA_DEBUG_CHECKS=1 only: device metadata invalid     */
+  PA_ERR_HIP = 8           /* a HIP runtime call or kernel launch failed          */
+} pa_status;
+
+/* Element type T of query/key/value/caches/output (README, Type constraints:
+ * T = float16; S = int32 for every index input). */
+typedef enum pa_dtype { PA_DTYPE_F16 = 1 } pa_dtype;
+
+/*
+ * Arguments of one call.  Tensor layouts are dense row-major.
+ *
+ *  query        T [num_tokens, query_width].  query_width = num_heads*head_size,
+ *               or (num_heads + 2*kv_num_heads)*head_size when key and value
+ *               are both NULL (packed [Q|K|V] rows).  (README, Inputs: query)
+ *  key, value   T [num_tokens, kv_num_heads*head_size], or both NULL.
+ *               (README, Inputs: key, value)
+ *  key_cache,
+ *  value_cache  T [num_blocks, block_size, cache_kv_heads, cache_head_size],
+ *               read and written in place; the two are always updated
+ *               together.  (README, Inputs: key_cache, value_cache; Outputs)
+ *  cumulative_sequence_length
+ *               S [batch_size + 1], exclusive prefix sums of the new-token
+ *               counts: sequence b owns tokens [cum[b], cum[b+1]); cum[0] = 0
+ *               and cum[batch_size] = num_tokens.  (README, Inputs)
+ *  past_seqlens S [batch_size], tokens already cached per sequence.
+ *  block_table  S [batch_size, max_blocks_per_seq]: physical block of each
+ *               logical block.  Entries 0 .. ceil(L_b/block_size)-1 of row b
+ *               (L_b = past_seqlens[b] + new tokens) must lie in
+ *               [0, num_blocks); later entries are never read.
+ *  slot_mapping S [num_tokens] or NULL: flat destination slot
+ *               block_id*block_size + offset of each token, -1 = no write.
+ *  output       T [num_tokens, num_heads*head_size], written; must not
+ *               overlap any input.  (README, Outputs: output)
+ *
+ * Device metadata (cum, past, block_table, slot_mapping) is trusted: values
+ * outside the rules above (cum not non-decreasing, a block id or slot out of
+ * range, two tokens naming one slot) give undefined results.  Set the
+ * environment variable PA_DEBUG_CHECKS=1 to have the call copy the metadata to
+ * the host, check it and return PA_ERR_METADATA (this synchronises).
+ *
+ * Supported by the kernels (else PA_ERR_UNSUPPORTED): dtype PA_DTYPE_F16,
+ * is_causal == 1, head_size 64 or 128, block_size a multiple of 16 up to
+ * 4096, num_heads/kv_num_heads <= 64.  All tensor pointers 16-byte aligned.
+ */
+typedef struct pa_args {
+  uint32_t struct_size;          /* = sizeof(pa_args)                      */
+  int32_t dtype;                 /* pa_dtype                               */
+
+  const void *query;
+  const void *key;               /* NULL together with value => packed     */
+  const void *value;
+  void *key_cache;
+  void *value_cache;
+  const int32_t *cumulative_sequence_length;
+  const int32_t *past_seqlens;
+  const int32_t *block_table;
+  const int32_t *slot_mapping;   /* may be NULL                            */
+  void *output;
+
+  int64_t num_tokens;            /* N                                      */
+  int64_t query_width;           /* columns of query                       */
+  int32_t batch_size;            /* B                                      */
+  int32_t num_heads;             /* H   (attribute num_heads)              */
+  int32_t kv_num_heads;          /* Hkv (attribute kv_num_heads)           */
+  int32_t num_blocks;            /* cache dim 0                            */
+  int32_t block_size;            /* cache dim 1                            */
+  int32_t cache_kv_heads;        /* cache dim 2, must equal kv_num_heads   */
+  int32_t cache_head_size;       /* cache dim 3, must equal head_size      */
+  int32_t max_blocks_per_seq;    /* block_table dim 1                      */
+  float scale;                   /* 0 => 1/sqrt(head_size) (README, Attributes) */
+  int32_t is_causal;             /* must be 1 (README, Attributes)         */
+
+  void *workspace;               /* device scratch, caller-owned           */
+  size_t workspace_bytes;        /* its size, >= pa_workspace_bytes(args)  */
+
+  /* Optional measurement hook, NULL = off.  Otherwise an array of
+   * 2*PA_KERNEL_COUNT hipEvent_t handles (created by the caller with timing
+   * enabled): the call records events[2k] on `stream` right before it
+   * launches kernel k and events[2k+1] right after, so a tool can time each
+   * kernel on the stream it runs on.  Kernel k = enum pa_kernel. */
+  void *const *kernel_events;
+} pa_args;
+
+/* Kernels launched by one call, in launch order (indices into kernel_events). */
+enum pa_kernel {
+  PA_KERNEL_SCATTER_PLAN = 0,  /* cache writes + device work lists        */
+  PA_KERNEL_DECODE = 1,        /* split-KV attention of single-token rows */
+  PA_KERNEL_MERGE = 2,         /* fixed-order merge of decode splits      */
+  PA_KERNEL_PREFILL = 3,       /* MFMA attention of multi-token rows      */
+  PA_KERNEL_COUNT = 4
+};
+
+/* Run the operator on `stream` (a hipStream_t, NULL = default stream).
+ * Validates every host-visible argument first; on any error nothing is
+ * enqueued and the caches are untouched.  PA_ERR_HIP means a launch failed;
+ * the caches may then be partly written. */
+pa_status pa_paged_attention(const pa_args *args, void *stream);
+
+/* Bytes of device workspace pa_paged_attention needs for these shapes (an
+ * upper bound from static sizes only: num_tokens, batch_size, num_heads,
+ * head_size, block_size, max_blocks_per_seq).  Pure host function; returns 0
+ * when the shape fields are invalid.  Pointer fields are ignored. */
+size_t pa_workspace_bytes(const pa_args *args);
+
+/* Static, NUL-terminated description of a status code. */
+const char *pa_status_string(pa_status status);
+
+/* PA_ABI_VERSION of the built library. */
+int32_t pa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

@@ -1,0 +1,214 @@
+"""Python binding of libpagedattn.so (the MI355X paged KV-cache attention library).
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every step of the computation runs in the library's HIP kernels.
+There is no fallback: if the library is not built, every call raises.
+
+    out = paged_attention(query, key, value, key_cache, value_cache,
+                          cumulative_sequence_length, past_seqlens, block_table,
+                          slot_mapping=None, num_heads=H, kv_num_heads=Hkv,
+                          scale=0.0)
+
+Argument meaning follows the com.microsoft PagedAttention operator (model-card
+README "com.microsoft.PagedAttention", sections Inputs, Outputs, Attributes);
+key_cache and value_cache are updated in place.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["paged_attention", "workspace_bytes", "PagedAttentionError", "PaArgs", "library",
+           "library_path", "STATUS"]
+
+library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
+
+PA_DTYPE_F16 = 1
+ABI_VERSION = 1
+KERNELS = ("scatter_plan", "decode", "merge", "prefill")  # enum pa_kernel order
+STATUS = {
+    0: "PA_OK", 1: "PA_ERR_NULL_ARG", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED",
+    4: "PA_ERR_WORKSPACE", 5: "PA_ERR_ALIGNMENT", 6: "PA_ERR_ABI", 7: "PA_ERR_METADATA",
+    8: "PA_ERR_HIP",
+}
+
+
+class PaArgs(ctypes.Structure):
+    """Mirror of pa_args in include/pagedattn.h (same order and types)."""
+
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("dtype", ctypes.c_int32),
+        ("query", ctypes.c_void_p),
+        ("key", ctypes.c_void_p),
+        ("value", ctypes.c_void_p),
+        ("key_cache", ctypes.c_void_p),
+        ("value_cache", ctypes.c_void_p),
+        ("cumulative_sequence_length", ctypes.c_void_p),
+        ("past_seqlens", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("slot_mapping", ctypes.c_void_p),
+        ("output", ctypes.c_void_p),
+        ("num_tokens", ctypes.c_int64),
+        ("query_width", ctypes.c_int64),
+        ("batch_size", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("kv_num_heads", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("cache_kv_heads", ctypes.c_int32),
+        ("cache_head_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("is_causal", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("kernel_events", ctypes.c_void_p),
+    ]
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_LIB = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libpagedattn.so (once).  Raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(f"{library_path} is missing: build it with "
+                               "`python -m paged_kv_varlen_amd.build`")
+        lib = ctypes.CDLL(library_path)
+        lib.pa_paged_attention.argtypes = [ctypes.POINTER(PaArgs), ctypes.c_void_p]
+        lib.pa_paged_attention.restype = ctypes.c_int
+        lib.pa_workspace_bytes.argtypes = [ctypes.POINTER(PaArgs)]
+        lib.pa_workspace_bytes.restype = ctypes.c_size_t
+        lib.pa_status_string.argtypes = [ctypes.c_int]
+        lib.pa_status_string.restype = ctypes.c_char_p
+        lib.pa_abi_version.argtypes = []
+        lib.pa_abi_version.restype = ctypes.c_int32
+        if lib.pa_abi_version() != ABI_VERSION:
+            raise RuntimeError("libpagedattn.so ABI version mismatch")
+        _LIB = lib
+    return _LIB
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    return PA_DTYPE_F16 if t.dtype == torch.float16 else 0
+
+
+def make_args(query, key, value, key_cache, value_cache, cumulative_sequence_length,
+              past_seqlens, block_table, slot_mapping, output, *, num_heads: int,
+              kv_num_heads: int, scale: float = 0.0, is_causal: int = 1,
+              workspace: Optional[torch.Tensor] = None) -> PaArgs:
+    """Fill a PaArgs from tensors (no checks beyond what marshalling needs:
+    the library validates shapes, dtypes and alignment itself)."""
+    for name, t in (("query", query), ("key", key), ("value", value), ("key_cache", key_cache),
+                    ("value_cache", value_cache),
+                    ("cumulative_sequence_length", cumulative_sequence_length),
+                    ("past_seqlens", past_seqlens), ("block_table", block_table),
+                    ("slot_mapping", slot_mapping), ("output", output)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    for name, t in (("cumulative_sequence_length", cumulative_sequence_length),
+                    ("past_seqlens", past_seqlens), ("block_table", block_table),
+                    ("slot_mapping", slot_mapping)):
+        if t is not None and t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32 (type constraint S)")
+    a = PaArgs()
+    a.struct_size = ctypes.sizeof(PaArgs)
+    same = all(t is None or t.dtype == query.dtype
+               for t in (key, value, key_cache, value_cache, output))
+    a.dtype = _dtype_code(query) if same else 0
+    a.query = _ptr(query)
+    a.key = _ptr(key)
+    a.value = _ptr(value)
+    a.key_cache = _ptr(key_cache)
+    a.value_cache = _ptr(value_cache)
+    a.cumulative_sequence_length = _ptr(cumulative_sequence_length)
+    a.past_seqlens = _ptr(past_seqlens)
+    a.block_table = _ptr(block_table)
+    a.slot_mapping = _ptr(slot_mapping)
+    a.output = _ptr(output)
+    a.num_tokens = query.shape[0]
+    a.query_width = query.shape[1]
+    a.batch_size = past_seqlens.shape[0]
+    a.num_heads = num_heads
+    a.kv_num_heads = kv_num_heads
+    a.num_blocks, a.block_size, a.cache_kv_heads, a.cache_head_size = key_cache.shape
+    if value_cache.shape != key_cache.shape:
+        raise ValueError("value_cache must have key_cache's shape")
+    a.max_blocks_per_seq = block_table.shape[1] if block_table.dim() == 2 else 0
+    a.scale = float(scale)
+    a.is_causal = int(is_causal)
+    if workspace is not None:
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    return a
+
+
+def workspace_bytes(args: PaArgs) -> int:
+    return int(library().pa_workspace_bytes(ctypes.byref(args)))
+
+
+def call(args: PaArgs, stream: Optional[int] = None) -> None:
+    """Run the library's entry point on a filled PaArgs; raise on error."""
+    lib = library()
+    st = lib.pa_paged_attention(ctypes.byref(args), stream)
+    if st != 0:
+        raise PagedAttentionError(st, lib.pa_status_string(st).decode())
+
+
+def paged_attention(query: torch.Tensor, key: Optional[torch.Tensor],
+                    value: Optional[torch.Tensor], key_cache: torch.Tensor,
+                    value_cache: torch.Tensor, cumulative_sequence_length: torch.Tensor,
+                    past_seqlens: torch.Tensor, block_table: torch.Tensor,
+                    slot_mapping: Optional[torch.Tensor] = None, *, num_heads: int,
+                    kv_num_heads: int, scale: float = 0.0, is_causal: int = 1,
+                    output: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None,
+                    stream: Optional[torch.cuda.Stream] = None,
+                    kernel_events=None) -> torch.Tensor:
+    """Scatter the step's K/V into the caches (in place) and return the
+    attention output [num_tokens, num_heads * head_size].
+
+    ``kernel_events``: optional sequence of 2*len(KERNELS) torch.cuda.Event
+    (enable_timing=True); the library records pair k around its k-th kernel."""
+    lib = library()
+    dev = query.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a HIP device")
+    packed = key is None
+    heads = num_heads + 2 * kv_num_heads if packed else num_heads
+    D = query.shape[1] // heads if heads > 0 else 0
+    if output is None:
+        output = torch.empty((query.shape[0], num_heads * D), dtype=query.dtype, device=dev)
+    args = make_args(query, key, value, key_cache, value_cache, cumulative_sequence_length,
+                     past_seqlens, block_table, slot_mapping, output, num_heads=num_heads,
+                     kv_num_heads=kv_num_heads, scale=scale, is_causal=is_causal)
+    need = int(lib.pa_workspace_bytes(ctypes.byref(args)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    args.workspace = workspace.data_ptr()
+    args.workspace_bytes = workspace.numel()
+    ev_array = None
+    if kernel_events is not None:
+        if len(kernel_events) != 2 * len(KERNELS):
+            raise ValueError(f"kernel_events needs {2 * len(KERNELS)} events")
+        ev_array = (ctypes.c_void_p * len(kernel_events))(*[e.cuda_event for e in kernel_events])
+        args.kernel_events = ctypes.cast(ev_array, ctypes.c_void_p)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    call(args, s.cuda_stream)
+    return output

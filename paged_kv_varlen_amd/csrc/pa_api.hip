@@ -1,0 +1,292 @@
+// Host side of the C ABI: argument checks, workspace layout, launch plan.
+//
+// Every check here uses host-visible sizes only, so a call never waits for
+// the device (except under PA_DEBUG_CHECKS=1, which copies the metadata back
+// to check it).  Grids come from static shapes; the kernels read the real
+// amount of work from the plan the first kernel writes into the workspace.
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <set>
+#include <vector>
+
+#include "../../include/pagedattn.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kDecodeSplitKeys = 512;  // positions per decode split (multiple of 64)
+constexpr int kDecodeWavesPerCu = 8;   // decode workgroups resident per CU (grid sizing)
+constexpr int kPrefillWgPerCu = 2;     // prefill workgroups resident per CU (grid sizing)
+
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct Resolved {
+  int64_t N;
+  int B, H, Hkv, G, D, bs, NB, MB;
+  bool packed;
+  float scale;
+};
+
+pa_status resolve(const pa_args* a, Resolved* r) {
+  if (a == nullptr) return PA_ERR_NULL_ARG;
+  if (a->struct_size != sizeof(pa_args)) return PA_ERR_ABI;
+  if (a->num_tokens < 0 || a->num_tokens > INT32_MAX || a->batch_size < 0) return PA_ERR_SHAPE;
+  if (a->num_heads <= 0 || a->kv_num_heads <= 0 || a->num_heads % a->kv_num_heads != 0)
+    return PA_ERR_SHAPE;
+  if ((a->key == nullptr) != (a->value == nullptr)) return PA_ERR_SHAPE;
+  r->packed = a->key == nullptr;
+  const int64_t heads = r->packed ? a->num_heads + 2LL * a->kv_num_heads : a->num_heads;
+  if (a->query_width <= 0 || a->query_width % heads != 0) return PA_ERR_SHAPE;
+  const int64_t D = a->query_width / heads;
+  if (a->cache_kv_heads != a->kv_num_heads || a->cache_head_size != D) return PA_ERR_SHAPE;
+  if (a->num_blocks <= 0 || a->block_size <= 0 || a->max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+  if (a->batch_size == 0 && a->num_tokens != 0) return PA_ERR_SHAPE;
+  if (static_cast<int64_t>(a->max_blocks_per_seq) * a->block_size > INT32_MAX ||
+      static_cast<int64_t>(a->num_blocks) * a->block_size > INT32_MAX)
+    return PA_ERR_SHAPE;
+  if (a->dtype != PA_DTYPE_F16 || a->is_causal != 1) return PA_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return PA_ERR_UNSUPPORTED;
+  if (a->block_size % 16 != 0 || a->block_size > 4096) return PA_ERR_UNSUPPORTED;
+  if (a->num_heads / a->kv_num_heads > 64) return PA_ERR_UNSUPPORTED;
+  r->N = a->num_tokens;
+  r->B = a->batch_size;
+  r->H = a->num_heads;
+  r->Hkv = a->kv_num_heads;
+  r->G = a->num_heads / a->kv_num_heads;
+  r->D = static_cast<int>(D);
+  r->bs = a->block_size;
+  r->NB = a->num_blocks;
+  r->MB = a->max_blocks_per_seq;
+  r->scale = a->scale == 0.f ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(D))) : a->scale;
+  return PA_OK;
+}
+
+int prefill_positions(int G) { return kPrefillRows / G; }
+
+WorkspaceLayout layout(const Resolved& r) {
+  WorkspaceLayout w{};
+  const int64_t live = std::min<int64_t>(r.B, r.N);  // sequences with >= 1 token
+  const int64_t splits = (static_cast<int64_t>(r.MB) * r.bs + kDecodeSplitKeys - 1) / kDecodeSplitKeys;
+  w.max_dec_items = live * splits;
+  const int64_t P = prefill_positions(r.G);
+  w.max_pf_items = (r.N + P - 1) / P + live;
+  size_t off = 0;
+  w.ctrl = off;
+  off = align256(off + kCtrlSlots * sizeof(int32_t));
+  w.dec_items = off;
+  off = align256(off + w.max_dec_items * sizeof(int2));
+  w.seq_split = off;
+  off = align256(off + static_cast<size_t>(r.B) * sizeof(int2));
+  w.pf_items = off;
+  off = align256(off + w.max_pf_items * sizeof(int2));
+  w.part_lse = off;
+  off = align256(off + static_cast<size_t>(w.max_dec_items) * r.H * sizeof(float));
+  w.part_o = off;
+  off = align256(off + static_cast<size_t>(w.max_dec_items) * r.H * r.D * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int device_cus() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (static_cast<int>(cache.size()) <= dev) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
+// PA_DEBUG_CHECKS=1: copy the metadata to the host and check the contract.
+pa_status debug_check(const pa_args* a, const Resolved& r, hipStream_t s) {
+  if (hipStreamSynchronize(s) != hipSuccess) return PA_ERR_HIP;
+  std::vector<int32_t> cum(r.B + 1), past(r.B), table(static_cast<size_t>(r.B) * r.MB), slots;
+  auto get = [](void* dst, const void* src, size_t n) {
+    return hipMemcpy(dst, src, n, hipMemcpyDeviceToHost) == hipSuccess;
+  };
+  if (!get(cum.data(), a->cumulative_sequence_length, cum.size() * 4) ||
+      !get(past.data(), a->past_seqlens, past.size() * 4) ||
+      !get(table.data(), a->block_table, table.size() * 4))
+    return PA_ERR_HIP;
+  if (a->slot_mapping != nullptr) {
+    slots.resize(r.N);
+    if (r.N > 0 && !get(slots.data(), a->slot_mapping, slots.size() * 4)) return PA_ERR_HIP;
+  }
+  if (cum[0] != 0 || cum[r.B] != r.N) return PA_ERR_METADATA;
+  std::set<int64_t> written;
+  for (int b = 0; b < r.B; ++b) {
+    const int q = cum[b + 1] - cum[b];
+    if (q < 0 || past[b] < 0) return PA_ERR_METADATA;
+    const int64_t L = static_cast<int64_t>(past[b]) + q;
+    if (L > static_cast<int64_t>(r.MB) * r.bs) return PA_ERR_METADATA;
+    const int64_t n = (L + r.bs - 1) / r.bs;
+    std::set<int32_t> row;
+    for (int64_t j = 0; j < n; ++j) {
+      const int32_t pg = table[static_cast<size_t>(b) * r.MB + j];
+      if (pg < 0 || pg >= r.NB || !row.insert(pg).second) return PA_ERR_METADATA;
+    }
+    for (int i = 0; i < q; ++i) {
+      int64_t slot;
+      if (a->slot_mapping != nullptr) {
+        slot = slots[cum[b] + i];
+        if (slot < -1 || slot >= static_cast<int64_t>(r.NB) * r.bs) return PA_ERR_METADATA;
+      } else {
+        const int64_t pos = past[b] + i;
+        slot = static_cast<int64_t>(table[static_cast<size_t>(b) * r.MB + pos / r.bs]) * r.bs + pos % r.bs;
+      }
+      if (slot >= 0 && !written.insert(slot).second) return PA_ERR_METADATA;
+    }
+  }
+  return PA_OK;
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" {
+
+size_t pa_workspace_bytes(const pa_args* a) {
+  pa::Resolved r{};
+  if (pa::resolve(a, &r) != PA_OK) return 0;
+  return pa::layout(r).total;
+}
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL_ARG: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "inconsistent sizes";
+    case PA_ERR_UNSUPPORTED: return "valid for the operator but not supported by these kernels";
+    case PA_ERR_WORKSPACE: return "workspace missing or smaller than pa_workspace_bytes()";
+    case PA_ERR_ALIGNMENT: return "a tensor pointer is not 16-byte aligned";
+    case PA_ERR_ABI: return "pa_args.struct_size does not match the library";
+    case PA_ERR_METADATA: return "device metadata violates the operator contract";
+    case PA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
+
+pa_status pa_paged_attention(const pa_args* a, void* stream) {
+  using namespace pa;
+  Resolved r{};
+  pa_status st = resolve(a, &r);
+  if (st != PA_OK) return st;
+  if (r.N == 0) return PA_OK;  // no token: nothing is written or read
+  if (a->query == nullptr || a->key_cache == nullptr || a->value_cache == nullptr ||
+      a->cumulative_sequence_length == nullptr || a->past_seqlens == nullptr ||
+      a->block_table == nullptr || a->output == nullptr)
+    return PA_ERR_NULL_ARG;
+  if (!aligned16(a->query) || !aligned16(a->key) || !aligned16(a->value) ||
+      !aligned16(a->key_cache) || !aligned16(a->value_cache) || !aligned16(a->output) ||
+      !aligned4(a->cumulative_sequence_length) || !aligned4(a->past_seqlens) ||
+      !aligned4(a->block_table) || !aligned4(a->slot_mapping) || !aligned16(a->workspace))
+    return PA_ERR_ALIGNMENT;
+  const WorkspaceLayout w = layout(r);
+  if (a->workspace == nullptr || a->workspace_bytes < w.total) return PA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  const char* dbg = std::getenv("PA_DEBUG_CHECKS");
+  if (dbg != nullptr && dbg[0] == '1') {
+    st = debug_check(a, r, s);
+    if (st != PA_OK) return st;
+  }
+
+  // optional per-kernel events (measurement hook)
+  hipEvent_t const* ev = reinterpret_cast<hipEvent_t const*>(a->kernel_events);
+  auto mark = [&](int k, int edge) {
+    if (ev != nullptr) (void)hipEventRecord(ev[2 * k + edge], s);
+  };
+
+  char* ws = static_cast<char*>(a->workspace);
+  const uint16_t* q = static_cast<const uint16_t*>(a->query);
+  const int64_t qw = a->query_width;
+
+  ScatterPlanParams sp{};
+  if (r.packed) {
+    sp.key_src = q + static_cast<int64_t>(r.H) * r.D;
+    sp.value_src = q + static_cast<int64_t>(r.H + r.Hkv) * r.D;
+    sp.src_stride = qw;
+  } else {
+    sp.key_src = static_cast<const uint16_t*>(a->key);
+    sp.value_src = static_cast<const uint16_t*>(a->value);
+    sp.src_stride = static_cast<int64_t>(r.Hkv) * r.D;
+  }
+  sp.key_cache = static_cast<uint16_t*>(a->key_cache);
+  sp.value_cache = static_cast<uint16_t*>(a->value_cache);
+  sp.cum = a->cumulative_sequence_length;
+  sp.past = a->past_seqlens;
+  sp.block_table = a->block_table;
+  sp.slot_mapping = a->slot_mapping;
+  sp.ws_ctrl = reinterpret_cast<int32_t*>(ws + w.ctrl);
+  sp.dec_items = reinterpret_cast<int2*>(ws + w.dec_items);
+  sp.seq_split = reinterpret_cast<int2*>(ws + w.seq_split);
+  sp.pf_items = reinterpret_cast<int2*>(ws + w.pf_items);
+  sp.num_tokens = r.N;
+  sp.batch = r.B;
+  sp.max_blocks = r.MB;
+  sp.block_size = r.bs;
+  sp.row_elems = r.Hkv * r.D;
+  sp.split_keys = kDecodeSplitKeys;
+  sp.prefill_positions = prefill_positions(r.G);
+  mark(PA_KERNEL_SCATTER_PLAN, 0);
+  if (launch_scatter_plan(sp, s) != hipSuccess) return PA_ERR_HIP;
+  mark(PA_KERNEL_SCATTER_PLAN, 1);
+
+  AttnParams ap{};
+  ap.q = q;
+  ap.q_stride = qw;
+  ap.key_cache = sp.key_cache;
+  ap.value_cache = sp.value_cache;
+  ap.cum = sp.cum;
+  ap.past = sp.past;
+  ap.block_table = sp.block_table;
+  ap.out = static_cast<uint16_t*>(a->output);
+  ap.ws_ctrl = sp.ws_ctrl;
+  ap.seq_split = sp.seq_split;
+  ap.part_o = reinterpret_cast<float*>(ws + w.part_o);
+  ap.part_lse = reinterpret_cast<float*>(ws + w.part_lse);
+  ap.batch = r.B;
+  ap.num_heads = r.H;
+  ap.kv_heads = r.Hkv;
+  ap.group = r.G;
+  ap.max_blocks = r.MB;
+  ap.block_size = r.bs;
+  ap.split_keys = kDecodeSplitKeys;
+  ap.prefill_positions = prefill_positions(r.G);
+  ap.scale_log2 = r.scale * 1.4426950408889634f;
+
+  const int cus = device_cus();
+  const int64_t dec_work = w.max_dec_items * r.Hkv * (r.G / decode_heads_per_item(r.G));
+  const int dec_grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(dec_work, int64_t(cus) * kDecodeWavesPerCu)));
+  ap.items = sp.dec_items;
+  mark(PA_KERNEL_DECODE, 0);
+  if (launch_decode(ap, r.D, dec_grid, s) != hipSuccess) return PA_ERR_HIP;
+  mark(PA_KERNEL_DECODE, 1);
+  mark(PA_KERNEL_MERGE, 0);
+  if (launch_merge(ap, r.D, s) != hipSuccess) return PA_ERR_HIP;
+  mark(PA_KERNEL_MERGE, 1);
+
+  const int64_t pf_work = w.max_pf_items * r.Hkv;
+  const int pf_grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(pf_work, int64_t(cus) * kPrefillWgPerCu)));
+  ap.items = sp.pf_items;
+  mark(PA_KERNEL_PREFILL, 0);
+  if (launch_prefill(ap, r.D, pf_grid, s) != hipSuccess) return PA_ERR_HIP;
+  mark(PA_KERNEL_PREFILL, 1);
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+"""C-ABI checks that need no GPU (CPU only).
+
+* libpagedattn.so loads and exports every function include/pagedattn.h
+  declares.
+* The ctypes mirror of pa_args has the layout a C compiler gives the header.
+* Host-side validation returns the typed status codes before any device work
+  (the acceptance criteria of "Add Qwen3.8 packed hybrid PagedAttention export
+  for ORT GenAI Engine" ask for typed errors on unsupported combinations);
+  the pointers used here are fake and are never dereferenced because every
+  case fails, or has no token, before a launch.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import paged_kv_varlen_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+
+OK, NULL, SHAPE, UNSUP, WS, ALIGN, ABI, META, HIP = range(9)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    lib = pa.library()
+    names = declared_functions()
+    assert set(names) == {"pa_paged_attention", "pa_workspace_bytes", "pa_status_string",
+                          "pa_abi_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", pa.library_path], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (pa_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_struct_layout_matches_c(tmp_path):
+    fields = [f for f, _ in pa.PaArgs._fields_]
+    src = tmp_path / "layout.c"
+    body = "\n".join(f'  printf("{f} %zu\\n", offsetof(pa_args, {f}));' for f in fields)
+    src.write_text(f"""#include <stdio.h>
+#include <stddef.h>
+#include "pagedattn.h"
+int main(void) {{
+  printf("sizeof %zu\\n", sizeof(pa_args));
+{body}
+  return 0;
+}}
+""")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
+                    str(src), "-o", str(exe)], check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True,
+                                                         text=True, check=True).stdout.splitlines())
+    assert int(got["sizeof"]) == ctypes.sizeof(pa.PaArgs)
+    for f in fields:
+        assert int(got[f]) == getattr(pa.PaArgs, f).offset, f
+
+
+FAKE = 1 << 20  # an aligned, never-dereferenced address
+
+
+def args(**kw):
+    a = pa.PaArgs()
+    a.struct_size = ctypes.sizeof(pa.PaArgs)
+    a.dtype = 1
+    for p in ("query", "key", "value", "key_cache", "value_cache", "cumulative_sequence_length",
+              "past_seqlens", "block_table", "output"):
+        setattr(a, p, FAKE)
+    a.num_tokens, a.batch_size = 4, 2
+    a.num_heads, a.kv_num_heads = 4, 2
+    a.query_width = 4 * 64
+    a.num_blocks, a.block_size, a.cache_kv_heads, a.cache_head_size = 8, 16, 2, 64
+    a.max_blocks_per_seq = 4
+    a.is_causal = 1
+    a.workspace = FAKE
+    a.workspace_bytes = 0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def status(a):
+    return pa.library().pa_paged_attention(ctypes.byref(a) if a is not None else None, None)
+
+
+def test_workspace_bytes_static_bound():
+    a = args()
+    need = pa.workspace_bytes(a)
+    assert need > 0 and need % 256 == 0
+    bigger = args(max_blocks_per_seq=400)
+    assert pa.workspace_bytes(bigger) > need
+    assert pa.workspace_bytes(args(num_heads=3)) == 0  # invalid shape -> 0
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(), WS),                                        # workspace too small
+    (dict(struct_size=8), ABI),
+    (dict(num_heads=3), SHAPE),                          # H % Hkv != 0
+    (dict(value=None), SHAPE),                           # key without value
+    (dict(query_width=4 * 64 + 1), SHAPE),
+    (dict(cache_head_size=32), SHAPE),                   # cache dims disagree with D
+    (dict(cache_kv_heads=1), SHAPE),
+    (dict(batch_size=0), SHAPE),                         # tokens without sequences
+    (dict(num_tokens=-1), SHAPE),
+    (dict(num_blocks=0), SHAPE),
+    (dict(is_causal=0), UNSUP),                          # only is_causal=1 exists
+    (dict(dtype=0), UNSUP),                              # T must be float16
+    (dict(block_size=8), UNSUP),
+    (dict(query_width=4 * 32, cache_head_size=32), UNSUP),  # D=32 not built
+    (dict(query=None), NULL),
+    (dict(output=None), NULL),
+    (dict(query=FAKE + 2), ALIGN),
+    (dict(key_cache=FAKE + 8), ALIGN),
+    (dict(num_tokens=0, batch_size=2), OK),              # nothing to do: no device work
+])
+def test_host_validation(case, expect):
+    assert status(args(**case)) == expect
+
+
+def test_null_args_pointer():
+    assert pa.library().pa_paged_attention(None, None) == NULL
+
+
+def test_readme_example_shape_is_typed_unsupported():
+    # README example: H=2, Hkv=1, D=2, block_size 2, 3 blocks, B=1, N=2.
+    a = args(num_tokens=2, batch_size=1, num_heads=2, kv_num_heads=1, query_width=4,
+             num_blocks=3, block_size=2, cache_kv_heads=1, cache_head_size=2,
+             max_blocks_per_seq=3)
+    assert status(a) == UNSUP
+
+
+def test_packed_width_resolution():
+    # packed [Q|K|V] width (H+2Hkv)*D with key=value=NULL resolves D=64
+    a = args(key=None, value=None, query_width=(4 + 4) * 64)
+    assert pa.workspace_bytes(a) > 0
+    assert status(a) == WS
+
+
+def test_status_strings():
+    lib = pa.library()
+    for s in range(9):
+        assert lib.pa_status_string(s)
+    assert lib.pa_abi_version() == 1

@@ -1,0 +1,269 @@
+"""GPU parity of the HIP path against the CPU oracle (needs an MI355X).
+
+Bar (stated with the workloads): both caches bit-exact over every slot,
+written or untouched; outputs within max-abs 4e-3 of the fp64 oracle (fp16
+inputs, fp32 accumulation, O(1) data).  Full-size workloads are checked on
+every cache slot and on sampled output rows the oracle computes one by one.
+Every call goes through the C ABI (libpagedattn.so via ctypes).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_varlen_amd as pa
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+TOL = 4e-3
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def to_dev(x, dtype=None):
+    if x is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    return t.to(DEV) if dtype is None else t.to(DEV, dtype)
+
+
+class DevBatch:
+    def __init__(self, b: W.Batch):
+        self.q = to_dev(b.query)
+        self.k = to_dev(b.key)
+        self.v = to_dev(b.value)
+        self.kc = to_dev(b.key_cache)
+        self.vc = to_dev(b.value_cache)
+        self.cum = to_dev(b.cum)
+        self.past = to_dev(b.past)
+        self.table = to_dev(b.block_table)
+        self.slots = to_dev(b.slot_mapping)
+        self.b = b
+
+    def run(self, **kw):
+        b = self.b
+        return pa.paged_attention(self.q, self.k, self.v, self.kc, self.vc, self.cum, self.past,
+                                  self.table, self.slots, num_heads=b.num_heads,
+                                  kv_num_heads=b.kv_num_heads, scale=b.scale, **kw)
+
+
+def gpu_run(b: W.Batch):
+    say(f"[gpu] {b.name} seed={b.seed} N={b.num_tokens} B={b.batch_size} "
+        f"H={b.num_heads}/{b.kv_num_heads} D={b.head_size} bs={b.block_size} NB={b.num_blocks}")
+    d = DevBatch(b)
+    out = d.run()
+    torch.cuda.synchronize()
+    return (out.cpu().numpy(), d.kc.cpu().numpy(), d.vc.cpu().numpy())
+
+
+def sample_rows(b: W.Batch, per_seq=6, max_seqs=None, must=(), seed=0):
+    rng = np.random.default_rng(seed)
+    seqs = np.arange(b.batch_size)
+    if max_seqs is not None and b.batch_size > max_seqs:
+        seqs = np.sort(rng.choice(seqs, max_seqs, replace=False))
+    rows = set(int(x) for x in must)
+    for i in seqs:
+        t0, t1 = int(b.cum[i]), int(b.cum[i + 1])
+        if t1 - t0 <= per_seq:
+            rows.update(range(t0, t1))
+        else:
+            rows.update([t0, t1 - 1, t0 + (t1 - t0) // 2])
+            rows.update(int(x) for x in rng.choice(np.arange(t0, t1), per_seq - 3, replace=False))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def check(b: W.Batch, rows=None, gpu=None):
+    out, kc, vc = gpu if gpu is not None else gpu_run(b)
+    ref, rkc, rvc = oracle.paged_attention(b.query, b.key, b.value, b.key_cache, b.value_cache,
+                                           b.cum, b.past, b.block_table, b.slot_mapping,
+                                           num_heads=b.num_heads, kv_num_heads=b.kv_num_heads,
+                                           scale=b.scale, rows=rows)
+    assert np.array_equal(kc.view(np.uint16), rkc.view(np.uint16)), "key_cache differs"
+    assert np.array_equal(vc.view(np.uint16), rvc.view(np.uint16)), "value_cache differs"
+    sel = np.arange(b.num_tokens) if rows is None else rows
+    got = out[sel].astype(np.float64)
+    assert np.all(np.isfinite(got))
+    err = np.max(np.abs(got - ref[sel])) if sel.size else 0.0
+    say(f"      rows checked {sel.size}, max|err| {err:.3e}")
+    assert err <= TOL, f"max abs error {err}"
+    return err
+
+
+# ------------------------------------------------------------------ the five workloads
+
+def test_tiny():
+    check(W.tiny(0))
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_pure_decode_full(seed):
+    check(W.pure_decode(seed))
+
+
+def test_mixed():
+    b = W.mixed(0)
+    check(b, rows=sample_rows(b, per_seq=10))
+
+
+def test_long_prefill():
+    b = W.long_prefill(0)
+    # rows at query-tile edges (32 positions per tile for 4 heads per group) and random ones
+    edges = [0, 1, 31, 32, 33, 1023, 1024, 2015, 2016, 2046, 2047]
+    check(b, rows=sample_rows(b, per_seq=40, must=edges))
+
+
+@pytest.mark.timeout(900)
+def test_serving():
+    b = W.serving(0)
+    dropped = np.nonzero(b.slot_mapping < 0)[0]
+    rows = sample_rows(b, per_seq=5, max_seqs=48, must=dropped[:24])
+    check(b, rows=rows)
+
+
+# ------------------------------------------------------------------ shape and edge sweeps
+
+SWEEP = [
+    # (q_lens, past_lens, H, Hkv, D, bs)
+    ([1, 2, 17, 128, 129, 0, 300], [0, 1, 15, 16, 17, 5, 1000], 8, 2, 128, 16),
+    ([1, 1, 64, 3, 200], [255, 256, 257, 0, 511], 8, 8, 128, 256),
+    ([5, 1, 33, 1], [31, 32, 64, 700], 16, 2, 64, 32),
+    ([1, 40, 1, 7], [4000, 90, 9000, 1], 32, 4, 128, 64),
+    ([2, 1, 70], [0, 0, 0], 12, 4, 64, 16),      # G=3
+    ([1, 9, 1], [100, 100, 5000], 64, 1, 128, 16),  # G=64
+    ([1, 16, 1], [17, 3, 2000], 20, 4, 128, 48),  # G=5, block_size 48
+]
+
+
+@pytest.mark.parametrize("case", range(len(SWEEP)))
+@pytest.mark.parametrize("packed,slots", [(False, None), (True, "drop")])
+def test_sweep(case, packed, slots):
+    q, p, H, Hkv, D, bs = SWEEP[case]
+    n = sum(q)
+    b = W.make_batch(q, p, num_heads=H, kv_num_heads=Hkv, head_size=D, block_size=bs,
+                     seed=100 + case, packed=packed, slot_mode=slots,
+                     drop_count=max(1, n // 20) if slots else 0, num_blocks=None,
+                     name=f"sweep{case}")
+    check(b)
+
+
+def test_custom_scale_and_spare_pages():
+    b = W.make_batch([1, 30, 1], [77, 12, 3000], num_heads=8, kv_num_heads=2, head_size=128,
+                     block_size=16, seed=7, scale=-0.21, num_blocks=400, name="scale")
+    check(b)
+
+
+def test_first_token_returns_its_value_row_exactly():
+    # past 0, one new token: the only weight is exactly 1
+    b = W.make_batch([1, 1, 1], [0, 0, 0], num_heads=8, kv_num_heads=2, head_size=128,
+                     block_size=16, seed=8, name="first")
+    out, _, _ = gpu_run(b)
+    G = 4
+    for t in range(3):
+        for h in range(8):
+            k = h // G
+            assert np.array_equal(out[t, h * 128:(h + 1) * 128].view(np.uint16),
+                                  b.value[t, k * 128:(k + 1) * 128].view(np.uint16))
+
+
+def test_garbage_outside_history_is_never_used():
+    # every cache slot the call must not read holds NaN: results are unchanged
+    b = W.make_batch([1, 37, 1, 5], [50, 20, 4095, 0], num_heads=8, kv_num_heads=2,
+                     head_size=128, block_size=64, seed=9, num_blocks=200, name="nan")
+    keep = np.zeros(b.num_blocks * b.block_size, dtype=bool)
+    for i in range(b.batch_size):
+        L = int(b.kv_lens[i])
+        for j in range(L):
+            keep[int(b.block_table[i, j // b.block_size]) * b.block_size + j % b.block_size] = True
+    for cache in (b.key_cache, b.value_cache):
+        flat = cache.reshape(b.num_blocks * b.block_size, -1)
+        flat[~keep] = np.float16(np.nan)
+    check(b)
+
+
+def test_empty_sequences_and_empty_call():
+    b = W.make_batch([0, 3, 0, 1, 0], [4, 10, 0, 33, 2], num_heads=4, kv_num_heads=2,
+                     head_size=64, block_size=16, seed=10, name="empties")
+    check(b)
+    e = W.make_batch([0, 0], [3, 9], num_heads=4, kv_num_heads=2, head_size=64, block_size=16,
+                     seed=11, name="no_tokens")
+    out, kc, vc = gpu_run(e)
+    assert out.shape == (0, 256)
+    assert np.array_equal(kc.view(np.uint16), e.key_cache.view(np.uint16))
+
+
+def test_long_decode_many_splits():
+    b = W.make_batch([1, 1, 1, 2], [16383, 9000, 511, 12000], num_heads=32, kv_num_heads=8,
+                     head_size=128, block_size=256, seed=12, name="long_decode")
+    check(b)
+
+
+def test_deterministic_bits():
+    b = W.mixed(1)
+    d = DevBatch(b)
+    o1 = d.run().clone()
+    o2 = d.run().clone()  # idempotent: the second call rewrites the same cache bits
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_chunked_continuation_matches_one_shot():
+    H, Hkv, D, bs = 8, 2, 128, 16
+    b = W.make_batch([150], [37], num_heads=H, kv_num_heads=Hkv, head_size=D, block_size=bs,
+                     seed=13, name="chunks")
+    one = DevBatch(b)
+    o_full = one.run()
+    two = DevBatch(b)
+    cut = 61
+    mk = lambda x: x.contiguous()
+    o_a = pa.paged_attention(mk(two.q[:cut]), mk(two.k[:cut]), mk(two.v[:cut]), two.kc, two.vc,
+                             to_dev(np.array([0, cut], np.int32)), two.past, two.table,
+                             num_heads=H, kv_num_heads=Hkv)
+    o_b = pa.paged_attention(mk(two.q[cut:]), mk(two.k[cut:]), mk(two.v[cut:]), two.kc, two.vc,
+                             to_dev(np.array([0, 150 - cut], np.int32)), two.past + cut,
+                             two.table, num_heads=H, kv_num_heads=Hkv)
+    torch.cuda.synchronize()
+    assert torch.equal(one.kc.view(torch.int16), two.kc.view(torch.int16))
+    assert torch.equal(one.vc.view(torch.int16), two.vc.view(torch.int16))
+    diff = (torch.cat([o_a, o_b]).float() - o_full.float()).abs().max().item()
+    assert diff <= 2 * TOL
+
+
+def test_unsupported_example_shape_is_typed_error():
+    # README example call: H=2, Hkv=1, D=2, block_size 2 -> typed PA_ERR_UNSUPPORTED
+    q = torch.zeros(2, 4, dtype=torch.float16, device=DEV)
+    k = torch.zeros(2, 2, dtype=torch.float16, device=DEV)
+    kc = torch.zeros(3, 2, 1, 2, dtype=torch.float16, device=DEV)
+    with pytest.raises(pa.PagedAttentionError) as ei:
+        pa.paged_attention(q, k, k.clone(), kc, kc.clone(), to_dev(np.array([0, 2], np.int32)),
+                           to_dev(np.array([1], np.int32)), to_dev(np.array([[0, 1, 2]], np.int32)),
+                           num_heads=2, kv_num_heads=1)
+    assert ei.value.status == 3
+
+
+def test_hip_graph_replay_matches_eager():
+    b = W.mixed(2)
+    d = DevBatch(b)
+    ref = d.run().clone()
+    torch.cuda.synchronize()
+    ws = torch.empty(1 << 28, dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        d.run(output=out, workspace=ws, stream=s)  # warm-up on the capture stream
+        s.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            d.run(output=out, workspace=ws, stream=s)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))

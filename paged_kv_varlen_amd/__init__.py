@@ -101,8 +101,17 @@ def library() -> ctypes.CDLL:
     return _LIB
 
 
+_EMPTY_ADDR = 256  # aligned stand-in for a present but empty tensor; never dereferenced
+
+
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
-    return None if t is None else t.data_ptr()
+    """Device address of a tensor; None (NULL) only for an absent input.
+    torch gives empty tensors address 0, which the ABI would read as
+    "absent" (e.g. key/value NULL = packed [Q|K|V]), so a present empty
+    tensor gets a non-NULL stand-in: with no elements nothing is read."""
+    if t is None:
+        return None
+    return t.data_ptr() if t.data_ptr() != 0 or t.numel() > 0 else _EMPTY_ADDR
 
 
 def _dtype_code(t: torch.Tensor) -> int:

@@ -19,7 +19,7 @@ namespace {
 
 constexpr int kDecodeSplitKeys = 512;  // positions per decode split (multiple of 64)
 constexpr int kDecodeWavesPerCu = 8;   // decode workgroups resident per CU (grid sizing)
-constexpr int kPrefillWgPerCu = 2;     // prefill workgroups resident per CU (grid sizing)
+constexpr int kPrefillWgPerCu = 1;     // prefill workgroups resident per CU (LDS-limited)
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -76,6 +76,8 @@ WorkspaceLayout layout(const Resolved& r) {
   size_t off = 0;
   w.ctrl = off;
   off = align256(off + kCtrlSlots * sizeof(int32_t));
+  w.zeros = off;
+  off = align256(off + 256);
   w.dec_items = off;
   off = align256(off + w.max_dec_items * sizeof(int2));
   w.seq_split = off;
@@ -232,6 +234,7 @@ pa_status pa_paged_attention(const pa_args* a, void* stream) {
   sp.block_table = a->block_table;
   sp.slot_mapping = a->slot_mapping;
   sp.ws_ctrl = reinterpret_cast<int32_t*>(ws + w.ctrl);
+  sp.zeros = reinterpret_cast<int32_t*>(ws + w.zeros);
   sp.dec_items = reinterpret_cast<int2*>(ws + w.dec_items);
   sp.seq_split = reinterpret_cast<int2*>(ws + w.seq_split);
   sp.pf_items = reinterpret_cast<int2*>(ws + w.pf_items);
@@ -255,6 +258,7 @@ pa_status pa_paged_attention(const pa_args* a, void* stream) {
   ap.past = sp.past;
   ap.block_table = sp.block_table;
   ap.out = static_cast<uint16_t*>(a->output);
+  ap.zeros = reinterpret_cast<const uint16_t*>(ws + w.zeros);
   ap.ws_ctrl = sp.ws_ctrl;
   ap.seq_split = sp.seq_split;
   ap.part_o = reinterpret_cast<float*>(ws + w.part_o);

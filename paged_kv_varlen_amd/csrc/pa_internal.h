@@ -25,9 +25,9 @@ namespace pa {
 // ---- tiling constants -----------------------------------------------------
 constexpr int kDecodeThreads = 256;   // 4 waves per decode workgroup
 constexpr int kDecodeTile = 16;       // keys per wave per decode iteration
-constexpr int kPrefillThreads = 256;  // 4 waves per prefill workgroup
+constexpr int kPrefillThreads = 512;  // 8 waves per prefill workgroup
 constexpr int kPrefillRows = 128;     // (position, head) rows per prefill workgroup
-constexpr int kPrefillKeys = 64;      // keys per prefill LDS tile
+constexpr int kPrefillKeys = 64;      // keys per kv group per prefill super-tile
 constexpr int kPlanThreads = 1024;    // threads of the planning workgroup
 
 // ---- control block at the start of the workspace ---------------------------
@@ -36,12 +36,22 @@ enum CtrlSlot {
   kCtrlPrefillNext = 1,  // prefill queue head (atomic)
   kCtrlDecodeItems = 2,  // number of (sequence, split) decode items
   kCtrlPrefillItems = 3, // number of (sequence, tile) prefill items
+  kCtrlPrefillQueue0 = 8,  // heads of the (up to 8) prefill queues, slots 8..15
   kCtrlSlots = 64
 };
+
+// Prefill queues: queue q serves kv heads q, q+Q, ... so that workgroups of
+// one XCD (workgroup id mod 8) share the K/V of few heads in their L2.
+__host__ __device__ inline int prefill_queue_count(int kv_heads) {
+  if (kv_heads % 8 == 0) return 8;
+  if (8 % kv_heads == 0) return kv_heads;
+  return 1;
+}
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct WorkspaceLayout {
   size_t ctrl;         // int32[kCtrlSlots]
+  size_t zeros;        // 256 zero bytes, read in place of keys past a history
   size_t dec_items;    // int2[max_dec_items]   (sequence, split)
   size_t seq_split;    // int2[batch]           (first partial slot, #splits)
   size_t pf_items;     // int2[max_pf_items]    (sequence, tile)
@@ -64,6 +74,7 @@ struct ScatterPlanParams {
   const int32_t* block_table;
   const int32_t* slot_mapping; // may be null
   int32_t* ws_ctrl;
+  int32_t* zeros;              // 64 ints cleared by the plan
   int2* dec_items;
   int2* seq_split;
   int2* pf_items;
@@ -85,6 +96,7 @@ struct AttnParams {
   const int32_t* past;
   const int32_t* block_table;
   uint16_t* out;               // [N, H*D]
+  const uint16_t* zeros;       // 256 zero bytes
   int32_t* ws_ctrl;
   const int2* items;           // dec_items or pf_items
   const int2* seq_split;
@@ -106,6 +118,7 @@ hipError_t launch_scatter_plan(const ScatterPlanParams& p, hipStream_t s);
 hipError_t launch_decode(const AttnParams& p, int head_size, int grid, hipStream_t s);
 hipError_t launch_merge(const AttnParams& p, int head_size, hipStream_t s);
 hipError_t launch_prefill(const AttnParams& p, int head_size, int grid, hipStream_t s);
+size_t prefill_lds_bytes(int head_size);
 
 // Heads handled together by one decode work item (a divisor of group <= 8).
 int decode_heads_per_item(int group);

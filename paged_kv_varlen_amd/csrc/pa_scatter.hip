@@ -70,9 +70,11 @@ __device__ void plan(const ScatterPlanParams& p) {
     dec_base += tot_d;
     pf_base += tot_p;
   }
+  if (tid < 64) p.zeros[tid] = 0;
   if (tid == 0) {
     p.ws_ctrl[kCtrlDecodeNext] = 0;
     p.ws_ctrl[kCtrlPrefillNext] = 0;
+    for (int q = 0; q < 8; ++q) p.ws_ctrl[kCtrlPrefillQueue0 + q] = 0;
     p.ws_ctrl[kCtrlDecodeItems] = dec_base;
     p.ws_ctrl[kCtrlPrefillItems] = pf_base;
   }

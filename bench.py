@@ -221,6 +221,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (for scaling HBM counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -235,6 +237,17 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch
+        # calibrate the counters used for the kernels' HBM traffic
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "dispatches": args.steps}), flush=True)
+        return
     pa.library()  # fail loudly if the HIP library is missing
 
     b, work, ms, wall_ms, kms = time_workload(args.workload, args.steps, args.warmup, args.seed,

@@ -17,8 +17,7 @@
 namespace pa {
 namespace {
 
-constexpr int kDecodeSplitKeys = 512;  // positions per decode split (multiple of 64)
-constexpr int kDecodeWavesPerCu = 8;   // decode workgroups resident per CU (grid sizing)
+constexpr int kDecodeWgPerCu = 2;      // decode workgroups (4 waves each) resident per CU
 constexpr int kPrefillWgPerCu = 1;     // prefill workgroups resident per CU (LDS-limited)
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -275,7 +274,7 @@ pa_status pa_paged_attention(const pa_args* a, void* stream) {
 
   const int cus = device_cus();
   const int64_t dec_work = w.max_dec_items * r.Hkv * (r.G / decode_heads_per_item(r.G));
-  const int dec_grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(dec_work, int64_t(cus) * kDecodeWavesPerCu)));
+  const int dec_grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>((dec_work + 3) / 4, int64_t(cus) * kDecodeWgPerCu)));
   ap.items = sp.dec_items;
   mark(PA_KERNEL_DECODE, 0);
   if (launch_decode(ap, r.D, dec_grid, s) != hipSuccess) return PA_ERR_HIP;

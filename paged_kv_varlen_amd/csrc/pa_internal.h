@@ -25,6 +25,7 @@ namespace pa {
 // ---- tiling constants -----------------------------------------------------
 constexpr int kDecodeThreads = 256;   // 4 waves per decode workgroup
 constexpr int kDecodeTile = 16;       // keys per wave per decode iteration
+constexpr int kDecodeSplitKeys = 256; // positions per decode split (work item of one wave)
 constexpr int kPrefillThreads = 512;  // 8 waves per prefill workgroup
 constexpr int kPrefillRows = 128;     // (position, head) rows per prefill workgroup
 constexpr int kPrefillKeys = 64;      // keys per kv group per prefill super-tile

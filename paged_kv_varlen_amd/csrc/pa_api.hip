@@ -17,7 +17,6 @@
 namespace pa {
 namespace {
 
-constexpr int kDecodeWgPerCu = 2;      // decode workgroups (4 waves each) resident per CU
 constexpr int kPrefillWgPerCu = 1;     // prefill workgroups resident per CU (LDS-limited)
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -50,6 +49,12 @@ pa_status resolve(const pa_args* a, Resolved* r) {
   if (D != 64 && D != 128) return PA_ERR_UNSUPPORTED;
   if (a->block_size % 16 != 0 || a->block_size > 4096) return PA_ERR_UNSUPPORTED;
   if (a->num_heads / a->kv_num_heads > 64) return PA_ERR_UNSUPPORTED;
+  {  // decode tile indices are 32-bit
+    const int64_t tiles = (static_cast<int64_t>(a->max_blocks_per_seq) * a->block_size + 15) / 16;
+    const int64_t units = static_cast<int64_t>(a->kv_num_heads) *
+                          decode_head_chunks(a->num_heads / a->kv_num_heads);
+    if (static_cast<int64_t>(a->batch_size) * tiles * units > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  }
   r->N = a->num_tokens;
   r->B = a->batch_size;
   r->H = a->num_heads;
@@ -65,28 +70,39 @@ pa_status resolve(const pa_args* a, Resolved* r) {
 
 int prefill_positions(int G) { return kPrefillRows / G; }
 
+int device_cus();
+
 WorkspaceLayout layout(const Resolved& r) {
   WorkspaceLayout w{};
   const int64_t live = std::min<int64_t>(r.B, r.N);  // sequences with >= 1 token
-  const int64_t splits = (static_cast<int64_t>(r.MB) * r.bs + kDecodeSplitKeys - 1) / kDecodeSplitKeys;
-  w.max_dec_items = live * splits;
   const int64_t P = prefill_positions(r.G);
   w.max_pf_items = (r.N + P - 1) / P + live;
+  // decode waves: the resident count, fewer when the history can hold only a
+  // few tiles per wave
+  const int hs = decode_head_slots(r.G);
+  const int64_t units = static_cast<int64_t>(r.Hkv) * decode_head_chunks(r.G);
+  const int64_t max_tiles = std::min<int64_t>(r.B, r.N) * units *
+                            ((static_cast<int64_t>(r.MB) * r.bs + kDecodeTile - 1) / kDecodeTile);
+  const int64_t resident = static_cast<int64_t>(device_cus()) * decode_wg_per_cu(r.D, hs);
+  w.decode_grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(resident, (max_tiles + 31) / 32)));
+  w.decode_waves = w.decode_grid * kDecodeWaves;
+  const size_t W = static_cast<size_t>(w.decode_waves);
   size_t off = 0;
   w.ctrl = off;
   off = align256(off + kCtrlSlots * sizeof(int32_t));
   w.zeros = off;
   off = align256(off + 256);
-  w.dec_items = off;
-  off = align256(off + w.max_dec_items * sizeof(int2));
-  w.seq_split = off;
-  off = align256(off + static_cast<size_t>(r.B) * sizeof(int2));
+  w.dec_seq = off;
+  off = align256(off + (static_cast<size_t>(r.B) + 1) * sizeof(int4));
+  w.dec_start = off;
+  off = align256(off + (W + 1) * 8 * sizeof(int32_t));
+
   w.pf_items = off;
   off = align256(off + w.max_pf_items * sizeof(int2));
   w.part_lse = off;
-  off = align256(off + static_cast<size_t>(w.max_dec_items) * r.H * sizeof(float));
+  off = align256(off + 2 * W * kDecodeUnitHeads * sizeof(float));
   w.part_o = off;
-  off = align256(off + static_cast<size_t>(w.max_dec_items) * r.H * r.D * sizeof(float));
+  off = align256(off + 2 * W * kDecodeUnitHeads * r.D * sizeof(float));
   w.total = off;
   return w;
 }
@@ -234,15 +250,17 @@ pa_status pa_paged_attention(const pa_args* a, void* stream) {
   sp.slot_mapping = a->slot_mapping;
   sp.ws_ctrl = reinterpret_cast<int32_t*>(ws + w.ctrl);
   sp.zeros = reinterpret_cast<int32_t*>(ws + w.zeros);
-  sp.dec_items = reinterpret_cast<int2*>(ws + w.dec_items);
-  sp.seq_split = reinterpret_cast<int2*>(ws + w.seq_split);
+  sp.dec_seq = reinterpret_cast<int4*>(ws + w.dec_seq);
+  sp.dec_start = reinterpret_cast<int32_t*>(ws + w.dec_start);
+
   sp.pf_items = reinterpret_cast<int2*>(ws + w.pf_items);
   sp.num_tokens = r.N;
   sp.batch = r.B;
   sp.max_blocks = r.MB;
   sp.block_size = r.bs;
   sp.row_elems = r.Hkv * r.D;
-  sp.split_keys = kDecodeSplitKeys;
+  sp.decode_units = r.Hkv * decode_head_chunks(r.G);
+  sp.decode_waves = w.decode_waves;
   sp.prefill_positions = prefill_positions(r.G);
   mark(PA_KERNEL_SCATTER_PLAN, 0);
   if (launch_scatter_plan(sp, s) != hipSuccess) return PA_ERR_HIP;
@@ -259,7 +277,9 @@ pa_status pa_paged_attention(const pa_args* a, void* stream) {
   ap.out = static_cast<uint16_t*>(a->output);
   ap.zeros = reinterpret_cast<const uint16_t*>(ws + w.zeros);
   ap.ws_ctrl = sp.ws_ctrl;
-  ap.seq_split = sp.seq_split;
+  ap.dec_seq = sp.dec_seq;
+  ap.dec_start = sp.dec_start;
+
   ap.part_o = reinterpret_cast<float*>(ws + w.part_o);
   ap.part_lse = reinterpret_cast<float*>(ws + w.part_lse);
   ap.batch = r.B;
@@ -268,19 +288,16 @@ pa_status pa_paged_attention(const pa_args* a, void* stream) {
   ap.group = r.G;
   ap.max_blocks = r.MB;
   ap.block_size = r.bs;
-  ap.split_keys = kDecodeSplitKeys;
+  ap.decode_units = sp.decode_units;
+  ap.decode_waves = w.decode_waves;
   ap.prefill_positions = prefill_positions(r.G);
   ap.scale_log2 = r.scale * 1.4426950408889634f;
 
   const int cus = device_cus();
-  const int64_t dec_work = w.max_dec_items * r.Hkv * (r.G / decode_heads_per_item(r.G));
-  const int dec_grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>((dec_work + 3) / 4, int64_t(cus) * kDecodeWgPerCu)));
-  ap.items = sp.dec_items;
   mark(PA_KERNEL_DECODE, 0);
-  if (launch_decode(ap, r.D, dec_grid, s) != hipSuccess) return PA_ERR_HIP;
+  if (launch_decode(ap, r.D, decode_head_slots(r.G), w.decode_grid, s) != hipSuccess) return PA_ERR_HIP;
   mark(PA_KERNEL_DECODE, 1);
-  mark(PA_KERNEL_MERGE, 0);
-  if (launch_merge(ap, r.D, s) != hipSuccess) return PA_ERR_HIP;
+  mark(PA_KERNEL_MERGE, 0);  // the merge of cut decode segments opens the prefill launch
   mark(PA_KERNEL_MERGE, 1);
 
   const int64_t pf_work = w.max_pf_items * r.Hkv;

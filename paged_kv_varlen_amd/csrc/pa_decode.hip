@@ -1,491 +1,589 @@
-// Split-KV paged decode attention and the fixed-order merge of its splits.
+// Decode attention: sequences with one new token, on gfx950 matrix cores.
 //
-// Decode rows are sequences with exactly one new token.  Their history is cut
-// into splits of split_keys positions; one work item is (sequence, split,
-// kv head, head chunk) and covers GH query heads of one GQA group, so each
-// key/value byte is read once for all of them.  Inside a workgroup the four
-// waves take interleaved 16-key tiles of the split and keep their own
-// online-softmax state; the waves' states are combined in wave order and the
-// split's (out, lse) state is either written as the final fp16 row (one
-// split) or stored as fp32 partials for merge_kernel.
+// Operation (model-card README "com.microsoft.PagedAttention", Inputs and
+// Outputs; "WS2 CP-Aware Attention Contract", Mode-Specific Metadata): the
+// new token of sequence b sits at position L-1 = past[b] and attends to the
+// L cached positions 0..L-1, read through block_table after this call's cache
+// writes.  Query head h reads kv head h / G.
 //
-// Partial states and their merge follow "WS2 CP-Aware Attention Contract",
-// Reduction Semantics: partial state (out, lse), online-softmax merge by lse,
-// fp32 accumulation, fixed order of increasing key position, one downcast at
-// the final write.  Here lse is kept in base 2 of the scaled scores
-// (lse2 = lse / ln 2), which is the same merge.
+// Work split.  A unit is one kv head with up to 16 of its query heads; a
+// segment is (decode sequence, unit) and has ceil(L / 16) tiles of 16 keys.
+// Segments are laid end to end and wave w of W streams the tiles
+// [floor(w T / W), floor((w + 1) T / W)), so every wave moves the same number
+// of K/V bytes whatever the length mix.  A segment that is whole in one wave
+// is written as fp16 directly.  A cut segment leaves one normalised partial
+// (o, lse) per piece in the wave's two partial slots; the next launch merges
+// them in wave order (pa_merge.h).
 //
-// Per 16-key tile a wave
-//   * loads K in "QK layout": 8 lanes per key, each lane 16-byte pieces
-//     r, r+8 of the key row (contiguous 128-byte runs per instruction), and V
-//     in "PV layout": D/8 lanes per key, one 16-byte piece each;
-//   * forms q.k with v_dot2 (fp16 pairs, fp32 accumulate) and sums the 8
-//     lanes of a key with DPP;
-//   * takes the tile max across lanes, rescales its running sums only when
-//     the max grew by more than 2^8 (exact: out = acc/l uses one reference);
-//   * hands the probabilities to the PV layout through a per-wave LDS slot
-//     and accumulates p*v in fp32 with mixed-precision FMAs.
-// The next tile's K/V registers are loaded before the current tile is used.
-#include "pa_internal.h"
-
+// Stream.  Each wave runs a ring of R LDS slots filled with direct
+// global->LDS loads (global_load_lds_dwordx4: lane i's 16 bytes land at
+// M0 + 16 i), up to R-1 tiles ahead of the tile it computes, across segment
+// boundaries.  A slot holds the K and V tile (16 keys x D, row-major with
+// XOR-swizzled 16-byte chunks) and, for the first tile of a piece, the
+// query block of the unit.  The page ids of the sequence (64 block-table
+// entries at a time) and the next sequence's record are also fetched with
+// direct loads, one window ahead, so the issuing side never waits on a
+// register load.  Every wait on these loads is an explicit vmcnt whose count
+// comes from the number of loads issued since (loads complete in order), and
+// every LDS read is an asm block that ends with its own lgkmcnt wait, so the
+// compiler never has to guess (and over-wait) on the direct loads.
+//
+// Per tile (all heads of the unit at once):
+//   S^T[key][head] = K Q^T      4 x v_mfma_f32_16x16x32_f16 (D = 128)
+//   online softmax in base 2, fp32, lazy rescale (only when the running max
+//   grows by more than 2^8), P rounded to fp16
+//   O^T[d][head] += V^T P^T     8 x v_mfma_f32_16x16x16_f16
+// P^T is the S^T accumulator itself (lane = head + 16 * key group); the V^T
+// operand comes from the transposing LDS read ds_read_b64_tr_b16.
 #include <utility>
+
+#include "pa_internal.h"
 
 namespace pa {
 
 namespace {
 
-typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-
-constexpr float kNegInf = -__builtin_huge_valf();
-
-template <int CTRL>
-__device__ inline float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
-}
-constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
-constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
-constexpr int kDppHalfMirror = 0x141;
-constexpr int kDppRowRor8 = 0x128;
-
-__device__ inline float dot8(const uint4& a, const uint4& b, float acc) {
-  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a.x), __builtin_bit_cast(h2_t, b.x), acc, false);
-  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a.y), __builtin_bit_cast(h2_t, b.y), acc, false);
-  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a.z), __builtin_bit_cast(h2_t, b.z), acc, false);
-  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a.w), __builtin_bit_cast(h2_t, b.w), acc, false);
-  return acc;
-}
-
-__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ inline void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-__device__ inline float half_lo(uint32_t w) {
-  return static_cast<float>(__builtin_bit_cast(h2_t, w).x);
-}
-__device__ inline float half_hi(uint32_t w) {
-  return static_cast<float>(__builtin_bit_cast(h2_t, w).y);
-}
-
-__device__ inline uint16_t to_half_bits(float x) {
-  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
-}
-
-template <int D, int GH>
-struct DecodeShape {
-  static constexpr int R = 8;                  // lanes per key (QK)
-  static constexpr int CH = D / (8 * R);       // 16-byte pieces per lane (QK)
-  static constexpr int C = D / 8;              // lanes per key (PV)
-  static constexpr int KPV = 64 / C;           // keys per PV pass
-  static constexpr int PVP = kDecodeTile / KPV;  // PV passes per tile
-  static_assert(CH >= 1 && PVP >= 1, "unsupported head size");
-};
-
-// x combined with lane x^16 / x^32 (VALU lane swaps, no LDS round trip)
-__device__ inline float max_xor16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ inline float max_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define PA_LDS __attribute__((address_space(3)))
 #define PA_GLOBAL __attribute__((address_space(1)))
 
-template <typename F, int... I>
-__device__ inline void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ inline void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 __device__ inline uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
       reinterpret_cast<const PA_LDS char*>(reinterpret_cast<uintptr_t>(p))));
 }
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-// 16-byte LDS read of a buffer filled by direct global->LDS loads.  Written as
-// asm so that the compiler adds no wait on those loads of its own (the caller
-// waits on them explicitly); the value may only be used after lds_ready().
-template <int OFF>
-__device__ inline u32x4 lds_read16(uint32_t addr) {
+
+// x combined with lane x^16 / x^32 (VALU lane swaps)
+__device__ inline float swap16(float x, bool want_max) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return want_max ? fmaxf(a, b) : a + b;
+}
+__device__ inline float swap32(float x, bool want_max) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return want_max ? fmaxf(a, b) : a + b;
+}
+
+// Direct global->LDS load: each lane moves BYTES bytes; they land at
+// lds + BYTES * lane.  `lds` must be wave-uniform.
+template <int BYTES>
+__device__ inline void dma(const void* src, uint32_t lds) {
+  if constexpr (BYTES == 16)
+    __builtin_amdgcn_global_load_lds((PA_GLOBAL void*)src, (PA_LDS void*)(uintptr_t)lds, 16, 0, 0);
+  else
+    __builtin_amdgcn_global_load_lds((PA_GLOBAL void*)src, (PA_LDS void*)(uintptr_t)lds, 4, 0, 0);
+}
+
+// Wait until at most `younger` vector-memory operations are outstanding, i.e.
+// every operation issued before the last `younger` ones has completed (they
+// complete in order).  Rounded down to the nearest count below, so it may wait
+// a little longer than needed, never shorter.
+__device__ inline void wait_vm(int younger) {
+  if (younger >= 48) asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
+  else if (younger >= 32) asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+  else if (younger >= 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+  else if (younger >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if (younger >= 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  else if (younger >= 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if (younger >= 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  else if (younger >= 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else if (younger >= 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  else if (younger >= 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// LDS reads that return only once the data is in the registers.
+__device__ inline u32x4 lds_read_b128(uint32_t a) {
   u32x4 v;
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF) : "memory");
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
   return v;
 }
-// Waits for the LDS reads above; tying the value to the wait keeps every use
-// after it.
-__device__ inline uint4 lds_ready(u32x4 v) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v)::"memory");
-  return make_uint4(v.x, v.y, v.z, v.w);
+__device__ inline uint32_t lds_read_b32(uint32_t a) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+  return v;
+}
+__device__ inline void lds_write_b128(uint32_t a, u32x4 v) {
+  asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(v) : "memory");
 }
 
+template <typename F, int... I>
+__device__ __attribute__((always_inline)) inline void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __attribute__((always_inline)) inline void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// The tile's MFMA operands: KS 16-byte K reads and DB transposing V reads at
+// fixed per-lane addresses plus the slot's offset, issued back to back and
+// waited for once.
 template <int D>
-struct DecodeTileShape {
-  static constexpr int CH = D / 64;        // QK pieces per lane per key
-  static constexpr int KLOADS = 2 * CH;    // 1 KB direct loads of K per tile
-  static constexpr int VLOADS = D / 32;    // 1 KB direct loads of V per tile (PVP)
-  static constexpr int LOADS = KLOADS + VLOADS;
-  static constexpr int BYTES = LOADS * 1024;
+struct TileRegs;
+template <>
+struct TileRegs<128> {
+  u32x4 k[4];
+  u32x2 v[8];
+  template <int OFF>
+  __device__ void read(const uint32_t (&ka)[4], const uint32_t (&va)[8]) {
+    asm volatile(
+        "ds_read_b128 %0, %12 offset:%24\n\t"
+        "ds_read_b128 %1, %13 offset:%24\n\t"
+        "ds_read_b128 %2, %14 offset:%24\n\t"
+        "ds_read_b128 %3, %15 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %4, %16 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %5, %17 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %6, %18 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %7, %19 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %8, %20 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %9, %21 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %10, %22 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %11, %23 offset:%24\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]),
+          "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]),
+          "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7]), "n"(OFF)
+        : "memory");
+  }
+};
+template <>
+struct TileRegs<64> {
+  u32x4 k[2];
+  u32x2 v[4];
+  template <int OFF>
+  __device__ void read(const uint32_t (&ka)[2], const uint32_t (&va)[4]) {
+    asm volatile(
+        "ds_read_b128 %0, %6 offset:%12\n\t"
+        "ds_read_b128 %1, %7 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %5, %11 offset:%12\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(ka[0]), "v"(ka[1]), "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "n"(OFF)
+        : "memory");
+  }
 };
 
-// One work item per wave: (sequence, split of kDecodeSplitKeys positions, kv
-// head, head chunk).  Waves are independent (no barriers) and take items in
-// grid-stride order (split items are near-uniform in cost; a shared queue
-// counter would serialise every wave on one device-scope atomic).  A wave
-// streams its item's 16-key tiles through a ring of two LDS buffers filled by
-// direct global->LDS loads (global_load_lds_dwordx4), one tile ahead: in-flight
-// bytes cost no registers, and the lane mapping of each 1 KB load is the
-// compute layout itself, so lane i reads back its own 16 bytes at 16 i.  The
-// next item's page ids and query rows are fetched while the current item is
-// finished.
-template <int D, int GH>
-__global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(AttnParams p) {
-  using S = DecodeShape<D, GH>;
-  using TS = DecodeTileShape<D>;
-  constexpr int CH = S::CH, C = S::C, KPV = S::KPV, PVP = S::PVP;
-  constexpr int NW = kDecodeThreads / 64;
+// Query operand reads (once per piece).
+template <int KS, int OFF>
+__device__ inline void read_q(u32x4 (&q)[KS], const uint32_t (&qa)[KS]) {
+  if constexpr (KS == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %4 offset:%8\n\tds_read_b128 %1, %5 offset:%8\n\t"
+        "ds_read_b128 %2, %6 offset:%8\n\tds_read_b128 %3, %7 offset:%8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3])
+        : "v"(qa[0]), "v"(qa[1]), "v"(qa[2]), "v"(qa[3]), "n"(OFF)
+        : "memory");
+  } else {
+    asm volatile("ds_read_b128 %0, %2 offset:%4\n\tds_read_b128 %1, %3 offset:%4\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(q[0]), "=&v"(q[1])
+                 : "v"(qa[0]), "v"(qa[1]), "n"(OFF)
+                 : "memory");
+  }
+}
 
-  __shared__ float lds_p[NW][kDecodeTile][GH];
-  // the ring: two separate objects so that reading one never waits for a
-  // fill of the other
-  __shared__ __align__(16) char ring0[NW][TS::BYTES];
-  __shared__ __align__(16) char ring1[NW][TS::BYTES];
+// XOR swizzle (in 16-byte chunks) of key row k (0..15) of a tile: chosen so
+// that the 16-byte K reads (16 keys, one chunk) and the transposing V reads
+// (4 keys x 2 chunks per 16 lanes) touch distinct LDS banks.
+template <int D>
+__device__ inline int swz(int k) {
+  if constexpr (D == 128) {
+    return ((k & 7) << 1) | ((k >> 3) & 1);
+  } else {
+    const int x = (k >> 1) & 7;
+    return ((x & 3) << 1) | (x >> 2);
+  }
+}
+
+// per-tile flags handed from the issuing side to the computing side
+constexpr int kFirst = 1 << 8;     // first tile of a piece
+constexpr int kLast = 1 << 9;      // last tile of a piece
+constexpr int kComplete = 1 << 10; // the piece is the whole segment
+constexpr int kSecond = 1 << 11;   // partial goes to the wave's second slot
+
+template <int D, int HS>
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnParams p) {
+  constexpr int ROW = 2 * D;                      // bytes of one key of one kv head
+  constexpr int CPR = ROW / 16;                   // 16-byte chunks per row
+  constexpr int KPI = 1024 / ROW;                 // rows per 1 KB direct load
+  constexpr int NK = kDecodeTile / KPI;           // direct loads per tensor per tile
+  constexpr int TB = kDecodeTile * ROW;           // bytes per tensor per tile
+  constexpr int QB = decode_q_bytes(D, HS);
+  constexpr int NQ = QB / 1024;                   // direct loads of a query block
+  constexpr int SLOT = decode_slot_bytes(D, HS);
+  constexpr int R = decode_ring(D, HS);
+  constexpr int KS = D / 32;                      // QK MFMA steps
+  constexpr int DB = D / 16;                      // PV MFMA blocks (16 dims each)
+  static_assert(SLOT == 2 * TB + QB, "slot layout");
+  static_assert(R >= 2, "ring");
+
+  __shared__ __align__(1024) char ring[kDecodeWaves][R][SLOT];
+  __shared__ __align__(16) int meta[kDecodeWaves][2][64];  // [0] next window, [1] next sequence
+  // a piece's (token, first head, heads), handed over with its first tile
+  __shared__ __align__(16) int piece[kDecodeWaves][R][4];
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kk = lane >> 3, r = lane & 7;  // QK layout
-  const int a = lane / C, c = lane % C;    // PV layout
+  const int wave = uniform(threadIdx.x >> 6);
+  const int W = p.decode_waves;
+  const int w = static_cast<int>(blockIdx.x) * kDecodeWaves + wave;
+  if (w >= W) return;
 
-  const int hc_count = p.group / GH;
-  const int per_item = p.kv_heads * hc_count;
-  const int total = p.ws_ctrl[kCtrlDecodeItems] * per_item;
-  const int64_t kv_row = static_cast<int64_t>(p.kv_heads) * D;
-  // element offsets of this lane's pieces inside one tile (relative to key 0)
-  int koffs[2][CH], voffs[PVP];
-#pragma unroll
-  for (int pp = 0; pp < 2; ++pp)
-#pragma unroll
-    for (int ci = 0; ci < CH; ++ci)
-      koffs[pp][ci] = (8 * pp + kk) * static_cast<int>(kv_row) + (r + 8 * ci) * 8;
-#pragma unroll
-  for (int tt = 0; tt < PVP; ++tt) voffs[tt] = (KPV * tt + a) * static_cast<int>(kv_row) + c * 8;
+  // ---- this wave's share ---------------------------------------------------
+  const int* rec = p.dec_start + 8 * w;
+  const int rv = rec[lane & 7];
+  const int g1 = p.dec_start[8 * (w + 1) + 3];
+  const int g0 = uniform(__builtin_amdgcn_readlane(rv, 3));
+  if (g0 >= g1) return;
+  const int Bd = p.ws_ctrl[kCtrlDecodeSeqs];
+  const int U = p.decode_units;
+  const int hcc = decode_head_chunks(p.group);
+  const int G = p.group;
+  const int bs = p.block_size;
+  const int tpp = bs / kDecodeTile;  // tiles per page
+  const int MB = p.max_blocks;
+  const int kv_row = p.kv_heads * D;                      // elements per cache slot
+  const int64_t page_elems = static_cast<int64_t>(bs) * kv_row;
+  const int tile_elems = kDecodeTile * kv_row;
 
-  const int nwaves = static_cast<int>(gridDim.x) * NW;
-  struct ItemInfo {
-    int b, split, kvh, hc, t, j_begin, j_end, ntiles, h0;
-  };
-  auto describe = [&](int item) {
-    ItemInfo it;
-    const int2 bsplit = p.items[item / per_item];
-    const int rem = item % per_item;
-    it.kvh = rem / hc_count;
-    it.hc = rem % hc_count;
-    it.b = bsplit.x;
-    it.split = bsplit.y;
-    it.t = p.cum[it.b];
-    const int L = p.past[it.b] + 1;
-    it.j_begin = it.split * kDecodeSplitKeys;
-    it.j_end = min(L, it.j_begin + kDecodeSplitKeys);
-    it.ntiles = (it.j_end - it.j_begin + kDecodeTile - 1) / kDecodeTile;
-    it.h0 = it.kvh * p.group + it.hc * GH;
-    return it;
-  };
-  // page ids of all tiles of an item (a tile lies inside one page): lane i
-  // holds tile i's page
-  auto pages_of = [&](const ItemInfo& it) {
-    const int32_t* btab = p.block_table + static_cast<int64_t>(it.b) * p.max_blocks;
-    return lane < it.ntiles ? btab[(it.j_begin + kDecodeTile * lane) / p.block_size] : 0;
-  };
-  auto q_of = [&](const ItemInfo& it, uint4 (&q)[GH][CH]) {
-    const uint16_t* qrow = p.q + static_cast<int64_t>(it.t) * p.q_stride + static_cast<int64_t>(it.h0) * D;
+  // ---- per-lane constant offsets ---------------------------------------------
+  // tile loads: byte offset of lane's 16 bytes (key, logical chunk) for direct load j
+  uint32_t src_off[NK];
 #pragma unroll
-    for (int g = 0; g < GH; ++g)
+  for (int j = 0; j < NK; ++j) {
+    const int kj = j * KPI + lane / CPR;
+    const int c = (lane % CPR) ^ swz<D>(kj);
+    src_off[j] = static_cast<uint32_t>(kj * kv_row + 8 * c) * 2u;
+  }
+  const int qchunk = (lane % CPR) * 8;
+  // MFMA operand addresses of ring slot 0 (slot s adds s * SLOT)
+  const int n = lane & 15, g = lane >> 4;
+  const uint32_t ring0 = uniform(static_cast<int>(lds_addr(&ring[wave][0][0])));
+  uint32_t ka[KS], va[DB], qa[KS];
 #pragma unroll
-      for (int i = 0; i < CH; ++i)
-        q[g][i] = *reinterpret_cast<const uint4*>(qrow + g * D + (r + 8 * i) * 8);
-  };
+  for (int s = 0; s < KS; ++s) {
+    ka[s] = ring0 + n * ROW + 16 * ((4 * s + g) ^ swz<D>(n));
+    qa[s] = ring0 + 2 * TB + (n < QB / ROW ? n : 0) * ROW + 16 * (4 * s + g);
+  }
+  {
+    const int kv = 4 * g + (n >> 2), cc = n & 3;
+#pragma unroll
+    for (int blk = 0; blk < DB; ++blk)
+      va[blk] = ring0 + TB + kv * ROW + 16 * ((2 * blk + (cc >> 1)) ^ swz<D>(kv)) + 8 * (cc & 1);
+  }
+  const uint32_t meta_w = lds_addr(&meta[wave][0][0]);
+  const uint32_t piece0 = uniform(static_cast<int>(lds_addr(&piece[wave][0][0])));
 
-  int item = static_cast<int>(blockIdx.x) * NW + wave;
-  if (item >= total) return;
-  ItemInfo nx = describe(item);
-  int page_nx = pages_of(nx);
-  uint4 qr[GH][CH];
-  q_of(nx, qr);
-  for (; item < total; item += nwaves) {
-    const ItemInfo it = nx;
-    const int my_page = page_nx;
-    const bool has_next = item + nwaves < total;
-    if (has_next) {  // the next item's metadata and page ids
-      nx = describe(item + nwaves);
-      page_nx = pages_of(nx);
+  const uint32_t meta_s = lds_addr(&meta[wave][1][0]);
+
+  int opc = 0;  // direct loads issued so far by this wave
+
+  // ---- issuing side: cursor over (sequence d, unit u, tile i) ---------------
+  int d_i = uniform(__builtin_amdgcn_readlane(rv, 0));
+  int u_i = uniform(__builtin_amdgcn_readlane(rv, 1));
+  int i_i = uniform(__builtin_amdgcn_readlane(rv, 2));
+  int b_i = uniform(__builtin_amdgcn_readlane(rv, 4));
+  int t_i = uniform(__builtin_amdgcn_readlane(rv, 5));
+  int L_i = uniform(__builtin_amdgcn_readlane(rv, 6));
+  int P_i = uniform(__builtin_amdgcn_readlane(rv, 7));
+  int n_i = (L_i + kDecodeTile - 1) / kDecodeTile;
+  int kvh_i = u_i / hcc, hc_i = u_i % hcc;
+  int pi = i_i / tpp, ip = i_i % tpp;  // page of the tile and tile within the page
+  int g_i = g0;
+  // per-segment values
+  int h0_i = 0, nh_i = 0, segfl = 0, seg0_i = 0;
+  const uint16_t* kp = nullptr;  // K and V of the next tile to issue (this kv head)
+  const uint16_t* vp = nullptr;
+
+  // next sequence record (direct load into meta_s)
+  int ns_opc = 0, ns_b = 0, ns_t = 0, ns_L = 0, ns_P = 0;
+  bool ns_have = false;
+  auto issue_nseq = [&](int d) __attribute__((always_inline)) {
+    const int* src = reinterpret_cast<const int*>(p.dec_seq + min(d, Bd)) + (lane & 3);
+    dma<4>(src, meta_s);
+    ns_opc = ++opc;
+    ns_have = false;
+  };
+  auto ensure_nseq = [&]() __attribute__((always_inline)) {
+    if (!ns_have) {
+      wait_vm(opc - ns_opc);
+      const u32x4 v = lds_read_b128(meta_s);
+      ns_b = uniform(static_cast<int>(v.x));
+      ns_t = uniform(static_cast<int>(v.y));
+      ns_L = uniform(static_cast<int>(v.z));
+      ns_P = uniform(static_cast<int>(v.w));
+      ns_have = true;
     }
-    const int b = it.b, split = it.split, kvh = it.kvh, t = it.t;
-    const int j_begin = it.j_begin, j_end = it.j_end, ntiles = it.ntiles, h0 = it.h0;
+  };
 
-    float m[GH], l[GH], acc[GH][8];
-#pragma unroll
-    for (int g = 0; g < GH; ++g) {
-      m[g] = kNegInf;
-      l[g] = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+  // block-table window: lane j holds the page id of page wp0 + j of sequence wd
+  int wcur = 0, wd = -1, wp0 = 0;
+  bool nw_valid = false;
+  int nw_opc = 0, nw_d = 0, nw_p0 = 0;
+  auto issue_window = [&](int d, int b, int p0) __attribute__((always_inline)) {
+    const int idx = min(p0 + lane, MB - 1);
+    dma<4>(p.block_table + static_cast<int64_t>(b) * MB + idx, meta_w);
+    nw_opc = ++opc;
+    nw_d = d;
+    nw_p0 = p0;
+    nw_valid = true;
+  };
+  // prefetch the next window the cursor will need after the current one
+  auto plan_window = [&]() __attribute__((always_inline)) {
+    if (nw_valid) return;
+    const int np = (L_i + bs - 1) / bs;
+    if (wd == d_i && wp0 + kDecodeWindow < np) {
+      issue_window(d_i, b_i, wp0 + kDecodeWindow);
+    } else if (u_i + 1 < U) {
+      if (wd != d_i || wp0 != 0) issue_window(d_i, b_i, 0);
+    } else if (d_i + 1 < Bd) {
+      ensure_nseq();
+      issue_window(d_i + 1, ns_b, 0);
     }
+  };
+  // make the window hold page pi of the cursor's sequence
+  auto need_window = [&]() __attribute__((always_inline)) {
+    if (!(wd == d_i && pi >= wp0 && pi < wp0 + kDecodeWindow)) {
+      if (!(nw_valid && nw_d == d_i && nw_p0 == pi)) issue_window(d_i, b_i, pi);
+      wait_vm(opc - nw_opc);
+      wcur = static_cast<int>(lds_read_b32(meta_w + 4 * lane));
+      wd = d_i;
+      wp0 = nw_p0;
+      nw_valid = false;
+    }
+    plan_window();
+  };
+  auto set_pointers = [&]() __attribute__((always_inline)) {
+    const int page = uniform(__builtin_amdgcn_readlane(wcur, pi - wp0));
+    const int64_t base = static_cast<int64_t>(page) * page_elems + ip * tile_elems + kvh_i * D;
+    kp = p.key_cache + base;
+    vp = p.value_cache + base;
+  };
+  auto enter_segment = [&]() __attribute__((always_inline)) {
+    h0_i = kvh_i * G + kDecodeUnitHeads * hc_i;
+    nh_i = min(kDecodeUnitHeads, G - kDecodeUnitHeads * hc_i);
+    seg0_i = P_i + u_i * n_i;
+    segfl = (seg0_i >= g0 && seg0_i + n_i <= g1 ? kComplete : 0) | (seg0_i > g0 ? kSecond : 0);
+    need_window();
+    set_pointers();
+  };
 
-    const uint16_t* kc = p.key_cache + static_cast<int64_t>(kvh) * D;
-    const uint16_t* vc = p.value_cache + static_cast<int64_t>(kvh) * D;
-    // direct fill of one ring buffer with tile i (clamped to the last tile so
-    // that every path issues the same loads; a repeated tile is an L2 hit)
-    auto issue = [&](int i, char* buf) {
-      const int j0 = j_begin + kDecodeTile * i;
-      const int pb = __builtin_amdgcn_readlane(my_page, i);
-      const int64_t base = (static_cast<int64_t>(pb) * p.block_size + j0 % p.block_size) * kv_row;
-      const uint16_t* kt = kc + base;
-      const uint16_t* vt = vc + base;
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp)
-#pragma unroll
-        for (int ci = 0; ci < CH; ++ci)
-          __builtin_amdgcn_global_load_lds((PA_GLOBAL void*)(kt + koffs[pp][ci]),
-                                           (PA_LDS void*)(buf + 1024 * (pp * CH + ci)), 16, 0, 0);
-#pragma unroll
-      for (int tt = 0; tt < PVP; ++tt)
-        __builtin_amdgcn_global_load_lds((PA_GLOBAL void*)(vt + voffs[tt]),
-                                         (PA_LDS void*)(buf + 1024 * (TS::KLOADS + tt)), 16, 0, 0);
-    };
+  issue_nseq(d_i + 1);
+  issue_window(d_i, b_i, pi);
+  enter_segment();
 
-    auto compute = [&](int i, const char* buf) {
-      const int nvalid = j_end - (j_begin + kDecodeTile * i);
-      // the tile's bytes: lane reads back its own 16 bytes of each 1 KB load
-      u32x4 kx[2 * CH], vx[PVP];
-      const uint32_t at = lds_addr(buf) + 16 * lane;
-      static_for<2 * CH>([&](auto n) { kx[n] = lds_read16<1024 * n>(at); });
-      static_for<PVP>([&](auto n) { vx[n] = lds_read16<1024 * (TS::KLOADS + n)>(at); });
-      uint4 kr[2][CH], vr[PVP];
+  // per-slot hand-over (static indices only: these stay in scalar registers);
+  // a piece's (token, first head, heads) goes through LDS with its first tile
+  int m_opc[R], m_fl[R];
+
+  auto issue = [&](auto slot_c) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot_c)::value;
+    const uint32_t sb = ring0 + S * SLOT;
 #pragma unroll
-      for (int n = 0; n < 2 * CH; ++n) kr[n / CH][n % CH] = lds_ready(kx[n]);
+    for (int j = 0; j < NK; ++j) dma<16>(reinterpret_cast<const char*>(kp) + src_off[j], sb + 1024 * j);
 #pragma unroll
-      for (int n = 0; n < PVP; ++n) vr[n] = lds_ready(vx[n]);
-      // scores of this lane's two keys (8*pp + kk), all GH heads
-      float s[2][GH];
+    for (int j = 0; j < NK; ++j) dma<16>(reinterpret_cast<const char*>(vp) + src_off[j], sb + TB + 1024 * j);
+    opc += 2 * NK;
+    const bool first = g_i == g0 || i_i == 0;
+    if (first) {  // the unit's query heads (absent heads read zeros)
+      const uint16_t* qtok = p.q + static_cast<int64_t>(t_i) * p.q_stride + static_cast<int64_t>(h0_i) * D;
 #pragma unroll
-      for (int pp = 0; pp < 2; ++pp)
-#pragma unroll
-        for (int g = 0; g < GH; ++g) {
-          float x = 0.f;
-#pragma unroll
-          for (int ci = 0; ci < CH; ++ci) x = dot8(qr[g][ci], kr[pp][ci], x);
-          x += dpp<kDppQuadXor1>(x);
-          x += dpp<kDppQuadXor2>(x);
-          x += dpp<kDppHalfMirror>(x);
-          s[pp][g] = (8 * pp + kk < nvalid) ? x * p.scale_log2 : kNegInf;
-        }
-      // tile max per head (made wave-uniform) and lazy rescale
-#pragma unroll
-      for (int g = 0; g < GH; ++g) {
-        float mx = fmaxf(s[0][g], s[1][g]);
-        mx = fmaxf(mx, dpp<kDppRowRor8>(mx));
-        mx = max_xor32(max_xor16(mx));
-        mx = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mx)));
-        if (mx > m[g] + 8.f) {
-          const float alpha = fast_exp2(m[g] - mx);
-          l[g] *= alpha;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[g][e] *= alpha;
-          m[g] = mx;
-        }
+      for (int j = 0; j < NQ; ++j) {
+        const int hh = j * KPI + lane / CPR;
+        dma<16>(hh < nh_i ? qtok + hh * D + qchunk : p.zeros + qchunk, sb + 2 * TB + 1024 * j);
       }
-      // probabilities; lane r==0 of each key publishes them for the PV layout
-      if (r == 0) {
+      opc += NQ;
+      lds_write_b128(piece0 + 16 * S, u32x4{static_cast<uint32_t>(t_i), static_cast<uint32_t>(h0_i),
+                                          static_cast<uint32_t>(nh_i), 0u});
+    }
+    const bool last = i_i == n_i - 1 || g_i == g1 - 1;
+    m_opc[S] = opc;
+    m_fl[S] = min(kDecodeTile, L_i - kDecodeTile * i_i) | (first ? kFirst : 0) | (last ? kLast : 0) | segfl;
+    // advance the cursor
+    ++g_i;
+    if (++i_i == n_i) {
+      if (g_i < g1) {  // next segment
+        i_i = 0;
+        pi = 0;
+        ip = 0;
+        ++u_i;
+        if (++hc_i == hcc) {
+          hc_i = 0;
+          ++kvh_i;
+        }
+        if (u_i == U) {
+          u_i = 0;
+          kvh_i = 0;
+          ++d_i;
+          ensure_nseq();
+          b_i = ns_b;
+          t_i = ns_t;
+          L_i = ns_L;
+          P_i = ns_P;
+          n_i = (L_i + kDecodeTile - 1) / kDecodeTile;
+          issue_nseq(d_i + 1);
+        }
+        enter_segment();
+      }
+    } else if (++ip == tpp) {  // next page
+      ip = 0;
+      ++pi;
+      if (pi == wp0 + kDecodeWindow) need_window();
+      set_pointers();
+    } else {
+      kp += tile_elems;
+      vp += tile_elems;
+    }
+  };
+
+  // ---- computing side ---------------------------------------------------------
+  f32x4_t acc[DB];
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp)
+  for (int blk = 0; blk < DB; ++blk) acc[blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = kNegInf, l = 0.f;
+  u32x4 qv[KS];
+  int nh_c = 0, h0_c = 0, t_c = 0;
+  const half2_t one2 = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+
+  auto compute = [&](auto slot_c) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot_c)::value;
+    wait_vm(opc - m_opc[S]);  // this tile's loads (and everything before) landed
+    const int fl = m_fl[S];
+    const int nvalid = fl & 0xff;
+    if (fl & kFirst) {  // first tile of a piece: query operand, fresh running state
+      const u32x4 pc = lds_read_b128(piece0 + 16 * S);
+      t_c = uniform(static_cast<int>(pc.x));
+      h0_c = uniform(static_cast<int>(pc.y));
+      nh_c = uniform(static_cast<int>(pc.z));
+      read_q<KS, S * SLOT>(qv, qa);
+      if (n >= nh_c) {
 #pragma unroll
-          for (int g = 0; g < GH; ++g) {
-            const float pr = fast_exp2(s[pp][g] - m[g]);
-            l[g] += pr;
-            lds_p[wave][8 * pp + kk][g] = pr;
+        for (int s = 0; s < KS; ++s) qv[s] = u32x4{0u, 0u, 0u, 0u};
+      }
+      // acc is rescaled by exp2(-inf) = 0 below, as every lane's max grows
+      m = kNegInf;
+      l = 0.f;
+    }
+    TileRegs<D> tr;
+    tr.template read<S * SLOT>(ka, va);
+    // S^T: lane = head n + 16 * key group g, element e = key 4 g + e
+    f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      st = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, tr.k[s]),
+                                                  __builtin_bit_cast(half8_t, qv[s]), st, 0, 0, 0);
+    float sc[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sc[e] = st[e] * p.scale_log2;
+    if (nvalid < kDecodeTile) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * g + e >= nvalid) sc[e] = kNegInf;
+    }
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mx = swap32(swap16(mx, true), true);  // over the 16 keys of head n
+    const bool grow = mx > m + 8.f;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float alpha = grow ? fast_exp2(m - mx) : 1.f;
+      l *= alpha;
+#pragma unroll
+      for (int blk = 0; blk < DB; ++blk) acc[blk] *= alpha;
+      m = grow ? mx : m;
+    }
+    half4_t pb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pb[e] = static_cast<_Float16>(fast_exp2(sc[e] - m));
+    // row sum of exactly the fp16 weights the MFMA multiplies
+    l = __builtin_amdgcn_fdot2(half2_t{pb[0], pb[1]}, one2, l, false);
+    l = __builtin_amdgcn_fdot2(half2_t{pb[2], pb[3]}, one2, l, false);
+    if (nvalid < kDecodeTile) {
+      // keys past the history may hold any bits (NaN included): zero their values
+      const int k0 = 4 * g;
+      const uint32_t lo = (k0 < nvalid ? 0xffffu : 0u) | (k0 + 1 < nvalid ? 0xffff0000u : 0u);
+      const uint32_t hi = (k0 + 2 < nvalid ? 0xffffu : 0u) | (k0 + 3 < nvalid ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int blk = 0; blk < DB; ++blk) {
+        tr.v[blk].x &= lo;
+        tr.v[blk].y &= hi;
+      }
+    }
+#pragma unroll
+    for (int blk = 0; blk < DB; ++blk)
+      acc[blk] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, tr.v[blk]), pb, acc[blk],
+                                                       0, 0, 0);
+    if (fl & kLast) {  // last tile of the piece: normalise and write
+      const float lt = swap32(swap16(l, false), false);
+      const float inv = 1.f / lt;
+      if (fl & kComplete) {  // whole segment here: the final fp16 output
+        if (n < nh_c) {
+          uint16_t* o = p.out + (static_cast<int64_t>(t_c) * p.num_heads + h0_c + n) * D + 4 * g;
+#pragma unroll
+          for (int blk = 0; blk < DB; ++blk) {
+            half4_t hv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hv[e] = static_cast<_Float16>(acc[blk][e] * inv);
+            *reinterpret_cast<half4_t*>(o + 16 * blk) = hv;
           }
-      }
-      wave_lds_sync();
-      // keys beyond the history may hold any bits: zero their values
-      if (nvalid < kDecodeTile) {
-#pragma unroll
-        for (int tt = 0; tt < PVP; ++tt)
-          if (KPV * tt + a >= nvalid) vr[tt] = make_uint4(0u, 0u, 0u, 0u);
-      }
-#pragma unroll
-      for (int tt = 0; tt < PVP; ++tt) {
-        float pv[GH];
-#pragma unroll
-        for (int g = 0; g < GH; ++g) pv[g] = lds_p[wave][KPV * tt + a][g];
-        const uint32_t w[4] = {vr[tt].x, vr[tt].y, vr[tt].z, vr[tt].w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float v0 = half_lo(w[q]), v1 = half_hi(w[q]);
-#pragma unroll
-          for (int g = 0; g < GH; ++g) {
-            acc[g][2 * q] = fmaf(pv[g], v0, acc[g][2 * q]);
-            acc[g][2 * q + 1] = fmaf(pv[g], v1, acc[g][2 * q + 1]);
-          }
         }
-      }
-      wave_lds_sync();
-    };
-
-    char* buf0 = ring0[wave];
-    char* buf1 = ring1[wave];
-    const int last = ntiles - 1;
-    issue(0, buf0);
-    for (int i = 0; i < ntiles; i += 2) {
-      issue(min(i + 1, last), buf1);
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(TS::LOADS) : "memory");  // tile i landed
-      compute(i, buf0);
-      issue(min(i + 2, last), buf0);
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(TS::LOADS) : "memory");  // tile i+1 landed
-      if (i + 1 < ntiles) compute(i + 1, buf1);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no fill in flight past the item
-
-    if (has_next) q_of(nx, qr);  // lands while this item is reduced and written
-
-    // wave totals: l over all lanes, acc over the KPV key groups of a piece
+      } else if (n < nh_c) {  // a piece: partial (o, lse) in the wave's slot
+        const int ps = 2 * w + ((fl & kSecond) ? 1 : 0);
+        float* po = p.part_o + (static_cast<int64_t>(ps) * kDecodeUnitHeads + n) * D + 4 * g;
 #pragma unroll
-    for (int g = 0; g < GH; ++g) {
-      float x = l[g];
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
-      l[g] = x;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float y = acc[g][e];
-#pragma unroll
-        for (int off = C; off < 64; off <<= 1) y += __shfl_xor(y, off);
-        acc[g][e] = y;
+        for (int blk = 0; blk < DB; ++blk) *reinterpret_cast<f32x4_t*>(po + 16 * blk) = acc[blk] * inv;
+        if (g == 0) p.part_lse[ps * kDecodeUnitHeads + n] = m + __log2f(lt);
       }
     }
-    if (a == 0) {  // lanes 0..C-1 hold head-dim piece c of every head
-      const int2 ss = p.seq_split[b];
-#pragma unroll
-      for (int g = 0; g < GH; ++g) {
-        const int h = h0 + g;
-        const float inv = 1.f / l[g];
-        if (ss.y == 1) {
-          uint32_t w[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            w[q] = static_cast<uint32_t>(to_half_bits(acc[g][2 * q] * inv)) |
-                   (static_cast<uint32_t>(to_half_bits(acc[g][2 * q + 1] * inv)) << 16);
-          *reinterpret_cast<uint4*>(p.out + static_cast<int64_t>(t) * p.num_heads * D +
-                                    static_cast<int64_t>(h) * D + c * 8) = make_uint4(w[0], w[1], w[2], w[3]);
-        } else {
-          const int64_t slot = static_cast<int64_t>(ss.x + split) * p.num_heads + h;
-          float4* po = reinterpret_cast<float4*>(p.part_o + slot * D + c * 8);
-          po[0] = make_float4(acc[g][0] * inv, acc[g][1] * inv, acc[g][2] * inv, acc[g][3] * inv);
-          po[1] = make_float4(acc[g][4] * inv, acc[g][5] * inv, acc[g][6] * inv, acc[g][7] * inv);
-          if (c == 0) p.part_lse[slot] = m[g] + __log2f(l[g]);
-        }
+  };
+
+  // ---- the stream: tile k lives in slot k % R, issued R-1 tiles ahead --------
+  const int count = g1 - g0;
+  static_for<R - 1>([&](auto S) __attribute__((always_inline)) {
+    if (g_i < g1) issue(S);
+  });
+  for (int k = 0; k < count; k += R) {
+    static_for<R>([&](auto S) __attribute__((always_inline)) {
+      constexpr int s = decltype(S)::value;
+      if (k + s < count) {
+        if (g_i < g1) issue(std::integral_constant<int, (s + R - 1) % R>{});
+        compute(S);
       }
-    }
+    });
   }
-}
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-// Fixed-order merge of the split partials of one decode row, one wave per
-// (sequence, head): out = sum_s 2^{lse_s - M} o_s / sum_s 2^{lse_s - M}.
-// Lane s reads lse_s, the wave forms M and the weights, then every lane sums
-// its head-dim elements over s = 0, 1, ... in that order.
-template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
-  constexpr int E = D / 64;
-  const int b = blockIdx.x;
-  const int2 ss = p.seq_split[b];
-  if (ss.y <= 1) return;
-  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
-  if (h >= p.num_heads) return;
-  const int lane = threadIdx.x & 63;
-  const int n = ss.y;
-  float M = kNegInf;
-  for (int s0 = 0; s0 < n; s0 += 64) {
-    const int s = s0 + lane;
-    const float x = s < n ? p.part_lse[static_cast<int64_t>(ss.x + s) * p.num_heads + h] : kNegInf;
-    M = fmaxf(M, x);
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  float num[E], den = 0.f;
-#pragma unroll
-  for (int e = 0; e < E; ++e) num[e] = 0.f;
-  for (int s0 = 0; s0 < n; s0 += 64) {
-    const int cnt = min(64, n - s0);
-    const float lw = lane < cnt
-        ? fast_exp2(p.part_lse[static_cast<int64_t>(ss.x + s0 + lane) * p.num_heads + h] - M) : 0.f;
-    for (int k = 0; k < cnt; ++k) {
-      const float w = __shfl(lw, k);
-      const int64_t slot = static_cast<int64_t>(ss.x + s0 + k) * p.num_heads + h;
-      den += w;
-      if constexpr (E == 2) {
-        const float2 o = *reinterpret_cast<const float2*>(p.part_o + slot * D + lane * 2);
-        num[0] = fmaf(w, o.x, num[0]);
-        num[1] = fmaf(w, o.y, num[1]);
-      } else {
-        num[0] = fmaf(w, p.part_o[slot * D + lane], num[0]);
-      }
-    }
-  }
-  const int t = p.cum[b];
-  uint16_t* o = p.out + static_cast<int64_t>(t) * p.num_heads * D + static_cast<int64_t>(h) * D;
-#pragma unroll
-  for (int e = 0; e < E; ++e) o[lane * E + e] = to_half_bits(num[e] / den);
-}
-
-template <int D, int GH>
-hipError_t launch_decode_t(const AttnParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((decode_kernel<D, GH>), dim3(grid), dim3(kDecodeThreads), 0, s, p);
-  return hipGetLastError();
-}
-
-template <int D>
-hipError_t launch_decode_d(const AttnParams& p, int gh, int grid, hipStream_t s) {
-  switch (gh) {
-    case 1: return launch_decode_t<D, 1>(p, grid, s);
-    case 2: return launch_decode_t<D, 2>(p, grid, s);
-    case 3: return launch_decode_t<D, 3>(p, grid, s);
-    case 4: return launch_decode_t<D, 4>(p, grid, s);
-    case 5: return launch_decode_t<D, 5>(p, grid, s);
-    case 6: return launch_decode_t<D, 6>(p, grid, s);
-    case 7: return launch_decode_t<D, 7>(p, grid, s);
-    case 8: return launch_decode_t<D, 8>(p, grid, s);
-  }
-  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-int decode_heads_per_item(int group) {
-  for (int gh = 8; gh > 1; --gh)
-    if (group % gh == 0) return gh;
-  return 1;
-}
-
-hipError_t launch_decode(const AttnParams& p, int head_size, int grid, hipStream_t s) {
-  const int gh = decode_heads_per_item(p.group);
-  if (head_size == 128) return launch_decode_d<128>(p, gh, grid, s);
-  if (head_size == 64) return launch_decode_d<64>(p, gh, grid, s);
+hipError_t launch_decode(const AttnParams& p, int head_size, int head_slots, int grid, hipStream_t s) {
+#define PA_DECODE(DD, HH)                                                         \
+  if (head_size == DD && head_slots == HH) {                                      \
+    hipLaunchKernelGGL((decode_kernel<DD, HH>), dim3(grid), dim3(kDecodeThreads), 0, s, p); \
+    return hipGetLastError();                                                     \
+  }
+  PA_DECODE(128, 4)
+  PA_DECODE(128, 8)
+  PA_DECODE(128, 16)
+  PA_DECODE(64, 4)
+  PA_DECODE(64, 8)
+  PA_DECODE(64, 16)
+#undef PA_DECODE
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_merge(const AttnParams& p, int head_size, hipStream_t s) {
-  const dim3 grid(p.batch, (p.num_heads + 3) / 4);
-  if (head_size == 128) hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(256), 0, s, p);
-  else if (head_size == 64) hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(256), 0, s, p);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
 }
 
 }  // namespace pa

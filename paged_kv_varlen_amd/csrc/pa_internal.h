@@ -4,17 +4,20 @@
 // stream, with no host synchronisation:
 //   1. scatter_plan_kernel  - writes the step's K/V rows into the caches
 //                             (one workgroup per token) and, in its last
-//                             workgroup, builds the device work lists for the
-//                             two attention kernels from cum/past.
-//   2. decode_kernel        - split-KV attention for single-token sequences,
-//                             persistent workgroups pulling (sequence, split,
-//                             kv-head) items from a device queue.
-//   3. merge_kernel         - fixed-order (out, lse) merge of the splits.
-//   4. prefill_kernel       - MFMA causal attention for multi-token
+//                             workgroup, builds the device work plan from
+//                             cum/past: the decode sequences with their tile
+//                             offsets, each decode wave's start, the prefill
+//                             items.
+//   2. decode_kernel        - single-token sequences: every wave streams an
+//                             equal share of the 16-key tiles of all
+//                             (sequence, kv head) segments.
+//   3. prefill_kernel       - first merges (fixed order) the decode segments
+//                             that a wave boundary cut in pieces, then runs
+//                             MFMA causal attention for multi-token
 //                             sequences, persistent workgroups pulling
 //                             (sequence, query tile, kv-head) items.
-// Grid sizes come from static shapes only; each persistent workgroup reads
-// the real item counts from the workspace and leaves when the queue is empty.
+// Grid sizes come from static shapes only; the kernels read the real amount
+// of work from the plan.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -23,9 +26,11 @@
 namespace pa {
 
 // ---- tiling constants -----------------------------------------------------
-constexpr int kDecodeThreads = 256;   // 4 waves per decode workgroup
-constexpr int kDecodeTile = 16;       // keys per wave per decode iteration
-constexpr int kDecodeSplitKeys = 256; // positions per decode split (work item of one wave)
+constexpr int kDecodeWaves = 4;       // waves per decode workgroup
+constexpr int kDecodeThreads = 64 * kDecodeWaves;
+constexpr int kDecodeTile = 16;       // keys per decode tile
+constexpr int kDecodeUnitHeads = 16;  // query heads of one decode segment (MFMA N)
+constexpr int kDecodeWindow = 64;     // block-table entries a wave holds (one per lane)
 constexpr int kPrefillThreads = 512;  // 8 waves per prefill workgroup
 constexpr int kPrefillRows = 128;     // (position, head) rows per prefill workgroup
 constexpr int kPrefillKeys = 64;      // keys per kv group per prefill super-tile
@@ -33,9 +38,9 @@ constexpr int kPlanThreads = 1024;    // threads of the planning workgroup
 
 // ---- control block at the start of the workspace ---------------------------
 enum CtrlSlot {
-  kCtrlDecodeNext = 0,   // decode queue head (atomic)
+  kCtrlDecodeTiles = 0,  // decode tiles of all segments (T)
   kCtrlPrefillNext = 1,  // prefill queue head (atomic)
-  kCtrlDecodeItems = 2,  // number of (sequence, split) decode items
+  kCtrlDecodeSeqs = 2,   // number of single-token (decode) sequences
   kCtrlPrefillItems = 3, // number of (sequence, tile) prefill items
   kCtrlPrefillQueue0 = 8,  // heads of the (up to 8) prefill queues, slots 8..15
   kCtrlSlots = 64
@@ -49,18 +54,58 @@ __host__ __device__ inline int prefill_queue_count(int kv_heads) {
   return 1;
 }
 
+// ---- decode geometry ----------------------------------------------------------
+// A decode "unit" is one kv head and up to 16 of its query heads; a segment
+// is (decode sequence, unit) and has ceil(L / 16) tiles.  Segments are laid
+// end to end (sequence-major) and wave w of W takes tiles
+// [floor(w T / W), floor((w + 1) T / W)).
+__host__ __device__ constexpr int decode_head_chunks(int group) { return (group + 15) / 16; }
+// query-head slots of a unit, rounded up to 4, 8 or 16
+__host__ __device__ constexpr int decode_head_slots(int group) {
+  return group >= 16 ? 16 : group > 4 ? (group > 8 ? 16 : 8) : 4;
+}
+// LDS per ring slot: K tile, V tile (16 keys each) and the query block
+__host__ __device__ constexpr int decode_q_bytes(int D, int hslots) {
+  return hslots * 2 * D > 1024 ? hslots * 2 * D : 1024;
+}
+__host__ __device__ constexpr int decode_slot_bytes(int D, int hslots) {
+  return 2 * kDecodeTile * 2 * D + decode_q_bytes(D, hslots);
+}
+// ring depth: as many slots as fit four waves in about 150 KB, at most 4
+__host__ __device__ constexpr int decode_ring(int D, int hslots) {
+  return (150 * 1024) / (kDecodeWaves * decode_slot_bytes(D, hslots)) > 4
+             ? 4
+             : (150 * 1024) / (kDecodeWaves * decode_slot_bytes(D, hslots));
+}
+// per wave: the ring, a 16-byte piece record per slot, 512 bytes of
+// prefetched metadata
+__host__ __device__ constexpr int decode_lds_bytes(int D, int hslots) {
+  return kDecodeWaves * (decode_ring(D, hslots) * (decode_slot_bytes(D, hslots) + 16) + 512);
+}
+__host__ __device__ constexpr int decode_wg_per_cu(int D, int hslots) {
+  return (160 * 1024) / decode_lds_bytes(D, hslots) > 0 ? (160 * 1024) / decode_lds_bytes(D, hslots) : 1;
+}
+// the wave whose tile range holds global tile g (ranges as above)
+__host__ __device__ inline int decode_wave_of(int64_t g, int64_t T, int W) {
+  return static_cast<int>(((g + 1) * W - 1) / T);
+}
+__host__ __device__ inline int64_t decode_wave_begin(int w, int64_t T, int W) {
+  return static_cast<int64_t>(w) * T / W;
+}
+
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct WorkspaceLayout {
   size_t ctrl;         // int32[kCtrlSlots]
-  size_t zeros;        // 256 zero bytes, read in place of keys past a history
-  size_t dec_items;    // int2[max_dec_items]   (sequence, split)
-  size_t seq_split;    // int2[batch]           (first partial slot, #splits)
+  size_t zeros;        // 256 zero bytes, read in place of absent query heads
+  size_t dec_seq;      // int4[batch + 1]: (b, token, L, first tile); last = (.., .., .., T)
+  size_t dec_start;    // int32[8 * (waves + 1)]: per wave (d, unit, tile, g, b, token, L, first tile)
   size_t pf_items;     // int2[max_pf_items]    (sequence, tile)
-  size_t part_lse;     // float[max_dec_items * H]
-  size_t part_o;       // float[max_dec_items * H * D]
+  size_t part_lse;     // float[2 * waves * 16]
+  size_t part_o;       // float[2 * waves * 16 * D]
   size_t total;
-  int64_t max_dec_items;
   int64_t max_pf_items;
+  int decode_waves;    // W
+  int decode_grid;     // workgroups of the decode launch
 };
 
 // ---- kernel parameter blocks ------------------------------------------------
@@ -76,15 +121,16 @@ struct ScatterPlanParams {
   const int32_t* slot_mapping; // may be null
   int32_t* ws_ctrl;
   int32_t* zeros;              // 64 ints cleared by the plan
-  int2* dec_items;
-  int2* seq_split;
+  int4* dec_seq;
+  int32_t* dec_start;
   int2* pf_items;
   int64_t num_tokens;
   int32_t batch;
   int32_t max_blocks;
   int32_t block_size;
   int32_t row_elems;           // Hkv * D
-  int32_t split_keys;          // keys per decode split
+  int32_t decode_units;        // units per sequence (Hkv * head chunks)
+  int32_t decode_waves;        // W
   int32_t prefill_positions;   // query positions per prefill tile
 };
 
@@ -99,8 +145,9 @@ struct AttnParams {
   uint16_t* out;               // [N, H*D]
   const uint16_t* zeros;       // 256 zero bytes
   int32_t* ws_ctrl;
-  const int2* items;           // dec_items or pf_items
-  const int2* seq_split;
+  const int2* items;           // prefill items
+  const int4* dec_seq;
+  const int32_t* dec_start;
   float* part_o;
   float* part_lse;
   int32_t batch;
@@ -109,19 +156,16 @@ struct AttnParams {
   int32_t group;               // num_heads / kv_heads
   int32_t max_blocks;
   int32_t block_size;
-  int32_t split_keys;
+  int32_t decode_units;        // units per sequence
+  int32_t decode_waves;        // W
   int32_t prefill_positions;
   float scale_log2;            // scale * log2(e)
 };
 
 // ---- launchers (defined in the .hip files) ---------------------------------
 hipError_t launch_scatter_plan(const ScatterPlanParams& p, hipStream_t s);
-hipError_t launch_decode(const AttnParams& p, int head_size, int grid, hipStream_t s);
-hipError_t launch_merge(const AttnParams& p, int head_size, hipStream_t s);
+hipError_t launch_decode(const AttnParams& p, int head_size, int head_slots, int grid, hipStream_t s);
 hipError_t launch_prefill(const AttnParams& p, int head_size, int grid, hipStream_t s);
 size_t prefill_lds_bytes(int head_size);
-
-// Heads handled together by one decode work item (a divisor of group <= 8).
-int decode_heads_per_item(int group);
 
 }  // namespace pa

@@ -1,0 +1,86 @@
+// Fixed-order merge of decode segments that wave boundaries cut in pieces.
+//
+// "WS2 ReductionSpec" (CP-aware attention contract page): partial results
+// (o_i normalised, lse_i in base 2) of one query row are combined as
+// sum_i 2^(lse_i - M) o_i / sum_i 2^(lse_i - M), M = max_i lse_i, in fp32 and
+// in a fixed order (here: the order of the decode waves), with one rounding
+// to fp16 at the end.
+//
+// The decode kernel leaves the pieces of segment S..S+n-1 (tiles of one
+// sequence and unit) in the partial slots of waves wf..wl: the first piece in
+// wf's second slot when the segment starts inside wf's range, every other in
+// the wave's first slot; waves whose range is empty hold none.  It runs as a
+// prologue of the prefill kernel, the next launch on the stream, so every
+// partial is visible without any cross-workgroup synchronisation.
+#pragma once
+
+#include "pa_internal.h"
+
+namespace pa {
+
+// One segment (decode sequence d, unit u) per call, all 64 lanes: lane = query
+// head (lane & 15) + 16 * quarter of the head dimension.
+template <int D>
+__device__ inline void merge_segment(const AttnParams& p, int task, int T, int lane) {
+  const int U = p.decode_units;
+  const int d = task / U, u = task % U;
+  const int4 sq = p.dec_seq[d];  // (b, token, L, first tile)
+  const int n = (sq.z + kDecodeTile - 1) / kDecodeTile;
+  const int W = p.decode_waves;
+  const int S = sq.w + u * n;
+  const int wf = decode_wave_of(S, T, W), wl = decode_wave_of(S + n - 1, T, W);
+  if (wf == wl) return;  // written whole by its wave
+  const int first_k = decode_wave_begin(wf, T, W) < S ? 1 : 0;
+  const int hcc = decode_head_chunks(p.group);
+  const int kvh = u / hcc, hc = u % hcc;
+  const int nh = min(kDecodeUnitHeads, p.group - kDecodeUnitHeads * hc);
+  const int hn = lane & 15, qd = lane >> 4;
+  if (hn >= nh) return;
+  constexpr int E = D / 4;  // head-dim elements per lane
+  auto holds = [&](int v) {
+    return v == wf || decode_wave_begin(v, T, W) < decode_wave_begin(v + 1, T, W);
+  };
+  float M = -__builtin_huge_valf();
+  for (int v = wf; v <= wl; ++v) {
+    if (!holds(v)) continue;
+    const int ps = 2 * v + (v == wf ? first_k : 0);
+    M = fmaxf(M, p.part_lse[ps * kDecodeUnitHeads + hn]);
+  }
+  float o[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = 0.f;
+  float wsum = 0.f;
+  for (int v = wf; v <= wl; ++v) {
+    if (!holds(v)) continue;
+    const int ps = 2 * v + (v == wf ? first_k : 0);
+    const float wk = __builtin_amdgcn_exp2f(p.part_lse[ps * kDecodeUnitHeads + hn] - M);
+    const float4* po =
+        reinterpret_cast<const float4*>(p.part_o + (static_cast<int64_t>(ps) * kDecodeUnitHeads + hn) * D + E * qd);
+#pragma unroll
+    for (int e = 0; e < E / 4; ++e) {
+      const float4 x = po[e];
+      o[4 * e] = fmaf(wk, x.x, o[4 * e]);
+      o[4 * e + 1] = fmaf(wk, x.y, o[4 * e + 1]);
+      o[4 * e + 2] = fmaf(wk, x.z, o[4 * e + 2]);
+      o[4 * e + 3] = fmaf(wk, x.w, o[4 * e + 3]);
+    }
+    wsum += wk;
+  }
+  const float inv = 1.f / wsum;
+  const int h = kvh * p.group + kDecodeUnitHeads * hc + hn;
+  uint16_t* out = p.out + (static_cast<int64_t>(sq.y) * p.num_heads + h) * D + E * qd;
+#pragma unroll
+  for (int e = 0; e < E; e += 4) {
+    uint32_t w2[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const _Float16 lo = static_cast<_Float16>(o[e + 2 * c] * inv);
+      const _Float16 hi = static_cast<_Float16>(o[e + 2 * c + 1] * inv);
+      w2[c] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
+              (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+    }
+    *reinterpret_cast<uint2*>(out + e) = make_uint2(w2[0], w2[1]);
+  }
+}
+
+}  // namespace pa

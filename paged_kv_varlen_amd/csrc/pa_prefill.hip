@@ -42,6 +42,7 @@
 #include <type_traits>
 
 #include "pa_internal.h"
+#include "pa_merge.h"
 
 namespace pa {
 
@@ -115,6 +116,15 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
   const int64_t out_stride = static_cast<int64_t>(p.num_heads) * D;
   const float c = fabsf(p.scale_log2);
   const bool negate_q = p.scale_log2 < 0.f;  // fold the sign into Q (exact)
+
+  // decode segments cut by a wave boundary: one wave per segment
+  {
+    const int segments = p.ws_ctrl[kCtrlDecodeSeqs] * p.decode_units;
+    const int T = p.ws_ctrl[kCtrlDecodeTiles];
+    const int nw = static_cast<int>(gridDim.x) * (kPrefillThreads / 64);
+    for (int task = static_cast<int>(blockIdx.x) * (kPrefillThreads / 64) + wave; task < segments; task += nw)
+      merge_segment<D>(p, task, T, lane);
+  }
 
   const int nq = prefill_queue_count(p.kv_heads);
   const int hq = p.kv_heads / nq;

@@ -27,56 +27,96 @@ __device__ inline int find_sequence(const int32_t* cum, int batch, int64_t t) {
   return lo;
 }
 
-// Exclusive scan of one int per thread over a 256-thread block; returns the
-// exclusive prefix and writes the block total to *total.
-__device__ inline int block_exclusive_scan(int v, int* lds, int* total) {
+// Exclusive scan of three ints per thread over a 256-thread block (one pass);
+// returns the exclusive prefixes and writes the block totals to tot.
+__device__ inline int3 block_exclusive_scan3(int3 v, int3* lds, int3* tot) {
   const int tid = threadIdx.x;
   lds[tid] = v;
   __syncthreads();
   for (int off = 1; off < 256; off <<= 1) {
-    int add = tid >= off ? lds[tid - off] : 0;
+    const int3 add = tid >= off ? lds[tid - off] : make_int3(0, 0, 0);
     __syncthreads();
-    lds[tid] += add;
+    lds[tid].x += add.x;
+    lds[tid].y += add.y;
+    lds[tid].z += add.z;
     __syncthreads();
   }
-  int incl = lds[tid];
-  *total = lds[255];
+  const int3 incl = lds[tid];
+  *tot = lds[255];
   __syncthreads();
-  return incl - v;
+  return make_int3(incl.x - v.x, incl.y - v.y, incl.z - v.z);
 }
 
+constexpr int kPlanLdsSeqs = 8192;  // decode sequences whose first tile the plan keeps in LDS
+
+// The plan.  Decode sequences (one new token) get their index d and the tile
+// offset of their first segment; each decode wave gets the segment and tile
+// where its equal share of all tiles begins (a binary search over the
+// sequences' first tiles, in LDS).
+// Multi-token sequences get one prefill item per query tile, the last
+// (longest) tile first.
 __device__ void plan(const ScatterPlanParams& p) {
-  __shared__ int scan_lds[256];
+  __shared__ int3 scan_lds[256];
+  __shared__ int first_tile[kPlanLdsSeqs];
   const int tid = threadIdx.x;
-  int dec_base = 0, pf_base = 0;
+  const int U = p.decode_units;
+  int dec_base = 0, tile_base = 0, pf_base = 0;
   for (int start = 0; start < p.batch; start += 256) {
     const int b = start + tid;
-    int nd = 0, np = 0;
+    int nd = 0, nt = 0, np = 0, t0 = 0, L = 0;
     if (b < p.batch) {
-      const int q = p.cum[b + 1] - p.cum[b];
-      const int L = p.past[b] + q;
-      if (q == 1) nd = (L + p.split_keys - 1) / p.split_keys;
-      else if (q > 1) np = (q + p.prefill_positions - 1) / p.prefill_positions;
+      t0 = p.cum[b];
+      const int q = p.cum[b + 1] - t0;
+      L = p.past[b] + q;
+      if (q == 1) {
+        nd = 1;
+        nt = (L + kDecodeTile - 1) / kDecodeTile * U;
+      } else if (q > 1) {
+        np = (q + p.prefill_positions - 1) / p.prefill_positions;
+      }
     }
-    int tot_d, tot_p;
-    const int od = block_exclusive_scan(nd, scan_lds, &tot_d);
-    const int op = block_exclusive_scan(np, scan_lds, &tot_p);
-    if (b < p.batch) {
-      p.seq_split[b] = make_int2(dec_base + od, nd);
-      for (int s = 0; s < nd; ++s) p.dec_items[dec_base + od + s] = make_int2(b, s);
-      // last (longest) query tile of a sequence first
-      for (int t = 0; t < np; ++t) p.pf_items[pf_base + op + t] = make_int2(b, np - 1 - t);
+    int3 tot;
+    const int3 o = block_exclusive_scan3(make_int3(nd, nt, np), scan_lds, &tot);
+    if (nd != 0) {
+      const int d = dec_base + o.x;
+      p.dec_seq[d] = make_int4(b, t0, L, tile_base + o.y);
+      if (d < kPlanLdsSeqs) first_tile[d] = tile_base + o.y;
     }
-    dec_base += tot_d;
-    pf_base += tot_p;
+    for (int t = 0; t < np; ++t) p.pf_items[pf_base + o.z + t] = make_int2(b, np - 1 - t);
+    dec_base += tot.x;
+    tile_base += tot.y;
+    pf_base += tot.z;
   }
   if (tid < 64) p.zeros[tid] = 0;
   if (tid == 0) {
-    p.ws_ctrl[kCtrlDecodeNext] = 0;
+    p.dec_seq[dec_base] = make_int4(0, 0, 0, tile_base);  // sentinel: T
+    p.ws_ctrl[kCtrlDecodeTiles] = tile_base;
+    p.ws_ctrl[kCtrlDecodeSeqs] = dec_base;
     p.ws_ctrl[kCtrlPrefillNext] = 0;
     for (int q = 0; q < 8; ++q) p.ws_ctrl[kCtrlPrefillQueue0 + q] = 0;
-    p.ws_ctrl[kCtrlDecodeItems] = dec_base;
     p.ws_ctrl[kCtrlPrefillItems] = pf_base;
+  }
+  __syncthreads();  // first_tile and dec_seq are read back below
+  const int T = tile_base, W = p.decode_waves;
+  const bool in_lds = dec_base <= kPlanLdsSeqs;
+  for (int w = tid; w <= W; w += 256) {
+    int4 lo4 = make_int4(dec_base, 0, 0, T), hi4 = make_int4(0, 0, 0, 0);
+    if (w < W && T > 0) {
+      const int g = static_cast<int>(decode_wave_begin(w, T, W));
+      int lo = 0, hi = dec_base - 1;  // last d with first tile <= g
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        const int f = in_lds ? first_tile[mid] : p.dec_seq[mid].w;
+        if (f <= g) lo = mid; else hi = mid - 1;
+      }
+      const int4 sq = p.dec_seq[lo];
+      const int n = (sq.z + kDecodeTile - 1) / kDecodeTile;
+      const int off = g - sq.w;
+      lo4 = make_int4(lo, off / n, off % n, g);
+      hi4 = sq;
+    }
+    reinterpret_cast<int4*>(p.dec_start)[2 * w] = lo4;
+    reinterpret_cast<int4*>(p.dec_start)[2 * w + 1] = hi4;
   }
 }
 

@@ -149,9 +149,13 @@ typedef struct pa_args {
 /* Kernels launched by one call, in launch order (indices into kernel_events). */
 enum pa_kernel {
   PA_KERNEL_SCATTER_PLAN = 0,  /* cache writes + device work lists        */
-  PA_KERNEL_DECODE = 1,        /* split-KV attention of single-token rows */
-  PA_KERNEL_MERGE = 2,         /* fixed-order merge of decode splits      */
-  PA_KERNEL_PREFILL = 3,       /* MFMA attention of multi-token rows      */
+  PA_KERNEL_DECODE = 1,        /* balanced split-KV attention of single-token rows */
+  PA_KERNEL_MERGE = 2,         /* no launch of its own: its two events are
+                                  recorded back to back; the fixed-order
+                                  merge of cut decode segments opens the
+                                  prefill launch                          */
+  PA_KERNEL_PREFILL = 3,       /* decode merge, then MFMA attention of
+                                  multi-token rows                        */
   PA_KERNEL_COUNT = 4
 };
 
@@ -163,8 +167,10 @@ pa_status pa_paged_attention(const pa_args *args, void *stream);
 
 /* Bytes of device workspace pa_paged_attention needs for these shapes (an
  * upper bound from static sizes only: num_tokens, batch_size, num_heads,
- * head_size, block_size, max_blocks_per_seq).  Pure host function; returns 0
- * when the shape fields are invalid.  Pointer fields are ignored. */
+ * head_size, block_size, max_blocks_per_seq, and the compute-unit count of
+ * the current device, which sets the number of decode waves).  Host function
+ * (it may query the current device once); returns 0 when the shape fields
+ * are invalid.  Pointer fields are ignored. */
 size_t pa_workspace_bytes(const pa_args *args);
 
 /* Static, NUL-terminated description of a status code. */

@@ -68,15 +68,19 @@ pa_status resolve(const pa_args* a, Resolved* r) {
   return PA_OK;
 }
 
-int prefill_positions(int G) { return kPrefillRows / G; }
+// query positions per prefill half-tile: a workgroup's 128 rows are two
+// half-tiles of 64 (position, head) rows
+int prefill_positions(int G) { return (kPrefillRows / 2) / G; }
 
 int device_cus();
 
 WorkspaceLayout layout(const Resolved& r) {
   WorkspaceLayout w{};
   const int64_t live = std::min<int64_t>(r.B, r.N);  // sequences with >= 1 token
+  // a sequence of q tokens has ceil(ceil(q / P) / 2) half-tile pairs, at most
+  // q / (2P) + 1
   const int64_t P = prefill_positions(r.G);
-  w.max_pf_items = (r.N + P - 1) / P + live;
+  w.max_pf_items = (r.N + 2 * P - 1) / (2 * P) + live;
   // decode waves: the resident count, fewer when the history can hold only a
   // few tiles per wave
   const int hs = decode_head_slots(r.G);

@@ -15,7 +15,7 @@
 //                             that a wave boundary cut in pieces, then runs
 //                             MFMA causal attention for multi-token
 //                             sequences, persistent workgroups pulling
-//                             (sequence, query tile, kv-head) items.
+//                             (sequence, half-tile pair, kv-head) items.
 // Grid sizes come from static shapes only; the kernels read the real amount
 // of work from the plan.
 #pragma once
@@ -32,8 +32,8 @@ constexpr int kDecodeTile = 16;       // keys per decode tile
 constexpr int kDecodeUnitHeads = 16;  // query heads of one decode segment (MFMA N)
 constexpr int kDecodeWindow = 64;     // block-table entries a wave holds (one per lane)
 constexpr int kPrefillThreads = 512;  // 8 waves per prefill workgroup
-constexpr int kPrefillRows = 128;     // (position, head) rows per prefill workgroup
-constexpr int kPrefillKeys = 64;      // keys per kv group per prefill super-tile
+constexpr int kPrefillRows = 128;     // (position, head) rows per prefill workgroup (two half-tiles)
+constexpr int kPrefillKeys = 64;      // keys per prefill step (32 per kv group)
 constexpr int kPlanThreads = 1024;    // threads of the planning workgroup
 
 // ---- control block at the start of the workspace ---------------------------
@@ -41,7 +41,7 @@ enum CtrlSlot {
   kCtrlDecodeTiles = 0,  // decode tiles of all segments (T)
   kCtrlPrefillNext = 1,  // prefill queue head (atomic)
   kCtrlDecodeSeqs = 2,   // number of single-token (decode) sequences
-  kCtrlPrefillItems = 3, // number of (sequence, tile) prefill items
+  kCtrlPrefillItems = 3, // number of (sequence, half-tile pair) prefill items
   kCtrlPrefillQueue0 = 8,  // heads of the (up to 8) prefill queues, slots 8..15
   kCtrlSlots = 64
 };
@@ -99,7 +99,7 @@ struct WorkspaceLayout {
   size_t zeros;        // 256 zero bytes, read in place of absent query heads
   size_t dec_seq;      // int4[batch + 1]: (b, token, L, first tile); last = (.., .., .., T)
   size_t dec_start;    // int32[8 * (waves + 1)]: per wave (d, unit, tile, g, b, token, L, first tile)
-  size_t pf_items;     // int2[max_pf_items]    (sequence, tile)
+  size_t pf_items;     // int2[max_pf_items]    (sequence, half-tile pair)
   size_t part_lse;     // float[2 * waves * 16]
   size_t part_o;       // float[2 * waves * 16 * D]
   size_t total;
@@ -131,7 +131,7 @@ struct ScatterPlanParams {
   int32_t row_elems;           // Hkv * D
   int32_t decode_units;        // units per sequence (Hkv * head chunks)
   int32_t decode_waves;        // W
-  int32_t prefill_positions;   // query positions per prefill tile
+  int32_t prefill_positions;   // query positions per prefill half-tile
 };
 
 struct AttnParams {

@@ -1,29 +1,41 @@
 // Causal varlen (chunked) prefill attention on gfx950 matrix cores.
 //
-// Rows are sequences with more than one new token.  A work item is
-// (sequence, query tile, kv head): the workgroup owns kPrefillRows rows, each
-// a (new-token position, query head) pair of one GQA group, laid out
+// Rows are sequences with more than one new token.  A sequence's new tokens
+// are cut into half-tiles of P = 64 / G positions; a work item is (sequence,
+// half-tile pair t, kv head) and the workgroup owns 128 rows: rows 0..63 are
+// half-tile t, rows 64..127 half-tile nt-1-t (nt half-tiles in the sequence),
+// each row a (new-token position, query head) pair of one GQA group, laid out
 // position-major (row f = position f / G, head f % G), so every K/V byte
-// staged in LDS serves all G query heads of the group.
+// staged in LDS serves all G query heads of the group.  Under the causal mask
+// a late half-tile sees more keys than an early one, and the pair's total is
+// the same for every t, so all items cost about the same.
 //
-// Eight waves: wave w owns rows 32*(w%4) .. +31 ("row group") and the keys of
-// one half ("kv group" w/4) of every 128-key super-tile, so each SIMD runs two
-// waves while every wave keeps 32 rows of MFMA operands.  The two kv groups
-// keep separate online-softmax states and are merged once, in LDS, at the end
-// of the item (fixed order: group 0 then group 1).
+// Eight waves: a wave owns 32 rows (a "row group") and the keys of one half
+// ("kv group") of every 64-key step; the two kv groups keep separate
+// online-softmax states and are merged once, in LDS, at the end of the item
+// (fixed order: group 0 then group 1).  Waves w and w+4 share a SIMD, so they
+// get row groups of different halves: when the early half-tile has run out
+// of keys each SIMD still has one busy wave.
 //
-// Per 128-key super-tile (double-buffered LDS, one barrier per super-tile):
-//   * every wave fills 16 key rows of K and V with direct global->LDS loads
-//     (global_load_lds_dwordx4: lane i's 16 bytes land at M0 + 16 i), one
-//     super-tile ahead, through block_table (the page id is a scalar value
-//     fetched one super-tile earlier).  Keys past the history read a zeroed
-//     page of the workspace instead of the cache.  K and V rows stay
-//     row-major (2*D bytes); their 16-byte chunks are XOR-swizzled per row so
-//     that the reads below hit distinct LDS banks;
+// K/V staging: a ring of four LDS buffers, each holding the K and V rows of
+// one 64-key step.  Step j's rows are fetched during step j-3 with direct
+// global->LDS loads (global_load_lds_dwordx4: lane i's 16 bytes land at
+// M0 + 16 i), each wave fetching 8 rows of K and of V after its products of
+// the step, so that the load path (about 64 bytes per clock per CU) streams
+// while the matrix cores work on the next step.  A step ends with a wait for the loads of the next
+// step only (the two later steps stay in flight) and one barrier.  Page ids
+// come from a window of cache slots (one per 16 keys, from block_table) kept
+// in LDS.  Keys
+// past the history read a zeroed page of the workspace instead of the cache.
+// K and V rows stay row-major (2*D bytes); their 16-byte chunks are
+// XOR-swizzled per row so that the reads below hit distinct LDS banks.
+//
+// Per step and wave (32 keys x 32 rows):
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_f16 (fp16 in, fp32 accumulate): a
 //     lane holds 16 keys of one query row, so the row max needs a single
-//     exchange with lane^32;
-//   * keys after a row's position are masked only on tiles that cross the
+//     exchange with lane^32.  All K and V fragments of the step are read from
+//     LDS before the first product, so the step waits for one LDS round trip;
+//   * keys after a row's position are masked only on steps that cross the
 //     diagonal (bottom-right causal offset: new row i of sequence b is at
 //     past_b + i, "WS2 CP-Aware Attention Contract", Mode-Specific Metadata);
 //   * online softmax in fp32 on base-2 scores (running sums rescaled only
@@ -56,7 +68,13 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 #define PA_GLOBAL __attribute__((address_space(1)))
 
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int kSuper = 2 * kPrefillKeys;  // keys per super-tile (two kv groups)
+constexpr int kGroupKeys = kPrefillKeys / 2;  // keys per kv group per step
+constexpr int kRing = 4;                      // LDS buffers (steps in flight + 1)
+constexpr int kSlotWindow = 2048;             // 16-key cache slots held in LDS
+// steps per slot window: 4 slots per step, 3 steps fetched ahead, and a whole
+// number of ring turns
+constexpr int kChunk = (kSlotWindow / 4 - 3) / kRing * kRing;
+static_assert(4 * (kChunk + 3) <= kSlotWindow && kChunk % kRing == 0, "slot window");
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -71,15 +89,30 @@ __device__ inline float swap_halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt bits 3:0 and 15:14,
+// expcnt 6:4 left at its maximum, lgkmcnt 11:8)
+template <int N>
+__device__ inline void wait_fills() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+// workgroup barrier without the memory fence of __syncthreads() (which would
+// also wait for every fill in flight); the empty asm statements keep the
+// compiler from moving memory accesses across it
+__device__ inline void plain_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int D>
 struct PrefillShape {
   static constexpr int ROWB = D * 2;                 // bytes per key row
   static constexpr int CPR = D / 8;                  // 16-byte chunks per row
   static constexpr int ROWS_PER_LOAD = 64 / CPR;     // rows per 1 KB direct load
-  static constexpr int LOADS = 16 / ROWS_PER_LOAD;   // direct loads per wave per tensor
-  static constexpr int BUF = kSuper * ROWB;          // bytes per K (or V) buffer
-  static constexpr int K0 = 0;                       // K buffers at [0, 2 BUF)
-  static constexpr int V0 = 2 * BUF;                 // V buffers at [2 BUF, 4 BUF)
+  static constexpr int WAVE_ROWS = kPrefillKeys / 8; // rows of K (and V) each wave fetches
+  static constexpr int LOADS = WAVE_ROWS / ROWS_PER_LOAD;  // direct loads per wave per tensor
+  static constexpr int BUF = kPrefillKeys * ROWB;    // bytes per K (or V) buffer
   static constexpr int QK_STEPS = D / 16;            // MFMA k-steps over the head dim
   static constexpr int O_TILES = D / 32;             // 32-wide d tiles of O^T
   // chunk swizzles (in 16-byte chunks) of K and V rows
@@ -91,27 +124,36 @@ template <int D>
 __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) {
   using S = PrefillShape<D>;
   constexpr int ROWB = S::ROWB, CPR = S::CPR;
+  static_assert(S::LOADS >= 1, "loads per wave");
 
-  // four separate LDS objects (K/V x two buffers): the compiler can then see
-  // that a fill of one buffer never aliases reads of the other and does not
-  // make those reads wait for the fill
+  // one LDS object per ring buffer and tensor: the compiler can then see that
+  // a fill of one buffer never aliases reads of another and does not make
+  // those reads wait for the fill
   __shared__ __align__(16) char k_lds0[S::BUF];
   __shared__ __align__(16) char k_lds1[S::BUF];
+  __shared__ __align__(16) char k_lds2[S::BUF];
+  __shared__ __align__(16) char k_lds3[S::BUF];
   __shared__ __align__(16) char v_lds0[S::BUF];
   __shared__ __align__(16) char v_lds1[S::BUF];
+  __shared__ __align__(16) char v_lds2[S::BUF];
+  __shared__ __align__(16) char v_lds3[S::BUF];
+  __shared__ int slot_lds[kSlotWindow];
   __shared__ int lds_item;
-  auto kbuf = [&](int b) -> char* { return b == 0 ? k_lds0 : k_lds1; };
-  auto vbuf = [&](int b) -> char* { return b == 0 ? v_lds0 : v_lds1; };
+  auto kbuf = [&](int b) -> char* { return b == 0 ? k_lds0 : b == 1 ? k_lds1 : b == 2 ? k_lds2 : k_lds3; };
+  auto vbuf = [&](int b) -> char* { return b == 0 ? v_lds0 : b == 1 ? v_lds1 : b == 2 ? v_lds2 : v_lds3; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rg = wave & 3;      // row group
-  const int kvg = wave >> 2;    // kv group
+  // waves w and w+4 run on one SIMD: same kv group, row groups r and r+2
+  const int rg = (wave & 1) + 2 * (wave >> 2);  // row group (rows 32*rg .. +31)
+  const int kvg = (wave >> 1) & 1;              // kv group
+  const int half = rg >> 1;                     // half-tile of the pair
   const int lrow = lane & 31;   // MFMA column owned by this lane
   const int lhalf = lane >> 5;  // which k-half of the MFMA operand
   const int G = p.group;
-  const int P = p.prefill_positions;
+  const int P = p.prefill_positions;  // positions per half-tile
+  const int bs = p.block_size;
   const int64_t kv_row = static_cast<int64_t>(p.kv_heads) * D;
   const int64_t out_stride = static_cast<int64_t>(p.num_heads) * D;
   const float c = fabsf(p.scale_log2);
@@ -131,22 +173,21 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
   const int per_queue = p.ws_ctrl[kCtrlPrefillItems] * hq;
   if (per_queue == 0) return;  // no multi-token sequence in this call
   const int home = static_cast<int>(blockIdx.x % 8) % nq;
-  // the two waves of a SIMD (kv groups 0 and 1, same row group) run the same
-  // phases; giving group 0 priority lets it run ahead, so one wave's softmax
-  // (VALU) overlaps the other's matrix products
-  if (kvg == 0) __builtin_amdgcn_s_setprio(1);
+  // one wave of each SIMD runs ahead, so that its softmax (VALU) overlaps the
+  // other wave's matrix products
+  if (wave >= 4) __builtin_amdgcn_s_setprio(1);
 
   // per-lane LDS byte offsets (everything else is an immediate)
-  int koff[S::QK_STEPS];  // K fragment kk of row kvg*64 + lrow (+32 nt)
+  int koff[S::QK_STEPS];  // K fragment kk of row kvg*32 + lrow
 #pragma unroll
   for (int kk = 0; kk < S::QK_STEPS; ++kk) {
-    const int row = kvg * kPrefillKeys + lrow;
+    const int row = kvg * kGroupKeys + lrow;
     koff[kk] = row * ROWB + (((2 * kk + lhalf) ^ S::k_swz(row)) << 4);
   }
-  int voff[S::O_TILES];  // transpose-read address of d tile mt (keys kvg*64 + ...)
+  int voff[S::O_TILES];  // transpose-read address of d tile mt (keys kvg*32 + ...)
   {
     const int grp = lane >> 4, i = lane & 15, r = i >> 2, q = i & 3;
-    const int row = kvg * kPrefillKeys + 4 * (grp >> 1) + r;
+    const int row = kvg * kGroupKeys + 4 * (grp >> 1) + r;
 #pragma unroll
     for (int mt = 0; mt < S::O_TILES; ++mt) {
       const int chunk = 4 * mt + 2 * (grp & 1) + (q >> 1);
@@ -154,17 +195,18 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
     }
   }
 
-  // loader: lane's row (within the wave's 16) and swizzled chunk per direct load
-  int lk[S::LOADS], lv[S::LOADS], zk[S::LOADS], zv[S::LOADS], lrr[S::LOADS];
+  // loader: a direct load covers ROWS_PER_LOAD rows of the wave's 8; byte
+  // offsets (from the wave's first row) of this lane's swizzled 16-byte chunk
+  // for each load, and of the same chunk in the zero page
+  const int lrow0 = lane / CPR;
+  const int lchunk = lane % CPR;
+  uint32_t offk[S::LOADS], offv[S::LOADS];
 #pragma unroll
   for (int i = 0; i < S::LOADS; ++i) {
-    const int rl = S::ROWS_PER_LOAD * i + lane / CPR;  // 16*wave + rl is the tile row
-    const int phys = lane % CPR;
-    zk[i] = (phys ^ S::k_swz(rl)) * 8;  // swizzles only see the low 4 row bits
-    zv[i] = (phys ^ S::v_swz(rl)) * 8;
-    lk[i] = rl * static_cast<int>(kv_row) + zk[i];
-    lv[i] = rl * static_cast<int>(kv_row) + zv[i];
-    lrr[i] = rl;
+    const int rl = S::ROWS_PER_LOAD * i + lrow0;  // row within the wave's 8
+    const int trow = S::WAVE_ROWS * wave + rl;    // row within the step's 64
+    offk[i] = static_cast<uint32_t>((rl * static_cast<int>(kv_row) + (lchunk ^ S::k_swz(trow)) * 8) * 2);
+    offv[i] = static_cast<uint32_t>((rl * static_cast<int>(kv_row) + (lchunk ^ S::v_swz(trow)) * 8) * 2);
   }
 
   int queue = home, tried = 0;
@@ -184,30 +226,36 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
   for (int j = fetch(); j >= 0; j = fetch()) {
     const int2 bt = p.items[j / hq];
     const int kvh = queue + nq * (j % hq);
-    const int b = bt.x, tile = bt.y;
+    const int b = bt.x, pair = bt.y;
     const int t0 = p.cum[b];
     const int qlen = p.cum[b + 1] - t0;
     const int past = p.past[b];
     const int L = past + qlen;
-    const int i0 = tile * P;
+    const int nt = (qlen + P - 1) / P;  // half-tiles of this sequence
+    const int tb = nt - 1 - pair;       // half-tile of rows 64..127 (none if == pair)
+    // keys [0, kv_end) are visible to some row of the item
+    const int kv_end = past + min((tb > pair ? tb : pair) * P + P, qlen);
+    const int nsteps = (kv_end + kPrefillKeys - 1) / kPrefillKeys;
+    const int i0 = (half == 0 ? pair : tb) * P;  // this wave's half-tile
     const int i1 = min(i0 + P, qlen);
-    const int kv_end = past + i1;  // keys [0, kv_end) are visible to some row
 
     // this lane's query row
-    const int f = rg * 32 + lrow;
-    const int pos_local = f / G;
-    const int g = f % G;
-    const bool row_valid = (f < P * G) && (i0 + pos_local < i1);
+    const int fh = (rg & 1) * 32 + lrow;  // row within the half-tile
+    const int pos_local = fh / G;
+    const int g = fh % G;
+    const bool half_valid = half == 0 || tb > pair;
+    const bool row_valid = half_valid && (fh < P * G) && (i0 + pos_local < i1);
     const int row_pos = past + i0 + (row_valid ? pos_local : 0);
     const int head = kvh * G + g;
-    // positions spanned by this wave's valid rows
-    const int wave_first = past + i0 + min((rg * 32) / G, max(0, i1 - i0 - 1));
-    const int last_f = min(rg * 32 + 31, P * G - 1);
-    const int wave_last = past + min(i0 + last_f / G, i1 - 1);
+    // positions spanned by this wave's valid rows (none: wave_last = -1)
+    const int fh0 = (rg & 1) * 32;
+    const bool wave_valid = half_valid && fh0 < P * G && i0 + fh0 / G < i1;
+    const int wave_first = past + i0 + fh0 / G;
+    const int wave_last = wave_valid ? past + min(i0 + min(fh0 + 31, P * G - 1) / G, i1 - 1) : -1;
 
     half8_t qf[S::QK_STEPS];
     {
-      const uint16_t* qrow = p.q + static_cast<int64_t>(t0 + i0 + pos_local) * p.q_stride +
+      const uint16_t* qrow = p.q + static_cast<int64_t>(t0 + i0 + (row_valid ? pos_local : 0)) * p.q_stride +
                              static_cast<int64_t>(head) * D;
 #pragma unroll
       for (int kk = 0; kk < S::QK_STEPS; ++kk) {
@@ -228,65 +276,104 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
     const int32_t* btab = p.block_table + static_cast<int64_t>(b) * p.max_blocks;
     const uint16_t* kcache = p.key_cache + static_cast<int64_t>(kvh) * D;
     const uint16_t* vcache = p.value_cache + static_cast<int64_t>(kvh) * D;
-
-    // page id of this wave's 16 keys of super-tile j0 (0 past the history);
-    // fetched one super-tile before its K/V so the dependent loads never wait
-    auto page_of = [&](int j0) -> int {
-      const int jw = j0 + 16 * wave;
-      return jw < L ? btab[jw / p.block_size] : 0;
-    };
-    // direct global->LDS fill of this wave's 16 rows of super-tile j0
-    auto issue = [&](int j0, int page, int buf) {
-      const int jw = j0 + 16 * wave;
-      const int pb = __builtin_amdgcn_readfirstlane(page);
-      const int64_t at = (static_cast<int64_t>(pb) * p.block_size + (jw % p.block_size)) * kv_row;
-      const uint16_t* kb = kcache + at;
-      const uint16_t* vb = vcache + at;
-      const bool all_in = jw + 16 <= L;  // uniform: the usual case
-#pragma unroll
-      for (int i = 0; i < S::LOADS; ++i) {
-        const uint16_t* ksrc = kb + lk[i];
-        const uint16_t* vsrc = vb + lv[i];
-        if (!all_in && jw + lrr[i] >= L) {  // keys past the history read zeros
-          ksrc = p.zeros + zk[i];
-          vsrc = p.zeros + zv[i];
-        }
-        const int dst = (16 * wave + S::ROWS_PER_LOAD * i) * ROWB;
-        __builtin_amdgcn_global_load_lds((PA_GLOBAL void*)ksrc, (PA_LDS void*)(kbuf(buf) + dst), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((PA_GLOBAL void*)vsrc, (PA_LDS void*)(vbuf(buf) + dst), 16, 0, 0);
+    // cache slot (block_table[k / bs] * bs + k % bs) of every 16th key k <
+    // min(L, nsteps * 64), for 16-key groups [gbase, gbase + kSlotWindow);
+    // a wave's 8 rows of a step never cross a page (bs is a multiple of 16)
+    const int ngroups = (min(L, nsteps * kPrefillKeys) + 15) / 16;
+    const char* kbytes = reinterpret_cast<const char*>(kcache);
+    const char* vbytes = reinterpret_cast<const char*>(vcache);
+    const uint32_t row_bytes = static_cast<uint32_t>(kv_row) * 2;
+    int gbase = 0;
+    auto fill_window = [&](int first) {
+      gbase = first;
+      const int n = min(kSlotWindow, ngroups - first);
+      for (int i = tid; i < n; i += kPrefillThreads) {
+        const int key = 16 * (first + i);
+        slot_lds[i] = btab[key / bs] * bs + key % bs;
       }
+      __syncthreads();
     };
 
-    // one 64-key half-tile of this wave: S (two interleaved 32x32 chains),
-    // softmax over the 64 keys, PV (four accumulators in turn)
-    auto compute = [&](auto buf_tag, int jk, bool masked) {
+    // direct global->LDS fills of this wave's 8 rows of step s (ring buffer
+    // BUF), loads i0 .. i1-1
+    // (slot16: the window entry of the wave's rows, read ahead by slot_of)
+    auto slot_of = [&](int s) -> int { return slot_lds[((s * kPrefillKeys + S::WAVE_ROWS * wave) >> 4) - gbase]; };
+    auto issue = [&](auto buf_tag, int s, int slot16, int i_first, int i_last) __attribute__((always_inline)) {
       constexpr int buf = decltype(buf_tag)::value;
-      f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
-#pragma unroll
-      for (int kk = 0; kk < S::QK_STEPS; ++kk) {
-        half8_t ka[2];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          ka[nt] = *reinterpret_cast<const half8_t*>(kbuf(buf) + koff[kk] + nt * 32 * ROWB);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          s[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[nt], qf[kk], s[nt], 0, 0, 0);
+      const int jw = s * kPrefillKeys + S::WAVE_ROWS * wave;  // first key of the wave's rows
+      if (jw + S::WAVE_ROWS <= L) {  // the usual case: all 8 rows are history
+        const uint32_t slot = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(slot16) + (jw & 15));
+        const uint64_t at = static_cast<uint64_t>(slot) * row_bytes;
+        const char* kb = kbytes + at;
+        const char* vb = vbytes + at;
+        for (int i = i_first; i < i_last; ++i) {
+          const int dst = (S::WAVE_ROWS * wave + S::ROWS_PER_LOAD * i) * ROWB;
+          __builtin_amdgcn_global_load_lds((PA_GLOBAL void*)(kb + offk[i]), (PA_LDS void*)(kbuf(buf) + dst), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((PA_GLOBAL void*)(vb + offv[i]), (PA_LDS void*)(vbuf(buf) + dst), 16, 0, 0);
+        }
+      } else {
+        // rows past the history: read the zero page (rows < L read as usual)
+        const int slot = jw < L ? __builtin_amdgcn_readfirstlane(slot16) + (jw & 15) : 0;
+        const char* zb = reinterpret_cast<const char*>(p.zeros);
+        for (int i = i_first; i < i_last; ++i) {
+          const int rl = S::ROWS_PER_LOAD * i + lrow0;
+          const bool hist = jw + rl < L;
+          const int64_t at = static_cast<int64_t>(slot) * row_bytes;
+          const uint32_t zk = offk[i] - static_cast<uint32_t>(rl) * row_bytes;  // chunk offset alone
+          const uint32_t zv = offv[i] - static_cast<uint32_t>(rl) * row_bytes;
+          const char* ks = hist ? kbytes + at + offk[i] : zb + zk;
+          const char* vs = hist ? vbytes + at + offv[i] : zb + zv;
+          const int dst = (S::WAVE_ROWS * wave + S::ROWS_PER_LOAD * i) * ROWB;
+          __builtin_amdgcn_global_load_lds((PA_GLOBAL void*)ks, (PA_LDS void*)(kbuf(buf) + dst), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((PA_GLOBAL void*)vs, (PA_LDS void*)(vbuf(buf) + dst), 16, 0, 0);
+        }
       }
-      // register i of chain nt holds key jk + 32nt + 8(i/4) + 4*lhalf + i%4
+    };
+
+    // one step of this wave: S (32 keys x 32 rows), softmax over the 32 keys,
+    // PV (four accumulators in turn).  The K fragments of the step are all
+    // read before the first product and the V fragments before the softmax,
+    // so the step waits for one LDS round trip, not one per product.
+    auto compute = [&](auto buf_tag, int jk, bool masked) __attribute__((always_inline)) {
+      constexpr int buf = decltype(buf_tag)::value;
+      half8_t kf[S::QK_STEPS];
+#pragma unroll
+      for (int kk = 0; kk < S::QK_STEPS; ++kk) kf[kk] = *reinterpret_cast<const half8_t*>(kbuf(buf) + koff[kk]);
+      asm volatile("" ::: "memory");  // keep the reads ahead of the products
+      f32x16_t s = f32x16_t{};
+#pragma unroll
+      for (int kk = 0; kk < S::QK_STEPS; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[kk], qf[kk], s, 0, 0, 0);
+      // V^T fragments, read while the products and the softmax run: the
+      // transpose read of rows key0..key0+3 (key0 = 16ks + 4*lhalf, then +8)
+      // gives each lane the 4 keys of its d column, in the key order of the
+      // P^T registers
+      half8_t va[2][S::O_TILES];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < S::O_TILES; ++mt) {
+          char* vb = vbuf(buf) + voff[mt] + 16 * ks * ROWB;
+          const fp16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((PA_LDS fp16x4_t*)vb);
+          const fp16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((PA_LDS fp16x4_t*)(vb + 8 * ROWB));
+          va[ks][mt] = __builtin_shufflevector(__builtin_bit_cast(half4_t, lo), __builtin_bit_cast(half4_t, hi),
+                                               0, 1, 2, 3, 4, 5, 6, 7);
+        }
+      asm volatile("" ::: "memory");
+      // register i holds key jk + 8(i/4) + 4*lhalf + i%4
       if (masked) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = jk + 32 * nt + 8 * (i >> 2) + 4 * lhalf + (i & 3);
-            if (key > row_pos) s[nt][i] = kNegInf;
-          }
+        for (int i = 0; i < 16; ++i) {
+          const int key = jk + 8 * (i >> 2) + 4 * lhalf + (i & 3);
+          if (key > row_pos) s[i] = kNegInf;
+        }
       }
-      float mx = s[0][0];
+      // row max as a tree (short dependency chain)
+      float t8[8];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int i = 0; i < 8; ++i) t8[i] = fmaxf(s[i], s[i + 8]);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[nt][i]);
+      for (int i = 0; i < 4; ++i) t8[i] = fmaxf(t8[i], t8[i + 4]);
+      float mx = fmaxf(fmaxf(t8[0], t8[2]), fmaxf(t8[1], t8[3]));
       mx = swap_halves_max(mx) * c;
       const bool grow = mx > m + 8.f;
       if (__ballot(grow) != 0) {  // wave-uniform branch; other lanes scale by 1
@@ -296,82 +383,113 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
         for (int mt = 0; mt < S::O_TILES; ++mt) o[mt] *= alpha;
         m = grow ? mx : m;
       }
-      // P^T operand of 16-key step ks = registers 8(ks%2)..+7 of chain ks/2,
-      // i.e. keys 16ks + 4*lhalf + 0..3 and 16ks + 8 + 4*lhalf + 0..3.  A row
-      // that has seen no key yet (m = -inf) has only masked scores here.
+      // P^T operand of 16-key k-step ks = registers 8ks..8ks+7, i.e. keys
+      // 16ks + 4*lhalf + 0..3 and 16ks + 8 + 4*lhalf + 0..3.  A row that has
+      // seen no key yet (m = -inf) has only masked scores here.
       const float mref = m == kNegInf ? 0.f : m;
-      half8_t pb[4];
+      half8_t pb[2];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pb[ks][e] = static_cast<_Float16>(fast_exp2(fmaf(s[ks >> 1][8 * (ks & 1) + e], c, -mref)));
+        for (int e = 0; e < 8; ++e) pb[ks][e] = static_cast<_Float16>(fast_exp2(fmaf(s[8 * ks + e], c, -mref)));
       // row sum of exactly the fp16 weights the MFMA multiplies (v_dot2 with 1)
       typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
       const half2_t one2 = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+      // (two partial sums: shorter dependency chains; fixed order)
+      float la = 0.f, lb = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int e = 0; e < 8; e += 2) {
+        la = __builtin_amdgcn_fdot2(half2_t{pb[0][e], pb[0][e + 1]}, one2, la, false);
+        lb = __builtin_amdgcn_fdot2(half2_t{pb[1][e], pb[1][e + 1]}, one2, lb, false);
+      }
+      l += la + lb;
+      // O^T[d][row] += V^T[d][key] P^T[key][row]
 #pragma unroll
-        for (int e = 0; e < 8; e += 2)
-          l = __builtin_amdgcn_fdot2(half2_t{pb[ks][e], pb[ks][e + 1]}, one2, l, false);
-      // O^T[d][row] += V^T[d][key] P^T[key][row]: the transpose read of rows
-      // key0..key0+3 (key0 = 16ks + 4*lhalf, then +8) gives each lane the 4
-      // keys of its d column, matching the order of the P^T registers
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        half8_t va[S::O_TILES];
-#pragma unroll
-        for (int mt = 0; mt < S::O_TILES; ++mt) {
-          char* vb = vbuf(buf) + voff[mt] + 16 * ks * ROWB;
-          const fp16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((PA_LDS fp16x4_t*)vb);
-          const fp16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((PA_LDS fp16x4_t*)(vb + 8 * ROWB));
-          va[mt] = __builtin_shufflevector(__builtin_bit_cast(half4_t, lo), __builtin_bit_cast(half4_t, hi),
-                                           0, 1, 2, 3, 4, 5, 6, 7);
-        }
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int mt = 0; mt < S::O_TILES; ++mt)
-          o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[mt], pb[ks], o[mt], 0, 0, 0);
-      }
+          o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[ks][mt], pb[ks], o[mt], 0, 0, 0);
     };
 
-    auto step = [&](auto buf_tag, int j0, int& page_next) {
+    // Step j computes from ring buffer j % 4 and fetches step j + 3 into ring
+    // buffer (j + 3) % 4, which held step j - 1 (finished by every wave at the
+    // barrier that ended it).  Each step issues 2 * LOADS direct loads per
+    // wave, so "step j + 1 landed" is "at most 4 * LOADS loads outstanding"
+    // while steps j + 2 and j + 3 are both in flight.
+    auto step = [&](auto buf_tag, int jstep) __attribute__((always_inline)) {
       constexpr int buf = decltype(buf_tag)::value;
-      if (j0 + kSuper < kv_end) {  // fill the other buffer while this one is used
-        issue(j0 + kSuper, page_next, buf ^ 1);
-        page_next = page_of(j0 + 2 * kSuper);
-      }
-      const int jk = j0 + kvg * kPrefillKeys;  // first key of this wave's half
-      if (jk <= wave_last) {
-        const bool masked = __builtin_amdgcn_readfirstlane(jk + kPrefillKeys - 1 > wave_first);
-        compute(buf_tag, jk, masked);
-      }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's LDS fills landed
-      __syncthreads();
+      constexpr int nbuf = (buf + kRing - 1) % kRing;
+      const int s_next = jstep + kRing - 1;  // step fetched now
+      const bool more = s_next < nsteps;
+      const int slot16 = slot_of(s_next);  // (in the window; unused past the history)
+      const int jk = jstep * kPrefillKeys + kvg * kGroupKeys;  // first key of this wave's half
+      if (jk <= wave_last) compute(buf_tag, jk, jk + kGroupKeys - 1 > wave_first);
+      // the fills of step j + 3, after the products: issued in one burst they
+      // stream while the other waves compute and the next step runs
+      if (more) issue(std::integral_constant<int, nbuf>{}, s_next, slot16, 0, S::LOADS);
+      // a plain barrier: __syncthreads() would also wait for the fills still
+      // in flight.  The waits go through the builtin so that the compiler
+      // knows which fills have landed and adds no wait of its own.
+      if (more) wait_fills<4 * S::LOADS>();
+      else wait_fills<0>();
+      plain_barrier();
     };
 
-    issue(0, page_of(0), 0);
-    int page_next = page_of(kSuper);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    for (int j0 = 0; j0 < kv_end; j0 += 2 * kSuper) {
-      step(std::integral_constant<int, 0>{}, j0, page_next);
-      if (j0 + kSuper < kv_end) step(std::integral_constant<int, 1>{}, j0 + kSuper, page_next);
+    fill_window(0);
+    // steps 0..2 in flight before the first step (nested conditions: no path
+    // that the compiler considers skips a step and fetches a later one)
+    issue(std::integral_constant<int, 0>{}, 0, slot_of(0), 0, S::LOADS);
+    if (nsteps > 2) {
+      issue(std::integral_constant<int, 1>{}, 1, slot_of(1), 0, S::LOADS);
+      issue(std::integral_constant<int, 2>{}, 2, slot_of(2), 0, S::LOADS);
+      wait_fills<4 * S::LOADS>();
+    } else {
+      if (nsteps > 1) issue(std::integral_constant<int, 1>{}, 1, slot_of(1), 0, S::LOADS);
+      wait_fills<0>();
+    }
+    plain_barrier();
+    // Steps in chunks of kChunk: the slot window holds the chunk's steps and
+    // the three fetched ahead of it, and is refilled between chunks (the
+    // fills already in flight read the previous window).  Within a chunk,
+    // whole turns of the ring, then the last 0..3 steps: every turn runs all
+    // four, so the compiler can see that the wait ending each step covers the
+    // fills of the next turn's first step.
+    for (int c0 = 0; c0 < nsteps; c0 += kChunk) {
+      if (c0 > 0) fill_window(4 * c0);  // uniform; all waves are between barriers
+      const int c1 = min(nsteps, c0 + kChunk);
+      int j0 = c0;
+      for (; j0 + kRing <= c1; j0 += kRing) {
+        step(std::integral_constant<int, 0>{}, j0);
+        step(std::integral_constant<int, 1>{}, j0 + 1);
+        step(std::integral_constant<int, 2>{}, j0 + 2);
+        step(std::integral_constant<int, 3>{}, j0 + 3);
+      }
+      // (nested so that no path skips a step and runs a later one)
+      if (j0 < c1) {
+        step(std::integral_constant<int, 0>{}, j0);
+        if (j0 + 1 < c1) {
+          step(std::integral_constant<int, 1>{}, j0 + 1);
+          if (j0 + 2 < c1) step(std::integral_constant<int, 2>{}, j0 + 2);
+        }
+      }
     }
 
-    // merge the two kv groups (group 0 first) and write; reuse the K buffers
-    // [4 row groups][O_TILES*16][64 lanes] over the K buffers, [4][2][64] after
-    float* xo = reinterpret_cast<float*>(k_lds0);
+    // merge the two kv groups (group 0 first) and write.  Row group r's O of
+    // kv group 1 goes to K buffer r ([O_TILES*16][64 lanes] floats), (m, l)
+    // of all row groups to V buffer 0.
+    wait_fills<0>();  // (the last steps already waited)
+    float* xo = reinterpret_cast<float*>(kbuf(rg));
     float* xml = reinterpret_cast<float*>(v_lds0);
     if (kvg == 1) {
 #pragma unroll
       for (int mt = 0; mt < S::O_TILES; ++mt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) xo[(rg * S::O_TILES * 16 + mt * 16 + i) * 64 + lane] = o[mt][i];
+        for (int i = 0; i < 16; ++i) xo[(mt * 16 + i) * 64 + lane] = o[mt][i];
       xml[(rg * 2 + 0) * 64 + lane] = m;
       xml[(rg * 2 + 1) * 64 + lane] = l;
     }
     __syncthreads();
-    if (kvg == 0) {
+    if (kvg == 0 && wave_valid) {
       const float m1 = xml[(rg * 2 + 0) * 64 + lane];
       const float l1 = xml[(rg * 2 + 1) * 64 + lane];
       const float mm = fmaxf(m, m1);
@@ -390,7 +508,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
               const int ir = 4 * q + 2 * e;
-              const float* x1 = &xo[(rg * S::O_TILES * 16 + mt * 16 + ir) * 64 + lane];
+              const float* x1 = &xo[(mt * 16 + ir) * 64 + lane];
               const float v0 = (o[mt][ir] * a0 + x1[0] * a1) * inv;
               const float v1 = (o[mt][ir + 1] * a0 + x1[64] * a1) * inv;
               w[e] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(v0))) |
@@ -406,10 +524,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
 
 template <int D>
 constexpr size_t prefill_smem() {
-  return 4 * static_cast<size_t>(PrefillShape<D>::BUF);
+  return 2 * kRing * static_cast<size_t>(PrefillShape<D>::BUF) + kSlotWindow * sizeof(int) + 16;
 }
-// the merge area (O of four row groups over the K buffers) must fit
-static_assert(4 * 4 * 16 * 64 * sizeof(float) <= 2 * PrefillShape<128>::BUF, "merge area");
+// the merge area (O of one row group) must fit one K buffer, (m, l) one V buffer
+static_assert(4 * 16 * 64 * sizeof(float) <= PrefillShape<128>::BUF, "merge area");
+static_assert(2 * 16 * 64 * sizeof(float) <= PrefillShape<64>::BUF, "merge area");
+static_assert(prefill_smem<128>() <= 160 * 1024, "LDS budget");
 
 template <int D>
 hipError_t launch_prefill_t(const AttnParams& p, int grid, hipStream_t s) {

@@ -53,8 +53,9 @@ constexpr int kPlanLdsSeqs = 8192;  // decode sequences whose first tile the pla
 // offset of their first segment; each decode wave gets the segment and tile
 // where its equal share of all tiles begins (a binary search over the
 // sequences' first tiles, in LDS).
-// Multi-token sequences get one prefill item per query tile, the last
-// (longest) tile first.
+// Multi-token sequences get one prefill item per pair of query half-tiles
+// (t and nt-1-t of the sequence's nt), which all cost about the same under
+// the causal mask.
 __device__ void plan(const ScatterPlanParams& p) {
   __shared__ int3 scan_lds[256];
   __shared__ int first_tile[kPlanLdsSeqs];
@@ -72,7 +73,7 @@ __device__ void plan(const ScatterPlanParams& p) {
         nd = 1;
         nt = (L + kDecodeTile - 1) / kDecodeTile * U;
       } else if (q > 1) {
-        np = (q + p.prefill_positions - 1) / p.prefill_positions;
+        np = ((q + p.prefill_positions - 1) / p.prefill_positions + 1) / 2;  // half-tile pairs
       }
     }
     int3 tot;
@@ -82,7 +83,7 @@ __device__ void plan(const ScatterPlanParams& p) {
       p.dec_seq[d] = make_int4(b, t0, L, tile_base + o.y);
       if (d < kPlanLdsSeqs) first_tile[d] = tile_base + o.y;
     }
-    for (int t = 0; t < np; ++t) p.pf_items[pf_base + o.z + t] = make_int2(b, np - 1 - t);
+    for (int t = 0; t < np; ++t) p.pf_items[pf_base + o.z + t] = make_int2(b, t);
     dec_base += tot.x;
     tile_base += tot.y;
     pf_base += tot.z;

@@ -202,6 +202,15 @@ def test_long_decode_many_splits():
     check(b)
 
 
+def test_long_history_prefill():
+    # a chunk on top of 40000 cached tokens: the prefill reads more than
+    # 32768 keys, past what one window of cache slots covers; an odd number
+    # of half-tiles leaves one item with a single half
+    b = W.make_batch([37, 1, 20], [40000, 100, 33000], num_heads=8, kv_num_heads=1,
+                     head_size=128, block_size=16, seed=13, name="long_history")
+    check(b, rows=sample_rows(b, per_seq=8, seed=13))
+
+
 def test_deterministic_bits():
     b = W.mixed(1)
     d = DevBatch(b)

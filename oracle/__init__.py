@@ -10,8 +10,9 @@ Modules
   paged_attention  numpy fp64 implementation of the operator: scatter the
                    step's K/V into copies of the caches, gather each sequence's
                    history through block_table, brute-force causal GQA softmax
-                   attention.  Also the partial (out, lse) state over a key
-                   subset and its fixed-order merge.
+                   attention, optionally with each row's attention-domain
+                   lse.  Also the partial (out, lse) state over a key subset
+                   and the fixed-order merge of such states.
   scalar           a second, independent formulation in plain Python scalars
                    (nested loops, math.fsum) for tiny inputs, used to pin the
                    numpy version.
@@ -27,5 +28,6 @@ from .paged_attention import (  # noqa: F401
     attend_sequence,
     partial_state,
     merge_partials,
+    merge_states,
     resolve_call,
 )

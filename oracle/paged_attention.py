@@ -118,44 +118,51 @@ def gather_history(kc: np.ndarray, vc: np.ndarray, block_table: np.ndarray, b: i
 
 
 def attend_sequence(Qb: np.ndarray, Kb: np.ndarray, Vb: np.ndarray, past_b: int,
-                    scale: float, rows: Optional[Sequence[int]] = None) -> np.ndarray:
+                    scale: float, rows: Optional[Sequence[int]] = None, with_lse: bool = False):
     """Causal grouped-query softmax attention of one sequence, brute force.
 
     Qb [q, H, D], Kb/Vb [L, Hkv, D] (fp64, L = past_b + q).  For head h with
     kv head k = h // (H/Hkv): S = scale * Q_h K_k^T, entries with key
     position j > past_b + i set to -inf, P = softmax over keys, O = P V_k.
     ``rows`` restricts the work to those new-token rows (others are NaN).
-    Returns [q, H, D] fp64.
+    Returns [q, H, D] fp64; with ``with_lse`` also the attention-domain lse
+    [q, H] = log sum_j exp(S_j) over the visible keys (natural log; "WS2
+    CP-Aware Attention Contract", Reduction Semantics: the partial state of a
+    row is (out, lse)).
     """
     q, H, D = Qb.shape
     L, Hkv, _ = Kb.shape
     G = H // Hkv
     sel = np.arange(q) if rows is None else np.asarray(rows, dtype=np.int64)
     out = np.full((q, H, D), np.nan)
+    lse = np.full((q, H), np.nan)
     if sel.size == 0:
-        return out
+        return (out, lse) if with_lse else out
     pos = int(past_b) + sel
     masked = np.arange(L)[None, :] > pos[:, None]
     for h in range(H):
         k = h // G
         S = scale * (Qb[sel, h, :] @ Kb[:, k, :].T)
         S[masked] = -np.inf
-        S = S - S.max(axis=1, keepdims=True)
-        P = np.exp(S)
-        P /= P.sum(axis=1, keepdims=True)
-        out[sel, h, :] = P @ Vb[:, k, :]
-    return out
+        mx = S.max(axis=1, keepdims=True)
+        P = np.exp(S - mx)
+        den = P.sum(axis=1, keepdims=True)
+        out[sel, h, :] = (P / den) @ Vb[:, k, :]
+        lse[sel, h] = (mx + np.log(den))[:, 0]
+    return (out, lse) if with_lse else out
 
 
 def paged_attention(query, key, value, key_cache, value_cache, cum, past, block_table,
                     slot_mapping=None, *, num_heads: int, kv_num_heads: int,
-                    scale: float = 0.0, is_causal: int = 1, rows=None):
+                    scale: float = 0.0, is_causal: int = 1, rows=None, with_lse: bool = False):
     """The whole operator: returns (output fp64 [N, H*D], key_cache', value_cache').
 
     README, Description/Outputs: the caches are updated (here: copies are
     returned) and output holds one row of H*D values per packed token.
     ``rows``: optional sorted token indices to compute (others are NaN), so
-    that full-size workloads can be checked on a sample.
+    that full-size workloads can be checked on a sample.  ``with_lse``: also
+    return the attention-domain lse [N, H] of every row (see attend_sequence)
+    as a fourth value.
     """
     if int(is_causal) != 1:
         raise ValueError("only is_causal=1 is defined")
@@ -167,6 +174,7 @@ def paged_attention(query, key, value, key_cache, value_cache, cum, past, block_
         raise ValueError("cumulative_sequence_length must run from 0 to N")
     kc, vc = scatter_kv(key_cache, value_cache, K, V, cum, past, block_table, slot_mapping)
     out = np.full((N, num_heads, D), np.nan)
+    lse = np.full((N, num_heads), np.nan)
     want = None if rows is None else np.zeros(N, dtype=bool)
     if want is not None:
         want[np.asarray(rows, dtype=np.int64)] = True
@@ -182,7 +190,13 @@ def paged_attention(query, key, value, key_cache, value_cache, cum, past, block_
         L = int(past[b]) + (t1 - t0)
         Kb, Vb = gather_history(kc, vc, block_table, b, L)
         Qb = Q[t0:t1].astype(np.float64)
-        out[t0:t1] = attend_sequence(Qb, Kb, Vb, int(past[b]), s, rows=local)
+        if with_lse:
+            out[t0:t1], lse[t0:t1] = attend_sequence(Qb, Kb, Vb, int(past[b]), s, rows=local,
+                                                     with_lse=True)
+        else:
+            out[t0:t1] = attend_sequence(Qb, Kb, Vb, int(past[b]), s, rows=local)
+    if with_lse:
+        return out.reshape(N, num_heads * D), kc, vc, lse
     return out.reshape(N, num_heads * D), kc, vc
 
 
@@ -216,3 +230,31 @@ def merge_partials(outs: Sequence[np.ndarray], lses: Sequence[float]) -> np.ndar
         num = num + w * np.asarray(o, dtype=np.float64)
         den += w
     return num / den
+
+
+def merge_states(outs: np.ndarray, lses: np.ndarray):
+    """Merge of partial states, whole tensors at once ("WS2 CP-Aware Attention
+    Contract", Reduction Semantics: partial state (out, attention-domain lse),
+    online-softmax merge, fixed order, one downcast at the final write).
+
+    outs [P, R, D], lses [P, R] (R rows, P states per row, in merge order).
+    The merged state of a row is the state of the union of the key sets:
+    lse = log sum_p exp(lse_p) and out = sum_p exp(lse_p - lse) out_p, here
+    evaluated with the shift M = max_p lse_p, in fp64.  A state with lse =
+    -inf (no keys) has weight 0; a row whose states are all empty merges to
+    out = 0, lse = -inf.  Returns (out [R, D], lse [R]) fp64.
+    """
+    outs = np.asarray(outs, dtype=np.float64)
+    lses = np.asarray(lses, dtype=np.float64)
+    M = lses.max(axis=0)
+    empty = ~np.isfinite(M)
+    Ms = np.where(empty, 0.0, M)
+    w = np.exp(lses - Ms[None, :])            # [P, R], 0 for empty states
+    den = w.sum(axis=0)
+    out = np.zeros(outs.shape[1:])
+    for p in range(outs.shape[0]):             # summed in the given order
+        out += w[p][:, None] * outs[p]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        out = np.where(empty[:, None], 0.0, out / np.where(empty, 1.0, den)[:, None])
+        lse = np.where(empty, -np.inf, Ms + np.log(np.where(empty, 1.0, den)))
+    return out, lse

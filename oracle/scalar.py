@@ -18,9 +18,12 @@ def _row(arr, t, start, count):
 
 
 def paged_attention_scalar(query, key, value, key_cache, value_cache, cum, past,
-                           block_table, slot_mapping, num_heads, kv_num_heads, scale):
+                           block_table, slot_mapping, num_heads, kv_num_heads, scale,
+                           with_lse=False):
     """Returns (out as nested lists [N][H*D], dict slot->(krow, vrow) of the
-    slots written).  Inputs are numpy arrays only as containers."""
+    slots written), and with ``with_lse`` also lse as nested lists [N][H]
+    (log of the fsum of exp(score) over the visible keys, natural log).
+    Inputs are numpy arrays only as containers."""
     H, Hkv = int(num_heads), int(kv_num_heads)
     N, width = query.shape
     packed = key is None
@@ -62,11 +65,13 @@ def paged_attention_scalar(query, key, value, key_cache, value_cache, cum, past,
         return [float(x) for x in src[blk][off].reshape(-1)]
 
     out = []
+    lse = []
     for t in range(N):
         b, i = owner[t]
         pos = int(past[b]) + i
         qrow = _row(query, t, 0, H * D)
         orow = []
+        lrow = []
         for h in range(H):
             kvh = h * Hkv // H  # = h // (H/Hkv)
             scores = []
@@ -83,5 +88,7 @@ def paged_attention_scalar(query, key, value, key_cache, value_cache, cum, past,
             z = math.fsum(w)
             for d in range(D):
                 orow.append(math.fsum(w[j] * vals[j][d] for j in range(len(w))) / z)
+            lrow.append(top + math.log(z))
         out.append(orow)
-    return out, written
+        lse.append(lrow)
+    return (out, written, lse) if with_lse else (out, written)

@@ -480,3 +480,142 @@ def test_planted_mistakes(name):
         except (AssertionError, IndexError, ValueError):
             caught.append(check.__name__)
     assert caught, f"planted mistake {name} passed every pin"
+
+
+# ------------------------------------------------------------------ lse and state merge
+
+# Pins of the attention-domain lse the oracle exports with its output, and of
+# its whole-tensor merge of partial states ("WS2 CP-Aware Attention Contract",
+# Reduction Semantics: the partial state of a row is (out, lse); states merge
+# by the online-softmax rule in a fixed order).
+#   L1  lone first token: one visible key, lse = scale <q, k0>; zero query:
+#       all scores 0, lse = log(number of visible keys).
+#   L2  the scalar formulation's fsum lse agrees within 1e-12.
+#   M1  splitting a row's visible keys into parts, the merged partial states
+#       equal the direct (out, lse) of the row (union of the key sets).
+#   M2  one state is returned unchanged; a state with lse = -inf is ignored;
+#       all-empty rows give (0, -inf); permuting the states changes nothing
+#       beyond rounding.
+
+
+def _scale_of(b):
+    return b.scale if b.scale != 0 else 1.0 / math.sqrt(b.head_size)
+
+
+def check_L(fn_lse):
+    b = W.make_batch([1, 1], [0, 9], num_heads=4, kv_num_heads=2, head_size=8, block_size=16,
+                     seed=21, name="lse_pins")
+    o, _, _, lse = fn_lse(b)
+    # first sequence: past 0, one token: a single visible key (its own K row)
+    Q = b.query.astype(np.float64).reshape(b.num_tokens, b.num_heads, -1)
+    K = b.key.astype(np.float64).reshape(b.num_tokens, b.kv_num_heads, -1)
+    D = Q.shape[2]
+    for h in range(b.num_heads):
+        assert abs(lse[0, h] - _scale_of(b) * Q[0, h] @ K[0, h // 2]) < 1e-12
+    # zero query: every score is 0
+    bz = W.make_batch([3], [13], num_heads=2, kv_num_heads=1, head_size=8, block_size=16, seed=22,
+                      name="lse_zero")
+    bz.query[:] = 0
+    _, _, _, lz = fn_lse(bz)
+    for i in range(3):
+        assert np.all(np.abs(lz[i] - math.log(13 + i + 1)) < 1e-12)
+    # scalar formulation
+    for bb in (b, small(seed=23, head_size=4), small(seed=24, head_size=4, packed=True,
+                                                     slot_mode="drop", drop_count=2)):
+        _, _, _, l1 = fn_lse(bb)
+        _, _, l2 = scalar.paged_attention_scalar(bb.query, bb.key, bb.value, bb.key_cache,
+                                                 bb.value_cache, bb.cum, bb.past, bb.block_table,
+                                                 bb.slot_mapping, bb.num_heads, bb.kv_num_heads,
+                                                 bb.scale, with_lse=True)
+        assert np.max(np.abs(l1 - np.array(l2))) < 1e-12
+
+
+def _oracle_with_lse(b):
+    return call(oracle.paged_attention, b, with_lse=True)
+
+
+def test_oracle_lse_pins():
+    check_L(_oracle_with_lse)
+
+
+def check_M(merge):
+    rng = np.random.default_rng(31)
+    b = W.make_batch([5, 1], [40, 70], num_heads=4, kv_num_heads=2, head_size=16, block_size=16,
+                     seed=32, name="merge_pins")
+    o, kc, vc, lse = _oracle_with_lse(b)
+    Q, _, _, D, s = oracle.resolve_call(b.query, b.key, b.value, b.num_heads, b.kv_num_heads,
+                                        b.scale)
+    G = b.num_heads // b.kv_num_heads
+    for i in range(b.batch_size):
+        L = int(b.kv_lens[i])
+        Kb, Vb = oracle.gather_history(kc, vc, b.block_table, i, L)
+        for r in range(int(b.q_lens[i])):
+            t = int(b.cum[i]) + r
+            vis = int(b.past[i]) + r + 1
+            for h in range(b.num_heads):
+                keys = rng.permutation(vis)
+                parts = np.split(keys, np.sort(rng.choice(np.arange(1, vis), 3, replace=False)))
+                st = [oracle.partial_state(Q[t, h].astype(np.float64), Kb[:, h // G], Vb[:, h // G],
+                                           s, p) for p in parts]
+                mo, ml = merge(np.stack([x[0] for x in st])[:, None, :],
+                               np.array([x[1] for x in st])[:, None])
+                assert np.max(np.abs(mo[0] - o[t, h * D:(h + 1) * D])) < 1e-12
+                assert abs(ml[0] - lse[t, h]) < 1e-12
+    # identities on random states
+    P, R, Dm = 4, 6, 8
+    outs = rng.standard_normal((P, R, Dm))
+    lses = rng.standard_normal((P, R)) * 3
+    mo, ml = merge(outs[:1], lses[:1])
+    assert np.max(np.abs(mo - outs[0])) < 1e-15 and np.max(np.abs(ml - lses[0])) < 1e-15
+    l2 = lses.copy()
+    l2[2] = -np.inf
+    a_o, a_l = merge(outs, l2)
+    b_o, b_l = merge(np.delete(outs, 2, axis=0), np.delete(l2, 2, axis=0))
+    assert np.max(np.abs(a_o - b_o)) < 1e-12 and np.max(np.abs(a_l - b_l)) < 1e-12
+    e_o, e_l = merge(outs, np.full((P, R), -np.inf))
+    assert np.all(e_o == 0) and np.all(e_l == -np.inf)
+    perm = rng.permutation(P)
+    p_o, p_l = merge(outs[perm], lses[perm])
+    m_o, m_l = merge(outs, lses)
+    assert np.max(np.abs(p_o - m_o)) < 1e-12 and np.max(np.abs(p_l - m_l)) < 1e-12
+
+
+def test_oracle_merge_pins():
+    check_M(oracle.merge_states)
+
+
+def _merge_unnormalised(outs, lses):
+    o, l = oracle.merge_states(outs, lses)
+    return o * np.exp(l - np.max(lses, axis=0))[:, None], l
+
+
+def _merge_lse_is_max(outs, lses):
+    o, _ = oracle.merge_states(outs, lses)
+    return o, np.max(lses, axis=0)
+
+
+def _merge_last_state_only(outs, lses):
+    return np.asarray(outs[-1], dtype=np.float64), np.asarray(lses[-1], dtype=np.float64)
+
+
+def _lse_log2(b):
+    o, kc, vc, lse = _oracle_with_lse(b)
+    return o, kc, vc, lse / math.log(2)
+
+
+def _lse_unscaled(b):
+    o, kc, vc, lse = _oracle_with_lse(b)
+    return o, kc, vc, lse / _scale_of(b)
+
+
+@pytest.mark.parametrize("mutant", [_merge_unnormalised, _merge_lse_is_max, _merge_last_state_only],
+                         ids=lambda f: f.__name__)
+def test_merge_pins_catch_planted_mistakes(mutant):
+    with pytest.raises(AssertionError):
+        check_M(mutant)
+
+
+@pytest.mark.parametrize("mutant", [_lse_log2, _lse_unscaled], ids=lambda f: f.__name__)
+def test_lse_pins_catch_planted_mistakes(mutant):
+    with pytest.raises(AssertionError):
+        check_L(mutant)

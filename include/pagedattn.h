@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 
 /* Result codes.  Every host-checkable fault returns one of these before any
  * device work is enqueued (typed errors, as the acceptance criteria of "Add
@@ -144,6 +144,20 @@ typedef struct pa_args {
    * launches kernel k and events[2k+1] right after, so a tool can time each
    * kernel on the stream it runs on.  Kernel k = enum pa_kernel. */
   void *const *kernel_events;
+
+  /* Optional outputs of the row's partial state, NULL = not written ("WS2
+   * CP-Aware Attention Contract", Reduction Semantics: the state of a row is
+   * (out, attention-domain lse), accumulated in fp32 and rounded only at the
+   * final write):
+   *  lse         float [num_tokens, num_heads], 4-byte aligned:
+   *              log sum_j exp(scale * <q, k_j>) over the row's visible keys
+   *              (natural log);
+   *  output_f32  float [num_tokens, num_heads*head_size], 16-byte aligned:
+   *              the output before its rounding to T.
+   * Neither may overlap any other tensor of the call.  Such states merge with
+   * pa_merge_states(). */
+  float *lse;
+  float *output_f32;
 } pa_args;
 
 /* Kernels launched by one call, in launch order (indices into kernel_events). */
@@ -172,6 +186,45 @@ pa_status pa_paged_attention(const pa_args *args, void *stream);
  * (it may query the current device once); returns 0 when the shape fields
  * are invalid.  Pointer fields are ignored. */
 size_t pa_workspace_bytes(const pa_args *args);
+
+/*
+ * Fixed-order merge of partial attention states ("WS2 CP-Aware Attention
+ * Contract", Reduction Semantics: partial state (out, attention-domain lse),
+ * merge online_softmax_lse, fp32 accumulation, fixed order, downcast at the
+ * final write).  Row r of state p is (state_out[p][r], state_lse[p][r]), the
+ * normalised output and the natural-log lse over some key set; the merged row
+ * is the state of the union of the key sets of states 0..P-1, accumulated in
+ * that order:
+ *   lse = lse_0,  out = out_0;  for p = 1 .. P-1:
+ *     lse' = log(exp(lse) + exp(lse_p)),
+ *     out  = exp(lse - lse') out + exp(lse_p - lse') out_p,  lse = lse'.
+ * A state with lse = -inf (no keys) has weight 0; a row whose states are all
+ * empty merges to out = 0, lse = -inf.
+ *
+ *  state_out    float [num_states, num_rows, head_size], 16-byte aligned
+ *  state_lse    float [num_states, num_rows]
+ *  output       T [num_rows, head_size] (dtype), or NULL
+ *  output_f32   float [num_rows, head_size], 16-byte aligned, or NULL
+ *  lse          float [num_rows], or NULL
+ * Rows are independent, e.g. num_rows = num_tokens * num_heads for states
+ * written by pa_paged_attention.  Outputs must not overlap the states.
+ * Supported: num_states >= 1, head_size a multiple of 4 up to 512, dtype
+ * PA_DTYPE_F16.  Asynchronous on `stream`; no workspace, no allocation.
+ */
+typedef struct pa_merge_args {
+  uint32_t struct_size;          /* = sizeof(pa_merge_args)                */
+  int32_t dtype;                 /* pa_dtype of output                     */
+  int32_t num_states;            /* P                                      */
+  int32_t head_size;             /* D                                      */
+  int64_t num_rows;              /* R                                      */
+  const float *state_out;
+  const float *state_lse;
+  void *output;
+  float *output_f32;
+  float *lse;
+} pa_merge_args;
+
+pa_status pa_merge_states(const pa_merge_args *args, void *stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *pa_status_string(pa_status status);

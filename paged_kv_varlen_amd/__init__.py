@@ -8,6 +8,8 @@ There is no fallback: if the library is not built, every call raises.
                           cumulative_sequence_length, past_seqlens, block_table,
                           slot_mapping=None, num_heads=H, kv_num_heads=Hkv,
                           scale=0.0)
+    out, lse = paged_attention(..., return_lse=True)      # + fp32 lse [N, H]
+    out, lse = merge_states(state_out, state_lse)          # fixed-order merge
 
 Argument meaning follows the com.microsoft PagedAttention operator (model-card
 README "com.microsoft.PagedAttention", sections Inputs, Outputs, Attributes);
@@ -21,13 +23,13 @@ from typing import Optional
 
 import torch
 
-__all__ = ["paged_attention", "workspace_bytes", "PagedAttentionError", "PaArgs", "library",
-           "library_path", "STATUS"]
+__all__ = ["paged_attention", "merge_states", "workspace_bytes", "PagedAttentionError", "PaArgs",
+           "PaMergeArgs", "library", "library_path", "STATUS"]
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
 
 PA_DTYPE_F16 = 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 KERNELS = ("scatter_plan", "decode", "merge", "prefill")  # enum pa_kernel order
 STATUS = {
     0: "PA_OK", 1: "PA_ERR_NULL_ARG", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED",
@@ -67,6 +69,25 @@ class PaArgs(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("kernel_events", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p),
+        ("output_f32", ctypes.c_void_p),
+    ]
+
+
+class PaMergeArgs(ctypes.Structure):
+    """Mirror of pa_merge_args in include/pagedattn.h."""
+
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("dtype", ctypes.c_int32),
+        ("num_states", ctypes.c_int32),
+        ("head_size", ctypes.c_int32),
+        ("num_rows", ctypes.c_int64),
+        ("state_out", ctypes.c_void_p),
+        ("state_lse", ctypes.c_void_p),
+        ("output", ctypes.c_void_p),
+        ("output_f32", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p),
     ]
 
 
@@ -93,6 +114,8 @@ def library() -> ctypes.CDLL:
         lib.pa_workspace_bytes.restype = ctypes.c_size_t
         lib.pa_status_string.argtypes = [ctypes.c_int]
         lib.pa_status_string.restype = ctypes.c_char_p
+        lib.pa_merge_states.argtypes = [ctypes.POINTER(PaMergeArgs), ctypes.c_void_p]
+        lib.pa_merge_states.restype = ctypes.c_int
         lib.pa_abi_version.argtypes = []
         lib.pa_abi_version.restype = ctypes.c_int32
         if lib.pa_abi_version() != ABI_VERSION:
@@ -189,9 +212,17 @@ def paged_attention(query: torch.Tensor, key: Optional[torch.Tensor],
                     output: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None,
                     stream: Optional[torch.cuda.Stream] = None,
-                    kernel_events=None) -> torch.Tensor:
+                    kernel_events=None, return_lse: bool = False,
+                    lse: Optional[torch.Tensor] = None,
+                    output_f32: Optional[torch.Tensor] = None):
     """Scatter the step's K/V into the caches (in place) and return the
     attention output [num_tokens, num_heads * head_size].
+
+    With ``return_lse`` (or a given ``lse`` tensor, fp32 [num_tokens,
+    num_heads]) the call also writes each row's attention-domain lse and
+    returns (output, lse).  ``output_f32`` (fp32 [num_tokens, num_heads *
+    head_size]) receives the output before its rounding; together with lse it
+    is the row's partial state for merge_states().
 
     ``kernel_events``: optional sequence of 2*len(KERNELS) torch.cuda.Event
     (enable_timing=True); the library records pair k around its k-th kernel."""
@@ -207,6 +238,13 @@ def paged_attention(query: torch.Tensor, key: Optional[torch.Tensor],
     args = make_args(query, key, value, key_cache, value_cache, cumulative_sequence_length,
                      past_seqlens, block_table, slot_mapping, output, num_heads=num_heads,
                      kv_num_heads=kv_num_heads, scale=scale, is_causal=is_causal)
+    if return_lse and lse is None:
+        lse = torch.empty((query.shape[0], num_heads), dtype=torch.float32, device=dev)
+    for name, t in (("lse", lse), ("output_f32", output_f32)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 tensor")
+    args.lse = _ptr(lse)
+    args.output_f32 = _ptr(output_f32)
     need = int(lib.pa_workspace_bytes(ctypes.byref(args)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -220,4 +258,44 @@ def paged_attention(query: torch.Tensor, key: Optional[torch.Tensor],
         args.kernel_events = ctypes.cast(ev_array, ctypes.c_void_p)
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     call(args, s.cuda_stream)
-    return output
+    return (output, lse) if lse is not None else output
+
+
+def merge_states(state_out: torch.Tensor, state_lse: torch.Tensor, *,
+                 output: Optional[torch.Tensor] = None,
+                 output_f32: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None,
+                 stream: Optional[torch.cuda.Stream] = None):
+    """Fixed-order merge of partial states (library entry pa_merge_states).
+
+    state_out fp32 [P, R, D], state_lse fp32 [P, R] (natural log, -inf =
+    empty); states fold in index order.  Returns (output fp16 [R, D], lse fp32
+    [R]); ``output_f32`` optionally receives the unrounded output."""
+    lib = library()
+    if state_out.dim() != 3 or state_lse.shape != state_out.shape[:2]:
+        raise ValueError("state_out must be [P, R, D] and state_lse [P, R]")
+    for name, t in (("state_out", state_out), ("state_lse", state_lse)):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 tensor")
+    P, R, D = state_out.shape
+    dev = state_out.device
+    if output is None:
+        output = torch.empty((R, D), dtype=torch.float16, device=dev)
+    if lse is None:
+        lse = torch.empty((R,), dtype=torch.float32, device=dev)
+    a = PaMergeArgs()
+    a.struct_size = ctypes.sizeof(PaMergeArgs)
+    a.dtype = PA_DTYPE_F16 if output.dtype == torch.float16 else 0
+    a.num_states = P
+    a.head_size = D
+    a.num_rows = R
+    a.state_out = _ptr(state_out)
+    a.state_lse = _ptr(state_lse)
+    a.output = _ptr(output)
+    a.output_f32 = _ptr(output_f32)
+    a.lse = _ptr(lse)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    st = lib.pa_merge_states(ctypes.byref(a), s.cuda_stream)
+    if st != 0:
+        raise PagedAttentionError(st, lib.pa_status_string(st).decode())
+    return output, lse

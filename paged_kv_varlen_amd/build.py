@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpagedattn.so")
-SOURCES = ["pa_api.hip", "pa_scatter.hip", "pa_decode.hip", "pa_prefill.hip"]
+SOURCES = ["pa_api.hip", "pa_scatter.hip", "pa_decode.hip", "pa_prefill.hip", "pa_states.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

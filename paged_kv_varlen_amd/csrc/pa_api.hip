@@ -192,7 +192,7 @@ const char* pa_status_string(pa_status s) {
     case PA_ERR_UNSUPPORTED: return "valid for the operator but not supported by these kernels";
     case PA_ERR_WORKSPACE: return "workspace missing or smaller than pa_workspace_bytes()";
     case PA_ERR_ALIGNMENT: return "a tensor pointer is not 16-byte aligned";
-    case PA_ERR_ABI: return "pa_args.struct_size does not match the library";
+    case PA_ERR_ABI: return "struct_size does not match the library";
     case PA_ERR_METADATA: return "device metadata violates the operator contract";
     case PA_ERR_HIP: return "HIP runtime error";
   }
@@ -214,7 +214,8 @@ pa_status pa_paged_attention(const pa_args* a, void* stream) {
   if (!aligned16(a->query) || !aligned16(a->key) || !aligned16(a->value) ||
       !aligned16(a->key_cache) || !aligned16(a->value_cache) || !aligned16(a->output) ||
       !aligned4(a->cumulative_sequence_length) || !aligned4(a->past_seqlens) ||
-      !aligned4(a->block_table) || !aligned4(a->slot_mapping) || !aligned16(a->workspace))
+      !aligned4(a->block_table) || !aligned4(a->slot_mapping) || !aligned16(a->workspace) ||
+      !aligned4(a->lse) || !aligned16(a->output_f32))
     return PA_ERR_ALIGNMENT;
   const WorkspaceLayout w = layout(r);
   if (a->workspace == nullptr || a->workspace_bytes < w.total) return PA_ERR_WORKSPACE;
@@ -296,6 +297,8 @@ pa_status pa_paged_attention(const pa_args* a, void* stream) {
   ap.decode_waves = w.decode_waves;
   ap.prefill_positions = prefill_positions(r.G);
   ap.scale_log2 = r.scale * 1.4426950408889634f;
+  ap.lse_out = a->lse;
+  ap.out_f32 = a->output_f32;
 
   const int cus = device_cus();
   mark(PA_KERNEL_DECODE, 0);
@@ -310,6 +313,30 @@ pa_status pa_paged_attention(const pa_args* a, void* stream) {
   mark(PA_KERNEL_PREFILL, 0);
   if (launch_prefill(ap, r.D, pf_grid, s) != hipSuccess) return PA_ERR_HIP;
   mark(PA_KERNEL_PREFILL, 1);
+  return PA_OK;
+}
+
+pa_status pa_merge_states(const pa_merge_args* a, void* stream) {
+  using namespace pa;
+  if (a == nullptr) return PA_ERR_NULL_ARG;
+  if (a->struct_size != sizeof(pa_merge_args)) return PA_ERR_ABI;
+  if (a->num_states < 1 || a->num_rows < 0 || a->head_size <= 0) return PA_ERR_SHAPE;
+  if (a->dtype != PA_DTYPE_F16 || a->head_size % 4 != 0 || a->head_size > 512) return PA_ERR_UNSUPPORTED;
+  if (a->num_rows == 0) return PA_OK;
+  if (a->state_out == nullptr || a->state_lse == nullptr) return PA_ERR_NULL_ARG;
+  if (!aligned16(a->state_out) || !aligned4(a->state_lse) || !aligned16(a->output_f32) ||
+      !aligned4(a->lse) || (reinterpret_cast<uintptr_t>(a->output) & 7u) != 0)
+    return PA_ERR_ALIGNMENT;
+  MergeStatesParams mp{};
+  mp.state_out = a->state_out;
+  mp.state_lse = a->state_lse;
+  mp.out = static_cast<uint16_t*>(a->output);
+  mp.out_f32 = a->output_f32;
+  mp.lse = a->lse;
+  mp.rows = a->num_rows;
+  mp.states = a->num_states;
+  mp.head_size = a->head_size;
+  if (launch_merge_states(mp, static_cast<hipStream_t>(stream)) != hipSuccess) return PA_ERR_HIP;
   return PA_OK;
 }
 

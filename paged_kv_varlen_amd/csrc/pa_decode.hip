@@ -53,6 +53,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define PA_GLOBAL __attribute__((address_space(1)))
 
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLn2 = 0.6931471805599453f;  // natural log of 2 (lse in base e)
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -531,7 +532,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnParams p) {
       const float inv = 1.f / lt;
       if (fl & kComplete) {  // whole segment here: the final fp16 output
         if (n < nh_c) {
-          uint16_t* o = p.out + (static_cast<int64_t>(t_c) * p.num_heads + h0_c + n) * D + 4 * g;
+          const int64_t row = static_cast<int64_t>(t_c) * p.num_heads + h0_c + n;
+          uint16_t* o = p.out + row * D + 4 * g;
 #pragma unroll
           for (int blk = 0; blk < DB; ++blk) {
             half4_t hv;
@@ -539,6 +541,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnParams p) {
             for (int e = 0; e < 4; ++e) hv[e] = static_cast<_Float16>(acc[blk][e] * inv);
             *reinterpret_cast<half4_t*>(o + 16 * blk) = hv;
           }
+          // optional partial state: fp32 output and natural-log lse
+          if (p.out_f32 != nullptr) {
+#pragma unroll
+            for (int blk = 0; blk < DB; ++blk)
+              *reinterpret_cast<f32x4_t*>(p.out_f32 + row * D + 4 * g + 16 * blk) = acc[blk] * inv;
+          }
+          if (p.lse_out != nullptr && g == 0) p.lse_out[row] = (m + __log2f(lt)) * kLn2;
         }
       } else if (n < nh_c) {  // a piece: partial (o, lse) in the wave's slot
         const int ps = 2 * w + ((fl & kSecond) ? 1 : 0);

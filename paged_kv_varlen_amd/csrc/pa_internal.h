@@ -160,6 +160,20 @@ struct AttnParams {
   int32_t decode_waves;        // W
   int32_t prefill_positions;
   float scale_log2;            // scale * log2(e)
+  float* lse_out;              // [N, H] natural-log lse, or null
+  float* out_f32;              // [N, H*D] output before rounding, or null
+};
+
+// fixed-order merge of partial states (pa_merge_states)
+struct MergeStatesParams {
+  const float* state_out;      // [P, R, D]
+  const float* state_lse;      // [P, R]
+  uint16_t* out;               // [R, D] fp16, or null
+  float* out_f32;              // [R, D], or null
+  float* lse;                  // [R], or null
+  int64_t rows;
+  int32_t states;
+  int32_t head_size;
 };
 
 // ---- launchers (defined in the .hip files) ---------------------------------
@@ -167,5 +181,6 @@ hipError_t launch_scatter_plan(const ScatterPlanParams& p, hipStream_t s);
 hipError_t launch_decode(const AttnParams& p, int head_size, int head_slots, int grid, hipStream_t s);
 hipError_t launch_prefill(const AttnParams& p, int head_size, int grid, hipStream_t s);
 size_t prefill_lds_bytes(int head_size);
+hipError_t launch_merge_states(const MergeStatesParams& p, hipStream_t s);
 
 }  // namespace pa

@@ -68,7 +68,16 @@ __device__ inline void merge_segment(const AttnParams& p, int task, int T, int l
   }
   const float inv = 1.f / wsum;
   const int h = kvh * p.group + kDecodeUnitHeads * hc + hn;
-  uint16_t* out = p.out + (static_cast<int64_t>(sq.y) * p.num_heads + h) * D + E * qd;
+  const int64_t row = static_cast<int64_t>(sq.y) * p.num_heads + h;
+  // optional partial state of the whole row: fp32 output and natural-log lse
+  if (p.out_f32 != nullptr) {
+    float4* of = reinterpret_cast<float4*>(p.out_f32 + row * D + E * qd);
+#pragma unroll
+    for (int e = 0; e < E / 4; ++e)
+      of[e] = make_float4(o[4 * e] * inv, o[4 * e + 1] * inv, o[4 * e + 2] * inv, o[4 * e + 3] * inv);
+  }
+  if (p.lse_out != nullptr && qd == 0) p.lse_out[row] = (M + __log2f(wsum)) * 0.6931471805599453f;
+  uint16_t* out = p.out + row * D + E * qd;
 #pragma unroll
   for (int e = 0; e < E; e += 4) {
     uint32_t w2[2];

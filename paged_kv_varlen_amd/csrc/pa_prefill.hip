@@ -497,24 +497,31 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
       const float lt = swap_halves_sum(l * a0 + l1 * a1);
       const float inv = 1.f / lt;
       if (row_valid) {
-        uint16_t* orow = p.out + static_cast<int64_t>(t0 + i0 + pos_local) * out_stride +
-                         static_cast<int64_t>(head) * D;
+        const int64_t tok = t0 + i0 + pos_local;
+        // optional partial state: natural-log lse (both lane halves hold it)
+        if (p.lse_out != nullptr && lhalf == 0)
+          p.lse_out[tok * p.num_heads + head] = (mm + __log2f(lt)) * 0.6931471805599453f;
+        float* orow_f = p.out_f32 == nullptr ? nullptr : p.out_f32 + tok * out_stride + static_cast<int64_t>(head) * D;
+        uint16_t* orow = p.out + tok * out_stride + static_cast<int64_t>(head) * D;
         // register i of tile mt is d = 32mt + 8(i/4) + 4*lhalf + i%4
 #pragma unroll
         for (int mt = 0; mt < S::O_TILES; ++mt)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             uint32_t w[2];
+            float v[4];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
               const int ir = 4 * q + 2 * e;
               const float* x1 = &xo[(mt * 16 + ir) * 64 + lane];
-              const float v0 = (o[mt][ir] * a0 + x1[0] * a1) * inv;
-              const float v1 = (o[mt][ir + 1] * a0 + x1[64] * a1) * inv;
-              w[e] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(v0))) |
-                     (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(v1))) << 16);
+              v[2 * e] = (o[mt][ir] * a0 + x1[0] * a1) * inv;
+              v[2 * e + 1] = (o[mt][ir + 1] * a0 + x1[64] * a1) * inv;
+              w[e] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(v[2 * e]))) |
+                     (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(v[2 * e + 1]))) << 16);
             }
             *reinterpret_cast<uint2*>(orow + 32 * mt + 8 * q + 4 * lhalf) = make_uint2(w[0], w[1]);
+            if (orow_f != nullptr)
+              *reinterpret_cast<float4*>(orow_f + 32 * mt + 8 * q + 4 * lhalf) = make_float4(v[0], v[1], v[2], v[3]);
           }
       }
     }

@@ -34,7 +34,7 @@ def test_exports_every_declared_function():
     lib = pa.library()
     names = declared_functions()
     assert set(names) == {"pa_paged_attention", "pa_workspace_bytes", "pa_status_string",
-                          "pa_abi_version"}
+                          "pa_abi_version", "pa_merge_states"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", pa.library_path], capture_output=True,
@@ -43,15 +43,16 @@ def test_exports_every_declared_function():
     assert set(names) <= exported
 
 
-def test_struct_layout_matches_c(tmp_path):
-    fields = [f for f, _ in pa.PaArgs._fields_]
+@pytest.mark.parametrize("cls,cname", [(pa.PaArgs, "pa_args"), (pa.PaMergeArgs, "pa_merge_args")])
+def test_struct_layout_matches_c(tmp_path, cls, cname):
+    fields = [f for f, _ in cls._fields_]
     src = tmp_path / "layout.c"
-    body = "\n".join(f'  printf("{f} %zu\\n", offsetof(pa_args, {f}));' for f in fields)
+    body = "\n".join(f'  printf("{f} %zu\\n", offsetof({cname}, {f}));' for f in fields)
     src.write_text(f"""#include <stdio.h>
 #include <stddef.h>
 #include "pagedattn.h"
 int main(void) {{
-  printf("sizeof %zu\\n", sizeof(pa_args));
+  printf("sizeof %zu\\n", sizeof({cname}));
 {body}
   return 0;
 }}
@@ -61,9 +62,9 @@ int main(void) {{
                     str(src), "-o", str(exe)], check=True)
     got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True,
                                                          text=True, check=True).stdout.splitlines())
-    assert int(got["sizeof"]) == ctypes.sizeof(pa.PaArgs)
+    assert int(got["sizeof"]) == ctypes.sizeof(cls)
     for f in fields:
-        assert int(got[f]) == getattr(pa.PaArgs, f).offset, f
+        assert int(got[f]) == getattr(cls, f).offset, f
 
 
 FAKE = 1 << 20  # an aligned, never-dereferenced address
@@ -121,6 +122,9 @@ def test_workspace_bytes_static_bound():
     (dict(output=None), NULL),
     (dict(query=FAKE + 2), ALIGN),
     (dict(key_cache=FAKE + 8), ALIGN),
+    (dict(lse=FAKE + 2), ALIGN),                         # lse needs 4-byte alignment
+    (dict(output_f32=FAKE + 4), ALIGN),                  # output_f32 needs 16
+    (dict(lse=FAKE, output_f32=FAKE), WS),               # both present and aligned
     (dict(num_tokens=0, batch_size=2), OK),              # nothing to do: no device work
 ])
 def test_host_validation(case, expect):
@@ -150,4 +154,38 @@ def test_status_strings():
     lib = pa.library()
     for s in range(9):
         assert lib.pa_status_string(s)
-    assert lib.pa_abi_version() == 1
+    assert lib.pa_abi_version() == 2
+
+
+def merge_args(**kw):
+    a = pa.PaMergeArgs()
+    a.struct_size = ctypes.sizeof(pa.PaMergeArgs)
+    a.dtype = 1
+    a.num_states, a.head_size, a.num_rows = 3, 128, 10
+    a.state_out = a.state_lse = a.output = FAKE
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(struct_size=8), ABI),
+    (dict(num_states=0), SHAPE),
+    (dict(num_rows=-1), SHAPE),
+    (dict(head_size=0), SHAPE),
+    (dict(head_size=6), UNSUP),                          # not a multiple of 4
+    (dict(head_size=1024), UNSUP),
+    (dict(dtype=0), UNSUP),
+    (dict(state_out=None), NULL),
+    (dict(state_lse=None), NULL),
+    (dict(state_out=FAKE + 4), ALIGN),
+    (dict(output_f32=FAKE + 8), ALIGN),
+    (dict(num_rows=0), OK),                              # no rows: no device work
+])
+def test_merge_host_validation(case, expect):
+    a = merge_args(**case)
+    assert pa.library().pa_merge_states(ctypes.byref(a), None) == expect
+
+
+def test_merge_null_args_pointer():
+    assert pa.library().pa_merge_states(None, None) == NULL

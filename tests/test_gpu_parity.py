@@ -276,3 +276,85 @@ def test_hip_graph_replay_matches_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+# ------------------------------------------------------------------ partial states: lse export and merge
+
+# lse tolerance: P is rounded to fp16 before it is summed (relative error at
+# most 2^-11 per weight), so log(sum) is off by at most about 2^-11 = 4.9e-4
+# in natural-log units; fp32 score and sum rounding add ~1e-6.
+LSE_TOL = 1e-3
+
+
+def rounding_of(f32, f16):
+    """f16 is a nearest fp16 value of f32 elementwise.  The packed fp32->fp16
+    conversion of gfx950 (v_cvt_pk_f16_f32) may break an exact tie away from
+    the even neighbour, where numpy rounds to even; both are nearest."""
+    r = f32.astype(np.float16)
+    diff = r.view(np.uint16) != f16.view(np.uint16)
+    x = f32.astype(np.float64)
+    tie = np.abs(x - r.astype(np.float64)) == np.abs(x - f16.astype(np.float64))
+    if np.any(diff & ~tie):
+        i = np.argwhere(diff & ~tie)[0]
+        say(f"      not a rounding at {tuple(i)}: f32 {f32[tuple(i)]!r} f16 {f16[tuple(i)]!r}")
+    say(f"      fp16 output == rounding of fp32 output ({int(np.sum(diff))} ties broken the other way)")
+    return not np.any(diff & ~tie)
+
+
+@pytest.mark.parametrize("name", ["tiny", "sweep0", "long_decode", "mixed"])
+def test_lse_and_fp32_output(name):
+    if name == "tiny":
+        b = W.tiny(0)
+    elif name == "sweep0":
+        q, p, H, Hkv, D, bs = SWEEP[0]
+        b = W.make_batch(q, p, num_heads=H, kv_num_heads=Hkv, head_size=D, block_size=bs,
+                         seed=100, name="sweep0")
+    elif name == "long_decode":  # decode segments cut across waves: merged states
+        b = W.make_batch([1, 1, 1, 2], [16383, 9000, 511, 12000], num_heads=32, kv_num_heads=8,
+                         head_size=128, block_size=256, seed=12, name="long_decode")
+    else:
+        b = W.mixed(0)
+    say(f"[gpu] lse {b.name} N={b.num_tokens} B={b.batch_size}")
+    d = DevBatch(b)
+    f32 = torch.empty((b.num_tokens, b.num_heads * b.head_size), dtype=torch.float32, device=DEV)
+    out, lse = d.run(return_lse=True, output_f32=f32)
+    torch.cuda.synchronize()
+    rows = None if b.num_tokens <= 64 else sample_rows(b, per_seq=4, seed=5)
+    ref, _, _, rlse = oracle.paged_attention(b.query, b.key, b.value, b.key_cache, b.value_cache,
+                                             b.cum, b.past, b.block_table, b.slot_mapping,
+                                             num_heads=b.num_heads, kv_num_heads=b.kv_num_heads,
+                                             scale=b.scale, rows=rows, with_lse=True)
+    sel = np.arange(b.num_tokens) if rows is None else rows
+    o16, o32, l32 = out.cpu().numpy(), f32.cpu().numpy(), lse.cpu().numpy()
+    assert rounding_of(o32, o16)
+    e_o = np.max(np.abs(o32[sel].astype(np.float64) - ref[sel]))
+    e_l = np.max(np.abs(l32[sel].astype(np.float64) - rlse[sel]))
+    say(f"      rows {sel.size}: max|err| out_f32 {e_o:.3e}, lse {e_l:.3e}")
+    assert e_o <= TOL and e_l <= LSE_TOL
+
+
+@pytest.mark.parametrize("P,R,D", [(1, 37, 128), (3, 1000, 128), (5, 777, 64), (2, 4096, 256)])
+def test_merge_states(P, R, D):
+    rng = np.random.default_rng(P * 1000 + R)
+    outs = rng.standard_normal((P, R, D)).astype(np.float32)
+    lses = (rng.standard_normal((P, R)) * 4).astype(np.float32)
+    lses[rng.random((P, R)) < 0.2] = -np.inf      # empty states
+    lses[:, :3] = -np.inf                           # rows with no keys at all
+    ref_o, ref_l = oracle.merge_states(outs, lses)
+    so, sl = torch.from_numpy(outs).to(DEV), torch.from_numpy(lses).to(DEV)
+    f32 = torch.empty((R, D), dtype=torch.float32, device=DEV)
+    o16, l32 = pa.merge_states(so, sl, output_f32=f32)
+    o16b, l32b = pa.merge_states(so, sl)
+    torch.cuda.synchronize()
+    o16, o32, l32 = o16.cpu().numpy(), f32.cpu().numpy(), l32.cpu().numpy()
+    assert np.array_equal(o16.view(np.uint16), o16b.cpu().numpy().view(np.uint16))   # deterministic
+    assert np.array_equal(l32.view(np.uint32), l32b.cpu().numpy().view(np.uint32))
+    assert rounding_of(o32, o16)
+    fin = np.isfinite(ref_l)
+    assert np.all(o32[~fin] == 0) and np.all(l32[~fin] == -np.inf)
+    # fp32 sequential merge of O(1) states: relative rounding ~P * 2^-24
+    e_o = np.max(np.abs(o32 - ref_o) / (1.0 + np.abs(ref_o)))
+    e_l = np.max(np.abs(l32[fin] - ref_l[fin]) / (1.0 + np.abs(ref_l[fin])))
+    say(f"[gpu] merge P={P} R={R} D={D}: max rel err out {e_o:.2e}, lse {e_l:.2e}")
+    assert e_o <= 1e-5 and e_l <= 1e-6
+    assert np.max(np.abs(o16.astype(np.float64) - ref_o)) <= TOL * (1 + np.abs(ref_o).max())

@@ -18,6 +18,12 @@ Measured:
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
                 workload, in the same unit
   also          the other workloads' step times, TFLOP/s, GB/s, tokens/s
+
+A prefill roofline also carries "measured_ceiling": the dense matrix-core rate
+that paged_kv_varlen_amd/probe_mfma_rate reaches on random unit-variance fp16
+operands (the distribution the workloads draw from), run once before the
+timed work.  Under that load the chip lowers its clock to stay in its power
+limit, so this rate sits well below the published peak that "frac" uses.
 """
 from __future__ import annotations
 
@@ -25,6 +31,8 @@ import argparse
 import hashlib
 import json
 import os
+import re
+import subprocess
 import sys
 import time
 
@@ -194,6 +202,28 @@ def summarize(name, b, work, ms, kernel_ms):
     return out
 
 
+PROBE = os.path.join(ROOT, "paged_kv_varlen_amd", "probe_mfma_rate")
+
+
+def mfma_ceiling():
+    """Run the matrix-core rate probe in a child process (before this process
+    touches the GPU); returns (TFLOP/s on random unit-variance operands at 8
+    waves per CU, the probe's output), or (None, reason)."""
+    if not os.access(PROBE, os.X_OK):
+        return None, "probe not built"
+    try:
+        res = subprocess.run([PROBE], capture_output=True, text=True, timeout=120)
+    except subprocess.TimeoutExpired:
+        return None, "probe timed out"
+    if res.returncode != 0:
+        return None, res.stderr.strip()[-200:]
+    m = re.search(r"random, unit variance\s+8 waves/CU:.*?([0-9.]+) TFLOP/s", res.stdout)
+    return (float(m.group(1)) if m else None), res.stdout
+
+
+CEILING = {"value": None}  # filled by main()
+
+
 def roofline(name, work, kernel_ms):
     """Dominant kernel: decode (bytes) unless prefill flops dominate."""
     dec_t, pf_t = kernel_ms["decode"] / 1e3, kernel_ms["prefill"] / 1e3
@@ -204,7 +234,11 @@ def roofline(name, work, kernel_ms):
                 "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic,
                 "kernel_us": round(kernel_ms["prefill"] * 1e3, 2),
-                "work_per_launch": work["prefill_flops"]}
+                "work_per_launch": work["prefill_flops"],
+                "measured_ceiling": None if CEILING["value"] is None else {
+                    "value": CEILING["value"], "unit": "TFLOP/s",
+                    "operands": "random fp16, unit variance (probe_mfma_rate)",
+                    "frac": round(achieved / CEILING["value"], 4)}}
     achieved = work["decode_kv_hist_bytes"] / dec_t / 1e9
     traffic = measured_traffic("decode", name)
     return {"kernel": "decode", "bound": "hbm", "achieved": round(achieved, 1),
@@ -277,6 +311,10 @@ def main():
                     help="write profiles/traffic_<kernel>_<workload>.json from rocprofv3 "
                          "counter CSVs (with --traffic-kernel, --workload, --copy-calibration)")
     ap.add_argument("--traffic-kernel", default="decode", choices=sorted(KERNEL_SYMBOL))
+    ap.add_argument("--mfma-rate", action="store_true",
+                    help="only run the matrix-core rate probe and print its table")
+    ap.add_argument("--no-mfma-rate", action="store_true",
+                    help="skip the probe run (prefill rooflines then carry no measured ceiling)")
     args = ap.parse_args()
 
     if args.traffic_from:
@@ -288,6 +326,15 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU mode in this build)", file=sys.stderr)
         sys.exit(2)
+
+    if args.mfma_rate:
+        rate, text = mfma_ceiling()
+        print(text, end="" if text.endswith("\n") else "\n", flush=True)
+        sys.exit(0 if rate is not None else 1)
+    if not args.no_mfma_rate:
+        CEILING["value"], text = mfma_ceiling()
+        log(f"matrix-core rate on random operands: {CEILING['value']} TFLOP/s"
+            + ("" if CEILING["value"] is not None else f" ({text})"))
 
     import torch
     import paged_kv_varlen_amd as pa

@@ -30,4 +30,5 @@ from .paged_attention import (  # noqa: F401
     merge_partials,
     merge_states,
     resolve_call,
+    values,
 )

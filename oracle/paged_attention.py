@@ -29,8 +29,10 @@ reason in the design notes of the repository):
   * Slot writes are applied in token order (two tokens naming one slot is
     outside the contract, so the order only makes the oracle definite).
 
-All floating point is fp64; the caches returned are fp16 with their bits
-copied, never converted.
+All floating point is fp64; the caches returned hold the input bits copied,
+never converted.  Data tensors are fp16 (numpy float16) or bf16 (numpy uint16
+arrays of bfloat16 bit patterns, since numpy has no bfloat16); ``values``
+turns either into fp64 exactly.
 """
 from __future__ import annotations
 
@@ -40,6 +42,18 @@ from typing import Optional, Sequence
 import numpy as np
 
 
+def values(x: np.ndarray) -> np.ndarray:
+    """Exact fp64 values of a data tensor: float16 as is; uint16 as bfloat16
+    bit patterns, which are the upper 16 bits of an IEEE binary32 (the lower
+    16 are zero), so widening the pattern gives the number exactly."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if x.dtype != np.float16:
+        raise TypeError("data tensors are float16, or uint16 holding bfloat16 bits")
+    return x.astype(np.float64)
+
+
 def resolve_call(query: np.ndarray, key: Optional[np.ndarray], value: Optional[np.ndarray],
                  num_heads: int, kv_num_heads: int, scale: float):
     """Split the query input and fix head_size and scale.
@@ -47,7 +61,7 @@ def resolve_call(query: np.ndarray, key: Optional[np.ndarray], value: Optional[n
     README, Inputs (query, key, value) and Attributes (scale): query is
     [N, H*D], or [N, (H+2*Hkv)*D] carrying [Q|K|V] when key and value are both
     absent; scale == 0 selects 1/sqrt(D).  Returns (Q, K, V, D, scale) with Q
-    [N, H, D], K and V [N, Hkv, D], still fp16.
+    [N, H, D], K and V [N, Hkv, D], still in the input's type.
     """
     if (key is None) != (value is None):
         raise ValueError("key and value must be given together")
@@ -82,7 +96,7 @@ def scatter_kv(key_cache: np.ndarray, value_cache: np.ndarray, K: np.ndarray, V:
     block_id*block_size + offset; -1 suppresses the write; without
     slot_mapping the slot follows from past_seqlens (token i of sequence b is
     at position past_b + i, found through block_table).  The copy is bit
-    exact: fp16 in, fp16 out.
+    exact: the stored bits are the input's bits.
     """
     kc = key_cache.copy()
     vc = value_cache.copy()
@@ -112,8 +126,8 @@ def gather_history(kc: np.ndarray, vc: np.ndarray, block_table: np.ndarray, b: i
     NB, bs, Hkv, D = kc.shape
     j = np.arange(int(length), dtype=np.int64)
     idx = block_table[b, j // bs].astype(np.int64) * bs + j % bs
-    Kb = kc.reshape(NB * bs, Hkv, D)[idx].astype(np.float64)
-    Vb = vc.reshape(NB * bs, Hkv, D)[idx].astype(np.float64)
+    Kb = values(kc.reshape(NB * bs, Hkv, D)[idx])
+    Vb = values(vc.reshape(NB * bs, Hkv, D)[idx])
     return Kb, Vb
 
 
@@ -189,7 +203,7 @@ def paged_attention(query, key, value, key_cache, value_cache, cum, past, block_
                 continue
         L = int(past[b]) + (t1 - t0)
         Kb, Vb = gather_history(kc, vc, block_table, b, L)
-        Qb = Q[t0:t1].astype(np.float64)
+        Qb = values(Q[t0:t1])
         if with_lse:
             out[t0:t1], lse[t0:t1] = attend_sequence(Qb, Kb, Vb, int(past[b]), s, rows=local,
                                                      with_lse=True)

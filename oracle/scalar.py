@@ -1,8 +1,9 @@
 """Second oracle formulation in plain Python scalars (test infrastructure only).
 
 Independent of paged_attention.py: no numpy arithmetic, no array gathers.  The
-cache is modelled as a dict from flat slot to a per-head list of fp16 values
-(as Python floats); each output element is a sum over visible keys taken with
+cache is modelled as a dict from flat slot to a per-head list of element
+values (as Python floats: fp16 values, or bf16 values decoded from their bit
+patterns with struct); each output element is a sum over visible keys taken with
 math.fsum.  Used only on tiny inputs to pin the numpy oracle (same operator:
 model-card README "com.microsoft.PagedAttention", Description and Inputs;
 causal offsets and GQA grouping as read from "WS2 CP-Aware Attention
@@ -11,10 +12,19 @@ Contract").
 from __future__ import annotations
 
 import math
+import struct
+
+
+def _num(x) -> float:
+    """Value of one element: a float16 as is; a uint16 as a bfloat16 bit
+    pattern, i.e. the upper half of an IEEE binary32 whose lower half is 0."""
+    if getattr(x, "dtype", None) is not None and x.dtype.kind == "u":
+        return struct.unpack("<f", struct.pack("<I", int(x) << 16))[0]
+    return float(x)
 
 
 def _row(arr, t, start, count):
-    return [float(x) for x in arr[t][start:start + count]]
+    return [_num(x) for x in arr[t][start:start + count]]
 
 
 def paged_attention_scalar(query, key, value, key_cache, value_cache, cum, past,
@@ -62,7 +72,7 @@ def paged_attention_scalar(query, key, value, key_cache, value_cache, cum, past,
             return written[slot][which]
         blk, off = divmod(slot, bs)
         src = key_cache if which == 0 else value_cache
-        return [float(x) for x in src[blk][off].reshape(-1)]
+        return [_num(x) for x in src[blk][off].reshape(-1)]
 
     out = []
     lse = []

@@ -619,3 +619,114 @@ def test_merge_pins_catch_planted_mistakes(mutant):
 def test_lse_pins_catch_planted_mistakes(mutant):
     with pytest.raises(AssertionError):
         check_L(mutant)
+
+
+# ------------------------------------------------------------------ bf16 data
+
+# bf16 tensors travel as uint16 bit patterns (numpy has no bfloat16); the
+# oracle decodes them exactly ("values").  Pins:
+#   B1  hand-decoded bit patterns (closed forms of the binary32 layout);
+#   B2  one contiguous bf16 sequence == torch's scaled_dot_product_attention
+#       on torch's own bf16 -> float64 conversion of the same bits;
+#   B3  the bf16 cache writes are bit copies (slot -1 untouched, every other
+#       slot equal to its token's row) and the scalar formulation, which
+#       decodes bits with struct, agrees within 1e-12.
+
+def check_B1(values):
+    bits = np.array([0x3F80, 0xC000, 0x3F81, 0x0001, 0x7F7F, 0x8000, 0x4049], dtype=np.uint16)
+    want = [1.0, -2.0, 1.0 + 2.0 ** -7, 2.0 ** -133, (2.0 - 2.0 ** -7) * 2.0 ** 127, -0.0,
+            3.140625]
+    got = values(bits)
+    assert got.dtype == np.float64
+    assert [float(x) for x in got] == want
+    assert np.signbit(got[5])
+    h = np.array([1.5, -0.25, 65504.0], dtype=np.float16)
+    assert [float(x) for x in values(h)] == [1.5, -0.25, 65504.0]
+
+
+def check_B2(fn):
+    rng = np.random.default_rng(21)
+    H, Hkv, D, p, q, bs = 4, 2, 16, 9, 6, 4
+    L = p + q
+    nb = W.pages_needed(L, bs)
+    table = np.arange(nb, dtype=np.int32)[None, :]
+    kc = W.normal_bf16(rng, (nb, bs, Hkv, D))
+    vc = W.normal_bf16(rng, (nb, bs, Hkv, D))
+    Q = W.normal_bf16(rng, (q, H * D))
+    K = W.normal_bf16(rng, (q, Hkv * D))
+    V = W.normal_bf16(rng, (q, Hkv * D))
+    scale = -0.29
+    o, _, _ = fn(Q, K, V, kc, vc, np.array([0, q], np.int32), np.array([p], np.int32), table,
+                 None, num_heads=H, kv_num_heads=Hkv, scale=scale)
+
+    def t64(x):  # torch's own bf16 decode
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).double()
+    kf = t64(kc.reshape(-1, Hkv, D)[:L]).clone()
+    vf = t64(vc.reshape(-1, Hkv, D)[:L]).clone()
+    kf[p:] = t64(K.reshape(q, Hkv, D))
+    vf[p:] = t64(V.reshape(q, Hkv, D))
+    G = H // Hkv
+    qt = t64(Q.reshape(q, H, D)).permute(1, 0, 2)
+    kt = kf.permute(1, 0, 2).repeat_interleave(G, dim=0)
+    vt = vf.permute(1, 0, 2).repeat_interleave(G, dim=0)
+    allow = torch.ones(q, L, dtype=torch.bool).tril(diagonal=p)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=allow,
+                                                           scale=scale)
+    ref = ref.permute(1, 0, 2).reshape(q, H * D).numpy()
+    assert np.max(np.abs(o - ref)) < 1e-12
+
+
+def check_B3(fn):
+    b = small(seed=23, slot_mode="drop", drop_count=3, dtype="bf16")
+    o, kc, vc = call(fn, b)
+    assert kc.dtype == np.uint16 and vc.dtype == np.uint16
+    slots = W.allocator_slots(b.block_table, b.past, b.q_lens, b.block_size)
+    NB, bs, Hkv, D = b.key_cache.shape
+    before_k = b.key_cache.reshape(NB * bs, Hkv * D)
+    after_k = kc.reshape(NB * bs, Hkv * D)
+    after_v = vc.reshape(NB * bs, Hkv * D)
+    dropped = np.nonzero(b.slot_mapping < 0)[0]
+    for t in range(b.num_tokens):
+        s = int(slots[t])
+        if t in dropped:
+            assert np.array_equal(after_k[s], before_k[s])
+        else:
+            assert np.array_equal(after_k[s], b.key[t]) and np.array_equal(after_v[s], b.value[t])
+    for case in (W.tiny(0, dtype="bf16"), small(seed=24, head_size=4, packed=True, dtype="bf16")):
+        oo, _, _ = call(fn, case)
+        so, _ = scalar.paged_attention_scalar(case.query, case.key, case.value, case.key_cache,
+                                              case.value_cache, case.cum, case.past,
+                                              case.block_table, case.slot_mapping,
+                                              case.num_heads, case.kv_num_heads, case.scale)
+        assert np.max(np.abs(oo - np.array(so))) < 1e-12
+
+
+def test_oracle_bf16_pins():
+    check_B1(oracle.values)
+    check_B2(oracle.paged_attention)
+    check_B3(oracle.paged_attention)
+
+
+def _values_as_f16(x):
+    x = np.asarray(x)
+    return x.view(np.float16).astype(np.float64) if x.dtype == np.uint16 else x.astype(np.float64)
+
+
+def _values_shift15(x):
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+@pytest.mark.parametrize("mutant", [_values_as_f16, _values_shift15], ids=lambda f: f.__name__)
+def test_bf16_pins_catch_planted_mistakes(mutant):
+    with pytest.raises(AssertionError):
+        check_B1(mutant)
+    saved = pa_mod.values
+    pa_mod.values = mutant
+    try:
+        with pytest.raises(AssertionError):
+            check_B2(oracle.paged_attention)
+    finally:
+        pa_mod.values = saved

@@ -1,7 +1,7 @@
 """Seeded synthetic inputs for the paged KV-cache attention path.
 
 This module only *builds inputs*: lengths, page tables, page-id permutations,
-fp16 N(0,1) tensors and the slot list a page allocator hands out.  It holds no
+N(0,1) tensors in fp16 or bf16 and the slot list a page allocator hands out.  It holds no
 attention arithmetic (no scatter, gather, softmax or merge), so both the oracle
 tests and the HIP path can draw their inputs from it without sharing any of the
 method's computation.
@@ -25,8 +25,13 @@ Draw order for one batch (fixed so that a seed names one input exactly):
   1. per-sequence new-token counts (order permutation), 2. past lengths,
   3. physical page permutation, 4. slot_mapping entries switched to -1,
   5. query / key / value (or packed query), 6. key_cache, 7. value_cache.
-With ``meta_only=True`` the draws stop after step 4 and the fp16 tensors are
+With ``meta_only=True`` the draws stop after step 4 and the data tensors are
 left uninitialised (only their shapes are meaningful).
+
+Data type: every workload takes ``dtype`` "f16" (default) or "bf16".  The
+float32 draws are the same for both; they are rounded to nearest (ties to
+even) to the type.  numpy has no bfloat16, so bf16 tensors are numpy uint16
+arrays holding the bit patterns (the upper half of the float32 pattern).
 """
 from __future__ import annotations
 
@@ -47,6 +52,29 @@ def normal_f16(rng: np.random.Generator, shape) -> np.ndarray:
         e = min(flat.size, s + _CHUNK)
         flat[s:e] = rng.standard_normal(e - s, dtype=np.float32)
     return out
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """float32 (finite) -> bfloat16 bit patterns as uint16, round to nearest,
+    ties to even."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+
+
+def normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
+    """N(0,1) bf16 tensor (uint16 bit patterns), same float32 draws as
+    normal_f16."""
+    out = np.empty(shape, dtype=np.uint16)
+    flat = out.reshape(-1)
+    for s in range(0, flat.size, _CHUNK):
+        e = min(flat.size, s + _CHUNK)
+        flat[s:e] = round_bf16(rng.standard_normal(e - s, dtype=np.float32))
+    return out
+
+
+def storage_dtype(dtype: str):
+    """numpy dtype that holds tensors of data type ``dtype``."""
+    return {"f16": np.float16, "bf16": np.uint16}[dtype]
 
 
 @dataclasses.dataclass
@@ -70,6 +98,7 @@ class Batch:
     block_size: int
     scale: float = 0.0
     note: str = ""
+    dtype: str = "f16"                # "f16" (float16 arrays) or "bf16" (uint16 bit patterns)
 
     @property
     def num_tokens(self) -> int:
@@ -198,7 +227,7 @@ def make_batch(q_lens: Sequence[int], past_lens: Sequence[int], *, num_heads: in
                slot_mode: Optional[str] = None, drop_count: int = 0,
                num_blocks: Optional[int] = None, max_blocks: Optional[int] = None,
                shared_prefix: Optional[Sequence[int]] = None, scale: float = 0.0,
-               name: str = "custom", note: str = "") -> Batch:
+               name: str = "custom", note: str = "", dtype: str = "f16") -> Batch:
     """Build one batch.  ``slot_mode``: None (omit slot_mapping), "derived"
     (allocator slots), or "drop" (allocator slots with ``drop_count`` entries
     set to -1, chosen by ``rng.choice(N, drop_count, replace=False)``)."""
@@ -209,11 +238,11 @@ def make_batch(q_lens: Sequence[int], past_lens: Sequence[int], *, num_heads: in
     table, nb, _ = allocate_pages(rng, kv, block_size, num_blocks=num_blocks,
                                   max_blocks=max_blocks, shared_prefix=shared_prefix)
     return _fill(rng, name, seed, q_lens, past, table, nb, num_heads, kv_num_heads,
-                 head_size, block_size, packed, slot_mode, drop_count, scale, note)
+                 head_size, block_size, packed, slot_mode, drop_count, scale, note, dtype=dtype)
 
 
 def _fill(rng, name, seed, q_lens, past, table, nb, H, Hkv, D, bs, packed, slot_mode,
-          drop_count, scale, note, meta_only=False) -> Batch:
+          drop_count, scale, note, meta_only=False, dtype="f16") -> Batch:
     cum = cum_from_lens(q_lens)
     N = int(cum[-1])
     slots = None
@@ -224,8 +253,9 @@ def _fill(rng, name, seed, q_lens, past, table, nb, H, Hkv, D, bs, packed, slot_
             slots[idx] = -1
         elif slot_mode not in ("derived", "drop"):
             raise ValueError(slot_mode)
-    draw = (lambda shape: np.empty(shape, np.float16)) if meta_only else \
-        (lambda shape: normal_f16(rng, shape))
+    normal = {"f16": normal_f16, "bf16": normal_bf16}[dtype]
+    draw = (lambda shape: np.empty(shape, storage_dtype(dtype))) if meta_only else \
+        (lambda shape: normal(rng, shape))
     if packed:
         query = draw((N, (H + 2 * Hkv) * D))
         key = value = None
@@ -239,14 +269,14 @@ def _fill(rng, name, seed, q_lens, past, table, nb, H, Hkv, D, bs, packed, slot_
                  key_cache=key_cache, value_cache=value_cache, cum=cum,
                  past=past.astype(np.int32), block_table=table, slot_mapping=slots,
                  num_heads=H, kv_num_heads=Hkv, head_size=D, block_size=bs,
-                 scale=float(scale), note=note)
+                 scale=float(scale), note=note, dtype=dtype)
 
 
 # ---------------------------------------------------------------------------
 # the five named workloads
 # ---------------------------------------------------------------------------
 
-def tiny(seed: int = 0, meta_only: bool = False) -> Batch:
+def tiny(seed: int = 0, meta_only: bool = False, dtype: str = "f16") -> Batch:
     """B=2, H/Hkv=4/2, D=64, block_size 16, 8 pages, past [5,20], new [3,1];
     block_table is a random permutation of all 8 pages, no slot_mapping."""
     rng = np.random.default_rng(seed)
@@ -254,10 +284,10 @@ def tiny(seed: int = 0, meta_only: bool = False) -> Batch:
     past = np.array([5, 20])
     table = rng.permutation(8).astype(np.int32).reshape(2, 4)
     return _fill(rng, "tiny", seed, q_lens, past, table, 8, 4, 2, 64, 16, False, None,
-                 0, 0.0, "B=2 4/2 heads D=64 bs=16 NB=8 past=[5,20] q=[3,1]", meta_only)
+                 0, 0.0, "B=2 4/2 heads D=64 bs=16 NB=8 past=[5,20] q=[3,1]", meta_only, dtype)
 
 
-def pure_decode(seed: int = 0, meta_only: bool = False) -> Batch:
+def pure_decode(seed: int = 0, meta_only: bool = False, dtype: str = "f16") -> Batch:
     """B=64 single-token decodes, past ~ U[512,4096], 32/8 heads, D=128,
     block_size 16, pool sized to fit, shuffled page ids."""
     rng = np.random.default_rng(seed)
@@ -265,10 +295,10 @@ def pure_decode(seed: int = 0, meta_only: bool = False) -> Batch:
     past = rng.integers(512, 4096 + 1, size=64)
     table, nb, _ = allocate_pages(rng, past + q_lens, 16)
     return _fill(rng, "pure_decode", seed, q_lens, past, table, nb, 32, 8, 128, 16, False,
-                 None, 0, 0.0, "B=64 q=1 past~U[512,4096] 32/8 D=128 bs=16", meta_only)
+                 None, 0, 0.0, "B=64 q=1 past~U[512,4096] 32/8 D=128 bs=16", meta_only, dtype)
 
 
-def mixed(seed: int = 0, meta_only: bool = False) -> Batch:
+def mixed(seed: int = 0, meta_only: bool = False, dtype: str = "f16") -> Batch:
     """B=16: 8 decodes + 8 chunks of 512 new tokens (order shuffled), past ~
     U[0,8192], 32/8 heads, D=128, block_size 256, random page table."""
     rng = np.random.default_rng(seed)
@@ -276,10 +306,10 @@ def mixed(seed: int = 0, meta_only: bool = False) -> Batch:
     past = rng.integers(0, 8192 + 1, size=16)
     table, nb, _ = allocate_pages(rng, past + q_lens, 256)
     return _fill(rng, "mixed", seed, q_lens, past, table, nb, 32, 8, 128, 256, False, None,
-                 0, 0.0, "B=16 (8x1 + 8x512) past~U[0,8192] 32/8 D=128 bs=256", meta_only)
+                 0, 0.0, "B=16 (8x1 + 8x512) past~U[0,8192] 32/8 D=128 bs=256", meta_only, dtype)
 
 
-def long_prefill(seed: int = 0, meta_only: bool = False) -> Batch:
+def long_prefill(seed: int = 0, meta_only: bool = False, dtype: str = "f16") -> Batch:
     """One sequence, 2048 new tokens on top of 2048 cached (second half of a
     4096-token sequence), 16/4 heads (one of two tensor-parallel ranks of a
     32/8 model), D=128, block_size 256, 16 pages in shuffled order."""
@@ -288,10 +318,10 @@ def long_prefill(seed: int = 0, meta_only: bool = False) -> Batch:
     past = np.array([2048])
     table = rng.permutation(16).astype(np.int32)[None, :]
     return _fill(rng, "long_prefill", seed, q_lens, past, table, 16, 16, 4, 128, 256,
-                 False, None, 0, 0.0, "B=1 q=2048 past=2048 16/4 D=128 bs=256", meta_only)
+                 False, None, 0, 0.0, "B=1 q=2048 past=2048 16/4 D=128 bs=256", meta_only, dtype)
 
 
-def serving(seed: int = 0, meta_only: bool = False) -> Batch:
+def serving(seed: int = 0, meta_only: bool = False, dtype: str = "f16") -> Batch:
     """B=256: 224 decodes + 32 chunks of 128 (order shuffled), past ~
     U[256,16384], 32/8 heads, D=128, block_size 256, 4096 pages, packed
     [Q|K|V] query, explicit slot_mapping with 5% of entries -1.
@@ -318,7 +348,7 @@ def serving(seed: int = 0, meta_only: bool = False) -> Batch:
     return _fill(rng, "serving", seed, q_lens, past, table, nb_, 32, 8, 128, bs, True,
                  "drop", int(round(0.05 * N)), 0.0,
                  "B=256 (224x1 + 32x128) past~U[256,16384] 32/8 D=128 bs=256 NB=4096 "
-                 "packed QKV, slot_mapping 5% -1, groups of 4 share prefix pages", meta_only)
+                 "packed QKV, slot_mapping 5% -1, groups of 4 share prefix pages", meta_only, dtype)
 
 
 WORKLOADS = {
@@ -330,8 +360,8 @@ WORKLOADS = {
 }
 
 
-def workload(name: str, seed: int = 0, meta_only: bool = False) -> Batch:
-    return WORKLOADS[name](seed, meta_only)
+def workload(name: str, seed: int = 0, meta_only: bool = False, dtype: str = "f16") -> Batch:
+    return WORKLOADS[name](seed, meta_only, dtype)
 
 
 # ---------------------------------------------------------------------------

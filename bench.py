@@ -45,8 +45,8 @@ if ROOT not in sys.path:
 METRIC = "decode KV-read GB/s (% HBM peak); prefill TFLOP/s (% MFMA peak); tokens/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
-KERNEL_SRC = {"decode": ("pa_decode.hip", "pa_internal.h"),
-              "prefill": ("pa_prefill.hip", "pa_merge.h", "pa_internal.h"),
+KERNEL_SRC = {"decode": ("pa_decode.hip", "pa_elem.h", "pa_internal.h"),
+              "prefill": ("pa_prefill.hip", "pa_merge.h", "pa_elem.h", "pa_internal.h"),
               "scatter_plan": ("pa_scatter.hip", "pa_internal.h")}
 KERNEL_SYMBOL = {"decode": "decode_kernel", "prefill": "prefill_kernel",
                  "scatter_plan": "scatter_plan_kernel"}
@@ -121,13 +121,19 @@ class Runner:
     def __init__(self, batch, torch, pa):
         self.torch, self.pa, self.b = torch, pa, batch
         dev = "cuda:0"
-        to = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        def to(x):  # uint16 arrays hold bf16 bit patterns
+            if x is None:
+                return None
+            x = np.ascontiguousarray(x)
+            if x.dtype == np.uint16:
+                return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+            return torch.from_numpy(x).to(dev)
         self.q, self.k, self.v = to(batch.query), to(batch.key), to(batch.value)
         self.kc, self.vc = to(batch.key_cache), to(batch.value_cache)
         self.cum, self.past = to(batch.cum), to(batch.past)
         self.table, self.slots = to(batch.block_table), to(batch.slot_mapping)
         D = batch.head_size
-        self.out = torch.empty((batch.num_tokens, batch.num_heads * D), dtype=torch.float16,
+        self.out = torch.empty((batch.num_tokens, batch.num_heads * D), dtype=self.q.dtype,
                                device=dev)
         args = pa.make_args(self.q, self.k, self.v, self.kc, self.vc, self.cum, self.past,
                             self.table, self.slots, self.out, num_heads=batch.num_heads,
@@ -142,9 +148,9 @@ class Runner:
                                 workspace=self.ws, kernel_events=events)
 
 
-def time_workload(name: str, steps: int, warmup: int, seed: int, torch, pa, W):
+def time_workload(name: str, steps: int, warmup: int, seed: int, torch, pa, W, dtype="f16"):
     t_gen = time.perf_counter()
-    b = W.workload(name, seed)
+    b = W.workload(name, seed, dtype=dtype)
     work = W.work(b)
     log(f"[bench] {name}: generated in {time.perf_counter() - t_gen:.1f}s "
         f"(N={b.num_tokens}, B={b.batch_size}, KV {work['kv_hist_bytes'] / 1e9:.3f} GB, "
@@ -256,7 +262,7 @@ def sub_batch(b, seqs, W):
                    cum=W.cum_from_lens(b.q_lens[seqs]), past=b.past[seqs],
                    block_table=b.block_table[seqs], slot_mapping=pick(b.slot_mapping),
                    num_heads=b.num_heads, kv_num_heads=b.kv_num_heads, head_size=b.head_size,
-                   block_size=b.block_size, scale=b.scale)
+                   block_size=b.block_size, scale=b.scale, dtype=b.dtype)
 
 
 def cpu_baseline(b, W, target_s: float):
@@ -302,6 +308,8 @@ def main():
     ap.add_argument("--also", default="mixed,long_prefill",
                     help="comma list of other workloads to time (empty for none)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--dtype", default="f16", choices=("f16", "bf16"),
+                    help="data type of the workloads (the line's dtype field)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -357,12 +365,12 @@ def main():
     pa.library()  # fail loudly if the HIP library is missing
 
     b, work, ms, wall_ms, kms = time_workload(args.workload, args.steps, args.warmup, args.seed,
-                                              torch, pa, W)
+                                              torch, pa, W, args.dtype)
     head = summarize(args.workload, b, work, ms, kms)
     also = []
     for name in [x for x in args.also.split(",") if x and x != args.workload]:
         ob, owork, oms, _, okms = time_workload(name, args.steps, args.warmup, args.seed, torch,
-                                                pa, W)
+                                                pa, W, args.dtype)
         entry = summarize(name, ob, owork, oms, okms)
         entry["roofline"] = roofline(name, owork, okms)
         also.append(entry)
@@ -379,7 +387,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": args.dtype,
         "data": "synthetic",
         "config": {"workload": args.workload, "seed": args.seed, "batch": b.batch_size,
                    "num_tokens": b.num_tokens, "num_heads": b.num_heads,

@@ -67,9 +67,16 @@ typedef enum pa_status {
   PA_ERR_HIP = 8           /* a HIP runtime call or kernel launch failed          */
 } pa_status;
 
-/* Element type T of query/key/value/caches/output (README, Type constraints:
- * T = float16; S = int32 for every index input). */
-typedef enum pa_dtype { PA_DTYPE_F16 = 1 } pa_dtype;
+/* Element type T of query/key/value/caches/output.  The model card (README,
+ * Type constraints) names T = float16 and S = int32 for every index input; the
+ * Qwen3.8 export issue (Phase 1 scope) targets fp16 and bf16, and the WS2
+ * contract's Qwen3-8B example runs in bf16.  Either way the caches are copied
+ * bit for bit, scores and sums are fp32, and the output is rounded once (to
+ * nearest) to T. */
+typedef enum pa_dtype {
+  PA_DTYPE_F16 = 1,  /* IEEE binary16                                   */
+  PA_DTYPE_BF16 = 2  /* bfloat16 (the upper 16 bits of an IEEE binary32) */
+} pa_dtype;
 
 /*
  * Arguments of one call.  Tensor layouts are dense row-major.
@@ -103,8 +110,8 @@ typedef enum pa_dtype { PA_DTYPE_F16 = 1 } pa_dtype;
  * environment variable PA_DEBUG_CHECKS=1 to have the call copy the metadata to
  * the host, check it and return PA_ERR_METADATA (this synchronises).
  *
- * Supported by the kernels (else PA_ERR_UNSUPPORTED): dtype PA_DTYPE_F16,
- * is_causal == 1, head_size 64 or 128, block_size a multiple of 16 up to
+ * Supported by the kernels (else PA_ERR_UNSUPPORTED): dtype PA_DTYPE_F16 or
+ * PA_DTYPE_BF16, is_causal == 1, head_size 64 or 128, block_size a multiple of 16 up to
  * 4096, num_heads/kv_num_heads <= 64.  All tensor pointers 16-byte aligned.
  */
 typedef struct pa_args {
@@ -209,7 +216,7 @@ size_t pa_workspace_bytes(const pa_args *args);
  * Rows are independent, e.g. num_rows = num_tokens * num_heads for states
  * written by pa_paged_attention.  Outputs must not overlap the states.
  * Supported: num_states >= 1, head_size a multiple of 4 up to 512, dtype
- * PA_DTYPE_F16.  Asynchronous on `stream`; no workspace, no allocation.
+ * PA_DTYPE_F16 or PA_DTYPE_BF16 (the type of output).  Asynchronous on `stream`; no workspace, no allocation.
  */
 typedef struct pa_merge_args {
   uint32_t struct_size;          /* = sizeof(pa_merge_args)                */

@@ -29,6 +29,8 @@ __all__ = ["paged_attention", "merge_states", "workspace_bytes", "PagedAttention
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
 
 PA_DTYPE_F16 = 1
+PA_DTYPE_BF16 = 2
+_DTYPE_CODES = {torch.float16: PA_DTYPE_F16, torch.bfloat16: PA_DTYPE_BF16}
 ABI_VERSION = 2
 KERNELS = ("scatter_plan", "decode", "merge", "prefill")  # enum pa_kernel order
 STATUS = {
@@ -138,7 +140,8 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 
 
 def _dtype_code(t: torch.Tensor) -> int:
-    return PA_DTYPE_F16 if t.dtype == torch.float16 else 0
+    """pa_dtype of a tensor (0, which the library rejects, for other types)."""
+    return _DTYPE_CODES.get(t.dtype, 0)
 
 
 def make_args(query, key, value, key_cache, value_cache, cumulative_sequence_length,
@@ -265,12 +268,14 @@ def merge_states(state_out: torch.Tensor, state_lse: torch.Tensor, *,
                  output: Optional[torch.Tensor] = None,
                  output_f32: Optional[torch.Tensor] = None,
                  lse: Optional[torch.Tensor] = None,
+                 dtype: torch.dtype = torch.float16,
                  stream: Optional[torch.cuda.Stream] = None):
     """Fixed-order merge of partial states (library entry pa_merge_states).
 
     state_out fp32 [P, R, D], state_lse fp32 [P, R] (natural log, -inf =
-    empty); states fold in index order.  Returns (output fp16 [R, D], lse fp32
-    [R]); ``output_f32`` optionally receives the unrounded output."""
+    empty); states fold in index order.  Returns (output [R, D] in ``dtype``
+    (fp16 or bf16; the type of ``output`` when given), lse fp32 [R]);
+    ``output_f32`` optionally receives the unrounded output."""
     lib = library()
     if state_out.dim() != 3 or state_lse.shape != state_out.shape[:2]:
         raise ValueError("state_out must be [P, R, D] and state_lse [P, R]")
@@ -280,12 +285,12 @@ def merge_states(state_out: torch.Tensor, state_lse: torch.Tensor, *,
     P, R, D = state_out.shape
     dev = state_out.device
     if output is None:
-        output = torch.empty((R, D), dtype=torch.float16, device=dev)
+        output = torch.empty((R, D), dtype=dtype, device=dev)
     if lse is None:
         lse = torch.empty((R,), dtype=torch.float32, device=dev)
     a = PaMergeArgs()
     a.struct_size = ctypes.sizeof(PaMergeArgs)
-    a.dtype = PA_DTYPE_F16 if output.dtype == torch.float16 else 0
+    a.dtype = _dtype_code(output)
     a.num_states = P
     a.head_size = D
     a.num_rows = R

@@ -45,7 +45,7 @@ pa_status resolve(const pa_args* a, Resolved* r) {
   if (static_cast<int64_t>(a->max_blocks_per_seq) * a->block_size > INT32_MAX ||
       static_cast<int64_t>(a->num_blocks) * a->block_size > INT32_MAX)
     return PA_ERR_SHAPE;
-  if (a->dtype != PA_DTYPE_F16 || a->is_causal != 1) return PA_ERR_UNSUPPORTED;
+  if ((a->dtype != PA_DTYPE_F16 && a->dtype != PA_DTYPE_BF16) || a->is_causal != 1) return PA_ERR_UNSUPPORTED;
   if (D != 64 && D != 128) return PA_ERR_UNSUPPORTED;
   if (a->block_size % 16 != 0 || a->block_size > 4096) return PA_ERR_UNSUPPORTED;
   if (a->num_heads / a->kv_num_heads > 64) return PA_ERR_UNSUPPORTED;
@@ -302,7 +302,8 @@ pa_status pa_paged_attention(const pa_args* a, void* stream) {
 
   const int cus = device_cus();
   mark(PA_KERNEL_DECODE, 0);
-  if (launch_decode(ap, r.D, decode_head_slots(r.G), w.decode_grid, s) != hipSuccess) return PA_ERR_HIP;
+  const bool bf16 = a->dtype == PA_DTYPE_BF16;
+  if (launch_decode(ap, r.D, decode_head_slots(r.G), bf16, w.decode_grid, s) != hipSuccess) return PA_ERR_HIP;
   mark(PA_KERNEL_DECODE, 1);
   mark(PA_KERNEL_MERGE, 0);  // the merge of cut decode segments opens the prefill launch
   mark(PA_KERNEL_MERGE, 1);
@@ -311,7 +312,7 @@ pa_status pa_paged_attention(const pa_args* a, void* stream) {
   const int pf_grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(pf_work, int64_t(cus) * kPrefillWgPerCu)));
   ap.items = sp.pf_items;
   mark(PA_KERNEL_PREFILL, 0);
-  if (launch_prefill(ap, r.D, pf_grid, s) != hipSuccess) return PA_ERR_HIP;
+  if (launch_prefill(ap, r.D, bf16, pf_grid, s) != hipSuccess) return PA_ERR_HIP;
   mark(PA_KERNEL_PREFILL, 1);
   return PA_OK;
 }
@@ -321,7 +322,8 @@ pa_status pa_merge_states(const pa_merge_args* a, void* stream) {
   if (a == nullptr) return PA_ERR_NULL_ARG;
   if (a->struct_size != sizeof(pa_merge_args)) return PA_ERR_ABI;
   if (a->num_states < 1 || a->num_rows < 0 || a->head_size <= 0) return PA_ERR_SHAPE;
-  if (a->dtype != PA_DTYPE_F16 || a->head_size % 4 != 0 || a->head_size > 512) return PA_ERR_UNSUPPORTED;
+  if ((a->dtype != PA_DTYPE_F16 && a->dtype != PA_DTYPE_BF16) || a->head_size % 4 != 0 || a->head_size > 512)
+    return PA_ERR_UNSUPPORTED;
   if (a->num_rows == 0) return PA_OK;
   if (a->state_out == nullptr || a->state_lse == nullptr) return PA_ERR_NULL_ARG;
   if (!aligned16(a->state_out) || !aligned4(a->state_lse) || !aligned16(a->output_f32) ||
@@ -336,6 +338,7 @@ pa_status pa_merge_states(const pa_merge_args* a, void* stream) {
   mp.rows = a->num_rows;
   mp.states = a->num_states;
   mp.head_size = a->head_size;
+  mp.bf16 = a->dtype == PA_DTYPE_BF16 ? 1 : 0;
   if (launch_merge_states(mp, static_cast<hipStream_t>(stream)) != hipSuccess) return PA_ERR_HIP;
   return PA_OK;
 }

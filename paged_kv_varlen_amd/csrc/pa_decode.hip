@@ -11,7 +11,7 @@
 // Segments are laid end to end and wave w of W streams the tiles
 // [floor(w T / W), floor((w + 1) T / W)), so every wave moves the same number
 // of K/V bytes whatever the length mix.  A segment that is whole in one wave
-// is written as fp16 directly.  A cut segment leaves one normalised partial
+// is written (rounded to the data type) directly.  A cut segment leaves one normalised partial
 // (o, lse) per piece in the wave's two partial slots; the next launch merges
 // them in wave order (pa_merge.h).
 //
@@ -29,24 +29,21 @@
 // compiler never has to guess (and over-wait) on the direct loads.
 //
 // Per tile (all heads of the unit at once):
-//   S^T[key][head] = K Q^T      4 x v_mfma_f32_16x16x32_f16 (D = 128)
+//   S^T[key][head] = K Q^T      4 x v_mfma_f32_16x16x32_{f16,bf16} (D = 128)
 //   online softmax in base 2, fp32, lazy rescale (only when the running max
-//   grows by more than 2^8), P rounded to fp16
-//   O^T[d][head] += V^T P^T     8 x v_mfma_f32_16x16x16_f16
+//   grows by more than 2^8), P rounded to the data type (fp16 or bf16)
+//   O^T[d][head] += V^T P^T     8 x v_mfma_f32_16x16x16_{f16,bf16}
 // P^T is the S^T accumulator itself (lane = head + 16 * key group); the V^T
 // operand comes from the transposing LDS read ds_read_b64_tr_b16.
 #include <utility>
 
+#include "pa_elem.h"
 #include "pa_internal.h"
 
 namespace pa {
 
 namespace {
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define PA_LDS __attribute__((address_space(3)))
@@ -218,8 +215,9 @@ constexpr int kLast = 1 << 9;      // last tile of a piece
 constexpr int kComplete = 1 << 10; // the piece is the whole segment
 constexpr int kSecond = 1 << 11;   // partial goes to the wave's second slot
 
-template <int D, int HS>
+template <int D, int HS, bool BF16>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnParams p) {
+  using E = Elem<BF16>;
   constexpr int ROW = 2 * D;                      // bytes of one key of one kv head
   constexpr int CPR = ROW / 16;                   // 16-byte chunks per row
   constexpr int KPI = 1024 / ROW;                 // rows per 1 KB direct load
@@ -459,7 +457,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnParams p) {
   float m = kNegInf, l = 0.f;
   u32x4 qv[KS];
   int nh_c = 0, h0_c = 0, t_c = 0;
-  const half2_t one2 = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
 
   auto compute = [&](auto slot_c) __attribute__((always_inline)) {
     constexpr int S = decltype(slot_c)::value;
@@ -486,8 +483,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnParams p) {
     f32x4_t st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      st = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, tr.k[s]),
-                                                  __builtin_bit_cast(half8_t, qv[s]), st, 0, 0, 0);
+      st = E::mfma_16x16x32(__builtin_bit_cast(typename E::x8, tr.k[s]), __builtin_bit_cast(typename E::x8, qv[s]),
+                            st);
     float sc[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) sc[e] = st[e] * p.scale_log2;
@@ -506,12 +503,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnParams p) {
       for (int blk = 0; blk < DB; ++blk) acc[blk] *= alpha;
       m = grow ? mx : m;
     }
-    half4_t pb;
+    typename E::x4 pb;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pb[e] = static_cast<_Float16>(fast_exp2(sc[e] - m));
-    // row sum of exactly the fp16 weights the MFMA multiplies
-    l = __builtin_amdgcn_fdot2(half2_t{pb[0], pb[1]}, one2, l, false);
-    l = __builtin_amdgcn_fdot2(half2_t{pb[2], pb[3]}, one2, l, false);
+    for (int e = 0; e < 4; ++e) pb[e] = E::round(fast_exp2(sc[e] - m));
+    // row sum of exactly the rounded weights the MFMA multiplies
+    l = E::sum2(typename E::x2{pb[0], pb[1]}, l);
+    l = E::sum2(typename E::x2{pb[2], pb[3]}, l);
     if (nvalid < kDecodeTile) {
       // keys past the history may hold any bits (NaN included): zero their values
       const int k0 = 4 * g;
@@ -525,21 +522,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnParams p) {
     }
 #pragma unroll
     for (int blk = 0; blk < DB; ++blk)
-      acc[blk] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, tr.v[blk]), pb, acc[blk],
-                                                       0, 0, 0);
+      acc[blk] = E::mfma_16x16x16(__builtin_bit_cast(typename E::x4, tr.v[blk]), pb, acc[blk]);
     if (fl & kLast) {  // last tile of the piece: normalise and write
       const float lt = swap32(swap16(l, false), false);
       const float inv = 1.f / lt;
-      if (fl & kComplete) {  // whole segment here: the final fp16 output
+      if (fl & kComplete) {  // whole segment here: the final output
         if (n < nh_c) {
           const int64_t row = static_cast<int64_t>(t_c) * p.num_heads + h0_c + n;
           uint16_t* o = p.out + row * D + 4 * g;
 #pragma unroll
           for (int blk = 0; blk < DB; ++blk) {
-            half4_t hv;
+            typename E::x4 hv;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) hv[e] = static_cast<_Float16>(acc[blk][e] * inv);
-            *reinterpret_cast<half4_t*>(o + 16 * blk) = hv;
+            for (int e = 0; e < 4; ++e) hv[e] = E::round(acc[blk][e] * inv);
+            *reinterpret_cast<typename E::x4*>(o + 16 * blk) = hv;
           }
           // optional partial state: fp32 output and natural-log lse
           if (p.out_f32 != nullptr) {
@@ -579,11 +575,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnParams p) {
 
 }  // namespace
 
-hipError_t launch_decode(const AttnParams& p, int head_size, int head_slots, int grid, hipStream_t s) {
-#define PA_DECODE(DD, HH)                                                         \
-  if (head_size == DD && head_slots == HH) {                                      \
-    hipLaunchKernelGGL((decode_kernel<DD, HH>), dim3(grid), dim3(kDecodeThreads), 0, s, p); \
-    return hipGetLastError();                                                     \
+hipError_t launch_decode(const AttnParams& p, int head_size, int head_slots, bool bf16, int grid, hipStream_t s) {
+#define PA_DECODE(DD, HH)                                                                         \
+  if (head_size == DD && head_slots == HH) {                                                      \
+    if (bf16)                                                                                     \
+      hipLaunchKernelGGL((decode_kernel<DD, HH, true>), dim3(grid), dim3(kDecodeThreads), 0, s, p);  \
+    else                                                                                          \
+      hipLaunchKernelGGL((decode_kernel<DD, HH, false>), dim3(grid), dim3(kDecodeThreads), 0, s, p); \
+    return hipGetLastError();                                                                     \
   }
   PA_DECODE(128, 4)
   PA_DECODE(128, 8)

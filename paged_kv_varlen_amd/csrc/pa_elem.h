@@ -1,0 +1,75 @@
+// The element type of the operator's data tensors (query, key, value, the two
+// caches and the output) as the kernels use it: fp16 or bf16, both 16 bits,
+// chosen at compile time.  The caches are copied bit for bit whatever the
+// type; only the matrix products, the rounding of the softmax weights P and of
+// the output, and the row sum of the rounded weights depend on it.
+//
+// The model card ("com.microsoft.PagedAttention", Type constraints) names
+// fp16; the Qwen3.8 export issue ("Add Qwen3.8 packed hybrid PagedAttention
+// export for ORT GenAI Engine", Phase 1 scope) targets fp16 and bf16, and the
+// "WS2 CP-Aware Attention Contract" example (Qwen3-8B TP=2 CP=2) runs in bf16.
+// Both types accumulate in fp32 and round once at the final write (WS2,
+// Reduction Semantics).
+#pragma once
+
+#include <stdint.h>
+
+namespace pa {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <bool BF16>
+struct Elem;
+
+template <>
+struct Elem<false> {  // IEEE binary16
+  typedef _Float16 T;
+  typedef _Float16 x8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 x4 __attribute__((ext_vector_type(4)));
+  typedef _Float16 x2 __attribute__((ext_vector_type(2)));
+  static __device__ inline f32x16_t mfma_32x32x16(x8 a, x8 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ inline f32x4_t mfma_16x16x32(x8 a, x8 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ inline f32x4_t mfma_16x16x16(x4 a, x4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+  }
+  // c + a.x + a.y, the two values exactly as rounded (v_dot2 with (1, 1))
+  static __device__ inline float sum2(x2 a, float c) {
+    const x2 one = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+    return __builtin_amdgcn_fdot2(a, one, c, false);
+  }
+  static __device__ inline T round(float x) { return static_cast<_Float16>(x); }
+  static __device__ inline uint16_t bits(float x) { return __builtin_bit_cast(uint16_t, round(x)); }
+};
+
+template <>
+struct Elem<true> {  // bfloat16: the upper half of a binary32
+  typedef __bf16 T;
+  typedef __bf16 x8 __attribute__((ext_vector_type(8)));
+  typedef __bf16 x4 __attribute__((ext_vector_type(4)));
+  typedef __bf16 x2 __attribute__((ext_vector_type(2)));
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  static __device__ inline f32x16_t mfma_32x32x16(x8 a, x8 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ inline f32x4_t mfma_16x16x32(x8 a, x8 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ inline f32x4_t mfma_16x16x16(x4 a, x4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, a), __builtin_bit_cast(s4, b), c, 0, 0,
+                                                     0);
+  }
+  static __device__ inline float sum2(x2 a, float c) {
+    const x2 one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+    return __builtin_amdgcn_fdot2_f32_bf16(a, one, c, false);
+  }
+  // round to nearest, ties to even (v_cvt_pk_bf16_f32)
+  static __device__ inline T round(float x) { return static_cast<__bf16>(x); }
+  static __device__ inline uint16_t bits(float x) { return __builtin_bit_cast(uint16_t, round(x)); }
+};
+
+}  // namespace pa

@@ -142,7 +142,7 @@ struct AttnParams {
   const int32_t* cum;
   const int32_t* past;
   const int32_t* block_table;
-  uint16_t* out;               // [N, H*D]
+  uint16_t* out;               // [N, H*D] in the data type
   const uint16_t* zeros;       // 256 zero bytes
   int32_t* ws_ctrl;
   const int2* items;           // prefill items
@@ -168,18 +168,19 @@ struct AttnParams {
 struct MergeStatesParams {
   const float* state_out;      // [P, R, D]
   const float* state_lse;      // [P, R]
-  uint16_t* out;               // [R, D] fp16, or null
+  uint16_t* out;               // [R, D] fp16 or bf16, or null
   float* out_f32;              // [R, D], or null
   float* lse;                  // [R], or null
   int64_t rows;
   int32_t states;
   int32_t head_size;
+  int32_t bf16;                // output type: 0 fp16, 1 bf16
 };
 
 // ---- launchers (defined in the .hip files) ---------------------------------
 hipError_t launch_scatter_plan(const ScatterPlanParams& p, hipStream_t s);
-hipError_t launch_decode(const AttnParams& p, int head_size, int head_slots, int grid, hipStream_t s);
-hipError_t launch_prefill(const AttnParams& p, int head_size, int grid, hipStream_t s);
+hipError_t launch_decode(const AttnParams& p, int head_size, int head_slots, bool bf16, int grid, hipStream_t s);
+hipError_t launch_prefill(const AttnParams& p, int head_size, bool bf16, int grid, hipStream_t s);
 size_t prefill_lds_bytes(int head_size);
 hipError_t launch_merge_states(const MergeStatesParams& p, hipStream_t s);
 

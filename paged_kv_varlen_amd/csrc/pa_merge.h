@@ -4,7 +4,7 @@
 // (o_i normalised, lse_i in base 2) of one query row are combined as
 // sum_i 2^(lse_i - M) o_i / sum_i 2^(lse_i - M), M = max_i lse_i, in fp32 and
 // in a fixed order (here: the order of the decode waves), with one rounding
-// to fp16 at the end.
+// to the data type (fp16 or bf16) at the end.
 //
 // The decode kernel leaves the pieces of segment S..S+n-1 (tiles of one
 // sequence and unit) in the partial slots of waves wf..wl: the first piece in
@@ -14,13 +14,14 @@
 // partial is visible without any cross-workgroup synchronisation.
 #pragma once
 
+#include "pa_elem.h"
 #include "pa_internal.h"
 
 namespace pa {
 
 // One segment (decode sequence d, unit u) per call, all 64 lanes: lane = query
 // head (lane & 15) + 16 * quarter of the head dimension.
-template <int D>
+template <int D, bool BF16>
 __device__ inline void merge_segment(const AttnParams& p, int task, int T, int lane) {
   const int U = p.decode_units;
   const int d = task / U, u = task % U;
@@ -83,10 +84,8 @@ __device__ inline void merge_segment(const AttnParams& p, int task, int T, int l
     uint32_t w2[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const _Float16 lo = static_cast<_Float16>(o[e + 2 * c] * inv);
-      const _Float16 hi = static_cast<_Float16>(o[e + 2 * c + 1] * inv);
-      w2[c] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
-              (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+      w2[c] = static_cast<uint32_t>(Elem<BF16>::bits(o[e + 2 * c] * inv)) |
+              (static_cast<uint32_t>(Elem<BF16>::bits(o[e + 2 * c + 1] * inv)) << 16);
     }
     *reinterpret_cast<uint2*>(out + e) = make_uint2(w2[0], w2[1]);
   }

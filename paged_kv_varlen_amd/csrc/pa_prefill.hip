@@ -31,7 +31,7 @@
 // XOR-swizzled per row so that the reads below hit distinct LDS banks.
 //
 // Per step and wave (32 keys x 32 rows):
-//   * S^T = K Q^T with v_mfma_f32_32x32x16_f16 (fp16 in, fp32 accumulate): a
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_{f16,bf16} (fp32 accumulate): a
 //     lane holds 16 keys of one query row, so the row max needs a single
 //     exchange with lane^32.  All K and V fragments of the step are read from
 //     LDS before the first product, so the step waits for one LDS round trip;
@@ -53,6 +53,7 @@
 // L2 holds the K/V of few heads; when its queue is empty it helps the others.
 #include <type_traits>
 
+#include "pa_elem.h"
 #include "pa_internal.h"
 #include "pa_merge.h"
 
@@ -60,10 +61,7 @@ namespace pa {
 
 namespace {
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 #define PA_LDS __attribute__((address_space(3)))
 #define PA_GLOBAL __attribute__((address_space(1)))
 
@@ -120,9 +118,12 @@ struct PrefillShape {
   static __device__ int v_swz(int row) { return D == 128 ? ((row & 3) << 2) : 0; }
 };
 
-template <int D>
+template <int D, bool BF16>
 __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) {
   using S = PrefillShape<D>;
+  using E = Elem<BF16>;
+  typedef typename E::x8 x8;
+  typedef typename E::x4 x4;
   constexpr int ROWB = S::ROWB, CPR = S::CPR;
   static_assert(S::LOADS >= 1, "loads per wave");
 
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
     const int T = p.ws_ctrl[kCtrlDecodeTiles];
     const int nw = static_cast<int>(gridDim.x) * (kPrefillThreads / 64);
     for (int task = static_cast<int>(blockIdx.x) * (kPrefillThreads / 64) + wave; task < segments; task += nw)
-      merge_segment<D>(p, task, T, lane);
+      merge_segment<D, BF16>(p, task, T, lane);
   }
 
   const int nq = prefill_queue_count(p.kv_heads);
@@ -253,7 +254,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
     const int wave_first = past + i0 + fh0 / G;
     const int wave_last = wave_valid ? past + min(i0 + min(fh0 + 31, P * G - 1) / G, i1 - 1) : -1;
 
-    half8_t qf[S::QK_STEPS];
+    x8 qf[S::QK_STEPS];
     {
       const uint16_t* qrow = p.q + static_cast<int64_t>(t0 + i0 + (row_valid ? pos_local : 0)) * p.q_stride +
                              static_cast<int64_t>(head) * D;
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
         if (negate_q) {
           raw.x ^= 0x80008000u; raw.y ^= 0x80008000u; raw.z ^= 0x80008000u; raw.w ^= 0x80008000u;
         }
-        qf[kk] = __builtin_bit_cast(half8_t, raw);
+        qf[kk] = __builtin_bit_cast(x8, raw);
       }
     }
 
@@ -336,18 +337,18 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
     // so the step waits for one LDS round trip, not one per product.
     auto compute = [&](auto buf_tag, int jk, bool masked) __attribute__((always_inline)) {
       constexpr int buf = decltype(buf_tag)::value;
-      half8_t kf[S::QK_STEPS];
+      x8 kf[S::QK_STEPS];
 #pragma unroll
-      for (int kk = 0; kk < S::QK_STEPS; ++kk) kf[kk] = *reinterpret_cast<const half8_t*>(kbuf(buf) + koff[kk]);
+      for (int kk = 0; kk < S::QK_STEPS; ++kk) kf[kk] = *reinterpret_cast<const x8*>(kbuf(buf) + koff[kk]);
       asm volatile("" ::: "memory");  // keep the reads ahead of the products
       f32x16_t s = f32x16_t{};
 #pragma unroll
-      for (int kk = 0; kk < S::QK_STEPS; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[kk], qf[kk], s, 0, 0, 0);
+      for (int kk = 0; kk < S::QK_STEPS; ++kk) s = E::mfma_32x32x16(kf[kk], qf[kk], s);
       // V^T fragments, read while the products and the softmax run: the
       // transpose read of rows key0..key0+3 (key0 = 16ks + 4*lhalf, then +8)
       // gives each lane the 4 keys of its d column, in the key order of the
       // P^T registers
-      half8_t va[2][S::O_TILES];
+      x8 va[2][S::O_TILES];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -355,7 +356,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
           char* vb = vbuf(buf) + voff[mt] + 16 * ks * ROWB;
           const fp16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((PA_LDS fp16x4_t*)vb);
           const fp16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((PA_LDS fp16x4_t*)(vb + 8 * ROWB));
-          va[ks][mt] = __builtin_shufflevector(__builtin_bit_cast(half4_t, lo), __builtin_bit_cast(half4_t, hi),
+          va[ks][mt] = __builtin_shufflevector(__builtin_bit_cast(x4, lo), __builtin_bit_cast(x4, hi),
                                                0, 1, 2, 3, 4, 5, 6, 7);
         }
       asm volatile("" ::: "memory");
@@ -387,20 +388,18 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
       // 16ks + 4*lhalf + 0..3 and 16ks + 8 + 4*lhalf + 0..3.  A row that has
       // seen no key yet (m = -inf) has only masked scores here.
       const float mref = m == kNegInf ? 0.f : m;
-      half8_t pb[2];
+      x8 pb[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pb[ks][e] = static_cast<_Float16>(fast_exp2(fmaf(s[8 * ks + e], c, -mref)));
+        for (int e = 0; e < 8; ++e) pb[ks][e] = E::round(fast_exp2(fmaf(s[8 * ks + e], c, -mref)));
       // row sum of exactly the fp16 weights the MFMA multiplies (v_dot2 with 1)
-      typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-      const half2_t one2 = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
       // (two partial sums: shorter dependency chains; fixed order)
       float la = 0.f, lb = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        la = __builtin_amdgcn_fdot2(half2_t{pb[0][e], pb[0][e + 1]}, one2, la, false);
-        lb = __builtin_amdgcn_fdot2(half2_t{pb[1][e], pb[1][e + 1]}, one2, lb, false);
+        la = E::sum2(typename E::x2{pb[0][e], pb[0][e + 1]}, la);
+        lb = E::sum2(typename E::x2{pb[1][e], pb[1][e + 1]}, lb);
       }
       l += la + lb;
       // O^T[d][row] += V^T[d][key] P^T[key][row]
@@ -408,7 +407,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int mt = 0; mt < S::O_TILES; ++mt)
-          o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[ks][mt], pb[ks], o[mt], 0, 0, 0);
+          o[mt] = E::mfma_32x32x16(va[ks][mt], pb[ks], o[mt]);
     };
 
     // Step j computes from ring buffer j % 4 and fetches step j + 3 into ring
@@ -516,8 +515,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
               const float* x1 = &xo[(mt * 16 + ir) * 64 + lane];
               v[2 * e] = (o[mt][ir] * a0 + x1[0] * a1) * inv;
               v[2 * e + 1] = (o[mt][ir + 1] * a0 + x1[64] * a1) * inv;
-              w[e] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(v[2 * e]))) |
-                     (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(v[2 * e + 1]))) << 16);
+              w[e] = static_cast<uint32_t>(E::bits(v[2 * e])) | (static_cast<uint32_t>(E::bits(v[2 * e + 1])) << 16);
             }
             *reinterpret_cast<uint2*>(orow + 32 * mt + 8 * q + 4 * lhalf) = make_uint2(w[0], w[1]);
             if (orow_f != nullptr)
@@ -539,8 +537,11 @@ static_assert(2 * 16 * 64 * sizeof(float) <= PrefillShape<64>::BUF, "merge area"
 static_assert(prefill_smem<128>() <= 160 * 1024, "LDS budget");
 
 template <int D>
-hipError_t launch_prefill_t(const AttnParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(prefill_kernel<D>, dim3(grid), dim3(kPrefillThreads), 0, s, p);
+hipError_t launch_prefill_t(const AttnParams& p, bool bf16, int grid, hipStream_t s) {
+  if (bf16)
+    hipLaunchKernelGGL((prefill_kernel<D, true>), dim3(grid), dim3(kPrefillThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, false>), dim3(grid), dim3(kPrefillThreads), 0, s, p);
   return hipGetLastError();
 }
 
@@ -550,9 +551,9 @@ size_t prefill_lds_bytes(int head_size) {
   return head_size == 128 ? prefill_smem<128>() : prefill_smem<64>();
 }
 
-hipError_t launch_prefill(const AttnParams& p, int head_size, int grid, hipStream_t s) {
-  if (head_size == 128) return launch_prefill_t<128>(p, grid, s);
-  if (head_size == 64) return launch_prefill_t<64>(p, grid, s);
+hipError_t launch_prefill(const AttnParams& p, int head_size, bool bf16, int grid, hipStream_t s) {
+  if (head_size == 128) return launch_prefill_t<128>(p, bf16, grid, s);
+  if (head_size == 64) return launch_prefill_t<64>(p, bf16, grid, s);
   return hipErrorInvalidValue;
 }
 

@@ -2,7 +2,8 @@
 //
 // "WS2 CP-Aware Attention Contract", Reduction Semantics: a partial state is
 // (out, attention-domain lse); states merge by the online-softmax rule, in
-// fp32, in a fixed order, with one rounding at the final write.  Row r of the
+// fp32, in a fixed order, with one rounding (to fp16 or bf16) at the final
+// write.  Row r of the
 // result folds states 0, 1, .. P-1 in that order:
 //   lse' = m + log(e^(lse - m) + e^(lse_p - m)), m = max(lse, lse_p),
 //   out  = (e^(lse - m) out + e^(lse_p - m) out_p) / (e^(lse - m) + e^(lse_p - m)).
@@ -12,6 +13,7 @@
 // Memory-bound: a lane owns 4 consecutive head-dim values of one row and
 // reads them (16-byte loads) from every state; consecutive lanes cover a row,
 // then the next row, so each state is streamed once, coalesced.
+#include "pa_elem.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -20,6 +22,7 @@ namespace {
 
 constexpr int kMergeThreads = 256;
 
+template <bool BF16>
 __global__ __launch_bounds__(kMergeThreads) void merge_states_kernel(MergeStatesParams p) {
   const int qpr = p.head_size / 4;  // lanes per row
   const int64_t lanes = p.rows * qpr;
@@ -51,10 +54,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_states_kernel(MergeStates
     }
     if (p.out_f32 != nullptr) reinterpret_cast<float4*>(p.out_f32 + row * p.head_size)[q] = o;
     if (p.out != nullptr) {
-      typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-      const half4_t h = {static_cast<_Float16>(o.x), static_cast<_Float16>(o.y), static_cast<_Float16>(o.z),
-                         static_cast<_Float16>(o.w)};
-      reinterpret_cast<half4_t*>(p.out + row * p.head_size)[q] = h;
+      using E = Elem<BF16>;
+      const typename E::x4 h = {E::round(o.x), E::round(o.y), E::round(o.z), E::round(o.w)};
+      reinterpret_cast<typename E::x4*>(p.out + row * p.head_size)[q] = h;
     }
     if (p.lse != nullptr && q == 0) p.lse[row] = lse;
   }
@@ -66,7 +68,10 @@ hipError_t launch_merge_states(const MergeStatesParams& p, hipStream_t s) {
   const int64_t lanes = p.rows * (p.head_size / 4);
   const int64_t blocks = (lanes + kMergeThreads - 1) / kMergeThreads;
   const int grid = static_cast<int>(blocks < 65536 ? blocks : 65536);
-  hipLaunchKernelGGL(merge_states_kernel, dim3(grid), dim3(kMergeThreads), 0, s, p);
+  if (p.bf16)
+    hipLaunchKernelGGL(merge_states_kernel<true>, dim3(grid), dim3(kMergeThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(merge_states_kernel<false>, dim3(grid), dim3(kMergeThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -115,7 +115,9 @@ def test_workspace_bytes_static_bound():
     (dict(num_tokens=-1), SHAPE),
     (dict(num_blocks=0), SHAPE),
     (dict(is_causal=0), UNSUP),                          # only is_causal=1 exists
-    (dict(dtype=0), UNSUP),                              # T must be float16
+    (dict(dtype=0), UNSUP),                              # T must be float16 or bfloat16
+    (dict(dtype=3), UNSUP),
+    (dict(dtype=2), WS),                                 # bfloat16 passes validation
     (dict(block_size=8), UNSUP),
     (dict(query_width=4 * 32, cache_head_size=32), UNSUP),  # D=32 not built
     (dict(query=None), NULL),
@@ -176,6 +178,8 @@ def merge_args(**kw):
     (dict(head_size=6), UNSUP),                          # not a multiple of 4
     (dict(head_size=1024), UNSUP),
     (dict(dtype=0), UNSUP),
+    (dict(dtype=3), UNSUP),
+    (dict(dtype=2, num_rows=0), OK),                     # bfloat16 output accepted
     (dict(state_out=None), NULL),
     (dict(state_lse=None), NULL),
     (dict(state_out=FAKE + 4), ALIGN),

@@ -2,7 +2,10 @@
 
 Bar (stated with the workloads): both caches bit-exact over every slot,
 written or untouched; outputs within max-abs 4e-3 of the fp64 oracle (fp16
-inputs, fp32 accumulation, O(1) data).  Full-size workloads are checked on
+inputs, fp32 accumulation, O(1) data).  For bf16 data the bar scales with the
+unit roundoff: bf16 keeps 8 significant bits to fp16's 11, so every rounding
+in the path (P before the PV product, the output) is 8 times coarser and the
+bar is 8 * 4e-3 = 3.2e-2.  Full-size workloads are checked on
 every cache slot and on sampled output rows the oracle computes one by one.
 Every call goes through the C ABI (libpagedattn.so via ctypes).
 """
@@ -18,7 +21,12 @@ import workloads as W
 
 pytestmark = pytest.mark.gpu
 TOL = 4e-3
+TOL_BF16 = 8 * TOL
 DEV = "cuda:0"
+
+
+def tol(b) -> float:
+    return TOL_BF16 if b.dtype == "bf16" else TOL
 
 
 def say(msg):
@@ -26,10 +34,28 @@ def say(msg):
 
 
 def to_dev(x, dtype=None):
+    """numpy -> device tensor; uint16 arrays hold bf16 bit patterns."""
     if x is None:
         return None
-    t = torch.from_numpy(np.ascontiguousarray(x))
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).to(DEV).view(torch.bfloat16)
+    t = torch.from_numpy(x)
     return t.to(DEV) if dtype is None else t.to(DEV, dtype)
+
+
+def to_host(t):
+    """device tensor -> numpy; bf16 comes back as uint16 bit patterns."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def as_f64(x):
+    """Values of host data: float16 as is, uint16 as bf16 bits (torch's decode)."""
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).double().numpy()
+    return x.astype(np.float64)
 
 
 class DevBatch:
@@ -53,12 +79,12 @@ class DevBatch:
 
 
 def gpu_run(b: W.Batch):
-    say(f"[gpu] {b.name} seed={b.seed} N={b.num_tokens} B={b.batch_size} "
+    say(f"[gpu] {b.name} {b.dtype} seed={b.seed} N={b.num_tokens} B={b.batch_size} "
         f"H={b.num_heads}/{b.kv_num_heads} D={b.head_size} bs={b.block_size} NB={b.num_blocks}")
     d = DevBatch(b)
     out = d.run()
     torch.cuda.synchronize()
-    return (out.cpu().numpy(), d.kc.cpu().numpy(), d.vc.cpu().numpy())
+    return (to_host(out), to_host(d.kc), to_host(d.vc))
 
 
 def sample_rows(b: W.Batch, per_seq=6, max_seqs=None, must=(), seed=0):
@@ -86,11 +112,11 @@ def check(b: W.Batch, rows=None, gpu=None):
     assert np.array_equal(kc.view(np.uint16), rkc.view(np.uint16)), "key_cache differs"
     assert np.array_equal(vc.view(np.uint16), rvc.view(np.uint16)), "value_cache differs"
     sel = np.arange(b.num_tokens) if rows is None else rows
-    got = out[sel].astype(np.float64)
+    got = as_f64(out[sel])
     assert np.all(np.isfinite(got))
     err = np.max(np.abs(got - ref[sel])) if sel.size else 0.0
     say(f"      rows checked {sel.size}, max|err| {err:.3e}")
-    assert err <= TOL, f"max abs error {err}"
+    assert err <= tol(b), f"max abs error {err}"
     return err
 
 
@@ -282,39 +308,48 @@ def test_hip_graph_replay_matches_eager():
 
 # lse tolerance: P is rounded to fp16 before it is summed (relative error at
 # most 2^-11 per weight), so log(sum) is off by at most about 2^-11 = 4.9e-4
-# in natural-log units; fp32 score and sum rounding add ~1e-6.
+# in natural-log units; fp32 score and sum rounding add ~1e-6.  bf16 weights
+# round 8 times coarser.
 LSE_TOL = 1e-3
+LSE_TOL_BF16 = 8 * LSE_TOL
 
 
-def rounding_of(f32, f16):
-    """f16 is a nearest fp16 value of f32 elementwise.  The packed fp32->fp16
-    conversion of gfx950 (v_cvt_pk_f16_f32) may break an exact tie away from
-    the even neighbour, where numpy rounds to even; both are nearest."""
-    r = f32.astype(np.float16)
-    diff = r.view(np.uint16) != f16.view(np.uint16)
+def rounding_of(f32, low):
+    """``low`` (fp16, or bf16 bits as uint16) is a nearest value of f32
+    elementwise.  The packed fp32->fp16 conversion of gfx950
+    (v_cvt_pk_f16_f32) may break an exact tie away from the even neighbour,
+    where numpy rounds to even; both are nearest."""
+    if low.dtype == np.uint16:
+        r = W.round_bf16(f32)
+        diff = r != low
+    else:
+        r = f32.astype(np.float16)
+        diff = r.view(np.uint16) != low.view(np.uint16)
     x = f32.astype(np.float64)
-    tie = np.abs(x - r.astype(np.float64)) == np.abs(x - f16.astype(np.float64))
+    tie = np.abs(x - as_f64(r)) == np.abs(x - as_f64(low))
     if np.any(diff & ~tie):
         i = np.argwhere(diff & ~tie)[0]
-        say(f"      not a rounding at {tuple(i)}: f32 {f32[tuple(i)]!r} f16 {f16[tuple(i)]!r}")
-    say(f"      fp16 output == rounding of fp32 output ({int(np.sum(diff))} ties broken the other way)")
+        say(f"      not a rounding at {tuple(i)}: f32 {f32[tuple(i)]!r} low {low[tuple(i)]!r}")
+    say(f"      rounded output == rounding of fp32 output ({int(np.sum(diff))} ties broken the other way)")
     return not np.any(diff & ~tie)
 
 
-@pytest.mark.parametrize("name", ["tiny", "sweep0", "long_decode", "mixed"])
-def test_lse_and_fp32_output(name):
+@pytest.mark.parametrize("name,dtype", [("tiny", "f16"), ("sweep0", "f16"), ("long_decode", "f16"),
+                                        ("mixed", "f16"), ("tiny", "bf16"), ("long_decode", "bf16"),
+                                        ("mixed", "bf16")])
+def test_lse_and_fp32_output(name, dtype):
     if name == "tiny":
-        b = W.tiny(0)
+        b = W.tiny(0, dtype=dtype)
     elif name == "sweep0":
         q, p, H, Hkv, D, bs = SWEEP[0]
         b = W.make_batch(q, p, num_heads=H, kv_num_heads=Hkv, head_size=D, block_size=bs,
-                         seed=100, name="sweep0")
+                         seed=100, name="sweep0", dtype=dtype)
     elif name == "long_decode":  # decode segments cut across waves: merged states
         b = W.make_batch([1, 1, 1, 2], [16383, 9000, 511, 12000], num_heads=32, kv_num_heads=8,
-                         head_size=128, block_size=256, seed=12, name="long_decode")
+                         head_size=128, block_size=256, seed=12, name="long_decode", dtype=dtype)
     else:
-        b = W.mixed(0)
-    say(f"[gpu] lse {b.name} N={b.num_tokens} B={b.batch_size}")
+        b = W.mixed(0, dtype=dtype)
+    say(f"[gpu] lse {b.name} {b.dtype} N={b.num_tokens} B={b.batch_size}")
     d = DevBatch(b)
     f32 = torch.empty((b.num_tokens, b.num_heads * b.head_size), dtype=torch.float32, device=DEV)
     out, lse = d.run(return_lse=True, output_f32=f32)
@@ -325,16 +360,18 @@ def test_lse_and_fp32_output(name):
                                              num_heads=b.num_heads, kv_num_heads=b.kv_num_heads,
                                              scale=b.scale, rows=rows, with_lse=True)
     sel = np.arange(b.num_tokens) if rows is None else rows
-    o16, o32, l32 = out.cpu().numpy(), f32.cpu().numpy(), lse.cpu().numpy()
+    o16, o32, l32 = to_host(out), f32.cpu().numpy(), lse.cpu().numpy()
     assert rounding_of(o32, o16)
     e_o = np.max(np.abs(o32[sel].astype(np.float64) - ref[sel]))
     e_l = np.max(np.abs(l32[sel].astype(np.float64) - rlse[sel]))
     say(f"      rows {sel.size}: max|err| out_f32 {e_o:.3e}, lse {e_l:.3e}")
-    assert e_o <= TOL and e_l <= LSE_TOL
+    assert e_o <= tol(b) and e_l <= (LSE_TOL_BF16 if dtype == "bf16" else LSE_TOL)
 
 
-@pytest.mark.parametrize("P,R,D", [(1, 37, 128), (3, 1000, 128), (5, 777, 64), (2, 4096, 256)])
-def test_merge_states(P, R, D):
+@pytest.mark.parametrize("P,R,D,dtype", [(1, 37, 128, torch.float16), (3, 1000, 128, torch.float16),
+                                         (5, 777, 64, torch.float16), (2, 4096, 256, torch.float16),
+                                         (3, 1000, 128, torch.bfloat16)])
+def test_merge_states(P, R, D, dtype):
     rng = np.random.default_rng(P * 1000 + R)
     outs = rng.standard_normal((P, R, D)).astype(np.float32)
     lses = (rng.standard_normal((P, R)) * 4).astype(np.float32)
@@ -343,11 +380,12 @@ def test_merge_states(P, R, D):
     ref_o, ref_l = oracle.merge_states(outs, lses)
     so, sl = torch.from_numpy(outs).to(DEV), torch.from_numpy(lses).to(DEV)
     f32 = torch.empty((R, D), dtype=torch.float32, device=DEV)
-    o16, l32 = pa.merge_states(so, sl, output_f32=f32)
-    o16b, l32b = pa.merge_states(so, sl)
+    o16, l32 = pa.merge_states(so, sl, output_f32=f32, dtype=dtype)
+    o16b, l32b = pa.merge_states(so, sl, dtype=dtype)
     torch.cuda.synchronize()
-    o16, o32, l32 = o16.cpu().numpy(), f32.cpu().numpy(), l32.cpu().numpy()
-    assert np.array_equal(o16.view(np.uint16), o16b.cpu().numpy().view(np.uint16))   # deterministic
+    assert o16.dtype == dtype
+    o16, o32, l32 = to_host(o16), f32.cpu().numpy(), l32.cpu().numpy()
+    assert np.array_equal(o16.view(np.uint16), to_host(o16b).view(np.uint16))   # deterministic
     assert np.array_equal(l32.view(np.uint32), l32b.cpu().numpy().view(np.uint32))
     assert rounding_of(o32, o16)
     fin = np.isfinite(ref_l)
@@ -357,4 +395,54 @@ def test_merge_states(P, R, D):
     e_l = np.max(np.abs(l32[fin] - ref_l[fin]) / (1.0 + np.abs(ref_l[fin])))
     say(f"[gpu] merge P={P} R={R} D={D}: max rel err out {e_o:.2e}, lse {e_l:.2e}")
     assert e_o <= 1e-5 and e_l <= 1e-6
-    assert np.max(np.abs(o16.astype(np.float64) - ref_o)) <= TOL * (1 + np.abs(ref_o).max())
+    t = TOL_BF16 if dtype == torch.bfloat16 else TOL
+    assert np.max(np.abs(as_f64(o16) - ref_o)) <= t * (1 + np.abs(ref_o).max())
+
+
+# ------------------------------------------------------------------ bf16 data
+
+@pytest.mark.parametrize("case", ["tiny"] + [f"sweep{i}" for i in range(len(SWEEP))] + ["packed3"])
+def test_bf16_shapes(case):
+    if case == "tiny":
+        b = W.tiny(0, dtype="bf16")
+    elif case == "packed3":
+        q, p, H, Hkv, D, bs = SWEEP[3]
+        b = W.make_batch(q, p, num_heads=H, kv_num_heads=Hkv, head_size=D, block_size=bs,
+                         seed=203, packed=True, slot_mode="drop", drop_count=2, name="packed3",
+                         dtype="bf16")
+    else:
+        i = int(case[5:])
+        q, p, H, Hkv, D, bs = SWEEP[i]
+        b = W.make_batch(q, p, num_heads=H, kv_num_heads=Hkv, head_size=D, block_size=bs,
+                         seed=200 + i, name=case, dtype="bf16")
+    check(b)
+
+
+def test_bf16_pure_decode_full():
+    check(W.pure_decode(0, dtype="bf16"))
+
+
+def test_bf16_mixed():
+    b = W.mixed(0, dtype="bf16")
+    check(b, rows=sample_rows(b, per_seq=10))
+
+
+def test_bf16_long_prefill():
+    b = W.long_prefill(0, dtype="bf16")
+    edges = [0, 1, 31, 32, 33, 1023, 1024, 2015, 2016, 2046, 2047]
+    check(b, rows=sample_rows(b, per_seq=40, must=edges))
+
+
+def test_bf16_first_token_and_determinism():
+    b = W.make_batch([1, 1, 1], [0, 0, 0], num_heads=8, kv_num_heads=2, head_size=128,
+                     block_size=16, seed=8, name="first", dtype="bf16")
+    out, _, _ = gpu_run(b)
+    for t in range(3):
+        for h in range(8):
+            k = h // 4
+            assert np.array_equal(out[t, h * 128:(h + 1) * 128], b.value[t, k * 128:(k + 1) * 128])
+    d = DevBatch(W.mixed(1, dtype="bf16"))
+    o1 = d.run().clone()
+    o2 = d.run().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))

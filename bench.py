@@ -148,9 +148,10 @@ class Runner:
                                 workspace=self.ws, kernel_events=events)
 
 
-def time_workload(name: str, steps: int, warmup: int, seed: int, torch, pa, W, dtype="f16"):
+def time_workload(name: str, steps: int, warmup: int, seed: int, torch, pa, W, dtype="f16",
+                  head_size=0):
     t_gen = time.perf_counter()
-    b = W.workload(name, seed, dtype=dtype)
+    b = W.workload(name, seed, dtype=dtype, head_size=head_size)
     work = W.work(b)
     log(f"[bench] {name}: generated in {time.perf_counter() - t_gen:.1f}s "
         f"(N={b.num_tokens}, B={b.batch_size}, KV {work['kv_hist_bytes'] / 1e9:.3f} GB, "
@@ -310,6 +311,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--dtype", default="f16", choices=("f16", "bf16"),
                     help="data type of the workloads (the line's dtype field)")
+    ap.add_argument("--head-size", type=int, default=0, choices=(0, 64, 128, 256),
+                    help="replace the workloads' head size (0: their own)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -365,12 +368,12 @@ def main():
     pa.library()  # fail loudly if the HIP library is missing
 
     b, work, ms, wall_ms, kms = time_workload(args.workload, args.steps, args.warmup, args.seed,
-                                              torch, pa, W, args.dtype)
+                                              torch, pa, W, args.dtype, args.head_size)
     head = summarize(args.workload, b, work, ms, kms)
     also = []
     for name in [x for x in args.also.split(",") if x and x != args.workload]:
         ob, owork, oms, _, okms = time_workload(name, args.steps, args.warmup, args.seed, torch,
-                                                pa, W, args.dtype)
+                                                pa, W, args.dtype, args.head_size)
         entry = summarize(name, ob, owork, oms, okms)
         entry["roofline"] = roofline(name, owork, okms)
         also.append(entry)

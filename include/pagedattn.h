@@ -111,7 +111,7 @@ typedef enum pa_dtype {
  * the host, check it and return PA_ERR_METADATA (this synchronises).
  *
  * Supported by the kernels (else PA_ERR_UNSUPPORTED): dtype PA_DTYPE_F16 or
- * PA_DTYPE_BF16, is_causal == 1, head_size 64 or 128, block_size a multiple of 16 up to
+ * PA_DTYPE_BF16, is_causal == 1, head_size 64, 128 or 256, block_size a multiple of 16 up to
  * 4096, num_heads/kv_num_heads <= 64.  All tensor pointers 16-byte aligned.
  */
 typedef struct pa_args {

@@ -46,7 +46,7 @@ pa_status resolve(const pa_args* a, Resolved* r) {
       static_cast<int64_t>(a->num_blocks) * a->block_size > INT32_MAX)
     return PA_ERR_SHAPE;
   if ((a->dtype != PA_DTYPE_F16 && a->dtype != PA_DTYPE_BF16) || a->is_causal != 1) return PA_ERR_UNSUPPORTED;
-  if (D != 64 && D != 128) return PA_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128 && D != 256) return PA_ERR_UNSUPPORTED;
   if (a->block_size % 16 != 0 || a->block_size > 4096) return PA_ERR_UNSUPPORTED;
   if (a->num_heads / a->kv_num_heads > 64) return PA_ERR_UNSUPPORTED;
   {  // decode tile indices are 32-bit
@@ -89,13 +89,13 @@ WorkspaceLayout layout(const Resolved& r) {
                             ((static_cast<int64_t>(r.MB) * r.bs + kDecodeTile - 1) / kDecodeTile);
   const int64_t resident = static_cast<int64_t>(device_cus()) * decode_wg_per_cu(r.D, hs);
   w.decode_grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(resident, (max_tiles + 31) / 32)));
-  w.decode_waves = w.decode_grid * kDecodeWaves;
+  w.decode_waves = w.decode_grid * decode_wg_waves(r.D);
   const size_t W = static_cast<size_t>(w.decode_waves);
   size_t off = 0;
   w.ctrl = off;
   off = align256(off + kCtrlSlots * sizeof(int32_t));
   w.zeros = off;
-  off = align256(off + 256);
+  off = align256(off + kZeroPageBytes);
   w.dec_seq = off;
   off = align256(off + (static_cast<size_t>(r.B) + 1) * sizeof(int4));
   w.dec_start = off;

@@ -157,6 +157,56 @@ struct TileRegs<128> {
         : "memory");
   }
 };
+// head_size 256: the second 16 key-dims of every K read and the second 8 d
+// blocks of every V read sit 256 bytes after the first (the swizzle only
+// permutes chunks within 16-chunk halves), so the addresses of the first
+// half serve both, with an offset.  Two blocks keep each asm statement small.
+template <>
+struct TileRegs<256> {
+  u32x4 k[8];
+  u32x2 v[16];
+  template <int OFF>
+  __device__ void read(const uint32_t (&ka)[8], const uint32_t (&va)[16]) {
+    asm volatile(
+        "ds_read_b128 %0, %8 offset:%12\n\t"
+        "ds_read_b128 %1, %9 offset:%12\n\t"
+        "ds_read_b128 %2, %10 offset:%12\n\t"
+        "ds_read_b128 %3, %11 offset:%12\n\t"
+        "ds_read_b128 %4, %8 offset:%13\n\t"
+        "ds_read_b128 %5, %9 offset:%13\n\t"
+        "ds_read_b128 %6, %10 offset:%13\n\t"
+        "ds_read_b128 %7, %11 offset:%13\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]), "=&v"(k[6]),
+          "=&v"(k[7])
+        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "n"(OFF), "n"(OFF + 256)
+        : "memory");
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %1, %17 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %2, %18 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %3, %19 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %4, %20 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %5, %21 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %6, %22 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %7, %23 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %8, %16 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %9, %17 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %10, %18 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %11, %19 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %12, %20 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %13, %21 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %14, %22 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %15, %23 offset:%25\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]),
+          "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]),
+          "=&v"(v[14]), "=&v"(v[15])
+        : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7]),
+          "n"(OFF), "n"(OFF + 256)
+        : "memory");
+  }
+};
 template <>
 struct TileRegs<64> {
   u32x4 k[2];
@@ -180,7 +230,18 @@ struct TileRegs<64> {
 // Query operand reads (once per piece).
 template <int KS, int OFF>
 __device__ inline void read_q(u32x4 (&q)[KS], const uint32_t (&qa)[KS]) {
-  if constexpr (KS == 4) {
+  if constexpr (KS == 8) {
+    asm volatile(
+        "ds_read_b128 %0, %8 offset:%16\n\tds_read_b128 %1, %9 offset:%16\n\t"
+        "ds_read_b128 %2, %10 offset:%16\n\tds_read_b128 %3, %11 offset:%16\n\t"
+        "ds_read_b128 %4, %12 offset:%16\n\tds_read_b128 %5, %13 offset:%16\n\t"
+        "ds_read_b128 %6, %14 offset:%16\n\tds_read_b128 %7, %15 offset:%16\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3]), "=&v"(q[4]), "=&v"(q[5]), "=&v"(q[6]), "=&v"(q[7])
+        : "v"(qa[0]), "v"(qa[1]), "v"(qa[2]), "v"(qa[3]), "v"(qa[4]), "v"(qa[5]), "v"(qa[6]), "v"(qa[7]),
+          "n"(OFF)
+        : "memory");
+  } else if constexpr (KS == 4) {
     asm volatile(
         "ds_read_b128 %0, %4 offset:%8\n\tds_read_b128 %1, %5 offset:%8\n\t"
         "ds_read_b128 %2, %6 offset:%8\n\tds_read_b128 %3, %7 offset:%8\n\t"
@@ -201,7 +262,7 @@ __device__ inline void read_q(u32x4 (&q)[KS], const uint32_t (&qa)[KS]) {
 // (4 keys x 2 chunks per 16 lanes) touch distinct LDS banks.
 template <int D>
 __device__ inline int swz(int k) {
-  if constexpr (D == 128) {
+  if constexpr (D >= 128) {  // rows of 256 or 512 bytes: both start on bank 0
     return ((k & 7) << 1) | ((k >> 3) & 1);
   } else {
     const int x = (k >> 1) & 7;
@@ -216,8 +277,9 @@ constexpr int kComplete = 1 << 10; // the piece is the whole segment
 constexpr int kSecond = 1 << 11;   // partial goes to the wave's second slot
 
 template <int D, int HS, bool BF16>
-__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnParams p) {
+__global__ __launch_bounds__(64 * decode_wg_waves(D)) void decode_kernel(AttnParams p) {
   using E = Elem<BF16>;
+  constexpr int kDecodeWaves = decode_wg_waves(D);
   constexpr int ROW = 2 * D;                      // bytes of one key of one kv head
   constexpr int CPR = ROW / 16;                   // 16-byte chunks per row
   constexpr int KPI = 1024 / ROW;                 // rows per 1 KB direct load
@@ -579,9 +641,9 @@ hipError_t launch_decode(const AttnParams& p, int head_size, int head_slots, boo
 #define PA_DECODE(DD, HH)                                                                         \
   if (head_size == DD && head_slots == HH) {                                                      \
     if (bf16)                                                                                     \
-      hipLaunchKernelGGL((decode_kernel<DD, HH, true>), dim3(grid), dim3(kDecodeThreads), 0, s, p);  \
+      hipLaunchKernelGGL((decode_kernel<DD, HH, true>), dim3(grid), dim3(64 * decode_wg_waves(DD)), 0, s, p); \
     else                                                                                          \
-      hipLaunchKernelGGL((decode_kernel<DD, HH, false>), dim3(grid), dim3(kDecodeThreads), 0, s, p); \
+      hipLaunchKernelGGL((decode_kernel<DD, HH, false>), dim3(grid), dim3(64 * decode_wg_waves(DD)), 0, s, p); \
     return hipGetLastError();                                                                     \
   }
   PA_DECODE(128, 4)
@@ -590,6 +652,9 @@ hipError_t launch_decode(const AttnParams& p, int head_size, int head_slots, boo
   PA_DECODE(64, 4)
   PA_DECODE(64, 8)
   PA_DECODE(64, 16)
+  PA_DECODE(256, 4)
+  PA_DECODE(256, 8)
+  PA_DECODE(256, 16)
 #undef PA_DECODE
   return hipErrorInvalidValue;
 }

@@ -26,15 +26,18 @@
 namespace pa {
 
 // ---- tiling constants -----------------------------------------------------
-constexpr int kDecodeWaves = 4;       // waves per decode workgroup
-constexpr int kDecodeThreads = 64 * kDecodeWaves;
+// waves per decode workgroup: 4, or 2 at head_size 256 (so that a ring of
+// three or four 16-key tiles per wave still fits in LDS)
+__host__ __device__ constexpr int decode_wg_waves(int D) { return D > 128 ? 2 : 4; }
 constexpr int kDecodeTile = 16;       // keys per decode tile
 constexpr int kDecodeUnitHeads = 16;  // query heads of one decode segment (MFMA N)
 constexpr int kDecodeWindow = 64;     // block-table entries a wave holds (one per lane)
-constexpr int kPrefillThreads = 512;  // 8 waves per prefill workgroup
 constexpr int kPrefillRows = 128;     // (position, head) rows per prefill workgroup (two half-tiles)
 constexpr int kPrefillKeys = 64;      // keys per prefill step (32 per kv group)
 constexpr int kPlanThreads = 1024;    // threads of the planning workgroup
+// zero bytes read in place of absent query heads and of keys past a history:
+// one key row of the largest head size (256 x 2 bytes)
+constexpr int kZeroPageBytes = 512;
 
 // ---- control block at the start of the workspace ---------------------------
 enum CtrlSlot {
@@ -71,16 +74,17 @@ __host__ __device__ constexpr int decode_q_bytes(int D, int hslots) {
 __host__ __device__ constexpr int decode_slot_bytes(int D, int hslots) {
   return 2 * kDecodeTile * 2 * D + decode_q_bytes(D, hslots);
 }
-// ring depth: as many slots as fit four waves in about 150 KB, at most 4
+// ring depth: as many slots as fit the workgroup's waves in about 150 KB, at
+// most 4
 __host__ __device__ constexpr int decode_ring(int D, int hslots) {
-  return (150 * 1024) / (kDecodeWaves * decode_slot_bytes(D, hslots)) > 4
+  return (150 * 1024) / (decode_wg_waves(D) * decode_slot_bytes(D, hslots)) > 4
              ? 4
-             : (150 * 1024) / (kDecodeWaves * decode_slot_bytes(D, hslots));
+             : (150 * 1024) / (decode_wg_waves(D) * decode_slot_bytes(D, hslots));
 }
 // per wave: the ring, a 16-byte piece record per slot, 512 bytes of
 // prefetched metadata
 __host__ __device__ constexpr int decode_lds_bytes(int D, int hslots) {
-  return kDecodeWaves * (decode_ring(D, hslots) * (decode_slot_bytes(D, hslots) + 16) + 512);
+  return decode_wg_waves(D) * (decode_ring(D, hslots) * (decode_slot_bytes(D, hslots) + 16) + 512);
 }
 __host__ __device__ constexpr int decode_wg_per_cu(int D, int hslots) {
   return (160 * 1024) / decode_lds_bytes(D, hslots) > 0 ? (160 * 1024) / decode_lds_bytes(D, hslots) : 1;
@@ -96,7 +100,7 @@ __host__ __device__ inline int64_t decode_wave_begin(int w, int64_t T, int W) {
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct WorkspaceLayout {
   size_t ctrl;         // int32[kCtrlSlots]
-  size_t zeros;        // 256 zero bytes, read in place of absent query heads
+  size_t zeros;        // kZeroPageBytes zero bytes, read in place of absent rows
   size_t dec_seq;      // int4[batch + 1]: (b, token, L, first tile); last = (.., .., .., T)
   size_t dec_start;    // int32[8 * (waves + 1)]: per wave (d, unit, tile, g, b, token, L, first tile)
   size_t pf_items;     // int2[max_pf_items]    (sequence, half-tile pair)
@@ -120,7 +124,7 @@ struct ScatterPlanParams {
   const int32_t* block_table;
   const int32_t* slot_mapping; // may be null
   int32_t* ws_ctrl;
-  int32_t* zeros;              // 64 ints cleared by the plan
+  int32_t* zeros;              // kZeroPageBytes / 4 ints cleared by the plan
   int4* dec_seq;
   int32_t* dec_start;
   int2* pf_items;
@@ -143,7 +147,7 @@ struct AttnParams {
   const int32_t* past;
   const int32_t* block_table;
   uint16_t* out;               // [N, H*D] in the data type
-  const uint16_t* zeros;       // 256 zero bytes
+  const uint16_t* zeros;       // kZeroPageBytes zero bytes
   int32_t* ws_ctrl;
   const int2* items;           // prefill items
   const int4* dec_seq;

@@ -52,6 +52,7 @@
 // first the queue of the XCD it runs on (workgroup id mod 8), so each XCD's
 // L2 holds the K/V of few heads; when its queue is empty it helps the others.
 #include <type_traits>
+#include <utility>
 
 #include "pa_elem.h"
 #include "pa_internal.h"
@@ -67,14 +68,18 @@ typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kGroupKeys = kPrefillKeys / 2;  // keys per kv group per step
-constexpr int kRing = 4;                      // LDS buffers (steps in flight + 1)
 constexpr int kSlotWindow = 2048;             // 16-key cache slots held in LDS
-// steps per slot window: 4 slots per step, 3 steps fetched ahead, and a whole
-// number of ring turns
-constexpr int kChunk = (kSlotWindow / 4 - 3) / kRing * kRing;
-static_assert(4 * (kChunk + 3) <= kSlotWindow && kChunk % kRing == 0, "slot window");
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <typename F, int... I>
+__device__ __attribute__((always_inline)) inline void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __attribute__((always_inline)) inline void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // x combined with the same register of lane^32 (v_permlane32_swap: a VALU
 // exchange of the two wave halves, no LDS round trip)
@@ -103,28 +108,46 @@ __device__ inline void plain_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Head sizes up to 128: eight waves, two kv groups, a ring of four steps.
+// Head size 256: the Q and O of a 32-row group take 192 registers, so a wave
+// needs a SIMD of its own (four waves, up to 512 registers each); each wave
+// then takes all 64 keys of a step as two 32-key sub-steps (one kv group),
+// and a ring of two steps (64 KB each) fits in LDS.
 template <int D>
 struct PrefillShape {
+  static constexpr bool WIDE = D > 128;
+  static constexpr int WAVES = WIDE ? 4 : 8;         // waves per workgroup
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int KVG = WIDE ? 1 : 2;           // kv groups (waves sharing a row group)
+  static constexpr int SUBS = 2 / KVG;               // 32-key sub-steps per wave and step
+  static constexpr int RING = WIDE ? 2 : 4;          // LDS buffers per tensor
   static constexpr int ROWB = D * 2;                 // bytes per key row
   static constexpr int CPR = D / 8;                  // 16-byte chunks per row
   static constexpr int ROWS_PER_LOAD = 64 / CPR;     // rows per 1 KB direct load
-  static constexpr int WAVE_ROWS = kPrefillKeys / 8; // rows of K (and V) each wave fetches
+  static constexpr int WAVE_ROWS = kPrefillKeys / WAVES;  // rows of K (and V) each wave fetches
   static constexpr int LOADS = WAVE_ROWS / ROWS_PER_LOAD;  // direct loads per wave per tensor
   static constexpr int BUF = kPrefillKeys * ROWB;    // bytes per K (or V) buffer
   static constexpr int QK_STEPS = D / 16;            // MFMA k-steps over the head dim
   static constexpr int O_TILES = D / 32;             // 32-wide d tiles of O^T
-  // chunk swizzles (in 16-byte chunks) of K and V rows
-  static __device__ int k_swz(int row) { return D == 128 ? (row & 15) : (row & 7); }
-  static __device__ int v_swz(int row) { return D == 128 ? ((row & 3) << 2) : 0; }
+  // steps per slot window: 4 slots per step, RING - 1 steps fetched ahead,
+  // and a whole number of ring turns
+  static constexpr int CHUNK = (kSlotWindow / 4 - (RING - 1)) / RING * RING;
+  static_assert(4 * (CHUNK + RING - 1) <= kSlotWindow && CHUNK % RING == 0, "slot window");
+  // chunk swizzles (in 16-byte chunks) of K and V rows; rows of 256 and 512
+  // bytes both start on bank 0, so they share one
+  static __device__ int k_swz(int row) { return D >= 128 ? (row & 15) : (row & 7); }
+  static __device__ int v_swz(int row) { return D >= 128 ? ((row & 3) << 2) : 0; }
 };
 
 template <int D, bool BF16>
-__global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) {
+__global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnParams p) {
   using S = PrefillShape<D>;
   using E = Elem<BF16>;
   typedef typename E::x8 x8;
   typedef typename E::x4 x4;
   constexpr int ROWB = S::ROWB, CPR = S::CPR;
+  constexpr int kRing = S::RING;
+  constexpr int kChunk = S::CHUNK;
   static_assert(S::LOADS >= 1, "loads per wave");
 
   // one LDS object per ring buffer and tensor: the compiler can then see that
@@ -132,12 +155,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
   // those reads wait for the fill
   __shared__ __align__(16) char k_lds0[S::BUF];
   __shared__ __align__(16) char k_lds1[S::BUF];
-  __shared__ __align__(16) char k_lds2[S::BUF];
-  __shared__ __align__(16) char k_lds3[S::BUF];
+  __shared__ __align__(16) char k_lds2[kRing > 2 ? S::BUF : 16];
+  __shared__ __align__(16) char k_lds3[kRing > 2 ? S::BUF : 16];
   __shared__ __align__(16) char v_lds0[S::BUF];
   __shared__ __align__(16) char v_lds1[S::BUF];
-  __shared__ __align__(16) char v_lds2[S::BUF];
-  __shared__ __align__(16) char v_lds3[S::BUF];
+  __shared__ __align__(16) char v_lds2[kRing > 2 ? S::BUF : 16];
+  __shared__ __align__(16) char v_lds3[kRing > 2 ? S::BUF : 16];
   __shared__ int slot_lds[kSlotWindow];
   __shared__ int lds_item;
   auto kbuf = [&](int b) -> char* { return b == 0 ? k_lds0 : b == 1 ? k_lds1 : b == 2 ? k_lds2 : k_lds3; };
@@ -146,9 +169,10 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // waves w and w+4 run on one SIMD: same kv group, row groups r and r+2
-  const int rg = (wave & 1) + 2 * (wave >> 2);  // row group (rows 32*rg .. +31)
-  const int kvg = (wave >> 1) & 1;              // kv group
+  // eight waves: w and w+4 run on one SIMD, same kv group, row groups r and
+  // r+2; four waves: one row group each, all keys
+  const int rg = S::WIDE ? wave : (wave & 1) + 2 * (wave >> 2);  // row group (rows 32*rg .. +31)
+  const int kvg = S::WIDE ? 0 : (wave >> 1) & 1;                  // kv group
   const int half = rg >> 1;                     // half-tile of the pair
   const int lrow = lane & 31;   // MFMA column owned by this lane
   const int lhalf = lane >> 5;  // which k-half of the MFMA operand
@@ -164,8 +188,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
   {
     const int segments = p.ws_ctrl[kCtrlDecodeSeqs] * p.decode_units;
     const int T = p.ws_ctrl[kCtrlDecodeTiles];
-    const int nw = static_cast<int>(gridDim.x) * (kPrefillThreads / 64);
-    for (int task = static_cast<int>(blockIdx.x) * (kPrefillThreads / 64) + wave; task < segments; task += nw)
+    const int nw = static_cast<int>(gridDim.x) * S::WAVES;
+    for (int task = static_cast<int>(blockIdx.x) * S::WAVES + wave; task < segments; task += nw)
       merge_segment<D, BF16>(p, task, T, lane);
   }
 
@@ -178,19 +202,24 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
   // other wave's matrix products
   if (wave >= 4) __builtin_amdgcn_s_setprio(1);
 
-  // per-lane LDS byte offsets (everything else is an immediate)
-  int koff[S::QK_STEPS];  // K fragment kk of row kvg*32 + lrow
+  // per-lane LDS byte offsets (everything else is an immediate).  The
+  // swizzles permute chunks within 16-chunk (256-byte) halves of a row, so
+  // for head size 256 fragment kk + 8 (d tile mt + 4) sits 256 bytes after
+  // fragment kk (d tile mt): one register serves both.
+  constexpr int KOFF = S::QK_STEPS < 8 ? S::QK_STEPS : 8;
+  constexpr int VOFF = S::O_TILES < 4 ? S::O_TILES : 4;
+  int koff[KOFF];  // K fragment kk of row kvg*32 + lrow
 #pragma unroll
-  for (int kk = 0; kk < S::QK_STEPS; ++kk) {
+  for (int kk = 0; kk < KOFF; ++kk) {
     const int row = kvg * kGroupKeys + lrow;
     koff[kk] = row * ROWB + (((2 * kk + lhalf) ^ S::k_swz(row)) << 4);
   }
-  int voff[S::O_TILES];  // transpose-read address of d tile mt (keys kvg*32 + ...)
+  int voff[VOFF];  // transpose-read address of d tile mt (keys kvg*32 + ...)
   {
     const int grp = lane >> 4, i = lane & 15, r = i >> 2, q = i & 3;
     const int row = kvg * kGroupKeys + 4 * (grp >> 1) + r;
 #pragma unroll
-    for (int mt = 0; mt < S::O_TILES; ++mt) {
+    for (int mt = 0; mt < VOFF; ++mt) {
       const int chunk = 4 * mt + 2 * (grp & 1) + (q >> 1);
       voff[mt] = row * ROWB + ((chunk ^ S::v_swz(row)) << 4) + ((q & 1) << 3);
     }
@@ -288,7 +317,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
     auto fill_window = [&](int first) {
       gbase = first;
       const int n = min(kSlotWindow, ngroups - first);
-      for (int i = tid; i < n; i += kPrefillThreads) {
+      for (int i = tid; i < n; i += S::THREADS) {
         const int key = 16 * (first + i);
         slot_lds[i] = btab[key / bs] * bs + key % bs;
       }
@@ -335,30 +364,42 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
     // PV (four accumulators in turn).  The K fragments of the step are all
     // read before the first product and the V fragments before the softmax,
     // so the step waits for one LDS round trip, not one per product.
-    auto compute = [&](auto buf_tag, int jk, bool masked) __attribute__((always_inline)) {
+    // (sub: the 32-key sub-step of a wave that takes all keys of a step; its
+    // rows sit 32 rows further into the buffer, swizzled alike)
+    auto compute = [&](auto buf_tag, auto sub_tag, int jk, bool masked) __attribute__((always_inline)) {
       constexpr int buf = decltype(buf_tag)::value;
-      x8 kf[S::QK_STEPS];
-#pragma unroll
-      for (int kk = 0; kk < S::QK_STEPS; ++kk) kf[kk] = *reinterpret_cast<const x8*>(kbuf(buf) + koff[kk]);
-      asm volatile("" ::: "memory");  // keep the reads ahead of the products
+      constexpr int so = decltype(sub_tag)::value * kGroupKeys * ROWB;
+      // K fragments in batches of at most 8 (one batch up to head size 128)
       f32x16_t s = f32x16_t{};
+      static_for<S::QK_STEPS / KOFF>([&](auto kb) __attribute__((always_inline)) {
+        constexpr int k0 = decltype(kb)::value * KOFF;
+        x8 kf[KOFF];
 #pragma unroll
-      for (int kk = 0; kk < S::QK_STEPS; ++kk) s = E::mfma_32x32x16(kf[kk], qf[kk], s);
+        for (int kk = 0; kk < KOFF; ++kk)
+          kf[kk] = *reinterpret_cast<const x8*>(kbuf(buf) + so + 256 * decltype(kb)::value + koff[kk]);
+        asm volatile("" ::: "memory");  // keep the reads ahead of the products
+#pragma unroll
+        for (int kk = 0; kk < KOFF; ++kk) s = E::mfma_32x32x16(kf[kk], qf[k0 + kk], s);
+      });
       // V^T fragments, read while the products and the softmax run: the
       // transpose read of rows key0..key0+3 (key0 = 16ks + 4*lhalf, then +8)
       // gives each lane the 4 keys of its d column, in the key order of the
       // P^T registers
-      x8 va[2][S::O_TILES];
+      // (head size 256: only the first 16 keys' fragments here, the rest
+      // after the softmax, to bound the registers in flight)
+      constexpr int VPRE = S::O_TILES > 4 ? 1 : 2;
+      auto read_v = [&](int ks, int mt) __attribute__((always_inline)) -> x8 {
+        char* vb = vbuf(buf) + so + voff[mt % VOFF] + 256 * (mt / VOFF) + 16 * ks * ROWB;
+        const fp16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((PA_LDS fp16x4_t*)vb);
+        const fp16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((PA_LDS fp16x4_t*)(vb + 8 * ROWB));
+        return __builtin_shufflevector(__builtin_bit_cast(x4, lo), __builtin_bit_cast(x4, hi), 0, 1, 2, 3, 4, 5, 6,
+                                       7);
+      };
+      x8 va[VPRE][S::O_TILES];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int ks = 0; ks < VPRE; ++ks)
 #pragma unroll
-        for (int mt = 0; mt < S::O_TILES; ++mt) {
-          char* vb = vbuf(buf) + voff[mt] + 16 * ks * ROWB;
-          const fp16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((PA_LDS fp16x4_t*)vb);
-          const fp16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((PA_LDS fp16x4_t*)(vb + 8 * ROWB));
-          va[ks][mt] = __builtin_shufflevector(__builtin_bit_cast(x4, lo), __builtin_bit_cast(x4, hi),
-                                               0, 1, 2, 3, 4, 5, 6, 7);
-        }
+        for (int mt = 0; mt < S::O_TILES; ++mt) va[ks][mt] = read_v(ks, mt);
       asm volatile("" ::: "memory");
       // register i holds key jk + 8(i/4) + 4*lhalf + i%4
       if (masked) {
@@ -404,10 +445,17 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
       l += la + lb;
       // O^T[d][row] += V^T[d][key] P^T[key][row]
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int ks = 0; ks < VPRE; ++ks)
 #pragma unroll
         for (int mt = 0; mt < S::O_TILES; ++mt)
           o[mt] = E::mfma_32x32x16(va[ks][mt], pb[ks], o[mt]);
+      if constexpr (VPRE == 1) {
+        x8 vb[S::O_TILES];
+#pragma unroll
+        for (int mt = 0; mt < S::O_TILES; ++mt) vb[mt] = read_v(1, mt);
+#pragma unroll
+        for (int mt = 0; mt < S::O_TILES; ++mt) o[mt] = E::mfma_32x32x16(vb[mt], pb[1], o[mt]);
+      }
     };
 
     // Step j computes from ring buffer j % 4 and fetches step j + 3 into ring
@@ -415,22 +463,36 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
     // barrier that ended it).  Each step issues 2 * LOADS direct loads per
     // wave, so "step j + 1 landed" is "at most 4 * LOADS loads outstanding"
     // while steps j + 2 and j + 3 are both in flight.
+    //
+    // With a ring of two (head size 256) the fill of step j + 1 goes into
+    // buffer (j + 1) % 2 at the start of step j (its last reader, step j - 1,
+    // ended at the barrier) and lands before the barrier that ends step j.
     auto step = [&](auto buf_tag, int jstep) __attribute__((always_inline)) {
       constexpr int buf = decltype(buf_tag)::value;
       constexpr int nbuf = (buf + kRing - 1) % kRing;
       const int s_next = jstep + kRing - 1;  // step fetched now
       const bool more = s_next < nsteps;
       const int slot16 = slot_of(s_next);  // (in the window; unused past the history)
-      const int jk = jstep * kPrefillKeys + kvg * kGroupKeys;  // first key of this wave's half
-      if (jk <= wave_last) compute(buf_tag, jk, jk + kGroupKeys - 1 > wave_first);
-      // the fills of step j + 3, after the products: issued in one burst they
-      // stream while the other waves compute and the next step runs
-      if (more) issue(std::integral_constant<int, nbuf>{}, s_next, slot16, 0, S::LOADS);
-      // a plain barrier: __syncthreads() would also wait for the fills still
-      // in flight.  The waits go through the builtin so that the compiler
-      // knows which fills have landed and adds no wait of its own.
-      if (more) wait_fills<4 * S::LOADS>();
-      else wait_fills<0>();
+      if constexpr (kRing == 2) {
+        if (more) issue(std::integral_constant<int, nbuf>{}, s_next, slot16, 0, S::LOADS);
+      }
+      static_for<S::SUBS>([&](auto sub) __attribute__((always_inline)) {
+        // first key of this wave's 32 keys
+        const int jk = jstep * kPrefillKeys + (kvg + decltype(sub)::value) * kGroupKeys;
+        if (jk <= wave_last) compute(buf_tag, sub, jk, jk + kGroupKeys - 1 > wave_first);
+      });
+      if constexpr (kRing == 2) {
+        wait_fills<0>();
+      } else {
+        // the fills of step j + 3, after the products: issued in one burst
+        // they stream while the other waves compute and the next step runs
+        if (more) issue(std::integral_constant<int, nbuf>{}, s_next, slot16, 0, S::LOADS);
+        // a plain barrier: __syncthreads() would also wait for the fills
+        // still in flight.  The waits go through the builtin so that the
+        // compiler knows which fills have landed and adds no wait of its own.
+        if (more) wait_fills<4 * S::LOADS>();
+        else wait_fills<0>();
+      }
       plain_barrier();
     };
 
@@ -438,9 +500,11 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
     // steps 0..2 in flight before the first step (nested conditions: no path
     // that the compiler considers skips a step and fetches a later one)
     issue(std::integral_constant<int, 0>{}, 0, slot_of(0), 0, S::LOADS);
-    if (nsteps > 2) {
+    if constexpr (kRing == 2) {
+      wait_fills<0>();
+    } else if (nsteps > 2) {
       issue(std::integral_constant<int, 1>{}, 1, slot_of(1), 0, S::LOADS);
-      issue(std::integral_constant<int, 2>{}, 2, slot_of(2), 0, S::LOADS);
+      issue(std::integral_constant<int, 2 % kRing>{}, 2, slot_of(2), 0, S::LOADS);
       wait_fills<4 * S::LOADS>();
     } else {
       if (nsteps > 1) issue(std::integral_constant<int, 1>{}, 1, slot_of(1), 0, S::LOADS);
@@ -458,39 +522,43 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
       const int c1 = min(nsteps, c0 + kChunk);
       int j0 = c0;
       for (; j0 + kRing <= c1; j0 += kRing) {
-        step(std::integral_constant<int, 0>{}, j0);
-        step(std::integral_constant<int, 1>{}, j0 + 1);
-        step(std::integral_constant<int, 2>{}, j0 + 2);
-        step(std::integral_constant<int, 3>{}, j0 + 3);
+        static_for<kRing>([&](auto r) __attribute__((always_inline)) { step(r, j0 + decltype(r)::value); });
       }
       // (nested so that no path skips a step and runs a later one)
       if (j0 < c1) {
         step(std::integral_constant<int, 0>{}, j0);
-        if (j0 + 1 < c1) {
-          step(std::integral_constant<int, 1>{}, j0 + 1);
-          if (j0 + 2 < c1) step(std::integral_constant<int, 2>{}, j0 + 2);
+        if constexpr (kRing > 2) {
+          if (j0 + 1 < c1) {
+            step(std::integral_constant<int, 1>{}, j0 + 1);
+            if (j0 + 2 < c1) step(std::integral_constant<int, 2 % kRing>{}, j0 + 2);
+          }
         }
       }
     }
 
     // merge the two kv groups (group 0 first) and write.  Row group r's O of
     // kv group 1 goes to K buffer r ([O_TILES*16][64 lanes] floats), (m, l)
-    // of all row groups to V buffer 0.
+    // of all row groups to V buffer 0.  (One kv group: nothing to merge.)
     wait_fills<0>();  // (the last steps already waited)
     float* xo = reinterpret_cast<float*>(kbuf(rg));
     float* xml = reinterpret_cast<float*>(v_lds0);
-    if (kvg == 1) {
+    if constexpr (S::KVG == 2) {
+      if (kvg == 1) {
 #pragma unroll
-      for (int mt = 0; mt < S::O_TILES; ++mt)
+        for (int mt = 0; mt < S::O_TILES; ++mt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) xo[(mt * 16 + i) * 64 + lane] = o[mt][i];
-      xml[(rg * 2 + 0) * 64 + lane] = m;
-      xml[(rg * 2 + 1) * 64 + lane] = l;
+          for (int i = 0; i < 16; ++i) xo[(mt * 16 + i) * 64 + lane] = o[mt][i];
+        xml[(rg * 2 + 0) * 64 + lane] = m;
+        xml[(rg * 2 + 1) * 64 + lane] = l;
+      }
+      __syncthreads();
     }
-    __syncthreads();
     if (kvg == 0 && wave_valid) {
-      const float m1 = xml[(rg * 2 + 0) * 64 + lane];
-      const float l1 = xml[(rg * 2 + 1) * 64 + lane];
+      float m1 = kNegInf, l1 = 0.f;
+      if constexpr (S::KVG == 2) {
+        m1 = xml[(rg * 2 + 0) * 64 + lane];
+        l1 = xml[(rg * 2 + 1) * 64 + lane];
+      }
       const float mm = fmaxf(m, m1);
       const float a0 = fast_exp2(m - mm), a1 = fast_exp2(m1 - mm);
       const float lt = swap_halves_sum(l * a0 + l1 * a1);
@@ -512,9 +580,14 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
               const int ir = 4 * q + 2 * e;
-              const float* x1 = &xo[(mt * 16 + ir) * 64 + lane];
-              v[2 * e] = (o[mt][ir] * a0 + x1[0] * a1) * inv;
-              v[2 * e + 1] = (o[mt][ir + 1] * a0 + x1[64] * a1) * inv;
+              if constexpr (S::KVG == 2) {
+                const float* x1 = &xo[(mt * 16 + ir) * 64 + lane];
+                v[2 * e] = (o[mt][ir] * a0 + x1[0] * a1) * inv;
+                v[2 * e + 1] = (o[mt][ir + 1] * a0 + x1[64] * a1) * inv;
+              } else {
+                v[2 * e] = o[mt][ir] * inv;
+                v[2 * e + 1] = o[mt][ir + 1] * inv;
+              }
               w[e] = static_cast<uint32_t>(E::bits(v[2 * e])) | (static_cast<uint32_t>(E::bits(v[2 * e + 1])) << 16);
             }
             *reinterpret_cast<uint2*>(orow + 32 * mt + 8 * q + 4 * lhalf) = make_uint2(w[0], w[1]);
@@ -529,29 +602,32 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(AttnParams p) 
 
 template <int D>
 constexpr size_t prefill_smem() {
-  return 2 * kRing * static_cast<size_t>(PrefillShape<D>::BUF) + kSlotWindow * sizeof(int) + 16;
+  using S = PrefillShape<D>;
+  return 2 * S::RING * static_cast<size_t>(S::BUF) + (S::RING > 2 ? 0 : 4 * 16) + kSlotWindow * sizeof(int) + 16;
 }
 // the merge area (O of one row group) must fit one K buffer, (m, l) one V buffer
 static_assert(4 * 16 * 64 * sizeof(float) <= PrefillShape<128>::BUF, "merge area");
 static_assert(2 * 16 * 64 * sizeof(float) <= PrefillShape<64>::BUF, "merge area");
 static_assert(prefill_smem<128>() <= 160 * 1024, "LDS budget");
+static_assert(prefill_smem<256>() <= 160 * 1024, "LDS budget");
 
 template <int D>
 hipError_t launch_prefill_t(const AttnParams& p, bool bf16, int grid, hipStream_t s) {
   if (bf16)
-    hipLaunchKernelGGL((prefill_kernel<D, true>), dim3(grid), dim3(kPrefillThreads), 0, s, p);
+    hipLaunchKernelGGL((prefill_kernel<D, true>), dim3(grid), dim3(PrefillShape<D>::THREADS), 0, s, p);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, false>), dim3(grid), dim3(kPrefillThreads), 0, s, p);
+    hipLaunchKernelGGL((prefill_kernel<D, false>), dim3(grid), dim3(PrefillShape<D>::THREADS), 0, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 size_t prefill_lds_bytes(int head_size) {
-  return head_size == 128 ? prefill_smem<128>() : prefill_smem<64>();
+  return head_size == 256 ? prefill_smem<256>() : head_size == 128 ? prefill_smem<128>() : prefill_smem<64>();
 }
 
 hipError_t launch_prefill(const AttnParams& p, int head_size, bool bf16, int grid, hipStream_t s) {
+  if (head_size == 256) return launch_prefill_t<256>(p, bf16, grid, s);
   if (head_size == 128) return launch_prefill_t<128>(p, bf16, grid, s);
   if (head_size == 64) return launch_prefill_t<64>(p, bf16, grid, s);
   return hipErrorInvalidValue;

@@ -88,7 +88,8 @@ __device__ void plan(const ScatterPlanParams& p) {
     tile_base += tot.y;
     pf_base += tot.z;
   }
-  if (tid < 64) p.zeros[tid] = 0;
+  static_assert(kZeroPageBytes / 4 <= kPlanThreads, "zero page");
+  if (tid < kZeroPageBytes / 4) p.zeros[tid] = 0;
   if (tid == 0) {
     p.dec_seq[dec_base] = make_int4(0, 0, 0, tile_base);  // sentinel: T
     p.ws_ctrl[kCtrlDecodeTiles] = tile_base;

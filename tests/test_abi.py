@@ -120,6 +120,7 @@ def test_workspace_bytes_static_bound():
     (dict(dtype=2), WS),                                 # bfloat16 passes validation
     (dict(block_size=8), UNSUP),
     (dict(query_width=4 * 32, cache_head_size=32), UNSUP),  # D=32 not built
+    (dict(query_width=4 * 256, cache_head_size=256), WS),   # D=256 passes validation
     (dict(query=None), NULL),
     (dict(output=None), NULL),
     (dict(query=FAKE + 2), ALIGN),

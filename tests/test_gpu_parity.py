@@ -446,3 +446,45 @@ def test_bf16_first_token_and_determinism():
     o2 = d.run().clone()
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+# ------------------------------------------------------------------ head_size 256
+
+HD256 = [
+    # (q_lens, past_lens, H, Hkv, bs)
+    ([1, 5, 1, 70, 200, 1, 0, 33], [0, 33, 4000, 17, 300, 1500, 9, 64], 16, 2, 16),  # G=8
+    ([1, 1, 1, 1, 2, 130], [9000, 12000, 700, 1, 3, 0], 4, 4, 64),                  # MHA, cut decodes
+    ([1, 17, 1, 64], [2500, 100, 31, 6000], 16, 1, 256),                              # G=16
+]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("case", range(len(HD256)))
+def test_head_size_256(case, dtype):
+    q, p, H, Hkv, bs = HD256[case]
+    b = W.make_batch(q, p, num_heads=H, kv_num_heads=Hkv, head_size=256, block_size=bs,
+                     seed=300 + case, name=f"hd256_{case}", dtype=dtype)
+    check(b, rows=sample_rows(b, per_seq=12, seed=case))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_head_size_256_long_prefill_and_state(dtype):
+    b = W.make_batch([700, 1, 1], [1100, 20000, 3], num_heads=8, kv_num_heads=2, head_size=256,
+                     block_size=256, seed=310, name="hd256_long", dtype=dtype, packed=True,
+                     slot_mode="drop", drop_count=7)
+    rows = sample_rows(b, per_seq=30, seed=3)
+    check(b, rows=rows)
+    d = DevBatch(b)
+    f32 = torch.empty((b.num_tokens, b.num_heads * 256), dtype=torch.float32, device=DEV)
+    out, lse = d.run(return_lse=True, output_f32=f32)
+    torch.cuda.synchronize()
+    ref, _, _, rlse = oracle.paged_attention(b.query, b.key, b.value, b.key_cache, b.value_cache,
+                                             b.cum, b.past, b.block_table, b.slot_mapping,
+                                             num_heads=b.num_heads, kv_num_heads=b.kv_num_heads,
+                                             scale=b.scale, rows=rows, with_lse=True)
+    o_low, o32, l32 = to_host(out), f32.cpu().numpy(), lse.cpu().numpy()
+    assert rounding_of(o32, o_low)
+    e_o = np.max(np.abs(o32[rows].astype(np.float64) - ref[rows]))
+    e_l = np.max(np.abs(l32[rows].astype(np.float64) - rlse[rows]))
+    say(f"      state: max|err| out_f32 {e_o:.3e}, lse {e_l:.3e}")
+    assert e_o <= tol(b) and e_l <= (LSE_TOL_BF16 if dtype == "bf16" else LSE_TOL)

@@ -28,7 +28,9 @@ Draw order for one batch (fixed so that a seed names one input exactly):
 With ``meta_only=True`` the draws stop after step 4 and the data tensors are
 left uninitialised (only their shapes are meaningful).
 
-Data type: every workload takes ``dtype`` "f16" (default) or "bf16".  The
+Data type: every workload takes ``dtype`` "f16" (default) or "bf16", and
+``head_size`` (0 = its own; 256 for the head_size-256 variant: same heads,
+lengths and pages, wider heads).  The
 float32 draws are the same for both; they are rounded to nearest (ties to
 even) to the type.  numpy has no bfloat16, so bf16 tensors are numpy uint16
 arrays holding the bit patterns (the upper half of the float32 pattern).
@@ -276,40 +278,40 @@ def _fill(rng, name, seed, q_lens, past, table, nb, H, Hkv, D, bs, packed, slot_
 # the five named workloads
 # ---------------------------------------------------------------------------
 
-def tiny(seed: int = 0, meta_only: bool = False, dtype: str = "f16") -> Batch:
+def tiny(seed: int = 0, meta_only: bool = False, dtype: str = "f16", head_size: int = 0) -> Batch:
     """B=2, H/Hkv=4/2, D=64, block_size 16, 8 pages, past [5,20], new [3,1];
     block_table is a random permutation of all 8 pages, no slot_mapping."""
     rng = np.random.default_rng(seed)
     q_lens = np.array([3, 1])
     past = np.array([5, 20])
     table = rng.permutation(8).astype(np.int32).reshape(2, 4)
-    return _fill(rng, "tiny", seed, q_lens, past, table, 8, 4, 2, 64, 16, False, None,
+    return _fill(rng, "tiny", seed, q_lens, past, table, 8, 4, 2, head_size or 64, 16, False, None,
                  0, 0.0, "B=2 4/2 heads D=64 bs=16 NB=8 past=[5,20] q=[3,1]", meta_only, dtype)
 
 
-def pure_decode(seed: int = 0, meta_only: bool = False, dtype: str = "f16") -> Batch:
+def pure_decode(seed: int = 0, meta_only: bool = False, dtype: str = "f16", head_size: int = 0) -> Batch:
     """B=64 single-token decodes, past ~ U[512,4096], 32/8 heads, D=128,
     block_size 16, pool sized to fit, shuffled page ids."""
     rng = np.random.default_rng(seed)
     q_lens = np.ones(64, dtype=np.int64)
     past = rng.integers(512, 4096 + 1, size=64)
     table, nb, _ = allocate_pages(rng, past + q_lens, 16)
-    return _fill(rng, "pure_decode", seed, q_lens, past, table, nb, 32, 8, 128, 16, False,
+    return _fill(rng, "pure_decode", seed, q_lens, past, table, nb, 32, 8, head_size or 128, 16, False,
                  None, 0, 0.0, "B=64 q=1 past~U[512,4096] 32/8 D=128 bs=16", meta_only, dtype)
 
 
-def mixed(seed: int = 0, meta_only: bool = False, dtype: str = "f16") -> Batch:
+def mixed(seed: int = 0, meta_only: bool = False, dtype: str = "f16", head_size: int = 0) -> Batch:
     """B=16: 8 decodes + 8 chunks of 512 new tokens (order shuffled), past ~
     U[0,8192], 32/8 heads, D=128, block_size 256, random page table."""
     rng = np.random.default_rng(seed)
     q_lens = rng.permutation(np.array([1] * 8 + [512] * 8))
     past = rng.integers(0, 8192 + 1, size=16)
     table, nb, _ = allocate_pages(rng, past + q_lens, 256)
-    return _fill(rng, "mixed", seed, q_lens, past, table, nb, 32, 8, 128, 256, False, None,
+    return _fill(rng, "mixed", seed, q_lens, past, table, nb, 32, 8, head_size or 128, 256, False, None,
                  0, 0.0, "B=16 (8x1 + 8x512) past~U[0,8192] 32/8 D=128 bs=256", meta_only, dtype)
 
 
-def long_prefill(seed: int = 0, meta_only: bool = False, dtype: str = "f16") -> Batch:
+def long_prefill(seed: int = 0, meta_only: bool = False, dtype: str = "f16", head_size: int = 0) -> Batch:
     """One sequence, 2048 new tokens on top of 2048 cached (second half of a
     4096-token sequence), 16/4 heads (one of two tensor-parallel ranks of a
     32/8 model), D=128, block_size 256, 16 pages in shuffled order."""
@@ -317,11 +319,11 @@ def long_prefill(seed: int = 0, meta_only: bool = False, dtype: str = "f16") -> 
     q_lens = np.array([2048])
     past = np.array([2048])
     table = rng.permutation(16).astype(np.int32)[None, :]
-    return _fill(rng, "long_prefill", seed, q_lens, past, table, 16, 16, 4, 128, 256,
+    return _fill(rng, "long_prefill", seed, q_lens, past, table, 16, 16, 4, head_size or 128, 256,
                  False, None, 0, 0.0, "B=1 q=2048 past=2048 16/4 D=128 bs=256", meta_only, dtype)
 
 
-def serving(seed: int = 0, meta_only: bool = False, dtype: str = "f16") -> Batch:
+def serving(seed: int = 0, meta_only: bool = False, dtype: str = "f16", head_size: int = 0) -> Batch:
     """B=256: 224 decodes + 32 chunks of 128 (order shuffled), past ~
     U[256,16384], 32/8 heads, D=128, block_size 256, 4096 pages, packed
     [Q|K|V] query, explicit slot_mapping with 5% of entries -1.
@@ -345,7 +347,7 @@ def serving(seed: int = 0, meta_only: bool = False, dtype: str = "f16") -> Batch
         except ValueError:
             continue
     N = int(q_lens.sum())
-    return _fill(rng, "serving", seed, q_lens, past, table, nb_, 32, 8, 128, bs, True,
+    return _fill(rng, "serving", seed, q_lens, past, table, nb_, 32, 8, head_size or 128, bs, True,
                  "drop", int(round(0.05 * N)), 0.0,
                  "B=256 (224x1 + 32x128) past~U[256,16384] 32/8 D=128 bs=256 NB=4096 "
                  "packed QKV, slot_mapping 5% -1, groups of 4 share prefix pages", meta_only, dtype)
@@ -360,8 +362,11 @@ WORKLOADS = {
 }
 
 
-def workload(name: str, seed: int = 0, meta_only: bool = False, dtype: str = "f16") -> Batch:
-    return WORKLOADS[name](seed, meta_only, dtype)
+def workload(name: str, seed: int = 0, meta_only: bool = False, dtype: str = "f16",
+             head_size: int = 0) -> Batch:
+    """A named workload; ``head_size`` (0: the workload's own) replaces only
+    the head size, for the head_size-256 variants of the same shapes."""
+    return WORKLOADS[name](seed, meta_only, dtype, head_size)
 
 
 # ---------------------------------------------------------------------------

@@ -89,12 +89,19 @@ __host__ __device__ constexpr int decode_lds_bytes(int D, int hslots) {
 __host__ __device__ constexpr int decode_wg_per_cu(int D, int hslots) {
   return (160 * 1024) / decode_lds_bytes(D, hslots) > 0 ? (160 * 1024) / decode_lds_bytes(D, hslots) : 1;
 }
+// floor(a / b) for 0 <= a, 0 < b: in 32 bits when both fit (a 64-bit
+// division is a long instruction sequence on the GPU)
+__host__ __device__ inline int64_t div_floor(int64_t a, int64_t b) {
+  if ((static_cast<uint64_t>(a) | static_cast<uint64_t>(b)) <= 0xffffffffull)
+    return static_cast<uint32_t>(a) / static_cast<uint32_t>(b);
+  return a / b;
+}
 // the wave whose tile range holds global tile g (ranges as above)
 __host__ __device__ inline int decode_wave_of(int64_t g, int64_t T, int W) {
-  return static_cast<int>(((g + 1) * W - 1) / T);
+  return static_cast<int>(div_floor((g + 1) * W - 1, T));
 }
 __host__ __device__ inline int64_t decode_wave_begin(int w, int64_t T, int W) {
-  return static_cast<int64_t>(w) * T / W;
+  return div_floor(static_cast<int64_t>(w) * T, W);
 }
 
 // Byte offsets of the workspace regions (each 256-byte aligned).

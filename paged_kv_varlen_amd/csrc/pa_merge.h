@@ -19,16 +19,22 @@
 
 namespace pa {
 
-// One segment (decode sequence d, unit u) per call, all 64 lanes: lane = query
-// head (lane & 15) + 16 * quarter of the head dimension.
+// One segment (decode sequence d = task / U, unit u = task % U) per call, all
+// 64 lanes: lane = query head (lane & 15) + 16 * quarter of the head
+// dimension.  sq is the sequence's record (b, token, L, first tile).
 template <int D, bool BF16>
-__device__ inline void merge_segment(const AttnParams& p, int task, int T, int lane) {
+__device__ inline void merge_segment(const AttnParams& p, int task, int T, int lane, int4 sq) {
+  // Everything but the lane's head and quarter is the same on all lanes: the
+  // record goes to scalar registers, so every branch below is uniform and the
+  // index arithmetic scalar (32-bit: the partial area holds < 2^31 floats).
+  const int L = __builtin_amdgcn_readfirstlane(sq.z);
+  const int tile0 = __builtin_amdgcn_readfirstlane(sq.w);
+  const int token = __builtin_amdgcn_readfirstlane(sq.y);
   const int U = p.decode_units;
-  const int d = task / U, u = task % U;
-  const int4 sq = p.dec_seq[d];  // (b, token, L, first tile)
-  const int n = (sq.z + kDecodeTile - 1) / kDecodeTile;
+  const int u = task % U;
+  const int n = (L + kDecodeTile - 1) / kDecodeTile;
   const int W = p.decode_waves;
-  const int S = sq.w + u * n;
+  const int S = tile0 + u * n;
   const int wf = decode_wave_of(S, T, W), wl = decode_wave_of(S + n - 1, T, W);
   if (wf == wl) return;  // written whole by its wave
   const int first_k = decode_wave_begin(wf, T, W) < S ? 1 : 0;
@@ -38,38 +44,45 @@ __device__ inline void merge_segment(const AttnParams& p, int task, int T, int l
   const int hn = lane & 15, qd = lane >> 4;
   if (hn >= nh) return;
   constexpr int E = D / 4;  // head-dim elements per lane
+  // (with at least as many tiles as waves every range is non-empty)
+  const bool every_wave_holds = T >= W;
   auto holds = [&](int v) {
-    return v == wf || decode_wave_begin(v, T, W) < decode_wave_begin(v + 1, T, W);
+    return every_wave_holds || v == wf || decode_wave_begin(v, T, W) < decode_wave_begin(v + 1, T, W);
   };
+  // partial slot of wave v's piece: the first piece in wf's second slot when
+  // the segment starts inside wf's range, every other in the wave's first
+  auto slot_of_piece = [&](int v) { return 2 * v + (v == wf ? first_k : 0); };
+  const float* lse_base = p.part_lse + hn;
+  const float* o_base = p.part_o + hn * D + E * qd;
+  // Pieces are combined in wave order with weights 2^(lse - M), M the
+  // largest lse: a pass for M, then one for the weighted sum.
   float M = -__builtin_huge_valf();
-  for (int v = wf; v <= wl; ++v) {
-    if (!holds(v)) continue;
-    const int ps = 2 * v + (v == wf ? first_k : 0);
-    M = fmaxf(M, p.part_lse[ps * kDecodeUnitHeads + hn]);
-  }
+  for (int v = wf; v <= wl; ++v)
+    if (holds(v)) M = fmaxf(M, lse_base[slot_of_piece(v) * kDecodeUnitHeads]);
   float o[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) o[e] = 0.f;
   float wsum = 0.f;
   for (int v = wf; v <= wl; ++v) {
     if (!holds(v)) continue;
-    const int ps = 2 * v + (v == wf ? first_k : 0);
-    const float wk = __builtin_amdgcn_exp2f(p.part_lse[ps * kDecodeUnitHeads + hn] - M);
-    const float4* po =
-        reinterpret_cast<const float4*>(p.part_o + (static_cast<int64_t>(ps) * kDecodeUnitHeads + hn) * D + E * qd);
+    const int ps = slot_of_piece(v);
+    const float wk = __builtin_amdgcn_exp2f(lse_base[ps * kDecodeUnitHeads] - M);
+    const float4* po = reinterpret_cast<const float4*>(o_base + ps * (kDecodeUnitHeads * D));
+    float4 x[E / 4];
+#pragma unroll
+    for (int e = 0; e < E / 4; ++e) x[e] = po[e];
 #pragma unroll
     for (int e = 0; e < E / 4; ++e) {
-      const float4 x = po[e];
-      o[4 * e] = fmaf(wk, x.x, o[4 * e]);
-      o[4 * e + 1] = fmaf(wk, x.y, o[4 * e + 1]);
-      o[4 * e + 2] = fmaf(wk, x.z, o[4 * e + 2]);
-      o[4 * e + 3] = fmaf(wk, x.w, o[4 * e + 3]);
+      o[4 * e] = fmaf(wk, x[e].x, o[4 * e]);
+      o[4 * e + 1] = fmaf(wk, x[e].y, o[4 * e + 1]);
+      o[4 * e + 2] = fmaf(wk, x[e].z, o[4 * e + 2]);
+      o[4 * e + 3] = fmaf(wk, x[e].w, o[4 * e + 3]);
     }
     wsum += wk;
   }
   const float inv = 1.f / wsum;
   const int h = kvh * p.group + kDecodeUnitHeads * hc + hn;
-  const int64_t row = static_cast<int64_t>(sq.y) * p.num_heads + h;
+  const int64_t row = static_cast<int64_t>(token) * p.num_heads + h;
   // optional partial state of the whole row: fp32 output and natural-log lse
   if (p.out_f32 != nullptr) {
     float4* of = reinterpret_cast<float4*>(p.out_f32 + row * D + E * qd);

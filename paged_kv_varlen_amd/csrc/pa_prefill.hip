@@ -184,13 +184,18 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
   const float c = fabsf(p.scale_log2);
   const bool negate_q = p.scale_log2 < 0.f;  // fold the sign into Q (exact)
 
-  // decode segments cut by a wave boundary: one wave per segment
+  // decode segments cut by a wave boundary: one wave per segment.  The first
+  // task's sequence record is read together with the control block (the
+  // record array always holds batch + 1 entries).
   {
-    const int segments = p.ws_ctrl[kCtrlDecodeSeqs] * p.decode_units;
+    const int U = p.decode_units;
+    const int first = static_cast<int>(blockIdx.x) * S::WAVES + wave;
+    const int4 sq0 = p.dec_seq[min(first / U, p.batch)];
+    const int segments = p.ws_ctrl[kCtrlDecodeSeqs] * U;
     const int T = p.ws_ctrl[kCtrlDecodeTiles];
     const int nw = static_cast<int>(gridDim.x) * S::WAVES;
-    for (int task = static_cast<int>(blockIdx.x) * S::WAVES + wave; task < segments; task += nw)
-      merge_segment<D, BF16>(p, task, T, lane);
+    for (int task = first; task < segments; task += nw)
+      merge_segment<D, BF16>(p, task, T, lane, task == first ? sq0 : p.dec_seq[task / U]);
   }
 
   const int nq = prefill_queue_count(p.kv_heads);

@@ -16,9 +16,10 @@ namespace pa {
 
 namespace {
 
-__device__ inline int find_sequence(const int32_t* cum, int batch, int64_t t) {
-  // largest b with cum[b] <= t < cum[b+1] (sequences with no tokens are
-  // skipped because their cum[b] == cum[b+1])
+// largest b with cum[b] <= t < cum[b+1] (sequences with no tokens are
+// skipped because their cum[b] == cum[b+1]); cum may be in LDS or global
+template <typename C>
+__device__ inline int find_sequence(const C* cum, int batch, int64_t t) {
   int lo = 0, hi = batch - 1;
   while (lo < hi) {
     int mid = (lo + hi) >> 1;
@@ -26,6 +27,10 @@ __device__ inline int find_sequence(const int32_t* cum, int batch, int64_t t) {
   }
   return lo;
 }
+
+// LDS of this kernel is allocated in every workgroup (the scatter ones too),
+// so both staging arrays stay small: 27 KB in all, five workgroups per CU
+constexpr int kScatterLdsCum = 2048;  // cum entries a scatter workgroup stages in LDS
 
 // Exclusive scan of three ints per thread over a 256-thread block (one pass);
 // returns the exclusive prefixes and writes the block totals to tot.
@@ -47,18 +52,19 @@ __device__ inline int3 block_exclusive_scan3(int3 v, int3* lds, int3* tot) {
   return make_int3(incl.x - v.x, incl.y - v.y, incl.z - v.z);
 }
 
-constexpr int kPlanLdsSeqs = 8192;  // decode sequences whose first tile the plan keeps in LDS
+constexpr int kPlanLdsSeqs = 1024;  // decode sequences whose record the plan keeps in LDS
 
 // The plan.  Decode sequences (one new token) get their index d and the tile
 // offset of their first segment; each decode wave gets the segment and tile
 // where its equal share of all tiles begins (a binary search over the
-// sequences' first tiles, in LDS).
+// sequences' first tiles; the records stay in LDS, so this needs no global
+// load that waits for the plan's own writes).
 // Multi-token sequences get one prefill item per pair of query half-tiles
 // (t and nt-1-t of the sequence's nt), which all cost about the same under
 // the causal mask.
 __device__ void plan(const ScatterPlanParams& p) {
   __shared__ int3 scan_lds[256];
-  __shared__ int first_tile[kPlanLdsSeqs];
+  __shared__ int4 seq_lds[kPlanLdsSeqs];  // dec_seq records of the first kPlanLdsSeqs
   const int tid = threadIdx.x;
   const int U = p.decode_units;
   int dec_base = 0, tile_base = 0, pf_base = 0;
@@ -80,8 +86,9 @@ __device__ void plan(const ScatterPlanParams& p) {
     const int3 o = block_exclusive_scan3(make_int3(nd, nt, np), scan_lds, &tot);
     if (nd != 0) {
       const int d = dec_base + o.x;
-      p.dec_seq[d] = make_int4(b, t0, L, tile_base + o.y);
-      if (d < kPlanLdsSeqs) first_tile[d] = tile_base + o.y;
+      const int4 rec = make_int4(b, t0, L, tile_base + o.y);
+      p.dec_seq[d] = rec;
+      if (d < kPlanLdsSeqs) seq_lds[d] = rec;
     }
     for (int t = 0; t < np; ++t) p.pf_items[pf_base + o.z + t] = make_int2(b, t);
     dec_base += tot.x;
@@ -98,7 +105,7 @@ __device__ void plan(const ScatterPlanParams& p) {
     for (int q = 0; q < 8; ++q) p.ws_ctrl[kCtrlPrefillQueue0 + q] = 0;
     p.ws_ctrl[kCtrlPrefillItems] = pf_base;
   }
-  __syncthreads();  // first_tile and dec_seq are read back below
+  __syncthreads();  // seq_lds (and, past it, dec_seq) is read back below
   const int T = tile_base, W = p.decode_waves;
   const bool in_lds = dec_base <= kPlanLdsSeqs;
   for (int w = tid; w <= W; w += 256) {
@@ -108,10 +115,10 @@ __device__ void plan(const ScatterPlanParams& p) {
       int lo = 0, hi = dec_base - 1;  // last d with first tile <= g
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        const int f = in_lds ? first_tile[mid] : p.dec_seq[mid].w;
+        const int f = in_lds ? seq_lds[mid].w : p.dec_seq[mid].w;
         if (f <= g) lo = mid; else hi = mid - 1;
       }
-      const int4 sq = p.dec_seq[lo];
+      const int4 sq = in_lds ? seq_lds[lo] : p.dec_seq[lo];
       const int n = (sq.z + kDecodeTile - 1) / kDecodeTile;
       const int off = g - sq.w;
       lo4 = make_int4(lo, off / n, off % n, g);
@@ -128,7 +135,19 @@ __global__ __launch_bounds__(256) void scatter_plan_kernel(ScatterPlanParams p) 
     plan(p);
     return;
   }
-  const int b = find_sequence(p.cum, p.batch, t);
+  // the sequence of token t: a binary search over cum, staged in LDS by one
+  // coalesced load (long batches search global memory)
+  __shared__ int cum_lds[kScatterLdsCum];
+  int b;
+  if (p.slot_mapping != nullptr) {
+    b = 0;  // not needed
+  } else if (p.batch < kScatterLdsCum) {
+    for (int i = threadIdx.x; i <= p.batch; i += blockDim.x) cum_lds[i] = p.cum[i];
+    __syncthreads();
+    b = find_sequence(cum_lds, p.batch, t);
+  } else {
+    b = find_sequence(p.cum, p.batch, t);
+  }
   int64_t slot;
   if (p.slot_mapping != nullptr) {
     slot = p.slot_mapping[t];

@@ -488,3 +488,49 @@ def test_head_size_256_long_prefill_and_state(dtype):
     e_l = np.max(np.abs(l32[rows].astype(np.float64) - rlse[rows]))
     say(f"      state: max|err| out_f32 {e_o:.3e}, lse {e_l:.3e}")
     assert e_o <= tol(b) and e_l <= (LSE_TOL_BF16 if dtype == "bf16" else LSE_TOL)
+
+
+# ------------------------------------------------------------------ adversarial cases for the wider paths
+
+@pytest.mark.parametrize("D,dtype", [(256, "f16"), (256, "bf16"), (128, "bf16")])
+def test_garbage_outside_history_wide(D, dtype):
+    # every slot the call must not read holds a NaN pattern (fp16 0x7E00, bf16
+    # 0x7FC0): keys past a history come from the zero page, never the cache
+    b = W.make_batch([1, 37, 1, 5, 70], [50, 20, 4095, 0, 190], num_heads=8, kv_num_heads=2,
+                     head_size=D, block_size=64, seed=40 + D, num_blocks=200, name=f"nan{D}",
+                     dtype=dtype)
+    keep = np.zeros(b.num_blocks * b.block_size, dtype=bool)
+    for i in range(b.batch_size):
+        for j in range(int(b.kv_lens[i])):
+            keep[int(b.block_table[i, j // b.block_size]) * b.block_size + j % b.block_size] = True
+    nan_bits = np.uint16(0x7FC0 if dtype == "bf16" else 0x7E00)
+    for cache in (b.key_cache, b.value_cache):
+        flat = cache.reshape(b.num_blocks * b.block_size, -1).view(np.uint16)
+        flat[~keep] = nan_bits
+    check(b)
+
+
+@pytest.mark.parametrize("D,dtype", [(256, "bf16"), (128, "bf16")])
+def test_hip_graph_replay_wide(D, dtype):
+    b = W.make_batch([1, 1, 300, 1, 64], [900, 5000, 40, 7, 3000], num_heads=16, kv_num_heads=2,
+                     head_size=D, block_size=16, seed=50 + D, name=f"graph{D}", dtype=dtype)
+    d = DevBatch(b)
+    ref = d.run().clone()
+    torch.cuda.synchronize()
+    ws = torch.empty(1 << 27, dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        d.run(output=out, workspace=ws, stream=s)
+        s.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            d.run(output=out, workspace=ws, stream=s)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))

@@ -34,7 +34,7 @@ constexpr int kDecodeUnitHeads = 16;  // query heads of one decode segment (MFMA
 constexpr int kDecodeWindow = 64;     // block-table entries a wave holds (one per lane)
 constexpr int kPrefillRows = 128;     // (position, head) rows per prefill workgroup (two half-tiles)
 constexpr int kPrefillKeys = 64;      // keys per prefill step (32 per kv group)
-constexpr int kPlanThreads = 1024;    // threads of the planning workgroup
+constexpr int kPlanThreads = 256;     // threads of every scatter_plan workgroup (the plan's one too)
 // zero bytes read in place of absent query heads and of keys past a history:
 // one key row of the largest head size (256 x 2 bytes)
 constexpr int kZeroPageBytes = 512;

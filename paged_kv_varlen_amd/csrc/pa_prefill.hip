@@ -39,14 +39,20 @@
 //     diagonal (bottom-right causal offset: new row i of sequence b is at
 //     past_b + i, "WS2 CP-Aware Attention Contract", Mode-Specific Metadata);
 //   * online softmax in fp32 on base-2 scores (running sums rescaled only
-//     when the max grows by more than 2^8), P rounded to fp16;
+//     when the max grows by more than 2^8), P rounded to the data type
+//     (fp16 or bf16);
 //   * O^T += V^T P^T with the same MFMA.  P^T comes straight from the S^T
 //     registers; the V^T operand is read from the row-major V tile with the
 //     LDS transpose read ds_read_b64_tr_b16 (within 16 lanes, lanes 4r..4r+3
 //     supply 16 consecutive halves of "row" r and lane i receives element i
 //     of rows 0..3), which yields 4 consecutive keys of one head-dim column
 //     per lane, in the key order of the P^T registers.
-// O is divided by the row sum and rounded to fp16 once, at the final write.
+// O is divided by the row sum and rounded to the data type once, at the final
+// write.
+//
+// Head size 256 (PrefillShape): four waves, one per SIMD, each with a row
+// group and all keys of a step (two 32-key sub-steps), and a ring of two
+// steps; everything else as above.
 //
 // Items are spread over up to eight queues by kv head and a workgroup serves
 // first the queue of the XCD it runs on (workgroup id mod 8), so each XCD's
@@ -439,7 +445,7 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e) pb[ks][e] = E::round(fast_exp2(fmaf(s[8 * ks + e], c, -mref)));
-      // row sum of exactly the fp16 weights the MFMA multiplies (v_dot2 with 1)
+      // row sum of exactly the rounded weights the MFMA multiplies (v_dot2 with 1)
       // (two partial sums: shorter dependency chains; fixed order)
       float la = 0.f, lb = 0.f;
 #pragma unroll

@@ -5,7 +5,8 @@
 // logical position past[b] + (t - cum[b]), is written to flat slot
 // slot_mapping[t] when slot_mapping is given (-1 = no write), else to
 // block_table[b, pos / block_size] * block_size + pos % block_size.  A slot is
-// Hkv*D contiguous fp16 values of each cache; the copy is a bit copy.
+// Hkv*D contiguous 16-bit values (fp16 or bf16) of each cache; the copy is a
+// bit copy.
 //
 // One workgroup per token: the row is moved in 16-byte pieces, one per lane,
 // so a 2 KB row (Hkv=8, D=128) is one fully coalesced 128-lane read and write
@@ -32,13 +33,13 @@ __device__ inline int find_sequence(const C* cum, int batch, int64_t t) {
 // so both staging arrays stay small: 27 KB in all, five workgroups per CU
 constexpr int kScatterLdsCum = 2048;  // cum entries a scatter workgroup stages in LDS
 
-// Exclusive scan of three ints per thread over a 256-thread block (one pass);
+// Exclusive scan of three ints per thread over a kPlanThreads block (one pass);
 // returns the exclusive prefixes and writes the block totals to tot.
 __device__ inline int3 block_exclusive_scan3(int3 v, int3* lds, int3* tot) {
   const int tid = threadIdx.x;
   lds[tid] = v;
   __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
+  for (int off = 1; off < kPlanThreads; off <<= 1) {
     const int3 add = tid >= off ? lds[tid - off] : make_int3(0, 0, 0);
     __syncthreads();
     lds[tid].x += add.x;
@@ -47,7 +48,7 @@ __device__ inline int3 block_exclusive_scan3(int3 v, int3* lds, int3* tot) {
     __syncthreads();
   }
   const int3 incl = lds[tid];
-  *tot = lds[255];
+  *tot = lds[kPlanThreads - 1];
   __syncthreads();
   return make_int3(incl.x - v.x, incl.y - v.y, incl.z - v.z);
 }
@@ -63,12 +64,12 @@ constexpr int kPlanLdsSeqs = 1024;  // decode sequences whose record the plan ke
 // (t and nt-1-t of the sequence's nt), which all cost about the same under
 // the causal mask.
 __device__ void plan(const ScatterPlanParams& p) {
-  __shared__ int3 scan_lds[256];
+  __shared__ int3 scan_lds[kPlanThreads];
   __shared__ int4 seq_lds[kPlanLdsSeqs];  // dec_seq records of the first kPlanLdsSeqs
   const int tid = threadIdx.x;
   const int U = p.decode_units;
   int dec_base = 0, tile_base = 0, pf_base = 0;
-  for (int start = 0; start < p.batch; start += 256) {
+  for (int start = 0; start < p.batch; start += kPlanThreads) {
     const int b = start + tid;
     int nd = 0, nt = 0, np = 0, t0 = 0, L = 0;
     if (b < p.batch) {
@@ -108,7 +109,7 @@ __device__ void plan(const ScatterPlanParams& p) {
   __syncthreads();  // seq_lds (and, past it, dec_seq) is read back below
   const int T = tile_base, W = p.decode_waves;
   const bool in_lds = dec_base <= kPlanLdsSeqs;
-  for (int w = tid; w <= W; w += 256) {
+  for (int w = tid; w <= W; w += kPlanThreads) {
     int4 lo4 = make_int4(dec_base, 0, 0, T), hi4 = make_int4(0, 0, 0, 0);
     if (w < W && T > 0) {
       const int g = static_cast<int>(decode_wave_begin(w, T, W));
@@ -129,7 +130,7 @@ __device__ void plan(const ScatterPlanParams& p) {
   }
 }
 
-__global__ __launch_bounds__(256) void scatter_plan_kernel(ScatterPlanParams p) {
+__global__ __launch_bounds__(kPlanThreads) void scatter_plan_kernel(ScatterPlanParams p) {
   const int64_t t = blockIdx.x;
   if (t == p.num_tokens) {
     plan(p);
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(256) void scatter_plan_kernel(ScatterPlanParams p) 
 
 hipError_t launch_scatter_plan(const ScatterPlanParams& p, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(p.num_tokens + 1));
-  hipLaunchKernelGGL(scatter_plan_kernel, grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL(scatter_plan_kernel, grid, dim3(kPlanThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -31,4 +31,6 @@ from .paged_attention import (  # noqa: F401
     merge_states,
     resolve_call,
     values,
+    quantize_int8,
+    dequantize,
 )

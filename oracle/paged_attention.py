@@ -54,6 +54,22 @@ def values(x: np.ndarray) -> np.ndarray:
     return x.astype(np.float64)
 
 
+def quantize_int8(x: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """INT8 code of each element of x with its per-channel scale s (the
+    Qwen3.8 export issue's "INT8/INT4 per-channel paged KV cache and
+    calibrated scale loading", read plainly as symmetric scales given by the
+    caller, one per (kv head, channel)): code = clamp(rint(x / s), -127, 127),
+    the quotient taken in fp32 (x is exact there) and rounded half to even."""
+    q = values(x).astype(np.float32) / np.asarray(s, dtype=np.float32)
+    return np.clip(np.rint(q), -127, 127).astype(np.int8)
+
+
+def dequantize(codes: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """Exact fp64 value code * s of every cached element (s broadcasts over
+    the trailing [Hkv, D])."""
+    return codes.astype(np.float64) * np.asarray(s, dtype=np.float32).astype(np.float64)
+
+
 def resolve_call(query: np.ndarray, key: Optional[np.ndarray], value: Optional[np.ndarray],
                  num_heads: int, kv_num_heads: int, scale: float):
     """Split the query input and fix head_size and scale.
@@ -89,14 +105,15 @@ def resolve_call(query: np.ndarray, key: Optional[np.ndarray], value: Optional[n
 
 def scatter_kv(key_cache: np.ndarray, value_cache: np.ndarray, K: np.ndarray, V: np.ndarray,
                cum: np.ndarray, past: np.ndarray, block_table: np.ndarray,
-               slot_mapping: Optional[np.ndarray]):
+               slot_mapping: Optional[np.ndarray], k_scale=None, v_scale=None):
     """Write each new token's K/V rows into copies of the caches.
 
     README, Inputs (slot_mapping): token t goes to flat slot
     block_id*block_size + offset; -1 suppresses the write; without
     slot_mapping the slot follows from past_seqlens (token i of sequence b is
     at position past_b + i, found through block_table).  The copy is bit
-    exact: the stored bits are the input's bits.
+    exact: the stored bits are the input's bits.  With INT8 caches (scales
+    given) each row is stored as its codes (quantize_int8).
     """
     kc = key_cache.copy()
     vc = value_cache.copy()
@@ -112,22 +129,25 @@ def scatter_kv(key_cache: np.ndarray, value_cache: np.ndarray, K: np.ndarray, V:
                 pos = int(past[b]) + i
                 slot = int(block_table[b, pos // bs]) * bs + pos % bs
             if slot >= 0:
-                kslots[slot] = K[t]
-                vslots[slot] = V[t]
+                kslots[slot] = K[t] if k_scale is None else quantize_int8(K[t], k_scale)
+                vslots[slot] = V[t] if v_scale is None else quantize_int8(V[t], v_scale)
     return kc, vc
 
 
 def gather_history(kc: np.ndarray, vc: np.ndarray, block_table: np.ndarray, b: int,
-                   length: int):
+                   length: int, k_scale=None, v_scale=None):
     """Contiguous fp64 copies [length, Hkv, D] of sequence b's positions
     0..length-1, each read at slot block_table[b, j // bs]*bs + j % bs
     (README, Inputs: block_table maps a sequence's logical blocks to
-    physical blocks and defines the read path)."""
+    physical blocks and defines the read path).  INT8 caches read as
+    code * scale."""
     NB, bs, Hkv, D = kc.shape
     j = np.arange(int(length), dtype=np.int64)
     idx = block_table[b, j // bs].astype(np.int64) * bs + j % bs
-    Kb = values(kc.reshape(NB * bs, Hkv, D)[idx])
-    Vb = values(vc.reshape(NB * bs, Hkv, D)[idx])
+    kr = kc.reshape(NB * bs, Hkv, D)[idx]
+    vr = vc.reshape(NB * bs, Hkv, D)[idx]
+    Kb = values(kr) if k_scale is None else dequantize(kr, k_scale)
+    Vb = values(vr) if v_scale is None else dequantize(vr, v_scale)
     return Kb, Vb
 
 
@@ -168,7 +188,8 @@ def attend_sequence(Qb: np.ndarray, Kb: np.ndarray, Vb: np.ndarray, past_b: int,
 
 def paged_attention(query, key, value, key_cache, value_cache, cum, past, block_table,
                     slot_mapping=None, *, num_heads: int, kv_num_heads: int,
-                    scale: float = 0.0, is_causal: int = 1, rows=None, with_lse: bool = False):
+                    scale: float = 0.0, is_causal: int = 1, rows=None, with_lse: bool = False,
+                    k_scale=None, v_scale=None):
     """The whole operator: returns (output fp64 [N, H*D], key_cache', value_cache').
 
     README, Description/Outputs: the caches are updated (here: copies are
@@ -176,8 +197,12 @@ def paged_attention(query, key, value, key_cache, value_cache, cum, past, block_
     ``rows``: optional sorted token indices to compute (others are NaN), so
     that full-size workloads can be checked on a sample.  ``with_lse``: also
     return the attention-domain lse [N, H] of every row (see attend_sequence)
-    as a fourth value.
+    as a fourth value.  ``k_scale``/``v_scale`` ([Hkv, D] fp32, both or
+    neither): the caches hold INT8 codes; the step's rows are quantized on
+    write and every cached element reads as code * scale.
     """
+    if (k_scale is None) != (v_scale is None):
+        raise ValueError("k_scale and v_scale go together")
     if int(is_causal) != 1:
         raise ValueError("only is_causal=1 is defined")
     Q, K, V, D, s = resolve_call(query, key, value, num_heads, kv_num_heads, scale)
@@ -186,7 +211,8 @@ def paged_attention(query, key, value, key_cache, value_cache, cum, past, block_
     N = Q.shape[0]
     if cum[0] != 0 or cum[-1] != N or np.any(np.diff(cum) < 0):
         raise ValueError("cumulative_sequence_length must run from 0 to N")
-    kc, vc = scatter_kv(key_cache, value_cache, K, V, cum, past, block_table, slot_mapping)
+    kc, vc = scatter_kv(key_cache, value_cache, K, V, cum, past, block_table, slot_mapping,
+                        k_scale, v_scale)
     out = np.full((N, num_heads, D), np.nan)
     lse = np.full((N, num_heads), np.nan)
     want = None if rows is None else np.zeros(N, dtype=bool)
@@ -202,7 +228,7 @@ def paged_attention(query, key, value, key_cache, value_cache, cum, past, block_
             if local.size == 0:
                 continue
         L = int(past[b]) + (t1 - t0)
-        Kb, Vb = gather_history(kc, vc, block_table, b, L)
+        Kb, Vb = gather_history(kc, vc, block_table, b, L, k_scale, v_scale)
         Qb = values(Q[t0:t1])
         if with_lse:
             out[t0:t1], lse[t0:t1] = attend_sequence(Qb, Kb, Vb, int(past[b]), s, rows=local,

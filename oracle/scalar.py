@@ -27,13 +27,28 @@ def _row(arr, t, start, count):
     return [_num(x) for x in arr[t][start:start + count]]
 
 
+def _f32(x: float) -> float:
+    """x rounded to the nearest binary32 (ties to even)."""
+    return struct.unpack("<f", struct.pack("<f", x))[0]
+
+
+def _code(x: float, s: float) -> int:
+    """INT8 code clamp(round(x / s), -127, 127) with x / s rounded to binary32
+    first (x, s are binary32 values, so the binary64 quotient rounded once
+    more is the correctly rounded binary32 quotient); round() is half to
+    even."""
+    return max(-127, min(127, round(_f32(x / s))))
+
+
 def paged_attention_scalar(query, key, value, key_cache, value_cache, cum, past,
                            block_table, slot_mapping, num_heads, kv_num_heads, scale,
-                           with_lse=False):
+                           with_lse=False, k_scale=None, v_scale=None):
     """Returns (out as nested lists [N][H*D], dict slot->(krow, vrow) of the
     slots written), and with ``with_lse`` also lse as nested lists [N][H]
     (log of the fsum of exp(score) over the visible keys, natural log).
-    Inputs are numpy arrays only as containers."""
+    Inputs are numpy arrays only as containers.  With ``k_scale``/``v_scale``
+    ([Hkv, D]) the caches hold INT8 codes: written rows are stored as codes,
+    and a cached element reads as code * scale."""
     H, Hkv = int(num_heads), int(kv_num_heads)
     N, width = query.shape
     packed = key is None
@@ -41,6 +56,11 @@ def paged_attention_scalar(query, key, value, key_cache, value_cache, cum, past,
     sc = 1.0 / math.sqrt(D) if scale == 0 else float(scale)
     NB, bs = key_cache.shape[0], key_cache.shape[1]
     B = len(past)
+
+    quant = k_scale is not None
+    scales = None
+    if quant:
+        scales = ([float(x) for x in k_scale.reshape(-1)], [float(x) for x in v_scale.reshape(-1)])
 
     def k_of(t):
         return _row(query, t, H * D, Hkv * D) if packed else _row(key, t, 0, Hkv * D)
@@ -65,14 +85,22 @@ def paged_attention_scalar(query, key, value, key_cache, value_cache, cum, past,
             blk, off = divmod(pos, bs)
             slot = int(block_table[b][blk]) * bs + off
         if slot >= 0:
-            written[slot] = (k_of(t), v_of(t))
+            if quant:
+                written[slot] = ([_code(x, sv) for x, sv in zip(k_of(t), scales[0])],
+                                 [_code(x, sv) for x, sv in zip(v_of(t), scales[1])])
+            else:
+                written[slot] = (k_of(t), v_of(t))
 
     def cache_row(slot, which):
         if slot in written:
-            return written[slot][which]
-        blk, off = divmod(slot, bs)
-        src = key_cache if which == 0 else value_cache
-        return [_num(x) for x in src[blk][off].reshape(-1)]
+            row = written[slot][which]
+        else:
+            blk, off = divmod(slot, bs)
+            src = key_cache if which == 0 else value_cache
+            row = [_num(x) if not quant else int(x) for x in src[blk][off].reshape(-1)]
+        if quant:
+            return [c * sv for c, sv in zip(row, scales[which])]
+        return row
 
     out = []
     lse = []

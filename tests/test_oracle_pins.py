@@ -730,3 +730,116 @@ def test_bf16_pins_catch_planted_mistakes(mutant):
             check_B2(oracle.paged_attention)
     finally:
         pa_mod.values = saved
+
+
+# ------------------------------------------------------------------ INT8 caches
+
+# INT8 per-channel caches (codes + fp32 scales per (kv head, channel)).  Pins:
+#   Q1  hand values of the code clamp(rint(x / s), -127, 127): exact
+#       multiples, ties to even, clamping, and two cases where the quotient
+#       taken in fp32 rounds to a tie that the fp64 quotient does not reach;
+#   Q2  with power-of-two scales every code * scale is an fp16 value: the
+#       INT8 oracle equals the fp16 oracle run on those values (and on step
+#       rows that quantize exactly), bit for bit;
+#   Q3  the scalar formulation (its own binary32 rounding) agrees within 1e-12.
+
+def check_Q1(quant):
+    s = np.full((1, 8), 0.25, dtype=np.float32)
+    x = np.array([[1.0, 0.375, 0.625, 0.875, -0.625, 40.0, -40.0, 0.0]], dtype=np.float16)
+    assert quant(x, s).tolist() == [[4, 2, 2, 4, -2, 127, -127, 0]]
+    # x / s in fp32 is exactly 48.5 (code 48) and 53.5 (code 54); in fp64 the
+    # quotients are 48.5000003 and 53.4999993 (codes 49 and 53)
+    xs = np.array([[0x3C7D, 0x40E1]], dtype=np.uint16).view(np.float16)
+    ss = np.array([[1019053721, 1027261488]], dtype=np.uint32).view(np.float32)
+    assert quant(xs, ss).tolist() == [[48, 54]]
+    # bf16 input (uint16 bit patterns): 3.0 / 0.5 = 6, -1.5 / 1 = -2 (tie to even)
+    xb = np.array([[0x4040, 0xBFC0]], dtype=np.uint16)
+    assert quant(xb, np.array([[0.5, 1.0]], dtype=np.float32)).tolist() == [[6, -2]]
+
+
+def check_Q2(fn):
+    rng = np.random.default_rng(31)
+    H, Hkv, D, bs = 4, 2, 16, 4
+    q_lens, past = [3, 1, 6], [5, 11, 0]
+    b = W.make_batch(q_lens, past, num_heads=H, kv_num_heads=Hkv, head_size=D, block_size=bs,
+                     seed=31, kv_quant="int8")
+    s = np.full((Hkv, D), 2.0 ** -5, dtype=np.float32)
+    # step rows that are exact multiples of the scale within the code range
+    K = (rng.integers(-127, 128, b.key.shape) * 2.0 ** -5).astype(np.float16)
+    V = (rng.integers(-127, 128, b.value.shape) * 2.0 ** -5).astype(np.float16)
+    o8, kc8, vc8 = fn(b.query, K, V, b.key_cache, b.value_cache, b.cum, b.past, b.block_table,
+                      None, num_heads=H, kv_num_heads=Hkv, k_scale=s, v_scale=s)
+    kf = (b.key_cache.astype(np.float64) * 2.0 ** -5).astype(np.float16)
+    vf = (b.value_cache.astype(np.float64) * 2.0 ** -5).astype(np.float16)
+    o16, kc16, vc16 = fn(b.query, K, V, kf, vf, b.cum, b.past, b.block_table, None,
+                         num_heads=H, kv_num_heads=Hkv)
+    assert np.array_equal(o8, o16)
+    assert np.array_equal((kc8.astype(np.float64) * 2.0 ** -5).astype(np.float16), kc16)
+    assert np.array_equal((vc8.astype(np.float64) * 2.0 ** -5).astype(np.float16), vc16)
+
+
+def check_Q3(fn):
+    for b in (W.tiny(0, kv_quant="int8"),
+              small(seed=33, head_size=4, packed=True, slot_mode="drop", drop_count=2,
+                    dtype="bf16", kv_quant="int8")):
+        o, kc, _ = call(fn, b, k_scale=b.k_scale, v_scale=b.v_scale)
+        so, written = scalar.paged_attention_scalar(b.query, b.key, b.value, b.key_cache,
+                                                    b.value_cache, b.cum, b.past,
+                                                    b.block_table, b.slot_mapping,
+                                                    b.num_heads, b.kv_num_heads, b.scale,
+                                                    k_scale=b.k_scale, v_scale=b.v_scale)
+        assert np.max(np.abs(o - np.array(so))) < 1e-12
+        NB, bs, Hkv, D = kc.shape
+        for slot, (krow, _) in written.items():
+            assert kc.reshape(NB * bs, Hkv * D)[slot].tolist() == krow
+
+
+def test_oracle_int8_pins():
+    check_Q1(oracle.quantize_int8)
+    check_Q2(oracle.paged_attention)
+    check_Q3(oracle.paged_attention)
+
+
+def _quant_trunc(x, s):
+    return np.clip(oracle.values(x).astype(np.float32) / np.asarray(s, np.float32), -127, 127).astype(np.int8)
+
+
+def _quant_half_up(x, s):
+    q = oracle.values(x).astype(np.float32) / np.asarray(s, np.float32)
+    return np.clip(np.floor(q + np.float32(0.5)), -127, 127).astype(np.int8)
+
+
+def _quant_fp64(x, s):
+    q = oracle.values(x) / np.asarray(s, np.float32).astype(np.float64)
+    return np.clip(np.rint(q), -127, 127).astype(np.int8)
+
+
+def _quant_clamp128(x, s):
+    q = oracle.values(x).astype(np.float32) / np.asarray(s, np.float32)
+    return np.clip(np.rint(q), -128, 127).astype(np.int8)
+
+
+def _quant_times(x, s):
+    q = oracle.values(x).astype(np.float32) * np.asarray(s, np.float32)
+    return np.clip(np.rint(q), -127, 127).astype(np.int8)
+
+
+@pytest.mark.parametrize("mutant", [_quant_trunc, _quant_half_up, _quant_fp64, _quant_clamp128,
+                                    _quant_times], ids=lambda f: f.__name__)
+def test_int8_pins_catch_planted_mistakes(mutant):
+    with pytest.raises(AssertionError):
+        check_Q1(mutant)
+
+
+def _dequant_no_scale(codes, s):
+    return codes.astype(np.float64)
+
+
+def test_int8_pins_catch_dequant_mistake():
+    saved = pa_mod.dequantize
+    pa_mod.dequantize = _dequant_no_scale
+    try:
+        with pytest.raises(AssertionError):
+            check_Q2(oracle.paged_attention)
+    finally:
+        pa_mod.dequantize = saved

@@ -28,6 +28,9 @@ Draw order for one batch (fixed so that a seed names one input exactly):
 With ``meta_only=True`` the draws stop after step 4 and the data tensors are
 left uninitialised (only their shapes are meaningful).
 
+INT8 caches (``kv_quant="int8"``): the cache tensors are int8 codes and the
+batch carries per-(kv head, channel) scales; the step's K/V stay in dtype.
+
 Data type: every workload takes ``dtype`` "f16" (default) or "bf16", and
 ``head_size`` (0 = its own; 256 for the head_size-256 variant: same heads,
 lengths and pages, wider heads).  The
@@ -74,6 +77,27 @@ def normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
     return out
 
 
+# INT8 caches: synthetic codes round(28 * N(0,1)) clipped to [-127, 127], and
+# per-(kv head, channel) scales 4.5/127 * 2^U(-1/4, 1/4) that cover about
+# 4.5 standard deviations of the step's N(0,1) rows
+INT8_CODE_GAIN = 28.0
+INT8_SCALE = 4.5 / 127.0
+
+
+def int8_codes(rng: np.random.Generator, shape) -> np.ndarray:
+    out = np.empty(shape, dtype=np.int8)
+    flat = out.reshape(-1)
+    for s in range(0, flat.size, _CHUNK):
+        e = min(flat.size, s + _CHUNK)
+        x = rng.standard_normal(e - s, dtype=np.float32) * np.float32(INT8_CODE_GAIN)
+        flat[s:e] = np.clip(np.rint(x), -127, 127).astype(np.int8)
+    return out
+
+
+def int8_scales(rng: np.random.Generator, Hkv: int, D: int) -> np.ndarray:
+    return (INT8_SCALE * np.exp2(rng.uniform(-0.25, 0.25, (Hkv, D)))).astype(np.float32)
+
+
 def storage_dtype(dtype: str):
     """numpy dtype that holds tensors of data type ``dtype``."""
     return {"f16": np.float16, "bf16": np.uint16}[dtype]
@@ -101,6 +125,9 @@ class Batch:
     scale: float = 0.0
     note: str = ""
     dtype: str = "f16"                # "f16" (float16 arrays) or "bf16" (uint16 bit patterns)
+    kv_quant: str = "none"            # "none" (caches in dtype) or "int8" (int8 codes + scales)
+    k_scale: Optional[np.ndarray] = None  # fp32 [Hkv, D] with kv_quant "int8"
+    v_scale: Optional[np.ndarray] = None
 
     @property
     def num_tokens(self) -> int:
@@ -229,7 +256,8 @@ def make_batch(q_lens: Sequence[int], past_lens: Sequence[int], *, num_heads: in
                slot_mode: Optional[str] = None, drop_count: int = 0,
                num_blocks: Optional[int] = None, max_blocks: Optional[int] = None,
                shared_prefix: Optional[Sequence[int]] = None, scale: float = 0.0,
-               name: str = "custom", note: str = "", dtype: str = "f16") -> Batch:
+               name: str = "custom", note: str = "", dtype: str = "f16",
+               kv_quant: str = "none") -> Batch:
     """Build one batch.  ``slot_mode``: None (omit slot_mapping), "derived"
     (allocator slots), or "drop" (allocator slots with ``drop_count`` entries
     set to -1, chosen by ``rng.choice(N, drop_count, replace=False)``)."""
@@ -240,11 +268,12 @@ def make_batch(q_lens: Sequence[int], past_lens: Sequence[int], *, num_heads: in
     table, nb, _ = allocate_pages(rng, kv, block_size, num_blocks=num_blocks,
                                   max_blocks=max_blocks, shared_prefix=shared_prefix)
     return _fill(rng, name, seed, q_lens, past, table, nb, num_heads, kv_num_heads,
-                 head_size, block_size, packed, slot_mode, drop_count, scale, note, dtype=dtype)
+                 head_size, block_size, packed, slot_mode, drop_count, scale, note, dtype=dtype,
+                 kv_quant=kv_quant)
 
 
 def _fill(rng, name, seed, q_lens, past, table, nb, H, Hkv, D, bs, packed, slot_mode,
-          drop_count, scale, note, meta_only=False, dtype="f16") -> Batch:
+          drop_count, scale, note, meta_only=False, dtype="f16", kv_quant="none") -> Batch:
     cum = cum_from_lens(q_lens)
     N = int(cum[-1])
     slots = None
@@ -265,20 +294,35 @@ def _fill(rng, name, seed, q_lens, past, table, nb, H, Hkv, D, bs, packed, slot_
         query = draw((N, H * D))
         key = draw((N, Hkv * D))
         value = draw((N, Hkv * D))
-    key_cache = draw((nb, bs, Hkv, D))
-    value_cache = draw((nb, bs, Hkv, D))
+    k_scale = v_scale = None
+    if kv_quant == "int8":
+        if meta_only:
+            key_cache = np.empty((nb, bs, Hkv, D), np.int8)
+            value_cache = np.empty((nb, bs, Hkv, D), np.int8)
+        else:
+            key_cache = int8_codes(rng, (nb, bs, Hkv, D))
+            value_cache = int8_codes(rng, (nb, bs, Hkv, D))
+        k_scale = int8_scales(rng, Hkv, D)
+        v_scale = int8_scales(rng, Hkv, D)
+    elif kv_quant == "none":
+        key_cache = draw((nb, bs, Hkv, D))
+        value_cache = draw((nb, bs, Hkv, D))
+    else:
+        raise ValueError(kv_quant)
     return Batch(name=name, seed=seed, query=query, key=key, value=value,
                  key_cache=key_cache, value_cache=value_cache, cum=cum,
                  past=past.astype(np.int32), block_table=table, slot_mapping=slots,
                  num_heads=H, kv_num_heads=Hkv, head_size=D, block_size=bs,
-                 scale=float(scale), note=note, dtype=dtype)
+                 scale=float(scale), note=note, dtype=dtype, kv_quant=kv_quant,
+                 k_scale=k_scale, v_scale=v_scale)
 
 
 # ---------------------------------------------------------------------------
 # the five named workloads
 # ---------------------------------------------------------------------------
 
-def tiny(seed: int = 0, meta_only: bool = False, dtype: str = "f16", head_size: int = 0) -> Batch:
+def tiny(seed: int = 0, meta_only: bool = False, dtype: str = "f16", head_size: int = 0,
+         kv_quant: str = "none") -> Batch:
     """B=2, H/Hkv=4/2, D=64, block_size 16, 8 pages, past [5,20], new [3,1];
     block_table is a random permutation of all 8 pages, no slot_mapping."""
     rng = np.random.default_rng(seed)
@@ -286,10 +330,12 @@ def tiny(seed: int = 0, meta_only: bool = False, dtype: str = "f16", head_size: 
     past = np.array([5, 20])
     table = rng.permutation(8).astype(np.int32).reshape(2, 4)
     return _fill(rng, "tiny", seed, q_lens, past, table, 8, 4, 2, head_size or 64, 16, False, None,
-                 0, 0.0, "B=2 4/2 heads D=64 bs=16 NB=8 past=[5,20] q=[3,1]", meta_only, dtype)
+                 0, 0.0, "B=2 4/2 heads D=64 bs=16 NB=8 past=[5,20] q=[3,1]", meta_only, dtype,
+                 kv_quant)
 
 
-def pure_decode(seed: int = 0, meta_only: bool = False, dtype: str = "f16", head_size: int = 0) -> Batch:
+def pure_decode(seed: int = 0, meta_only: bool = False, dtype: str = "f16", head_size: int = 0,
+                kv_quant: str = "none") -> Batch:
     """B=64 single-token decodes, past ~ U[512,4096], 32/8 heads, D=128,
     block_size 16, pool sized to fit, shuffled page ids."""
     rng = np.random.default_rng(seed)
@@ -297,10 +343,11 @@ def pure_decode(seed: int = 0, meta_only: bool = False, dtype: str = "f16", head
     past = rng.integers(512, 4096 + 1, size=64)
     table, nb, _ = allocate_pages(rng, past + q_lens, 16)
     return _fill(rng, "pure_decode", seed, q_lens, past, table, nb, 32, 8, head_size or 128, 16, False,
-                 None, 0, 0.0, "B=64 q=1 past~U[512,4096] 32/8 D=128 bs=16", meta_only, dtype)
+                 None, 0, 0.0, "B=64 q=1 past~U[512,4096] 32/8 D=128 bs=16", meta_only, dtype, kv_quant)
 
 
-def mixed(seed: int = 0, meta_only: bool = False, dtype: str = "f16", head_size: int = 0) -> Batch:
+def mixed(seed: int = 0, meta_only: bool = False, dtype: str = "f16", head_size: int = 0,
+          kv_quant: str = "none") -> Batch:
     """B=16: 8 decodes + 8 chunks of 512 new tokens (order shuffled), past ~
     U[0,8192], 32/8 heads, D=128, block_size 256, random page table."""
     rng = np.random.default_rng(seed)
@@ -308,10 +355,11 @@ def mixed(seed: int = 0, meta_only: bool = False, dtype: str = "f16", head_size:
     past = rng.integers(0, 8192 + 1, size=16)
     table, nb, _ = allocate_pages(rng, past + q_lens, 256)
     return _fill(rng, "mixed", seed, q_lens, past, table, nb, 32, 8, head_size or 128, 256, False, None,
-                 0, 0.0, "B=16 (8x1 + 8x512) past~U[0,8192] 32/8 D=128 bs=256", meta_only, dtype)
+                 0, 0.0, "B=16 (8x1 + 8x512) past~U[0,8192] 32/8 D=128 bs=256", meta_only, dtype, kv_quant)
 
 
-def long_prefill(seed: int = 0, meta_only: bool = False, dtype: str = "f16", head_size: int = 0) -> Batch:
+def long_prefill(seed: int = 0, meta_only: bool = False, dtype: str = "f16", head_size: int = 0,
+                 kv_quant: str = "none") -> Batch:
     """One sequence, 2048 new tokens on top of 2048 cached (second half of a
     4096-token sequence), 16/4 heads (one of two tensor-parallel ranks of a
     32/8 model), D=128, block_size 256, 16 pages in shuffled order."""
@@ -320,10 +368,11 @@ def long_prefill(seed: int = 0, meta_only: bool = False, dtype: str = "f16", hea
     past = np.array([2048])
     table = rng.permutation(16).astype(np.int32)[None, :]
     return _fill(rng, "long_prefill", seed, q_lens, past, table, 16, 16, 4, head_size or 128, 256,
-                 False, None, 0, 0.0, "B=1 q=2048 past=2048 16/4 D=128 bs=256", meta_only, dtype)
+                 False, None, 0, 0.0, "B=1 q=2048 past=2048 16/4 D=128 bs=256", meta_only, dtype, kv_quant)
 
 
-def serving(seed: int = 0, meta_only: bool = False, dtype: str = "f16", head_size: int = 0) -> Batch:
+def serving(seed: int = 0, meta_only: bool = False, dtype: str = "f16", head_size: int = 0,
+            kv_quant: str = "none") -> Batch:
     """B=256: 224 decodes + 32 chunks of 128 (order shuffled), past ~
     U[256,16384], 32/8 heads, D=128, block_size 256, 4096 pages, packed
     [Q|K|V] query, explicit slot_mapping with 5% of entries -1.
@@ -350,7 +399,8 @@ def serving(seed: int = 0, meta_only: bool = False, dtype: str = "f16", head_siz
     return _fill(rng, "serving", seed, q_lens, past, table, nb_, 32, 8, head_size or 128, bs, True,
                  "drop", int(round(0.05 * N)), 0.0,
                  "B=256 (224x1 + 32x128) past~U[256,16384] 32/8 D=128 bs=256 NB=4096 "
-                 "packed QKV, slot_mapping 5% -1, groups of 4 share prefix pages", meta_only, dtype)
+                 "packed QKV, slot_mapping 5% -1, groups of 4 share prefix pages", meta_only, dtype,
+                 kv_quant)
 
 
 WORKLOADS = {
@@ -363,10 +413,10 @@ WORKLOADS = {
 
 
 def workload(name: str, seed: int = 0, meta_only: bool = False, dtype: str = "f16",
-             head_size: int = 0) -> Batch:
+             head_size: int = 0, kv_quant: str = "none") -> Batch:
     """A named workload; ``head_size`` (0: the workload's own) replaces only
     the head size, for the head_size-256 variants of the same shapes."""
-    return WORKLOADS[name](seed, meta_only, dtype, head_size)
+    return WORKLOADS[name](seed, meta_only, dtype, head_size, kv_quant)
 
 
 # ---------------------------------------------------------------------------

@@ -438,7 +438,7 @@ def _attend_variant(head_map=None, top_left=False, no_scale=False, off_by_one=Fa
     return attend
 
 
-def _scatter_ignoring_minus_one(kc, vc, K, V, cum, past, table, sm):
+def _scatter_ignoring_minus_one(kc, vc, K, V, cum, past, table, sm, k_scale=None, v_scale=None):
     sm2 = None if sm is None else np.where(sm < 0, 0, sm)
     return _orig_scatter(kc, vc, K, V, cum, past, table, sm2)
 
@@ -446,11 +446,11 @@ def _scatter_ignoring_minus_one(kc, vc, K, V, cum, past, table, sm):
 _orig_scatter = pa_mod.scatter_kv
 
 
-def _scatter_nothing(kc, vc, K, V, cum, past, table, sm):
+def _scatter_nothing(kc, vc, K, V, cum, past, table, sm, k_scale=None, v_scale=None):
     return kc.copy(), vc.copy()
 
 
-def _gather_wrong_offset(kc, vc, table, b, length):
+def _gather_wrong_offset(kc, vc, table, b, length, k_scale=None, v_scale=None):
     NB, bs, Hkv, D = kc.shape
     j = np.arange(int(length))
     idx = table[b, j // bs].astype(np.int64) * bs + (bs - 1 - j % bs)

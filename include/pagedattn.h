@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 2
+#define PA_ABI_VERSION 3
 
 /* Result codes.  Every host-checkable fault returns one of these before any
  * device work is enqueued (typed errors, as the acceptance criteria of "Add
@@ -78,6 +78,16 @@ typedef enum pa_dtype {
   PA_DTYPE_BF16 = 2  /* bfloat16 (the upper 16 bits of an IEEE binary32) */
 } pa_dtype;
 
+/* Element type of key_cache/value_cache.  The Qwen3.8 export issue (its
+ * non-goals and follow-ups) asks for INT8/INT4 per-channel paged KV caches
+ * with calibrated scales; read plainly: symmetric codes with one fp32 scale
+ * per (kv head, channel), given by the caller.
+ *  PA_KV_SAME  the caches hold T, like query/key/value;
+ *  PA_KV_INT8  the caches hold int8 codes.  A step row x is stored as
+ *              clamp(rint(x / s), -127, 127), the quotient taken in fp32 and
+ *              rounded half to even; a cached code c reads as c * s. */
+typedef enum pa_kv_quant { PA_KV_SAME = 0, PA_KV_INT8 = 1 } pa_kv_quant;
+
 /*
  * Arguments of one call.  Tensor layouts are dense row-major.
  *
@@ -87,9 +97,10 @@ typedef enum pa_dtype {
  *  key, value   T [num_tokens, kv_num_heads*head_size], or both NULL.
  *               (README, Inputs: key, value)
  *  key_cache,
- *  value_cache  T [num_blocks, block_size, cache_kv_heads, cache_head_size],
- *               read and written in place; the two are always updated
- *               together.  (README, Inputs: key_cache, value_cache; Outputs)
+ *  value_cache  T [num_blocks, block_size, cache_kv_heads, cache_head_size]
+ *               (int8 with kv_quant PA_KV_INT8), read and written in place;
+ *               the two are always updated together.  (README, Inputs:
+ *               key_cache, value_cache; Outputs)
  *  cumulative_sequence_length
  *               S [batch_size + 1], exclusive prefix sums of the new-token
  *               counts: sequence b owns tokens [cum[b], cum[b+1]); cum[0] = 0
@@ -165,6 +176,14 @@ typedef struct pa_args {
    * pa_merge_states(). */
   float *lse;
   float *output_f32;
+
+  /* Cache element type (pa_kv_quant).  With PA_KV_INT8, k_scale and v_scale
+   * are float [kv_num_heads, head_size] (16-byte aligned), the per-channel
+   * scales of the two caches; otherwise they are ignored. */
+  int32_t kv_quant;
+  int32_t reserved;              /* 0                                      */
+  const float *k_scale;
+  const float *v_scale;
 } pa_args;
 
 /* Kernels launched by one call, in launch order (indices into kernel_events). */

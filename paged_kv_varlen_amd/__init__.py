@@ -30,8 +30,9 @@ library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpage
 
 PA_DTYPE_F16 = 1
 PA_DTYPE_BF16 = 2
+PA_KV_SAME, PA_KV_INT8 = 0, 1
 _DTYPE_CODES = {torch.float16: PA_DTYPE_F16, torch.bfloat16: PA_DTYPE_BF16}
-ABI_VERSION = 2
+ABI_VERSION = 3
 KERNELS = ("scatter_plan", "decode", "merge", "prefill")  # enum pa_kernel order
 STATUS = {
     0: "PA_OK", 1: "PA_ERR_NULL_ARG", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED",
@@ -73,6 +74,10 @@ class PaArgs(ctypes.Structure):
         ("kernel_events", ctypes.c_void_p),
         ("lse", ctypes.c_void_p),
         ("output_f32", ctypes.c_void_p),
+        ("kv_quant", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
     ]
 
 
@@ -147,9 +152,13 @@ def _dtype_code(t: torch.Tensor) -> int:
 def make_args(query, key, value, key_cache, value_cache, cumulative_sequence_length,
               past_seqlens, block_table, slot_mapping, output, *, num_heads: int,
               kv_num_heads: int, scale: float = 0.0, is_causal: int = 1,
-              workspace: Optional[torch.Tensor] = None) -> PaArgs:
+              workspace: Optional[torch.Tensor] = None,
+              k_scale: Optional[torch.Tensor] = None,
+              v_scale: Optional[torch.Tensor] = None) -> PaArgs:
     """Fill a PaArgs from tensors (no checks beyond what marshalling needs:
-    the library validates shapes, dtypes and alignment itself)."""
+    the library validates shapes, dtypes and alignment itself).  int8 caches
+    with fp32 ``k_scale``/``v_scale`` [kv_num_heads, head_size] select the
+    INT8 cache path."""
     for name, t in (("query", query), ("key", key), ("value", value), ("key_cache", key_cache),
                     ("value_cache", value_cache),
                     ("cumulative_sequence_length", cumulative_sequence_length),
@@ -164,9 +173,19 @@ def make_args(query, key, value, key_cache, value_cache, cumulative_sequence_len
             raise TypeError(f"{name} must be int32 (type constraint S)")
     a = PaArgs()
     a.struct_size = ctypes.sizeof(PaArgs)
-    same = all(t is None or t.dtype == query.dtype
-               for t in (key, value, key_cache, value_cache, output))
+    int8_cache = key_cache.dtype == torch.int8
+    caches = () if int8_cache else (key_cache, value_cache)
+    same = all(t is None or t.dtype == query.dtype for t in (key, value, output) + caches)
+    if int8_cache and value_cache.dtype != torch.int8:
+        same = False
     a.dtype = _dtype_code(query) if same else 0
+    if int8_cache:
+        for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+            if t is None or t.dtype != torch.float32 or not t.is_contiguous():
+                raise ValueError(f"int8 caches need a contiguous float32 {name}")
+        a.kv_quant = PA_KV_INT8
+        a.k_scale = _ptr(k_scale)
+        a.v_scale = _ptr(v_scale)
     a.query = _ptr(query)
     a.key = _ptr(key)
     a.value = _ptr(value)
@@ -217,7 +236,9 @@ def paged_attention(query: torch.Tensor, key: Optional[torch.Tensor],
                     stream: Optional[torch.cuda.Stream] = None,
                     kernel_events=None, return_lse: bool = False,
                     lse: Optional[torch.Tensor] = None,
-                    output_f32: Optional[torch.Tensor] = None):
+                    output_f32: Optional[torch.Tensor] = None,
+                    k_scale: Optional[torch.Tensor] = None,
+                    v_scale: Optional[torch.Tensor] = None):
     """Scatter the step's K/V into the caches (in place) and return the
     attention output [num_tokens, num_heads * head_size].
 
@@ -228,7 +249,10 @@ def paged_attention(query: torch.Tensor, key: Optional[torch.Tensor],
     is the row's partial state for merge_states().
 
     ``kernel_events``: optional sequence of 2*len(KERNELS) torch.cuda.Event
-    (enable_timing=True); the library records pair k around its k-th kernel."""
+    (enable_timing=True); the library records pair k around its k-th kernel.
+
+    INT8 caches: int8 ``key_cache``/``value_cache`` with fp32 ``k_scale`` and
+    ``v_scale`` [kv_num_heads, head_size] (per-channel scales)."""
     lib = library()
     dev = query.device
     if dev.type != "cuda":
@@ -240,7 +264,8 @@ def paged_attention(query: torch.Tensor, key: Optional[torch.Tensor],
         output = torch.empty((query.shape[0], num_heads * D), dtype=query.dtype, device=dev)
     args = make_args(query, key, value, key_cache, value_cache, cumulative_sequence_length,
                      past_seqlens, block_table, slot_mapping, output, num_heads=num_heads,
-                     kv_num_heads=kv_num_heads, scale=scale, is_causal=is_causal)
+                     kv_num_heads=kv_num_heads, scale=scale, is_causal=is_causal,
+                     k_scale=k_scale, v_scale=v_scale)
     if return_lse and lse is None:
         lse = torch.empty((query.shape[0], num_heads), dtype=torch.float32, device=dev)
     for name, t in (("lse", lse), ("output_f32", output_f32)):

@@ -115,6 +115,29 @@ __device__ inline uint32_t lds_read_b32(uint32_t a) {
 __device__ inline void lds_write_b128(uint32_t a, u32x4 v) {
   asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(v) : "memory");
 }
+// four 16-byte reads at a + O0..O3, one wait
+template <int O0, int O1, int O2, int O3>
+__device__ inline void lds_read4_b128(u32x4 (&v)[4], uint32_t a) {
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%5\n\tds_read_b128 %1, %4 offset:%6\n\t"
+      "ds_read_b128 %2, %4 offset:%7\n\tds_read_b128 %3, %4 offset:%8\n\ts_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(a), "n"(O0), "n"(O1), "n"(O2), "n"(O3)
+      : "memory");
+}
+// N (2 or 4) 16-byte reads at a + i * STEP, one wait
+template <int N, int STEP>
+__device__ inline void lds_readn_b128(u32x4 (&v)[N], uint32_t a) {
+  if constexpr (N == 4) {
+    lds_read4_b128<0, STEP, 2 * STEP, 3 * STEP>(v, a);
+  } else {
+    static_assert(N == 2, "2 or 4 reads");
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:%3\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1])
+                 : "v"(a), "n"(STEP)
+                 : "memory");
+  }
+}
 
 template <typename F, int... I>
 __device__ __attribute__((always_inline)) inline void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
@@ -276,25 +299,34 @@ constexpr int kLast = 1 << 9;      // last tile of a piece
 constexpr int kComplete = 1 << 10; // the piece is the whole segment
 constexpr int kSecond = 1 << 11;   // partial goes to the wave's second slot
 
-template <int D, int HS, bool BF16>
+template <int D, int HS, bool BF16, bool Q8>
 __global__ __launch_bounds__(64 * decode_wg_waves(D)) void decode_kernel(AttnParams p) {
   using E = Elem<BF16>;
   constexpr int kDecodeWaves = decode_wg_waves(D);
-  constexpr int ROW = 2 * D;                      // bytes of one key of one kv head
+  constexpr int ROW = 2 * D;                      // bytes of one key of one kv head (data type)
   constexpr int CPR = ROW / 16;                   // 16-byte chunks per row
-  constexpr int KPI = 1024 / ROW;                 // rows per 1 KB direct load
+  constexpr int ROWC = Q8 ? D : ROW;              // bytes of a cached row (INT8: codes)
+  constexpr int CPRC = ROWC / 16;
+  constexpr int KPI = 1024 / ROWC;                // cached rows per 1 KB direct load
+  constexpr int QPI = 1024 / ROW;                 // query rows (data type) per 1 KB direct load
   constexpr int NK = kDecodeTile / KPI;           // direct loads per tensor per tile
-  constexpr int TB = kDecodeTile * ROW;           // bytes per tensor per tile
+  constexpr int TB = kDecodeTile * ROW;           // bytes per tensor per tile (data type)
+  constexpr int TBC = kDecodeTile * ROWC;         // bytes per tensor per tile as cached
   constexpr int QB = decode_q_bytes(D, HS);
   constexpr int NQ = QB / 1024;                   // direct loads of a query block
-  constexpr int SLOT = decode_slot_bytes(D, HS);
-  constexpr int R = decode_ring(D, HS);
+  constexpr int SB = Q8 ? decode_scale_bytes(D) : 0;  // k and v scale rows of the unit
+  constexpr int NSC = SB / 1024;                  // direct loads of the scale rows
+  constexpr int SLOT = decode_slot_bytes(D, HS, Q8);
+  constexpr int R = decode_ring(D, HS, Q8);
   constexpr int KS = D / 32;                      // QK MFMA steps
   constexpr int DB = D / 16;                      // PV MFMA blocks (16 dims each)
-  static_assert(SLOT == 2 * TB + QB, "slot layout");
+  constexpr int ES = Q8 ? 1 : 2;                  // bytes per cached element
+  static_assert(SLOT == 2 * TBC + QB + SB, "slot layout");
   static_assert(R >= 2, "ring");
 
   __shared__ __align__(1024) char ring[kDecodeWaves][R][SLOT];
+  // INT8 caches: the tile of the step, converted to the data type
+  __shared__ __align__(1024) char conv[kDecodeWaves][Q8 ? 2 * TB : 16];
   __shared__ __align__(16) int meta[kDecodeWaves][2][64];  // [0] next window, [1] next sequence
   // a piece's (token, first head, heads), handed over with its first tile
   __shared__ __align__(16) int piece[kDecodeWaves][R][4];
@@ -324,28 +356,32 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D)) void decode_kernel(AttnPar
 
   // ---- per-lane constant offsets ---------------------------------------------
   // tile loads: byte offset of lane's 16 bytes (key, logical chunk) for direct load j
+  // (INT8 caches: rows land unswizzled; the conversion places them)
   uint32_t src_off[NK];
 #pragma unroll
   for (int j = 0; j < NK; ++j) {
-    const int kj = j * KPI + lane / CPR;
-    const int c = (lane % CPR) ^ swz<D>(kj);
-    src_off[j] = static_cast<uint32_t>(kj * kv_row + 8 * c) * 2u;
+    const int kj = j * KPI + lane / CPRC;
+    const int c = Q8 ? lane % CPRC : (lane % CPR) ^ swz<D>(kj);
+    src_off[j] = Q8 ? static_cast<uint32_t>(kj * kv_row + 16 * c) : static_cast<uint32_t>(kj * kv_row + 8 * c) * 2u;
   }
   const int qchunk = (lane % CPR) * 8;
-  // MFMA operand addresses of ring slot 0 (slot s adds s * SLOT)
+  // MFMA operand addresses of ring slot 0 (slot s adds s * SLOT); with INT8
+  // caches the K/V operands come from the converted tile instead
   const int n = lane & 15, g = lane >> 4;
   const uint32_t ring0 = uniform(static_cast<int>(lds_addr(&ring[wave][0][0])));
+  const uint32_t conv0 = uniform(static_cast<int>(lds_addr(&conv[wave][0])));
+  const uint32_t tile0 = Q8 ? conv0 : ring0;
   uint32_t ka[KS], va[DB], qa[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    ka[s] = ring0 + n * ROW + 16 * ((4 * s + g) ^ swz<D>(n));
-    qa[s] = ring0 + 2 * TB + (n < QB / ROW ? n : 0) * ROW + 16 * (4 * s + g);
+    ka[s] = tile0 + n * ROW + 16 * ((4 * s + g) ^ swz<D>(n));
+    qa[s] = ring0 + 2 * TBC + (n < QB / ROW ? n : 0) * ROW + 16 * (4 * s + g);
   }
   {
     const int kv = 4 * g + (n >> 2), cc = n & 3;
 #pragma unroll
     for (int blk = 0; blk < DB; ++blk)
-      va[blk] = ring0 + TB + kv * ROW + 16 * ((2 * blk + (cc >> 1)) ^ swz<D>(kv)) + 8 * (cc & 1);
+      va[blk] = tile0 + TB + kv * ROW + 16 * ((2 * blk + (cc >> 1)) ^ swz<D>(kv)) + 8 * (cc & 1);
   }
   const uint32_t meta_w = lds_addr(&meta[wave][0][0]);
   const uint32_t piece0 = uniform(static_cast<int>(lds_addr(&piece[wave][0][0])));
@@ -368,8 +404,8 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D)) void decode_kernel(AttnPar
   int g_i = g0;
   // per-segment values
   int h0_i = 0, nh_i = 0, segfl = 0, seg0_i = 0;
-  const uint16_t* kp = nullptr;  // K and V of the next tile to issue (this kv head)
-  const uint16_t* vp = nullptr;
+  const char* kp = nullptr;  // K and V of the next tile to issue (this kv head)
+  const char* vp = nullptr;
 
   // next sequence record (direct load into meta_s)
   int ns_opc = 0, ns_b = 0, ns_t = 0, ns_L = 0, ns_P = 0;
@@ -431,9 +467,9 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D)) void decode_kernel(AttnPar
   };
   auto set_pointers = [&]() __attribute__((always_inline)) {
     const int page = uniform(__builtin_amdgcn_readlane(wcur, pi - wp0));
-    const int64_t base = static_cast<int64_t>(page) * page_elems + ip * tile_elems + kvh_i * D;
-    kp = p.key_cache + base;
-    vp = p.value_cache + base;
+    const int64_t base = (static_cast<int64_t>(page) * page_elems + ip * tile_elems + kvh_i * D) * ES;
+    kp = reinterpret_cast<const char*>(p.key_cache) + base;
+    vp = reinterpret_cast<const char*>(p.value_cache) + base;
   };
   auto enter_segment = [&]() __attribute__((always_inline)) {
     h0_i = kvh_i * G + kDecodeUnitHeads * hc_i;
@@ -456,19 +492,30 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D)) void decode_kernel(AttnPar
     constexpr int S = decltype(slot_c)::value;
     const uint32_t sb = ring0 + S * SLOT;
 #pragma unroll
-    for (int j = 0; j < NK; ++j) dma<16>(reinterpret_cast<const char*>(kp) + src_off[j], sb + 1024 * j);
+    for (int j = 0; j < NK; ++j) dma<16>(kp + src_off[j], sb + 1024 * j);
 #pragma unroll
-    for (int j = 0; j < NK; ++j) dma<16>(reinterpret_cast<const char*>(vp) + src_off[j], sb + TB + 1024 * j);
+    for (int j = 0; j < NK; ++j) dma<16>(vp + src_off[j], sb + TBC + 1024 * j);
     opc += 2 * NK;
     const bool first = g_i == g0 || i_i == 0;
     if (first) {  // the unit's query heads (absent heads read zeros)
       const uint16_t* qtok = p.q + static_cast<int64_t>(t_i) * p.q_stride + static_cast<int64_t>(h0_i) * D;
 #pragma unroll
       for (int j = 0; j < NQ; ++j) {
-        const int hh = j * KPI + lane / CPR;
-        dma<16>(hh < nh_i ? qtok + hh * D + qchunk : p.zeros + qchunk, sb + 2 * TB + 1024 * j);
+        const int hh = j * QPI + lane / CPR;
+        dma<16>(hh < nh_i ? qtok + hh * D + qchunk : p.zeros + qchunk, sb + 2 * TBC + 1024 * j);
       }
       opc += NQ;
+      if constexpr (Q8) {  // the kv head's scale rows: [k_scale (4D bytes) | v_scale (4D bytes) | zeros]
+#pragma unroll
+        for (int j = 0; j < NSC; ++j) {
+          const int o = 1024 * j + 16 * lane;
+          const void* src = o < 4 * D ? static_cast<const void*>(p.k_scale + kvh_i * D + o / 4)
+                            : o < 8 * D ? static_cast<const void*>(p.v_scale + kvh_i * D + (o - 4 * D) / 4)
+                                        : static_cast<const void*>(p.zeros);
+          dma<16>(src, sb + 2 * TBC + QB + 1024 * j);
+        }
+        opc += NSC;
+      }
       lds_write_b128(piece0 + 16 * S, u32x4{static_cast<uint32_t>(t_i), static_cast<uint32_t>(h0_i),
                                           static_cast<uint32_t>(nh_i), 0u});
     }
@@ -507,8 +554,8 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D)) void decode_kernel(AttnPar
       if (pi == wp0 + kDecodeWindow) need_window();
       set_pointers();
     } else {
-      kp += tile_elems;
-      vp += tile_elems;
+      kp += tile_elems * ES;
+      vp += tile_elems * ES;
     }
   };
 
@@ -516,6 +563,11 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D)) void decode_kernel(AttnPar
   f32x4_t acc[DB];
 #pragma unroll
   for (int blk = 0; blk < DB; ++blk) acc[blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // INT8 caches: the v scale of each output value of this lane (d = 16 blk +
+  // 4 g + e), read with the piece's first tile
+  f32x4_t vsc[Q8 ? DB : 1];
+#pragma unroll
+  for (int blk = 0; blk < (Q8 ? DB : 1); ++blk) vsc[blk] = f32x4_t{1.f, 1.f, 1.f, 1.f};
   float m = kNegInf, l = 0.f;
   u32x4 qv[KS];
   int nh_c = 0, h0_c = 0, t_c = 0;
@@ -535,12 +587,68 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D)) void decode_kernel(AttnPar
 #pragma unroll
         for (int s = 0; s < KS; ++s) qv[s] = u32x4{0u, 0u, 0u, 0u};
       }
+      if constexpr (Q8) {
+        // scores use the codes of K, so its per-channel scale goes into Q:
+        // q_d s_d, rounded to the data type (values d = 32 s + 8 g + e)
+        const uint32_t sc0 = ring0 + S * SLOT + 2 * TBC + QB;
+        u32x4 ks[2 * KS];
+        static_for<KS / 2>([&](auto i) __attribute__((always_inline)) {
+          constexpr int b = 256 * decltype(i)::value;  // fragments 2i, 2i+1 (128 bytes each)
+          u32x4 t[4];
+          lds_read4_b128<b, b + 16, b + 128, b + 144>(t, sc0 + 32 * g);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) ks[4 * decltype(i)::value + k] = t[k];
+        });
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          typename E::x8 qx = __builtin_bit_cast(typename E::x8, qv[s]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            qx[e] = E::round(static_cast<float>(qx[e]) * __uint_as_float(ks[2 * s + (e >> 2)][e & 3]));
+          qv[s] = __builtin_bit_cast(u32x4, qx);
+        }
+        static_for<DB / 4>([&](auto i) __attribute__((always_inline)) {
+          constexpr int b = 256 * decltype(i)::value;  // blocks 4i .. 4i+3 (64 bytes apart)
+          u32x4 t[4];
+          lds_read4_b128<b, b + 64, b + 128, b + 192>(t, sc0 + 4 * D + 16 * g);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) vsc[4 * decltype(i)::value + k] = __builtin_bit_cast(f32x4_t, t[k]);
+        });
+      }
       // acc is rescaled by exp2(-inf) = 0 below, as every lane's max grows
       m = kNegInf;
       l = 0.f;
     }
+    if constexpr (Q8) {
+      // codes of the tile -> data type, into the wave's converted tile in the
+      // layout a direct load of data-type rows would have produced: cached
+      // chunk c (16 codes) of key k becomes chunks 2c and 2c+1 of row k,
+      // swizzled.  Same wave, LDS in order: no wait before the reads below.
+      constexpr int NCH = 2 * D / 64;  // 16-byte chunks per lane (K then V)
+      u32x4 raw[NCH];
+      if constexpr (NCH == 8) {
+        u32x4 a[4], b[4];
+        lds_readn_b128<4, 1024>(a, ring0 + S * SLOT + 16 * lane);
+        lds_readn_b128<4, 1024>(b, ring0 + S * SLOT + 4096 + 16 * lane);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) raw[k] = a[k], raw[4 + k] = b[k];
+      } else {
+        lds_readn_b128<NCH, 1024>(raw, ring0 + S * SLOT + 16 * lane);
+      }
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int tensor = i / (NCH / 2);
+        const int j = 64 * (i % (NCH / 2)) + lane;  // chunk within the tensor
+        const int k = j / CPRC, c = j % CPRC;
+        const typename E::x8 lo = E::from_codes(raw[i][0], raw[i][1]);
+        const typename E::x8 hi = E::from_codes(raw[i][2], raw[i][3]);
+        const uint32_t row = conv0 + tensor * TB + k * ROW;
+        lds_write_b128(row + 16 * ((2 * c) ^ swz<D>(k)), __builtin_bit_cast(u32x4, lo));
+        lds_write_b128(row + 16 * ((2 * c + 1) ^ swz<D>(k)), __builtin_bit_cast(u32x4, hi));
+      }
+    }
     TileRegs<D> tr;
-    tr.template read<S * SLOT>(ka, va);
+    tr.template read<Q8 ? 0 : S * SLOT>(ka, va);
     // S^T: lane = head n + 16 * key group g, element e = key 4 g + e
     f32x4_t st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -596,14 +704,14 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D)) void decode_kernel(AttnPar
           for (int blk = 0; blk < DB; ++blk) {
             typename E::x4 hv;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) hv[e] = E::round(acc[blk][e] * inv);
+            for (int e = 0; e < 4; ++e) hv[e] = E::round(acc[blk][e] * inv * vsc[Q8 ? blk : 0][e]);
             *reinterpret_cast<typename E::x4*>(o + 16 * blk) = hv;
           }
           // optional partial state: fp32 output and natural-log lse
           if (p.out_f32 != nullptr) {
 #pragma unroll
             for (int blk = 0; blk < DB; ++blk)
-              *reinterpret_cast<f32x4_t*>(p.out_f32 + row * D + 4 * g + 16 * blk) = acc[blk] * inv;
+              *reinterpret_cast<f32x4_t*>(p.out_f32 + row * D + 4 * g + 16 * blk) = acc[blk] * inv * vsc[Q8 ? blk : 0];
           }
           if (p.lse_out != nullptr && g == 0) p.lse_out[row] = (m + __log2f(lt)) * kLn2;
         }
@@ -611,7 +719,7 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D)) void decode_kernel(AttnPar
         const int ps = 2 * w + ((fl & kSecond) ? 1 : 0);
         float* po = p.part_o + (static_cast<int64_t>(ps) * kDecodeUnitHeads + n) * D + 4 * g;
 #pragma unroll
-        for (int blk = 0; blk < DB; ++blk) *reinterpret_cast<f32x4_t*>(po + 16 * blk) = acc[blk] * inv;
+        for (int blk = 0; blk < DB; ++blk) *reinterpret_cast<f32x4_t*>(po + 16 * blk) = acc[blk] * inv * vsc[Q8 ? blk : 0];
         if (g == 0) p.part_lse[ps * kDecodeUnitHeads + n] = m + __log2f(lt);
       }
     }
@@ -637,14 +745,17 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D)) void decode_kernel(AttnPar
 
 }  // namespace
 
-hipError_t launch_decode(const AttnParams& p, int head_size, int head_slots, bool bf16, int grid, hipStream_t s) {
-#define PA_DECODE(DD, HH)                                                                         \
-  if (head_size == DD && head_slots == HH) {                                                      \
-    if (bf16)                                                                                     \
-      hipLaunchKernelGGL((decode_kernel<DD, HH, true>), dim3(grid), dim3(64 * decode_wg_waves(DD)), 0, s, p); \
-    else                                                                                          \
-      hipLaunchKernelGGL((decode_kernel<DD, HH, false>), dim3(grid), dim3(64 * decode_wg_waves(DD)), 0, s, p); \
-    return hipGetLastError();                                                                     \
+hipError_t launch_decode(const AttnParams& p, int head_size, int head_slots, bool bf16, bool q8, int grid,
+                         hipStream_t s) {
+  const dim3 g(grid);
+#define PA_DECODE(DD, HH)                                                                        \
+  if (head_size == DD && head_slots == HH) {                                                     \
+    const dim3 b(64 * decode_wg_waves(DD));                                                      \
+    if (bf16 && q8) hipLaunchKernelGGL((decode_kernel<DD, HH, true, true>), g, b, 0, s, p);       \
+    else if (bf16) hipLaunchKernelGGL((decode_kernel<DD, HH, true, false>), g, b, 0, s, p);       \
+    else if (q8) hipLaunchKernelGGL((decode_kernel<DD, HH, false, true>), g, b, 0, s, p);         \
+    else hipLaunchKernelGGL((decode_kernel<DD, HH, false, false>), g, b, 0, s, p);                \
+    return hipGetLastError();                                                                    \
   }
   PA_DECODE(128, 4)
   PA_DECODE(128, 8)

@@ -9,7 +9,8 @@
 // export for ORT GenAI Engine", Phase 1 scope) targets fp16 and bf16, and the
 // "WS2 CP-Aware Attention Contract" example (Qwen3-8B TP=2 CP=2) runs in bf16.
 // Both types accumulate in fp32 and round once at the final write (WS2,
-// Reduction Semantics).
+// Reduction Semantics).  With INT8 caches the matrix products take the codes
+// converted to the data type (exact: |code| <= 127).
 #pragma once
 
 #include <stdint.h>
@@ -44,6 +45,25 @@ struct Elem<false> {  // IEEE binary16
   }
   static __device__ inline T round(float x) { return static_cast<_Float16>(x); }
   static __device__ inline uint16_t bits(float x) { return __builtin_bit_cast(uint16_t, round(x)); }
+  // eight int8 codes (byte k of {w0, w1} is code k) as values, exactly: the
+  // byte u = code + 128 becomes the low mantissa byte of the half 1024 + u
+  // (v_perm_b32 puts it beside the high byte 0x64), and 1152 is subtracted
+  static __device__ inline x8 from_codes(uint32_t w0, uint32_t w1) {
+    const uint32_t u0 = w0 ^ 0x80808080u, u1 = w1 ^ 0x80808080u;
+    const uint32_t h[4] = {__builtin_amdgcn_perm(0x64646464u, u0, 0x04010400u),
+                           __builtin_amdgcn_perm(0x64646464u, u0, 0x04030402u),
+                           __builtin_amdgcn_perm(0x64646464u, u1, 0x04010400u),
+                           __builtin_amdgcn_perm(0x64646464u, u1, 0x04030402u)};
+    const x2 bias = {static_cast<_Float16>(1152.f), static_cast<_Float16>(1152.f)};
+    x8 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const x2 v = __builtin_bit_cast(x2, h[k]) - bias;
+      r[2 * k] = v[0];
+      r[2 * k + 1] = v[1];
+    }
+    return r;
+  }
 };
 
 template <>
@@ -70,6 +90,15 @@ struct Elem<true> {  // bfloat16: the upper half of a binary32
   // round to nearest, ties to even (v_cvt_pk_bf16_f32)
   static __device__ inline T round(float x) { return static_cast<__bf16>(x); }
   static __device__ inline uint16_t bits(float x) { return __builtin_bit_cast(uint16_t, round(x)); }
+  // eight int8 codes (byte k of {w0, w1} is code k) as values, exactly
+  // (integers up to 127 in magnitude fit the 8-bit significand)
+  static __device__ inline x8 from_codes(uint32_t w0, uint32_t w1) {
+    x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      r[e] = static_cast<__bf16>(static_cast<float>(static_cast<int8_t>((e < 4 ? w0 : w1) >> (8 * (e & 3)))));
+    return r;
+  }
 };
 
 }  // namespace pa

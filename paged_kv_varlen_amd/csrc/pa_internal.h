@@ -67,27 +67,36 @@ __host__ __device__ constexpr int decode_head_chunks(int group) { return (group 
 __host__ __device__ constexpr int decode_head_slots(int group) {
   return group >= 16 ? 16 : group > 4 ? (group > 8 ? 16 : 8) : 4;
 }
-// LDS per ring slot: K tile, V tile (16 keys each) and the query block
+// LDS per ring slot: K tile, V tile (16 keys each) and the query block; with
+// INT8 caches (q8) the tiles are codes (one byte per element) and the slot
+// also holds the unit's k and v scale rows (fp32, at least one 1 KB load)
 __host__ __device__ constexpr int decode_q_bytes(int D, int hslots) {
   return hslots * 2 * D > 1024 ? hslots * 2 * D : 1024;
 }
-__host__ __device__ constexpr int decode_slot_bytes(int D, int hslots) {
-  return 2 * kDecodeTile * 2 * D + decode_q_bytes(D, hslots);
+__host__ __device__ constexpr int decode_scale_bytes(int D) { return 8 * D > 1024 ? 8 * D : 1024; }
+__host__ __device__ constexpr int decode_slot_bytes(int D, int hslots, bool q8 = false) {
+  return q8 ? 2 * kDecodeTile * D + decode_q_bytes(D, hslots) + decode_scale_bytes(D)
+            : 2 * kDecodeTile * 2 * D + decode_q_bytes(D, hslots);
 }
+// q8: per wave, the K and V tiles converted to the data type for the MFMA
+__host__ __device__ constexpr int decode_conv_bytes(int D, bool q8) { return q8 ? 2 * kDecodeTile * 2 * D : 0; }
 // ring depth: as many slots as fit the workgroup's waves in about 150 KB, at
 // most 4
-__host__ __device__ constexpr int decode_ring(int D, int hslots) {
-  return (150 * 1024) / (decode_wg_waves(D) * decode_slot_bytes(D, hslots)) > 4
+__host__ __device__ constexpr int decode_ring(int D, int hslots, bool q8 = false) {
+  return (150 * 1024 - decode_wg_waves(D) * decode_conv_bytes(D, q8)) /
+                     (decode_wg_waves(D) * decode_slot_bytes(D, hslots, q8)) > 4
              ? 4
-             : (150 * 1024) / (decode_wg_waves(D) * decode_slot_bytes(D, hslots));
+             : (150 * 1024 - decode_wg_waves(D) * decode_conv_bytes(D, q8)) /
+                   (decode_wg_waves(D) * decode_slot_bytes(D, hslots, q8));
 }
 // per wave: the ring, a 16-byte piece record per slot, 512 bytes of
-// prefetched metadata
-__host__ __device__ constexpr int decode_lds_bytes(int D, int hslots) {
-  return decode_wg_waves(D) * (decode_ring(D, hslots) * (decode_slot_bytes(D, hslots) + 16) + 512);
+// prefetched metadata (and the converted tiles)
+__host__ __device__ constexpr int decode_lds_bytes(int D, int hslots, bool q8 = false) {
+  return decode_wg_waves(D) *
+         (decode_ring(D, hslots, q8) * (decode_slot_bytes(D, hslots, q8) + 16) + 512 + decode_conv_bytes(D, q8));
 }
-__host__ __device__ constexpr int decode_wg_per_cu(int D, int hslots) {
-  return (160 * 1024) / decode_lds_bytes(D, hslots) > 0 ? (160 * 1024) / decode_lds_bytes(D, hslots) : 1;
+__host__ __device__ constexpr int decode_wg_per_cu(int D, int hslots, bool q8 = false) {
+  return (160 * 1024) / decode_lds_bytes(D, hslots, q8) > 0 ? (160 * 1024) / decode_lds_bytes(D, hslots, q8) : 1;
 }
 // floor(a / b) for 0 <= a, 0 < b: in 32 bits when both fit (a 64-bit
 // division is a long instruction sequence on the GPU)
@@ -143,6 +152,10 @@ struct ScatterPlanParams {
   int32_t decode_units;        // units per sequence (Hkv * head chunks)
   int32_t decode_waves;        // W
   int32_t prefill_positions;   // query positions per prefill half-tile
+  const float* k_scale;        // [Hkv, D] with INT8 caches, else null
+  const float* v_scale;
+  int32_t q8;                  // caches hold INT8 codes
+  int32_t bf16;                // step rows are bf16 (else fp16)
 };
 
 struct AttnParams {
@@ -173,6 +186,8 @@ struct AttnParams {
   float scale_log2;            // scale * log2(e)
   float* lse_out;              // [N, H] natural-log lse, or null
   float* out_f32;              // [N, H*D] output before rounding, or null
+  const float* k_scale;        // [Hkv, D] with INT8 caches (codes), else null
+  const float* v_scale;
 };
 
 // fixed-order merge of partial states (pa_merge_states)
@@ -190,9 +205,9 @@ struct MergeStatesParams {
 
 // ---- launchers (defined in the .hip files) ---------------------------------
 hipError_t launch_scatter_plan(const ScatterPlanParams& p, hipStream_t s);
-hipError_t launch_decode(const AttnParams& p, int head_size, int head_slots, bool bf16, int grid, hipStream_t s);
-hipError_t launch_prefill(const AttnParams& p, int head_size, bool bf16, int grid, hipStream_t s);
-size_t prefill_lds_bytes(int head_size);
+hipError_t launch_decode(const AttnParams& p, int head_size, int head_slots, bool bf16, bool q8, int grid,
+                         hipStream_t s);
+hipError_t launch_prefill(const AttnParams& p, int head_size, bool bf16, bool q8, int grid, hipStream_t s);
 hipError_t launch_merge_states(const MergeStatesParams& p, hipStream_t s);
 
 }  // namespace pa

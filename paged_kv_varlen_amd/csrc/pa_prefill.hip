@@ -54,6 +54,14 @@
 // group and all keys of a step (two 32-key sub-steps), and a ring of two
 // steps; everything else as above.
 //
+// INT8 caches: the ring holds the cached codes (one byte per element, rows
+// of D bytes, unswizzled) and each step first turns them into data-type rows
+// of a stage buffer, in the swizzled layout above (exact: |code| <= 127), so
+// the products run as for 16-bit caches.  The scores then use the codes of K,
+// so each query row is multiplied by the kv head's K scales (rounded to the
+// data type) once per item; O is multiplied by the V scales at the final
+// write.
+//
 // Items are spread over up to eight queues by kv head and a workgroup serves
 // first the queue of the XCD it runs on (workgroup id mod 8), so each XCD's
 // L2 holds the K/V of few heads; when its queue is empty it helps the others.
@@ -105,6 +113,21 @@ __device__ inline void wait_fills() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
+// direct global->LDS load of LB bytes per lane (lane i's bytes land at
+// dst + LB * i).  The size is a literal in each branch: the host pass rejects
+// a size that is only known at template instantiation.
+template <int LB>
+__device__ inline void fill_lds(const char* src, char* dst) {
+  static_assert(LB == 16 || LB == 4, "direct load size");
+  if constexpr (LB == 16)
+    __builtin_amdgcn_global_load_lds((PA_GLOBAL void*)src, (PA_LDS void*)dst, 16, 0, 0);
+  else
+    __builtin_amdgcn_global_load_lds((PA_GLOBAL void*)src, (PA_LDS void*)dst, 4, 0, 0);
+}
+
+// s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt at their maximum): this
+// wave's LDS writes are done, the fills in flight are not waited for
+__device__ inline void wait_lds() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 // workgroup barrier without the memory fence of __syncthreads() (which would
 // also wait for every fill in flight); the empty asm statements keep the
 // compiler from moving memory accesses across it
@@ -119,7 +142,7 @@ __device__ inline void plain_barrier() {
 // needs a SIMD of its own (four waves, up to 512 registers each); each wave
 // then takes all 64 keys of a step as two 32-key sub-steps (one kv group),
 // and a ring of two steps (64 KB each) fits in LDS.
-template <int D>
+template <int D, bool Q8 = false>
 struct PrefillShape {
   static constexpr bool WIDE = D > 128;
   static constexpr int WAVES = WIDE ? 4 : 8;         // waves per workgroup
@@ -127,12 +150,20 @@ struct PrefillShape {
   static constexpr int KVG = WIDE ? 1 : 2;           // kv groups (waves sharing a row group)
   static constexpr int SUBS = 2 / KVG;               // 32-key sub-steps per wave and step
   static constexpr int RING = WIDE ? 2 : 4;          // LDS buffers per tensor
-  static constexpr int ROWB = D * 2;                 // bytes per key row
+  static constexpr int ROWB = D * 2;                 // bytes per key row (data type)
   static constexpr int CPR = D / 8;                  // 16-byte chunks per row
   static constexpr int ROWS_PER_LOAD = 64 / CPR;     // rows per 1 KB direct load
   static constexpr int WAVE_ROWS = kPrefillKeys / WAVES;  // rows of K (and V) each wave fetches
-  static constexpr int LOADS = WAVE_ROWS / ROWS_PER_LOAD;  // direct loads per wave per tensor
-  static constexpr int BUF = kPrefillKeys * ROWB;    // bytes per K (or V) buffer
+  static constexpr int BUF = kPrefillKeys * ROWB;    // bytes per K (or V) step, data type
+  // cached rows as fetched: ROWC bytes each (INT8: codes), LB bytes per lane
+  // and direct load (4 when a wave's rows are under 1 KB)
+  static constexpr int ROWC = Q8 ? D : ROWB;
+  static constexpr int LB = WAVE_ROWS * ROWC >= 1024 ? 16 : 4;
+  static constexpr int LOADS = WAVE_ROWS * ROWC / (64 * LB);  // direct loads per wave per tensor
+  static constexpr int CBUF = kPrefillKeys * ROWC;   // bytes per ring buffer
+  // INT8: the converted K and V rows of the step, and the kv-group merge
+  // area (one buffer of O per row group)
+  static constexpr int STAGE = Q8 ? (KVG == 2 ? 4 : 2) * BUF : 16;
   static constexpr int QK_STEPS = D / 16;            // MFMA k-steps over the head dim
   static constexpr int O_TILES = D / 32;             // 32-wide d tiles of O^T
   // steps per slot window: 4 slots per step, RING - 1 steps fetched ahead,
@@ -145,32 +176,37 @@ struct PrefillShape {
   static __device__ int v_swz(int row) { return D >= 128 ? ((row & 3) << 2) : 0; }
 };
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool Q8>
 __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnParams p) {
-  using S = PrefillShape<D>;
+  using S = PrefillShape<D, Q8>;
   using E = Elem<BF16>;
   typedef typename E::x8 x8;
   typedef typename E::x4 x4;
   constexpr int ROWB = S::ROWB, CPR = S::CPR;
   constexpr int kRing = S::RING;
   constexpr int kChunk = S::CHUNK;
-  static_assert(S::LOADS >= 1, "loads per wave");
+  static_assert(S::LOADS >= 1 && S::LOADS * 64 * S::LB == S::WAVE_ROWS * S::ROWC, "loads per wave");
+  constexpr int ES = Q8 ? 1 : 2;  // bytes per cached element
 
   // one LDS object per ring buffer and tensor: the compiler can then see that
   // a fill of one buffer never aliases reads of another and does not make
   // those reads wait for the fill
-  __shared__ __align__(16) char k_lds0[S::BUF];
-  __shared__ __align__(16) char k_lds1[S::BUF];
-  __shared__ __align__(16) char k_lds2[kRing > 2 ? S::BUF : 16];
-  __shared__ __align__(16) char k_lds3[kRing > 2 ? S::BUF : 16];
-  __shared__ __align__(16) char v_lds0[S::BUF];
-  __shared__ __align__(16) char v_lds1[S::BUF];
-  __shared__ __align__(16) char v_lds2[kRing > 2 ? S::BUF : 16];
-  __shared__ __align__(16) char v_lds3[kRing > 2 ? S::BUF : 16];
+  __shared__ __align__(16) char k_lds0[S::CBUF];
+  __shared__ __align__(16) char k_lds1[S::CBUF];
+  __shared__ __align__(16) char k_lds2[kRing > 2 ? S::CBUF : 16];
+  __shared__ __align__(16) char k_lds3[kRing > 2 ? S::CBUF : 16];
+  __shared__ __align__(16) char v_lds0[S::CBUF];
+  __shared__ __align__(16) char v_lds1[S::CBUF];
+  __shared__ __align__(16) char v_lds2[kRing > 2 ? S::CBUF : 16];
+  __shared__ __align__(16) char v_lds3[kRing > 2 ? S::CBUF : 16];
+  __shared__ __align__(16) char stage[S::STAGE];
   __shared__ int slot_lds[kSlotWindow];
   __shared__ int lds_item;
   auto kbuf = [&](int b) -> char* { return b == 0 ? k_lds0 : b == 1 ? k_lds1 : b == 2 ? k_lds2 : k_lds3; };
   auto vbuf = [&](int b) -> char* { return b == 0 ? v_lds0 : b == 1 ? v_lds1 : b == 2 ? v_lds2 : v_lds3; };
+  // the K and V rows the products read (data type, swizzled)
+  auto kread = [&](int b) -> char* { return Q8 ? stage : kbuf(b); };
+  auto vread = [&](int b) -> char* { return Q8 ? stage + S::BUF : vbuf(b); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -236,18 +272,26 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
     }
   }
 
-  // loader: a direct load covers ROWS_PER_LOAD rows of the wave's 8; byte
-  // offsets (from the wave's first row) of this lane's swizzled 16-byte chunk
-  // for each load, and of the same chunk in the zero page
+  // loader: direct load i of a wave covers 64 * LB bytes of its WAVE_ROWS
+  // rows; byte offsets (from the wave's first row) of this lane's piece for
+  // each load (16-bit rows: a swizzled 16-byte chunk; INT8: bytes in order),
+  // and of the same piece in the zero page
   const int lrow0 = lane / CPR;
   const int lchunk = lane % CPR;
+  auto load_row = [&](int i) -> int {  // row (within the wave's) of this lane's piece of load i
+    return Q8 ? (64 * S::LB * i + S::LB * lane) / S::ROWC : S::ROWS_PER_LOAD * i + lrow0;
+  };
   uint32_t offk[S::LOADS], offv[S::LOADS];
 #pragma unroll
   for (int i = 0; i < S::LOADS; ++i) {
-    const int rl = S::ROWS_PER_LOAD * i + lrow0;  // row within the wave's 8
-    const int trow = S::WAVE_ROWS * wave + rl;    // row within the step's 64
-    offk[i] = static_cast<uint32_t>((rl * static_cast<int>(kv_row) + (lchunk ^ S::k_swz(trow)) * 8) * 2);
-    offv[i] = static_cast<uint32_t>((rl * static_cast<int>(kv_row) + (lchunk ^ S::v_swz(trow)) * 8) * 2);
+    const int rl = load_row(i);
+    const int trow = S::WAVE_ROWS * wave + rl;  // row within the step's 64
+    if constexpr (Q8) {
+      offk[i] = offv[i] = static_cast<uint32_t>(rl * static_cast<int>(kv_row) + (64 * S::LB * i + S::LB * lane) % S::ROWC);
+    } else {
+      offk[i] = static_cast<uint32_t>((rl * static_cast<int>(kv_row) + (lchunk ^ S::k_swz(trow)) * 8) * 2);
+      offv[i] = static_cast<uint32_t>((rl * static_cast<int>(kv_row) + (lchunk ^ S::v_swz(trow)) * 8) * 2);
+    }
   }
 
   int queue = home, tried = 0;
@@ -302,6 +346,16 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
       for (int kk = 0; kk < S::QK_STEPS; ++kk) {
         uint4 raw = make_uint4(0u, 0u, 0u, 0u);
         if (row_valid) raw = *reinterpret_cast<const uint4*>(qrow + 16 * kk + 8 * lhalf);
+        if constexpr (Q8) {  // q_d * ks_d, d = 16 kk + 8 lhalf + e, rounded to the data type
+          const float4* ks = reinterpret_cast<const float4*>(p.k_scale + static_cast<int64_t>(kvh) * D + 16 * kk +
+                                                             8 * lhalf);
+          const float4 s0 = ks[0], s1 = ks[1];
+          const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+          x8 qx = __builtin_bit_cast(x8, raw);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qx[e] = E::round(static_cast<float>(qx[e]) * sv[e]);
+          raw = __builtin_bit_cast(uint4, qx);
+        }
         if (negate_q) {
           raw.x ^= 0x80008000u; raw.y ^= 0x80008000u; raw.z ^= 0x80008000u; raw.w ^= 0x80008000u;
         }
@@ -315,15 +369,13 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
     float m = kNegInf, l = 0.f;
 
     const int32_t* btab = p.block_table + static_cast<int64_t>(b) * p.max_blocks;
-    const uint16_t* kcache = p.key_cache + static_cast<int64_t>(kvh) * D;
-    const uint16_t* vcache = p.value_cache + static_cast<int64_t>(kvh) * D;
     // cache slot (block_table[k / bs] * bs + k % bs) of every 16th key k <
     // min(L, nsteps * 64), for 16-key groups [gbase, gbase + kSlotWindow);
     // a wave's 8 rows of a step never cross a page (bs is a multiple of 16)
     const int ngroups = (min(L, nsteps * kPrefillKeys) + 15) / 16;
-    const char* kbytes = reinterpret_cast<const char*>(kcache);
-    const char* vbytes = reinterpret_cast<const char*>(vcache);
-    const uint32_t row_bytes = static_cast<uint32_t>(kv_row) * 2;
+    const char* kbytes = reinterpret_cast<const char*>(p.key_cache) + static_cast<int64_t>(kvh) * D * ES;
+    const char* vbytes = reinterpret_cast<const char*>(p.value_cache) + static_cast<int64_t>(kvh) * D * ES;
+    const uint32_t row_bytes = static_cast<uint32_t>(kv_row) * ES;
     int gbase = 0;
     auto fill_window = [&](int first) {
       gbase = first;
@@ -348,25 +400,25 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
         const char* kb = kbytes + at;
         const char* vb = vbytes + at;
         for (int i = i_first; i < i_last; ++i) {
-          const int dst = (S::WAVE_ROWS * wave + S::ROWS_PER_LOAD * i) * ROWB;
-          __builtin_amdgcn_global_load_lds((PA_GLOBAL void*)(kb + offk[i]), (PA_LDS void*)(kbuf(buf) + dst), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds((PA_GLOBAL void*)(vb + offv[i]), (PA_LDS void*)(vbuf(buf) + dst), 16, 0, 0);
+          const int dst = S::WAVE_ROWS * wave * S::ROWC + 64 * S::LB * i;
+          fill_lds<S::LB>(kb + offk[i], kbuf(buf) + dst);
+          fill_lds<S::LB>(vb + offv[i], vbuf(buf) + dst);
         }
       } else {
         // rows past the history: read the zero page (rows < L read as usual)
         const int slot = jw < L ? __builtin_amdgcn_readfirstlane(slot16) + (jw & 15) : 0;
         const char* zb = reinterpret_cast<const char*>(p.zeros);
         for (int i = i_first; i < i_last; ++i) {
-          const int rl = S::ROWS_PER_LOAD * i + lrow0;
+          const int rl = load_row(i);
           const bool hist = jw + rl < L;
           const int64_t at = static_cast<int64_t>(slot) * row_bytes;
           const uint32_t zk = offk[i] - static_cast<uint32_t>(rl) * row_bytes;  // chunk offset alone
           const uint32_t zv = offv[i] - static_cast<uint32_t>(rl) * row_bytes;
           const char* ks = hist ? kbytes + at + offk[i] : zb + zk;
           const char* vs = hist ? vbytes + at + offv[i] : zb + zv;
-          const int dst = (S::WAVE_ROWS * wave + S::ROWS_PER_LOAD * i) * ROWB;
-          __builtin_amdgcn_global_load_lds((PA_GLOBAL void*)ks, (PA_LDS void*)(kbuf(buf) + dst), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds((PA_GLOBAL void*)vs, (PA_LDS void*)(vbuf(buf) + dst), 16, 0, 0);
+          const int dst = S::WAVE_ROWS * wave * S::ROWC + 64 * S::LB * i;
+          fill_lds<S::LB>(ks, kbuf(buf) + dst);
+          fill_lds<S::LB>(vs, vbuf(buf) + dst);
         }
       }
     };
@@ -387,7 +439,7 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
         x8 kf[KOFF];
 #pragma unroll
         for (int kk = 0; kk < KOFF; ++kk)
-          kf[kk] = *reinterpret_cast<const x8*>(kbuf(buf) + so + 256 * decltype(kb)::value + koff[kk]);
+          kf[kk] = *reinterpret_cast<const x8*>(kread(buf) + so + 256 * decltype(kb)::value + koff[kk]);
         asm volatile("" ::: "memory");  // keep the reads ahead of the products
 #pragma unroll
         for (int kk = 0; kk < KOFF; ++kk) s = E::mfma_32x32x16(kf[kk], qf[k0 + kk], s);
@@ -400,7 +452,7 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
       // after the softmax, to bound the registers in flight)
       constexpr int VPRE = S::O_TILES > 4 ? 1 : 2;
       auto read_v = [&](int ks, int mt) __attribute__((always_inline)) -> x8 {
-        char* vb = vbuf(buf) + so + voff[mt % VOFF] + 256 * (mt / VOFF) + 16 * ks * ROWB;
+        char* vb = vread(buf) + so + voff[mt % VOFF] + 256 * (mt / VOFF) + 16 * ks * ROWB;
         const fp16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((PA_LDS fp16x4_t*)vb);
         const fp16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((PA_LDS fp16x4_t*)(vb + 8 * ROWB));
         return __builtin_shufflevector(__builtin_bit_cast(x4, lo), __builtin_bit_cast(x4, hi), 0, 1, 2, 3, 4, 5, 6,
@@ -469,6 +521,35 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
       }
     };
 
+    // INT8: the codes of the step in ring buffer buf -> data-type rows of the
+    // stage, in the layout the products read: cached chunk c (16 codes) of
+    // row r becomes chunks 2c and 2c+1 of row r, swizzled
+    auto convert = [&](auto buf_tag) __attribute__((always_inline)) {
+      constexpr int buf = decltype(buf_tag)::value;
+      constexpr int NC = kPrefillKeys * D / 16;  // 16-code chunks per tensor
+      constexpr int CPRC = D / 16;               // per row
+      auto one = [&](bool is_v, int cc) __attribute__((always_inline)) {
+        const int r = cc / CPRC, k = cc % CPRC;
+        const uint4 raw = *reinterpret_cast<const uint4*>((is_v ? vbuf(buf) : kbuf(buf)) + 16 * cc);
+        const x8 lo = E::from_codes(raw.x, raw.y), hi = E::from_codes(raw.z, raw.w);
+        const int swz = is_v ? S::v_swz(r) : S::k_swz(r);
+        char* row = stage + (is_v ? S::BUF : 0) + r * ROWB;
+        *reinterpret_cast<x8*>(row + (((2 * k) ^ swz) << 4)) = lo;
+        *reinterpret_cast<x8*>(row + (((2 * k + 1) ^ swz) << 4)) = hi;
+      };
+      if constexpr (NC >= S::THREADS) {
+        static_assert(NC % S::THREADS == 0, "conversion split");
+#pragma unroll
+        for (int it = 0; it < NC / S::THREADS; ++it) {
+          one(false, it * S::THREADS + tid);
+          one(true, it * S::THREADS + tid);
+        }
+      } else {
+        static_assert(2 * NC == S::THREADS, "conversion split");
+        one(tid >= NC, tid >= NC ? tid - NC : tid);  // (wave-uniform tensor)
+      }
+    };
+
     // Step j computes from ring buffer j % 4 and fetches step j + 3 into ring
     // buffer (j + 3) % 4, which held step j - 1 (finished by every wave at the
     // barrier that ended it).  Each step issues 2 * LOADS direct loads per
@@ -478,6 +559,9 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
     // With a ring of two (head size 256) the fill of step j + 1 goes into
     // buffer (j + 1) % 2 at the start of step j (its last reader, step j - 1,
     // ended at the barrier) and lands before the barrier that ends step j.
+    // With INT8 caches a ring buffer's readers are the conversion at the start
+    // of its step, which ends at a barrier of its own; the products read the
+    // stage, which the barrier ending a step frees for the next conversion.
     auto step = [&](auto buf_tag, int jstep) __attribute__((always_inline)) {
       constexpr int buf = decltype(buf_tag)::value;
       constexpr int nbuf = (buf + kRing - 1) % kRing;
@@ -486,6 +570,13 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
       const int slot16 = slot_of(s_next);  // (in the window; unused past the history)
       if constexpr (kRing == 2) {
         if (more) issue(std::integral_constant<int, nbuf>{}, s_next, slot16, 0, S::LOADS);
+      }
+      if constexpr (Q8) {
+        // the stage's last readers finished at the barrier that ended the
+        // previous step; the codes of this step landed before it
+        convert(buf_tag);
+        wait_lds();
+        plain_barrier();
       }
       static_for<S::SUBS>([&](auto sub) __attribute__((always_inline)) {
         // first key of this wave's 32 keys
@@ -549,10 +640,11 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
 
     // merge the two kv groups (group 0 first) and write.  Row group r's O of
     // kv group 1 goes to K buffer r ([O_TILES*16][64 lanes] floats), (m, l)
-    // of all row groups to V buffer 0.  (One kv group: nothing to merge.)
+    // of all row groups to V buffer 0 (INT8: stage buffer r and the slot
+    // window).  (One kv group: nothing to merge.)
     wait_fills<0>();  // (the last steps already waited)
-    float* xo = reinterpret_cast<float*>(kbuf(rg));
-    float* xml = reinterpret_cast<float*>(v_lds0);
+    float* xo = reinterpret_cast<float*>(Q8 ? stage + (S::KVG == 2 ? rg * S::BUF : 0) : kbuf(rg));
+    float* xml = Q8 ? reinterpret_cast<float*>(slot_lds) : reinterpret_cast<float*>(v_lds0);
     if constexpr (S::KVG == 2) {
       if (kvg == 1) {
 #pragma unroll
@@ -586,7 +678,6 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
         for (int mt = 0; mt < S::O_TILES; ++mt)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            uint32_t w[2];
             float v[4];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
@@ -599,8 +690,19 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
                 v[2 * e] = o[mt][ir] * inv;
                 v[2 * e + 1] = o[mt][ir + 1] * inv;
               }
-              w[e] = static_cast<uint32_t>(E::bits(v[2 * e])) | (static_cast<uint32_t>(E::bits(v[2 * e + 1])) << 16);
             }
+            if constexpr (Q8) {  // O used the codes of V: times the V scales of d = 32mt + 8q + 4lhalf + 0..3
+              const float4 vs = *reinterpret_cast<const float4*>(p.v_scale + static_cast<int64_t>(kvh) * D + 32 * mt +
+                                                                 8 * q + 4 * lhalf);
+              v[0] *= vs.x;
+              v[1] *= vs.y;
+              v[2] *= vs.z;
+              v[3] *= vs.w;
+            }
+            uint32_t w[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+              w[e] = static_cast<uint32_t>(E::bits(v[2 * e])) | (static_cast<uint32_t>(E::bits(v[2 * e + 1])) << 16);
             *reinterpret_cast<uint2*>(orow + 32 * mt + 8 * q + 4 * lhalf) = make_uint2(w[0], w[1]);
             if (orow_f != nullptr)
               *reinterpret_cast<float4*>(orow_f + 32 * mt + 8 * q + 4 * lhalf) = make_float4(v[0], v[1], v[2], v[3]);
@@ -611,36 +713,43 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
   }
 }
 
-template <int D>
+template <int D, bool Q8>
 constexpr size_t prefill_smem() {
-  using S = PrefillShape<D>;
-  return 2 * S::RING * static_cast<size_t>(S::BUF) + (S::RING > 2 ? 0 : 4 * 16) + kSlotWindow * sizeof(int) + 16;
+  using S = PrefillShape<D, Q8>;
+  return 2 * S::RING * static_cast<size_t>(S::CBUF) + (S::RING > 2 ? 0 : 4 * 16) + S::STAGE +
+         kSlotWindow * sizeof(int) + 16;
 }
-// the merge area (O of one row group) must fit one K buffer, (m, l) one V buffer
-static_assert(4 * 16 * 64 * sizeof(float) <= PrefillShape<128>::BUF, "merge area");
-static_assert(2 * 16 * 64 * sizeof(float) <= PrefillShape<64>::BUF, "merge area");
-static_assert(prefill_smem<128>() <= 160 * 1024, "LDS budget");
-static_assert(prefill_smem<256>() <= 160 * 1024, "LDS budget");
+// the merge area (O of one row group) must fit one K buffer (INT8: one stage
+// buffer), (m, l) of the four row groups one V buffer (INT8: the slot window)
+static_assert(4 * 16 * 64 * sizeof(float) <= PrefillShape<128>::CBUF, "merge area");
+static_assert(2 * 16 * 64 * sizeof(float) <= PrefillShape<64>::CBUF, "merge area");
+static_assert(4 * 16 * 64 * sizeof(float) <= PrefillShape<128, true>::BUF, "merge area");
+static_assert(2 * 16 * 64 * sizeof(float) <= PrefillShape<64, true>::BUF, "merge area");
+static_assert(4 * 2 * 64 * sizeof(float) <= kSlotWindow * sizeof(int), "merge area");
+static_assert(prefill_smem<128, false>() <= 160 * 1024 && prefill_smem<256, false>() <= 160 * 1024, "LDS budget");
+static_assert(prefill_smem<128, true>() <= 160 * 1024 && prefill_smem<256, true>() <= 160 * 1024, "LDS budget");
+
+template <int D, bool BF16>
+hipError_t launch_prefill_q(const AttnParams& p, bool q8, int grid, hipStream_t s) {
+  if (q8)
+    hipLaunchKernelGGL((prefill_kernel<D, BF16, true>), dim3(grid), dim3(PrefillShape<D, true>::THREADS), 0, s, p);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, BF16, false>), dim3(grid), dim3(PrefillShape<D, false>::THREADS), 0, s,
+                       p);
+  return hipGetLastError();
+}
 
 template <int D>
-hipError_t launch_prefill_t(const AttnParams& p, bool bf16, int grid, hipStream_t s) {
-  if (bf16)
-    hipLaunchKernelGGL((prefill_kernel<D, true>), dim3(grid), dim3(PrefillShape<D>::THREADS), 0, s, p);
-  else
-    hipLaunchKernelGGL((prefill_kernel<D, false>), dim3(grid), dim3(PrefillShape<D>::THREADS), 0, s, p);
-  return hipGetLastError();
+hipError_t launch_prefill_t(const AttnParams& p, bool bf16, bool q8, int grid, hipStream_t s) {
+  return bf16 ? launch_prefill_q<D, true>(p, q8, grid, s) : launch_prefill_q<D, false>(p, q8, grid, s);
 }
 
 }  // namespace
 
-size_t prefill_lds_bytes(int head_size) {
-  return head_size == 256 ? prefill_smem<256>() : head_size == 128 ? prefill_smem<128>() : prefill_smem<64>();
-}
-
-hipError_t launch_prefill(const AttnParams& p, int head_size, bool bf16, int grid, hipStream_t s) {
-  if (head_size == 256) return launch_prefill_t<256>(p, bf16, grid, s);
-  if (head_size == 128) return launch_prefill_t<128>(p, bf16, grid, s);
-  if (head_size == 64) return launch_prefill_t<64>(p, bf16, grid, s);
+hipError_t launch_prefill(const AttnParams& p, int head_size, bool bf16, bool q8, int grid, hipStream_t s) {
+  if (head_size == 256) return launch_prefill_t<256>(p, bf16, q8, grid, s);
+  if (head_size == 128) return launch_prefill_t<128>(p, bf16, q8, grid, s);
+  if (head_size == 64) return launch_prefill_t<64>(p, bf16, q8, grid, s);
   return hipErrorInvalidValue;
 }
 

@@ -128,6 +128,15 @@ def test_workspace_bytes_static_bound():
     (dict(lse=FAKE + 2), ALIGN),                         # lse needs 4-byte alignment
     (dict(output_f32=FAKE + 4), ALIGN),                  # output_f32 needs 16
     (dict(lse=FAKE, output_f32=FAKE), WS),               # both present and aligned
+    (dict(kv_quant=2), UNSUP),                           # only PA_KV_SAME and PA_KV_INT8
+    (dict(kv_quant=-1), UNSUP),
+    (dict(kv_quant=1), NULL),                            # INT8 caches need both scale rows
+    (dict(kv_quant=1, k_scale=FAKE), NULL),
+    (dict(kv_quant=1, k_scale=FAKE, v_scale=FAKE + 4), ALIGN),  # scales need 16-byte alignment
+    (dict(kv_quant=1, k_scale=FAKE, v_scale=FAKE), WS),  # INT8 passes validation
+    (dict(kv_quant=0, k_scale=FAKE + 4), WS),            # scales ignored for 16-bit caches
+    (dict(kv_quant=1, k_scale=FAKE, v_scale=FAKE, dtype=2,
+          query_width=4 * 256, cache_head_size=256), WS),  # with bfloat16 and D=256
     (dict(num_tokens=0, batch_size=2), OK),              # nothing to do: no device work
 ])
 def test_host_validation(case, expect):
@@ -157,7 +166,7 @@ def test_status_strings():
     lib = pa.library()
     for s in range(9):
         assert lib.pa_status_string(s)
-    assert lib.pa_abi_version() == 2
+    assert lib.pa_abi_version() == 3
 
 
 def merge_args(**kw):

@@ -5,7 +5,10 @@ written or untouched; outputs within max-abs 4e-3 of the fp64 oracle (fp16
 inputs, fp32 accumulation, O(1) data).  For bf16 data the bar scales with the
 unit roundoff: bf16 keeps 8 significant bits to fp16's 11, so every rounding
 in the path (P before the PV product, the output) is 8 times coarser and the
-bar is 8 * 4e-3 = 3.2e-2.  Full-size workloads are checked on
+bar is 8 * 4e-3 = 3.2e-2.  INT8 caches keep the bar of their data type: the
+codes are bit-exact, and the one extra rounding (the K scales folded into the
+query, rounded to the data type) moves the scores by about 3e-4 (fp16) or
+2e-3 (bf16) of a unit, far inside it.  Full-size workloads are checked on
 every cache slot and on sampled output rows the oracle computes one by one.
 Every call goes through the C ABI (libpagedattn.so via ctypes).
 """
@@ -69,17 +72,20 @@ class DevBatch:
         self.past = to_dev(b.past)
         self.table = to_dev(b.block_table)
         self.slots = to_dev(b.slot_mapping)
+        self.ks = to_dev(b.k_scale)
+        self.vs = to_dev(b.v_scale)
         self.b = b
 
     def run(self, **kw):
         b = self.b
         return pa.paged_attention(self.q, self.k, self.v, self.kc, self.vc, self.cum, self.past,
                                   self.table, self.slots, num_heads=b.num_heads,
-                                  kv_num_heads=b.kv_num_heads, scale=b.scale, **kw)
+                                  kv_num_heads=b.kv_num_heads, scale=b.scale,
+                                  k_scale=self.ks, v_scale=self.vs, **kw)
 
 
 def gpu_run(b: W.Batch):
-    say(f"[gpu] {b.name} {b.dtype} seed={b.seed} N={b.num_tokens} B={b.batch_size} "
+    say(f"[gpu] {b.name} {b.dtype} kv={b.kv_quant} seed={b.seed} N={b.num_tokens} B={b.batch_size} "
         f"H={b.num_heads}/{b.kv_num_heads} D={b.head_size} bs={b.block_size} NB={b.num_blocks}")
     d = DevBatch(b)
     out = d.run()
@@ -103,14 +109,21 @@ def sample_rows(b: W.Batch, per_seq=6, max_seqs=None, must=(), seed=0):
     return np.array(sorted(rows), dtype=np.int64)
 
 
+def raw_bits(x):
+    """Cache contents as unsigned integers of their width (int8 codes or 16-bit values)."""
+    return x.view(np.uint8 if x.itemsize == 1 else np.uint16)
+
+
 def check(b: W.Batch, rows=None, gpu=None):
     out, kc, vc = gpu if gpu is not None else gpu_run(b)
     ref, rkc, rvc = oracle.paged_attention(b.query, b.key, b.value, b.key_cache, b.value_cache,
                                            b.cum, b.past, b.block_table, b.slot_mapping,
                                            num_heads=b.num_heads, kv_num_heads=b.kv_num_heads,
-                                           scale=b.scale, rows=rows)
-    assert np.array_equal(kc.view(np.uint16), rkc.view(np.uint16)), "key_cache differs"
-    assert np.array_equal(vc.view(np.uint16), rvc.view(np.uint16)), "value_cache differs"
+                                           scale=b.scale, rows=rows, k_scale=b.k_scale,
+                                           v_scale=b.v_scale)
+    assert kc.dtype == rkc.dtype and vc.dtype == rvc.dtype
+    assert np.array_equal(raw_bits(kc), raw_bits(rkc)), "key_cache differs"
+    assert np.array_equal(raw_bits(vc), raw_bits(rvc)), "value_cache differs"
     sel = np.arange(b.num_tokens) if rows is None else rows
     got = as_f64(out[sel])
     assert np.all(np.isfinite(got))
@@ -534,3 +547,90 @@ def test_hip_graph_replay_wide(D, dtype):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+# ------------------------------------------------------------------ INT8 caches (codes + per-channel scales)
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_int8_tiny(dtype):
+    check(W.tiny(0, dtype=dtype, kv_quant="int8"))
+
+
+@pytest.mark.parametrize("case", range(len(SWEEP)))
+@pytest.mark.parametrize("dtype,packed,slots", [("f16", False, None), ("bf16", True, "drop")])
+def test_int8_sweep(case, dtype, packed, slots):
+    q, p, H, Hkv, D, bs = SWEEP[case]
+    n = sum(q)
+    b = W.make_batch(q, p, num_heads=H, kv_num_heads=Hkv, head_size=D, block_size=bs,
+                     seed=500 + case, packed=packed, slot_mode=slots,
+                     drop_count=max(1, n // 20) if slots else 0, num_blocks=None,
+                     name=f"int8_sweep{case}", dtype=dtype, kv_quant="int8")
+    check(b)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_int8_pure_decode_full(dtype):
+    check(W.pure_decode(0, dtype=dtype, kv_quant="int8"))
+
+
+def test_int8_mixed():
+    b = W.mixed(0, kv_quant="int8")
+    check(b, rows=sample_rows(b, per_seq=10))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_int8_long_prefill(dtype):
+    b = W.long_prefill(0, dtype=dtype, kv_quant="int8")
+    edges = [0, 1, 31, 32, 33, 1023, 1024, 2015, 2016, 2046, 2047]
+    check(b, rows=sample_rows(b, per_seq=40, must=edges))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("case", range(len(HD256)))
+def test_int8_head_size_256(case, dtype):
+    q, p, H, Hkv, bs = HD256[case]
+    b = W.make_batch(q, p, num_heads=H, kv_num_heads=Hkv, head_size=256, block_size=bs,
+                     seed=520 + case, name=f"int8_hd256_{case}", dtype=dtype, kv_quant="int8")
+    check(b, rows=sample_rows(b, per_seq=12, seed=case))
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_int8_extreme_codes_outside_history(D):
+    # every slot the call must not read holds code 127: keys past a history
+    # come from the zero page, never the cache (a read would move the scores
+    # by tens of units)
+    b = W.make_batch([1, 37, 1, 5, 70], [50, 20, 4095, 0, 190], num_heads=8, kv_num_heads=2,
+                     head_size=D, block_size=64, seed=540 + D, num_blocks=200, name=f"int8_far{D}",
+                     kv_quant="int8")
+    keep = np.zeros(b.num_blocks * b.block_size, dtype=bool)
+    for i in range(b.batch_size):
+        for j in range(int(b.kv_lens[i])):
+            keep[int(b.block_table[i, j // b.block_size]) * b.block_size + j % b.block_size] = True
+    for cache in (b.key_cache, b.value_cache):
+        flat = cache.reshape(b.num_blocks * b.block_size, -1)
+        flat[~keep] = 127
+    check(b)
+
+
+def test_int8_state_and_determinism():
+    b = W.make_batch([300, 1, 1, 64], [700, 9000, 3, 0], num_heads=16, kv_num_heads=4, head_size=128,
+                     block_size=16, seed=550, name="int8_state", kv_quant="int8")
+    rows = sample_rows(b, per_seq=20, seed=5)
+    d = DevBatch(b)
+    f32 = torch.empty((b.num_tokens, b.num_heads * 128), dtype=torch.float32, device=DEV)
+    out, lse = d.run(return_lse=True, output_f32=f32)
+    out = out.clone()
+    again = d.run()  # the second call rewrites the same codes: same bits
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16))
+    ref, _, _, rlse = oracle.paged_attention(b.query, b.key, b.value, b.key_cache, b.value_cache,
+                                             b.cum, b.past, b.block_table, b.slot_mapping,
+                                             num_heads=b.num_heads, kv_num_heads=b.kv_num_heads,
+                                             scale=b.scale, rows=rows, with_lse=True,
+                                             k_scale=b.k_scale, v_scale=b.v_scale)
+    o_low, o32, l32 = to_host(out), f32.cpu().numpy(), lse.cpu().numpy()
+    assert rounding_of(o32, o_low)
+    e_o = np.max(np.abs(o32[rows].astype(np.float64) - ref[rows]))
+    e_l = np.max(np.abs(l32[rows].astype(np.float64) - rlse[rows]))
+    say(f"      state: max|err| out_f32 {e_o:.3e}, lse {e_l:.3e}")
+    assert e_o <= TOL and e_l <= LSE_TOL

@@ -78,24 +78,35 @@ def counter_means(csv_path: str, symbol: str) -> dict:
     return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
 
 
+def variant_suffix(dtype="f16", head_size=0, kv_quant="none") -> str:
+    """Names a workload variant in profile file names ('' for the workloads as
+    defined: fp16 data and caches, their own head size)."""
+    return ("" if dtype == "f16" else f"_{dtype}") + (f"_hd{head_size}" if head_size else "") + \
+        ("_int8" if kv_quant == "int8" else "")
+
+
+VARIANT = {"suffix": ""}  # set by main() from --dtype / --head-size / --kv-quant
+
+
 def write_traffic(kernel, workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv,
                   copy_bytes):
     """HBM bytes per launch of `kernel` from FETCH_SIZE / WRITE_SIZE runs (KiB per
     dispatch), each scaled by what the counter reads for a plain device copy of
-    copy_bytes bytes; written to profiles/traffic_<kernel>_<workload>.json."""
+    copy_bytes bytes; written to profiles/traffic_<kernel>_<workload><variant>.json."""
     sym = KERNEL_SYMBOL[kernel]
     f_k, nf = counter_means(fetch_csv, sym)["FETCH_SIZE"]
     w_k, nw = counter_means(write_csv, sym)["WRITE_SIZE"]
     f_c, _ = counter_means(copy_fetch_csv, "copyBuffer")["FETCH_SIZE"]
     w_c, _ = counter_means(copy_write_csv, "copyBuffer")["WRITE_SIZE"]
     sf, sw = copy_bytes / (f_c * 1024.0), copy_bytes / (w_c * 1024.0)
-    rec = {"kernel": kernel, "workload": workload, "source_hash": source_hash(kernel),
+    rec = {"kernel": kernel, "workload": workload + VARIANT["suffix"],
+           "source_hash": source_hash(kernel),
            "fetch_kib_per_dispatch": round(f_k, 1), "write_kib_per_dispatch": round(w_k, 1),
            "dispatches": [nf, nw], "copy_bytes": copy_bytes,
            "copy_fetch_kib": round(f_c, 1), "copy_write_kib": round(w_c, 1),
            "fetch_scale": round(sf, 4), "write_scale": round(sw, 4),
            "bytes_per_launch": int(f_k * 1024.0 * sf + w_k * 1024.0 * sw)}
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}{VARIANT['suffix']}.json")
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
@@ -105,7 +116,7 @@ def write_traffic(kernel, workload, fetch_csv, write_csv, copy_fetch_csv, copy_w
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from committed rocprofv3 counter summaries, or None
     when there is none or the kernel source changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}{VARIANT['suffix']}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -132,12 +143,14 @@ class Runner:
         self.kc, self.vc = to(batch.key_cache), to(batch.value_cache)
         self.cum, self.past = to(batch.cum), to(batch.past)
         self.table, self.slots = to(batch.block_table), to(batch.slot_mapping)
+        self.ks, self.vs = to(batch.k_scale), to(batch.v_scale)  # INT8 caches only
         D = batch.head_size
         self.out = torch.empty((batch.num_tokens, batch.num_heads * D), dtype=self.q.dtype,
                                device=dev)
         args = pa.make_args(self.q, self.k, self.v, self.kc, self.vc, self.cum, self.past,
                             self.table, self.slots, self.out, num_heads=batch.num_heads,
-                            kv_num_heads=batch.kv_num_heads, scale=batch.scale)
+                            kv_num_heads=batch.kv_num_heads, scale=batch.scale,
+                            k_scale=self.ks, v_scale=self.vs)
         self.ws = torch.empty(max(1, pa.workspace_bytes(args)), dtype=torch.uint8, device=dev)
 
     def step(self, events=None):
@@ -145,13 +158,14 @@ class Runner:
         self.pa.paged_attention(self.q, self.k, self.v, self.kc, self.vc, self.cum, self.past,
                                 self.table, self.slots, num_heads=b.num_heads,
                                 kv_num_heads=b.kv_num_heads, scale=b.scale, output=self.out,
-                                workspace=self.ws, kernel_events=events)
+                                workspace=self.ws, kernel_events=events, k_scale=self.ks,
+                                v_scale=self.vs)
 
 
 def time_workload(name: str, steps: int, warmup: int, seed: int, torch, pa, W, dtype="f16",
-                  head_size=0):
+                  head_size=0, kv_quant="none"):
     t_gen = time.perf_counter()
-    b = W.workload(name, seed, dtype=dtype, head_size=head_size)
+    b = W.workload(name, seed, dtype=dtype, head_size=head_size, kv_quant=kv_quant)
     work = W.work(b)
     log(f"[bench] {name}: generated in {time.perf_counter() - t_gen:.1f}s "
         f"(N={b.num_tokens}, B={b.batch_size}, KV {work['kv_hist_bytes'] / 1e9:.3f} GB, "
@@ -263,7 +277,8 @@ def sub_batch(b, seqs, W):
                    cum=W.cum_from_lens(b.q_lens[seqs]), past=b.past[seqs],
                    block_table=b.block_table[seqs], slot_mapping=pick(b.slot_mapping),
                    num_heads=b.num_heads, kv_num_heads=b.kv_num_heads, head_size=b.head_size,
-                   block_size=b.block_size, scale=b.scale, dtype=b.dtype)
+                   block_size=b.block_size, scale=b.scale, dtype=b.dtype, kv_quant=b.kv_quant,
+                   k_scale=b.k_scale, v_scale=b.v_scale)
 
 
 def cpu_baseline(b, W, target_s: float):
@@ -280,7 +295,8 @@ def cpu_baseline(b, W, target_s: float):
         t = time.perf_counter()
         oracle.paged_attention(sb.query, sb.key, sb.value, sb.key_cache, sb.value_cache, sb.cum,
                                sb.past, sb.block_table, sb.slot_mapping, num_heads=sb.num_heads,
-                               kv_num_heads=sb.kv_num_heads, scale=sb.scale)
+                               kv_num_heads=sb.kv_num_heads, scale=sb.scale,
+                               k_scale=sb.k_scale, v_scale=sb.v_scale)
         return time.perf_counter() - t, W.work(sb)
 
     t1, _ = run(1)
@@ -313,6 +329,9 @@ def main():
                     help="data type of the workloads (the line's dtype field)")
     ap.add_argument("--head-size", type=int, default=0, choices=(0, 64, 128, 256),
                     help="replace the workloads' head size (0: their own)")
+    ap.add_argument("--kv-quant", default="none", choices=("none", "int8"),
+                    help="cache element type: the data type, or int8 codes with per-channel "
+                         "scales (history bytes then count one byte per element)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -327,6 +346,7 @@ def main():
     ap.add_argument("--no-mfma-rate", action="store_true",
                     help="skip the probe run (prefill rooflines then carry no measured ceiling)")
     args = ap.parse_args()
+    VARIANT["suffix"] = variant_suffix(args.dtype, args.head_size, args.kv_quant)
 
     if args.traffic_from:
         write_traffic(args.traffic_kernel, args.workload, *args.traffic_from,
@@ -368,12 +388,13 @@ def main():
     pa.library()  # fail loudly if the HIP library is missing
 
     b, work, ms, wall_ms, kms = time_workload(args.workload, args.steps, args.warmup, args.seed,
-                                              torch, pa, W, args.dtype, args.head_size)
+                                              torch, pa, W, args.dtype, args.head_size,
+                                              args.kv_quant)
     head = summarize(args.workload, b, work, ms, kms)
     also = []
     for name in [x for x in args.also.split(",") if x and x != args.workload]:
         ob, owork, oms, _, okms = time_workload(name, args.steps, args.warmup, args.seed, torch,
-                                                pa, W, args.dtype, args.head_size)
+                                                pa, W, args.dtype, args.head_size, args.kv_quant)
         entry = summarize(name, ob, owork, oms, okms)
         entry["roofline"] = roofline(name, owork, okms)
         also.append(entry)
@@ -396,6 +417,7 @@ def main():
                    "num_tokens": b.num_tokens, "num_heads": b.num_heads,
                    "kv_num_heads": b.kv_num_heads, "head_size": b.head_size,
                    "block_size": b.block_size, "num_blocks": b.num_blocks,
+                   "kv_cache": "int8" if args.kv_quant == "int8" else args.dtype,
                    "kv_hist_bytes": work["kv_hist_bytes"], "wall_ms_per_step": round(wall_ms, 5)},
         "roofline": roofline(args.workload, work, kms),
         "tokens_per_s": head["tokens_per_s"],

@@ -92,7 +92,7 @@ WorkspaceLayout layout(const Resolved& r) {
                             ((static_cast<int64_t>(r.MB) * r.bs + kDecodeTile - 1) / kDecodeTile);
   const int64_t resident = static_cast<int64_t>(device_cus()) * decode_wg_per_cu(r.D, hs, r.q8);
   w.decode_grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(resident, (max_tiles + 31) / 32)));
-  w.decode_waves = w.decode_grid * decode_wg_waves(r.D);
+  w.decode_waves = w.decode_grid * decode_wg_waves(r.D, r.q8);
   const size_t W = static_cast<size_t>(w.decode_waves);
   size_t off = 0;
   w.ctrl = off;

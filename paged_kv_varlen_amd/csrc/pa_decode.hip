@@ -293,6 +293,224 @@ __device__ inline int swz(int k) {
   }
 }
 
+// INT8 caches: XOR swizzle (in 16-byte chunks) of code row r (0..15) of a
+// tile, chosen so that the 8-byte K reads (16 keys, 16 lanes each) and the
+// byte reads of V (keys 4g+j of 16 lanes g, one 16-byte chunk each) touch
+// distinct LDS banks (every 256 bytes hold 256 / D rows)
+template <int D>
+__device__ inline int swz8(int r) {
+  if constexpr (D == 64) return (r >> 2) & 3;
+  else if constexpr (D == 128) return (r >> 1) & 7;
+  else return ((r >> 2) & 3) | ((r & 3) << 2);
+}
+
+// INT8 caches: the tile's codes as operand bits, converted in registers.
+// k[s]: the 8 codes of key n at d = 32 s + 8 g .. +7 (one ds_read_b64).
+// v[4 blk + j]: the code of key 4 g + j at d = 16 blk + n (ds_read_u8, one
+// register each: the 16-bit d16 loads do not keep the other half of their
+// register on parts with SRAM ECC).  Byte j of block blk sits at vb[.] + a
+// constant: with the swizzle above, four base addresses per lane serve every
+// block.  Head size 256 reads in two parts (read, then read_rest), each with
+// its own wait, to bound the registers in flight.
+template <int D>
+struct CodeRegs;
+template <>
+struct CodeRegs<64> {
+  static constexpr int FIRST = 4;  // V blocks of read(); read_rest() has the others
+  u32x2 k[2];
+  uint32_t v[16];
+  template <int OFF>
+  __device__ void read(const uint32_t (&ka)[2], const uint32_t (&vb)[4]) {
+    asm volatile(
+        "ds_read_b64 %0, %18 offset:%24\n\t"
+        "ds_read_b64 %1, %19 offset:%24\n\t"
+        "ds_read_u8 %2, %20 offset:%24+0\n\t"
+        "ds_read_u8 %3, %20 offset:%24+64\n\t"
+        "ds_read_u8 %4, %20 offset:%24+128\n\t"
+        "ds_read_u8 %5, %20 offset:%24+192\n\t"
+        "ds_read_u8 %6, %21 offset:%24+0\n\t"
+        "ds_read_u8 %7, %21 offset:%24+64\n\t"
+        "ds_read_u8 %8, %21 offset:%24+128\n\t"
+        "ds_read_u8 %9, %21 offset:%24+192\n\t"
+        "ds_read_u8 %10, %22 offset:%24+0\n\t"
+        "ds_read_u8 %11, %22 offset:%24+64\n\t"
+        "ds_read_u8 %12, %22 offset:%24+128\n\t"
+        "ds_read_u8 %13, %22 offset:%24+192\n\t"
+        "ds_read_u8 %14, %23 offset:%24+0\n\t"
+        "ds_read_u8 %15, %23 offset:%24+64\n\t"
+        "ds_read_u8 %16, %23 offset:%24+128\n\t"
+        "ds_read_u8 %17, %23 offset:%24+192\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+          "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]),
+          "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15])
+        : "v"(ka[0]), "v"(ka[1]), "v"(vb[0]), "v"(vb[1]), "v"(vb[2]), "v"(vb[3]), "n"(OFF)
+        : "memory");
+  }
+  template <int OFF>
+  __device__ void read_rest(const uint32_t (&)[2], const uint32_t (&)[4]) {}
+};
+template <>
+struct CodeRegs<128> {
+  static constexpr int FIRST = 8;  // V blocks of read(); read_rest() has the others
+  u32x2 k[4];
+  uint32_t v[32];
+  template <int OFF>
+  __device__ void read(const uint32_t (&ka)[4], const uint32_t (&vb)[4]) {
+    asm volatile(
+        "ds_read_b64 %0, %36 offset:%44\n\t"
+        "ds_read_b64 %1, %37 offset:%44\n\t"
+        "ds_read_b64 %2, %38 offset:%44\n\t"
+        "ds_read_b64 %3, %39 offset:%44\n\t"
+        "ds_read_u8 %4, %40 offset:%44+0\n\t"
+        "ds_read_u8 %5, %40 offset:%44+128\n\t"
+        "ds_read_u8 %6, %40 offset:%44+272\n\t"
+        "ds_read_u8 %7, %40 offset:%44+400\n\t"
+        "ds_read_u8 %8, %40 offset:%44+16\n\t"
+        "ds_read_u8 %9, %40 offset:%44+144\n\t"
+        "ds_read_u8 %10, %40 offset:%44+256\n\t"
+        "ds_read_u8 %11, %40 offset:%44+384\n\t"
+        "ds_read_u8 %12, %41 offset:%44+0\n\t"
+        "ds_read_u8 %13, %41 offset:%44+128\n\t"
+        "ds_read_u8 %14, %41 offset:%44+272\n\t"
+        "ds_read_u8 %15, %41 offset:%44+400\n\t"
+        "ds_read_u8 %16, %41 offset:%44+16\n\t"
+        "ds_read_u8 %17, %41 offset:%44+144\n\t"
+        "ds_read_u8 %18, %41 offset:%44+256\n\t"
+        "ds_read_u8 %19, %41 offset:%44+384\n\t"
+        "ds_read_u8 %20, %42 offset:%44+0\n\t"
+        "ds_read_u8 %21, %42 offset:%44+128\n\t"
+        "ds_read_u8 %22, %42 offset:%44+272\n\t"
+        "ds_read_u8 %23, %42 offset:%44+400\n\t"
+        "ds_read_u8 %24, %42 offset:%44+16\n\t"
+        "ds_read_u8 %25, %42 offset:%44+144\n\t"
+        "ds_read_u8 %26, %42 offset:%44+256\n\t"
+        "ds_read_u8 %27, %42 offset:%44+384\n\t"
+        "ds_read_u8 %28, %43 offset:%44+0\n\t"
+        "ds_read_u8 %29, %43 offset:%44+128\n\t"
+        "ds_read_u8 %30, %43 offset:%44+272\n\t"
+        "ds_read_u8 %31, %43 offset:%44+400\n\t"
+        "ds_read_u8 %32, %43 offset:%44+16\n\t"
+        "ds_read_u8 %33, %43 offset:%44+144\n\t"
+        "ds_read_u8 %34, %43 offset:%44+256\n\t"
+        "ds_read_u8 %35, %43 offset:%44+384\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]),
+          "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]),
+          "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15]), "=&v"(v[16]), "=&v"(v[17]), "=&v"(v[18]),
+          "=&v"(v[19]), "=&v"(v[20]), "=&v"(v[21]), "=&v"(v[22]), "=&v"(v[23]), "=&v"(v[24]), "=&v"(v[25]),
+          "=&v"(v[26]), "=&v"(v[27]), "=&v"(v[28]), "=&v"(v[29]), "=&v"(v[30]), "=&v"(v[31])
+        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(vb[0]), "v"(vb[1]), "v"(vb[2]), "v"(vb[3]), "n"(OFF)
+        : "memory");
+  }
+  template <int OFF>
+  __device__ void read_rest(const uint32_t (&)[4], const uint32_t (&)[4]) {}
+};
+template <>
+struct CodeRegs<256> {
+  static constexpr int FIRST = 8;  // V blocks of read(); read_rest() has the others
+  u32x2 k[8];
+  uint32_t v[64];
+  template <int OFF>
+  __device__ void read(const uint32_t (&ka)[8], const uint32_t (&vb)[4]) {
+    asm volatile(
+        "ds_read_b64 %0, %40 offset:%52\n\t"
+        "ds_read_b64 %1, %41 offset:%52\n\t"
+        "ds_read_b64 %2, %42 offset:%52\n\t"
+        "ds_read_b64 %3, %43 offset:%52\n\t"
+        "ds_read_b64 %4, %44 offset:%52\n\t"
+        "ds_read_b64 %5, %45 offset:%52\n\t"
+        "ds_read_b64 %6, %46 offset:%52\n\t"
+        "ds_read_b64 %7, %47 offset:%52\n\t"
+        "ds_read_u8 %8, %48 offset:%52+0\n\t"
+        "ds_read_u8 %9, %48 offset:%52+320\n\t"
+        "ds_read_u8 %10, %48 offset:%52+640\n\t"
+        "ds_read_u8 %11, %48 offset:%52+960\n\t"
+        "ds_read_u8 %12, %49 offset:%52+0\n\t"
+        "ds_read_u8 %13, %49 offset:%52+320\n\t"
+        "ds_read_u8 %14, %49 offset:%52+640\n\t"
+        "ds_read_u8 %15, %49 offset:%52+960\n\t"
+        "ds_read_u8 %16, %50 offset:%52+0\n\t"
+        "ds_read_u8 %17, %50 offset:%52+320\n\t"
+        "ds_read_u8 %18, %50 offset:%52+640\n\t"
+        "ds_read_u8 %19, %50 offset:%52+960\n\t"
+        "ds_read_u8 %20, %51 offset:%52+0\n\t"
+        "ds_read_u8 %21, %51 offset:%52+320\n\t"
+        "ds_read_u8 %22, %51 offset:%52+640\n\t"
+        "ds_read_u8 %23, %51 offset:%52+960\n\t"
+        "ds_read_u8 %24, %48 offset:%52+64\n\t"
+        "ds_read_u8 %25, %48 offset:%52+256\n\t"
+        "ds_read_u8 %26, %48 offset:%52+704\n\t"
+        "ds_read_u8 %27, %48 offset:%52+896\n\t"
+        "ds_read_u8 %28, %49 offset:%52+64\n\t"
+        "ds_read_u8 %29, %49 offset:%52+256\n\t"
+        "ds_read_u8 %30, %49 offset:%52+704\n\t"
+        "ds_read_u8 %31, %49 offset:%52+896\n\t"
+        "ds_read_u8 %32, %50 offset:%52+64\n\t"
+        "ds_read_u8 %33, %50 offset:%52+256\n\t"
+        "ds_read_u8 %34, %50 offset:%52+704\n\t"
+        "ds_read_u8 %35, %50 offset:%52+896\n\t"
+        "ds_read_u8 %36, %51 offset:%52+64\n\t"
+        "ds_read_u8 %37, %51 offset:%52+256\n\t"
+        "ds_read_u8 %38, %51 offset:%52+704\n\t"
+        "ds_read_u8 %39, %51 offset:%52+896\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]), "=&v"(k[6]), "=&v"(k[7]),
+          "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
+          "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]),
+          "=&v"(v[15]), "=&v"(v[16]), "=&v"(v[17]), "=&v"(v[18]), "=&v"(v[19]), "=&v"(v[20]), "=&v"(v[21]),
+          "=&v"(v[22]), "=&v"(v[23]), "=&v"(v[24]), "=&v"(v[25]), "=&v"(v[26]), "=&v"(v[27]), "=&v"(v[28]),
+          "=&v"(v[29]), "=&v"(v[30]), "=&v"(v[31])
+        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(ka[4]), "v"(ka[5]), "v"(ka[6]), "v"(ka[7]),
+          "v"(vb[0]), "v"(vb[1]), "v"(vb[2]), "v"(vb[3]), "n"(OFF)
+        : "memory");
+  }
+  template <int OFF>
+  __device__ void read_rest(const uint32_t (&ka)[8], const uint32_t (&vb)[4]) {
+    asm volatile(
+        "ds_read_u8 %0, %32 offset:%36+128\n\t"
+        "ds_read_u8 %1, %32 offset:%36+448\n\t"
+        "ds_read_u8 %2, %32 offset:%36+512\n\t"
+        "ds_read_u8 %3, %32 offset:%36+832\n\t"
+        "ds_read_u8 %4, %33 offset:%36+128\n\t"
+        "ds_read_u8 %5, %33 offset:%36+448\n\t"
+        "ds_read_u8 %6, %33 offset:%36+512\n\t"
+        "ds_read_u8 %7, %33 offset:%36+832\n\t"
+        "ds_read_u8 %8, %34 offset:%36+128\n\t"
+        "ds_read_u8 %9, %34 offset:%36+448\n\t"
+        "ds_read_u8 %10, %34 offset:%36+512\n\t"
+        "ds_read_u8 %11, %34 offset:%36+832\n\t"
+        "ds_read_u8 %12, %35 offset:%36+128\n\t"
+        "ds_read_u8 %13, %35 offset:%36+448\n\t"
+        "ds_read_u8 %14, %35 offset:%36+512\n\t"
+        "ds_read_u8 %15, %35 offset:%36+832\n\t"
+        "ds_read_u8 %16, %32 offset:%36+192\n\t"
+        "ds_read_u8 %17, %32 offset:%36+384\n\t"
+        "ds_read_u8 %18, %32 offset:%36+576\n\t"
+        "ds_read_u8 %19, %32 offset:%36+768\n\t"
+        "ds_read_u8 %20, %33 offset:%36+192\n\t"
+        "ds_read_u8 %21, %33 offset:%36+384\n\t"
+        "ds_read_u8 %22, %33 offset:%36+576\n\t"
+        "ds_read_u8 %23, %33 offset:%36+768\n\t"
+        "ds_read_u8 %24, %34 offset:%36+192\n\t"
+        "ds_read_u8 %25, %34 offset:%36+384\n\t"
+        "ds_read_u8 %26, %34 offset:%36+576\n\t"
+        "ds_read_u8 %27, %34 offset:%36+768\n\t"
+        "ds_read_u8 %28, %35 offset:%36+192\n\t"
+        "ds_read_u8 %29, %35 offset:%36+384\n\t"
+        "ds_read_u8 %30, %35 offset:%36+576\n\t"
+        "ds_read_u8 %31, %35 offset:%36+768\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[32]), "=&v"(v[33]), "=&v"(v[34]), "=&v"(v[35]), "=&v"(v[36]), "=&v"(v[37]), "=&v"(v[38]),
+          "=&v"(v[39]), "=&v"(v[40]), "=&v"(v[41]), "=&v"(v[42]), "=&v"(v[43]), "=&v"(v[44]), "=&v"(v[45]),
+          "=&v"(v[46]), "=&v"(v[47]), "=&v"(v[48]), "=&v"(v[49]), "=&v"(v[50]), "=&v"(v[51]), "=&v"(v[52]),
+          "=&v"(v[53]), "=&v"(v[54]), "=&v"(v[55]), "=&v"(v[56]), "=&v"(v[57]), "=&v"(v[58]), "=&v"(v[59]),
+          "=&v"(v[60]), "=&v"(v[61]), "=&v"(v[62]), "=&v"(v[63])
+        : "v"(vb[0]), "v"(vb[1]), "v"(vb[2]), "v"(vb[3]), "n"(OFF)
+        : "memory");
+  }
+};
+
 // per-tile flags handed from the issuing side to the computing side
 constexpr int kFirst = 1 << 8;     // first tile of a piece
 constexpr int kLast = 1 << 9;      // last tile of a piece
@@ -300,9 +518,9 @@ constexpr int kComplete = 1 << 10; // the piece is the whole segment
 constexpr int kSecond = 1 << 11;   // partial goes to the wave's second slot
 
 template <int D, int HS, bool BF16, bool Q8>
-__global__ __launch_bounds__(64 * decode_wg_waves(D)) void decode_kernel(AttnParams p) {
+__global__ __launch_bounds__(64 * decode_wg_waves(D, Q8)) void decode_kernel(AttnParams p) {
   using E = Elem<BF16>;
-  constexpr int kDecodeWaves = decode_wg_waves(D);
+  constexpr int kDecodeWaves = decode_wg_waves(D, Q8);
   constexpr int ROW = 2 * D;                      // bytes of one key of one kv head (data type)
   constexpr int CPR = ROW / 16;                   // 16-byte chunks per row
   constexpr int ROWC = Q8 ? D : ROW;              // bytes of a cached row (INT8: codes)
@@ -325,8 +543,6 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D)) void decode_kernel(AttnPar
   static_assert(R >= 2, "ring");
 
   __shared__ __align__(1024) char ring[kDecodeWaves][R][SLOT];
-  // INT8 caches: the tile of the step, converted to the data type
-  __shared__ __align__(1024) char conv[kDecodeWaves][Q8 ? 2 * TB : 16];
   __shared__ __align__(16) int meta[kDecodeWaves][2][64];  // [0] next window, [1] next sequence
   // a piece's (token, first head, heads), handed over with its first tile
   __shared__ __align__(16) int piece[kDecodeWaves][R][4];
@@ -356,32 +572,38 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D)) void decode_kernel(AttnPar
 
   // ---- per-lane constant offsets ---------------------------------------------
   // tile loads: byte offset of lane's 16 bytes (key, logical chunk) for direct load j
-  // (INT8 caches: rows land unswizzled; the conversion places them)
+  // (INT8 caches: code rows, swizzled by swz8)
   uint32_t src_off[NK];
 #pragma unroll
   for (int j = 0; j < NK; ++j) {
     const int kj = j * KPI + lane / CPRC;
-    const int c = Q8 ? lane % CPRC : (lane % CPR) ^ swz<D>(kj);
+    const int c = Q8 ? (lane % CPRC) ^ swz8<D>(kj) : (lane % CPR) ^ swz<D>(kj);
     src_off[j] = Q8 ? static_cast<uint32_t>(kj * kv_row + 16 * c) : static_cast<uint32_t>(kj * kv_row + 8 * c) * 2u;
   }
   const int qchunk = (lane % CPR) * 8;
-  // MFMA operand addresses of ring slot 0 (slot s adds s * SLOT); with INT8
-  // caches the K/V operands come from the converted tile instead
+  // MFMA operand addresses of ring slot 0 (slot s adds s * SLOT); INT8
+  // caches: addresses of the code reads (CodeRegs) in ka and vb
   const int n = lane & 15, g = lane >> 4;
   const uint32_t ring0 = uniform(static_cast<int>(lds_addr(&ring[wave][0][0])));
-  const uint32_t conv0 = uniform(static_cast<int>(lds_addr(&conv[wave][0])));
-  const uint32_t tile0 = Q8 ? conv0 : ring0;
-  uint32_t ka[KS], va[DB], qa[KS];
+  uint32_t ka[KS], va[Q8 ? 1 : DB], vb[4], qa[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    ka[s] = tile0 + n * ROW + 16 * ((4 * s + g) ^ swz<D>(n));
+    ka[s] = Q8 ? ring0 + n * D + 16 * ((2 * s + (g >> 1)) ^ swz8<D>(n)) + 8 * (g & 1)
+               : ring0 + n * ROW + 16 * ((4 * s + g) ^ swz<D>(n));
     qa[s] = ring0 + 2 * TBC + (n < QB / ROW ? n : 0) * ROW + 16 * (4 * s + g);
   }
-  {
+  if constexpr (Q8) {
+    // byte j of block blk (key 4g+j, d = 16 blk + n) is at vb[i] + a constant
+    // (CodeRegs): D = 64: i = blk; 128: i = blk / 2; 256: i = blk % 4
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      vb[i] = ring0 + TBC + n + (D == 64 ? 256 * g + 16 * (i ^ g) : D == 128 ? 512 * g + 32 * (i ^ g)
+                                                                              : 1024 * g + 16 * (i ^ g));
+  } else {
     const int kv = 4 * g + (n >> 2), cc = n & 3;
 #pragma unroll
     for (int blk = 0; blk < DB; ++blk)
-      va[blk] = tile0 + TB + kv * ROW + 16 * ((2 * blk + (cc >> 1)) ^ swz<D>(kv)) + 8 * (cc & 1);
+      va[blk] = ring0 + TB + kv * ROW + 16 * ((2 * blk + (cc >> 1)) ^ swz<D>(kv)) + 8 * (cc & 1);
   }
   const uint32_t meta_w = lds_addr(&meta[wave][0][0]);
   const uint32_t piece0 = uniform(static_cast<int>(lds_addr(&piece[wave][0][0])));
@@ -619,42 +841,36 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D)) void decode_kernel(AttnPar
       m = kNegInf;
       l = 0.f;
     }
-    if constexpr (Q8) {
-      // codes of the tile -> data type, into the wave's converted tile in the
-      // layout a direct load of data-type rows would have produced: cached
-      // chunk c (16 codes) of key k becomes chunks 2c and 2c+1 of row k,
-      // swizzled.  Same wave, LDS in order: no wait before the reads below.
-      constexpr int NCH = 2 * D / 64;  // 16-byte chunks per lane (K then V)
-      u32x4 raw[NCH];
-      if constexpr (NCH == 8) {
-        u32x4 a[4], b[4];
-        lds_readn_b128<4, 1024>(a, ring0 + S * SLOT + 16 * lane);
-        lds_readn_b128<4, 1024>(b, ring0 + S * SLOT + 4096 + 16 * lane);
+    // the tile's operands: K fragments (KS) and V^T fragments (DB)
+    typename E::x8 kx[KS];
+    typename E::x4 vx[DB];
+    if constexpr (Q8) {  // codes -> data type in registers (exact)
+      CodeRegs<D> cr;
+      auto v_block = [&](int blk) __attribute__((always_inline)) {
+        const typename E::x2 a = E::from_code_halves(cr.v[4 * blk] | (cr.v[4 * blk + 1] << 16));
+        const typename E::x2 b = E::from_code_halves(cr.v[4 * blk + 2] | (cr.v[4 * blk + 3] << 16));
+        vx[blk] = typename E::x4{a[0], a[1], b[0], b[1]};
+      };
+      cr.template read<S * SLOT>(ka, vb);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) raw[k] = a[k], raw[4 + k] = b[k];
-      } else {
-        lds_readn_b128<NCH, 1024>(raw, ring0 + S * SLOT + 16 * lane);
-      }
+      for (int s = 0; s < KS; ++s) kx[s] = E::from_codes(cr.k[s].x, cr.k[s].y);
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        const int tensor = i / (NCH / 2);
-        const int j = 64 * (i % (NCH / 2)) + lane;  // chunk within the tensor
-        const int k = j / CPRC, c = j % CPRC;
-        const typename E::x8 lo = E::from_codes(raw[i][0], raw[i][1]);
-        const typename E::x8 hi = E::from_codes(raw[i][2], raw[i][3]);
-        const uint32_t row = conv0 + tensor * TB + k * ROW;
-        lds_write_b128(row + 16 * ((2 * c) ^ swz<D>(k)), __builtin_bit_cast(u32x4, lo));
-        lds_write_b128(row + 16 * ((2 * c + 1) ^ swz<D>(k)), __builtin_bit_cast(u32x4, hi));
-      }
+      for (int blk = 0; blk < CodeRegs<D>::FIRST; ++blk) v_block(blk);
+      cr.template read_rest<S * SLOT>(ka, vb);
+#pragma unroll
+      for (int blk = CodeRegs<D>::FIRST; blk < DB; ++blk) v_block(blk);
+    } else {
+      TileRegs<D> tr;
+      tr.template read<S * SLOT>(ka, va);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kx[s] = __builtin_bit_cast(typename E::x8, tr.k[s]);
+#pragma unroll
+      for (int blk = 0; blk < DB; ++blk) vx[blk] = __builtin_bit_cast(typename E::x4, tr.v[blk]);
     }
-    TileRegs<D> tr;
-    tr.template read<Q8 ? 0 : S * SLOT>(ka, va);
     // S^T: lane = head n + 16 * key group g, element e = key 4 g + e
     f32x4_t st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      st = E::mfma_16x16x32(__builtin_bit_cast(typename E::x8, tr.k[s]), __builtin_bit_cast(typename E::x8, qv[s]),
-                            st);
+    for (int s = 0; s < KS; ++s) st = E::mfma_16x16x32(kx[s], __builtin_bit_cast(typename E::x8, qv[s]), st);
     float sc[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) sc[e] = st[e] * p.scale_log2;
@@ -679,20 +895,22 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D)) void decode_kernel(AttnPar
     // row sum of exactly the rounded weights the MFMA multiplies
     l = E::sum2(typename E::x2{pb[0], pb[1]}, l);
     l = E::sum2(typename E::x2{pb[2], pb[3]}, l);
-    if (nvalid < kDecodeTile) {
-      // keys past the history may hold any bits (NaN included): zero their values
+    if (!Q8 && nvalid < kDecodeTile) {
+      // keys past the history may hold any bits (NaN included): zero their
+      // values (codes are always finite, and their weights are 0)
       const int k0 = 4 * g;
       const uint32_t lo = (k0 < nvalid ? 0xffffu : 0u) | (k0 + 1 < nvalid ? 0xffff0000u : 0u);
       const uint32_t hi = (k0 + 2 < nvalid ? 0xffffu : 0u) | (k0 + 3 < nvalid ? 0xffff0000u : 0u);
 #pragma unroll
       for (int blk = 0; blk < DB; ++blk) {
-        tr.v[blk].x &= lo;
-        tr.v[blk].y &= hi;
+        u32x2 w = __builtin_bit_cast(u32x2, vx[blk]);
+        w.x &= lo;
+        w.y &= hi;
+        vx[blk] = __builtin_bit_cast(typename E::x4, w);
       }
     }
 #pragma unroll
-    for (int blk = 0; blk < DB; ++blk)
-      acc[blk] = E::mfma_16x16x16(__builtin_bit_cast(typename E::x4, tr.v[blk]), pb, acc[blk]);
+    for (int blk = 0; blk < DB; ++blk) acc[blk] = E::mfma_16x16x16(vx[blk], pb, acc[blk]);
     if (fl & kLast) {  // last tile of the piece: normalise and write
       const float lt = swap32(swap16(l, false), false);
       const float inv = 1.f / lt;
@@ -750,7 +968,7 @@ hipError_t launch_decode(const AttnParams& p, int head_size, int head_slots, boo
   const dim3 g(grid);
 #define PA_DECODE(DD, HH)                                                                        \
   if (head_size == DD && head_slots == HH) {                                                     \
-    const dim3 b(64 * decode_wg_waves(DD));                                                      \
+    const dim3 b(64 * decode_wg_waves(DD, q8));                                                  \
     if (bf16 && q8) hipLaunchKernelGGL((decode_kernel<DD, HH, true, true>), g, b, 0, s, p);       \
     else if (bf16) hipLaunchKernelGGL((decode_kernel<DD, HH, true, false>), g, b, 0, s, p);       \
     else if (q8) hipLaunchKernelGGL((decode_kernel<DD, HH, false, true>), g, b, 0, s, p);         \

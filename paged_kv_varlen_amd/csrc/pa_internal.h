@@ -27,8 +27,13 @@ namespace pa {
 
 // ---- tiling constants -----------------------------------------------------
 // waves per decode workgroup: 4, or 2 at head_size 256 (so that a ring of
-// three or four 16-key tiles per wave still fits in LDS)
-__host__ __device__ constexpr int decode_wg_waves(int D) { return D > 128 ? 2 : 4; }
+// three or four 16-key tiles per wave still fits in LDS).  INT8 caches (q8)
+// halve the tile bytes and add the code conversion to every tile, so twice
+// the waves share the LDS (two per SIMD below head_size 256) with rings of
+// two to four tiles: one wave converts while the other waits on its loads.
+__host__ __device__ constexpr int decode_wg_waves(int D, bool q8 = false) {
+  return q8 ? (D > 128 ? 4 : 8) : (D > 128 ? 2 : 4);
+}
 constexpr int kDecodeTile = 16;       // keys per decode tile
 constexpr int kDecodeUnitHeads = 16;  // query heads of one decode segment (MFMA N)
 constexpr int kDecodeWindow = 64;     // block-table entries a wave holds (one per lane)
@@ -78,22 +83,17 @@ __host__ __device__ constexpr int decode_slot_bytes(int D, int hslots, bool q8 =
   return q8 ? 2 * kDecodeTile * D + decode_q_bytes(D, hslots) + decode_scale_bytes(D)
             : 2 * kDecodeTile * 2 * D + decode_q_bytes(D, hslots);
 }
-// q8: per wave, the K and V tiles converted to the data type for the MFMA
-__host__ __device__ constexpr int decode_conv_bytes(int D, bool q8) { return q8 ? 2 * kDecodeTile * 2 * D : 0; }
 // ring depth: as many slots as fit the workgroup's waves in about 150 KB, at
 // most 4
 __host__ __device__ constexpr int decode_ring(int D, int hslots, bool q8 = false) {
-  return (150 * 1024 - decode_wg_waves(D) * decode_conv_bytes(D, q8)) /
-                     (decode_wg_waves(D) * decode_slot_bytes(D, hslots, q8)) > 4
+  return (150 * 1024) / (decode_wg_waves(D, q8) * decode_slot_bytes(D, hslots, q8)) > 4
              ? 4
-             : (150 * 1024 - decode_wg_waves(D) * decode_conv_bytes(D, q8)) /
-                   (decode_wg_waves(D) * decode_slot_bytes(D, hslots, q8));
+             : (150 * 1024) / (decode_wg_waves(D, q8) * decode_slot_bytes(D, hslots, q8));
 }
 // per wave: the ring, a 16-byte piece record per slot, 512 bytes of
-// prefetched metadata (and the converted tiles)
+// prefetched metadata
 __host__ __device__ constexpr int decode_lds_bytes(int D, int hslots, bool q8 = false) {
-  return decode_wg_waves(D) *
-         (decode_ring(D, hslots, q8) * (decode_slot_bytes(D, hslots, q8) + 16) + 512 + decode_conv_bytes(D, q8));
+  return decode_wg_waves(D, q8) * (decode_ring(D, hslots, q8) * (decode_slot_bytes(D, hslots, q8) + 16) + 512);
 }
 __host__ __device__ constexpr int decode_wg_per_cu(int D, int hslots, bool q8 = false) {
   return (160 * 1024) / decode_lds_bytes(D, hslots, q8) > 0 ? (160 * 1024) / decode_lds_bytes(D, hslots, q8) : 1;

@@ -428,8 +428,10 @@ def work(batch: Batch) -> dict:
 
     flops  = 4*D*H * sum_b sum_{i<q_b} (past_b + i + 1)   (QK^T and PV over
              causally visible pairs, 2 flop per multiply-add)
-    kv_hist = sum_b L_b * 2 * Hkv * D * 2 bytes (logical history read)
-    plus query, output, the step's K/V and the cache writes.
+    kv_hist = sum_b L_b * 2 * Hkv * D * e bytes (logical history read; e = 2
+             for 16-bit caches, 1 for INT8 codes)
+    plus query, output, the step's K/V, the cache writes and (INT8) the two
+    scale tables.
     """
     H, Hkv, D = batch.num_heads, batch.kv_num_heads, batch.head_size
     q = batch.q_lens
@@ -437,7 +439,8 @@ def work(batch: Batch) -> dict:
     L = p + q
     pairs = int(np.sum(q * p + q * (q + 1) // 2))
     dec = q == 1
-    row = 2 * Hkv * D * 2
+    int8 = batch.kv_quant == "int8"
+    row = 2 * Hkv * D * (1 if int8 else 2)  # one slot of both caches
     n_write = int(batch.num_tokens if batch.slot_mapping is None
                   else np.count_nonzero(batch.slot_mapping >= 0))
     out = {
@@ -447,13 +450,14 @@ def work(batch: Batch) -> dict:
         "prefill_flops": 4 * D * H * int(np.sum((q * p + q * (q + 1) // 2)[~dec])),
         "q_bytes": batch.num_tokens * H * D * 2,
         "o_bytes": batch.num_tokens * H * D * 2,
-        "step_kv_bytes": batch.num_tokens * row,
+        "step_kv_bytes": batch.num_tokens * 2 * Hkv * D * 2,
         "cache_write_bytes": n_write * row,
+        "scale_bytes": 2 * Hkv * D * 4 if int8 else 0,
         "tokens": batch.num_tokens,
         "kv_tokens": int(L.sum()),
     }
     out["bytes"] = (out["kv_hist_bytes"] + out["q_bytes"] + out["o_bytes"]
-                    + out["step_kv_bytes"] + out["cache_write_bytes"])
+                    + out["step_kv_bytes"] + out["cache_write_bytes"] + out["scale_bytes"])
     if batch.name == "serving":
         # unique pages actually referenced (shared prefix pages count once)
         used = set()

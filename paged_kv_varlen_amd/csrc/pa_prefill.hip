@@ -187,6 +187,10 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
   constexpr int kChunk = S::CHUNK;
   static_assert(S::LOADS >= 1 && S::LOADS * 64 * S::LB == S::WAVE_ROWS * S::ROWC, "loads per wave");
   constexpr int ES = Q8 ? 1 : 2;  // bytes per cached element
+  // INT8 with two kv groups: two stages (step parity); step j converts the
+  // codes of step j + 1 while the products of step j run
+  constexpr bool kAhead = Q8 && S::KVG == 2;
+  static_assert(!kAhead || S::STAGE >= 4 * S::BUF, "two stages");
 
   // one LDS object per ring buffer and tensor: the compiler can then see that
   // a fill of one buffer never aliases reads of another and does not make
@@ -204,9 +208,10 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
   __shared__ int lds_item;
   auto kbuf = [&](int b) -> char* { return b == 0 ? k_lds0 : b == 1 ? k_lds1 : b == 2 ? k_lds2 : k_lds3; };
   auto vbuf = [&](int b) -> char* { return b == 0 ? v_lds0 : b == 1 ? v_lds1 : b == 2 ? v_lds2 : v_lds3; };
-  // the K and V rows the products read (data type, swizzled)
-  auto kread = [&](int b) -> char* { return Q8 ? stage : kbuf(b); };
-  auto vread = [&](int b) -> char* { return Q8 ? stage + S::BUF : vbuf(b); };
+  // the K and V rows the products of ring buffer b's step read (data type,
+  // swizzled); with two stages, a step's parity is that of its ring buffer
+  auto kread = [&](int b) -> char* { return Q8 ? stage + (kAhead ? (b & 1) * 2 * S::BUF : 0) : kbuf(b); };
+  auto vread = [&](int b) -> char* { return Q8 ? kread(b) + S::BUF : vbuf(b); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -524,6 +529,7 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
     // INT8: the codes of the step in ring buffer buf -> data-type rows of the
     // stage, in the layout the products read: cached chunk c (16 codes) of
     // row r becomes chunks 2c and 2c+1 of row r, swizzled
+    // (into the stage that the products of ring buffer buf's step read)
     auto convert = [&](auto buf_tag) __attribute__((always_inline)) {
       constexpr int buf = decltype(buf_tag)::value;
       constexpr int NC = kPrefillKeys * D / 16;  // 16-code chunks per tensor
@@ -533,7 +539,7 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
         const uint4 raw = *reinterpret_cast<const uint4*>((is_v ? vbuf(buf) : kbuf(buf)) + 16 * cc);
         const x8 lo = E::from_codes(raw.x, raw.y), hi = E::from_codes(raw.z, raw.w);
         const int swz = is_v ? S::v_swz(r) : S::k_swz(r);
-        char* row = stage + (is_v ? S::BUF : 0) + r * ROWB;
+        char* row = (is_v ? vread(buf) : kread(buf)) + r * ROWB;
         *reinterpret_cast<x8*>(row + (((2 * k) ^ swz) << 4)) = lo;
         *reinterpret_cast<x8*>(row + (((2 * k + 1) ^ swz) << 4)) = hi;
       };
@@ -571,7 +577,11 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
       if constexpr (kRing == 2) {
         if (more) issue(std::integral_constant<int, nbuf>{}, s_next, slot16, 0, S::LOADS);
       }
-      if constexpr (Q8) {
+      if constexpr (kAhead) {
+        // the next step's codes (landed before the barrier that ended the
+        // previous step) into the other stage, whose readers finished there
+        if (jstep + 1 < nsteps) convert(std::integral_constant<int, (buf + 1) % kRing>{});
+      } else if constexpr (Q8) {
         // the stage's last readers finished at the barrier that ended the
         // previous step; the codes of this step landed before it
         convert(buf_tag);
@@ -592,7 +602,9 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
         // a plain barrier: __syncthreads() would also wait for the fills
         // still in flight.  The waits go through the builtin so that the
         // compiler knows which fills have landed and adds no wait of its own.
-        if (more) wait_fills<4 * S::LOADS>();
+        // (Converting one step ahead: step j + 2 must have landed, only
+        // step j + 3 stays in flight; the wait also covers the stage writes.)
+        if (more) wait_fills<(kAhead ? 2 : 4) * S::LOADS>();
         else wait_fills<0>();
       }
       plain_barrier();
@@ -607,12 +619,17 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
     } else if (nsteps > 2) {
       issue(std::integral_constant<int, 1>{}, 1, slot_of(1), 0, S::LOADS);
       issue(std::integral_constant<int, 2 % kRing>{}, 2, slot_of(2), 0, S::LOADS);
-      wait_fills<4 * S::LOADS>();
+      wait_fills<(kAhead ? 2 : 4) * S::LOADS>();  // step 0 (converting ahead: and 1) landed
     } else {
       if (nsteps > 1) issue(std::integral_constant<int, 1>{}, 1, slot_of(1), 0, S::LOADS);
       wait_fills<0>();
     }
     plain_barrier();
+    if constexpr (kAhead) {  // step 0's rows, before its products
+      convert(std::integral_constant<int, 0>{});
+      wait_lds();
+      plain_barrier();
+    }
     // Steps in chunks of kChunk: the slot window holds the chunk's steps and
     // the three fetched ahead of it, and is refilled between chunks (the
     // fills already in flight read the previous window).  Within a chunk,

@@ -55,30 +55,54 @@ __device__ inline void merge_segment(const AttnParams& p, int task, int T, int l
   const float* lse_base = p.part_lse + hn;
   const float* o_base = p.part_o + hn * D + E * qd;
   // Pieces are combined in wave order with weights 2^(lse - M), M the
-  // largest lse: a pass for M, then one for the weighted sum.
+  // largest lse: a pass for M, then one for the weighted sum.  Each pass
+  // loads a batch of pieces before it uses any (a batch is one memory round
+  // trip, not one per piece); the sums still run in wave order.
+  constexpr int kLseBatch = 8, kOBatch = 2;
   float M = -__builtin_huge_valf();
-  for (int v = wf; v <= wl; ++v)
-    if (holds(v)) M = fmaxf(M, lse_base[slot_of_piece(v) * kDecodeUnitHeads]);
+  for (int v0 = wf; v0 <= wl; v0 += kLseBatch) {
+    float x[kLseBatch];
+#pragma unroll
+    for (int j = 0; j < kLseBatch; ++j) {  // (loads at a valid piece, then a select)
+      const float l = lse_base[slot_of_piece(min(v0 + j, wl)) * kDecodeUnitHeads];
+      x[j] = v0 + j <= wl && holds(v0 + j) ? l : -__builtin_huge_valf();
+    }
+#pragma unroll
+    for (int j = 0; j < kLseBatch; ++j) M = fmaxf(M, x[j]);
+  }
   float o[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) o[e] = 0.f;
   float wsum = 0.f;
-  for (int v = wf; v <= wl; ++v) {
-    if (!holds(v)) continue;
-    const int ps = slot_of_piece(v);
-    const float wk = __builtin_amdgcn_exp2f(lse_base[ps * kDecodeUnitHeads] - M);
-    const float4* po = reinterpret_cast<const float4*>(o_base + ps * (kDecodeUnitHeads * D));
-    float4 x[E / 4];
+  for (int v0 = wf; v0 <= wl; v0 += kOBatch) {
+    float lv[kOBatch];
+    float4 x[kOBatch][E / 4];
 #pragma unroll
-    for (int e = 0; e < E / 4; ++e) x[e] = po[e];
+    for (int j = 0; j < kOBatch; ++j) {
+      const int v = v0 + j;
+      const bool have = v <= wl && holds(v);
+      const int ps = slot_of_piece(min(v, wl));  // (loads at a valid piece, then a select)
+      const float l = lse_base[ps * kDecodeUnitHeads];
+      lv[j] = have ? l : -__builtin_huge_valf();
+      const float4* po = reinterpret_cast<const float4*>(o_base + ps * (kDecodeUnitHeads * D));
 #pragma unroll
-    for (int e = 0; e < E / 4; ++e) {
-      o[4 * e] = fmaf(wk, x[e].x, o[4 * e]);
-      o[4 * e + 1] = fmaf(wk, x[e].y, o[4 * e + 1]);
-      o[4 * e + 2] = fmaf(wk, x[e].z, o[4 * e + 2]);
-      o[4 * e + 3] = fmaf(wk, x[e].w, o[4 * e + 3]);
+      for (int e = 0; e < E / 4; ++e) {
+        const float4 t = po[e];
+        x[j][e] = have ? t : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
-    wsum += wk;
+#pragma unroll
+    for (int j = 0; j < kOBatch; ++j) {
+      const float wk = __builtin_amdgcn_exp2f(lv[j] - M);  // 0 for a missing piece
+#pragma unroll
+      for (int e = 0; e < E / 4; ++e) {
+        o[4 * e] = fmaf(wk, x[j][e].x, o[4 * e]);
+        o[4 * e + 1] = fmaf(wk, x[j][e].y, o[4 * e + 1]);
+        o[4 * e + 2] = fmaf(wk, x[j][e].z, o[4 * e + 2]);
+        o[4 * e + 3] = fmaf(wk, x[j][e].w, o[4 * e + 3]);
+      }
+      wsum += wk;
+    }
   }
   const float inv = 1.f / wsum;
   const int h = kvh * p.group + kDecodeUnitHeads * hc + hn;

@@ -82,7 +82,7 @@ def variant_suffix(dtype="f16", head_size=0, kv_quant="none") -> str:
     """Names a workload variant in profile file names ('' for the workloads as
     defined: fp16 data and caches, their own head size)."""
     return ("" if dtype == "f16" else f"_{dtype}") + (f"_hd{head_size}" if head_size else "") + \
-        ("_int8" if kv_quant == "int8" else "")
+        ("" if kv_quant == "none" else f"_{kv_quant}")
 
 
 VARIANT = {"suffix": ""}  # set by main() from --dtype / --head-size / --kv-quant
@@ -329,9 +329,10 @@ def main():
                     help="data type of the workloads (the line's dtype field)")
     ap.add_argument("--head-size", type=int, default=0, choices=(0, 64, 128, 256),
                     help="replace the workloads' head size (0: their own)")
-    ap.add_argument("--kv-quant", default="none", choices=("none", "int8"),
-                    help="cache element type: the data type, or int8 codes with per-channel "
-                         "scales (history bytes then count one byte per element)")
+    ap.add_argument("--kv-quant", default="none", choices=("none", "int8", "int4"),
+                    help="cache element type: the data type, or int8 / int4 codes with "
+                         "per-channel scales (history bytes then count one byte / half a byte "
+                         "per element)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -417,7 +418,7 @@ def main():
                    "num_tokens": b.num_tokens, "num_heads": b.num_heads,
                    "kv_num_heads": b.kv_num_heads, "head_size": b.head_size,
                    "block_size": b.block_size, "num_blocks": b.num_blocks,
-                   "kv_cache": "int8" if args.kv_quant == "int8" else args.dtype,
+                   "kv_cache": args.dtype if args.kv_quant == "none" else args.kv_quant,
                    "kv_hist_bytes": work["kv_hist_bytes"], "wall_ms_per_step": round(wall_ms, 5)},
         "roofline": roofline(args.workload, work, kms),
         "tokens_per_s": head["tokens_per_s"],

@@ -85,8 +85,12 @@ typedef enum pa_dtype {
  *  PA_KV_SAME  the caches hold T, like query/key/value;
  *  PA_KV_INT8  the caches hold int8 codes.  A step row x is stored as
  *              clamp(rint(x / s), -127, 127), the quotient taken in fp32 and
- *              rounded half to even; a cached code c reads as c * s. */
-typedef enum pa_kv_quant { PA_KV_SAME = 0, PA_KV_INT8 = 1 } pa_kv_quant;
+ *              rounded half to even; a cached code c reads as c * s;
+ *  PA_KV_INT4  the caches hold 4-bit codes clamp(rint(x / s), -7, 7) (same
+ *              rounding), two per byte: element 2i in bits 0-3, element 2i+1
+ *              in bits 4-7, each a 4-bit two's complement number; a cached
+ *              code c (-8..7) reads as c * s. */
+typedef enum pa_kv_quant { PA_KV_SAME = 0, PA_KV_INT8 = 1, PA_KV_INT4 = 2 } pa_kv_quant;
 
 /*
  * Arguments of one call.  Tensor layouts are dense row-major.
@@ -98,7 +102,9 @@ typedef enum pa_kv_quant { PA_KV_SAME = 0, PA_KV_INT8 = 1 } pa_kv_quant;
  *               (README, Inputs: key, value)
  *  key_cache,
  *  value_cache  T [num_blocks, block_size, cache_kv_heads, cache_head_size]
- *               (int8 with kv_quant PA_KV_INT8), read and written in place;
+ *               (int8 with kv_quant PA_KV_INT8; with PA_KV_INT4 bytes
+ *               [.., .., cache_kv_heads, head_size / 2], and cache_head_size
+ *               is that byte width), read and written in place;
  *               the two are always updated together.  (README, Inputs:
  *               key_cache, value_cache; Outputs)
  *  cumulative_sequence_length
@@ -148,7 +154,8 @@ typedef struct pa_args {
   int32_t num_blocks;            /* cache dim 0                            */
   int32_t block_size;            /* cache dim 1                            */
   int32_t cache_kv_heads;        /* cache dim 2, must equal kv_num_heads   */
-  int32_t cache_head_size;       /* cache dim 3, must equal head_size      */
+  int32_t cache_head_size;       /* cache dim 3: head_size (PA_KV_INT4:
+                                    head_size / 2, the bytes of a row)    */
   int32_t max_blocks_per_seq;    /* block_table dim 1                      */
   float scale;                   /* 0 => 1/sqrt(head_size) (README, Attributes) */
   int32_t is_causal;             /* must be 1 (README, Attributes)         */
@@ -177,9 +184,10 @@ typedef struct pa_args {
   float *lse;
   float *output_f32;
 
-  /* Cache element type (pa_kv_quant).  With PA_KV_INT8, k_scale and v_scale
-   * are float [kv_num_heads, head_size] (16-byte aligned), the per-channel
-   * scales of the two caches; otherwise they are ignored. */
+  /* Cache element type (pa_kv_quant).  With PA_KV_INT8 or PA_KV_INT4,
+   * k_scale and v_scale are float [kv_num_heads, head_size] (16-byte
+   * aligned), the per-channel scales of the two caches; otherwise they are
+   * ignored. */
   int32_t kv_quant;
   int32_t reserved;              /* 0                                      */
   const float *k_scale;

@@ -32,5 +32,8 @@ from .paged_attention import (  # noqa: F401
     resolve_call,
     values,
     quantize_int8,
+    quantize_int4,
+    pack_int4,
+    unpack_int4,
     dequantize,
 )

@@ -64,6 +64,31 @@ def quantize_int8(x: np.ndarray, s: np.ndarray) -> np.ndarray:
     return np.clip(np.rint(q), -127, 127).astype(np.int8)
 
 
+def quantize_int4(x: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """INT4 code of each element: the INT8 reading with the symmetric 4-bit
+    range, clamp(rint(x / s), -7, 7), the quotient in fp32, ties to even."""
+    q = values(x).astype(np.float32) / np.asarray(s, dtype=np.float32)
+    return np.clip(np.rint(q), -7, 7).astype(np.int8)
+
+
+def pack_int4(codes: np.ndarray) -> np.ndarray:
+    """Codes [..., D] (D even) as bytes [..., D/2]: element 2i in bits 0-3 and
+    element 2i+1 in bits 4-7, each as a 4-bit two's complement number (the
+    plainest packing of two per-channel codes into a byte, low channel
+    first)."""
+    c = np.asarray(codes).astype(np.int16) & 0xF
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_int4(b: np.ndarray) -> np.ndarray:
+    """Inverse of pack_int4: bytes [..., D/2] -> int8 codes [..., D] in [-8, 7]."""
+    w = np.asarray(b, dtype=np.uint8).astype(np.int16)
+    out = np.empty(w.shape[:-1] + (2 * w.shape[-1],), dtype=np.int8)
+    out[..., 0::2] = ((w & 0xF) ^ 8) - 8
+    out[..., 1::2] = ((w >> 4) ^ 8) - 8
+    return out
+
+
 def dequantize(codes: np.ndarray, s: np.ndarray) -> np.ndarray:
     """Exact fp64 value code * s of every cached element (s broadcasts over
     the trailing [Hkv, D])."""
@@ -112,14 +137,24 @@ def scatter_kv(key_cache: np.ndarray, value_cache: np.ndarray, K: np.ndarray, V:
     block_id*block_size + offset; -1 suppresses the write; without
     slot_mapping the slot follows from past_seqlens (token i of sequence b is
     at position past_b + i, found through block_table).  The copy is bit
-    exact: the stored bits are the input's bits.  With INT8 caches (scales
-    given) each row is stored as its codes (quantize_int8).
+    exact: the stored bits are the input's bits.  With quantized caches
+    (scales given) each row is stored as its codes: int8 caches hold INT8
+    codes (quantize_int8), uint8 caches two INT4 codes per byte
+    (quantize_int4, pack_int4).
     """
     kc = key_cache.copy()
     vc = value_cache.copy()
-    NB, bs, Hkv, D = kc.shape
-    kslots = kc.reshape(NB * bs, Hkv, D)
-    vslots = vc.reshape(NB * bs, Hkv, D)
+    NB, bs, Hkv, Dc = kc.shape
+    kslots = kc.reshape(NB * bs, Hkv, Dc)
+    vslots = vc.reshape(NB * bs, Hkv, Dc)
+
+    def stored(row, sc):
+        if sc is None:
+            return row
+        if kc.dtype == np.uint8:
+            return pack_int4(quantize_int4(row, sc))
+        return quantize_int8(row, sc)
+
     for b in range(past.shape[0]):
         for i in range(int(cum[b + 1]) - int(cum[b])):
             t = int(cum[b]) + i
@@ -129,8 +164,8 @@ def scatter_kv(key_cache: np.ndarray, value_cache: np.ndarray, K: np.ndarray, V:
                 pos = int(past[b]) + i
                 slot = int(block_table[b, pos // bs]) * bs + pos % bs
             if slot >= 0:
-                kslots[slot] = K[t] if k_scale is None else quantize_int8(K[t], k_scale)
-                vslots[slot] = V[t] if v_scale is None else quantize_int8(V[t], v_scale)
+                kslots[slot] = stored(K[t], k_scale)
+                vslots[slot] = stored(V[t], v_scale)
     return kc, vc
 
 
@@ -139,13 +174,15 @@ def gather_history(kc: np.ndarray, vc: np.ndarray, block_table: np.ndarray, b: i
     """Contiguous fp64 copies [length, Hkv, D] of sequence b's positions
     0..length-1, each read at slot block_table[b, j // bs]*bs + j % bs
     (README, Inputs: block_table maps a sequence's logical blocks to
-    physical blocks and defines the read path).  INT8 caches read as
-    code * scale."""
-    NB, bs, Hkv, D = kc.shape
+    physical blocks and defines the read path).  Quantized caches read as
+    code * scale (uint8 caches: two INT4 codes per byte, unpack_int4)."""
+    NB, bs, Hkv, Dc = kc.shape
     j = np.arange(int(length), dtype=np.int64)
     idx = block_table[b, j // bs].astype(np.int64) * bs + j % bs
-    kr = kc.reshape(NB * bs, Hkv, D)[idx]
-    vr = vc.reshape(NB * bs, Hkv, D)[idx]
+    kr = kc.reshape(NB * bs, Hkv, Dc)[idx]
+    vr = vc.reshape(NB * bs, Hkv, Dc)[idx]
+    if kc.dtype == np.uint8 and k_scale is not None:
+        kr, vr = unpack_int4(kr), unpack_int4(vr)
     Kb = values(kr) if k_scale is None else dequantize(kr, k_scale)
     Vb = values(vr) if v_scale is None else dequantize(vr, v_scale)
     return Kb, Vb
@@ -198,8 +235,9 @@ def paged_attention(query, key, value, key_cache, value_cache, cum, past, block_
     that full-size workloads can be checked on a sample.  ``with_lse``: also
     return the attention-domain lse [N, H] of every row (see attend_sequence)
     as a fourth value.  ``k_scale``/``v_scale`` ([Hkv, D] fp32, both or
-    neither): the caches hold INT8 codes; the step's rows are quantized on
-    write and every cached element reads as code * scale.
+    neither): the caches hold codes, INT8 (int8 caches) or INT4 (uint8
+    caches, [NB, bs, Hkv, D/2], two codes per byte); the step's rows are
+    quantized on write and every cached element reads as code * scale.
     """
     if (k_scale is None) != (v_scale is None):
         raise ValueError("k_scale and v_scale go together")

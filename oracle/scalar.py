@@ -40,6 +40,18 @@ def _code(x: float, s: float) -> int:
     return max(-127, min(127, round(_f32(x / s))))
 
 
+def _code4(x: float, s: float) -> int:
+    """INT4 code clamp(round(x / s), -7, 7), the quotient rounded as in _code."""
+    return max(-7, min(7, round(_f32(x / s))))
+
+
+def _nibbles(byte: int):
+    """The two INT4 codes of a cache byte: bits 0-3 (the even element), then
+    bits 4-7, each a 4-bit two's complement number."""
+    lo, hi = byte & 15, (byte >> 4) & 15
+    return [lo - 16 if lo >= 8 else lo, hi - 16 if hi >= 8 else hi]
+
+
 def paged_attention_scalar(query, key, value, key_cache, value_cache, cum, past,
                            block_table, slot_mapping, num_heads, kv_num_heads, scale,
                            with_lse=False, k_scale=None, v_scale=None):
@@ -47,8 +59,9 @@ def paged_attention_scalar(query, key, value, key_cache, value_cache, cum, past,
     slots written), and with ``with_lse`` also lse as nested lists [N][H]
     (log of the fsum of exp(score) over the visible keys, natural log).
     Inputs are numpy arrays only as containers.  With ``k_scale``/``v_scale``
-    ([Hkv, D]) the caches hold INT8 codes: written rows are stored as codes,
-    and a cached element reads as code * scale."""
+    ([Hkv, D]) the caches hold codes (int8 caches: INT8; uint8 caches: two
+    INT4 codes per byte): written rows are stored as codes (the dict holds
+    them one per element), and a cached element reads as code * scale."""
     H, Hkv = int(num_heads), int(kv_num_heads)
     N, width = query.shape
     packed = key is None
@@ -58,6 +71,8 @@ def paged_attention_scalar(query, key, value, key_cache, value_cache, cum, past,
     B = len(past)
 
     quant = k_scale is not None
+    int4 = quant and str(key_cache.dtype) == "uint8"
+    code = _code4 if int4 else _code
     scales = None
     if quant:
         scales = ([float(x) for x in k_scale.reshape(-1)], [float(x) for x in v_scale.reshape(-1)])
@@ -86,8 +101,8 @@ def paged_attention_scalar(query, key, value, key_cache, value_cache, cum, past,
             slot = int(block_table[b][blk]) * bs + off
         if slot >= 0:
             if quant:
-                written[slot] = ([_code(x, sv) for x, sv in zip(k_of(t), scales[0])],
-                                 [_code(x, sv) for x, sv in zip(v_of(t), scales[1])])
+                written[slot] = ([code(x, sv) for x, sv in zip(k_of(t), scales[0])],
+                                 [code(x, sv) for x, sv in zip(v_of(t), scales[1])])
             else:
                 written[slot] = (k_of(t), v_of(t))
 
@@ -97,7 +112,10 @@ def paged_attention_scalar(query, key, value, key_cache, value_cache, cum, past,
         else:
             blk, off = divmod(slot, bs)
             src = key_cache if which == 0 else value_cache
-            row = [_num(x) if not quant else int(x) for x in src[blk][off].reshape(-1)]
+            if int4:
+                row = [c for x in src[blk][off].reshape(-1) for c in _nibbles(int(x))]
+            else:
+                row = [_num(x) if not quant else int(x) for x in src[blk][off].reshape(-1)]
         if quant:
             return [c * sv for c, sv in zip(row, scales[which])]
         return row

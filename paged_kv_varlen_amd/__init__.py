@@ -30,7 +30,8 @@ library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpage
 
 PA_DTYPE_F16 = 1
 PA_DTYPE_BF16 = 2
-PA_KV_SAME, PA_KV_INT8 = 0, 1
+PA_KV_SAME, PA_KV_INT8, PA_KV_INT4 = 0, 1, 2
+_CODE_DTYPES = {torch.int8: PA_KV_INT8, torch.uint8: PA_KV_INT4}  # cache dtype -> kv_quant
 _DTYPE_CODES = {torch.float16: PA_DTYPE_F16, torch.bfloat16: PA_DTYPE_BF16}
 ABI_VERSION = 3
 KERNELS = ("scatter_plan", "decode", "merge", "prefill")  # enum pa_kernel order
@@ -156,9 +157,9 @@ def make_args(query, key, value, key_cache, value_cache, cumulative_sequence_len
               k_scale: Optional[torch.Tensor] = None,
               v_scale: Optional[torch.Tensor] = None) -> PaArgs:
     """Fill a PaArgs from tensors (no checks beyond what marshalling needs:
-    the library validates shapes, dtypes and alignment itself).  int8 caches
-    with fp32 ``k_scale``/``v_scale`` [kv_num_heads, head_size] select the
-    INT8 cache path."""
+    the library validates shapes, dtypes and alignment itself).  int8 (INT8)
+    or uint8 (INT4, two codes per byte) caches with fp32 ``k_scale``/``v_scale``
+    [kv_num_heads, head_size] select a quantized cache path."""
     for name, t in (("query", query), ("key", key), ("value", value), ("key_cache", key_cache),
                     ("value_cache", value_cache),
                     ("cumulative_sequence_length", cumulative_sequence_length),
@@ -173,17 +174,17 @@ def make_args(query, key, value, key_cache, value_cache, cumulative_sequence_len
             raise TypeError(f"{name} must be int32 (type constraint S)")
     a = PaArgs()
     a.struct_size = ctypes.sizeof(PaArgs)
-    int8_cache = key_cache.dtype == torch.int8
-    caches = () if int8_cache else (key_cache, value_cache)
+    kv_quant = _CODE_DTYPES.get(key_cache.dtype, PA_KV_SAME)
+    caches = () if kv_quant != PA_KV_SAME else (key_cache, value_cache)
     same = all(t is None or t.dtype == query.dtype for t in (key, value, output) + caches)
-    if int8_cache and value_cache.dtype != torch.int8:
+    if kv_quant != PA_KV_SAME and value_cache.dtype != key_cache.dtype:
         same = False
     a.dtype = _dtype_code(query) if same else 0
-    if int8_cache:
+    if kv_quant != PA_KV_SAME:
         for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
             if t is None or t.dtype != torch.float32 or not t.is_contiguous():
-                raise ValueError(f"int8 caches need a contiguous float32 {name}")
-        a.kv_quant = PA_KV_INT8
+                raise ValueError(f"quantized caches need a contiguous float32 {name}")
+        a.kv_quant = kv_quant
         a.k_scale = _ptr(k_scale)
         a.v_scale = _ptr(v_scale)
     a.query = _ptr(query)
@@ -252,7 +253,9 @@ def paged_attention(query: torch.Tensor, key: Optional[torch.Tensor],
     (enable_timing=True); the library records pair k around its k-th kernel.
 
     INT8 caches: int8 ``key_cache``/``value_cache`` with fp32 ``k_scale`` and
-    ``v_scale`` [kv_num_heads, head_size] (per-channel scales)."""
+    ``v_scale`` [kv_num_heads, head_size] (per-channel scales).  INT4 caches:
+    uint8 [num_blocks, block_size, kv_num_heads, head_size / 2], two codes per
+    byte (the even element in bits 0-3), with the same scales."""
     lib = library()
     dev = query.device
     if dev.type != "cuda":

@@ -25,7 +25,7 @@ struct Resolved {
   int64_t N;
   int B, H, Hkv, G, D, bs, NB, MB;
   bool packed;
-  bool q8;  // INT8 caches
+  int kq;  // cache codes: 0 (the caches hold T), 8 (INT8) or 4 (INT4)
   float scale;
 };
 
@@ -40,7 +40,12 @@ pa_status resolve(const pa_args* a, Resolved* r) {
   const int64_t heads = r->packed ? a->num_heads + 2LL * a->kv_num_heads : a->num_heads;
   if (a->query_width <= 0 || a->query_width % heads != 0) return PA_ERR_SHAPE;
   const int64_t D = a->query_width / heads;
-  if (a->cache_kv_heads != a->kv_num_heads || a->cache_head_size != D) return PA_ERR_SHAPE;
+  if (a->kv_quant != PA_KV_SAME && a->kv_quant != PA_KV_INT8 && a->kv_quant != PA_KV_INT4)
+    return PA_ERR_UNSUPPORTED;
+  r->kq = a->kv_quant == PA_KV_INT8 ? 8 : a->kv_quant == PA_KV_INT4 ? 4 : 0;
+  const int64_t cache_row = r->kq == 4 ? D / 2 : D;  // INT4: bytes of a row
+  if (a->cache_kv_heads != a->kv_num_heads || a->cache_head_size != cache_row || (r->kq == 4 && D % 2 != 0))
+    return PA_ERR_SHAPE;
   if (a->num_blocks <= 0 || a->block_size <= 0 || a->max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
   if (a->batch_size == 0 && a->num_tokens != 0) return PA_ERR_SHAPE;
   if (static_cast<int64_t>(a->max_blocks_per_seq) * a->block_size > INT32_MAX ||
@@ -48,8 +53,6 @@ pa_status resolve(const pa_args* a, Resolved* r) {
     return PA_ERR_SHAPE;
   if ((a->dtype != PA_DTYPE_F16 && a->dtype != PA_DTYPE_BF16) || a->is_causal != 1) return PA_ERR_UNSUPPORTED;
   if (D != 64 && D != 128 && D != 256) return PA_ERR_UNSUPPORTED;
-  if (a->kv_quant != PA_KV_SAME && a->kv_quant != PA_KV_INT8) return PA_ERR_UNSUPPORTED;
-  r->q8 = a->kv_quant == PA_KV_INT8;
   if (a->block_size % 16 != 0 || a->block_size > 4096) return PA_ERR_UNSUPPORTED;
   if (a->num_heads / a->kv_num_heads > 64) return PA_ERR_UNSUPPORTED;
   {  // decode tile indices are 32-bit
@@ -90,9 +93,9 @@ WorkspaceLayout layout(const Resolved& r) {
   const int64_t units = static_cast<int64_t>(r.Hkv) * decode_head_chunks(r.G);
   const int64_t max_tiles = std::min<int64_t>(r.B, r.N) * units *
                             ((static_cast<int64_t>(r.MB) * r.bs + kDecodeTile - 1) / kDecodeTile);
-  const int64_t resident = static_cast<int64_t>(device_cus()) * decode_wg_per_cu(r.D, hs, r.q8);
+  const int64_t resident = static_cast<int64_t>(device_cus()) * decode_wg_per_cu(r.D, hs, r.kq);
   w.decode_grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(resident, (max_tiles + 31) / 32)));
-  w.decode_waves = w.decode_grid * decode_wg_waves(r.D, r.q8);
+  w.decode_waves = w.decode_grid * decode_wg_waves(r.D, r.kq != 0);
   const size_t W = static_cast<size_t>(w.decode_waves);
   size_t off = 0;
   w.ctrl = off;
@@ -220,7 +223,7 @@ pa_status pa_paged_attention(const pa_args* a, void* stream) {
       !aligned4(a->block_table) || !aligned4(a->slot_mapping) || !aligned16(a->workspace) ||
       !aligned4(a->lse) || !aligned16(a->output_f32))
     return PA_ERR_ALIGNMENT;
-  if (r.q8) {
+  if (r.kq != 0) {
     if (a->k_scale == nullptr || a->v_scale == nullptr) return PA_ERR_NULL_ARG;
     if (!aligned16(a->k_scale) || !aligned16(a->v_scale)) return PA_ERR_ALIGNMENT;
   }
@@ -274,10 +277,10 @@ pa_status pa_paged_attention(const pa_args* a, void* stream) {
   sp.decode_units = r.Hkv * decode_head_chunks(r.G);
   sp.decode_waves = w.decode_waves;
   sp.prefill_positions = prefill_positions(r.G);
-  sp.q8 = r.q8 ? 1 : 0;
+  sp.kq = r.kq;
   sp.bf16 = a->dtype == PA_DTYPE_BF16 ? 1 : 0;
-  sp.k_scale = r.q8 ? a->k_scale : nullptr;
-  sp.v_scale = r.q8 ? a->v_scale : nullptr;
+  sp.k_scale = r.kq != 0 ? a->k_scale : nullptr;
+  sp.v_scale = r.kq != 0 ? a->v_scale : nullptr;
   mark(PA_KERNEL_SCATTER_PLAN, 0);
   if (launch_scatter_plan(sp, s) != hipSuccess) return PA_ERR_HIP;
   mark(PA_KERNEL_SCATTER_PLAN, 1);
@@ -316,7 +319,7 @@ pa_status pa_paged_attention(const pa_args* a, void* stream) {
   const int cus = device_cus();
   mark(PA_KERNEL_DECODE, 0);
   const bool bf16 = a->dtype == PA_DTYPE_BF16;
-  if (launch_decode(ap, r.D, decode_head_slots(r.G), bf16, r.q8, w.decode_grid, s) != hipSuccess)
+  if (launch_decode(ap, r.D, decode_head_slots(r.G), bf16, r.kq, w.decode_grid, s) != hipSuccess)
     return PA_ERR_HIP;
   mark(PA_KERNEL_DECODE, 1);
   mark(PA_KERNEL_MERGE, 0);  // the merge of cut decode segments opens the prefill launch
@@ -326,7 +329,7 @@ pa_status pa_paged_attention(const pa_args* a, void* stream) {
   const int pf_grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(pf_work, int64_t(cus) * kPrefillWgPerCu)));
   ap.items = sp.pf_items;
   mark(PA_KERNEL_PREFILL, 0);
-  if (launch_prefill(ap, r.D, bf16, r.q8, pf_grid, s) != hipSuccess) return PA_ERR_HIP;
+  if (launch_prefill(ap, r.D, bf16, r.kq, pf_grid, s) != hipSuccess) return PA_ERR_HIP;
   mark(PA_KERNEL_PREFILL, 1);
   return PA_OK;
 }

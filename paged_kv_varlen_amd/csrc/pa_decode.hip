@@ -511,35 +511,252 @@ struct CodeRegs<256> {
   }
 };
 
+// INT4 caches: XOR swizzle (16-byte chunks) of code row r for head sizes 128
+// and 256 (rows of 64 and 128 bytes), chosen like swz8 for the 4-byte K reads
+// and the byte reads of V; head size 64 (32-byte rows, 4-byte direct loads)
+// is not swizzled
+template <int D>
+__device__ inline int swz4(int r) {
+  if constexpr (D == 128) return (r >> 2) & 3;
+  else if constexpr (D == 256) return (r >> 1) & 7;
+  else return 0;
+}
+
+// INT4 caches: the tile's code bytes, converted in registers.  k[s]: the 8
+// codes of key n at d = 32 s + 8 g .. +7 (4 bytes, one ds_read_b32).  v[4 blk
+// + j]: the byte holding the code of key 4 g + j at d = 16 blk + n (its
+// nibble n & 1).  As for CodeRegs, four base addresses per lane serve every
+// block, and head size 256 reads in two parts.
+template <int D>
+struct CodeRegs4;
+template <>
+struct CodeRegs4<64> {
+  static constexpr int FIRST = 4;  // V blocks of read(); read_rest() has the others
+  uint32_t k[2];
+  uint32_t v[16];
+  template <int OFF>
+  __device__ void read(const uint32_t (&ka)[2], const uint32_t (&vb)[4]) {
+    asm volatile(
+        "ds_read_b32 %0, %18 offset:%24\n\t"
+        "ds_read_b32 %1, %19 offset:%24\n\t"
+        "ds_read_u8 %2, %20 offset:%24+0\n\t"
+        "ds_read_u8 %3, %20 offset:%24+32\n\t"
+        "ds_read_u8 %4, %20 offset:%24+64\n\t"
+        "ds_read_u8 %5, %20 offset:%24+96\n\t"
+        "ds_read_u8 %6, %21 offset:%24+0\n\t"
+        "ds_read_u8 %7, %21 offset:%24+32\n\t"
+        "ds_read_u8 %8, %21 offset:%24+64\n\t"
+        "ds_read_u8 %9, %21 offset:%24+96\n\t"
+        "ds_read_u8 %10, %22 offset:%24+0\n\t"
+        "ds_read_u8 %11, %22 offset:%24+32\n\t"
+        "ds_read_u8 %12, %22 offset:%24+64\n\t"
+        "ds_read_u8 %13, %22 offset:%24+96\n\t"
+        "ds_read_u8 %14, %23 offset:%24+0\n\t"
+        "ds_read_u8 %15, %23 offset:%24+32\n\t"
+        "ds_read_u8 %16, %23 offset:%24+64\n\t"
+        "ds_read_u8 %17, %23 offset:%24+96\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+          "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]),
+          "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15])
+        : "v"(ka[0]), "v"(ka[1]), "v"(vb[0]), "v"(vb[1]), "v"(vb[2]), "v"(vb[3]), "n"(OFF)
+        : "memory");
+  }
+  template <int OFF>
+  __device__ void read_rest(const uint32_t (&)[2], const uint32_t (&)[4]) {}
+};
+template <>
+struct CodeRegs4<128> {
+  static constexpr int FIRST = 8;  // V blocks of read(); read_rest() has the others
+  uint32_t k[4];
+  uint32_t v[32];
+  template <int OFF>
+  __device__ void read(const uint32_t (&ka)[4], const uint32_t (&vb)[4]) {
+    asm volatile(
+        "ds_read_b32 %0, %36 offset:%44\n\t"
+        "ds_read_b32 %1, %37 offset:%44\n\t"
+        "ds_read_b32 %2, %38 offset:%44\n\t"
+        "ds_read_b32 %3, %39 offset:%44\n\t"
+        "ds_read_u8 %4, %40 offset:%44+0\n\t"
+        "ds_read_u8 %5, %40 offset:%44+64\n\t"
+        "ds_read_u8 %6, %40 offset:%44+128\n\t"
+        "ds_read_u8 %7, %40 offset:%44+192\n\t"
+        "ds_read_u8 %8, %40 offset:%44+8\n\t"
+        "ds_read_u8 %9, %40 offset:%44+72\n\t"
+        "ds_read_u8 %10, %40 offset:%44+136\n\t"
+        "ds_read_u8 %11, %40 offset:%44+200\n\t"
+        "ds_read_u8 %12, %41 offset:%44+0\n\t"
+        "ds_read_u8 %13, %41 offset:%44+64\n\t"
+        "ds_read_u8 %14, %41 offset:%44+128\n\t"
+        "ds_read_u8 %15, %41 offset:%44+192\n\t"
+        "ds_read_u8 %16, %41 offset:%44+8\n\t"
+        "ds_read_u8 %17, %41 offset:%44+72\n\t"
+        "ds_read_u8 %18, %41 offset:%44+136\n\t"
+        "ds_read_u8 %19, %41 offset:%44+200\n\t"
+        "ds_read_u8 %20, %42 offset:%44+0\n\t"
+        "ds_read_u8 %21, %42 offset:%44+64\n\t"
+        "ds_read_u8 %22, %42 offset:%44+128\n\t"
+        "ds_read_u8 %23, %42 offset:%44+192\n\t"
+        "ds_read_u8 %24, %42 offset:%44+8\n\t"
+        "ds_read_u8 %25, %42 offset:%44+72\n\t"
+        "ds_read_u8 %26, %42 offset:%44+136\n\t"
+        "ds_read_u8 %27, %42 offset:%44+200\n\t"
+        "ds_read_u8 %28, %43 offset:%44+0\n\t"
+        "ds_read_u8 %29, %43 offset:%44+64\n\t"
+        "ds_read_u8 %30, %43 offset:%44+128\n\t"
+        "ds_read_u8 %31, %43 offset:%44+192\n\t"
+        "ds_read_u8 %32, %43 offset:%44+8\n\t"
+        "ds_read_u8 %33, %43 offset:%44+72\n\t"
+        "ds_read_u8 %34, %43 offset:%44+136\n\t"
+        "ds_read_u8 %35, %43 offset:%44+200\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]),
+          "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]),
+          "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15]), "=&v"(v[16]), "=&v"(v[17]), "=&v"(v[18]),
+          "=&v"(v[19]), "=&v"(v[20]), "=&v"(v[21]), "=&v"(v[22]), "=&v"(v[23]), "=&v"(v[24]), "=&v"(v[25]),
+          "=&v"(v[26]), "=&v"(v[27]), "=&v"(v[28]), "=&v"(v[29]), "=&v"(v[30]), "=&v"(v[31])
+        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(vb[0]), "v"(vb[1]), "v"(vb[2]), "v"(vb[3]), "n"(OFF)
+        : "memory");
+  }
+  template <int OFF>
+  __device__ void read_rest(const uint32_t (&)[4], const uint32_t (&)[4]) {}
+};
+template <>
+struct CodeRegs4<256> {
+  static constexpr int FIRST = 8;  // V blocks of read(); read_rest() has the others
+  uint32_t k[8];
+  uint32_t v[64];
+  template <int OFF>
+  __device__ void read(const uint32_t (&ka)[8], const uint32_t (&vb)[4]) {
+    asm volatile(
+        "ds_read_b32 %0, %40 offset:%52\n\t"
+        "ds_read_b32 %1, %41 offset:%52\n\t"
+        "ds_read_b32 %2, %42 offset:%52\n\t"
+        "ds_read_b32 %3, %43 offset:%52\n\t"
+        "ds_read_b32 %4, %44 offset:%52\n\t"
+        "ds_read_b32 %5, %45 offset:%52\n\t"
+        "ds_read_b32 %6, %46 offset:%52\n\t"
+        "ds_read_b32 %7, %47 offset:%52\n\t"
+        "ds_read_u8 %8, %48 offset:%52+0\n\t"
+        "ds_read_u8 %9, %48 offset:%52+128\n\t"
+        "ds_read_u8 %10, %48 offset:%52+272\n\t"
+        "ds_read_u8 %11, %48 offset:%52+400\n\t"
+        "ds_read_u8 %12, %48 offset:%52+8\n\t"
+        "ds_read_u8 %13, %48 offset:%52+136\n\t"
+        "ds_read_u8 %14, %48 offset:%52+280\n\t"
+        "ds_read_u8 %15, %48 offset:%52+408\n\t"
+        "ds_read_u8 %16, %48 offset:%52+16\n\t"
+        "ds_read_u8 %17, %48 offset:%52+144\n\t"
+        "ds_read_u8 %18, %48 offset:%52+256\n\t"
+        "ds_read_u8 %19, %48 offset:%52+384\n\t"
+        "ds_read_u8 %20, %48 offset:%52+24\n\t"
+        "ds_read_u8 %21, %48 offset:%52+152\n\t"
+        "ds_read_u8 %22, %48 offset:%52+264\n\t"
+        "ds_read_u8 %23, %48 offset:%52+392\n\t"
+        "ds_read_u8 %24, %49 offset:%52+0\n\t"
+        "ds_read_u8 %25, %49 offset:%52+128\n\t"
+        "ds_read_u8 %26, %49 offset:%52+272\n\t"
+        "ds_read_u8 %27, %49 offset:%52+400\n\t"
+        "ds_read_u8 %28, %49 offset:%52+8\n\t"
+        "ds_read_u8 %29, %49 offset:%52+136\n\t"
+        "ds_read_u8 %30, %49 offset:%52+280\n\t"
+        "ds_read_u8 %31, %49 offset:%52+408\n\t"
+        "ds_read_u8 %32, %49 offset:%52+16\n\t"
+        "ds_read_u8 %33, %49 offset:%52+144\n\t"
+        "ds_read_u8 %34, %49 offset:%52+256\n\t"
+        "ds_read_u8 %35, %49 offset:%52+384\n\t"
+        "ds_read_u8 %36, %49 offset:%52+24\n\t"
+        "ds_read_u8 %37, %49 offset:%52+152\n\t"
+        "ds_read_u8 %38, %49 offset:%52+264\n\t"
+        "ds_read_u8 %39, %49 offset:%52+392\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]), "=&v"(k[6]), "=&v"(k[7]),
+          "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
+          "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]),
+          "=&v"(v[15]), "=&v"(v[16]), "=&v"(v[17]), "=&v"(v[18]), "=&v"(v[19]), "=&v"(v[20]), "=&v"(v[21]),
+          "=&v"(v[22]), "=&v"(v[23]), "=&v"(v[24]), "=&v"(v[25]), "=&v"(v[26]), "=&v"(v[27]), "=&v"(v[28]),
+          "=&v"(v[29]), "=&v"(v[30]), "=&v"(v[31])
+        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(ka[4]), "v"(ka[5]), "v"(ka[6]), "v"(ka[7]),
+          "v"(vb[0]), "v"(vb[1]), "v"(vb[2]), "v"(vb[3]), "n"(OFF)
+        : "memory");
+  }
+  template <int OFF>
+  __device__ void read_rest(const uint32_t (&ka)[8], const uint32_t (&vb)[4]) {
+    asm volatile(
+        "ds_read_u8 %0, %34 offset:%36+0\n\t"
+        "ds_read_u8 %1, %34 offset:%36+128\n\t"
+        "ds_read_u8 %2, %34 offset:%36+272\n\t"
+        "ds_read_u8 %3, %34 offset:%36+400\n\t"
+        "ds_read_u8 %4, %34 offset:%36+8\n\t"
+        "ds_read_u8 %5, %34 offset:%36+136\n\t"
+        "ds_read_u8 %6, %34 offset:%36+280\n\t"
+        "ds_read_u8 %7, %34 offset:%36+408\n\t"
+        "ds_read_u8 %8, %34 offset:%36+16\n\t"
+        "ds_read_u8 %9, %34 offset:%36+144\n\t"
+        "ds_read_u8 %10, %34 offset:%36+256\n\t"
+        "ds_read_u8 %11, %34 offset:%36+384\n\t"
+        "ds_read_u8 %12, %34 offset:%36+24\n\t"
+        "ds_read_u8 %13, %34 offset:%36+152\n\t"
+        "ds_read_u8 %14, %34 offset:%36+264\n\t"
+        "ds_read_u8 %15, %34 offset:%36+392\n\t"
+        "ds_read_u8 %16, %35 offset:%36+0\n\t"
+        "ds_read_u8 %17, %35 offset:%36+128\n\t"
+        "ds_read_u8 %18, %35 offset:%36+272\n\t"
+        "ds_read_u8 %19, %35 offset:%36+400\n\t"
+        "ds_read_u8 %20, %35 offset:%36+8\n\t"
+        "ds_read_u8 %21, %35 offset:%36+136\n\t"
+        "ds_read_u8 %22, %35 offset:%36+280\n\t"
+        "ds_read_u8 %23, %35 offset:%36+408\n\t"
+        "ds_read_u8 %24, %35 offset:%36+16\n\t"
+        "ds_read_u8 %25, %35 offset:%36+144\n\t"
+        "ds_read_u8 %26, %35 offset:%36+256\n\t"
+        "ds_read_u8 %27, %35 offset:%36+384\n\t"
+        "ds_read_u8 %28, %35 offset:%36+24\n\t"
+        "ds_read_u8 %29, %35 offset:%36+152\n\t"
+        "ds_read_u8 %30, %35 offset:%36+264\n\t"
+        "ds_read_u8 %31, %35 offset:%36+392\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[32]), "=&v"(v[33]), "=&v"(v[34]), "=&v"(v[35]), "=&v"(v[36]), "=&v"(v[37]), "=&v"(v[38]),
+          "=&v"(v[39]), "=&v"(v[40]), "=&v"(v[41]), "=&v"(v[42]), "=&v"(v[43]), "=&v"(v[44]), "=&v"(v[45]),
+          "=&v"(v[46]), "=&v"(v[47]), "=&v"(v[48]), "=&v"(v[49]), "=&v"(v[50]), "=&v"(v[51]), "=&v"(v[52]),
+          "=&v"(v[53]), "=&v"(v[54]), "=&v"(v[55]), "=&v"(v[56]), "=&v"(v[57]), "=&v"(v[58]), "=&v"(v[59]),
+          "=&v"(v[60]), "=&v"(v[61]), "=&v"(v[62]), "=&v"(v[63])
+        : "v"(vb[0]), "v"(vb[1]), "v"(vb[2]), "v"(vb[3]), "n"(OFF)
+        : "memory");
+  }
+};
+
 // per-tile flags handed from the issuing side to the computing side
 constexpr int kFirst = 1 << 8;     // first tile of a piece
 constexpr int kLast = 1 << 9;      // last tile of a piece
 constexpr int kComplete = 1 << 10; // the piece is the whole segment
 constexpr int kSecond = 1 << 11;   // partial goes to the wave's second slot
 
-template <int D, int HS, bool BF16, bool Q8>
-__global__ __launch_bounds__(64 * decode_wg_waves(D, Q8)) void decode_kernel(AttnParams p) {
+template <int D, int HS, bool BF16, int KQ>
+__global__ __launch_bounds__(64 * decode_wg_waves(D, KQ != 0)) void decode_kernel(AttnParams p) {
   using E = Elem<BF16>;
-  constexpr int kDecodeWaves = decode_wg_waves(D, Q8);
+  constexpr bool QNT = KQ != 0;                   // the caches hold codes (INT8 or INT4)
+  constexpr bool Q4 = KQ == 4;
+  constexpr int kDecodeWaves = decode_wg_waves(D, QNT);
   constexpr int ROW = 2 * D;                      // bytes of one key of one kv head (data type)
   constexpr int CPR = ROW / 16;                   // 16-byte chunks per row
-  constexpr int ROWC = Q8 ? D : ROW;              // bytes of a cached row (INT8: codes)
-  constexpr int CPRC = ROWC / 16;
-  constexpr int KPI = 1024 / ROWC;                // cached rows per 1 KB direct load
+  constexpr int ROWC = cache_row_bytes(D, KQ);    // bytes of a cached row (codes when quantized)
   constexpr int QPI = 1024 / ROW;                 // query rows (data type) per 1 KB direct load
-  constexpr int NK = kDecodeTile / KPI;           // direct loads per tensor per tile
+  // direct loads of LBK bytes per lane (4 when a tile is under 1 KB)
+  constexpr int LBK = kDecodeTile * ROWC >= 1024 ? 16 : 4;
+  constexpr int NK = kDecodeTile * ROWC / (64 * LBK);  // direct loads per tensor per tile
   constexpr int TB = kDecodeTile * ROW;           // bytes per tensor per tile (data type)
   constexpr int TBC = kDecodeTile * ROWC;         // bytes per tensor per tile as cached
   constexpr int QB = decode_q_bytes(D, HS);
   constexpr int NQ = QB / 1024;                   // direct loads of a query block
-  constexpr int SB = Q8 ? decode_scale_bytes(D) : 0;  // k and v scale rows of the unit
+  constexpr int SB = QNT ? decode_scale_bytes(D) : 0;  // k and v scale rows of the unit
   constexpr int NSC = SB / 1024;                  // direct loads of the scale rows
-  constexpr int SLOT = decode_slot_bytes(D, HS, Q8);
-  constexpr int R = decode_ring(D, HS, Q8);
+  constexpr int SLOT = decode_slot_bytes(D, HS, KQ);
+  constexpr int R = decode_ring(D, HS, KQ);
   constexpr int KS = D / 32;                      // QK MFMA steps
   constexpr int DB = D / 16;                      // PV MFMA blocks (16 dims each)
-  constexpr int ES = Q8 ? 1 : 2;                  // bytes per cached element
   static_assert(SLOT == 2 * TBC + QB + SB, "slot layout");
+  static_assert(NK >= 1 && NK * 64 * LBK == TBC, "tile loads");
   static_assert(R >= 2, "ring");
 
   __shared__ __align__(1024) char ring[kDecodeWaves][R][SLOT];
@@ -571,28 +788,39 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, Q8)) void decode_kernel(Att
   const int tile_elems = kDecodeTile * kv_row;
 
   // ---- per-lane constant offsets ---------------------------------------------
-  // tile loads: byte offset of lane's 16 bytes (key, logical chunk) for direct load j
-  // (INT8 caches: code rows, swizzled by swz8)
+  // tile loads: byte offset (from the tile's first cached row) of the LBK
+  // bytes that land at lane * LBK of direct load j: row kj, 16-byte chunk c
+  // (16-bit caches: swizzled by swz; INT8: swz8; INT4: swz4, none at D = 64)
+  const int slot_bytes = p.kv_heads * ROWC;  // bytes of one cache slot
   uint32_t src_off[NK];
 #pragma unroll
   for (int j = 0; j < NK; ++j) {
-    const int kj = j * KPI + lane / CPRC;
-    const int c = Q8 ? (lane % CPRC) ^ swz8<D>(kj) : (lane % CPR) ^ swz<D>(kj);
-    src_off[j] = Q8 ? static_cast<uint32_t>(kj * kv_row + 16 * c) : static_cast<uint32_t>(kj * kv_row + 8 * c) * 2u;
+    const int o = 64 * LBK * j + LBK * lane;
+    const int kj = o / ROWC, pos = (o % ROWC) / 16;
+    const int c = KQ == 8 ? pos ^ swz8<D>(kj) : KQ == 4 ? pos ^ swz4<D>(kj) : pos ^ swz<D>(kj);
+    src_off[j] = static_cast<uint32_t>(kj * slot_bytes + (LBK == 16 ? 16 * c : o % ROWC));
   }
   const int qchunk = (lane % CPR) * 8;
   // MFMA operand addresses of ring slot 0 (slot s adds s * SLOT); INT8
   // caches: addresses of the code reads (CodeRegs) in ka and vb
   const int n = lane & 15, g = lane >> 4;
   const uint32_t ring0 = uniform(static_cast<int>(lds_addr(&ring[wave][0][0])));
-  uint32_t ka[KS], va[Q8 ? 1 : DB], vb[4], qa[KS];
+  uint32_t ka[KS], va[QNT ? 1 : DB], vb[4], qa[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    ka[s] = Q8 ? ring0 + n * D + 16 * ((2 * s + (g >> 1)) ^ swz8<D>(n)) + 8 * (g & 1)
-               : ring0 + n * ROW + 16 * ((4 * s + g) ^ swz<D>(n));
+    ka[s] = Q4    ? ring0 + n * ROWC + 16 * (s ^ swz4<D>(n)) + 4 * g
+            : QNT ? ring0 + n * D + 16 * ((2 * s + (g >> 1)) ^ swz8<D>(n)) + 8 * (g & 1)
+                  : ring0 + n * ROW + 16 * ((4 * s + g) ^ swz<D>(n));
     qa[s] = ring0 + 2 * TBC + (n < QB / ROW ? n : 0) * ROW + 16 * (4 * s + g);
   }
-  if constexpr (Q8) {
+  if constexpr (Q4) {
+    // the byte of block blk and key 4g+j (CodeRegs4) is at vb[i] + a constant:
+    // D = 64: i = blk; 128: i = blk / 2; 256: i = blk / 4
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      vb[i] = ring0 + TBC + (n >> 1) + (D == 64 ? 128 * g + 8 * i : D == 128 ? 256 * g + 16 * (i ^ g)
+                                                                             : 512 * g + 32 * (i ^ g));
+  } else if constexpr (QNT) {
     // byte j of block blk (key 4g+j, d = 16 blk + n) is at vb[i] + a constant
     // (CodeRegs): D = 64: i = blk; 128: i = blk / 2; 256: i = blk % 4
 #pragma unroll
@@ -689,7 +917,7 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, Q8)) void decode_kernel(Att
   };
   auto set_pointers = [&]() __attribute__((always_inline)) {
     const int page = uniform(__builtin_amdgcn_readlane(wcur, pi - wp0));
-    const int64_t base = (static_cast<int64_t>(page) * page_elems + ip * tile_elems + kvh_i * D) * ES;
+    const int64_t base = (static_cast<int64_t>(page) * page_elems + ip * tile_elems + kvh_i * D) / D * ROWC;
     kp = reinterpret_cast<const char*>(p.key_cache) + base;
     vp = reinterpret_cast<const char*>(p.value_cache) + base;
   };
@@ -714,9 +942,9 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, Q8)) void decode_kernel(Att
     constexpr int S = decltype(slot_c)::value;
     const uint32_t sb = ring0 + S * SLOT;
 #pragma unroll
-    for (int j = 0; j < NK; ++j) dma<16>(kp + src_off[j], sb + 1024 * j);
+    for (int j = 0; j < NK; ++j) dma<LBK>(kp + src_off[j], sb + 64 * LBK * j);
 #pragma unroll
-    for (int j = 0; j < NK; ++j) dma<16>(vp + src_off[j], sb + TBC + 1024 * j);
+    for (int j = 0; j < NK; ++j) dma<LBK>(vp + src_off[j], sb + TBC + 64 * LBK * j);
     opc += 2 * NK;
     const bool first = g_i == g0 || i_i == 0;
     if (first) {  // the unit's query heads (absent heads read zeros)
@@ -727,7 +955,7 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, Q8)) void decode_kernel(Att
         dma<16>(hh < nh_i ? qtok + hh * D + qchunk : p.zeros + qchunk, sb + 2 * TBC + 1024 * j);
       }
       opc += NQ;
-      if constexpr (Q8) {  // the kv head's scale rows: [k_scale (4D bytes) | v_scale (4D bytes) | zeros]
+      if constexpr (QNT) {  // the kv head's scale rows: [k_scale (4D bytes) | v_scale (4D bytes) | zeros]
 #pragma unroll
         for (int j = 0; j < NSC; ++j) {
           const int o = 1024 * j + 16 * lane;
@@ -776,8 +1004,8 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, Q8)) void decode_kernel(Att
       if (pi == wp0 + kDecodeWindow) need_window();
       set_pointers();
     } else {
-      kp += tile_elems * ES;
-      vp += tile_elems * ES;
+      kp += tile_elems / D * ROWC;
+      vp += tile_elems / D * ROWC;
     }
   };
 
@@ -787,9 +1015,9 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, Q8)) void decode_kernel(Att
   for (int blk = 0; blk < DB; ++blk) acc[blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // INT8 caches: the v scale of each output value of this lane (d = 16 blk +
   // 4 g + e), read with the piece's first tile
-  f32x4_t vsc[Q8 ? DB : 1];
+  f32x4_t vsc[QNT ? DB : 1];
 #pragma unroll
-  for (int blk = 0; blk < (Q8 ? DB : 1); ++blk) vsc[blk] = f32x4_t{1.f, 1.f, 1.f, 1.f};
+  for (int blk = 0; blk < (QNT ? DB : 1); ++blk) vsc[blk] = f32x4_t{1.f, 1.f, 1.f, 1.f};
   float m = kNegInf, l = 0.f;
   u32x4 qv[KS];
   int nh_c = 0, h0_c = 0, t_c = 0;
@@ -809,7 +1037,7 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, Q8)) void decode_kernel(Att
 #pragma unroll
         for (int s = 0; s < KS; ++s) qv[s] = u32x4{0u, 0u, 0u, 0u};
       }
-      if constexpr (Q8) {
+      if constexpr (QNT) {
         // scores use the codes of K, so its per-channel scale goes into Q:
         // q_d s_d, rounded to the data type (values d = 32 s + 8 g + e)
         const uint32_t sc0 = ring0 + S * SLOT + 2 * TBC + QB;
@@ -844,7 +1072,24 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, Q8)) void decode_kernel(Att
     // the tile's operands: K fragments (KS) and V^T fragments (DB)
     typename E::x8 kx[KS];
     typename E::x4 vx[DB];
-    if constexpr (Q8) {  // codes -> data type in registers (exact)
+    if constexpr (Q4) {  // INT4 codes -> data type in registers (exact)
+      CodeRegs4<D> cr;
+      const int sh = 4 * (n & 1);  // this lane's nibble of a V byte
+      auto v_block = [&](int blk) __attribute__((always_inline)) {
+        const uint32_t* b = &cr.v[4 * blk];
+        const typename E::x2 a = E::from_nibble_pair(((b[0] >> sh) & 15u) | (((b[1] >> sh) & 15u) << 16));
+        const typename E::x2 c = E::from_nibble_pair(((b[2] >> sh) & 15u) | (((b[3] >> sh) & 15u) << 16));
+        vx[blk] = typename E::x4{a[0], a[1], c[0], c[1]};
+      };
+      cr.template read<S * SLOT>(ka, vb);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kx[s] = E::from_nibbles8(cr.k[s]);
+#pragma unroll
+      for (int blk = 0; blk < CodeRegs4<D>::FIRST; ++blk) v_block(blk);
+      cr.template read_rest<S * SLOT>(ka, vb);
+#pragma unroll
+      for (int blk = CodeRegs4<D>::FIRST; blk < DB; ++blk) v_block(blk);
+    } else if constexpr (QNT) {  // INT8 codes -> data type in registers (exact)
       CodeRegs<D> cr;
       auto v_block = [&](int blk) __attribute__((always_inline)) {
         const typename E::x2 a = E::from_code_halves(cr.v[4 * blk] | (cr.v[4 * blk + 1] << 16));
@@ -895,7 +1140,7 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, Q8)) void decode_kernel(Att
     // row sum of exactly the rounded weights the MFMA multiplies
     l = E::sum2(typename E::x2{pb[0], pb[1]}, l);
     l = E::sum2(typename E::x2{pb[2], pb[3]}, l);
-    if (!Q8 && nvalid < kDecodeTile) {
+    if (!QNT && nvalid < kDecodeTile) {
       // keys past the history may hold any bits (NaN included): zero their
       // values (codes are always finite, and their weights are 0)
       const int k0 = 4 * g;
@@ -922,14 +1167,14 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, Q8)) void decode_kernel(Att
           for (int blk = 0; blk < DB; ++blk) {
             typename E::x4 hv;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) hv[e] = E::round(acc[blk][e] * inv * vsc[Q8 ? blk : 0][e]);
+            for (int e = 0; e < 4; ++e) hv[e] = E::round(acc[blk][e] * inv * vsc[QNT ? blk : 0][e]);
             *reinterpret_cast<typename E::x4*>(o + 16 * blk) = hv;
           }
           // optional partial state: fp32 output and natural-log lse
           if (p.out_f32 != nullptr) {
 #pragma unroll
             for (int blk = 0; blk < DB; ++blk)
-              *reinterpret_cast<f32x4_t*>(p.out_f32 + row * D + 4 * g + 16 * blk) = acc[blk] * inv * vsc[Q8 ? blk : 0];
+              *reinterpret_cast<f32x4_t*>(p.out_f32 + row * D + 4 * g + 16 * blk) = acc[blk] * inv * vsc[QNT ? blk : 0];
           }
           if (p.lse_out != nullptr && g == 0) p.lse_out[row] = (m + __log2f(lt)) * kLn2;
         }
@@ -937,7 +1182,7 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, Q8)) void decode_kernel(Att
         const int ps = 2 * w + ((fl & kSecond) ? 1 : 0);
         float* po = p.part_o + (static_cast<int64_t>(ps) * kDecodeUnitHeads + n) * D + 4 * g;
 #pragma unroll
-        for (int blk = 0; blk < DB; ++blk) *reinterpret_cast<f32x4_t*>(po + 16 * blk) = acc[blk] * inv * vsc[Q8 ? blk : 0];
+        for (int blk = 0; blk < DB; ++blk) *reinterpret_cast<f32x4_t*>(po + 16 * blk) = acc[blk] * inv * vsc[QNT ? blk : 0];
         if (g == 0) p.part_lse[ps * kDecodeUnitHeads + n] = m + __log2f(lt);
       }
     }
@@ -963,16 +1208,21 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, Q8)) void decode_kernel(Att
 
 }  // namespace
 
-hipError_t launch_decode(const AttnParams& p, int head_size, int head_slots, bool bf16, bool q8, int grid,
+template <int D, int HS, bool BF16>
+void launch_decode_t(const AttnParams& p, int kq, dim3 g, hipStream_t s) {
+  const dim3 b(64 * decode_wg_waves(D, kq != 0));
+  if (kq == 8) hipLaunchKernelGGL((decode_kernel<D, HS, BF16, 8>), g, b, 0, s, p);
+  else if (kq == 4) hipLaunchKernelGGL((decode_kernel<D, HS, BF16, 4>), g, b, 0, s, p);
+  else hipLaunchKernelGGL((decode_kernel<D, HS, BF16, 0>), g, b, 0, s, p);
+}
+
+hipError_t launch_decode(const AttnParams& p, int head_size, int head_slots, bool bf16, int kq, int grid,
                          hipStream_t s) {
   const dim3 g(grid);
 #define PA_DECODE(DD, HH)                                                                        \
   if (head_size == DD && head_slots == HH) {                                                     \
-    const dim3 b(64 * decode_wg_waves(DD, q8));                                                  \
-    if (bf16 && q8) hipLaunchKernelGGL((decode_kernel<DD, HH, true, true>), g, b, 0, s, p);       \
-    else if (bf16) hipLaunchKernelGGL((decode_kernel<DD, HH, true, false>), g, b, 0, s, p);       \
-    else if (q8) hipLaunchKernelGGL((decode_kernel<DD, HH, false, true>), g, b, 0, s, p);         \
-    else hipLaunchKernelGGL((decode_kernel<DD, HH, false, false>), g, b, 0, s, p);                \
+    if (bf16) launch_decode_t<DD, HH, true>(p, kq, g, s);                                        \
+    else launch_decode_t<DD, HH, false>(p, kq, g, s);                                            \
     return hipGetLastError();                                                                    \
   }
   PA_DECODE(128, 4)

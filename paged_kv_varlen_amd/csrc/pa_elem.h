@@ -9,8 +9,8 @@
 // export for ORT GenAI Engine", Phase 1 scope) targets fp16 and bf16, and the
 // "WS2 CP-Aware Attention Contract" example (Qwen3-8B TP=2 CP=2) runs in bf16.
 // Both types accumulate in fp32 and round once at the final write (WS2,
-// Reduction Semantics).  With INT8 caches the matrix products take the codes
-// converted to the data type (exact: |code| <= 127).
+// Reduction Semantics).  With INT8 and INT4 caches the matrix products take
+// the codes converted to the data type (exact: |code| <= 127).
 #pragma once
 
 #include <stdint.h>
@@ -70,6 +70,27 @@ struct Elem<false> {  // IEEE binary16
     const x2 bias = {static_cast<_Float16>(1152.f), static_cast<_Float16>(1152.f)};
     return __builtin_bit_cast(x2, (w ^ 0x00800080u) + 0x64006400u) - bias;
   }
+  // two int4 codes (4-bit two's complement, zero-extended into the 16-bit
+  // halves of w) as values: the half 1024 + (u ^ 8), minus 1032
+  static __device__ inline x2 from_nibble_pair(uint32_t w) {
+    const x2 bias = {static_cast<_Float16>(1032.f), static_cast<_Float16>(1032.f)};
+    return __builtin_bit_cast(x2, (w ^ 0x00080008u) + 0x64006400u) - bias;
+  }
+  // eight int4 codes (nibble e of w is code e) as values: the even codes (low
+  // nibbles) and odd ones (high nibbles) of each byte are paired by v_perm_b32
+  static __device__ inline x8 from_nibbles8(uint32_t w) {
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    const uint32_t h[4] = {__builtin_amdgcn_perm(hi, lo, 0x0c040c00u), __builtin_amdgcn_perm(hi, lo, 0x0c050c01u),
+                           __builtin_amdgcn_perm(hi, lo, 0x0c060c02u), __builtin_amdgcn_perm(hi, lo, 0x0c070c03u)};
+    x8 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const x2 v = from_nibble_pair(h[k]);
+      r[2 * k] = v[0];
+      r[2 * k + 1] = v[1];
+    }
+    return r;
+  }
 };
 
 template <>
@@ -110,6 +131,20 @@ struct Elem<true> {  // bfloat16: the upper half of a binary32
     const uint32_t u = w ^ 0x00800080u;  // code + 128 in bits 0..7 and 16..23
     return x2{static_cast<__bf16>(static_cast<float>(u & 0xffu) - 128.f),
               static_cast<__bf16>(static_cast<float>((u >> 16) & 0xffu) - 128.f)};
+  }
+  // two int4 codes (4-bit two's complement, zero-extended into the 16-bit
+  // halves of w) as values
+  static __device__ inline x2 from_nibble_pair(uint32_t w) {
+    return x2{static_cast<__bf16>(static_cast<float>(static_cast<int>(w << 28) >> 28)),
+              static_cast<__bf16>(static_cast<float>(static_cast<int>(w << 12) >> 28))};
+  }
+  // eight int4 codes (nibble e of w is code e) as values
+  static __device__ inline x8 from_nibbles8(uint32_t w) {
+    x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      r[e] = static_cast<__bf16>(static_cast<float>(static_cast<int>(w << (28 - 4 * e)) >> 28));
+    return r;
   }
 };
 

@@ -27,12 +27,13 @@ namespace pa {
 
 // ---- tiling constants -----------------------------------------------------
 // waves per decode workgroup: 4, or 2 at head_size 256 (so that a ring of
-// three or four 16-key tiles per wave still fits in LDS).  INT8 caches (q8)
+// three or four 16-key tiles per wave still fits in LDS).  Quantized caches (INT8
+// or INT4: quant)
 // halve the tile bytes and add the code conversion to every tile, so twice
 // the waves share the LDS (two per SIMD below head_size 256) with rings of
 // two to four tiles: one wave converts while the other waits on its loads.
-__host__ __device__ constexpr int decode_wg_waves(int D, bool q8 = false) {
-  return q8 ? (D > 128 ? 4 : 8) : (D > 128 ? 2 : 4);
+__host__ __device__ constexpr int decode_wg_waves(int D, bool quant = false) {
+  return quant ? (D > 128 ? 4 : 8) : (D > 128 ? 2 : 4);
 }
 constexpr int kDecodeTile = 16;       // keys per decode tile
 constexpr int kDecodeUnitHeads = 16;  // query heads of one decode segment (MFMA N)
@@ -73,30 +74,32 @@ __host__ __device__ constexpr int decode_head_slots(int group) {
   return group >= 16 ? 16 : group > 4 ? (group > 8 ? 16 : 8) : 4;
 }
 // LDS per ring slot: K tile, V tile (16 keys each) and the query block; with
-// INT8 caches (q8) the tiles are codes (one byte per element) and the slot
-// also holds the unit's k and v scale rows (fp32, at least one 1 KB load)
+// quantized caches (kq = 8: INT8, one byte per element; kq = 4: INT4, half a
+// byte) the tiles are codes and the slot also holds the unit's k and v scale
+// rows (fp32, at least one 1 KB load)
 __host__ __device__ constexpr int decode_q_bytes(int D, int hslots) {
   return hslots * 2 * D > 1024 ? hslots * 2 * D : 1024;
 }
 __host__ __device__ constexpr int decode_scale_bytes(int D) { return 8 * D > 1024 ? 8 * D : 1024; }
-__host__ __device__ constexpr int decode_slot_bytes(int D, int hslots, bool q8 = false) {
-  return q8 ? 2 * kDecodeTile * D + decode_q_bytes(D, hslots) + decode_scale_bytes(D)
-            : 2 * kDecodeTile * 2 * D + decode_q_bytes(D, hslots);
+// bytes of one cached row of one kv head: 2D (16-bit), D (INT8), D / 2 (INT4)
+__host__ __device__ constexpr int cache_row_bytes(int D, int kq) { return kq == 8 ? D : kq == 4 ? D / 2 : 2 * D; }
+__host__ __device__ constexpr int decode_slot_bytes(int D, int hslots, int kq = 0) {
+  return 2 * kDecodeTile * cache_row_bytes(D, kq) + decode_q_bytes(D, hslots) + (kq != 0 ? decode_scale_bytes(D) : 0);
 }
 // ring depth: as many slots as fit the workgroup's waves in about 150 KB, at
 // most 4
-__host__ __device__ constexpr int decode_ring(int D, int hslots, bool q8 = false) {
-  return (150 * 1024) / (decode_wg_waves(D, q8) * decode_slot_bytes(D, hslots, q8)) > 4
+__host__ __device__ constexpr int decode_ring(int D, int hslots, int kq = 0) {
+  return (150 * 1024) / (decode_wg_waves(D, kq != 0) * decode_slot_bytes(D, hslots, kq)) > 4
              ? 4
-             : (150 * 1024) / (decode_wg_waves(D, q8) * decode_slot_bytes(D, hslots, q8));
+             : (150 * 1024) / (decode_wg_waves(D, kq != 0) * decode_slot_bytes(D, hslots, kq));
 }
 // per wave: the ring, a 16-byte piece record per slot, 512 bytes of
 // prefetched metadata
-__host__ __device__ constexpr int decode_lds_bytes(int D, int hslots, bool q8 = false) {
-  return decode_wg_waves(D, q8) * (decode_ring(D, hslots, q8) * (decode_slot_bytes(D, hslots, q8) + 16) + 512);
+__host__ __device__ constexpr int decode_lds_bytes(int D, int hslots, int kq = 0) {
+  return decode_wg_waves(D, kq != 0) * (decode_ring(D, hslots, kq) * (decode_slot_bytes(D, hslots, kq) + 16) + 512);
 }
-__host__ __device__ constexpr int decode_wg_per_cu(int D, int hslots, bool q8 = false) {
-  return (160 * 1024) / decode_lds_bytes(D, hslots, q8) > 0 ? (160 * 1024) / decode_lds_bytes(D, hslots, q8) : 1;
+__host__ __device__ constexpr int decode_wg_per_cu(int D, int hslots, int kq = 0) {
+  return (160 * 1024) / decode_lds_bytes(D, hslots, kq) > 0 ? (160 * 1024) / decode_lds_bytes(D, hslots, kq) : 1;
 }
 // floor(a / b) for 0 <= a, 0 < b: in 32 bits when both fit (a 64-bit
 // division is a long instruction sequence on the GPU)
@@ -154,7 +157,7 @@ struct ScatterPlanParams {
   int32_t prefill_positions;   // query positions per prefill half-tile
   const float* k_scale;        // [Hkv, D] with INT8 caches, else null
   const float* v_scale;
-  int32_t q8;                  // caches hold INT8 codes
+  int32_t kq;                  // caches hold codes: 8 (INT8), 4 (INT4), else 0
   int32_t bf16;                // step rows are bf16 (else fp16)
 };
 
@@ -205,9 +208,9 @@ struct MergeStatesParams {
 
 // ---- launchers (defined in the .hip files) ---------------------------------
 hipError_t launch_scatter_plan(const ScatterPlanParams& p, hipStream_t s);
-hipError_t launch_decode(const AttnParams& p, int head_size, int head_slots, bool bf16, bool q8, int grid,
+hipError_t launch_decode(const AttnParams& p, int head_size, int head_slots, bool bf16, int kq, int grid,
                          hipStream_t s);
-hipError_t launch_prefill(const AttnParams& p, int head_size, bool bf16, bool q8, int grid, hipStream_t s);
+hipError_t launch_prefill(const AttnParams& p, int head_size, bool bf16, int kq, int grid, hipStream_t s);
 hipError_t launch_merge_states(const MergeStatesParams& p, hipStream_t s);
 
 }  // namespace pa

@@ -54,9 +54,10 @@
 // group and all keys of a step (two 32-key sub-steps), and a ring of two
 // steps; everything else as above.
 //
-// INT8 caches: the ring holds the cached codes (one byte per element, rows
-// of D bytes, unswizzled) and each step first turns them into data-type rows
-// of a stage buffer, in the swizzled layout above (exact: |code| <= 127), so
+// INT8 / INT4 caches: the ring holds the cached codes (one byte or half a
+// byte per element, rows of D or D/2 bytes, unswizzled) and each step turns
+// them into data-type rows of a stage buffer, in the swizzled layout above
+// (exact: |code| <= 127), so
 // the products run as for 16-bit caches.  The scores then use the codes of K,
 // so each query row is multiplied by the kv head's K scales (rounded to the
 // data type) once per item; O is multiplied by the V scales at the final
@@ -142,8 +143,9 @@ __device__ inline void plain_barrier() {
 // needs a SIMD of its own (four waves, up to 512 registers each); each wave
 // then takes all 64 keys of a step as two 32-key sub-steps (one kv group),
 // and a ring of two steps (64 KB each) fits in LDS.
-template <int D, bool Q8 = false>
+template <int D, int KQ = 0>
 struct PrefillShape {
+  static constexpr bool QNT = KQ != 0;               // the caches hold codes (INT8 or INT4)
   static constexpr bool WIDE = D > 128;
   static constexpr int WAVES = WIDE ? 4 : 8;         // waves per workgroup
   static constexpr int THREADS = 64 * WAVES;
@@ -155,15 +157,15 @@ struct PrefillShape {
   static constexpr int ROWS_PER_LOAD = 64 / CPR;     // rows per 1 KB direct load
   static constexpr int WAVE_ROWS = kPrefillKeys / WAVES;  // rows of K (and V) each wave fetches
   static constexpr int BUF = kPrefillKeys * ROWB;    // bytes per K (or V) step, data type
-  // cached rows as fetched: ROWC bytes each (INT8: codes), LB bytes per lane
+  // cached rows as fetched: ROWC bytes each (quantized: codes), LB bytes per lane
   // and direct load (4 when a wave's rows are under 1 KB)
-  static constexpr int ROWC = Q8 ? D : ROWB;
+  static constexpr int ROWC = cache_row_bytes(D, KQ);
   static constexpr int LB = WAVE_ROWS * ROWC >= 1024 ? 16 : 4;
   static constexpr int LOADS = WAVE_ROWS * ROWC / (64 * LB);  // direct loads per wave per tensor
   static constexpr int CBUF = kPrefillKeys * ROWC;   // bytes per ring buffer
-  // INT8: the converted K and V rows of the step, and the kv-group merge
+  // quantized: the converted K and V rows of the step, and the kv-group merge
   // area (one buffer of O per row group)
-  static constexpr int STAGE = Q8 ? (KVG == 2 ? 4 : 2) * BUF : 16;
+  static constexpr int STAGE = QNT ? (KVG == 2 ? 4 : 2) * BUF : 16;
   static constexpr int QK_STEPS = D / 16;            // MFMA k-steps over the head dim
   static constexpr int O_TILES = D / 32;             // 32-wide d tiles of O^T
   // steps per slot window: 4 slots per step, RING - 1 steps fetched ahead,
@@ -176,9 +178,10 @@ struct PrefillShape {
   static __device__ int v_swz(int row) { return D >= 128 ? ((row & 3) << 2) : 0; }
 };
 
-template <int D, bool BF16, bool Q8>
+template <int D, bool BF16, int KQ>
 __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnParams p) {
-  using S = PrefillShape<D, Q8>;
+  using S = PrefillShape<D, KQ>;
+  constexpr bool QNT = S::QNT;
   using E = Elem<BF16>;
   typedef typename E::x8 x8;
   typedef typename E::x4 x4;
@@ -186,10 +189,9 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
   constexpr int kRing = S::RING;
   constexpr int kChunk = S::CHUNK;
   static_assert(S::LOADS >= 1 && S::LOADS * 64 * S::LB == S::WAVE_ROWS * S::ROWC, "loads per wave");
-  constexpr int ES = Q8 ? 1 : 2;  // bytes per cached element
-  // INT8 with two kv groups: two stages (step parity); step j converts the
+  // quantized, two kv groups: two stages (step parity); step j converts the
   // codes of step j + 1 while the products of step j run
-  constexpr bool kAhead = Q8 && S::KVG == 2;
+  constexpr bool kAhead = QNT && S::KVG == 2;
   static_assert(!kAhead || S::STAGE >= 4 * S::BUF, "two stages");
 
   // one LDS object per ring buffer and tensor: the compiler can then see that
@@ -210,8 +212,8 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
   auto vbuf = [&](int b) -> char* { return b == 0 ? v_lds0 : b == 1 ? v_lds1 : b == 2 ? v_lds2 : v_lds3; };
   // the K and V rows the products of ring buffer b's step read (data type,
   // swizzled); with two stages, a step's parity is that of its ring buffer
-  auto kread = [&](int b) -> char* { return Q8 ? stage + (kAhead ? (b & 1) * 2 * S::BUF : 0) : kbuf(b); };
-  auto vread = [&](int b) -> char* { return Q8 ? kread(b) + S::BUF : vbuf(b); };
+  auto kread = [&](int b) -> char* { return QNT ? stage + (kAhead ? (b & 1) * 2 * S::BUF : 0) : kbuf(b); };
+  auto vread = [&](int b) -> char* { return QNT ? kread(b) + S::BUF : vbuf(b); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -279,20 +281,20 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
 
   // loader: direct load i of a wave covers 64 * LB bytes of its WAVE_ROWS
   // rows; byte offsets (from the wave's first row) of this lane's piece for
-  // each load (16-bit rows: a swizzled 16-byte chunk; INT8: bytes in order),
+  // each load (16-bit rows: a swizzled 16-byte chunk; codes: bytes in order),
   // and of the same piece in the zero page
   const int lrow0 = lane / CPR;
   const int lchunk = lane % CPR;
   auto load_row = [&](int i) -> int {  // row (within the wave's) of this lane's piece of load i
-    return Q8 ? (64 * S::LB * i + S::LB * lane) / S::ROWC : S::ROWS_PER_LOAD * i + lrow0;
+    return QNT ? (64 * S::LB * i + S::LB * lane) / S::ROWC : S::ROWS_PER_LOAD * i + lrow0;
   };
   uint32_t offk[S::LOADS], offv[S::LOADS];
 #pragma unroll
   for (int i = 0; i < S::LOADS; ++i) {
     const int rl = load_row(i);
     const int trow = S::WAVE_ROWS * wave + rl;  // row within the step's 64
-    if constexpr (Q8) {
-      offk[i] = offv[i] = static_cast<uint32_t>(rl * static_cast<int>(kv_row) + (64 * S::LB * i + S::LB * lane) % S::ROWC);
+    if constexpr (QNT) {
+      offk[i] = offv[i] = static_cast<uint32_t>(rl * p.kv_heads * S::ROWC + (64 * S::LB * i + S::LB * lane) % S::ROWC);
     } else {
       offk[i] = static_cast<uint32_t>((rl * static_cast<int>(kv_row) + (lchunk ^ S::k_swz(trow)) * 8) * 2);
       offv[i] = static_cast<uint32_t>((rl * static_cast<int>(kv_row) + (lchunk ^ S::v_swz(trow)) * 8) * 2);
@@ -351,7 +353,7 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
       for (int kk = 0; kk < S::QK_STEPS; ++kk) {
         uint4 raw = make_uint4(0u, 0u, 0u, 0u);
         if (row_valid) raw = *reinterpret_cast<const uint4*>(qrow + 16 * kk + 8 * lhalf);
-        if constexpr (Q8) {  // q_d * ks_d, d = 16 kk + 8 lhalf + e, rounded to the data type
+        if constexpr (QNT) {  // q_d * ks_d, d = 16 kk + 8 lhalf + e, rounded to the data type
           const float4* ks = reinterpret_cast<const float4*>(p.k_scale + static_cast<int64_t>(kvh) * D + 16 * kk +
                                                              8 * lhalf);
           const float4 s0 = ks[0], s1 = ks[1];
@@ -378,9 +380,9 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
     // min(L, nsteps * 64), for 16-key groups [gbase, gbase + kSlotWindow);
     // a wave's 8 rows of a step never cross a page (bs is a multiple of 16)
     const int ngroups = (min(L, nsteps * kPrefillKeys) + 15) / 16;
-    const char* kbytes = reinterpret_cast<const char*>(p.key_cache) + static_cast<int64_t>(kvh) * D * ES;
-    const char* vbytes = reinterpret_cast<const char*>(p.value_cache) + static_cast<int64_t>(kvh) * D * ES;
-    const uint32_t row_bytes = static_cast<uint32_t>(kv_row) * ES;
+    const char* kbytes = reinterpret_cast<const char*>(p.key_cache) + static_cast<int64_t>(kvh) * S::ROWC;
+    const char* vbytes = reinterpret_cast<const char*>(p.value_cache) + static_cast<int64_t>(kvh) * S::ROWC;
+    const uint32_t row_bytes = static_cast<uint32_t>(p.kv_heads * S::ROWC);  // bytes of a cache slot
     int gbase = 0;
     auto fill_window = [&](int first) {
       gbase = first;
@@ -526,22 +528,33 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
       }
     };
 
-    // INT8: the codes of the step in ring buffer buf -> data-type rows of the
+    // quantized: the codes of the step in ring buffer buf -> data-type rows of the
     // stage, in the layout the products read: cached chunk c (16 codes) of
     // row r becomes chunks 2c and 2c+1 of row r, swizzled
     // (into the stage that the products of ring buffer buf's step read)
+    // (INT4: a 16-byte chunk holds 32 codes and becomes chunks 4c .. 4c+3)
     auto convert = [&](auto buf_tag) __attribute__((always_inline)) {
       constexpr int buf = decltype(buf_tag)::value;
-      constexpr int NC = kPrefillKeys * D / 16;  // 16-code chunks per tensor
-      constexpr int CPRC = D / 16;               // per row
+      constexpr int NC = kPrefillKeys * S::ROWC / 16;  // 16-byte code chunks per tensor
+      constexpr int CPRC = S::ROWC / 16;               // per row
+      constexpr int TPC = 2 * D / S::ROWC;             // data-type chunks per code chunk
       auto one = [&](bool is_v, int cc) __attribute__((always_inline)) {
         const int r = cc / CPRC, k = cc % CPRC;
         const uint4 raw = *reinterpret_cast<const uint4*>((is_v ? vbuf(buf) : kbuf(buf)) + 16 * cc);
-        const x8 lo = E::from_codes(raw.x, raw.y), hi = E::from_codes(raw.z, raw.w);
+        x8 t[TPC];
+        if constexpr (KQ == 4) {
+          t[0] = E::from_nibbles8(raw.x);
+          t[1] = E::from_nibbles8(raw.y);
+          t[2] = E::from_nibbles8(raw.z);
+          t[3] = E::from_nibbles8(raw.w);
+        } else {
+          t[0] = E::from_codes(raw.x, raw.y);
+          t[1] = E::from_codes(raw.z, raw.w);
+        }
         const int swz = is_v ? S::v_swz(r) : S::k_swz(r);
         char* row = (is_v ? vread(buf) : kread(buf)) + r * ROWB;
-        *reinterpret_cast<x8*>(row + (((2 * k) ^ swz) << 4)) = lo;
-        *reinterpret_cast<x8*>(row + (((2 * k + 1) ^ swz) << 4)) = hi;
+#pragma unroll
+        for (int i = 0; i < TPC; ++i) *reinterpret_cast<x8*>(row + (((TPC * k + i) ^ swz) << 4)) = t[i];
       };
       if constexpr (NC >= S::THREADS) {
         static_assert(NC % S::THREADS == 0, "conversion split");
@@ -551,8 +564,8 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
           one(true, it * S::THREADS + tid);
         }
       } else {
-        static_assert(2 * NC == S::THREADS, "conversion split");
-        one(tid >= NC, tid >= NC ? tid - NC : tid);  // (wave-uniform tensor)
+        static_assert(2 * NC <= S::THREADS, "conversion split");
+        if (tid < 2 * NC) one(tid >= NC, tid >= NC ? tid - NC : tid);  // (wave-uniform tensor)
       }
     };
 
@@ -565,7 +578,7 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
     // With a ring of two (head size 256) the fill of step j + 1 goes into
     // buffer (j + 1) % 2 at the start of step j (its last reader, step j - 1,
     // ended at the barrier) and lands before the barrier that ends step j.
-    // With INT8 caches a ring buffer's readers are the conversion at the start
+    // With quantized caches a ring buffer's readers are the conversion at the start
     // of its step, which ends at a barrier of its own; the products read the
     // stage, which the barrier ending a step frees for the next conversion.
     auto step = [&](auto buf_tag, int jstep) __attribute__((always_inline)) {
@@ -581,7 +594,7 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
         // the next step's codes (landed before the barrier that ended the
         // previous step) into the other stage, whose readers finished there
         if (jstep + 1 < nsteps) convert(std::integral_constant<int, (buf + 1) % kRing>{});
-      } else if constexpr (Q8) {
+      } else if constexpr (QNT) {
         // the stage's last readers finished at the barrier that ended the
         // previous step; the codes of this step landed before it
         convert(buf_tag);
@@ -657,11 +670,11 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
 
     // merge the two kv groups (group 0 first) and write.  Row group r's O of
     // kv group 1 goes to K buffer r ([O_TILES*16][64 lanes] floats), (m, l)
-    // of all row groups to V buffer 0 (INT8: stage buffer r and the slot
+    // of all row groups to V buffer 0 (quantized: stage buffer r and the slot
     // window).  (One kv group: nothing to merge.)
     wait_fills<0>();  // (the last steps already waited)
-    float* xo = reinterpret_cast<float*>(Q8 ? stage + (S::KVG == 2 ? rg * S::BUF : 0) : kbuf(rg));
-    float* xml = Q8 ? reinterpret_cast<float*>(slot_lds) : reinterpret_cast<float*>(v_lds0);
+    float* xo = reinterpret_cast<float*>(QNT ? stage + (S::KVG == 2 ? rg * S::BUF : 0) : kbuf(rg));
+    float* xml = QNT ? reinterpret_cast<float*>(slot_lds) : reinterpret_cast<float*>(v_lds0);
     if constexpr (S::KVG == 2) {
       if (kvg == 1) {
 #pragma unroll
@@ -708,7 +721,7 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
                 v[2 * e + 1] = o[mt][ir + 1] * inv;
               }
             }
-            if constexpr (Q8) {  // O used the codes of V: times the V scales of d = 32mt + 8q + 4lhalf + 0..3
+            if constexpr (QNT) {  // O used the codes of V: times the V scales of d = 32mt + 8q + 4lhalf + 0..3
               const float4 vs = *reinterpret_cast<const float4*>(p.v_scale + static_cast<int64_t>(kvh) * D + 32 * mt +
                                                                  8 * q + 4 * lhalf);
               v[0] *= vs.x;
@@ -730,43 +743,44 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
   }
 }
 
-template <int D, bool Q8>
+template <int D, int KQ>
 constexpr size_t prefill_smem() {
-  using S = PrefillShape<D, Q8>;
+  using S = PrefillShape<D, KQ>;
   return 2 * S::RING * static_cast<size_t>(S::CBUF) + (S::RING > 2 ? 0 : 4 * 16) + S::STAGE +
          kSlotWindow * sizeof(int) + 16;
 }
-// the merge area (O of one row group) must fit one K buffer (INT8: one stage
-// buffer), (m, l) of the four row groups one V buffer (INT8: the slot window)
+// the merge area (O of one row group) must fit one K buffer (quantized
+// caches: one stage buffer), (m, l) of the four row groups one V buffer (the
+// slot window)
 static_assert(4 * 16 * 64 * sizeof(float) <= PrefillShape<128>::CBUF, "merge area");
 static_assert(2 * 16 * 64 * sizeof(float) <= PrefillShape<64>::CBUF, "merge area");
-static_assert(4 * 16 * 64 * sizeof(float) <= PrefillShape<128, true>::BUF, "merge area");
-static_assert(2 * 16 * 64 * sizeof(float) <= PrefillShape<64, true>::BUF, "merge area");
+static_assert(4 * 16 * 64 * sizeof(float) <= PrefillShape<128, 8>::BUF, "merge area");
+static_assert(2 * 16 * 64 * sizeof(float) <= PrefillShape<64, 8>::BUF, "merge area");
 static_assert(4 * 2 * 64 * sizeof(float) <= kSlotWindow * sizeof(int), "merge area");
-static_assert(prefill_smem<128, false>() <= 160 * 1024 && prefill_smem<256, false>() <= 160 * 1024, "LDS budget");
-static_assert(prefill_smem<128, true>() <= 160 * 1024 && prefill_smem<256, true>() <= 160 * 1024, "LDS budget");
+static_assert(prefill_smem<128, 0>() <= 160 * 1024 && prefill_smem<256, 0>() <= 160 * 1024, "LDS budget");
+static_assert(prefill_smem<128, 8>() <= 160 * 1024 && prefill_smem<256, 8>() <= 160 * 1024, "LDS budget");
+static_assert(prefill_smem<128, 4>() <= 160 * 1024 && prefill_smem<256, 4>() <= 160 * 1024, "LDS budget");
 
 template <int D, bool BF16>
-hipError_t launch_prefill_q(const AttnParams& p, bool q8, int grid, hipStream_t s) {
-  if (q8)
-    hipLaunchKernelGGL((prefill_kernel<D, BF16, true>), dim3(grid), dim3(PrefillShape<D, true>::THREADS), 0, s, p);
-  else
-    hipLaunchKernelGGL((prefill_kernel<D, BF16, false>), dim3(grid), dim3(PrefillShape<D, false>::THREADS), 0, s,
-                       p);
+hipError_t launch_prefill_q(const AttnParams& p, int kq, int grid, hipStream_t s) {
+  const dim3 b(PrefillShape<D>::THREADS);
+  if (kq == 8) hipLaunchKernelGGL((prefill_kernel<D, BF16, 8>), dim3(grid), b, 0, s, p);
+  else if (kq == 4) hipLaunchKernelGGL((prefill_kernel<D, BF16, 4>), dim3(grid), b, 0, s, p);
+  else hipLaunchKernelGGL((prefill_kernel<D, BF16, 0>), dim3(grid), b, 0, s, p);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_prefill_t(const AttnParams& p, bool bf16, bool q8, int grid, hipStream_t s) {
-  return bf16 ? launch_prefill_q<D, true>(p, q8, grid, s) : launch_prefill_q<D, false>(p, q8, grid, s);
+hipError_t launch_prefill_t(const AttnParams& p, bool bf16, int kq, int grid, hipStream_t s) {
+  return bf16 ? launch_prefill_q<D, true>(p, kq, grid, s) : launch_prefill_q<D, false>(p, kq, grid, s);
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const AttnParams& p, int head_size, bool bf16, bool q8, int grid, hipStream_t s) {
-  if (head_size == 256) return launch_prefill_t<256>(p, bf16, q8, grid, s);
-  if (head_size == 128) return launch_prefill_t<128>(p, bf16, q8, grid, s);
-  if (head_size == 64) return launch_prefill_t<64>(p, bf16, q8, grid, s);
+hipError_t launch_prefill(const AttnParams& p, int head_size, bool bf16, int kq, int grid, hipStream_t s) {
+  if (head_size == 256) return launch_prefill_t<256>(p, bf16, kq, grid, s);
+  if (head_size == 128) return launch_prefill_t<128>(p, bf16, kq, grid, s);
+  if (head_size == 64) return launch_prefill_t<64>(p, bf16, kq, grid, s);
   return hipErrorInvalidValue;
 }
 

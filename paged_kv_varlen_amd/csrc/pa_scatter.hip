@@ -12,8 +12,9 @@
 // so a 2 KB row (Hkv=8, D=128) is one fully coalesced 128-lane read and write
 // per cache.  With INT8 caches a lane turns its 8 elements into 8 codes
 // clamp(rint(x / s), -127, 127) with the per-channel scales s, the quotient
-// in fp32 (IEEE division) and rounded half to even.  The last workgroup of
-// the grid plans the attention work.
+// in fp32 (IEEE division) and rounded half to even; with INT4 caches into 8
+// codes clamped to [-7, 7], packed as nibbles (element 2i in bits 0-3).  The
+// last workgroup of the grid plans the attention work.
 #include "pa_internal.h"
 
 namespace pa {
@@ -165,7 +166,8 @@ __global__ __launch_bounds__(kPlanThreads) void scatter_plan_kernel(ScatterPlanP
   const int chunks = p.row_elems >> 3;  // 16-byte pieces per row
   const int64_t src = t * p.src_stride;
   const int64_t dst = slot * p.row_elems;
-  if (p.q8) {
+  if (p.kq != 0) {
+    const float lim = p.kq == 4 ? 7.f : 127.f;
     for (int c = threadIdx.x; c < 2 * chunks; c += blockDim.x) {
       const bool is_v = c >= chunks;
       const int cc = is_v ? c - chunks : c;
@@ -174,17 +176,21 @@ __global__ __launch_bounds__(kPlanThreads) void scatter_plan_kernel(ScatterPlanP
       const float4 s0 = sc[0], s1 = sc[1];
       const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
       const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-      uint32_t packed[2] = {0u, 0u};
+      uint32_t packed[2] = {0u, 0u}, nib = 0u;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t bits = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
         const float x = p.bf16 ? __uint_as_float(bits << 16)
                                : static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
-        const float r = fminf(fmaxf(rintf(x / sv[e]), -127.f), 127.f);
-        packed[e >> 2] |= (static_cast<uint32_t>(static_cast<int>(r)) & 0xffu) << (8 * (e & 3));
+        const uint32_t code = static_cast<uint32_t>(static_cast<int>(fminf(fmaxf(rintf(x / sv[e]), -lim), lim)));
+        packed[e >> 2] |= (code & 0xffu) << (8 * (e & 3));
+        nib |= (code & 0xfu) << (4 * e);
       }
       int8_t* cache = reinterpret_cast<int8_t*>(is_v ? p.value_cache : p.key_cache);
-      *reinterpret_cast<uint2*>(cache + dst + 8 * cc) = make_uint2(packed[0], packed[1]);
+      if (p.kq == 4)  // a row is row_elems / 2 bytes
+        *reinterpret_cast<uint32_t*>(cache + dst / 2 + 4 * cc) = nib;
+      else
+        *reinterpret_cast<uint2*>(cache + dst + 8 * cc) = make_uint2(packed[0], packed[1]);
     }
     return;
   }

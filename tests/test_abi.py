@@ -128,8 +128,13 @@ def test_workspace_bytes_static_bound():
     (dict(lse=FAKE + 2), ALIGN),                         # lse needs 4-byte alignment
     (dict(output_f32=FAKE + 4), ALIGN),                  # output_f32 needs 16
     (dict(lse=FAKE, output_f32=FAKE), WS),               # both present and aligned
-    (dict(kv_quant=2), UNSUP),                           # only PA_KV_SAME and PA_KV_INT8
+    (dict(kv_quant=3), UNSUP),                           # only PA_KV_SAME, PA_KV_INT8, PA_KV_INT4
     (dict(kv_quant=-1), UNSUP),
+    (dict(kv_quant=2, k_scale=FAKE, v_scale=FAKE), SHAPE),  # INT4 rows are head_size / 2 bytes
+    (dict(kv_quant=2, cache_head_size=32), NULL),        # INT4 caches need both scale rows
+    (dict(kv_quant=2, cache_head_size=32, k_scale=FAKE, v_scale=FAKE), WS),  # INT4 passes validation
+    (dict(kv_quant=2, k_scale=FAKE, v_scale=FAKE, query_width=4 * 256, cache_head_size=128,
+          dtype=2), WS),                                 # INT4 with bfloat16 and D=256
     (dict(kv_quant=1), NULL),                            # INT8 caches need both scale rows
     (dict(kv_quant=1, k_scale=FAKE), NULL),
     (dict(kv_quant=1, k_scale=FAKE, v_scale=FAKE + 4), ALIGN),  # scales need 16-byte alignment

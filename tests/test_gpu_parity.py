@@ -549,72 +549,83 @@ def test_hip_graph_replay_wide(D, dtype):
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
 
 
-# ------------------------------------------------------------------ INT8 caches (codes + per-channel scales)
+# ------------------------------------------------------------------ INT8 / INT4 caches (codes + per-channel scales)
 
+QUANT = ["int8", "int4"]
+
+
+@pytest.mark.parametrize("kvq", QUANT)
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_int8_tiny(dtype):
-    check(W.tiny(0, dtype=dtype, kv_quant="int8"))
+def test_quant_tiny(dtype, kvq):
+    check(W.tiny(0, dtype=dtype, kv_quant=kvq))
 
 
+@pytest.mark.parametrize("kvq", QUANT)
 @pytest.mark.parametrize("case", range(len(SWEEP)))
 @pytest.mark.parametrize("dtype,packed,slots", [("f16", False, None), ("bf16", True, "drop")])
-def test_int8_sweep(case, dtype, packed, slots):
+def test_quant_sweep(case, dtype, packed, slots, kvq):
     q, p, H, Hkv, D, bs = SWEEP[case]
     n = sum(q)
     b = W.make_batch(q, p, num_heads=H, kv_num_heads=Hkv, head_size=D, block_size=bs,
                      seed=500 + case, packed=packed, slot_mode=slots,
                      drop_count=max(1, n // 20) if slots else 0, num_blocks=None,
-                     name=f"int8_sweep{case}", dtype=dtype, kv_quant="int8")
+                     name=f"{kvq}_sweep{case}", dtype=dtype, kv_quant=kvq)
     check(b)
 
 
+@pytest.mark.parametrize("kvq", QUANT)
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_int8_pure_decode_full(dtype):
-    check(W.pure_decode(0, dtype=dtype, kv_quant="int8"))
+def test_quant_pure_decode_full(dtype, kvq):
+    check(W.pure_decode(0, dtype=dtype, kv_quant=kvq))
 
 
-def test_int8_mixed():
-    b = W.mixed(0, kv_quant="int8")
+@pytest.mark.parametrize("kvq", QUANT)
+def test_quant_mixed(kvq):
+    b = W.mixed(0, kv_quant=kvq)
     check(b, rows=sample_rows(b, per_seq=10))
 
 
+@pytest.mark.parametrize("kvq", QUANT)
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_int8_long_prefill(dtype):
-    b = W.long_prefill(0, dtype=dtype, kv_quant="int8")
+def test_quant_long_prefill(dtype, kvq):
+    b = W.long_prefill(0, dtype=dtype, kv_quant=kvq)
     edges = [0, 1, 31, 32, 33, 1023, 1024, 2015, 2016, 2046, 2047]
     check(b, rows=sample_rows(b, per_seq=40, must=edges))
 
 
+@pytest.mark.parametrize("kvq", QUANT)
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("case", range(len(HD256)))
-def test_int8_head_size_256(case, dtype):
+def test_quant_head_size_256(case, dtype, kvq):
     q, p, H, Hkv, bs = HD256[case]
     b = W.make_batch(q, p, num_heads=H, kv_num_heads=Hkv, head_size=256, block_size=bs,
-                     seed=520 + case, name=f"int8_hd256_{case}", dtype=dtype, kv_quant="int8")
+                     seed=520 + case, name=f"{kvq}_hd256_{case}", dtype=dtype, kv_quant=kvq)
     check(b, rows=sample_rows(b, per_seq=12, seed=case))
 
 
+@pytest.mark.parametrize("kvq", QUANT)
 @pytest.mark.parametrize("D", [64, 128, 256])
-def test_int8_extreme_codes_outside_history(D):
-    # every slot the call must not read holds code 127: keys past a history
-    # come from the zero page, never the cache (a read would move the scores
-    # by tens of units)
+def test_quant_extreme_codes_outside_history(D, kvq):
+    # every slot the call must not read holds the code 7 (INT8: 127): keys past
+    # a history come from the zero page, never the cache (a read would move
+    # the scores by many units)
     b = W.make_batch([1, 37, 1, 5, 70], [50, 20, 4095, 0, 190], num_heads=8, kv_num_heads=2,
-                     head_size=D, block_size=64, seed=540 + D, num_blocks=200, name=f"int8_far{D}",
-                     kv_quant="int8")
+                     head_size=D, block_size=64, seed=540 + D, num_blocks=200, name=f"{kvq}_far{D}",
+                     kv_quant=kvq)
     keep = np.zeros(b.num_blocks * b.block_size, dtype=bool)
     for i in range(b.batch_size):
         for j in range(int(b.kv_lens[i])):
             keep[int(b.block_table[i, j // b.block_size]) * b.block_size + j % b.block_size] = True
     for cache in (b.key_cache, b.value_cache):
         flat = cache.reshape(b.num_blocks * b.block_size, -1)
-        flat[~keep] = 127
+        flat[~keep] = 127 if kvq == "int8" else 0x77
     check(b)
 
 
-def test_int8_state_and_determinism():
+@pytest.mark.parametrize("kvq", QUANT)
+def test_quant_state_and_determinism(kvq):
     b = W.make_batch([300, 1, 1, 64], [700, 9000, 3, 0], num_heads=16, kv_num_heads=4, head_size=128,
-                     block_size=16, seed=550, name="int8_state", kv_quant="int8")
+                     block_size=16, seed=550, name=f"{kvq}_state", kv_quant=kvq)
     rows = sample_rows(b, per_seq=20, seed=5)
     d = DevBatch(b)
     f32 = torch.empty((b.num_tokens, b.num_heads * 128), dtype=torch.float32, device=DEV)

@@ -843,3 +843,119 @@ def test_int8_pins_catch_dequant_mistake():
             check_Q2(oracle.paged_attention)
     finally:
         pa_mod.dequantize = saved
+
+
+# ------------------------------------------------------------------ INT4 caches
+
+# INT4 per-channel caches (uint8 [NB, bs, Hkv, D/2], two codes per byte, the
+# even element in bits 0-3).  Pins:
+#   Q4  hand values of the code clamp(rint(x / s), -7, 7) (ties to even, both
+#       clamps, never -8) and hand-packed bytes; every pair of codes in
+#       [-8, 7] survives pack/unpack;
+#   Q5  with power-of-two scales every code * scale is an fp16 value: the
+#       INT4 oracle equals the fp16 oracle run on those values, bit for bit;
+#   Q6  the scalar formulation (its own nibble decoding) agrees within 1e-12.
+
+def check_Q4(quant, pack, unpack):
+    s = np.full((1, 8), 0.25, dtype=np.float32)
+    x = np.array([[1.0, 0.375, 0.625, 0.875, -0.625, 40.0, -40.0, -1.875]], dtype=np.float16)
+    assert quant(x, s).tolist() == [[4, 2, 2, 4, -2, 7, -7, -7]]
+    c = np.array([[1, -1, 7, -7, 0, 3, -2, 5]], dtype=np.int8)
+    assert pack(c).tolist() == [[0xF1, 0x97, 0x30, 0x5E]]
+    allc = np.array([[a, b] for a in range(-8, 8) for b in range(-8, 8)], dtype=np.int8)
+    assert np.array_equal(unpack(pack(allc)), allc)
+    assert unpack(np.array([[0x8F]], dtype=np.uint8)).tolist() == [[-1, -8]]
+
+
+def check_Q5(fn):
+    rng = np.random.default_rng(35)
+    H, Hkv, D, bs = 4, 2, 16, 4
+    q_lens, past = [3, 1, 6], [5, 11, 0]
+    b = W.make_batch(q_lens, past, num_heads=H, kv_num_heads=Hkv, head_size=D, block_size=bs,
+                     seed=35, kv_quant="int4")
+    s = np.full((Hkv, D), 0.25, dtype=np.float32)
+    K = (rng.integers(-7, 8, b.key.shape) * 0.25).astype(np.float16)
+    V = (rng.integers(-7, 8, b.value.shape) * 0.25).astype(np.float16)
+    o4, kc4, vc4 = fn(b.query, K, V, b.key_cache, b.value_cache, b.cum, b.past, b.block_table,
+                      None, num_heads=H, kv_num_heads=Hkv, k_scale=s, v_scale=s)
+    # the same caches written out as fp16 values (nibble codes read by hand)
+    def as_f16(cache):
+        lo = (cache & 15).astype(np.int16)
+        hi = (cache >> 4).astype(np.int16)
+        lo = np.where(lo >= 8, lo - 16, lo)
+        hi = np.where(hi >= 8, hi - 16, hi)
+        codes = np.stack([lo, hi], axis=-1).reshape(cache.shape[:-1] + (2 * cache.shape[-1],))
+        return (codes * 0.25).astype(np.float16)
+    o16, kc16, vc16 = fn(b.query, K, V, as_f16(b.key_cache), as_f16(b.value_cache), b.cum, b.past,
+                         b.block_table, None, num_heads=H, kv_num_heads=Hkv)
+    assert np.array_equal(o4, o16)
+    assert np.array_equal(as_f16(kc4), kc16)
+    assert np.array_equal(as_f16(vc4), vc16)
+
+
+def check_Q6(fn):
+    for b in (W.tiny(0, kv_quant="int4"),
+              small(seed=37, head_size=4, packed=True, slot_mode="drop", drop_count=2,
+                    dtype="bf16", kv_quant="int4")):
+        o, kc, _ = call(fn, b, k_scale=b.k_scale, v_scale=b.v_scale)
+        so, written = scalar.paged_attention_scalar(b.query, b.key, b.value, b.key_cache,
+                                                    b.value_cache, b.cum, b.past,
+                                                    b.block_table, b.slot_mapping,
+                                                    b.num_heads, b.kv_num_heads, b.scale,
+                                                    k_scale=b.k_scale, v_scale=b.v_scale)
+        assert np.max(np.abs(o - np.array(so))) < 1e-12
+        NB, bs, Hkv, Dh = kc.shape
+        for slot, (krow, _) in written.items():
+            row = kc.reshape(NB * bs, Hkv * Dh)[slot]
+            got = [(v ^ 8) - 8 for byte in row.tolist() for v in (byte & 15, byte >> 4)]
+            assert got == krow
+
+
+def test_oracle_int4_pins():
+    check_Q4(oracle.quantize_int4, oracle.pack_int4, oracle.unpack_int4)
+    check_Q5(oracle.paged_attention)
+    check_Q6(oracle.paged_attention)
+
+
+def _quant4_clamp8(x, s):
+    q = oracle.values(x).astype(np.float32) / np.asarray(s, np.float32)
+    return np.clip(np.rint(q), -8, 7).astype(np.int8)
+
+
+def _pack_high_first(codes):
+    c = np.asarray(codes).astype(np.int16) & 0xF
+    return ((c[..., 0::2] << 4) | c[..., 1::2]).astype(np.uint8)
+
+
+def _unpack_unsigned(b):
+    w = np.asarray(b, dtype=np.uint8).astype(np.int16)
+    out = np.empty(w.shape[:-1] + (2 * w.shape[-1],), dtype=np.int8)
+    out[..., 0::2] = w & 0xF
+    out[..., 1::2] = w >> 4
+    return out
+
+
+@pytest.mark.parametrize("which", ["clamp8", "high_first", "unsigned"])
+def test_int4_pins_catch_planted_mistakes(which):
+    quant, pack, unpack = oracle.quantize_int4, oracle.pack_int4, oracle.unpack_int4
+    if which == "clamp8":
+        quant = _quant4_clamp8
+    elif which == "high_first":
+        pack = _pack_high_first
+    else:
+        unpack = _unpack_unsigned
+    with pytest.raises(AssertionError):
+        check_Q4(quant, pack, unpack)
+
+
+def test_int4_pins_catch_oracle_mistakes():
+    # the oracle itself with a nibble-order or sign mistake fails Q5 or Q6
+    for name, bad in (("pack_int4", _pack_high_first), ("unpack_int4", _unpack_unsigned)):
+        saved = getattr(pa_mod, name)
+        setattr(pa_mod, name, bad)
+        try:
+            with pytest.raises(AssertionError):
+                check_Q5(oracle.paged_attention)
+                check_Q6(oracle.paged_attention)
+        finally:
+            setattr(pa_mod, name, saved)

@@ -30,6 +30,9 @@ left uninitialised (only their shapes are meaningful).
 
 INT8 caches (``kv_quant="int8"``): the cache tensors are int8 codes and the
 batch carries per-(kv head, channel) scales; the step's K/V stay in dtype.
+INT4 caches (``kv_quant="int4"``): uint8 tensors [NB, bs, Hkv, D/2] whose two
+nibbles per byte are independent codes (the even element in bits 0-3), with
+scales as for INT8.
 
 Data type: every workload takes ``dtype`` "f16" (default) or "bf16", and
 ``head_size`` (0 = its own; 256 for the head_size-256 variant: same heads,
@@ -98,6 +101,31 @@ def int8_scales(rng: np.random.Generator, Hkv: int, D: int) -> np.ndarray:
     return (INT8_SCALE * np.exp2(rng.uniform(-0.25, 0.25, (Hkv, D)))).astype(np.float32)
 
 
+# INT4 caches: codes round(1.6 * N(0,1)) clipped to [-7, 7], each stored as the
+# 4-bit two's complement nibble (code & 15), two per byte; scales
+# 4.5/7 * 2^U(-1/4, 1/4), so a cached value is about N(0,1) and the step's
+# N(0,1) rows use about two thirds of the code range on each side
+INT4_CODE_GAIN = 1.6
+INT4_SCALE = 4.5 / 7.0
+
+
+def int4_bytes(rng: np.random.Generator, shape) -> np.ndarray:
+    """uint8 [..., D/2] for a logical shape [..., D]."""
+    *lead, D = shape
+    out = np.empty((*lead, D // 2), dtype=np.uint8)
+    flat = out.reshape(-1)
+    for s in range(0, flat.size, _CHUNK):
+        e = min(flat.size, s + _CHUNK)
+        c = np.clip(np.rint(rng.standard_normal((e - s, 2), dtype=np.float32) * np.float32(INT4_CODE_GAIN)),
+                    -7, 7).astype(np.int16) & 15
+        flat[s:e] = (c[:, 0] | (c[:, 1] << 4)).astype(np.uint8)
+    return out
+
+
+def int4_scales(rng: np.random.Generator, Hkv: int, D: int) -> np.ndarray:
+    return (INT4_SCALE * np.exp2(rng.uniform(-0.25, 0.25, (Hkv, D)))).astype(np.float32)
+
+
 def storage_dtype(dtype: str):
     """numpy dtype that holds tensors of data type ``dtype``."""
     return {"f16": np.float16, "bf16": np.uint16}[dtype]
@@ -125,8 +153,8 @@ class Batch:
     scale: float = 0.0
     note: str = ""
     dtype: str = "f16"                # "f16" (float16 arrays) or "bf16" (uint16 bit patterns)
-    kv_quant: str = "none"            # "none" (caches in dtype) or "int8" (int8 codes + scales)
-    k_scale: Optional[np.ndarray] = None  # fp32 [Hkv, D] with kv_quant "int8"
+    kv_quant: str = "none"            # "none" (caches in dtype), "int8" or "int4" (codes + scales)
+    k_scale: Optional[np.ndarray] = None  # fp32 [Hkv, D] with kv_quant "int8" / "int4"
     v_scale: Optional[np.ndarray] = None
 
     @property
@@ -304,6 +332,15 @@ def _fill(rng, name, seed, q_lens, past, table, nb, H, Hkv, D, bs, packed, slot_
             value_cache = int8_codes(rng, (nb, bs, Hkv, D))
         k_scale = int8_scales(rng, Hkv, D)
         v_scale = int8_scales(rng, Hkv, D)
+    elif kv_quant == "int4":
+        if meta_only:
+            key_cache = np.empty((nb, bs, Hkv, D // 2), np.uint8)
+            value_cache = np.empty((nb, bs, Hkv, D // 2), np.uint8)
+        else:
+            key_cache = int4_bytes(rng, (nb, bs, Hkv, D))
+            value_cache = int4_bytes(rng, (nb, bs, Hkv, D))
+        k_scale = int4_scales(rng, Hkv, D)
+        v_scale = int4_scales(rng, Hkv, D)
     elif kv_quant == "none":
         key_cache = draw((nb, bs, Hkv, D))
         value_cache = draw((nb, bs, Hkv, D))
@@ -429,9 +466,9 @@ def work(batch: Batch) -> dict:
     flops  = 4*D*H * sum_b sum_{i<q_b} (past_b + i + 1)   (QK^T and PV over
              causally visible pairs, 2 flop per multiply-add)
     kv_hist = sum_b L_b * 2 * Hkv * D * e bytes (logical history read; e = 2
-             for 16-bit caches, 1 for INT8 codes)
-    plus query, output, the step's K/V, the cache writes and (INT8) the two
-    scale tables.
+             for 16-bit caches, 1 for INT8 codes, 1/2 for INT4 codes)
+    plus query, output, the step's K/V, the cache writes and (quantized
+    caches) the two scale tables.
     """
     H, Hkv, D = batch.num_heads, batch.kv_num_heads, batch.head_size
     q = batch.q_lens
@@ -439,8 +476,8 @@ def work(batch: Batch) -> dict:
     L = p + q
     pairs = int(np.sum(q * p + q * (q + 1) // 2))
     dec = q == 1
-    int8 = batch.kv_quant == "int8"
-    row = 2 * Hkv * D * (1 if int8 else 2)  # one slot of both caches
+    quant = batch.kv_quant in ("int8", "int4")
+    row = {"none": 2 * Hkv * D * 2, "int8": 2 * Hkv * D, "int4": Hkv * D}[batch.kv_quant]  # a slot, both caches
     n_write = int(batch.num_tokens if batch.slot_mapping is None
                   else np.count_nonzero(batch.slot_mapping >= 0))
     out = {
@@ -452,7 +489,7 @@ def work(batch: Batch) -> dict:
         "o_bytes": batch.num_tokens * H * D * 2,
         "step_kv_bytes": batch.num_tokens * 2 * Hkv * D * 2,
         "cache_write_bytes": n_write * row,
-        "scale_bytes": 2 * Hkv * D * 4 if int8 else 0,
+        "scale_bytes": 2 * Hkv * D * 4 if quant else 0,
         "tokens": batch.num_tokens,
         "kv_tokens": int(L.sum()),
     }

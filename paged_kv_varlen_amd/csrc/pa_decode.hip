@@ -1076,9 +1076,9 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ != 0)) void decode_kerne
       CodeRegs4<D> cr;
       const int sh = 4 * (n & 1);  // this lane's nibble of a V byte
       auto v_block = [&](int blk) __attribute__((always_inline)) {
-        const uint32_t* b = &cr.v[4 * blk];
-        const typename E::x2 a = E::from_nibble_pair(((b[0] >> sh) & 15u) | (((b[1] >> sh) & 15u) << 16));
-        const typename E::x2 c = E::from_nibble_pair(((b[2] >> sh) & 15u) | (((b[3] >> sh) & 15u) << 16));
+        const uint32_t* b = &cr.v[4 * blk];  // keys j = 0..3, one byte each
+        const typename E::x2 a = E::from_nibble_bytes(__builtin_amdgcn_perm(b[1], b[0], 0x0c040c00u), sh);
+        const typename E::x2 c = E::from_nibble_bytes(__builtin_amdgcn_perm(b[3], b[2], 0x0c040c00u), sh);
         vx[blk] = typename E::x4{a[0], a[1], c[0], c[1]};
       };
       cr.template read<S * SLOT>(ka, vb);

@@ -70,22 +70,29 @@ struct Elem<false> {  // IEEE binary16
     const x2 bias = {static_cast<_Float16>(1152.f), static_cast<_Float16>(1152.f)};
     return __builtin_bit_cast(x2, (w ^ 0x00800080u) + 0x64006400u) - bias;
   }
-  // two int4 codes (4-bit two's complement, zero-extended into the 16-bit
-  // halves of w) as values: the half 1024 + (u ^ 8), minus 1032
-  static __device__ inline x2 from_nibble_pair(uint32_t w) {
+  // int4 codes as values: a 4-bit two's complement code c, its top bit
+  // flipped, is c + 8 in [0, 15]; placed under the exponent of 1024 it gives
+  // the half 1024 + c + 8, and 1032 is subtracted (exact)
+  static __device__ inline x2 minus_1032(uint32_t h) {
     const x2 bias = {static_cast<_Float16>(1032.f), static_cast<_Float16>(1032.f)};
-    return __builtin_bit_cast(x2, (w ^ 0x00080008u) + 0x64006400u) - bias;
+    return __builtin_bit_cast(x2, h | 0x64006400u) - bias;
+  }
+  // the codes in the nibbles at bit sh of the two bytes that sit (zero-extended)
+  // in the 16-bit halves of w
+  static __device__ inline x2 from_nibble_bytes(uint32_t w, int sh) {
+    return minus_1032(((w ^ 0x00880088u) >> sh) & 0x000F000Fu);
   }
   // eight int4 codes (nibble e of w is code e) as values: the even codes (low
   // nibbles) and odd ones (high nibbles) of each byte are paired by v_perm_b32
   static __device__ inline x8 from_nibbles8(uint32_t w) {
-    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    const uint32_t u = w ^ 0x88888888u;
+    const uint32_t lo = u & 0x0F0F0F0Fu, hi = (u >> 4) & 0x0F0F0F0Fu;
     const uint32_t h[4] = {__builtin_amdgcn_perm(hi, lo, 0x0c040c00u), __builtin_amdgcn_perm(hi, lo, 0x0c050c01u),
                            __builtin_amdgcn_perm(hi, lo, 0x0c060c02u), __builtin_amdgcn_perm(hi, lo, 0x0c070c03u)};
     x8 r;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const x2 v = from_nibble_pair(h[k]);
+      const x2 v = minus_1032(h[k]);
       r[2 * k] = v[0];
       r[2 * k + 1] = v[1];
     }
@@ -132,11 +139,13 @@ struct Elem<true> {  // bfloat16: the upper half of a binary32
     return x2{static_cast<__bf16>(static_cast<float>(u & 0xffu) - 128.f),
               static_cast<__bf16>(static_cast<float>((u >> 16) & 0xffu) - 128.f)};
   }
-  // two int4 codes (4-bit two's complement, zero-extended into the 16-bit
-  // halves of w) as values
-  static __device__ inline x2 from_nibble_pair(uint32_t w) {
-    return x2{static_cast<__bf16>(static_cast<float>(static_cast<int>(w << 28) >> 28)),
-              static_cast<__bf16>(static_cast<float>(static_cast<int>(w << 12) >> 28))};
+  // the codes in the nibbles at bit sh of the two bytes that sit (zero-extended)
+  // in the 16-bit halves of w
+  static __device__ inline x2 from_nibble_bytes(uint32_t w, int sh) {
+    // (the builtin's result type is unsigned: the sign-extended field is read back as int)
+    const int c0 = static_cast<int>(__builtin_amdgcn_sbfe(w, sh, 4));
+    const int c1 = static_cast<int>(__builtin_amdgcn_sbfe(w, 16 + sh, 4));
+    return x2{static_cast<__bf16>(static_cast<float>(c0)), static_cast<__bf16>(static_cast<float>(c1))};
   }
   // eight int4 codes (nibble e of w is code e) as values
   static __device__ inline x8 from_nibbles8(uint32_t w) {

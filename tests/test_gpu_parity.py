@@ -645,3 +645,20 @@ def test_quant_state_and_determinism(kvq):
     e_l = np.max(np.abs(l32[rows].astype(np.float64) - rlse[rows]))
     say(f"      state: max|err| out_f32 {e_o:.3e}, lse {e_l:.3e}")
     assert e_o <= TOL and e_l <= LSE_TOL
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_int4_every_nibble_value(dtype):
+    # INT4 caches may hold any nibble, -8 included (the quantizer never writes
+    # it, a cache filled elsewhere may): uniformly random bytes in every slot.
+    # Uniform codes spread about 3 times wider than the recipe's, so the
+    # scales are a quarter of the recipe's to keep the data O(1), as the bar
+    # assumes.
+    b = W.make_batch([1, 40, 1, 9], [300, 70, 2000, 5], num_heads=8, kv_num_heads=2, head_size=128,
+                     block_size=16, seed=560, name="int4_nibbles", dtype=dtype, kv_quant="int4")
+    rng = np.random.default_rng(561)
+    for cache in (b.key_cache, b.value_cache):
+        cache[...] = rng.integers(0, 256, cache.shape, dtype=np.uint8)
+    b.k_scale *= np.float32(0.25)
+    b.v_scale *= np.float32(0.25)
+    check(b)

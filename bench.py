@@ -143,7 +143,7 @@ class Runner:
         self.kc, self.vc = to(batch.key_cache), to(batch.value_cache)
         self.cum, self.past = to(batch.cum), to(batch.past)
         self.table, self.slots = to(batch.block_table), to(batch.slot_mapping)
-        self.ks, self.vs = to(batch.k_scale), to(batch.v_scale)  # INT8 caches only
+        self.ks, self.vs = to(batch.k_scale), to(batch.v_scale)  # quantized caches only
         D = batch.head_size
         self.out = torch.empty((batch.num_tokens, batch.num_heads * D), dtype=self.q.dtype,
                                device=dev)

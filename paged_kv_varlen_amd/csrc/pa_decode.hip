@@ -35,6 +35,13 @@
 //   O^T[d][head] += V^T P^T     8 x v_mfma_f32_16x16x16_{f16,bf16}
 // P^T is the S^T accumulator itself (lane = head + 16 * key group); the V^T
 // operand comes from the transposing LDS read ds_read_b64_tr_b16.
+//
+// INT8 / INT4 caches (codes with per-(kv head, channel) scales): the slot holds
+// code rows (and, with a piece's first tile, the kv head's two scale rows);
+// the K fragments and V^T columns are read as code bytes and converted to the
+// data type in registers (exact), the query is scaled by the K scales once per
+// piece and the output by the V scales at its write.  The smaller slots let a
+// workgroup run twice the waves.
 #include <utility>
 
 #include "pa_elem.h"
@@ -801,8 +808,8 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ != 0)) void decode_kerne
     src_off[j] = static_cast<uint32_t>(kj * slot_bytes + (LBK == 16 ? 16 * c : o % ROWC));
   }
   const int qchunk = (lane % CPR) * 8;
-  // MFMA operand addresses of ring slot 0 (slot s adds s * SLOT); INT8
-  // caches: addresses of the code reads (CodeRegs) in ka and vb
+  // MFMA operand addresses of ring slot 0 (slot s adds s * SLOT); quantized
+  // caches: addresses of the code reads (CodeRegs, CodeRegs4) in ka and vb
   const int n = lane & 15, g = lane >> 4;
   const uint32_t ring0 = uniform(static_cast<int>(lds_addr(&ring[wave][0][0])));
   uint32_t ka[KS], va[QNT ? 1 : DB], vb[4], qa[KS];
@@ -1013,7 +1020,7 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ != 0)) void decode_kerne
   f32x4_t acc[DB];
 #pragma unroll
   for (int blk = 0; blk < DB; ++blk) acc[blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // INT8 caches: the v scale of each output value of this lane (d = 16 blk +
+  // quantized caches: the v scale of each output value of this lane (d = 16 blk +
   // 4 g + e), read with the piece's first tile
   f32x4_t vsc[QNT ? DB : 1];
 #pragma unroll

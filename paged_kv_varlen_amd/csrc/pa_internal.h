@@ -155,7 +155,7 @@ struct ScatterPlanParams {
   int32_t decode_units;        // units per sequence (Hkv * head chunks)
   int32_t decode_waves;        // W
   int32_t prefill_positions;   // query positions per prefill half-tile
-  const float* k_scale;        // [Hkv, D] with INT8 caches, else null
+  const float* k_scale;        // [Hkv, D] with INT8 / INT4 caches, else null
   const float* v_scale;
   int32_t kq;                  // caches hold codes: 8 (INT8), 4 (INT4), else 0
   int32_t bf16;                // step rows are bf16 (else fp16)
@@ -189,7 +189,7 @@ struct AttnParams {
   float scale_log2;            // scale * log2(e)
   float* lse_out;              // [N, H] natural-log lse, or null
   float* out_f32;              // [N, H*D] output before rounding, or null
-  const float* k_scale;        // [Hkv, D] with INT8 caches (codes), else null
+  const float* k_scale;        // [Hkv, D] with INT8 / INT4 caches (codes), else null
   const float* v_scale;
 };
 

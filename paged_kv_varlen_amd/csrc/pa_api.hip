@@ -274,8 +274,15 @@ pa_status pa_paged_attention(const pa_args* a, void* stream) {
   sp.max_blocks = r.MB;
   sp.block_size = r.bs;
   sp.row_elems = r.Hkv * r.D;
-  sp.decode_units = r.Hkv * decode_head_chunks(r.G);
-  sp.decode_waves = w.decode_waves;
+  // INT4 rows under 128 bytes (head size 128: 64 bytes) are half a memory line:
+  // waves 2v and 2v+1 then stream the same tiles of units 2u and 2u+1 (adjacent
+  // kv heads, or head chunks of one kv head), so both halves of a line are read
+  // by one compute unit at nearly the same time; the plan sees the pairs
+  const int units = r.Hkv * decode_head_chunks(r.G);
+  const int pair =
+      r.kq == 4 && cache_row_bytes(r.D, r.kq) < 128 && units % 2 == 0 && w.decode_waves % 2 == 0 ? 2 : 1;
+  sp.decode_units = units / pair;
+  sp.decode_waves = w.decode_waves / pair;
   sp.prefill_positions = prefill_positions(r.G);
   sp.kq = r.kq;
   sp.bf16 = a->dtype == PA_DTYPE_BF16 ? 1 : 0;
@@ -307,8 +314,9 @@ pa_status pa_paged_attention(const pa_args* a, void* stream) {
   ap.group = r.G;
   ap.max_blocks = r.MB;
   ap.block_size = r.bs;
-  ap.decode_units = sp.decode_units;
+  ap.decode_units = units;
   ap.decode_waves = w.decode_waves;
+  ap.decode_pair = pair;
   ap.prefill_positions = prefill_positions(r.G);
   ap.scale_log2 = r.scale * 1.4426950408889634f;
   ap.lse_out = a->lse;

@@ -778,13 +778,17 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ != 0)) void decode_kerne
   if (w >= W) return;
 
   // ---- this wave's share ---------------------------------------------------
-  const int* rec = p.dec_start + 8 * w;
+  // paired waves (INT4 rows under a memory line): wave pair vw streams the
+  // tiles of unit pairs, wave 2vw taking units 2u, wave 2vw+1 units 2u+1
+  const int PF = p.decode_pair;
+  const int vw = w / PF, par = w % PF;
+  const int* rec = p.dec_start + 8 * vw;
   const int rv = rec[lane & 7];
-  const int g1 = p.dec_start[8 * (w + 1) + 3];
+  const int g1 = p.dec_start[8 * (vw + 1) + 3];
   const int g0 = uniform(__builtin_amdgcn_readlane(rv, 3));
   if (g0 >= g1) return;
   const int Bd = p.ws_ctrl[kCtrlDecodeSeqs];
-  const int U = p.decode_units;
+  const int U = p.decode_units / PF;  // units (pairs) per sequence in the tile order
   const int hcc = decode_head_chunks(p.group);
   const int G = p.group;
   const int bs = p.block_size;
@@ -856,7 +860,7 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ != 0)) void decode_kerne
   int L_i = uniform(__builtin_amdgcn_readlane(rv, 6));
   int P_i = uniform(__builtin_amdgcn_readlane(rv, 7));
   int n_i = (L_i + kDecodeTile - 1) / kDecodeTile;
-  int kvh_i = u_i / hcc, hc_i = u_i % hcc;
+  int kvh_i = (PF * u_i + par) / hcc, hc_i = (PF * u_i + par) % hcc;  // of the actual unit
   int pi = i_i / tpp, ip = i_i % tpp;  // page of the tile and tile within the page
   int g_i = g0;
   // per-segment values
@@ -987,13 +991,8 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ != 0)) void decode_kerne
         pi = 0;
         ip = 0;
         ++u_i;
-        if (++hc_i == hcc) {
-          hc_i = 0;
-          ++kvh_i;
-        }
         if (u_i == U) {
           u_i = 0;
-          kvh_i = 0;
           ++d_i;
           ensure_nseq();
           b_i = ns_b;
@@ -1003,6 +1002,8 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ != 0)) void decode_kerne
           n_i = (L_i + kDecodeTile - 1) / kDecodeTile;
           issue_nseq(d_i + 1);
         }
+        kvh_i = (PF * u_i + par) / hcc;
+        hc_i = (PF * u_i + par) % hcc;
         enter_segment();
       }
     } else if (++ip == tpp) {  // next page

@@ -152,8 +152,8 @@ struct ScatterPlanParams {
   int32_t max_blocks;
   int32_t block_size;
   int32_t row_elems;           // Hkv * D
-  int32_t decode_units;        // units per sequence (Hkv * head chunks)
-  int32_t decode_waves;        // W
+  int32_t decode_units;        // units per sequence (Hkv * head chunks; unit pairs when paired)
+  int32_t decode_waves;        // W (wave pairs when paired)
   int32_t prefill_positions;   // query positions per prefill half-tile
   const float* k_scale;        // [Hkv, D] with INT8 / INT4 caches, else null
   const float* v_scale;
@@ -185,6 +185,9 @@ struct AttnParams {
   int32_t block_size;
   int32_t decode_units;        // units per sequence
   int32_t decode_waves;        // W
+  // 2: waves 2v and 2v+1 stream the same tiles of units 2u and 2u+1 (the plan
+  // sees unit pairs and wave pairs); 1: one unit per wave
+  int32_t decode_pair;
   int32_t prefill_positions;
   float scale_log2;            // scale * log2(e)
   float* lse_out;              // [N, H] natural-log lse, or null

@@ -33,8 +33,11 @@ __device__ inline void merge_segment(const AttnParams& p, int task, int T, int l
   const int U = p.decode_units;
   const int u = task % U;
   const int n = (L + kDecodeTile - 1) / kDecodeTile;
-  const int W = p.decode_waves;
-  const int S = tile0 + u * n;
+  // paired waves: the tile order and the wave ranges are over unit pairs and
+  // wave pairs; unit u's pieces are in the waves of its parity
+  const int PF = p.decode_pair, par = u % PF;
+  const int W = p.decode_waves / PF;
+  const int S = tile0 + (u / PF) * n;
   const int wf = decode_wave_of(S, T, W), wl = decode_wave_of(S + n - 1, T, W);
   if (wf == wl) return;  // written whole by its wave
   const int first_k = decode_wave_begin(wf, T, W) < S ? 1 : 0;
@@ -51,7 +54,7 @@ __device__ inline void merge_segment(const AttnParams& p, int task, int T, int l
   };
   // partial slot of wave v's piece: the first piece in wf's second slot when
   // the segment starts inside wf's range, every other in the wave's first
-  auto slot_of_piece = [&](int v) { return 2 * v + (v == wf ? first_k : 0); };
+  auto slot_of_piece = [&](int v) { return 2 * (PF * v + par) + (v == wf ? first_k : 0); };
   const float* lse_base = p.part_lse + hn;
   const float* o_base = p.part_o + hn * D + E * qd;
   // Pieces are combined in wave order with weights 2^(lse - M), M the

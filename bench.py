@@ -356,7 +356,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path has no multi-GPU mode in this build)", file=sys.stderr)
+              "(the library runs on one GPU; the design notes say how it would shard)", file=sys.stderr)
         sys.exit(2)
 
     if args.mfma_rate:

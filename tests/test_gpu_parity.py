@@ -662,3 +662,39 @@ def test_int4_every_nibble_value(dtype):
     b.k_scale *= np.float32(0.25)
     b.v_scale *= np.float32(0.25)
     check(b)
+
+
+@pytest.mark.parametrize("kvq", QUANT)
+@pytest.mark.parametrize("H,Hkv", [(8, 1), (12, 3), (40, 5)])
+def test_quant_odd_unit_counts(H, Hkv, kvq):
+    # an odd number of units per sequence (1, 3, 5 kv heads): INT4 at head size
+    # 128 cannot pair units across waves then and streams one unit per wave
+    b = W.make_batch([1, 1, 23, 1], [900, 4000, 60, 17], num_heads=H, kv_num_heads=Hkv, head_size=128,
+                     block_size=32, seed=570 + Hkv, name=f"{kvq}_odd{Hkv}", kv_quant=kvq)
+    check(b)
+
+
+@pytest.mark.parametrize("kvq", QUANT)
+def test_quant_hip_graph_replay(kvq):
+    b = W.make_batch([1, 1, 300, 1, 64], [900, 5000, 40, 7, 3000], num_heads=16, kv_num_heads=4,
+                     head_size=128, block_size=16, seed=580, name=f"{kvq}_graph", kv_quant=kvq)
+    d = DevBatch(b)
+    ref = d.run().clone()
+    torch.cuda.synchronize()
+    ws = torch.empty(1 << 27, dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        d.run(output=out, workspace=ws, stream=s)
+        s.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            d.run(output=out, workspace=ws, stream=s)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))

@@ -36,4 +36,5 @@ from .paged_attention import (  # noqa: F401
     pack_int4,
     unpack_int4,
     dequantize,
+    output_gate,
 )

@@ -223,10 +223,22 @@ def attend_sequence(Qb: np.ndarray, Kb: np.ndarray, Vb: np.ndarray, past_b: int,
     return (out, lse) if with_lse else out
 
 
+def output_gate(out: np.ndarray, gate: np.ndarray) -> np.ndarray:
+    """The attention output times sigmoid(gate), elementwise, in fp64.
+
+    "Add Qwen3.8 packed hybrid PagedAttention export for ORT GenAI Engine",
+    Per-layer behavior (Full attention): the doubled Q projection is split per
+    head into the query and an output gate, and sigmoid(gate) is applied to
+    the attention output; read plainly, the gate has the output's shape
+    [N, H*D] and sigmoid(g) = 1 / (1 + exp(-g)) multiplies each element."""
+    g = values(gate)
+    return out * (1.0 / (1.0 + np.exp(-g)))
+
+
 def paged_attention(query, key, value, key_cache, value_cache, cum, past, block_table,
                     slot_mapping=None, *, num_heads: int, kv_num_heads: int,
                     scale: float = 0.0, is_causal: int = 1, rows=None, with_lse: bool = False,
-                    k_scale=None, v_scale=None):
+                    k_scale=None, v_scale=None, gate=None):
     """The whole operator: returns (output fp64 [N, H*D], key_cache', value_cache').
 
     README, Description/Outputs: the caches are updated (here: copies are
@@ -238,6 +250,8 @@ def paged_attention(query, key, value, key_cache, value_cache, cum, past, block_
     neither): the caches hold codes, INT8 (int8 caches) or INT4 (uint8
     caches, [NB, bs, Hkv, D/2], two codes per byte); the step's rows are
     quantized on write and every cached element reads as code * scale.
+    ``gate`` ([N, H*D] in the data type): the returned output is
+    output_gate(attention, gate); the lse (the row's state) is unchanged.
     """
     if (k_scale is None) != (v_scale is None):
         raise ValueError("k_scale and v_scale go together")
@@ -273,9 +287,12 @@ def paged_attention(query, key, value, key_cache, value_cache, cum, past, block_
                                                      with_lse=True)
         else:
             out[t0:t1] = attend_sequence(Qb, Kb, Vb, int(past[b]), s, rows=local)
+    out = out.reshape(N, num_heads * D)
+    if gate is not None:
+        out = output_gate(out, gate)
     if with_lse:
-        return out.reshape(N, num_heads * D), kc, vc, lse
-    return out.reshape(N, num_heads * D), kc, vc
+        return out, kc, vc, lse
+    return out, kc, vc
 
 
 def partial_state(q_row: np.ndarray, Kk: np.ndarray, Vk: np.ndarray, scale: float,

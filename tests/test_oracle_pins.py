@@ -959,3 +959,55 @@ def test_int4_pins_catch_oracle_mistakes():
                 check_Q6(oracle.paged_attention)
         finally:
             setattr(pa_mod, name, saved)
+
+
+# ------------------------------------------------------------------ output gate
+
+# sigmoid(gate) on the attention output.  Pins:
+#   G1  gate 0 halves the output exactly (sigmoid(0) = 1/2);
+#   G2  gates g and -g sum to the ungated output (sigmoid(g) + sigmoid(-g) = 1);
+#   G3  the gated output equals the ungated one times scipy.special.expit of
+#       the gate values;
+#   G4  a gate of +20 leaves the output within 1e-8, -20 brings it within 1e-8
+#       of zero; the lse is the ungated one in every case.
+
+def check_G(fn):
+    import scipy.special
+    b = small(seed=41)
+    o0, _, _, l0 = call(fn, b, with_lse=True)
+    zero = np.zeros((b.num_tokens, b.num_heads * b.head_size), dtype=np.float16)
+    o, _, _, l = call(fn, b, with_lse=True, gate=zero)
+    assert np.array_equal(o, 0.5 * o0) and np.array_equal(l, l0)              # G1
+    g = W.output_gate_input(b, 42)
+    op, _, _ = call(fn, b, gate=g)
+    om, _, _ = call(fn, b, gate=(-g.astype(np.float32)).astype(np.float16))
+    assert np.max(np.abs(op + om - o0)) < 1e-12                               # G2
+    assert np.max(np.abs(op - o0 * scipy.special.expit(g.astype(np.float64)))) < 1e-12  # G3
+    big = np.full_like(zero, 20.0)
+    oh, _, _ = call(fn, b, gate=big)
+    ol, _, _ = call(fn, b, gate=-big)
+    assert np.max(np.abs(oh - o0)) < 1e-8 * max(1.0, np.max(np.abs(o0)))     # G4
+    assert np.max(np.abs(ol)) < 1e-8 * max(1.0, np.max(np.abs(o0)))
+    gb = W.output_gate_input(small(seed=43, dtype="bf16"), 44)
+    bb = small(seed=43, dtype="bf16")
+    ob0, _, _ = call(fn, bb)
+    ob, _, _ = call(fn, bb, gate=gb)
+    assert np.max(np.abs(ob - ob0 * scipy.special.expit(oracle.values(gb)))) < 1e-12  # G3, bf16 gate
+
+
+def test_oracle_gate_pins():
+    check_G(oracle.paged_attention)
+
+
+@pytest.mark.parametrize("which", ["sign", "exp", "tanh"])
+def test_gate_pins_catch_planted_mistakes(which):
+    wrong = {"sign": lambda out, gate: out / (1.0 + np.exp(oracle.values(gate))),
+             "exp": lambda out, gate: out * np.exp(-oracle.values(gate)),
+             "tanh": lambda out, gate: out * np.tanh(oracle.values(gate))}[which]
+    saved = pa_mod.output_gate
+    pa_mod.output_gate = wrong
+    try:
+        with pytest.raises(AssertionError):
+            check_G(oracle.paged_attention)
+    finally:
+        pa_mod.output_gate = saved

@@ -456,6 +456,14 @@ def workload(name: str, seed: int = 0, meta_only: bool = False, dtype: str = "f1
     return WORKLOADS[name](seed, meta_only, dtype, head_size, kv_quant)
 
 
+def output_gate_input(batch: "Batch", seed: int) -> np.ndarray:
+    """An output-gate tensor [N, H*D] for the batch: N(0,1) in the batch's data
+    type (its own seeded stream, so the batch's other draws do not move)."""
+    rng = np.random.default_rng(seed)
+    normal = {"f16": normal_f16, "bf16": normal_bf16}[batch.dtype]
+    return normal(rng, (batch.num_tokens, batch.num_heads * batch.head_size))
+
+
 # ---------------------------------------------------------------------------
 # algorithmic work of a call (what a roofline is measured against)
 # ---------------------------------------------------------------------------

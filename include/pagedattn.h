@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 3
+#define PA_ABI_VERSION 4
 
 /* Result codes.  Every host-checkable fault returns one of these before any
  * device work is enqueued (typed errors, as the acceptance criteria of "Add
@@ -192,6 +192,14 @@ typedef struct pa_args {
   int32_t reserved;              /* 0                                      */
   const float *k_scale;
   const float *v_scale;
+
+  /* Optional output gate, T [num_tokens, num_heads*head_size], 16-byte
+   * aligned, or NULL.  The Qwen3.8 export issue (Per-layer behavior, Full
+   * attention) splits the doubled Q projection per head into the query and an
+   * output gate and applies sigmoid(gate) to the attention output; with a
+   * gate, output = round(attention * sigmoid(gate)) elementwise, fused into
+   * the final write.  lse and output_f32 stay the ungated state. */
+  const void *gate;
 } pa_args;
 
 /* Kernels launched by one call, in launch order (indices into kernel_events). */

@@ -33,7 +33,7 @@ PA_DTYPE_BF16 = 2
 PA_KV_SAME, PA_KV_INT8, PA_KV_INT4 = 0, 1, 2
 _CODE_DTYPES = {torch.int8: PA_KV_INT8, torch.uint8: PA_KV_INT4}  # cache dtype -> kv_quant
 _DTYPE_CODES = {torch.float16: PA_DTYPE_F16, torch.bfloat16: PA_DTYPE_BF16}
-ABI_VERSION = 3
+ABI_VERSION = 4
 KERNELS = ("scatter_plan", "decode", "merge", "prefill")  # enum pa_kernel order
 STATUS = {
     0: "PA_OK", 1: "PA_ERR_NULL_ARG", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED",
@@ -79,6 +79,7 @@ class PaArgs(ctypes.Structure):
         ("reserved", ctypes.c_int32),
         ("k_scale", ctypes.c_void_p),
         ("v_scale", ctypes.c_void_p),
+        ("gate", ctypes.c_void_p),
     ]
 
 
@@ -155,7 +156,8 @@ def make_args(query, key, value, key_cache, value_cache, cumulative_sequence_len
               kv_num_heads: int, scale: float = 0.0, is_causal: int = 1,
               workspace: Optional[torch.Tensor] = None,
               k_scale: Optional[torch.Tensor] = None,
-              v_scale: Optional[torch.Tensor] = None) -> PaArgs:
+              v_scale: Optional[torch.Tensor] = None,
+              gate: Optional[torch.Tensor] = None) -> PaArgs:
     """Fill a PaArgs from tensors (no checks beyond what marshalling needs:
     the library validates shapes, dtypes and alignment itself).  int8 (INT8)
     or uint8 (INT4, two codes per byte) caches with fp32 ``k_scale``/``v_scale``
@@ -187,6 +189,9 @@ def make_args(query, key, value, key_cache, value_cache, cumulative_sequence_len
         a.kv_quant = kv_quant
         a.k_scale = _ptr(k_scale)
         a.v_scale = _ptr(v_scale)
+    if gate is not None and (gate.dtype != query.dtype or not gate.is_contiguous()):
+        raise ValueError("gate must be a contiguous tensor of the query's dtype")
+    a.gate = _ptr(gate)
     a.query = _ptr(query)
     a.key = _ptr(key)
     a.value = _ptr(value)
@@ -239,7 +244,8 @@ def paged_attention(query: torch.Tensor, key: Optional[torch.Tensor],
                     lse: Optional[torch.Tensor] = None,
                     output_f32: Optional[torch.Tensor] = None,
                     k_scale: Optional[torch.Tensor] = None,
-                    v_scale: Optional[torch.Tensor] = None):
+                    v_scale: Optional[torch.Tensor] = None,
+                    gate: Optional[torch.Tensor] = None):
     """Scatter the step's K/V into the caches (in place) and return the
     attention output [num_tokens, num_heads * head_size].
 
@@ -255,7 +261,11 @@ def paged_attention(query: torch.Tensor, key: Optional[torch.Tensor],
     INT8 caches: int8 ``key_cache``/``value_cache`` with fp32 ``k_scale`` and
     ``v_scale`` [kv_num_heads, head_size] (per-channel scales).  INT4 caches:
     uint8 [num_blocks, block_size, kv_num_heads, head_size / 2], two codes per
-    byte (the even element in bits 0-3), with the same scales."""
+    byte (the even element in bits 0-3), with the same scales.
+
+    ``gate``: optional [num_tokens, num_heads * head_size] tensor of the
+    query's dtype; the output is then the attention times sigmoid(gate),
+    rounded once (``lse`` and ``output_f32`` stay ungated)."""
     lib = library()
     dev = query.device
     if dev.type != "cuda":
@@ -268,7 +278,7 @@ def paged_attention(query: torch.Tensor, key: Optional[torch.Tensor],
     args = make_args(query, key, value, key_cache, value_cache, cumulative_sequence_length,
                      past_seqlens, block_table, slot_mapping, output, num_heads=num_heads,
                      kv_num_heads=kv_num_heads, scale=scale, is_causal=is_causal,
-                     k_scale=k_scale, v_scale=v_scale)
+                     k_scale=k_scale, v_scale=v_scale, gate=gate)
     if return_lse and lse is None:
         lse = torch.empty((query.shape[0], num_heads), dtype=torch.float32, device=dev)
     for name, t in (("lse", lse), ("output_f32", output_f32)):

@@ -221,7 +221,7 @@ pa_status pa_paged_attention(const pa_args* a, void* stream) {
       !aligned16(a->key_cache) || !aligned16(a->value_cache) || !aligned16(a->output) ||
       !aligned4(a->cumulative_sequence_length) || !aligned4(a->past_seqlens) ||
       !aligned4(a->block_table) || !aligned4(a->slot_mapping) || !aligned16(a->workspace) ||
-      !aligned4(a->lse) || !aligned16(a->output_f32))
+      !aligned4(a->lse) || !aligned16(a->output_f32) || !aligned16(a->gate))
     return PA_ERR_ALIGNMENT;
   if (r.kq != 0) {
     if (a->k_scale == nullptr || a->v_scale == nullptr) return PA_ERR_NULL_ARG;
@@ -323,6 +323,7 @@ pa_status pa_paged_attention(const pa_args* a, void* stream) {
   ap.k_scale = sp.k_scale;
   ap.v_scale = sp.v_scale;
   ap.out_f32 = a->output_f32;
+  ap.gate = static_cast<const uint16_t*>(a->gate);
 
   const int cus = device_cus();
   mark(PA_KERNEL_DECODE, 0);

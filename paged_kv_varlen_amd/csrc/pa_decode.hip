@@ -1171,11 +1171,18 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ != 0)) void decode_kerne
         if (n < nh_c) {
           const int64_t row = static_cast<int64_t>(t_c) * p.num_heads + h0_c + n;
           uint16_t* o = p.out + row * D + 4 * g;
+          const uint16_t* gt = p.gate == nullptr ? nullptr : p.gate + row * D + 4 * g;  // output gate
 #pragma unroll
           for (int blk = 0; blk < DB; ++blk) {
+            f32x4_t sg = {1.f, 1.f, 1.f, 1.f};
+            if (gt != nullptr) {
+              const uint2 gw = *reinterpret_cast<const uint2*>(gt + 16 * blk);
+              sg = f32x4_t{gate_sigmoid(E::value(gw.x & 0xffffu)), gate_sigmoid(E::value(gw.x >> 16)),
+                           gate_sigmoid(E::value(gw.y & 0xffffu)), gate_sigmoid(E::value(gw.y >> 16))};
+            }
             typename E::x4 hv;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) hv[e] = E::round(acc[blk][e] * inv * vsc[QNT ? blk : 0][e]);
+            for (int e = 0; e < 4; ++e) hv[e] = E::round(acc[blk][e] * inv * vsc[QNT ? blk : 0][e] * sg[e]);
             *reinterpret_cast<typename E::x4*>(o + 16 * blk) = hv;
           }
           // optional partial state: fp32 output and natural-log lse

@@ -45,6 +45,7 @@ struct Elem<false> {  // IEEE binary16
   }
   static __device__ inline T round(float x) { return static_cast<_Float16>(x); }
   static __device__ inline uint16_t bits(float x) { return __builtin_bit_cast(uint16_t, round(x)); }
+  static __device__ inline float value(uint16_t b) { return static_cast<float>(__builtin_bit_cast(_Float16, b)); }
   // eight int8 codes (byte k of {w0, w1} is code k) as values, exactly: the
   // byte u = code + 128 becomes the low mantissa byte of the half 1024 + u
   // (v_perm_b32 puts it beside the high byte 0x64), and 1152 is subtracted
@@ -124,6 +125,7 @@ struct Elem<true> {  // bfloat16: the upper half of a binary32
   // round to nearest, ties to even (v_cvt_pk_bf16_f32)
   static __device__ inline T round(float x) { return static_cast<__bf16>(x); }
   static __device__ inline uint16_t bits(float x) { return __builtin_bit_cast(uint16_t, round(x)); }
+  static __device__ inline float value(uint16_t b) { return __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16); }
   // eight int8 codes (byte k of {w0, w1} is code k) as values, exactly
   // (integers up to 127 in magnitude fit the 8-bit significand)
   static __device__ inline x8 from_codes(uint32_t w0, uint32_t w1) {

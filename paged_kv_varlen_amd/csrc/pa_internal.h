@@ -194,6 +194,7 @@ struct AttnParams {
   float* out_f32;              // [N, H*D] output before rounding, or null
   const float* k_scale;        // [Hkv, D] with INT8 / INT4 caches (codes), else null
   const float* v_scale;
+  const uint16_t* gate;        // [N, H*D] output gate (sigmoid applied at the final write), or null
 };
 
 // fixed-order merge of partial states (pa_merge_states)
@@ -208,6 +209,12 @@ struct MergeStatesParams {
   int32_t head_size;
   int32_t bf16;                // output type: 0 fp16, 1 bf16
 };
+
+// sigmoid(g) = 1 / (1 + e^-g) in fp32 for the output gate (hardware exp2 and
+// reciprocal; about 1e-7 relative)
+__device__ inline float gate_sigmoid(float g) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
+}
 
 // ---- launchers (defined in the .hip files) ---------------------------------
 hipError_t launch_scatter_plan(const ScatterPlanParams& p, hipStream_t s);

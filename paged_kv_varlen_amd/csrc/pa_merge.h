@@ -119,13 +119,22 @@ __device__ inline void merge_segment(const AttnParams& p, int task, int T, int l
   }
   if (p.lse_out != nullptr && qd == 0) p.lse_out[row] = (M + __log2f(wsum)) * 0.6931471805599453f;
   uint16_t* out = p.out + row * D + E * qd;
+  const uint16_t* gt = p.gate == nullptr ? nullptr : p.gate + row * D + E * qd;  // output gate
 #pragma unroll
   for (int e = 0; e < E; e += 4) {
+    float sg[4] = {1.f, 1.f, 1.f, 1.f};
+    if (gt != nullptr) {
+      const uint2 gw = *reinterpret_cast<const uint2*>(gt + e);
+      sg[0] = gate_sigmoid(Elem<BF16>::value(gw.x & 0xffffu));
+      sg[1] = gate_sigmoid(Elem<BF16>::value(gw.x >> 16));
+      sg[2] = gate_sigmoid(Elem<BF16>::value(gw.y & 0xffffu));
+      sg[3] = gate_sigmoid(Elem<BF16>::value(gw.y >> 16));
+    }
     uint32_t w2[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      w2[c] = static_cast<uint32_t>(Elem<BF16>::bits(o[e + 2 * c] * inv)) |
-              (static_cast<uint32_t>(Elem<BF16>::bits(o[e + 2 * c + 1] * inv)) << 16);
+      w2[c] = static_cast<uint32_t>(Elem<BF16>::bits(o[e + 2 * c] * inv * sg[2 * c])) |
+              (static_cast<uint32_t>(Elem<BF16>::bits(o[e + 2 * c + 1] * inv * sg[2 * c + 1])) << 16);
     }
     *reinterpret_cast<uint2*>(out + e) = make_uint2(w2[0], w2[1]);
   }

@@ -729,10 +729,20 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
               v[2] *= vs.z;
               v[3] *= vs.w;
             }
+            float sg[4] = {1.f, 1.f, 1.f, 1.f};  // output gate (the fp32 state stays ungated)
+            if (p.gate != nullptr) {
+              const uint2 gw = *reinterpret_cast<const uint2*>(p.gate + tok * out_stride + static_cast<int64_t>(head) * D +
+                                                               32 * mt + 8 * q + 4 * lhalf);
+              sg[0] = gate_sigmoid(E::value(gw.x & 0xffffu));
+              sg[1] = gate_sigmoid(E::value(gw.x >> 16));
+              sg[2] = gate_sigmoid(E::value(gw.y & 0xffffu));
+              sg[3] = gate_sigmoid(E::value(gw.y >> 16));
+            }
             uint32_t w[2];
 #pragma unroll
             for (int e = 0; e < 2; ++e)
-              w[e] = static_cast<uint32_t>(E::bits(v[2 * e])) | (static_cast<uint32_t>(E::bits(v[2 * e + 1])) << 16);
+              w[e] = static_cast<uint32_t>(E::bits(v[2 * e] * sg[2 * e])) |
+                     (static_cast<uint32_t>(E::bits(v[2 * e + 1] * sg[2 * e + 1])) << 16);
             *reinterpret_cast<uint2*>(orow + 32 * mt + 8 * q + 4 * lhalf) = make_uint2(w[0], w[1]);
             if (orow_f != nullptr)
               *reinterpret_cast<float4*>(orow_f + 32 * mt + 8 * q + 4 * lhalf) = make_float4(v[0], v[1], v[2], v[3]);

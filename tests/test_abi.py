@@ -128,6 +128,8 @@ def test_workspace_bytes_static_bound():
     (dict(lse=FAKE + 2), ALIGN),                         # lse needs 4-byte alignment
     (dict(output_f32=FAKE + 4), ALIGN),                  # output_f32 needs 16
     (dict(lse=FAKE, output_f32=FAKE), WS),               # both present and aligned
+    (dict(gate=FAKE + 8), ALIGN),                        # the output gate needs 16-byte alignment
+    (dict(gate=FAKE), WS),                               # an aligned gate passes validation
     (dict(kv_quant=3), UNSUP),                           # only PA_KV_SAME, PA_KV_INT8, PA_KV_INT4
     (dict(kv_quant=-1), UNSUP),
     (dict(kv_quant=2, k_scale=FAKE, v_scale=FAKE), SHAPE),  # INT4 rows are head_size / 2 bytes
@@ -171,7 +173,7 @@ def test_status_strings():
     lib = pa.library()
     for s in range(9):
         assert lib.pa_status_string(s)
-    assert lib.pa_abi_version() == 3
+    assert lib.pa_abi_version() == 4
 
 
 def merge_args(**kw):

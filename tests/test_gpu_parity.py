@@ -698,3 +698,75 @@ def test_quant_hip_graph_replay(kvq):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+# ------------------------------------------------------------------ output gate: sigmoid(gate) on the output
+
+def check_gated(b: W.Batch, rows=None, seed=1):
+    gate = W.output_gate_input(b, seed)
+    say(f"[gpu] gated {b.name} {b.dtype} kv={b.kv_quant} N={b.num_tokens} B={b.batch_size} "
+        f"H={b.num_heads}/{b.kv_num_heads} D={b.head_size}")
+    d = DevBatch(b)
+    out = d.run(gate=to_dev(gate))
+    torch.cuda.synchronize()
+    ref, rkc, rvc = oracle.paged_attention(b.query, b.key, b.value, b.key_cache, b.value_cache,
+                                           b.cum, b.past, b.block_table, b.slot_mapping,
+                                           num_heads=b.num_heads, kv_num_heads=b.kv_num_heads,
+                                           scale=b.scale, rows=rows, k_scale=b.k_scale,
+                                           v_scale=b.v_scale, gate=gate)
+    assert np.array_equal(raw_bits(to_host(d.kc)), raw_bits(rkc)), "key_cache differs"
+    assert np.array_equal(raw_bits(to_host(d.vc)), raw_bits(rvc)), "value_cache differs"
+    sel = np.arange(b.num_tokens) if rows is None else rows
+    got = as_f64(to_host(out)[sel])
+    err = np.max(np.abs(got - ref[sel])) if sel.size else 0.0
+    say(f"      rows checked {sel.size}, max|err| {err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= tol(b), f"max abs error {err}"
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_gate_tiny(dtype):
+    check_gated(W.tiny(0, dtype=dtype))
+
+
+@pytest.mark.parametrize("case", range(len(SWEEP)))
+def test_gate_sweep(case):
+    q, p, H, Hkv, D, bs = SWEEP[case]
+    b = W.make_batch(q, p, num_heads=H, kv_num_heads=Hkv, head_size=D, block_size=bs,
+                     seed=600 + case, num_blocks=None, name=f"gate_sweep{case}")
+    check_gated(b, seed=case)
+
+
+def test_gate_pure_decode_full():
+    check_gated(W.pure_decode(0))  # whole segments in the decode kernel, cut ones in the merge
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_gate_long_prefill_and_mixed(dtype):
+    b = W.long_prefill(0, dtype=dtype)
+    check_gated(b, rows=sample_rows(b, per_seq=30, must=[0, 31, 32, 2047]))
+    m = W.mixed(0, dtype=dtype)
+    check_gated(m, rows=sample_rows(m, per_seq=8))
+
+
+@pytest.mark.parametrize("kvq", ["none", "int8", "int4"])
+def test_gate_head_size_256_and_quantized(kvq):
+    q, p, H, Hkv, bs = HD256[0]
+    b = W.make_batch(q, p, num_heads=H, kv_num_heads=Hkv, head_size=256, block_size=bs,
+                     seed=610, name=f"gate_hd256_{kvq}", kv_quant=kvq)
+    check_gated(b, rows=sample_rows(b, per_seq=12))
+    s = W.make_batch([1, 40, 1, 9], [3000, 70, 9000, 5], num_heads=32, kv_num_heads=8, head_size=128,
+                     block_size=16, seed=611, name=f"gate_q_{kvq}", kv_quant=kvq)
+    check_gated(s)
+
+
+def test_gate_leaves_the_state_ungated():
+    b = W.make_batch([1, 300, 1, 64], [2000, 700, 9000, 0], num_heads=16, kv_num_heads=4, head_size=128,
+                     block_size=16, seed=620, name="gate_state")
+    gate = to_dev(W.output_gate_input(b, 3))
+    d = DevBatch(b)
+    f0 = torch.empty((b.num_tokens, b.num_heads * 128), dtype=torch.float32, device=DEV)
+    f1 = torch.empty_like(f0)
+    _, l0 = d.run(return_lse=True, output_f32=f0)
+    _, l1 = d.run(return_lse=True, output_f32=f1, gate=gate)
+    torch.cuda.synchronize()
+    assert torch.equal(f0, f1) and torch.equal(l0, l1)

@@ -78,11 +78,11 @@ def counter_means(csv_path: str, symbol: str) -> dict:
     return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
 
 
-def variant_suffix(dtype="f16", head_size=0, kv_quant="none") -> str:
+def variant_suffix(dtype="f16", head_size=0, kv_quant="none", gate=False) -> str:
     """Names a workload variant in profile file names ('' for the workloads as
-    defined: fp16 data and caches, their own head size)."""
+    defined: fp16 data and caches, their own head size, no output gate)."""
     return ("" if dtype == "f16" else f"_{dtype}") + (f"_hd{head_size}" if head_size else "") + \
-        ("" if kv_quant == "none" else f"_{kv_quant}")
+        ("" if kv_quant == "none" else f"_{kv_quant}") + ("_gate" if gate else "")
 
 
 VARIANT = {"suffix": ""}  # set by main() from --dtype / --head-size / --kv-quant
@@ -129,7 +129,7 @@ def measured_traffic(kernel: str, workload: str):
 class Runner:
     """Device copies of one batch plus the preallocated output and workspace."""
 
-    def __init__(self, batch, torch, pa):
+    def __init__(self, batch, torch, pa, gate=None):
         self.torch, self.pa, self.b = torch, pa, batch
         dev = "cuda:0"
         def to(x):  # uint16 arrays hold bf16 bit patterns
@@ -144,13 +144,14 @@ class Runner:
         self.cum, self.past = to(batch.cum), to(batch.past)
         self.table, self.slots = to(batch.block_table), to(batch.slot_mapping)
         self.ks, self.vs = to(batch.k_scale), to(batch.v_scale)  # quantized caches only
+        self.gate = to(gate)  # optional output gate
         D = batch.head_size
         self.out = torch.empty((batch.num_tokens, batch.num_heads * D), dtype=self.q.dtype,
                                device=dev)
         args = pa.make_args(self.q, self.k, self.v, self.kc, self.vc, self.cum, self.past,
                             self.table, self.slots, self.out, num_heads=batch.num_heads,
                             kv_num_heads=batch.kv_num_heads, scale=batch.scale,
-                            k_scale=self.ks, v_scale=self.vs)
+                            k_scale=self.ks, v_scale=self.vs, gate=self.gate)
         self.ws = torch.empty(max(1, pa.workspace_bytes(args)), dtype=torch.uint8, device=dev)
 
     def step(self, events=None):
@@ -159,18 +160,18 @@ class Runner:
                                 self.table, self.slots, num_heads=b.num_heads,
                                 kv_num_heads=b.kv_num_heads, scale=b.scale, output=self.out,
                                 workspace=self.ws, kernel_events=events, k_scale=self.ks,
-                                v_scale=self.vs)
+                                v_scale=self.vs, gate=self.gate)
 
 
 def time_workload(name: str, steps: int, warmup: int, seed: int, torch, pa, W, dtype="f16",
-                  head_size=0, kv_quant="none"):
+                  head_size=0, kv_quant="none", gate=False):
     t_gen = time.perf_counter()
     b = W.workload(name, seed, dtype=dtype, head_size=head_size, kv_quant=kv_quant)
     work = W.work(b)
     log(f"[bench] {name}: generated in {time.perf_counter() - t_gen:.1f}s "
         f"(N={b.num_tokens}, B={b.batch_size}, KV {work['kv_hist_bytes'] / 1e9:.3f} GB, "
         f"{work['flops'] / 1e12:.3f} TFLOP)")
-    r = Runner(b, torch, pa)
+    r = Runner(b, torch, pa, W.output_gate_input(b, seed + 1) if gate else None)
     for _ in range(warmup):
         r.step()
     torch.cuda.synchronize()
@@ -333,6 +334,8 @@ def main():
                     help="cache element type: the data type, or int8 / int4 codes with "
                          "per-channel scales (history bytes then count one byte / half a byte "
                          "per element)")
+    ap.add_argument("--gate", action="store_true",
+                    help="pass an output gate: the outputs are multiplied by sigmoid(gate)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -347,7 +350,7 @@ def main():
     ap.add_argument("--no-mfma-rate", action="store_true",
                     help="skip the probe run (prefill rooflines then carry no measured ceiling)")
     args = ap.parse_args()
-    VARIANT["suffix"] = variant_suffix(args.dtype, args.head_size, args.kv_quant)
+    VARIANT["suffix"] = variant_suffix(args.dtype, args.head_size, args.kv_quant, args.gate)
 
     if args.traffic_from:
         write_traffic(args.traffic_kernel, args.workload, *args.traffic_from,
@@ -390,12 +393,13 @@ def main():
 
     b, work, ms, wall_ms, kms = time_workload(args.workload, args.steps, args.warmup, args.seed,
                                               torch, pa, W, args.dtype, args.head_size,
-                                              args.kv_quant)
+                                              args.kv_quant, args.gate)
     head = summarize(args.workload, b, work, ms, kms)
     also = []
     for name in [x for x in args.also.split(",") if x and x != args.workload]:
         ob, owork, oms, _, okms = time_workload(name, args.steps, args.warmup, args.seed, torch,
-                                                pa, W, args.dtype, args.head_size, args.kv_quant)
+                                                pa, W, args.dtype, args.head_size, args.kv_quant,
+                                                args.gate)
         entry = summarize(name, ob, owork, oms, okms)
         entry["roofline"] = roofline(name, owork, okms)
         also.append(entry)
@@ -419,6 +423,7 @@ def main():
                    "kv_num_heads": b.kv_num_heads, "head_size": b.head_size,
                    "block_size": b.block_size, "num_blocks": b.num_blocks,
                    "kv_cache": args.dtype if args.kv_quant == "none" else args.kv_quant,
+                   "output_gate": bool(args.gate),
                    "kv_hist_bytes": work["kv_hist_bytes"], "wall_ms_per_step": round(wall_ms, 5)},
         "roofline": roofline(args.workload, work, kms),
         "tokens_per_s": head["tokens_per_s"],

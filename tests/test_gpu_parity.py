@@ -250,6 +250,32 @@ def test_long_history_prefill():
     check(b, rows=sample_rows(b, per_seq=8, seed=13))
 
 
+def many_sequences(B, mixed, kv_quant="none"):
+    # B sequences of one new token each over pasts in [0, 300); with mixed, one
+    # sequence in 50 is a chunk of 2..40 new tokens and one in 37 is empty
+    rng = np.random.default_rng(14)
+    q = np.ones(B, dtype=np.int64)
+    if mixed:
+        q[::50] = rng.integers(2, 41, size=q[::50].size)
+        q[7::37] = 0
+    p = rng.integers(0, 300, size=B)
+    return W.make_batch(q, p, num_heads=8, kv_num_heads=2, head_size=128, block_size=16,
+                        seed=14, name=f"many_sequences_{B}", kv_quant=kv_quant)
+
+
+# The plan keeps up to 1024 decode records in LDS and the scatter stages up to
+# 2047 sequences' offsets in LDS for its token -> sequence search; past those
+# counts both read global memory.  1024 and 2047 are the largest staged cases,
+# 2300 sequences take both global paths.
+@pytest.mark.parametrize("B,mixed,kvq", [(1024, False, "none"), (2047, False, "none"),
+                                         (2300, True, "none"), (2300, True, "int8")])
+def test_many_sequences(B, mixed, kvq):
+    b = many_sequences(B, mixed, kvq)
+    seqs = [s for s in (0, 1, 1023, 1024, 1025, 1100, 2046, 2047, 2048, 2049, 2250, B - 1) if s < B]
+    must = np.concatenate([np.arange(b.cum[s], b.cum[s + 1]) for s in seqs])
+    check(b, rows=sample_rows(b, per_seq=4, max_seqs=300, must=must, seed=14))
+
+
 def test_deterministic_bits():
     b = W.mixed(1)
     d = DevBatch(b)

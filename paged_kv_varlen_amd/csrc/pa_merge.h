@@ -60,26 +60,13 @@ __device__ inline void merge_segment(const AttnParams& p, int task, int T, int l
   // Pieces are combined in wave order with weights 2^(lse - M), M the
   // largest lse: a pass for M, then one for the weighted sum.  Each pass
   // loads a batch of pieces before it uses any (a batch is one memory round
-  // trip, not one per piece); the sums still run in wave order.
-  constexpr int kLseBatch = 8, kOBatch = 2;
-  float M = -__builtin_huge_valf();
-  for (int v0 = wf; v0 <= wl; v0 += kLseBatch) {
-    float x[kLseBatch];
-#pragma unroll
-    for (int j = 0; j < kLseBatch; ++j) {  // (loads at a valid piece, then a select)
-      const float l = lse_base[slot_of_piece(min(v0 + j, wl)) * kDecodeUnitHeads];
-      x[j] = v0 + j <= wl && holds(v0 + j) ? l : -__builtin_huge_valf();
-    }
-#pragma unroll
-    for (int j = 0; j < kLseBatch; ++j) M = fmaxf(M, x[j]);
-  }
-  float o[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) o[e] = 0.f;
-  float wsum = 0.f;
-  for (int v0 = wf; v0 <= wl; v0 += kOBatch) {
-    float lv[kOBatch];
-    float4 x[kOBatch][E / 4];
+  // trip, not one per piece), and the first batch of the sum's loads is issued
+  // with the first lse batch, so a segment of up to kOBatch pieces costs one
+  // round trip; the sums still run in wave order.
+  constexpr int kLseBatch = 8, kOBatch = D <= 128 ? 4 : 2;
+  float lv[kOBatch];
+  float4 x[kOBatch][E / 4];
+  auto load_batch = [&](int v0) {
 #pragma unroll
     for (int j = 0; j < kOBatch; ++j) {
       const int v = v0 + j;
@@ -94,6 +81,25 @@ __device__ inline void merge_segment(const AttnParams& p, int task, int T, int l
         x[j][e] = have ? t : make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
+  };
+  load_batch(wf);
+  float M = -__builtin_huge_valf();
+  for (int v0 = wf; v0 <= wl; v0 += kLseBatch) {
+    float y[kLseBatch];
+#pragma unroll
+    for (int j = 0; j < kLseBatch; ++j) {
+      const float l = lse_base[slot_of_piece(min(v0 + j, wl)) * kDecodeUnitHeads];
+      y[j] = v0 + j <= wl && holds(v0 + j) ? l : -__builtin_huge_valf();
+    }
+#pragma unroll
+    for (int j = 0; j < kLseBatch; ++j) M = fmaxf(M, y[j]);
+  }
+  float o[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = 0.f;
+  float wsum = 0.f;
+  for (int v0 = wf; v0 <= wl; v0 += kOBatch) {
+    if (v0 != wf) load_batch(v0);
 #pragma unroll
     for (int j = 0; j < kOBatch; ++j) {
       const float wk = __builtin_amdgcn_exp2f(lv[j] - M);  // 0 for a missing piece

@@ -189,7 +189,7 @@ typedef struct pa_args {
    * aligned), the per-channel scales of the two caches; otherwise they are
    * ignored. */
   int32_t kv_quant;
-  int32_t reserved;              /* 0                                      */
+  int32_t reserved;              /* must be 0, else PA_ERR_UNSUPPORTED      */
   const float *k_scale;
   const float *v_scale;
 

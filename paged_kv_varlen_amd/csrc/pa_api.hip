@@ -42,6 +42,7 @@ pa_status resolve(const pa_args* a, Resolved* r) {
   const int64_t D = a->query_width / heads;
   if (a->kv_quant != PA_KV_SAME && a->kv_quant != PA_KV_INT8 && a->kv_quant != PA_KV_INT4)
     return PA_ERR_UNSUPPORTED;
+  if (a->reserved != 0) return PA_ERR_UNSUPPORTED;  // no meaning yet
   r->kq = a->kv_quant == PA_KV_INT8 ? 8 : a->kv_quant == PA_KV_INT4 ? 4 : 0;
   const int64_t cache_row = r->kq == 4 ? D / 2 : D;  // INT4: bytes of a row
   if (a->cache_kv_heads != a->kv_num_heads || a->cache_head_size != cache_row || (r->kq == 4 && D % 2 != 0))

@@ -132,6 +132,7 @@ def test_workspace_bytes_static_bound():
     (dict(gate=FAKE), WS),                               # an aligned gate passes validation
     (dict(kv_quant=3), UNSUP),                           # only PA_KV_SAME, PA_KV_INT8, PA_KV_INT4
     (dict(kv_quant=-1), UNSUP),
+    (dict(reserved=1), UNSUP),                           # reserved field must be 0
     (dict(kv_quant=2, k_scale=FAKE, v_scale=FAKE), SHAPE),  # INT4 rows are head_size / 2 bytes
     (dict(kv_quant=2, cache_head_size=32), NULL),        # INT4 caches need both scale rows
     (dict(kv_quant=2, cache_head_size=32, k_scale=FAKE, v_scale=FAKE), WS),  # INT4 passes validation

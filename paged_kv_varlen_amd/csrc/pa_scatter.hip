@@ -14,7 +14,7 @@
 // clamp(rint(x / s), -127, 127) with the per-channel scales s, the quotient
 // in fp32 (IEEE division) and rounded half to even; with INT4 caches into 8
 // codes clamped to [-7, 7], packed as nibbles (element 2i in bits 0-3).  The
-// last workgroup of the grid plans the attention work.
+// first workgroup of the grid plans the attention work.
 #include "pa_internal.h"
 
 namespace pa {
@@ -135,11 +135,13 @@ __device__ void plan(const ScatterPlanParams& p) {
 }
 
 __global__ __launch_bounds__(kPlanThreads) void scatter_plan_kernel(ScatterPlanParams p) {
-  const int64_t t = blockIdx.x;
-  if (t == p.num_tokens) {
+  // workgroup 0 plans (dispatched first, it overlaps the scatter of long
+  // calls); workgroup t + 1 scatters token t
+  if (blockIdx.x == 0) {
     plan(p);
     return;
   }
+  const int64_t t = static_cast<int64_t>(blockIdx.x) - 1;
   // the sequence of token t: a binary search over cum, staged in LDS by one
   // coalesced load (long batches search global memory)
   __shared__ int cum_lds[kScatterLdsCum];

@@ -273,22 +273,27 @@ def paged_attention(query: torch.Tensor, key: Optional[torch.Tensor],
     packed = key is None
     heads = num_heads + 2 * kv_num_heads if packed else num_heads
     D = query.shape[1] // heads if heads > 0 else 0
-    if output is None:
-        output = torch.empty((query.shape[0], num_heads * D), dtype=query.dtype, device=dev)
-    args = make_args(query, key, value, key_cache, value_cache, cumulative_sequence_length,
-                     past_seqlens, block_table, slot_mapping, output, num_heads=num_heads,
-                     kv_num_heads=kv_num_heads, scale=scale, is_causal=is_causal,
-                     k_scale=k_scale, v_scale=v_scale, gate=gate)
-    if return_lse and lse is None:
-        lse = torch.empty((query.shape[0], num_heads), dtype=torch.float32, device=dev)
-    for name, t in (("lse", lse), ("output_f32", output_f32)):
-        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous float32 tensor")
-    args.lse = _ptr(lse)
-    args.output_f32 = _ptr(output_f32)
-    need = int(lib.pa_workspace_bytes(ctypes.byref(args)))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    # Tensors made here are allocated on the stream the kernels run on: the
+    # caching allocator then hands a freed block (the workspace, dropped on
+    # return) only to later work on that stream, which runs after the kernels.
+    with torch.cuda.stream(s):
+        if output is None:
+            output = torch.empty((query.shape[0], num_heads * D), dtype=query.dtype, device=dev)
+        args = make_args(query, key, value, key_cache, value_cache, cumulative_sequence_length,
+                         past_seqlens, block_table, slot_mapping, output, num_heads=num_heads,
+                         kv_num_heads=kv_num_heads, scale=scale, is_causal=is_causal,
+                         k_scale=k_scale, v_scale=v_scale, gate=gate)
+        if return_lse and lse is None:
+            lse = torch.empty((query.shape[0], num_heads), dtype=torch.float32, device=dev)
+        for name, t in (("lse", lse), ("output_f32", output_f32)):
+            if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+                raise ValueError(f"{name} must be a contiguous float32 tensor")
+        args.lse = _ptr(lse)
+        args.output_f32 = _ptr(output_f32)
+        need = int(lib.pa_workspace_bytes(ctypes.byref(args)))
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     args.workspace = workspace.data_ptr()
     args.workspace_bytes = workspace.numel()
     ev_array = None
@@ -297,7 +302,6 @@ def paged_attention(query: torch.Tensor, key: Optional[torch.Tensor],
             raise ValueError(f"kernel_events needs {2 * len(KERNELS)} events")
         ev_array = (ctypes.c_void_p * len(kernel_events))(*[e.cuda_event for e in kernel_events])
         args.kernel_events = ctypes.cast(ev_array, ctypes.c_void_p)
-    s = stream if stream is not None else torch.cuda.current_stream(dev)
     call(args, s.cuda_stream)
     return (output, lse) if lse is not None else output
 
@@ -322,10 +326,12 @@ def merge_states(state_out: torch.Tensor, state_lse: torch.Tensor, *,
             raise ValueError(f"{name} must be a contiguous float32 tensor")
     P, R, D = state_out.shape
     dev = state_out.device
-    if output is None:
-        output = torch.empty((R, D), dtype=dtype, device=dev)
-    if lse is None:
-        lse = torch.empty((R,), dtype=torch.float32, device=dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.stream(s):  # results belong to the stream that writes them
+        if output is None:
+            output = torch.empty((R, D), dtype=dtype, device=dev)
+        if lse is None:
+            lse = torch.empty((R,), dtype=torch.float32, device=dev)
     a = PaMergeArgs()
     a.struct_size = ctypes.sizeof(PaMergeArgs)
     a.dtype = _dtype_code(output)
@@ -337,7 +343,6 @@ def merge_states(state_out: torch.Tensor, state_lse: torch.Tensor, *,
     a.output = _ptr(output)
     a.output_f32 = _ptr(output_f32)
     a.lse = _ptr(lse)
-    s = stream if stream is not None else torch.cuda.current_stream(dev)
     st = lib.pa_merge_states(ctypes.byref(a), s.cuda_stream)
     if st != 0:
         raise PagedAttentionError(st, lib.pa_status_string(st).decode())

@@ -3,9 +3,7 @@
     python -m paged_kv_varlen_amd.build        # or build() from Python
 
 Each .hip source is compiled to an object in parallel, then linked into
-paged_kv_varlen_amd/libpagedattn.so.  The matrix-core rate probe
-(paged_kv_varlen_amd/probe_mfma_rate, run by ``bench.py --mfma-rate``) is
-built beside it.  Packed-FP32 instructions are switched
+paged_kv_varlen_amd/libpagedattn.so.  Packed-FP32 instructions are switched
 off for all device code.
 """
 from __future__ import annotations
@@ -21,9 +19,6 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpagedattn.so")
 SOURCES = ["pa_api.hip", "pa_scatter.hip", "pa_decode.hip", "pa_prefill.hip", "pa_states.hip"]
-# a stand-alone measurement program (matrix-core rate by operand distribution)
-PROBE_SRC = "probe_mfma_rate.hip"
-PROBE = os.path.join(HERE, "probe_mfma_rate")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -63,11 +58,6 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB)
-    cmd = [HIPCC, *FLAGS, os.path.join(CSRC, PROBE_SRC), "-o", PROBE + ".tmp"]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {PROBE_SRC}:\n{res.stdout}\n{res.stderr}")
-    os.replace(PROBE + ".tmp", PROBE)
     return LIB
 
 

@@ -3,7 +3,7 @@
 // The launch sequence of one pa_paged_attention() call, all on the caller's
 // stream, with no host synchronisation:
 //   1. scatter_plan_kernel  - writes the step's K/V rows into the caches
-//                             (one workgroup per token) and, in its last
+//                             (one workgroup per token) and, in its first
 //                             workgroup, builds the device work plan from
 //                             cum/past: the decode sequences with their tile
 //                             offsets, each decode wave's start, the prefill

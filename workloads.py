@@ -504,10 +504,14 @@ def work(batch: Batch) -> dict:
     out["bytes"] = (out["kv_hist_bytes"] + out["q_bytes"] + out["o_bytes"]
                     + out["step_kv_bytes"] + out["cache_write_bytes"] + out["scale_bytes"])
     if batch.name == "serving":
-        # unique pages actually referenced (shared prefix pages count once)
-        used = set()
+        # unique pages actually referenced (shared prefix pages count once),
+        # over all rows and over the single-token (decode) rows alone
+        used, used_dec = set(), set()
         for b in range(batch.batch_size):
             n = pages_needed(int(L[b]), batch.block_size)
             used.update(batch.block_table[b, :n].tolist())
+            if dec[b]:
+                used_dec.update(batch.block_table[b, :n].tolist())
         out["kv_unique_bytes"] = len(used) * batch.block_size * row
+        out["decode_kv_unique_bytes"] = len(used_dec) * batch.block_size * row
     return out

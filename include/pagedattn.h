@@ -26,8 +26,10 @@
  *   - a packed query row is [Q | K | V], each head-major [heads, head_size].
  *
  * Memory ownership: every pointer is caller-owned.  The library never
- * allocates, frees or keeps a pointer after the call returns.  Device
- * pointers must point to memory of the current HIP device.
+ * allocates, frees or keeps a pointer after the call returns (the scratch
+ * of pa_paged_attention_noalloc is a static device array of the library's
+ * own code, loaded with it).  Device pointers must point to memory of the
+ * current HIP device.
  *
  * Ordering: the call is asynchronous on the given HIP stream.  It performs no
  * host<->device copy and no synchronisation (except under the environment
@@ -220,6 +222,23 @@ enum pa_kernel {
  * enqueued and the caches are untouched.  PA_ERR_HIP means a launch failed;
  * the caches may then be partly written. */
 pa_status pa_paged_attention(const pa_args *args, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operator as pa_paged_attention, with the same arguments and results, but
+ * the workspace is scratch memory the library owns, one array of
+ * PA_NOALLOC_SCRATCH_BYTES per GPU, held from the library's load to the end
+ * of the process.  args->workspace and args->workspace_bytes are ignored.
+ * The call allocates nothing (no hipMalloc, no allocating library routine).
+ * Returns PA_ERR_WORKSPACE, with nothing enqueued, when the shapes need more
+ * than PA_NOALLOC_SCRATCH_BYTES (pa_workspace_bytes(args) tells); the first
+ * call on a device looks up that device's scratch address (PA_ERR_HIP if
+ * that fails).  Every call on a GPU shares that GPU's scratch and leaves its
+ * contents there; the kernels clear what must start at zero.  Two calls
+ * that may overlap on one GPU (different streams without ordering) race on
+ * the scratch: the caller must order them. */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+pa_status pa_paged_attention_noalloc(const pa_args *args, void *stream);
 
 /* Bytes of device workspace pa_paged_attention needs for these shapes (an
  * upper bound from static sizes only: num_tokens, batch_size, num_heads,

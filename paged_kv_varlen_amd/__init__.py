@@ -23,8 +23,9 @@ from typing import Optional
 
 import torch
 
-__all__ = ["paged_attention", "merge_states", "workspace_bytes", "PagedAttentionError", "PaArgs",
-           "PaMergeArgs", "library", "library_path", "STATUS"]
+__all__ = ["paged_attention", "paged_attention_noalloc", "merge_states", "workspace_bytes",
+           "PagedAttentionError", "PaArgs", "PaMergeArgs", "library", "library_path", "STATUS",
+           "NOALLOC_SCRATCH_BYTES"]
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
 
@@ -35,6 +36,7 @@ _CODE_DTYPES = {torch.int8: PA_KV_INT8, torch.uint8: PA_KV_INT4}  # cache dtype 
 _DTYPE_CODES = {torch.float16: PA_DTYPE_F16, torch.bfloat16: PA_DTYPE_BF16}
 ABI_VERSION = 4
 KERNELS = ("scatter_plan", "decode", "merge", "prefill")  # enum pa_kernel order
+NOALLOC_SCRATCH_BYTES = 64 << 20  # PA_NOALLOC_SCRATCH_BYTES
 STATUS = {
     0: "PA_OK", 1: "PA_ERR_NULL_ARG", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED",
     4: "PA_ERR_WORKSPACE", 5: "PA_ERR_ALIGNMENT", 6: "PA_ERR_ABI", 7: "PA_ERR_METADATA",
@@ -119,6 +121,8 @@ def library() -> ctypes.CDLL:
         lib = ctypes.CDLL(library_path)
         lib.pa_paged_attention.argtypes = [ctypes.POINTER(PaArgs), ctypes.c_void_p]
         lib.pa_paged_attention.restype = ctypes.c_int
+        lib.pa_paged_attention_noalloc.argtypes = [ctypes.POINTER(PaArgs), ctypes.c_void_p]
+        lib.pa_paged_attention_noalloc.restype = ctypes.c_int
         lib.pa_workspace_bytes.argtypes = [ctypes.POINTER(PaArgs)]
         lib.pa_workspace_bytes.restype = ctypes.c_size_t
         lib.pa_status_string.argtypes = [ctypes.c_int]
@@ -223,12 +227,41 @@ def workspace_bytes(args: PaArgs) -> int:
     return int(library().pa_workspace_bytes(ctypes.byref(args)))
 
 
-def call(args: PaArgs, stream: Optional[int] = None) -> None:
-    """Run the library's entry point on a filled PaArgs; raise on error."""
+def call(args: PaArgs, stream: Optional[int] = None, noalloc: bool = False) -> None:
+    """Run the library's entry point (pa_paged_attention, or with ``noalloc``
+    pa_paged_attention_noalloc) on a filled PaArgs; raise on error."""
     lib = library()
-    st = lib.pa_paged_attention(ctypes.byref(args), stream)
+    fn = lib.pa_paged_attention_noalloc if noalloc else lib.pa_paged_attention
+    st = fn(ctypes.byref(args), stream)
     if st != 0:
         raise PagedAttentionError(st, lib.pa_status_string(st).decode())
+
+
+def paged_attention_noalloc(query, key, value, key_cache, value_cache, cumulative_sequence_length,
+                            past_seqlens, block_table, slot_mapping=None, *, num_heads: int,
+                            kv_num_heads: int, output: torch.Tensor, scale: float = 0.0,
+                            is_causal: int = 1, lse: Optional[torch.Tensor] = None,
+                            output_f32: Optional[torch.Tensor] = None,
+                            k_scale: Optional[torch.Tensor] = None,
+                            v_scale: Optional[torch.Tensor] = None,
+                            gate: Optional[torch.Tensor] = None,
+                            stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """pa_paged_attention_noalloc: paged_attention() with the library's own
+    per-GPU scratch as workspace.  Nothing is allocated here either: the
+    caller passes ``output`` (and ``lse`` / ``output_f32`` if wanted).  Calls
+    that may overlap on one GPU race on the scratch and must be ordered."""
+    args = make_args(query, key, value, key_cache, value_cache, cumulative_sequence_length,
+                     past_seqlens, block_table, slot_mapping, output, num_heads=num_heads,
+                     kv_num_heads=kv_num_heads, scale=scale, is_causal=is_causal,
+                     k_scale=k_scale, v_scale=v_scale, gate=gate)
+    for name, t in (("lse", lse), ("output_f32", output_f32)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 tensor")
+    args.lse = _ptr(lse)
+    args.output_f32 = _ptr(output_f32)
+    s = stream if stream is not None else torch.cuda.current_stream(query.device)
+    call(args, s.cuda_stream, noalloc=True)
+    return output
 
 
 def paged_attention(query: torch.Tensor, key: Optional[torch.Tensor],

@@ -197,7 +197,8 @@ const char* pa_status_string(pa_status s) {
     case PA_ERR_NULL_ARG: return "a required pointer is NULL";
     case PA_ERR_SHAPE: return "inconsistent sizes";
     case PA_ERR_UNSUPPORTED: return "valid for the operator but not supported by these kernels";
-    case PA_ERR_WORKSPACE: return "workspace missing or smaller than pa_workspace_bytes()";
+    case PA_ERR_WORKSPACE:
+      return "workspace missing or smaller than pa_workspace_bytes() (no-alloc entry point: over its scratch)";
     case PA_ERR_ALIGNMENT: return "a tensor pointer is not 16-byte aligned";
     case PA_ERR_ABI: return "struct_size does not match the library";
     case PA_ERR_METADATA: return "device metadata violates the operator contract";
@@ -208,12 +209,18 @@ const char* pa_status_string(pa_status s) {
 
 int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
 
-pa_status pa_paged_attention(const pa_args* a, void* stream) {
-  using namespace pa;
-  Resolved r{};
-  pa_status st = resolve(a, &r);
+}  // extern "C"
+
+namespace pa {
+namespace {
+
+// Every check of a call except the workspace's (the two entry points take
+// their workspace from different places).  PA_OK with r->N == 0 means there
+// is nothing to do.
+pa_status prepare(const pa_args* a, Resolved* r) {
+  pa_status st = resolve(a, r);
   if (st != PA_OK) return st;
-  if (r.N == 0) return PA_OK;  // no token: nothing is written or read
+  if (r->N == 0) return PA_OK;  // no token: nothing is written or read
   if (a->query == nullptr || a->key_cache == nullptr || a->value_cache == nullptr ||
       a->cumulative_sequence_length == nullptr || a->past_seqlens == nullptr ||
       a->block_table == nullptr || a->output == nullptr)
@@ -221,17 +228,21 @@ pa_status pa_paged_attention(const pa_args* a, void* stream) {
   if (!aligned16(a->query) || !aligned16(a->key) || !aligned16(a->value) ||
       !aligned16(a->key_cache) || !aligned16(a->value_cache) || !aligned16(a->output) ||
       !aligned4(a->cumulative_sequence_length) || !aligned4(a->past_seqlens) ||
-      !aligned4(a->block_table) || !aligned4(a->slot_mapping) || !aligned16(a->workspace) ||
+      !aligned4(a->block_table) || !aligned4(a->slot_mapping) ||
       !aligned4(a->lse) || !aligned16(a->output_f32) || !aligned16(a->gate))
     return PA_ERR_ALIGNMENT;
-  if (r.kq != 0) {
+  if (r->kq != 0) {
     if (a->k_scale == nullptr || a->v_scale == nullptr) return PA_ERR_NULL_ARG;
     if (!aligned16(a->k_scale) || !aligned16(a->v_scale)) return PA_ERR_ALIGNMENT;
   }
-  const WorkspaceLayout w = layout(r);
-  if (a->workspace == nullptr || a->workspace_bytes < w.total) return PA_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  return PA_OK;
+}
 
+// Enqueue the call's kernels on s with the workspace at ws (w.total bytes,
+// 256-byte aligned).
+pa_status enqueue(const pa_args* a, const Resolved& r, const WorkspaceLayout& w, char* ws,
+                  hipStream_t s) {
+  pa_status st = PA_OK;
   const char* dbg = std::getenv("PA_DEBUG_CHECKS");
   if (dbg != nullptr && dbg[0] == '1') {
     st = debug_check(a, r, s);
@@ -244,7 +255,6 @@ pa_status pa_paged_attention(const pa_args* a, void* stream) {
     if (ev != nullptr) (void)hipEventRecord(ev[2 * k + edge], s);
   };
 
-  char* ws = static_cast<char*>(a->workspace);
   const uint16_t* q = static_cast<const uint16_t*>(a->query);
   const int64_t qw = a->query_width;
 
@@ -342,6 +352,63 @@ pa_status pa_paged_attention(const pa_args* a, void* stream) {
   if (launch_prefill(ap, r.D, bf16, r.kq, pf_grid, s) != hipSuccess) return PA_ERR_HIP;
   mark(PA_KERNEL_PREFILL, 1);
   return PA_OK;
+}
+
+}  // namespace
+}  // namespace pa
+
+// Scratch of pa_paged_attention_noalloc: the workspace of a call, in device
+// memory the library owns.  Each GPU the library runs on holds its own copy
+// until the process ends.  Host code never uses the array's name as an
+// address (there it is a host-side stand-in): the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace pa {
+namespace {
+
+// Device address of this device's scratch (nullptr on a HIP error).
+char* scratch_address() {
+  static std::mutex mu;
+  static std::vector<char*> addr;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (static_cast<int>(addr.size()) <= dev) addr.resize(dev + 1, nullptr);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    addr[dev] = static_cast<char*>(ptr);
+  }
+  return addr[dev];
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" {
+
+pa_status pa_paged_attention(const pa_args* a, void* stream) {
+  using namespace pa;
+  Resolved r{};
+  const pa_status st = prepare(a, &r);
+  if (st != PA_OK || r.N == 0) return st;
+  if (!aligned16(a->workspace)) return PA_ERR_ALIGNMENT;
+  const WorkspaceLayout w = layout(r);
+  if (a->workspace == nullptr || a->workspace_bytes < w.total) return PA_ERR_WORKSPACE;
+  return enqueue(a, r, w, static_cast<char*>(a->workspace), static_cast<hipStream_t>(stream));
+}
+
+pa_status pa_paged_attention_noalloc(const pa_args* a, void* stream) {
+  using namespace pa;
+  Resolved r{};
+  const pa_status st = prepare(a, &r);
+  if (st != PA_OK || r.N == 0) return st;
+  const WorkspaceLayout w = layout(r);
+  if (w.total > PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
+  char* ws = scratch_address();
+  if (ws == nullptr) return PA_ERR_HIP;
+  return enqueue(a, r, w, ws, static_cast<hipStream_t>(stream));
 }
 
 pa_status pa_merge_states(const pa_merge_args* a, void* stream) {

@@ -34,7 +34,7 @@ def test_exports_every_declared_function():
     lib = pa.library()
     names = declared_functions()
     assert set(names) == {"pa_paged_attention", "pa_workspace_bytes", "pa_status_string",
-                          "pa_abi_version", "pa_merge_states"}
+                          "pa_abi_version", "pa_merge_states", "pa_paged_attention_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", pa.library_path], capture_output=True,
@@ -211,3 +211,35 @@ def test_merge_host_validation(case, expect):
 
 def test_merge_null_args_pointer():
     assert pa.library().pa_merge_states(None, None) == NULL
+
+
+def status_noalloc(a):
+    return pa.library().pa_paged_attention_noalloc(ctypes.byref(a) if a is not None else None, None)
+
+
+def test_noalloc_scratch_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define PA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == pa.NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(struct_size=8), ABI),
+    (dict(num_heads=3), SHAPE),
+    (dict(is_causal=0), UNSUP),
+    (dict(query=None), NULL),
+    (dict(query=FAKE + 2), ALIGN),
+    (dict(kv_quant=1), NULL),
+    (dict(num_tokens=0, batch_size=2), OK),              # nothing to do: no device work
+    # shapes whose workspace exceeds the scratch: rejected before any device work
+    (dict(num_tokens=4_000_000, batch_size=4_000_000), WS),
+])
+def test_noalloc_host_validation(case, expect):
+    a = args(**case)
+    if expect == WS:
+        assert pa.workspace_bytes(a) > pa.NOALLOC_SCRATCH_BYTES
+    assert status_noalloc(a) == expect
+
+
+def test_noalloc_null_args_pointer():
+    assert pa.library().pa_paged_attention_noalloc(None, None) == NULL

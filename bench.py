@@ -10,10 +10,13 @@ decodes over 512-4096 cached tokens, 32/8 heads, head_size 128, block_size 16.
 The run prints ONE JSON line on stdout; progress goes to stderr.
 
 Timing protocol, per workload (HIP events on the library's stream):
-  cold   the headline.  Before every step, outside the events, a scrub kernel
-         reads and writes a 1 GiB buffer (more than the 256 MB memory-side
-         cache plus the L2s), so each step starts with none of its inputs
-         cached.  K steps, each bracketed by its own event pair; reported as
+  cold   the headline.  Before every step, outside the events, a scrub pass
+         reads a 1 GiB buffer (more than the 256 MB memory-side cache plus the
+         L2s), so each step starts with none of its inputs cached and with
+         clean caches (a read+write scrub leaves dirty lines whose write-back
+         then lands inside the timed step: pure_decode's decode measured 178
+         us that way against 121 us after a read-only or a write-then-read
+         scrub).  K steps, each bracketed by its own event pair; reported as
          median (ms_per_step), p10, p90 and mean.
   warm   K steps back to back with no scrub (inputs partly cached), same
          statistics, as secondary fields.
@@ -49,7 +52,7 @@ if ROOT not in sys.path:
 METRIC = "decode KV-read GB/s (% HBM peak); prefill TFLOP/s (% MFMA peak); tokens/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 matrix peak
-SCRUB_BYTES = 1 << 30          # cold protocol: bytes the scrub kernel reads and writes
+SCRUB_BYTES = 1 << 30          # cold protocol: bytes of the scrub buffer
 KERNEL_SRC = {"decode": ("pa_decode.hip", "pa_elem.h", "pa_internal.h"),
               "prefill": ("pa_prefill.hip", "pa_merge.h", "pa_elem.h", "pa_internal.h"),
               "scatter_plan": ("pa_scatter.hip", "pa_internal.h")}
@@ -177,9 +180,26 @@ def stats_ms(xs) -> dict:
             "n": int(a.size)}
 
 
+SCRUB = {"mode": "read"}
+
+
+def do_scrub(scrub, torch):
+    """Evict the caches: 'read' reads the 1 GiB buffer (the caches then hold
+    clean, unrelated lines), 'rw' reads and writes it (dirty lines left behind
+    are written back during the next step), 'flush' writes it, then reads it
+    (dirty lines written back outside the events)."""
+    if SCRUB["mode"] == "rw":
+        scrub.add_(1)
+    elif SCRUB["mode"] == "flush":
+        scrub.add_(1)
+        torch.sum(scrub, dtype=torch.int64)
+    else:
+        torch.sum(scrub, dtype=torch.int64)
+
+
 def run_steps(r, steps, scrub, torch, kernel_events=False):
-    """K steps, each bracketed by its own events; with a scrub tensor, a
-    read+write pass over it precedes every step outside the events.  Returns
+    """K steps, each bracketed by its own events; with a scrub tensor, a pass
+    over it (do_scrub) precedes every step outside the events.  Returns
     per-step times (ms) and, with kernel_events, per-kernel times (ms) per step."""
     E = lambda: torch.cuda.Event(enable_timing=True)
     starts, ends = [E() for _ in range(steps)], [E() for _ in range(steps)]
@@ -192,7 +212,7 @@ def run_steps(r, steps, scrub, torch, kernel_events=False):
     torch.cuda.synchronize()
     for k in range(steps):
         if scrub is not None:
-            scrub.add_(1)
+            do_scrub(scrub, torch)
         starts[k].record()
         r.step(None if kev is None else kev[k])
         ends[k].record()
@@ -357,6 +377,8 @@ def main():
     ap.add_argument("--no-warm", action="store_true",
                     help="skip the warm phase (every timed dispatch is then cold, e.g. under a "
                          "profiler whose averages should match the cold figures)")
+    ap.add_argument("--scrub", default="read", choices=("read", "rw", "flush"),
+                    help="cold protocol cache eviction before each step (see do_scrub)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -368,6 +390,7 @@ def main():
     ap.add_argument("--traffic-kernel", default="decode", choices=sorted(KERNEL_SYMBOL))
     args = ap.parse_args()
     VARIANT["suffix"] = variant_suffix(args.dtype, args.head_size, args.kv_quant, args.gate)
+    SCRUB["mode"] = args.scrub
 
     if args.traffic_from:
         write_traffic(args.traffic_kernel, args.workload, *args.traffic_from,
@@ -438,8 +461,8 @@ def main():
                    "block_size": b.block_size, "num_blocks": b.num_blocks,
                    "kv_cache": args.dtype if args.kv_quant == "none" else args.kv_quant,
                    "output_gate": bool(args.gate), "kv_hist_bytes": work["kv_hist_bytes"],
-                   "protocol": "cold: 1 GiB read+write scrub before each step, outside the "
-                               "events; ms_per_step = median of the per-step event times"},
+                   "protocol": f"cold: 1 GiB scrub ({args.scrub}) before each step, outside "
+                               "the events; ms_per_step = median of the per-step event times"},
         "roofline": head_roof,
         "cold": head["cold"],
         "warm": head["warm"],

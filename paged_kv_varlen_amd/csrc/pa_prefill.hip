@@ -301,14 +301,36 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
     }
   }
 
+  // The first item of every workgroup is static: workgroup b takes item
+  // rank(b) of its home queue, rank(b) counting the workgroups of that home
+  // below b (nq divides 8).  Later items come from the queue counters (zeroed
+  // by the plan), offset by the number of static items of the queue, so a
+  // call with at most one item per workgroup needs no atomic at all.
+  const int gd = static_cast<int>(gridDim.x);
+  auto static_items = [&](int q) {  // workgroups whose home queue is q
+    const int rem = gd % 8;
+    return (gd / 8) * (8 / nq) + (q < rem ? (rem - 1 - q) / nq + 1 : 0);
+  };
   int queue = home, tried = 0;
+  bool first_item = true;
   auto fetch = [&]() -> int {  // next item of this workgroup, or -1
-    while (tried < nq) {
-      if (tid == 0) lds_item = atomicAdd(&p.ws_ctrl[kCtrlPrefillQueue0 + queue], 1);
-      __syncthreads();
-      const int j = lds_item;
-      __syncthreads();
+    if (first_item) {
+      first_item = false;
+      const int j = static_cast<int>(blockIdx.x / 8) * (8 / nq) + static_cast<int>(blockIdx.x % 8) / nq;
       if (j < per_queue) return j;
+    }
+    while (tried < nq) {
+      const int base = static_items(queue);
+      if (base < per_queue) {  // (uniform) the queue has items beyond the static ones
+        if (tid == 0) lds_item = atomicAdd(&p.ws_ctrl[kCtrlPrefillQueue0 + queue], 1) + base;
+        // LDS traffic only: no wait for the previous item's output stores
+        wait_lds();
+        plain_barrier();
+        const int j = lds_item;
+        wait_lds();
+        plain_barrier();
+        if (j < per_queue) return j;
+      }
       queue = queue + 1 == nq ? 0 : queue + 1;
       ++tried;
     }
@@ -345,14 +367,43 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
     const int wave_first = past + i0 + fh0 / G;
     const int wave_last = wave_valid ? past + min(i0 + min(fh0 + 31, P * G - 1) / G, i1 - 1) : -1;
 
+    const int32_t* btab = p.block_table + static_cast<int64_t>(b) * p.max_blocks;
+    // cache slot (block_table[k / bs] * bs + k % bs) of every 16th key k <
+    // min(L, nsteps * 64), for 16-key groups [gbase, gbase + kSlotWindow);
+    // a wave's 8 rows of a step never cross a page (bs is a multiple of 16)
+    const int ngroups = (min(L, nsteps * kPrefillKeys) + 15) / 16;
+    // the first window's block-table reads, issued before the query loads so
+    // that writing the window waits for them alone
+    // (head size 256: the old order, its registers are needed by the ring)
+    constexpr int kWinPer = S::WIDE ? 1 : kSlotWindow / S::THREADS;  // window entries per thread
+    int win0[kWinPer];
+    if constexpr (!S::WIDE) {
+      const int n = min(kSlotWindow, ngroups);
+#pragma unroll
+      for (int r = 0; r < kWinPer; ++r) {
+        const int i = tid + r * S::THREADS;
+        win0[r] = i < n ? btab[(16 * i) / bs] * bs + (16 * i) % bs : 0;
+      }
+    }
+    asm volatile("" ::: "memory");
+
     x8 qf[S::QK_STEPS];
+    uint4 qraw[S::QK_STEPS];
     {
       const uint16_t* qrow = p.q + static_cast<int64_t>(t0 + i0 + (row_valid ? pos_local : 0)) * p.q_stride +
                              static_cast<int64_t>(head) * D;
 #pragma unroll
       for (int kk = 0; kk < S::QK_STEPS; ++kk) {
-        uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-        if (row_valid) raw = *reinterpret_cast<const uint4*>(qrow + 16 * kk + 8 * lhalf);
+        qraw[kk] = make_uint4(0u, 0u, 0u, 0u);
+        if (row_valid) qraw[kk] = *reinterpret_cast<const uint4*>(qrow + 16 * kk + 8 * lhalf);
+      }
+    }
+    // the query row, finished once its loads landed (the first fills are in
+    // flight by then)
+    auto finish_q = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int kk = 0; kk < S::QK_STEPS; ++kk) {
+        uint4 raw = qraw[kk];
         if constexpr (QNT) {  // q_d * ks_d, d = 16 kk + 8 lhalf + e, rounded to the data type
           const float4* ks = reinterpret_cast<const float4*>(p.k_scale + static_cast<int64_t>(kvh) * D + 16 * kk +
                                                              8 * lhalf);
@@ -368,18 +419,15 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
         }
         qf[kk] = __builtin_bit_cast(x8, raw);
       }
-    }
+    };
+    // (head size 256: finished at once, its registers are needed by the ring)
+    if constexpr (S::WIDE) finish_q();
 
     f32x16_t o[S::O_TILES];
 #pragma unroll
     for (int mt = 0; mt < S::O_TILES; ++mt) o[mt] = f32x16_t{};
     float m = kNegInf, l = 0.f;
 
-    const int32_t* btab = p.block_table + static_cast<int64_t>(b) * p.max_blocks;
-    // cache slot (block_table[k / bs] * bs + k % bs) of every 16th key k <
-    // min(L, nsteps * 64), for 16-key groups [gbase, gbase + kSlotWindow);
-    // a wave's 8 rows of a step never cross a page (bs is a multiple of 16)
-    const int ngroups = (min(L, nsteps * kPrefillKeys) + 15) / 16;
     const char* kbytes = reinterpret_cast<const char*>(p.key_cache) + static_cast<int64_t>(kvh) * S::ROWC;
     const char* vbytes = reinterpret_cast<const char*>(p.value_cache) + static_cast<int64_t>(kvh) * S::ROWC;
     const uint32_t row_bytes = static_cast<uint32_t>(p.kv_heads * S::ROWC);  // bytes of a cache slot
@@ -623,7 +671,15 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
       plain_barrier();
     };
 
-    fill_window(0);
+    if constexpr (S::WIDE) {
+      fill_window(0);
+    } else {  // the first window (LDS only: the query loads stay in flight)
+#pragma unroll
+      for (int r = 0; r < kWinPer; ++r)
+        if (tid + r * S::THREADS < min(kSlotWindow, ngroups)) slot_lds[tid + r * S::THREADS] = win0[r];
+      wait_lds();
+      plain_barrier();
+    }
     // steps 0..2 in flight before the first step (nested conditions: no path
     // that the compiler considers skips a step and fetches a later one)
     issue(std::integral_constant<int, 0>{}, 0, slot_of(0), 0, S::LOADS);
@@ -637,6 +693,7 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
       if (nsteps > 1) issue(std::integral_constant<int, 1>{}, 1, slot_of(1), 0, S::LOADS);
       wait_fills<0>();
     }
+    if constexpr (!S::WIDE) finish_q();  // (loads issued before the fills: the wait above covers them)
     plain_barrier();
     if constexpr (kAhead) {  // step 0's rows, before its products
       convert(std::integral_constant<int, 0>{});
@@ -684,7 +741,8 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
         xml[(rg * 2 + 0) * 64 + lane] = m;
         xml[(rg * 2 + 1) * 64 + lane] = l;
       }
-      __syncthreads();
+      wait_lds();  // LDS traffic only
+      plain_barrier();
     }
     if (kvg == 0 && wave_valid) {
       float m1 = kNegInf, l1 = 0.f;
@@ -749,7 +807,9 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
           }
       }
     }
-    __syncthreads();  // LDS is reused by the next item
+    // LDS is reused by the next item (the output stores need not have landed)
+    wait_lds();
+    plain_barrier();
   }
 }
 

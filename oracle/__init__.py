@@ -12,7 +12,9 @@ Modules
                    history through block_table, brute-force causal GQA softmax
                    attention, optionally with each row's attention-domain
                    lse.  Also the partial (out, lse) state over a key subset
-                   and the fixed-order merge of such states.
+                   and the fixed-order merge of such states, and the fused
+                   prologue (Q/K OffsetRMSNorm, interleaved partial MRoPE,
+                   cast to the data type).
   scalar           a second, independent formulation in plain Python scalars
                    (nested loops, math.fsum) for tiny inputs, used to pin the
                    numpy version.
@@ -37,4 +39,11 @@ from .paged_attention import (  # noqa: F401
     unpack_int4,
     dequantize,
     output_gate,
+    qk_prologue,
+    offset_rms_norm,
+    mrope_components,
+    rotary_angles,
+    apply_rotary,
+    round_to_format,
+    to_dtype_bits,
 )

@@ -235,10 +235,142 @@ def output_gate(out: np.ndarray, gate: np.ndarray) -> np.ndarray:
     return out * (1.0 / (1.0 + np.exp(-g)))
 
 
+# ---------------------------------------------------------------------------
+# Fused prologue: Q/K OffsetRMSNorm, then interleaved partial MRoPE
+# ---------------------------------------------------------------------------
+#
+# "Add Qwen3.8 packed hybrid PagedAttention export for ORT GenAI Engine",
+# Per-layer behavior (Full attention, step 3): the query and key heads get an
+# OffsetRMSNorm and then an interleaved partial MRoPE, norm before RoPE, once
+# ("do not normalize twice"); the positions are position_ids INT64 [3, N]
+# (Packed graph contract, Shared inputs).  "WS2 CP-Aware Attention Contract",
+# RoPE / Position Semantics and the Qwen3-8B example: the cached K is
+# post-RoPE, the rotation has a base theta and a rotary_dim that fits the head
+# dimension, and the result is cast to the data type after RoPE.  Readings of
+# what the pages leave open (each a parameter here):
+#   * OffsetRMSNorm of a head row x [D] with weights w [D]:
+#     y = x * (1 + w) / sqrt(mean(x^2) + eps)  (the weight is an offset from 1);
+#   * partial: the first rotary_dim channels of each head rotate, the rest
+#     pass through; frequency pair i < rotary_dim / 2 has inverse frequency
+#     theta^(-2i / rotary_dim) and angle position * inverse frequency;
+#   * pairing: pair i is channels (i, i + rotary_dim/2) ("half"), or channels
+#     (2i, 2i+1) ("adjacent"), rotated as y1 = x1 cos - x2 sin,
+#     y2 = x2 cos + x1 sin;
+#   * MRoPE sections: pair i takes its position from component c(i) of the
+#     three rows of position_ids, with section sizes (s0, s1, s2) summing to
+#     rotary_dim / 2; "interleaved": c(i) = i mod 3 while that component still
+#     has room, else the first component that has; "contiguous": the first s0
+#     pairs use component 0, the next s1 component 1, the rest component 2.
+
+
+def round_to_format(x: np.ndarray, mant_bits: int, emin: int) -> np.ndarray:
+    """Round fp64 values to the nearest number with mant_bits significant
+    bits and minimum normal exponent emin (ties to even), as fp64: fp16 is
+    (11, -14), bf16 is (8, -126).  Quantum 2^(max(e, emin) - mant_bits + 1)
+    for |x| in [2^e, 2^(e+1)).  Finite inputs of moderate size only."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)                    # x = m 2^e, m in [0.5, 1)
+    q = np.ldexp(1.0, np.maximum(e - 1, emin) - mant_bits + 1)
+    return np.rint(x / q) * q
+
+
+def to_dtype_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    """fp64 values -> storage of the data type, rounded to nearest even:
+    float16 arrays for "f16", uint16 bfloat16 bit patterns for "bf16"."""
+    if dtype == "bf16":
+        r = round_to_format(x, 8, -126).astype(np.float32)  # exact in fp32
+        return (r.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    return round_to_format(x, 11, -14).astype(np.float16)   # exact in fp16
+
+
+def offset_rms_norm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """OffsetRMSNorm over the last axis: x * (1 + w) / sqrt(mean(x^2) + eps),
+    fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + float(eps)) * (1.0 + np.asarray(w, dtype=np.float64))
+
+
+def mrope_components(rotary_dim: int, sections, interleaved: bool = True) -> np.ndarray:
+    """Position component (0, 1 or 2) of each frequency pair i < rotary_dim/2."""
+    half = rotary_dim // 2
+    sections = [int(v) for v in sections]
+    if len(sections) != 3 or sum(sections) != half or min(sections) < 0:
+        raise ValueError("mrope sections must be three counts summing to rotary_dim / 2")
+    comp = np.empty(half, dtype=np.int64)
+    if interleaved:
+        used = [0, 0, 0]
+        for i in range(half):
+            c = i % 3
+            if used[c] >= sections[c]:
+                c = next(k for k in range(3) if used[k] < sections[k])
+            comp[i] = c
+            used[c] += 1
+    else:
+        comp[:] = np.repeat(np.arange(3), sections)
+    return comp
+
+
+def rotary_angles(position_ids: np.ndarray, rotary_dim: int, theta: float,
+                  components: np.ndarray) -> np.ndarray:
+    """Angles [N, rotary_dim/2] (fp64): position_ids[c(i), t] * theta^(-2i/rotary_dim)."""
+    half = rotary_dim // 2
+    inv = float(theta) ** (-2.0 * np.arange(half, dtype=np.float64) / rotary_dim)
+    pos = np.asarray(position_ids, dtype=np.int64)[components, :].T.astype(np.float64)  # [N, half]
+    return pos * inv[None, :]
+
+
+def apply_rotary(x: np.ndarray, angles: np.ndarray, rotary_dim: int,
+                 adjacent: bool = False) -> np.ndarray:
+    """Rotate the first rotary_dim channels of x [N, heads, D] (fp64) by
+    angles [N, rotary_dim/2]; the other channels are returned unchanged."""
+    y = np.array(x, dtype=np.float64, copy=True)
+    half = rotary_dim // 2
+    if adjacent:
+        i1, i2 = np.arange(0, rotary_dim, 2), np.arange(1, rotary_dim, 2)
+    else:
+        i1, i2 = np.arange(half), np.arange(half, rotary_dim)
+    cos = np.cos(angles)[:, None, :]
+    sin = np.sin(angles)[:, None, :]
+    x1, x2 = y[:, :, i1].copy(), y[:, :, i2].copy()
+    y[:, :, i1] = x1 * cos - x2 * sin
+    y[:, :, i2] = x2 * cos + x1 * sin
+    return y
+
+
+def qk_prologue(Q: np.ndarray, K: np.ndarray, *, position_ids=None, rotary_dim: int = 0,
+                theta: float = 1.0e6, sections=None, interleaved: bool = True,
+                adjacent: bool = False, q_norm_weight=None, k_norm_weight=None,
+                eps: float = 1e-6, rounded: bool = True):
+    """The fused prologue on Q [N, H, D] and K [N, Hkv, D] (data-type storage):
+    OffsetRMSNorm of every head (when its weights are given), then the
+    partial MRoPE (when rotary_dim > 0), then the cast to the data type.
+    Returns (Q', K') in the data type's storage, or fp64 with rounded=False."""
+    dtype = "bf16" if np.asarray(Q).dtype == np.uint16 else "f16"
+    q, k = values(Q), values(K)
+    if q_norm_weight is not None:
+        q = offset_rms_norm(q, q_norm_weight, eps)
+    if k_norm_weight is not None:
+        k = offset_rms_norm(k, k_norm_weight, eps)
+    if rotary_dim:
+        D = q.shape[-1]
+        if rotary_dim % 2 or not 0 < rotary_dim <= D:
+            raise ValueError("rotary_dim must be even and fit the head size")
+        if sections is None:
+            raise ValueError("rotary needs the three section sizes")
+        ang = rotary_angles(position_ids, rotary_dim, theta,
+                            mrope_components(rotary_dim, sections, interleaved))
+        q = apply_rotary(q, ang, rotary_dim, adjacent)
+        k = apply_rotary(k, ang, rotary_dim, adjacent)
+    if not rounded:
+        return q, k
+    return to_dtype_bits(q, dtype), to_dtype_bits(k, dtype)
+
+
 def paged_attention(query, key, value, key_cache, value_cache, cum, past, block_table,
                     slot_mapping=None, *, num_heads: int, kv_num_heads: int,
                     scale: float = 0.0, is_causal: int = 1, rows=None, with_lse: bool = False,
-                    k_scale=None, v_scale=None, gate=None):
+                    k_scale=None, v_scale=None, gate=None, prologue=None):
     """The whole operator: returns (output fp64 [N, H*D], key_cache', value_cache').
 
     README, Description/Outputs: the caches are updated (here: copies are
@@ -252,12 +384,17 @@ def paged_attention(query, key, value, key_cache, value_cache, cum, past, block_
     quantized on write and every cached element reads as code * scale.
     ``gate`` ([N, H*D] in the data type): the returned output is
     output_gate(attention, gate); the lse (the row's state) is unchanged.
+    ``prologue`` (a dict of qk_prologue's keyword arguments): the step's
+    query and key rows are first normalised and rotated (qk_prologue), and
+    those rows are what is cached and attended.
     """
     if (k_scale is None) != (v_scale is None):
         raise ValueError("k_scale and v_scale go together")
     if int(is_causal) != 1:
         raise ValueError("only is_causal=1 is defined")
     Q, K, V, D, s = resolve_call(query, key, value, num_heads, kv_num_heads, scale)
+    if prologue is not None:
+        Q, K = qk_prologue(Q, K, **prologue)
     cum = np.asarray(cum, dtype=np.int64)
     past = np.asarray(past, dtype=np.int64)
     N = Q.shape[0]

@@ -148,3 +148,57 @@ def paged_attention_scalar(query, key, value, key_cache, value_cache, cum, past,
         out.append(orow)
         lse.append(lrow)
     return (out, written, lse) if with_lse else (out, written)
+
+
+def qk_prologue_scalar(q_rows, k_rows, D, *, position_ids=None, rotary_dim=0, theta=1.0e6,
+                       sections=None, interleaved=True, adjacent=False, q_norm_weight=None,
+                       k_norm_weight=None, eps=1e-6):
+    """The fused prologue written out per element with Python floats ("Add
+    Qwen3.8 packed hybrid PagedAttention export for ORT GenAI Engine",
+    Per-layer behavior, Full attention, step 3: OffsetRMSNorm, then
+    interleaved partial MRoPE; "WS2 CP-Aware Attention Contract", RoPE /
+    Position Semantics: theta, rotary_dim).  q_rows / k_rows: lists over
+    tokens of lists over heads of D element values.  Returns the unrounded
+    (q, k) in the same nested form.
+
+    Independent of the numpy formulation: the section of each frequency pair
+    is found by counting per component, the angle is taken per element with
+    math.cos / math.sin, the mean square with math.fsum."""
+    half = rotary_dim // 2
+
+    def component(i):
+        if not interleaved:
+            if i < sections[0]:
+                return 0
+            return 1 if i < sections[0] + sections[1] else 2
+        used = [0, 0, 0]
+        c = 0
+        for j in range(i + 1):
+            c = j % 3
+            if used[c] >= sections[c]:
+                c = [k for k in range(3) if used[k] < sections[k]][0]
+            used[c] += 1
+        return c
+
+    comps = [component(i) for i in range(half)]
+
+    def one(row, w, t):
+        x = list(row)
+        if w is not None:
+            ms = math.fsum(v * v for v in x) / D
+            r = 1.0 / math.sqrt(ms + eps)
+            x = [x[d] * r * (1.0 + float(w[d])) for d in range(D)]
+        if rotary_dim:
+            y = list(x)
+            for i in range(half):
+                pos = float(position_ids[comps[i]][t])
+                ang = pos * theta ** (-2.0 * i / rotary_dim)
+                a, b = (2 * i, 2 * i + 1) if adjacent else (i, i + half)
+                y[a] = x[a] * math.cos(ang) - x[b] * math.sin(ang)
+                y[b] = x[b] * math.cos(ang) + x[a] * math.sin(ang)
+            x = y
+        return x
+
+    q = [[one(h, q_norm_weight, t) for h in heads] for t, heads in enumerate(q_rows)]
+    k = [[one(h, k_norm_weight, t) for h in heads] for t, heads in enumerate(k_rows)]
+    return q, k

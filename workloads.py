@@ -464,6 +464,41 @@ def output_gate_input(batch: "Batch", seed: int) -> np.ndarray:
     return normal(rng, (batch.num_tokens, batch.num_heads * batch.head_size))
 
 
+def token_positions(batch: "Batch") -> np.ndarray:
+    """Logical position past_b + i of every packed token (int64 [N])."""
+    return np.concatenate([np.arange(int(batch.past[i]), int(batch.past[i]) + int(q))
+                           for i, q in enumerate(batch.q_lens)] or [np.zeros(0)]).astype(np.int64)
+
+
+def prologue_inputs(batch: "Batch", seed: int, rotary_dim: int = 0, norm: bool = True,
+                    spatial: bool = False, theta: float = 1.0e6, adjacent: bool = False,
+                    interleaved: bool = True) -> dict:
+    """Inputs of the fused Q/K prologue for a batch (own seeded stream).
+
+    position_ids int64 [3, N]: every row is the token's logical position
+    (text tokens); with ``spatial`` rows 1 and 2 are drawn in [0, 64) instead
+    (a spatial grid position).  Norm weights fp32 [D]: offsets N(0, 0.1^2).
+    rotary_dim 0: the head size.  Sections: rotary_dim / 2 pairs split as
+    evenly as possible over the three rows, the remainder to row 0.  Returns
+    the keyword arguments of the oracle's qk_prologue."""
+    rng = np.random.default_rng(seed)
+    D = batch.head_size
+    rd = rotary_dim or D
+    half = rd // 2
+    pos = token_positions(batch)
+    ids = np.stack([pos, pos, pos]).astype(np.int64)
+    if spatial:
+        ids[1] = rng.integers(0, 64, pos.size)
+        ids[2] = rng.integers(0, 64, pos.size)
+    out = dict(position_ids=ids, rotary_dim=rd, theta=theta,
+               sections=(half - 2 * (half // 3), half // 3, half // 3),
+               interleaved=interleaved, adjacent=adjacent, eps=1e-6)
+    if norm:
+        out["q_norm_weight"] = (rng.standard_normal(D) * 0.1).astype(np.float32)
+        out["k_norm_weight"] = (rng.standard_normal(D) * 0.1).astype(np.float32)
+    return out
+
+
 # ---------------------------------------------------------------------------
 # algorithmic work of a call (what a roofline is measured against)
 # ---------------------------------------------------------------------------

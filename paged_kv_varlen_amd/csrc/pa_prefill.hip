@@ -107,6 +107,20 @@ __device__ inline float swap_halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// maximum of 16 scores: the IEEE maximum (NaN-propagating, like any product
+// of a NaN) compiles to gfx950's three-input v_maximum3_f32 and, unlike
+// fmaxf, needs no canonicalisation of the matrix-core results first
+__device__ inline float max16(const f32x16_t& v) {
+  float r = v[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) r = __builtin_elementwise_maximum(r, v[i]);
+  return r;
+}
+__device__ inline float swap_halves_maximum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt bits 3:0 and 15:14,
 // expcnt 6:4 left at its maximum, lgkmcnt 11:8)
 template <int N>
@@ -193,6 +207,8 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
   // codes of step j + 1 while the products of step j run
   constexpr bool kAhead = QNT && S::KVG == 2;
   static_assert(!kAhead || S::STAGE >= 4 * S::BUF, "two stages");
+  // 16-bit caches up to head size 128: software-pipelined steps (pstep)
+  constexpr bool kPipe = !QNT && !S::WIDE;
 
   // one LDS object per ring buffer and tensor: the compiler can then see that
   // a fill of one buffer never aliases reads of another and does not make
@@ -201,15 +217,15 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
   __shared__ __align__(16) char k_lds1[S::CBUF];
   __shared__ __align__(16) char k_lds2[kRing > 2 ? S::CBUF : 16];
   __shared__ __align__(16) char k_lds3[kRing > 2 ? S::CBUF : 16];
-  __shared__ __align__(16) char v_lds0[S::CBUF];
-  __shared__ __align__(16) char v_lds1[S::CBUF];
-  __shared__ __align__(16) char v_lds2[kRing > 2 ? S::CBUF : 16];
-  __shared__ __align__(16) char v_lds3[kRing > 2 ? S::CBUF : 16];
+  __shared__ __align__(16) char a_lds0[S::CBUF];
+  __shared__ __align__(16) char a_lds1[S::CBUF];
+  __shared__ __align__(16) char a_lds2[kRing > 2 ? S::CBUF : 16];
+  __shared__ __align__(16) char a_lds3[kRing > 2 ? S::CBUF : 16];
   __shared__ __align__(16) char stage[S::STAGE];
   __shared__ int slot_lds[kSlotWindow];
   __shared__ int lds_item;
   auto kbuf = [&](int b) -> char* { return b == 0 ? k_lds0 : b == 1 ? k_lds1 : b == 2 ? k_lds2 : k_lds3; };
-  auto vbuf = [&](int b) -> char* { return b == 0 ? v_lds0 : b == 1 ? v_lds1 : b == 2 ? v_lds2 : v_lds3; };
+  auto vbuf = [&](int b) -> char* { return b == 0 ? a_lds0 : b == 1 ? a_lds1 : b == 2 ? a_lds2 : a_lds3; };
   // the K and V rows the products of ring buffer b's step read (data type,
   // swizzled); with two stages, a step's parity is that of its ring buffer
   auto kread = [&](int b) -> char* { return QNT ? stage + (kAhead ? (b & 1) * 2 * S::BUF : 0) : kbuf(b); };
@@ -326,7 +342,9 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
         // LDS traffic only: no wait for the previous item's output stores
         wait_lds();
         plain_barrier();
-        const int j = lds_item;
+        // (uniform: every lane reads the same value, which the compiler
+        // cannot see; from here on the item's values live in scalar registers)
+        const int j = __builtin_amdgcn_readfirstlane(lds_item);
         wait_lds();
         plain_barrier();
         if (j < per_queue) return j;
@@ -427,6 +445,7 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
 #pragma unroll
     for (int mt = 0; mt < S::O_TILES; ++mt) o[mt] = f32x16_t{};
     float m = kNegInf, l = 0.f;
+    f32x16_t s_pipe = f32x16_t{};  // pipelined steps: S of the step computed next
 
     const char* kbytes = reinterpret_cast<const char*>(p.key_cache) + static_cast<int64_t>(kvh) * S::ROWC;
     const char* vbytes = reinterpret_cast<const char*>(p.value_cache) + static_cast<int64_t>(kvh) * S::ROWC;
@@ -576,6 +595,72 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
       }
     };
 
+    // Software-pipelined step (16-bit caches, head sizes up to 128).  S of
+    // step j is already in registers (computed by the previous step); this
+    // step reads K of step j + 1, runs the softmax of step j while those
+    // reads land, computes S of step j + 1 on the matrix cores, then reads V
+    // of step j and accumulates O += P V.  A wave thus keeps the products of
+    // the next step queued behind the vector work of this one.  (The next
+    // step's S is computed even on a wave's last step, from whatever ring
+    // buffer buf + 1 holds, and then unused.)
+    auto pstep = [&](auto buf_tag, int jk, bool masked, f32x16_t& s) __attribute__((always_inline)) {
+      constexpr int buf = decltype(buf_tag)::value;
+      constexpr int nbuf = (buf + 1) % kRing;
+      x8 kf[S::QK_STEPS];
+#pragma unroll
+      for (int kk = 0; kk < S::QK_STEPS; ++kk) kf[kk] = *reinterpret_cast<const x8*>(kbuf(nbuf) + koff[kk]);
+      // register i of S holds key jk + 8(i/4) + 4*lhalf + i%4
+      if (masked) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = jk + 8 * (i >> 2) + 4 * lhalf + (i & 3);
+          if (key > row_pos) s[i] = kNegInf;
+        }
+      }
+      const float mx = swap_halves_maximum(max16(s)) * c;
+      const bool grow = mx > m + 8.f;
+      if (__ballot(grow) != 0) {  // wave-uniform branch; other lanes scale by 1
+        const float alpha = grow ? fast_exp2(m - mx) : 1.f;
+        l *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < S::O_TILES; ++mt) o[mt] *= alpha;
+        m = grow ? mx : m;
+      }
+      const float mref = m == kNegInf ? 0.f : m;  // a row that has seen no key yet
+      x8 pb[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[ks][e] = E::round(fast_exp2(fmaf(s[8 * ks + e], c, -mref)));
+      float la = 0.f, lb = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        la = E::sum2(typename E::x2{pb[0][e], pb[0][e + 1]}, la);
+        lb = E::sum2(typename E::x2{pb[1][e], pb[1][e + 1]}, lb);
+      }
+      l += la + lb;
+      f32x16_t sn = f32x16_t{};
+#pragma unroll
+      for (int kk = 0; kk < S::QK_STEPS; ++kk) sn = E::mfma_32x32x16(kf[kk], qf[kk], sn);
+      x8 va[2][S::O_TILES];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < S::O_TILES; ++mt) {
+          char* vb = vbuf(buf) + voff[mt] + 16 * ks * ROWB;
+          const fp16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((PA_LDS fp16x4_t*)vb);
+          const fp16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((PA_LDS fp16x4_t*)(vb + 8 * ROWB));
+          va[ks][mt] = __builtin_shufflevector(__builtin_bit_cast(x4, lo), __builtin_bit_cast(x4, hi), 0, 1, 2, 3,
+                                               4, 5, 6, 7);
+        }
+      s = sn;
+      // O^T[d][row] += V^T[d][key] P^T[key][row]
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < S::O_TILES; ++mt) o[mt] = E::mfma_32x32x16(va[ks][mt], pb[ks], o[mt]);
+    };
+
     // quantized: the codes of the step in ring buffer buf -> data-type rows of the
     // stage, in the layout the products read: cached chunk c (16 codes) of
     // row r becomes chunks 2c and 2c+1 of row r, swizzled
@@ -649,11 +734,16 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
         wait_lds();
         plain_barrier();
       }
-      static_for<S::SUBS>([&](auto sub) __attribute__((always_inline)) {
-        // first key of this wave's 32 keys
-        const int jk = jstep * kPrefillKeys + (kvg + decltype(sub)::value) * kGroupKeys;
-        if (jk <= wave_last) compute(buf_tag, sub, jk, jk + kGroupKeys - 1 > wave_first);
-      });
+      if constexpr (kPipe) {
+        const int jk = jstep * kPrefillKeys + kvg * kGroupKeys;  // first key of this wave's 32 keys
+        if (jk <= wave_last) pstep(buf_tag, jk, jk + kGroupKeys - 1 > wave_first, s_pipe);
+      } else {
+        static_for<S::SUBS>([&](auto sub) __attribute__((always_inline)) {
+          // first key of this wave's 32 keys
+          const int jk = jstep * kPrefillKeys + (kvg + decltype(sub)::value) * kGroupKeys;
+          if (jk <= wave_last) compute(buf_tag, sub, jk, jk + kGroupKeys - 1 > wave_first);
+        });
+      }
       if constexpr (kRing == 2) {
         wait_fills<0>();
       } else {
@@ -663,9 +753,10 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
         // a plain barrier: __syncthreads() would also wait for the fills
         // still in flight.  The waits go through the builtin so that the
         // compiler knows which fills have landed and adds no wait of its own.
-        // (Converting one step ahead: step j + 2 must have landed, only
-        // step j + 3 stays in flight; the wait also covers the stage writes.)
-        if (more) wait_fills<(kAhead ? 2 : 4) * S::LOADS>();
+        // (Converting one step ahead, or reading the next step's K in this
+        // one: step j + 2 must have landed, only step j + 3 stays in flight;
+        // the wait also covers the stage writes.)
+        if (more) wait_fills<(kAhead || kPipe ? 2 : 4) * S::LOADS>();
         else wait_fills<0>();
       }
       plain_barrier();
@@ -688,7 +779,8 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
     } else if (nsteps > 2) {
       issue(std::integral_constant<int, 1>{}, 1, slot_of(1), 0, S::LOADS);
       issue(std::integral_constant<int, 2 % kRing>{}, 2, slot_of(2), 0, S::LOADS);
-      wait_fills<(kAhead ? 2 : 4) * S::LOADS>();  // step 0 (converting ahead: and 1) landed
+      // step 0 landed (converting ahead, or pipelined: and step 1)
+      wait_fills<(kAhead || kPipe ? 2 : 4) * S::LOADS>();
     } else {
       if (nsteps > 1) issue(std::integral_constant<int, 1>{}, 1, slot_of(1), 0, S::LOADS);
       wait_fills<0>();
@@ -699,6 +791,14 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
       convert(std::integral_constant<int, 0>{});
       wait_lds();
       plain_barrier();
+    }
+    if constexpr (kPipe) {  // S of step 0 (unused by a wave with no key)
+      x8 kf[S::QK_STEPS];
+#pragma unroll
+      for (int kk = 0; kk < S::QK_STEPS; ++kk) kf[kk] = *reinterpret_cast<const x8*>(kbuf(0) + koff[kk]);
+      s_pipe = f32x16_t{};
+#pragma unroll
+      for (int kk = 0; kk < S::QK_STEPS; ++kk) s_pipe = E::mfma_32x32x16(kf[kk], qf[kk], s_pipe);
     }
     // Steps in chunks of kChunk: the slot window holds the chunk's steps and
     // the three fetched ahead of it, and is refilled between chunks (the
@@ -731,7 +831,7 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
     // window).  (One kv group: nothing to merge.)
     wait_fills<0>();  // (the last steps already waited)
     float* xo = reinterpret_cast<float*>(QNT ? stage + (S::KVG == 2 ? rg * S::BUF : 0) : kbuf(rg));
-    float* xml = QNT ? reinterpret_cast<float*>(slot_lds) : reinterpret_cast<float*>(v_lds0);
+    float* xml = QNT ? reinterpret_cast<float*>(slot_lds) : reinterpret_cast<float*>(a_lds0);
     if constexpr (S::KVG == 2) {
       if (kvg == 1) {
 #pragma unroll

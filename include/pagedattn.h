@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 4
+#define PA_ABI_VERSION 5
 
 /* Result codes.  Every host-checkable fault returns one of these before any
  * device work is enqueued (typed errors, as the acceptance criteria of "Add
@@ -202,7 +202,60 @@ typedef struct pa_args {
    * gate, output = round(attention * sigmoid(gate)) elementwise, fused into
    * the final write.  lse and output_f32 stay the ungated state. */
   const void *gate;
+
+  /* Optional fused prologue (ABI version 5) on the step's query and key
+   * rows, applied before anything else: the cached key is post-RoPE and the
+   * query attends post-RoPE.  The Qwen3.8 export issue (Per-layer behavior,
+   * Full attention, step 3) applies a Q/K OffsetRMSNorm and then an
+   * interleaved partial MRoPE, norm before RoPE and only once, with
+   * position_ids INT64 [3, N] (Packed graph contract); "WS2 CP-Aware
+   * Attention Contract" (RoPE / Position Semantics, the Qwen3-8B example)
+   * gives the rotation a base theta and a rotary_dim that fits the head and
+   * casts to the data type after RoPE.  Where the pages leave the form open
+   * it is a parameter:
+   *  q_norm_weight, k_norm_weight
+   *               float [head_size] (16-byte aligned) or NULL: OffsetRMSNorm of
+   *               every query (key) head row x: x * (1 + w) / sqrt(mean(x^2)
+   *               + norm_eps), in fp32.  NULL leaves that tensor unnormalised.
+   *  rotary_dim   0: no rotation; else a multiple of 16 up to head_size: the
+   *               first rotary_dim channels of every query and key head turn,
+   *               the others pass through.
+   *  position_ids int64 [3, num_tokens] (8-byte aligned), needed with
+   *               rotary_dim > 0: the three MRoPE position rows.
+   *  rope_theta   > 0: frequency pair i (i < rotary_dim / 2) turns by
+   *               position * rope_theta^(-2i / rotary_dim) radians, as
+   *               y1 = x1 cos - x2 sin, y2 = x2 cos + x1 sin.
+   *  mrope_section
+   *               pairs per position row, three counts summing to
+   *               rotary_dim / 2.
+   *  rope_flags   PA_ROPE_ADJACENT: pair i is channels (2i, 2i + 1), else
+   *               (i, i + rotary_dim / 2).  PA_ROPE_CONTIGUOUS: the first
+   *               mrope_section[0] pairs take row 0, the next [1] row 1, the
+   *               rest row 2; else interleaved: pair i takes row i mod 3 while
+   *               that row has pairs left, else the first row that has.
+   *               Other bits: PA_ERR_UNSUPPORTED.
+   * The normalised and rotated rows are rounded (nearest, ties to even) to
+   * the data type; those rows are what is cached (quantized with INT8 / INT4
+   * caches) and attended.  A token whose slot is -1 still has its query row
+   * transformed.  With either norm weight or rotary_dim > 0 the workspace
+   * also holds the transformed query rows (pa_workspace_bytes accounts for
+   * them).  Errors: rotary_dim not a multiple of 16 in [0, head_size]
+   * PA_ERR_UNSUPPORTED; sections not summing to rotary_dim / 2, a negative
+   * count or rope_theta <= 0 PA_ERR_SHAPE; position_ids NULL with
+   * rotary_dim > 0 PA_ERR_NULL_ARG; misaligned weights or positions
+   * PA_ERR_ALIGNMENT. */
+  const float *q_norm_weight;
+  const float *k_norm_weight;
+  float norm_eps;
+  int32_t rotary_dim;
+  const int64_t *position_ids;
+  float rope_theta;
+  int32_t mrope_section[3];
+  int32_t rope_flags;
 } pa_args;
+
+#define PA_ROPE_ADJACENT 1
+#define PA_ROPE_CONTIGUOUS 2
 
 /* Kernels launched by one call, in launch order (indices into kernel_events). */
 enum pa_kernel {

@@ -32,9 +32,10 @@ library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpage
 PA_DTYPE_F16 = 1
 PA_DTYPE_BF16 = 2
 PA_KV_SAME, PA_KV_INT8, PA_KV_INT4 = 0, 1, 2
+PA_ROPE_ADJACENT, PA_ROPE_CONTIGUOUS = 1, 2
 _CODE_DTYPES = {torch.int8: PA_KV_INT8, torch.uint8: PA_KV_INT4}  # cache dtype -> kv_quant
 _DTYPE_CODES = {torch.float16: PA_DTYPE_F16, torch.bfloat16: PA_DTYPE_BF16}
-ABI_VERSION = 4
+ABI_VERSION = 5
 KERNELS = ("scatter_plan", "decode", "merge", "prefill")  # enum pa_kernel order
 NOALLOC_SCRATCH_BYTES = 64 << 20  # PA_NOALLOC_SCRATCH_BYTES
 STATUS = {
@@ -82,6 +83,14 @@ class PaArgs(ctypes.Structure):
         ("k_scale", ctypes.c_void_p),
         ("v_scale", ctypes.c_void_p),
         ("gate", ctypes.c_void_p),
+        ("q_norm_weight", ctypes.c_void_p),
+        ("k_norm_weight", ctypes.c_void_p),
+        ("norm_eps", ctypes.c_float),
+        ("rotary_dim", ctypes.c_int32),
+        ("position_ids", ctypes.c_void_p),
+        ("rope_theta", ctypes.c_float),
+        ("mrope_section", ctypes.c_int32 * 3),
+        ("rope_flags", ctypes.c_int32),
     ]
 
 
@@ -161,11 +170,13 @@ def make_args(query, key, value, key_cache, value_cache, cumulative_sequence_len
               workspace: Optional[torch.Tensor] = None,
               k_scale: Optional[torch.Tensor] = None,
               v_scale: Optional[torch.Tensor] = None,
-              gate: Optional[torch.Tensor] = None) -> PaArgs:
+              gate: Optional[torch.Tensor] = None,
+              prologue: Optional[dict] = None) -> PaArgs:
     """Fill a PaArgs from tensors (no checks beyond what marshalling needs:
     the library validates shapes, dtypes and alignment itself).  int8 (INT8)
     or uint8 (INT4, two codes per byte) caches with fp32 ``k_scale``/``v_scale``
-    [kv_num_heads, head_size] select a quantized cache path."""
+    [kv_num_heads, head_size] select a quantized cache path.  ``prologue``:
+    the fused Q/K norm and rotation (see set_prologue)."""
     for name, t in (("query", query), ("key", key), ("value", value), ("key_cache", key_cache),
                     ("value_cache", value_cache),
                     ("cumulative_sequence_length", cumulative_sequence_length),
@@ -220,7 +231,33 @@ def make_args(query, key, value, key_cache, value_cache, cumulative_sequence_len
     if workspace is not None:
         a.workspace = workspace.data_ptr()
         a.workspace_bytes = workspace.numel() * workspace.element_size()
+    if prologue is not None:
+        set_prologue(a, **prologue)
     return a
+
+
+def set_prologue(a: PaArgs, *, position_ids: Optional[torch.Tensor] = None, rotary_dim: int = 0,
+                 theta: float = 1.0e6, sections=(0, 0, 0), interleaved: bool = True,
+                 adjacent: bool = False, q_norm_weight: Optional[torch.Tensor] = None,
+                 k_norm_weight: Optional[torch.Tensor] = None, eps: float = 1e-6) -> None:
+    """The fused prologue's fields of pa_args: OffsetRMSNorm of the query and
+    key heads (fp32 weights [head_size], either may be None), then the partial
+    MRoPE of the first ``rotary_dim`` channels (0: none) with int64
+    ``position_ids`` [3, num_tokens], base ``theta``, pairs per position row
+    ``sections``, interleaved or contiguous sections, half-split or adjacent
+    pairs.  Keyword names follow the oracle's qk_prologue."""
+    for name, t, dt in (("position_ids", position_ids, torch.int64), ("q_norm_weight", q_norm_weight, torch.float32),
+                        ("k_norm_weight", k_norm_weight, torch.float32)):
+        if t is not None and (t.dtype != dt or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous {dt} tensor")
+    a.q_norm_weight = _ptr(q_norm_weight)
+    a.k_norm_weight = _ptr(k_norm_weight)
+    a.norm_eps = float(eps)
+    a.rotary_dim = int(rotary_dim)
+    a.position_ids = _ptr(position_ids)
+    a.rope_theta = float(theta)
+    a.mrope_section = (ctypes.c_int32 * 3)(*[int(x) for x in sections])
+    a.rope_flags = (PA_ROPE_ADJACENT if adjacent else 0) | (0 if interleaved else PA_ROPE_CONTIGUOUS)
 
 
 def workspace_bytes(args: PaArgs) -> int:
@@ -245,6 +282,7 @@ def paged_attention_noalloc(query, key, value, key_cache, value_cache, cumulativ
                             k_scale: Optional[torch.Tensor] = None,
                             v_scale: Optional[torch.Tensor] = None,
                             gate: Optional[torch.Tensor] = None,
+                            prologue: Optional[dict] = None,
                             stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
     """pa_paged_attention_noalloc: paged_attention() with the library's own
     per-GPU scratch as workspace.  Nothing is allocated here either: the
@@ -253,7 +291,7 @@ def paged_attention_noalloc(query, key, value, key_cache, value_cache, cumulativ
     args = make_args(query, key, value, key_cache, value_cache, cumulative_sequence_length,
                      past_seqlens, block_table, slot_mapping, output, num_heads=num_heads,
                      kv_num_heads=kv_num_heads, scale=scale, is_causal=is_causal,
-                     k_scale=k_scale, v_scale=v_scale, gate=gate)
+                     k_scale=k_scale, v_scale=v_scale, gate=gate, prologue=prologue)
     for name, t in (("lse", lse), ("output_f32", output_f32)):
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous float32 tensor")
@@ -278,7 +316,8 @@ def paged_attention(query: torch.Tensor, key: Optional[torch.Tensor],
                     output_f32: Optional[torch.Tensor] = None,
                     k_scale: Optional[torch.Tensor] = None,
                     v_scale: Optional[torch.Tensor] = None,
-                    gate: Optional[torch.Tensor] = None):
+                    gate: Optional[torch.Tensor] = None,
+                    prologue: Optional[dict] = None):
     """Scatter the step's K/V into the caches (in place) and return the
     attention output [num_tokens, num_heads * head_size].
 
@@ -298,7 +337,11 @@ def paged_attention(query: torch.Tensor, key: Optional[torch.Tensor],
 
     ``gate``: optional [num_tokens, num_heads * head_size] tensor of the
     query's dtype; the output is then the attention times sigmoid(gate),
-    rounded once (``lse`` and ``output_f32`` stay ungated)."""
+    rounded once (``lse`` and ``output_f32`` stay ungated).
+
+    ``prologue``: optional dict of the fused Q/K OffsetRMSNorm and partial
+    MRoPE applied to the step's query and key rows first (set_prologue's
+    keyword arguments, device tensors for position_ids and the weights)."""
     lib = library()
     dev = query.device
     if dev.type != "cuda":
@@ -316,7 +359,7 @@ def paged_attention(query: torch.Tensor, key: Optional[torch.Tensor],
         args = make_args(query, key, value, key_cache, value_cache, cumulative_sequence_length,
                          past_seqlens, block_table, slot_mapping, output, num_heads=num_heads,
                          kv_num_heads=kv_num_heads, scale=scale, is_causal=is_causal,
-                         k_scale=k_scale, v_scale=v_scale, gate=gate)
+                         k_scale=k_scale, v_scale=v_scale, gate=gate, prologue=prologue)
         if return_lse and lse is None:
             lse = torch.empty((query.shape[0], num_heads), dtype=torch.float32, device=dev)
         for name, t in (("lse", lse), ("output_f32", output_f32)):

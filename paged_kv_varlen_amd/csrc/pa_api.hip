@@ -27,6 +27,8 @@ struct Resolved {
   bool packed;
   int kq;  // cache codes: 0 (the caches hold T), 8 (INT8) or 4 (INT4)
   float scale;
+  bool pro;  // fused prologue: a norm weight given, or rotary_dim > 0
+  int rd;    // rotary_dim
 };
 
 pa_status resolve(const pa_args* a, Resolved* r) {
@@ -72,6 +74,17 @@ pa_status resolve(const pa_args* a, Resolved* r) {
   r->NB = a->num_blocks;
   r->MB = a->max_blocks_per_seq;
   r->scale = a->scale == 0.f ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(D))) : a->scale;
+  // fused prologue
+  if (a->rotary_dim < 0 || a->rotary_dim > D || a->rotary_dim % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if ((a->rope_flags & ~(PA_ROPE_ADJACENT | PA_ROPE_CONTIGUOUS)) != 0) return PA_ERR_UNSUPPORTED;
+  if (a->rotary_dim > 0) {
+    if (!(a->rope_theta > 0.f) || !std::isfinite(a->rope_theta)) return PA_ERR_SHAPE;
+    const int64_t sum = static_cast<int64_t>(a->mrope_section[0]) + a->mrope_section[1] + a->mrope_section[2];
+    if (a->mrope_section[0] < 0 || a->mrope_section[1] < 0 || a->mrope_section[2] < 0 || sum != a->rotary_dim / 2)
+      return PA_ERR_SHAPE;
+  }
+  r->rd = a->rotary_dim;
+  r->pro = a->q_norm_weight != nullptr || a->k_norm_weight != nullptr || a->rotary_dim > 0;
   return PA_OK;
 }
 
@@ -114,6 +127,8 @@ WorkspaceLayout layout(const Resolved& r) {
   off = align256(off + 2 * W * kDecodeUnitHeads * sizeof(float));
   w.part_o = off;
   off = align256(off + 2 * W * kDecodeUnitHeads * r.D * sizeof(float));
+  w.q_pro = off;  // the prologue's query rows [N, H*D] in T
+  if (r.pro) off = align256(off + static_cast<size_t>(r.N) * r.H * r.D * sizeof(uint16_t));
   w.total = off;
   return w;
 }
@@ -235,6 +250,10 @@ pa_status prepare(const pa_args* a, Resolved* r) {
     if (a->k_scale == nullptr || a->v_scale == nullptr) return PA_ERR_NULL_ARG;
     if (!aligned16(a->k_scale) || !aligned16(a->v_scale)) return PA_ERR_ALIGNMENT;
   }
+  if (r->rd > 0 && a->position_ids == nullptr) return PA_ERR_NULL_ARG;
+  if (!aligned16(a->q_norm_weight) || !aligned16(a->k_norm_weight) ||
+      (reinterpret_cast<uintptr_t>(a->position_ids) & 7u) != 0)
+    return PA_ERR_ALIGNMENT;
   return PA_OK;
 }
 
@@ -299,13 +318,31 @@ pa_status enqueue(const pa_args* a, const Resolved& r, const WorkspaceLayout& w,
   sp.bf16 = a->dtype == PA_DTYPE_BF16 ? 1 : 0;
   sp.k_scale = r.kq != 0 ? a->k_scale : nullptr;
   sp.v_scale = r.kq != 0 ? a->v_scale : nullptr;
+  if (r.pro) {
+    sp.pro = 1;
+    sp.q_src = q;
+    sp.q_src_stride = qw;
+    sp.q_out = reinterpret_cast<uint16_t*>(ws + w.q_pro);
+    sp.num_heads = r.H;
+    sp.head_size = r.D;
+    sp.q_norm_w = a->q_norm_weight;
+    sp.k_norm_w = a->k_norm_weight;
+    sp.norm_eps = a->norm_eps;
+    sp.rotary_dim = r.rd;
+    sp.position_ids = a->position_ids;
+    sp.rope_log2_theta = r.rd > 0 ? std::log2(static_cast<double>(a->rope_theta)) : 0.0;
+    sp.sec0 = a->mrope_section[0];
+    sp.sec1 = a->mrope_section[1];
+    sp.sec2 = a->mrope_section[2];
+    sp.rope_flags = a->rope_flags;
+  }
   mark(PA_KERNEL_SCATTER_PLAN, 0);
   if (launch_scatter_plan(sp, s) != hipSuccess) return PA_ERR_HIP;
   mark(PA_KERNEL_SCATTER_PLAN, 1);
 
   AttnParams ap{};
-  ap.q = q;
-  ap.q_stride = qw;
+  ap.q = r.pro ? sp.q_out : q;  // the prologue's rows, when there is one
+  ap.q_stride = r.pro ? static_cast<int64_t>(r.H) * r.D : qw;
   ap.key_cache = sp.key_cache;
   ap.value_cache = sp.value_cache;
   ap.cum = sp.cum;

@@ -125,6 +125,7 @@ struct WorkspaceLayout {
   size_t pf_items;     // int2[max_pf_items]    (sequence, half-tile pair)
   size_t part_lse;     // float[2 * waves * 16]
   size_t part_o;       // float[2 * waves * 16 * D]
+  size_t q_pro;        // T [N, H * D]: query rows after the fused prologue (when there is one)
   size_t total;
   int64_t max_pf_items;
   int decode_waves;    // W
@@ -159,6 +160,22 @@ struct ScatterPlanParams {
   const float* v_scale;
   int32_t kq;                  // caches hold codes: 8 (INT8), 4 (INT4), else 0
   int32_t bf16;                // step rows are bf16 (else fp16)
+  // fused prologue (pro != 0): OffsetRMSNorm and partial MRoPE of the step's
+  // query and key rows before they are cached and attended
+  int32_t pro;
+  const uint16_t* q_src;       // first Q element of token 0
+  int64_t q_src_stride;        // elements between tokens' Q rows
+  uint16_t* q_out;             // [N, H*D] transformed query rows
+  int32_t num_heads;
+  int32_t head_size;
+  const float* q_norm_w;       // [D] or null
+  const float* k_norm_w;       // [D] or null
+  float norm_eps;
+  int32_t rotary_dim;          // 0: no rotation
+  const int64_t* position_ids; // [3, N]
+  double rope_log2_theta;      // log2 of the base
+  int32_t sec0, sec1, sec2;    // pairs per position row
+  int32_t rope_flags;          // PA_ROPE_ADJACENT | PA_ROPE_CONTIGUOUS
 };
 
 struct AttnParams {

@@ -134,6 +134,186 @@ __device__ void plan(const ScatterPlanParams& p) {
   }
 }
 
+// ---- fused prologue --------------------------------------------------------
+// The Qwen3.8 export issue (Per-layer behavior, Full attention, step 3) puts a
+// Q/K OffsetRMSNorm and then an interleaved partial MRoPE before the
+// attention; "WS2 CP-Aware Attention Contract" (RoPE / Position Semantics)
+// caches K after RoPE and casts to the data type after RoPE.  A head row of D
+// elements is held by D / 8 consecutive lanes (one 16-byte chunk of 8
+// elements each), so a wave holds whole rows: the norm's sum of squares is a
+// butterfly over those lanes and the partner chunk of a rotation pair is
+// fetched from the lane rotary_dim / 16 away.
+
+__device__ inline float elem_value(uint32_t bits, int bf16) {
+  return bf16 ? __uint_as_float(bits << 16) : static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+}
+// x rounded to the data type (nearest, ties to even), as a 16-bit pattern
+__device__ inline uint32_t elem_bits(float x, int bf16) {
+  return bf16 ? __builtin_bit_cast(uint16_t, static_cast<__bf16>(x))
+              : __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+
+// position row (0, 1 or 2) of frequency pair i: contiguous sections, or
+// interleaved (pair j takes row j mod 3 while that row has pairs left, else
+// the first row that has)
+__device__ inline int mrope_row(int i, int s0, int s1, int s2, bool contiguous) {
+  if (contiguous) return i < s0 ? 0 : i < s0 + s1 ? 1 : 2;
+  int u0 = 0, u1 = 0, u2 = 0, c = 0;
+  for (int j = 0; j <= i; ++j) {
+    c = j % 3;
+    if ((c == 0 && u0 >= s0) || (c == 1 && u1 >= s1) || (c == 2 && u2 >= s2)) c = u0 < s0 ? 0 : u1 < s1 ? 1 : 2;
+    u0 += c == 0;
+    u1 += c == 1;
+    u2 += c == 2;
+  }
+  return c;
+}
+
+constexpr int kMaxRotaryPairs = 128;  // rotary_dim / 2 for head sizes up to 256
+
+// 8 values of a chunk -> the cache: 16-bit patterns, or INT8 / INT4 codes of
+// the values with their channel scales (fp32 IEEE quotient, nearest even,
+// clamped)
+__device__ inline void store_chunk(const ScatterPlanParams& p, bool is_v, int cc, int64_t dst, const float (&x)[8],
+                                   const uint32_t (&bits)[8]) {
+  if (p.kq == 0) {
+    uint16_t* cache = is_v ? p.value_cache : p.key_cache;
+    reinterpret_cast<uint4*>(cache + dst)[cc] =
+        make_uint4(bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16), bits[4] | (bits[5] << 16),
+                   bits[6] | (bits[7] << 16));
+    return;
+  }
+  const float lim = p.kq == 4 ? 7.f : 127.f;
+  const float4* sc = reinterpret_cast<const float4*>((is_v ? p.v_scale : p.k_scale) + 8 * cc);
+  const float4 s0 = sc[0], s1 = sc[1];
+  const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  uint32_t packed[2] = {0u, 0u}, nib = 0u;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t code = static_cast<uint32_t>(static_cast<int>(fminf(fmaxf(rintf(x[e] / sv[e]), -lim), lim)));
+    packed[e >> 2] |= (code & 0xffu) << (8 * (e & 3));
+    nib |= (code & 0xfu) << (4 * e);
+  }
+  int8_t* cache = reinterpret_cast<int8_t*>(is_v ? p.value_cache : p.key_cache);
+  if (p.kq == 4)  // a row is row_elems / 2 bytes
+    *reinterpret_cast<uint32_t*>(cache + dst / 2 + 4 * cc) = nib;
+  else
+    *reinterpret_cast<uint2*>(cache + dst + 8 * cc) = make_uint2(packed[0], packed[1]);
+}
+
+// Norm and rotation of `heads` head rows starting at src (token t's row),
+// rounded to the data type: into q_dst (queries), or into the key cache row
+// dst (keys; none when dst < 0).  cs: (cos, sin) of every frequency pair.
+__device__ void prologue_rows(const ScatterPlanParams& p, const uint16_t* src, int heads, const float* w,
+                              uint16_t* q_dst, int64_t dst, const float2* cs) {
+  const int D = p.head_size, cpr = D / 8, rd = p.rotary_dim;
+  const int lane = threadIdx.x & 63;
+  const int half8 = rd / 16;  // chunks in each half of the rotated channels
+  const bool adjacent = (p.rope_flags & 1) != 0;
+  for (int c = threadIdx.x; c < heads * cpr; c += blockDim.x) {  // (whole rows per wave)
+    const int k = c % cpr;  // chunk within the head row
+    const uint4 raw = reinterpret_cast<const uint4*>(src)[c];
+    const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = elem_value((wv[e >> 1] >> (16 * (e & 1))) & 0xffffu, p.bf16);
+    if (w != nullptr) {  // OffsetRMSNorm: x * (1 + w) / sqrt(mean(x^2) + eps)
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
+      for (int off = 1; off < cpr; off <<= 1) ss += __shfl_xor(ss, off);
+      const float r = 1.f / sqrtf(ss / static_cast<float>(D) + p.norm_eps);
+      const float4 w0 = reinterpret_cast<const float4*>(w + 8 * k)[0], w1 = reinterpret_cast<const float4*>(w + 8 * k)[1];
+      const float wk[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = v[e] * r * (1.f + wk[e]);
+    }
+    if (rd > 0) {  // y1 = x1 cos - x2 sin, y2 = x2 cos + x1 sin
+      if (adjacent) {  // pairs (2i, 2i + 1) inside the chunk
+        if (8 * k < rd) {
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const float2 a = cs[4 * k + e / 2];
+            const float x1 = v[e], x2 = v[e + 1];
+            v[e] = x1 * a.x - x2 * a.y;
+            v[e + 1] = x2 * a.x + x1 * a.y;
+          }
+        }
+      } else {  // pairs (i, i + rd / 2): the partner chunk is half8 lanes away
+        const int partner = k < half8 ? lane + half8 : k < 2 * half8 ? lane - half8 : lane;
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = __shfl(v[e], partner);
+        if (k < half8) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float2 a = cs[8 * k + e];
+            v[e] = v[e] * a.x - pv[e] * a.y;
+          }
+        } else if (k < 2 * half8) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float2 a = cs[8 * (k - half8) + e];
+            v[e] = v[e] * a.x + pv[e] * a.y;
+          }
+        }
+      }
+    }
+    uint32_t b[8];
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      b[e] = elem_bits(v[e], p.bf16);
+      x[e] = elem_value(b[e], p.bf16);  // the rounded value (what codes quantize)
+    }
+    if (q_dst != nullptr) {
+      reinterpret_cast<uint4*>(q_dst)[c] = make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16),
+                                                      b[4] | (b[5] << 16), b[6] | (b[7] << 16));
+    } else if (dst >= 0) {
+      store_chunk(p, false, c, dst, x, b);
+    }
+  }
+}
+
+// the prologue for token t: angles, query rows, key rows, then the value row
+// as usual (bit copy or codes); the key and value rows only when slot >= 0
+__device__ void prologue_token(const ScatterPlanParams& p, int64_t t, int64_t slot) {
+  __shared__ float2 cs_lds[kMaxRotaryPairs];
+  const int rd = p.rotary_dim;
+  if (rd > 0) {
+    for (int i = threadIdx.x; i < rd / 2; i += blockDim.x) {
+      const int row = mrope_row(i, p.sec0, p.sec1, p.sec2, (p.rope_flags & 2) != 0);
+      const double pos = static_cast<double>(p.position_ids[static_cast<int64_t>(row) * p.num_tokens + t]);
+      // angle in fp64 (positions up to 2^53 are exact), reduced to [-pi, pi]
+      const double inv = exp2(-2.0 * i / rd * p.rope_log2_theta);
+      double ang = pos * inv;
+      ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
+      double sn, cn;
+      sincos(ang, &sn, &cn);
+      cs_lds[i] = make_float2(static_cast<float>(cn), static_cast<float>(sn));
+    }
+    __syncthreads();
+  }
+  prologue_rows(p, p.q_src + t * p.q_src_stride, p.num_heads, p.q_norm_w,
+                p.q_out + t * static_cast<int64_t>(p.num_heads) * p.head_size, -1, cs_lds);
+  if (slot < 0) return;
+  const int64_t dst = slot * p.row_elems;
+  prologue_rows(p, p.key_src + t * p.src_stride, p.row_elems / p.head_size, p.k_norm_w, nullptr, dst, cs_lds);
+  const int chunks = p.row_elems >> 3;
+  for (int cc = threadIdx.x; cc < chunks; cc += blockDim.x) {
+    const uint4 raw = reinterpret_cast<const uint4*>(p.value_src + t * p.src_stride)[cc];
+    const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint32_t b[8];
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      b[e] = (wv[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+      x[e] = elem_value(b[e], p.bf16);
+    }
+    store_chunk(p, true, cc, dst, x, b);
+  }
+}
+
 __global__ __launch_bounds__(kPlanThreads) void scatter_plan_kernel(ScatterPlanParams p) {
   // workgroup 0 plans (dispatched first, it overlaps the scatter of long
   // calls); workgroup t + 1 scatters token t
@@ -163,6 +343,10 @@ __global__ __launch_bounds__(kPlanThreads) void scatter_plan_kernel(ScatterPlanP
     slot = static_cast<int64_t>(p.block_table[static_cast<int64_t>(b) * p.max_blocks +
                                               pos / p.block_size]) * p.block_size +
            pos % p.block_size;
+  }
+  if (p.pro) {  // (every token: its query row is transformed even when its slot is -1)
+    prologue_token(p, t, slot);
+    return;
   }
   if (slot < 0) return;
   const int chunks = p.row_elems >> 3;  // 16-byte pieces per row

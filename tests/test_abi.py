@@ -174,7 +174,7 @@ def test_status_strings():
     lib = pa.library()
     for s in range(9):
         assert lib.pa_status_string(s)
-    assert lib.pa_abi_version() == 4
+    assert lib.pa_abi_version() == 5
 
 
 def merge_args(**kw):
@@ -243,3 +243,36 @@ def test_noalloc_host_validation(case, expect):
 
 def test_noalloc_null_args_pointer():
     assert pa.library().pa_paged_attention_noalloc(None, None) == NULL
+
+
+def sections(a, b, c):
+    return (ctypes.c_int32 * 3)(a, b, c)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(rotary_dim=8), UNSUP),                          # not a multiple of 16
+    (dict(rotary_dim=80), UNSUP),                         # wider than the head (D=64)
+    (dict(rotary_dim=-16), UNSUP),
+    (dict(rope_flags=4), UNSUP),                          # unknown flag
+    (dict(rotary_dim=32, rope_theta=1e6, mrope_section=sections(16, 0, 0), position_ids=FAKE), WS),
+    (dict(rotary_dim=64, rope_theta=1e4, mrope_section=sections(11, 11, 10), position_ids=FAKE,
+          rope_flags=3), WS),                             # full rotation, both flags
+    (dict(rotary_dim=32, rope_theta=1e6, mrope_section=sections(10, 0, 0), position_ids=FAKE), SHAPE),
+    (dict(rotary_dim=32, rope_theta=1e6, mrope_section=sections(17, -1, 0), position_ids=FAKE), SHAPE),
+    (dict(rotary_dim=32, rope_theta=0.0, mrope_section=sections(16, 0, 0), position_ids=FAKE), SHAPE),
+    (dict(rotary_dim=32, rope_theta=1e6, mrope_section=sections(16, 0, 0)), NULL),  # no positions
+    (dict(rotary_dim=32, rope_theta=1e6, mrope_section=sections(16, 0, 0), position_ids=FAKE + 4), ALIGN),
+    (dict(q_norm_weight=FAKE + 4), ALIGN),                # norm weights need 16-byte alignment
+    (dict(k_norm_weight=FAKE + 8), ALIGN),
+    (dict(q_norm_weight=FAKE, k_norm_weight=FAKE), WS),   # norms alone pass validation
+    (dict(mrope_section=sections(1, 2, 3)), WS),          # sections are ignored without rotation
+])
+def test_prologue_host_validation(case, expect):
+    assert status(args(**case)) == expect
+
+
+def test_prologue_workspace_holds_the_query_rows():
+    plain = pa.workspace_bytes(args())
+    with_norm = pa.workspace_bytes(args(q_norm_weight=FAKE))
+    # the transformed query rows: num_tokens * num_heads * head_size 16-bit values
+    assert with_norm - plain >= 4 * 4 * 64 * 2

@@ -813,3 +813,154 @@ def test_side_stream_without_workspace():
     junk.fill_(0xFF)
     torch.cuda.synchronize()
     check(b, gpu=(to_host(out), to_host(d.kc), to_host(d.vc)))
+
+
+# ------------------------------------------------------------------ fused prologue: Q/K OffsetRMSNorm + partial MRoPE
+#
+# The kernels normalise and rotate in fp32 and round once to the data type;
+# the oracle does the same steps in fp64.  So every cache slot the call does
+# not write, and every value row, stays bit-exact.  A key element written
+# through the prologue must lie within one unit in the last place of the
+# exact (fp64) value plus the fp32 arithmetic's error: a handful of fp32
+# units (2^-24) of the head row's largest element, bounded here by
+# 2^-21 * max|row| (the products and sums of the norm and the rotation round
+# at the row's scale, so a result that nearly cancels, x1 cos - x2 sin close
+# to 0, carries an absolute error of that size, several units of its own
+# last place).  With INT8 / INT4 caches the codes lie within one code.
+# Outputs keep the bar of their data type.
+
+def prologue_dev(kw):
+    out = dict(kw)
+    for n in ("position_ids", "q_norm_weight", "k_norm_weight"):
+        if kw.get(n) is not None:
+            out[n] = to_dev(np.ascontiguousarray(kw[n]))
+    return out
+
+
+def token_slots(b: W.Batch) -> np.ndarray:
+    if b.slot_mapping is not None:
+        return b.slot_mapping.astype(np.int64)
+    pos = W.token_positions(b)
+    seq = np.repeat(np.arange(b.batch_size), b.q_lens)
+    return b.block_table[seq, pos // b.block_size].astype(np.int64) * b.block_size + pos % b.block_size
+
+
+def unit_in_last_place(v: np.ndarray, dtype: str) -> np.ndarray:
+    """Spacing of the data type's numbers at |v| (fp64)."""
+    a = np.maximum(np.abs(v), 2.0 ** -14 if dtype == "f16" else 2.0 ** -126)
+    e = np.floor(np.log2(a))
+    return np.exp2(e - (10 if dtype == "f16" else 7))
+
+
+def check_prologue(b: W.Batch, kw: dict, tag=""):
+    say(f"[gpu] prologue{tag} {b.name} {b.dtype} kv={b.kv_quant} N={b.num_tokens} D={b.head_size} "
+        f"rd={kw.get('rotary_dim')} norm={kw.get('q_norm_weight') is not None} "
+        f"adjacent={kw.get('adjacent')} interleaved={kw.get('interleaved')}")
+    d = DevBatch(b)
+    out = d.run(prologue=prologue_dev(kw))
+    torch.cuda.synchronize()
+    ref, rkc, rvc = oracle.paged_attention(b.query, b.key, b.value, b.key_cache, b.value_cache, b.cum,
+                                           b.past, b.block_table, b.slot_mapping, num_heads=b.num_heads,
+                                           kv_num_heads=b.kv_num_heads, scale=b.scale, k_scale=b.k_scale,
+                                           v_scale=b.v_scale, prologue=kw)
+    kc, vc = to_host(d.kc), to_host(d.vc)
+    assert np.array_equal(raw_bits(vc), raw_bits(rvc)), "value_cache differs"
+    nslot = b.num_blocks * b.block_size
+    slots = token_slots(b)
+    written = np.zeros(nslot, dtype=bool)
+    written[slots[slots >= 0]] = True
+    kg, kr = raw_bits(kc).reshape(nslot, -1), raw_bits(rkc).reshape(nslot, -1)
+    assert np.array_equal(kg[~written], kr[~written]), "key_cache differs outside the written slots"
+    toks = np.nonzero(slots >= 0)[0]
+    if toks.size:
+        Q, K, _, _, _ = oracle.resolve_call(b.query, b.key, b.value, b.num_heads, b.kv_num_heads, b.scale)
+        _, kex = oracle.qk_prologue(Q, K, rounded=False, **kw)      # exact key rows [N, Hkv, D]
+        rows = slots[toks]
+        if b.kv_quant == "none":
+            got = as_f64(kg[rows].view(np.uint16 if b.dtype == "bf16" else np.float16))
+            exact = kex[toks].reshape(got.shape)
+            D = b.head_size
+            rowmax = np.repeat(np.max(np.abs(exact.reshape(-1, D)), axis=1), D).reshape(exact.shape)
+            ulp = unit_in_last_place(exact, b.dtype)
+            excess = np.abs(got - exact) - ulp
+            worst = float(np.max(np.abs(got - exact) / ulp))
+            flips = int(np.sum(kg[rows] != kr[rows]))
+            i = np.unravel_index(np.argmax(excess / (2.0 ** -21 * rowmax)), exact.shape)
+            say(f"      written key rows: {rows.size}, worst |gpu - exact| {worst:.3f} ulp, "
+                f"{flips} of {kg[rows].size} roundings differ from the oracle's; "
+                f"{int(np.sum(excess > 0))} beyond one ulp, largest at exact {exact[i]:.4g} "
+                f"got {got[i]:.4g} (row max {rowmax[i]:.3g})")
+            assert np.all(excess <= 2.0 ** -21 * rowmax)
+        else:
+            cg, cr = kc.reshape(nslot, -1)[rows], rkc.reshape(nslot, -1)[rows]
+            if b.kv_quant == "int4":
+                cg, cr = oracle.unpack_int4(cg), oracle.unpack_int4(cr)
+            diff = np.abs(cg.astype(np.int64) - cr.astype(np.int64))
+            say(f"      written key rows: {rows.size}, codes differing by one: {int(np.sum(diff == 1))}")
+            assert diff.max() <= 1
+    got = as_f64(to_host(out))
+    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    say(f"      outputs: max|err| {err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= tol(b)
+
+
+PROLOGUE_SWEEP = [  # (sweep case, rotary_dim as a fraction of D, spatial, adjacent, interleaved, norm)
+    (0, 0.5, False, False, True, True),
+    (1, 1.0, True, False, True, True),
+    (2, 0.25, True, True, True, True),
+    (3, 0.5, False, False, False, True),
+    (4, 1.0, True, True, False, False),   # rotation only (G=3)
+    (5, 0.0, False, False, True, True),   # norm only (G=64)
+    (6, 0.5, True, False, True, True),    # G=5, block_size 48
+]
+
+
+@pytest.mark.parametrize("case", range(len(PROLOGUE_SWEEP)))
+@pytest.mark.parametrize("packed", [False, True])
+def test_prologue_sweep(case, packed):
+    i, frac, spatial, adjacent, interleaved, norm = PROLOGUE_SWEEP[case]
+    q, p, H, Hkv, D, bs = SWEEP[i]
+    n = sum(q)
+    b = W.make_batch(q, p, num_heads=H, kv_num_heads=Hkv, head_size=D, block_size=bs, seed=800 + case,
+                     packed=packed, slot_mode="drop" if packed else None,
+                     drop_count=max(1, n // 20) if packed else 0, name=f"prologue_sweep{case}")
+    kw = W.prologue_inputs(b, 810 + case, rotary_dim=int(D * frac), norm=norm, spatial=spatial,
+                           adjacent=adjacent, interleaved=interleaved)
+    if frac == 0.0:
+        kw.update(rotary_dim=0)
+    check_prologue(b, kw)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("kvq", ["none", "int8", "int4"])
+def test_prologue_tiny(dtype, kvq):
+    b = W.tiny(0, dtype=dtype, kv_quant=kvq)
+    check_prologue(b, W.prologue_inputs(b, 820, rotary_dim=32, spatial=True))
+
+
+def test_prologue_long_prefill():
+    # one rank's share of a 32/8 model, rotating half of each 128-wide head
+    b = W.long_prefill(0)
+    check_prologue(b, W.prologue_inputs(b, 830, rotary_dim=64))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prologue_mixed(dtype):
+    b = W.mixed(0, dtype=dtype)
+    check_prologue(b, W.prologue_inputs(b, 831, rotary_dim=128, adjacent=dtype == "bf16",
+                                        interleaved=dtype == "f16"))
+
+
+@pytest.mark.parametrize("kvq", ["none", "int8"])
+def test_prologue_head_size_256(kvq):
+    # head size 256 with a quarter of the channels rotating, spatial positions
+    q, p, H, Hkv, bs = HD256[0]
+    b = W.make_batch(q, p, num_heads=H, kv_num_heads=Hkv, head_size=256, block_size=bs, seed=840,
+                     name=f"prologue_hd256_{kvq}", dtype="bf16", kv_quant=kvq, packed=True,
+                     slot_mode="drop", drop_count=5)
+    check_prologue(b, W.prologue_inputs(b, 841, rotary_dim=64, spatial=True))
+
+
+def test_prologue_pure_decode_full():
+    b = W.pure_decode(0)
+    check_prologue(b, W.prologue_inputs(b, 850, rotary_dim=64))

@@ -86,11 +86,13 @@ def counter_means(csv_path: str, symbol: str) -> dict:
     return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
 
 
-def variant_suffix(dtype="f16", head_size=0, kv_quant="none", gate=False) -> str:
+def variant_suffix(dtype="f16", head_size=0, kv_quant="none", gate=False, prologue=0) -> str:
     """Names a workload variant in profile file names ('' for the workloads as
-    defined: fp16 data and caches, their own head size, no output gate)."""
+    defined: fp16 data and caches, their own head size, no output gate, no
+    fused prologue)."""
     return ("" if dtype == "f16" else f"_{dtype}") + (f"_hd{head_size}" if head_size else "") + \
-        ("" if kv_quant == "none" else f"_{kv_quant}") + ("_gate" if gate else "")
+        ("" if kv_quant == "none" else f"_{kv_quant}") + ("_gate" if gate else "") + \
+        (f"_rope{prologue}" if prologue else "")
 
 
 VARIANT = {"suffix": ""}  # set by main() from --dtype / --head-size / --kv-quant
@@ -137,7 +139,7 @@ def measured_traffic(kernel: str, workload: str):
 class Runner:
     """Device copies of one batch plus the preallocated output and workspace."""
 
-    def __init__(self, batch, torch, pa, gate=None):
+    def __init__(self, batch, torch, pa, gate=None, prologue=None):
         self.torch, self.pa, self.b = torch, pa, batch
         dev = "cuda:0"
 
@@ -154,13 +156,19 @@ class Runner:
         self.table, self.slots = to(batch.block_table), to(batch.slot_mapping)
         self.ks, self.vs = to(batch.k_scale), to(batch.v_scale)  # quantized caches only
         self.gate = to(gate)  # optional output gate
+        self.prologue = None  # optional fused Q/K norm and rotation
+        if prologue is not None:
+            self.prologue = dict(prologue)
+            for n in ("position_ids", "q_norm_weight", "k_norm_weight"):
+                if prologue.get(n) is not None:
+                    self.prologue[n] = to(prologue[n])
         D = batch.head_size
         self.out = torch.empty((batch.num_tokens, batch.num_heads * D), dtype=self.q.dtype,
                                device=dev)
         args = pa.make_args(self.q, self.k, self.v, self.kc, self.vc, self.cum, self.past,
                             self.table, self.slots, self.out, num_heads=batch.num_heads,
                             kv_num_heads=batch.kv_num_heads, scale=batch.scale,
-                            k_scale=self.ks, v_scale=self.vs, gate=self.gate)
+                            k_scale=self.ks, v_scale=self.vs, gate=self.gate, prologue=self.prologue)
         self.ws = torch.empty(max(1, pa.workspace_bytes(args)), dtype=torch.uint8, device=dev)
         self.stream = torch.cuda.current_stream()
 
@@ -170,7 +178,8 @@ class Runner:
                                 self.table, self.slots, num_heads=b.num_heads,
                                 kv_num_heads=b.kv_num_heads, scale=b.scale, output=self.out,
                                 workspace=self.ws, kernel_events=events, k_scale=self.ks,
-                                v_scale=self.vs, gate=self.gate, stream=self.stream)
+                                v_scale=self.vs, gate=self.gate, stream=self.stream,
+                                prologue=self.prologue)
 
 
 def stats_ms(xs) -> dict:
@@ -226,14 +235,15 @@ def run_steps(r, steps, scrub, torch, kernel_events=False):
 
 
 def time_workload(name: str, steps: int, warmup: int, seed: int, torch, pa, W, scrub,
-                  dtype="f16", head_size=0, kv_quant="none", gate=False, warm=True):
+                  dtype="f16", head_size=0, kv_quant="none", gate=False, warm=True, prologue=0):
     t_gen = time.perf_counter()
     b = W.workload(name, seed, dtype=dtype, head_size=head_size, kv_quant=kv_quant)
     work = W.work(b)
     log(f"[bench] {name}: generated in {time.perf_counter() - t_gen:.1f}s "
         f"(N={b.num_tokens}, B={b.batch_size}, KV {work['kv_hist_bytes'] / 1e9:.3f} GB, "
         f"{work['flops'] / 1e12:.3f} TFLOP)")
-    r = Runner(b, torch, pa, W.output_gate_input(b, seed + 1) if gate else None)
+    r = Runner(b, torch, pa, W.output_gate_input(b, seed + 1) if gate else None,
+               W.prologue_inputs(b, seed + 2, rotary_dim=prologue) if prologue else None)
     for _ in range(warmup):
         r.step()
     torch.cuda.synchronize()
@@ -374,6 +384,9 @@ def main():
                          "per element)")
     ap.add_argument("--gate", action="store_true",
                     help="pass an output gate: the outputs are multiplied by sigmoid(gate)")
+    ap.add_argument("--prologue", type=int, default=0, metavar="ROTARY_DIM",
+                    help="fuse the Q/K OffsetRMSNorm and a partial MRoPE over ROTARY_DIM channels "
+                         "into the calls (0: none)")
     ap.add_argument("--no-warm", action="store_true",
                     help="skip the warm phase (every timed dispatch is then cold, e.g. under a "
                          "profiler whose averages should match the cold figures)")
@@ -389,7 +402,8 @@ def main():
                          "counter CSVs (with --traffic-kernel, --workload, --copy-calibration)")
     ap.add_argument("--traffic-kernel", default="decode", choices=sorted(KERNEL_SYMBOL))
     args = ap.parse_args()
-    VARIANT["suffix"] = variant_suffix(args.dtype, args.head_size, args.kv_quant, args.gate)
+    VARIANT["suffix"] = variant_suffix(args.dtype, args.head_size, args.kv_quant, args.gate,
+                                       args.prologue)
     SCRUB["mode"] = args.scrub
 
     if args.traffic_from:
@@ -424,7 +438,7 @@ def main():
     pa.library()  # fail loudly if the HIP library is missing
     scrub = torch.zeros(SCRUB_BYTES // 4, dtype=torch.int32, device="cuda:0")
     variant = dict(dtype=args.dtype, head_size=args.head_size, kv_quant=args.kv_quant,
-                   gate=args.gate, warm=not args.no_warm)
+                   gate=args.gate, warm=not args.no_warm, prologue=args.prologue)
 
     WORKLOAD_NAME["current"] = args.workload
     b, work, res = time_workload(args.workload, args.steps, args.warmup, args.seed, torch, pa, W,
@@ -460,7 +474,8 @@ def main():
                    "kv_num_heads": b.kv_num_heads, "head_size": b.head_size,
                    "block_size": b.block_size, "num_blocks": b.num_blocks,
                    "kv_cache": args.dtype if args.kv_quant == "none" else args.kv_quant,
-                   "output_gate": bool(args.gate), "kv_hist_bytes": work["kv_hist_bytes"],
+                   "output_gate": bool(args.gate), "qk_prologue_rotary_dim": args.prologue,
+                   "kv_hist_bytes": work["kv_hist_bytes"],
                    "protocol": f"cold: 1 GiB scrub ({args.scrub}) before each step, outside "
                                "the events; ms_per_step = median of the per-step event times"},
         "roofline": head_roof,

@@ -94,6 +94,26 @@ int prefill_positions(int G) { return (kPrefillRows / 2) / G; }
 
 int device_cus();
 
+// Position row of every rotary frequency pair, two bits each (pair i in bits
+// 2(i % 16) of word i / 16): contiguous sections (the first s0 pairs row 0,
+// the next s1 row 1, the rest row 2), or interleaved (pair i on row i mod 3
+// while that row has pairs left, else the first row that has).
+void mrope_rows(int pairs, const int32_t sec[3], bool contiguous, uint32_t out[8]) {
+  for (int w = 0; w < 8; ++w) out[w] = 0u;
+  int used[3] = {0, 0, 0};
+  for (int i = 0; i < pairs && i < 128; ++i) {
+    int c;
+    if (contiguous) {
+      c = i < sec[0] ? 0 : i < sec[0] + sec[1] ? 1 : 2;
+    } else {
+      c = i % 3;
+      if (used[c] >= sec[c]) c = used[0] < sec[0] ? 0 : used[1] < sec[1] ? 1 : 2;
+    }
+    ++used[c];
+    out[i >> 4] |= static_cast<uint32_t>(c) << (2 * (i & 15));
+  }
+}
+
 WorkspaceLayout layout(const Resolved& r) {
   WorkspaceLayout w{};
   const int64_t live = std::min<int64_t>(r.B, r.N);  // sequences with >= 1 token
@@ -331,9 +351,7 @@ pa_status enqueue(const pa_args* a, const Resolved& r, const WorkspaceLayout& w,
     sp.rotary_dim = r.rd;
     sp.position_ids = a->position_ids;
     sp.rope_log2_theta = r.rd > 0 ? std::log2(static_cast<double>(a->rope_theta)) : 0.0;
-    sp.sec0 = a->mrope_section[0];
-    sp.sec1 = a->mrope_section[1];
-    sp.sec2 = a->mrope_section[2];
+    mrope_rows(r.rd / 2, a->mrope_section, (a->rope_flags & PA_ROPE_CONTIGUOUS) != 0, sp.rope_rows);
     sp.rope_flags = a->rope_flags;
   }
   mark(PA_KERNEL_SCATTER_PLAN, 0);

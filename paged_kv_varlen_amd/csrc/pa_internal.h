@@ -174,7 +174,7 @@ struct ScatterPlanParams {
   int32_t rotary_dim;          // 0: no rotation
   const int64_t* position_ids; // [3, N]
   double rope_log2_theta;      // log2 of the base
-  int32_t sec0, sec1, sec2;    // pairs per position row
+  uint32_t rope_rows[8];       // position row (0..2) of frequency pair i: bits 2(i%16).. of word i/16
   int32_t rope_flags;          // PA_ROPE_ADJACENT | PA_ROPE_CONTIGUOUS
 };
 

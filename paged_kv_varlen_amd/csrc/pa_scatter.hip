@@ -33,8 +33,9 @@ __device__ inline int find_sequence(const C* cum, int batch, int64_t t) {
   return lo;
 }
 
-// LDS of this kernel is allocated in every workgroup (the scatter ones too),
-// so both staging arrays stay small: 27 KB in all, five workgroups per CU
+// LDS of this kernel is allocated in every workgroup (the scatter ones too):
+// the plan's arrays and a scatter workgroup's share one buffer (kScatterSmem,
+// 19 KB, eight workgroups per CU)
 constexpr int kScatterLdsCum = 2048;  // cum entries a scatter workgroup stages in LDS
 
 // Exclusive scan of three ints per thread over a kPlanThreads block (one pass);
@@ -67,9 +68,9 @@ constexpr int kPlanLdsSeqs = 1024;  // decode sequences whose record the plan ke
 // Multi-token sequences get one prefill item per pair of query half-tiles
 // (t and nt-1-t of the sequence's nt), which all cost about the same under
 // the causal mask.
-__device__ void plan(const ScatterPlanParams& p) {
-  __shared__ int3 scan_lds[kPlanThreads];
-  __shared__ int4 seq_lds[kPlanLdsSeqs];  // dec_seq records of the first kPlanLdsSeqs
+__device__ void plan(const ScatterPlanParams& p, char* smem) {
+  int3* scan_lds = reinterpret_cast<int3*>(smem);
+  int4* seq_lds = reinterpret_cast<int4*>(smem + kPlanThreads * sizeof(int3));  // dec_seq records of the first kPlanLdsSeqs
   const int tid = threadIdx.x;
   const int U = p.decode_units;
   int dec_base = 0, tile_base = 0, pf_base = 0;
@@ -153,22 +154,6 @@ __device__ inline uint32_t elem_bits(float x, int bf16) {
               : __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
 }
 
-// position row (0, 1 or 2) of frequency pair i: contiguous sections, or
-// interleaved (pair j takes row j mod 3 while that row has pairs left, else
-// the first row that has)
-__device__ inline int mrope_row(int i, int s0, int s1, int s2, bool contiguous) {
-  if (contiguous) return i < s0 ? 0 : i < s0 + s1 ? 1 : 2;
-  int u0 = 0, u1 = 0, u2 = 0, c = 0;
-  for (int j = 0; j <= i; ++j) {
-    c = j % 3;
-    if ((c == 0 && u0 >= s0) || (c == 1 && u1 >= s1) || (c == 2 && u2 >= s2)) c = u0 < s0 ? 0 : u1 < s1 ? 1 : 2;
-    u0 += c == 0;
-    u1 += c == 1;
-    u2 += c == 2;
-  }
-  return c;
-}
-
 constexpr int kMaxRotaryPairs = 128;  // rotary_dim / 2 for head sizes up to 256
 
 // 8 values of a chunk -> the cache: 16-bit patterns, or INT8 / INT4 codes of
@@ -201,130 +186,198 @@ __device__ inline void store_chunk(const ScatterPlanParams& p, bool is_v, int cc
     *reinterpret_cast<uint2*>(cache + dst + 8 * cc) = make_uint2(packed[0], packed[1]);
 }
 
-// Norm and rotation of `heads` head rows starting at src (token t's row),
-// rounded to the data type: into q_dst (queries), or into the key cache row
-// dst (keys; none when dst < 0).  cs: (cos, sin) of every frequency pair.
-__device__ void prologue_rows(const ScatterPlanParams& p, const uint16_t* src, int heads, const float* w,
-                              uint16_t* q_dst, int64_t dst, const float2* cs) {
+// the 8 values of a 16-byte chunk of the data type
+__device__ inline void unpack8(uint4 raw, int bf16, float (&v)[8]) {
+  const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = elem_value((wv[e >> 1] >> (16 * (e & 1))) & 0xffffu, bf16);
+}
+
+// Norm and rotation of one 16-byte chunk (8 values) of a head row, in place.
+// The D / 8 chunks of a row sit in consecutive lanes of one wave (chunk k =
+// lane % (D / 8)) and all of them call this together: the norm's sum of
+// squares is a butterfly over those lanes, a rotation partner is rotary_dim
+// / 16 lanes away.  w: the chunk's norm weights (unused without a norm);
+// cs: (cos, sin) of every frequency pair.
+__device__ inline void transform8(const ScatterPlanParams& p, float (&v)[8], bool norm, const float (&w)[8],
+                                  const float2* cs) {
   const int D = p.head_size, cpr = D / 8, rd = p.rotary_dim;
   const int lane = threadIdx.x & 63;
-  const int half8 = rd / 16;  // chunks in each half of the rotated channels
-  const bool adjacent = (p.rope_flags & 1) != 0;
-  for (int c = threadIdx.x; c < heads * cpr; c += blockDim.x) {  // (whole rows per wave)
-    const int k = c % cpr;  // chunk within the head row
-    const uint4 raw = reinterpret_cast<const uint4*>(src)[c];
-    const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
-    float v[8];
+  const int k = lane % cpr;
+  if (norm) {  // OffsetRMSNorm: x * (1 + w) / sqrt(mean(x^2) + eps)
+    float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = elem_value((wv[e >> 1] >> (16 * (e & 1))) & 0xffffu, p.bf16);
-    if (w != nullptr) {  // OffsetRMSNorm: x * (1 + w) / sqrt(mean(x^2) + eps)
-      float ss = 0.f;
+    for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
+    for (int off = 1; off < cpr; off <<= 1) ss += __shfl_xor(ss, off);
+    const float r = 1.f / sqrtf(ss / static_cast<float>(D) + p.norm_eps);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
-      for (int off = 1; off < cpr; off <<= 1) ss += __shfl_xor(ss, off);
-      const float r = 1.f / sqrtf(ss / static_cast<float>(D) + p.norm_eps);
-      const float4 w0 = reinterpret_cast<const float4*>(w + 8 * k)[0], w1 = reinterpret_cast<const float4*>(w + 8 * k)[1];
-      const float wk[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    for (int e = 0; e < 8; ++e) v[e] = v[e] * r * (1.f + w[e]);
+  }
+  if (rd > 0) {  // y1 = x1 cos - x2 sin, y2 = x2 cos + x1 sin
+    if ((p.rope_flags & 1) != 0) {  // adjacent: pairs (2i, 2i + 1) inside the chunk
+      if (8 * k < rd) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = v[e] * r * (1.f + wk[e]);
-    }
-    if (rd > 0) {  // y1 = x1 cos - x2 sin, y2 = x2 cos + x1 sin
-      if (adjacent) {  // pairs (2i, 2i + 1) inside the chunk
-        if (8 * k < rd) {
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const float2 a = cs[4 * k + e / 2];
-            const float x1 = v[e], x2 = v[e + 1];
-            v[e] = x1 * a.x - x2 * a.y;
-            v[e + 1] = x2 * a.x + x1 * a.y;
-          }
-        }
-      } else {  // pairs (i, i + rd / 2): the partner chunk is half8 lanes away
-        const int partner = k < half8 ? lane + half8 : k < 2 * half8 ? lane - half8 : lane;
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = __shfl(v[e], partner);
-        if (k < half8) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float2 a = cs[8 * k + e];
-            v[e] = v[e] * a.x - pv[e] * a.y;
-          }
-        } else if (k < 2 * half8) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float2 a = cs[8 * (k - half8) + e];
-            v[e] = v[e] * a.x + pv[e] * a.y;
-          }
+        for (int e = 0; e < 8; e += 2) {
+          const float2 a = cs[4 * k + e / 2];
+          const float x1 = v[e], x2 = v[e + 1];
+          v[e] = x1 * a.x - x2 * a.y;
+          v[e + 1] = x2 * a.x + x1 * a.y;
         }
       }
-    }
-    uint32_t b[8];
-    float x[8];
+    } else {  // half split: pairs (i, i + rd / 2), the partner chunk is rd / 16 lanes away
+      const int half8 = rd / 16;
+      const int partner = k < half8 ? lane + half8 : k < 2 * half8 ? lane - half8 : lane;
+      float pv[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      b[e] = elem_bits(v[e], p.bf16);
-      x[e] = elem_value(b[e], p.bf16);  // the rounded value (what codes quantize)
-    }
-    if (q_dst != nullptr) {
-      reinterpret_cast<uint4*>(q_dst)[c] = make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16),
-                                                      b[4] | (b[5] << 16), b[6] | (b[7] << 16));
-    } else if (dst >= 0) {
-      store_chunk(p, false, c, dst, x, b);
+      for (int e = 0; e < 8; ++e) pv[e] = __shfl(v[e], partner);
+      if (k < half8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float2 a = cs[8 * k + e];
+          v[e] = v[e] * a.x - pv[e] * a.y;
+        }
+      } else if (k < 2 * half8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float2 a = cs[8 * (k - half8) + e];
+          v[e] = v[e] * a.x + pv[e] * a.y;
+        }
+      }
     }
   }
 }
 
-// the prologue for token t: angles, query rows, key rows, then the value row
-// as usual (bit copy or codes); the key and value rows only when slot >= 0
-__device__ void prologue_token(const ScatterPlanParams& p, int64_t t, int64_t slot) {
-  __shared__ float2 cs_lds[kMaxRotaryPairs];
-  const int rd = p.rotary_dim;
+// 8 transformed values rounded to the data type: patterns and rounded values
+__device__ inline void round8(const float (&v)[8], int bf16, uint32_t (&b)[8], float (&x)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    b[e] = elem_bits(v[e], bf16);
+    x[e] = elem_value(b[e], bf16);  // the rounded value (what codes quantize)
+  }
+}
+
+__device__ inline void load_weights8(const float* w, int k, float (&out)[8]) {
+  if (w == nullptr) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = 0.f;
+    return;
+  }
+  const float4 w0 = reinterpret_cast<const float4*>(w + 8 * k)[0], w1 = reinterpret_cast<const float4*>(w + 8 * k)[1];
+  out[0] = w0.x; out[1] = w0.y; out[2] = w0.z; out[3] = w0.w;
+  out[4] = w1.x; out[5] = w1.y; out[6] = w1.z; out[7] = w1.w;
+}
+
+// Query chunks a thread holds in registers from the token's first load on
+// (further chunks, for more than kQChunks * kPlanThreads, are loaded later)
+constexpr int kQChunks = 4;
+
+// The prologue for token t (one workgroup).  Every load of the token is issued
+// first (its positions, norm weights, query, key and value chunks), then the
+// (cos, sin) table of the frequency pairs is built, then the rows are
+// transformed, rounded and stored: the query rows into q_out, and, when slot
+// >= 0, the key rows into the key cache and the value row into the value
+// cache (bit copy or codes).  A token whose slot is -1 still gets its query
+// row.  Angles: position * theta^(-2i / rotary_dim) in fp64 (exact for
+// positions below 2^53), reduced to [-pi, pi], then sin and cos in fp32.
+__device__ void prologue_token(const ScatterPlanParams& p, int64_t t, int64_t slot, float2* cs_lds) {
+  const int D = p.head_size, cpr = D / 8, rd = p.rotary_dim;
+  const int tid = threadIdx.x;
+  const int k = tid % cpr;  // this thread's chunk within a head row
+  const int nq = p.num_heads * cpr;  // query chunks of the token
+  const int nk = p.row_elems >> 3;   // key (and value) chunks
+  const bool kv = slot >= 0;
+  // ---- loads ----
+  int64_t pos = 0;
+  if (tid < rd / 2) {
+    const int row = static_cast<int>((p.rope_rows[tid >> 4] >> (2 * (tid & 15))) & 3u);
+    pos = p.position_ids[static_cast<int64_t>(row) * p.num_tokens + t];
+  }
+  float wq[8], wk[8];
+  load_weights8(p.q_norm_w, k, wq);
+  load_weights8(p.k_norm_w, k, wk);
+  const uint4* qsrc = reinterpret_cast<const uint4*>(p.q_src + t * p.q_src_stride);
+  uint4 qr[kQChunks];
+#pragma unroll
+  for (int j = 0; j < kQChunks; ++j) {
+    const int c = tid + j * kPlanThreads;
+    qr[j] = c < nq ? qsrc[c] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  const uint4* ksrc = reinterpret_cast<const uint4*>(p.key_src + t * p.src_stride);
+  const uint4* vsrc = reinterpret_cast<const uint4*>(p.value_src + t * p.src_stride);
+  const uint4 kr = kv && tid < nk ? ksrc[tid] : make_uint4(0u, 0u, 0u, 0u);
+  const uint4 vr = kv && tid < nk ? vsrc[tid] : make_uint4(0u, 0u, 0u, 0u);
+  // ---- the (cos, sin) table ----
   if (rd > 0) {
-    for (int i = threadIdx.x; i < rd / 2; i += blockDim.x) {
-      const int row = mrope_row(i, p.sec0, p.sec1, p.sec2, (p.rope_flags & 2) != 0);
-      const double pos = static_cast<double>(p.position_ids[static_cast<int64_t>(row) * p.num_tokens + t]);
-      // angle in fp64 (positions up to 2^53 are exact), reduced to [-pi, pi]
-      const double inv = exp2(-2.0 * i / rd * p.rope_log2_theta);
-      double ang = pos * inv;
+    if (tid < rd / 2) {
+      const double inv = exp2(-2.0 * tid / rd * p.rope_log2_theta);
+      double ang = static_cast<double>(pos) * inv;
       ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
-      double sn, cn;
-      sincos(ang, &sn, &cn);
-      cs_lds[i] = make_float2(static_cast<float>(cn), static_cast<float>(sn));
+      float sn, cn;
+      sincosf(static_cast<float>(ang), &sn, &cn);
+      cs_lds[tid] = make_float2(cn, sn);
     }
     __syncthreads();
   }
-  prologue_rows(p, p.q_src + t * p.q_src_stride, p.num_heads, p.q_norm_w,
-                p.q_out + t * static_cast<int64_t>(p.num_heads) * p.head_size, -1, cs_lds);
-  if (slot < 0) return;
-  const int64_t dst = slot * p.row_elems;
-  prologue_rows(p, p.key_src + t * p.src_stride, p.row_elems / p.head_size, p.k_norm_w, nullptr, dst, cs_lds);
-  const int chunks = p.row_elems >> 3;
-  for (int cc = threadIdx.x; cc < chunks; cc += blockDim.x) {
-    const uint4 raw = reinterpret_cast<const uint4*>(p.value_src + t * p.src_stride)[cc];
-    const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+  const bool qnorm = p.q_norm_w != nullptr, knorm = p.k_norm_w != nullptr;
+  // ---- query rows (whole rows per wave: nq is a multiple of the row's lanes) ----
+  uint16_t* qdst = p.q_out + t * static_cast<int64_t>(p.num_heads) * D;
+  auto query_chunk = [&](int c, uint4 raw) __attribute__((always_inline)) {
+    float v[8], x[8];
     uint32_t b[8];
-    float x[8];
+    unpack8(raw, p.bf16, v);
+    transform8(p, v, qnorm, wq, cs_lds);
+    round8(v, p.bf16, b, x);
+    reinterpret_cast<uint4*>(qdst)[c] =
+        make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16));
+  };
+#pragma unroll
+  for (int j = 0; j < kQChunks; ++j) {
+    const int c = tid + j * kPlanThreads;
+    if (c < nq) query_chunk(c, qr[j]);
+  }
+  for (int c = tid + kQChunks * kPlanThreads; c < nq; c += kPlanThreads) query_chunk(c, qsrc[c]);
+  if (!kv) return;
+  // ---- key rows, then the value row ----
+  const int64_t dst = slot * p.row_elems;
+  auto key_value_chunk = [&](int c, uint4 kraw, uint4 vraw) __attribute__((always_inline)) {
+    float v[8], x[8];
+    uint32_t b[8];
+    unpack8(kraw, p.bf16, v);
+    transform8(p, v, knorm, wk, cs_lds);
+    round8(v, p.bf16, b, x);
+    store_chunk(p, false, c, dst, x, b);
+    const uint32_t wv[4] = {vraw.x, vraw.y, vraw.z, vraw.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       b[e] = (wv[e >> 1] >> (16 * (e & 1))) & 0xffffu;
       x[e] = elem_value(b[e], p.bf16);
     }
-    store_chunk(p, true, cc, dst, x, b);
-  }
+    store_chunk(p, true, c, dst, x, b);
+  };
+  if (tid < nk) key_value_chunk(tid, kr, vr);
+  for (int c = tid + kPlanThreads; c < nk; c += kPlanThreads) key_value_chunk(c, ksrc[c], vsrc[c]);
 }
 
+// LDS of the kernel: the plan's scan buffer and decode records (first
+// workgroup), or a scatter workgroup's staged sequence offsets and the
+// prologue's (cos, sin) table, overlaid, so that the scatter workgroups are
+// not held to the plan's LDS (more of them per compute unit)
+constexpr size_t kPlanSmem = kPlanThreads * sizeof(int3) + kPlanLdsSeqs * sizeof(int4);
+constexpr size_t kTokenSmem = kScatterLdsCum * sizeof(int) + kMaxRotaryPairs * sizeof(float2);
+constexpr size_t kScatterSmem = kPlanSmem > kTokenSmem ? kPlanSmem : kTokenSmem;
+
 __global__ __launch_bounds__(kPlanThreads) void scatter_plan_kernel(ScatterPlanParams p) {
+  __shared__ __align__(16) char smem[kScatterSmem];
   // workgroup 0 plans (dispatched first, it overlaps the scatter of long
   // calls); workgroup t + 1 scatters token t
   if (blockIdx.x == 0) {
-    plan(p);
+    plan(p, smem);
     return;
   }
   const int64_t t = static_cast<int64_t>(blockIdx.x) - 1;
   // the sequence of token t: a binary search over cum, staged in LDS by one
   // coalesced load (long batches search global memory)
-  __shared__ int cum_lds[kScatterLdsCum];
+  int* cum_lds = reinterpret_cast<int*>(smem);
   int b;
   if (p.slot_mapping != nullptr) {
     b = 0;  // not needed
@@ -345,7 +398,7 @@ __global__ __launch_bounds__(kPlanThreads) void scatter_plan_kernel(ScatterPlanP
            pos % p.block_size;
   }
   if (p.pro) {  // (every token: its query row is transformed even when its slot is -1)
-    prologue_token(p, t, slot);
+    prologue_token(p, t, slot, reinterpret_cast<float2*>(smem + kScatterLdsCum * sizeof(int)));
     return;
   }
   if (slot < 0) return;

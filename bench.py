@@ -352,7 +352,7 @@ def cpu_baseline(b, W, target_s: float):
     k = int(min(b.batch_size, max(1, target_s / max(t1, 1e-3))))
     t, work = run(k)
     reps = 1
-    while t * reps < 0.5 * target_s and reps < 1000:  # whole batch is quick: repeat it
+    while t < target_s and reps < 1000:  # whole batch is quick: repeat it (t sums the runs)
         dt, _ = run(k)
         t += dt
         reps += 1

@@ -964,3 +964,59 @@ def test_prologue_head_size_256(kvq):
 def test_prologue_pure_decode_full():
     b = W.pure_decode(0)
     check_prologue(b, W.prologue_inputs(b, 850, rotary_dim=64))
+
+
+# ------------------------------------------------------------------ fused prologue with the other features
+
+def test_prologue_with_gate_and_state():
+    # The prologue transforms the step's query and key rows; the output gate
+    # multiplies the output only, and the exported (out, lse) state is the
+    # ungated attention over the transformed rows.  Decode segments cut
+    # across waves (merged) and whole ones, and chunked rows, in one call.
+    b = W.make_batch([1, 300, 1, 64], [2000, 700, 9000, 0], num_heads=16, kv_num_heads=4, head_size=128,
+                     block_size=16, seed=860, name="prologue_gate_state")
+    kw = W.prologue_inputs(b, 861, rotary_dim=64, spatial=True)
+    gate = W.output_gate_input(b, 862)
+    say(f"[gpu] prologue + gate + state {b.name} N={b.num_tokens} B={b.batch_size}")
+    d = DevBatch(b)
+    f32 = torch.empty((b.num_tokens, b.num_heads * b.head_size), dtype=torch.float32, device=DEV)
+    out, lse = d.run(return_lse=True, output_f32=f32, gate=to_dev(gate), prologue=prologue_dev(kw))
+    torch.cuda.synchronize()
+    args = (b.query, b.key, b.value, b.key_cache, b.value_cache, b.cum, b.past, b.block_table, b.slot_mapping)
+    common = dict(num_heads=b.num_heads, kv_num_heads=b.kv_num_heads, scale=b.scale, prologue=kw)
+    gated, _, _ = oracle.paged_attention(*args, gate=gate, **common)
+    plain, _, _, rlse = oracle.paged_attention(*args, with_lse=True, **common)
+    o16, o32, l32 = as_f64(to_host(out)), f32.cpu().numpy().astype(np.float64), lse.cpu().numpy()
+    e_g = float(np.max(np.abs(o16 - gated)))
+    e_o = float(np.max(np.abs(o32 - plain)))
+    e_l = float(np.max(np.abs(l32.astype(np.float64) - rlse)))
+    say(f"      max|err| gated output {e_g:.3e}, out_f32 {e_o:.3e}, lse {e_l:.3e}")
+    assert e_g <= tol(b) and e_o <= tol(b) and e_l <= LSE_TOL
+
+
+def test_prologue_hip_graph_replay_matches_eager():
+    # the prologue's query rows live in the workspace: a captured call must
+    # rebuild them on every replay (eager work on other data between replays)
+    b = W.mixed(3)
+    kw = prologue_dev(W.prologue_inputs(b, 870, rotary_dim=64))
+    d = DevBatch(b)
+    ref = d.run(prologue=kw).clone()
+    torch.cuda.synchronize()
+    ws = torch.empty(1 << 28, dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        d.run(output=out, workspace=ws, stream=s, prologue=kw)  # warm-up on the capture stream
+        s.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            d.run(output=out, workspace=ws, stream=s, prologue=kw)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        out.zero_()
+        ws.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))

@@ -31,7 +31,7 @@ def dev(x):
     return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
 
 
-def run(b, noalloc):
+def run(b, noalloc, prologue=None):
     t = {k: dev(getattr(b, k)) for k in ("query", "key", "value", "key_cache", "value_cache", "cum",
                                          "past", "block_table", "slot_mapping", "k_scale",
                                          "v_scale")}
@@ -41,6 +41,8 @@ def run(b, noalloc):
               t["past"], t["block_table"], t["slot_mapping"])
     kw = dict(num_heads=b.num_heads, kv_num_heads=b.kv_num_heads, scale=b.scale, output=out,
               lse=lse, k_scale=t["k_scale"], v_scale=t["v_scale"])
+    if prologue is not None:  # the fused Q/K prologue (its query rows live in the scratch too)
+        kw["prologue"] = {k: dev(v) if isinstance(v, np.ndarray) else v for k, v in prologue.items()}
     if noalloc:
         pa.paged_attention_noalloc(*common, **kw)
     else:
@@ -49,10 +51,11 @@ def run(b, noalloc):
     return out, lse, t["key_cache"], t["value_cache"]
 
 
-def compare(b):
-    say(f"[gpu] noalloc {b.name} N={b.num_tokens} B={b.batch_size} kv={b.kv_quant}")
-    o1, l1, k1, v1 = run(b, noalloc=False)
-    o2, l2, k2, v2 = run(b, noalloc=True)
+def compare(b, prologue=None):
+    say(f"[gpu] noalloc {b.name} N={b.num_tokens} B={b.batch_size} kv={b.kv_quant}"
+        + (" with the fused prologue" if prologue else ""))
+    o1, l1, k1, v1 = run(b, noalloc=False, prologue=prologue)
+    o2, l2, k2, v2 = run(b, noalloc=True, prologue=prologue)
     assert torch.equal(k1.view(torch.uint8), k2.view(torch.uint8))
     assert torch.equal(v1.view(torch.uint8), v2.view(torch.uint8))
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
@@ -60,9 +63,11 @@ def compare(b):
     ref, rkc, rvc = oracle.paged_attention(b.query, b.key, b.value, b.key_cache, b.value_cache,
                                            b.cum, b.past, b.block_table, b.slot_mapping,
                                            num_heads=b.num_heads, kv_num_heads=b.kv_num_heads,
-                                           scale=b.scale, k_scale=b.k_scale, v_scale=b.v_scale)
+                                           scale=b.scale, k_scale=b.k_scale, v_scale=b.v_scale,
+                                           prologue=prologue)
     raw = lambda x: x.view(np.uint8 if x.itemsize == 1 else np.uint16)
-    assert np.array_equal(raw(k2.cpu().numpy()), raw(rkc))
+    if prologue is None:  # (written key rows carry the kernel's fp32 rounding: the parity tests bound them)
+        assert np.array_equal(raw(k2.cpu().numpy()), raw(rkc))
     assert np.array_equal(raw(v2.cpu().numpy()), raw(rvc))
     err = float(np.max(np.abs(o2.double().cpu().numpy() - ref)))
     say(f"      identical to the workspace entry point; max|err| vs oracle {err:.3e}")
@@ -84,4 +89,13 @@ def test_noalloc_matches_workspace_entry_two_calls():
 
 def test_noalloc_full_workload_then_smaller():
     compare(W.mixed(0))
+    compare(W.tiny(0))
+
+
+def test_noalloc_with_the_fused_prologue_then_without():
+    # the prologue's transformed query rows sit in the scratch; the next call
+    # (no prologue) must not read them
+    b = W.make_batch([1, 120, 1, 33], [3000, 200, 40, 900], num_heads=16, kv_num_heads=4, head_size=128,
+                     block_size=16, seed=902, name="noalloc_prologue")
+    compare(b, prologue=W.prologue_inputs(b, 903, rotary_dim=64, spatial=True))
     compare(W.tiny(0))

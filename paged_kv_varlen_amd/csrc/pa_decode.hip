@@ -770,6 +770,7 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ != 0)) void decode_kerne
   __shared__ __align__(16) int meta[kDecodeWaves][2][64];  // [0] next window, [1] next sequence
   // a piece's (token, first head, heads), handed over with its first tile
   __shared__ __align__(16) int piece[kDecodeWaves][R][4];
+  __shared__ int prog[kDecodeWaves];  // tiles computed, per wave (two waves per SIMD)
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -1205,6 +1206,15 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ != 0)) void decode_kerne
 
   // ---- the stream: tile k lives in slot k % R, issued R-1 tiles ahead --------
   const int count = g1 - g0;
+  // Two waves per SIMD (quantized caches, D <= 128): the SIMD issues for the
+  // older wave first when both are ready, so with equal shares the younger
+  // one (waves 4..7 beside waves 0..3) would end several microseconds later,
+  // alone on its SIMD.  After every tile the wave that is behind its sibling
+  // takes the higher issue priority, so the two progress together.
+  constexpr bool kPaired = kDecodeWaves == 8;
+  const uint32_t prog_a = lds_addr(&prog[0]);
+  int done = 0;
+  if constexpr (kPaired) asm volatile("ds_write_b32 %0, %1" ::"v"(prog_a + 4 * wave), "v"(0) : "memory");
   static_for<R - 1>([&](auto S) __attribute__((always_inline)) {
     if (g_i < g1) issue(S);
   });
@@ -1214,6 +1224,13 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ != 0)) void decode_kerne
       if (k + s < count) {
         if (g_i < g1) issue(std::integral_constant<int, (s + R - 1) % R>{});
         compute(S);
+        if constexpr (kPaired) {
+          ++done;
+          asm volatile("ds_write_b32 %0, %1" ::"v"(prog_a + 4 * wave), "v"(done) : "memory");
+          const int sib = uniform(static_cast<int>(lds_read_b32(prog_a + 4 * (wave ^ 4))));
+          if (done > sib) __builtin_amdgcn_s_setprio(0);
+          else if (done < sib) __builtin_amdgcn_s_setprio(1);
+        }
       }
     });
   }

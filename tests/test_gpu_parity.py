@@ -288,6 +288,22 @@ def test_deterministic_bits():
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
 
+@pytest.mark.parametrize("kv_quant", ["int8", "int4"])
+def test_deterministic_bits_quantized_decode(kv_quant):
+    # two waves per SIMD take turns at the higher issue priority by progress:
+    # the schedule changes from run to run, the cut points and bits must not
+    b = W.workload("pure_decode", 2, kv_quant=kv_quant)
+    d = DevBatch(b)
+    runs = []
+    for _ in range(3):
+        out, lse = d.run(return_lse=True)
+        runs.append((out.clone(), lse.clone()))
+    torch.cuda.synchronize()
+    for out, lse in runs[1:]:
+        assert torch.equal(out.view(torch.int16), runs[0][0].view(torch.int16))
+        assert torch.equal(lse.view(torch.int32), runs[0][1].view(torch.int32))
+
+
 def test_chunked_continuation_matches_one_shot():
     H, Hkv, D, bs = 8, 2, 128, 16
     b = W.make_batch([150], [37], num_heads=H, kv_num_heads=Hkv, head_size=D, block_size=bs,

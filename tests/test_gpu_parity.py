@@ -182,6 +182,8 @@ BIG_PAGES = [
     ([1, 129, 1, 2, 1], [4095, 4000, 9000, 4096, 4097], 16, 4, 128, 4096, "f16", "none"),
     ([1, 70, 1], [4095, 4090, 12000], 8, 2, 256, 4096, "bf16", "none"),
     ([1, 33, 1, 1], [1023, 1000, 8191, 1025], 8, 2, 128, 1024, "f16", "int8"),
+    ([1, 40, 1, 1], [4095, 3000, 12000, 4097], 16, 4, 128, 4096, "f16", "int4"),
+    ([1, 17, 1], [2047, 100, 3000], 8, 2, 64, 1024, "bf16", "int8"),
 ]
 
 

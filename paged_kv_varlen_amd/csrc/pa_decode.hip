@@ -776,6 +776,13 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ != 0)) void decode_kerne
   const int wave = uniform(threadIdx.x >> 6);
   const int W = p.decode_waves;
   const int w = static_cast<int>(blockIdx.x) * kDecodeWaves + wave;
+  // two waves per SIMD: every wave's progress count starts at zero before any
+  // wave can leave early (a wave without tiles stays at zero)
+  constexpr bool kPaired = kDecodeWaves == 8;
+  if constexpr (kPaired) {
+    if (lane == 0) prog[wave] = 0;
+    __syncthreads();
+  }
   if (w >= W) return;
 
   // ---- this wave's share ---------------------------------------------------
@@ -1211,10 +1218,8 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ != 0)) void decode_kerne
   // one (waves 4..7 beside waves 0..3) would end several microseconds later,
   // alone on its SIMD.  After every tile the wave that is behind its sibling
   // takes the higher issue priority, so the two progress together.
-  constexpr bool kPaired = kDecodeWaves == 8;
   const uint32_t prog_a = lds_addr(&prog[0]);
   int done = 0;
-  if constexpr (kPaired) asm volatile("ds_write_b32 %0, %1" ::"v"(prog_a + 4 * wave), "v"(0) : "memory");
   static_for<R - 1>([&](auto S) __attribute__((always_inline)) {
     if (g_i < g1) issue(S);
   });

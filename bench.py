@@ -30,9 +30,11 @@ Reported:
                 over its mean cold duration
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
                 workload, in the same unit
-  also          the other workloads (mixed, long_prefill, serving): cold and
-                warm step statistics, TFLOP/s, GB/s (serving: on unique and on
-                logical history bytes), tokens/s and their own roofline
+  also          the other workloads (mixed, long_prefill, serving, and
+                pure_decode with INT8 and with INT4 caches): cold and warm step
+                statistics, TFLOP/s, GB/s (serving: on unique and on logical
+                history bytes; quantized caches: on code bytes), tokens/s and
+                their own roofline
 """
 from __future__ import annotations
 
@@ -371,8 +373,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="pure_decode")
-    ap.add_argument("--also", default="mixed,long_prefill,serving",
-                    help="comma list of other workloads to time (empty for none)")
+    ap.add_argument("--also", default="mixed,long_prefill,serving,pure_decode:int8,pure_decode:int4",
+                    help="comma list of other workloads to time (empty for none); "
+                         "name:int8 or name:int4 times that workload with quantized caches")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--dtype", default="f16", choices=("f16", "bf16"),
                     help="data type of the workloads (the line's dtype field)")
@@ -446,14 +449,23 @@ def main():
     head = summarize(args.workload, work, res)
     head_roof = roofline(work, res)
     also = []
-    for name in [x for x in args.also.split(",") if x and x != args.workload]:
+    for spec in [x for x in args.also.split(",") if x and x != args.workload]:
+        name, _, kvq = spec.partition(":")
+        if kvq not in ("", "int8", "int4"):
+            raise SystemExit(f"--also {spec}: the cache type after ':' is int8 or int4")
+        ov = dict(variant, kv_quant=kvq or args.kv_quant)
+        VARIANT["suffix"] = variant_suffix(args.dtype, args.head_size, ov["kv_quant"], args.gate,
+                                           args.prologue)
         WORKLOAD_NAME["current"] = name
         ob, owork, ores = time_workload(name, args.steps, args.warmup, args.seed, torch, pa, W,
-                                        scrub, **variant)
+                                        scrub, **ov)
         entry = summarize(name, owork, ores)
+        entry["kv_cache"] = ov["kv_quant"] if ov["kv_quant"] != "none" else args.dtype
         entry["roofline"] = roofline(owork, ores)
         also.append(entry)
         del ob
+    VARIANT["suffix"] = variant_suffix(args.dtype, args.head_size, args.kv_quant, args.gate,
+                                       args.prologue)
 
     ms = res["cold"]["median"]
     line = {

@@ -59,6 +59,20 @@ __device__ inline int3 block_exclusive_scan3(int3 v, int3* lds, int3* tot) {
 }
 
 constexpr int kPlanLdsSeqs = 1024;  // decode sequences whose record the plan keeps in LDS
+// Prefill items go out longest first: a sequence's items all cost about the
+// same (the half-tile pairs balance the causal mask), about 2 past + q keys
+// each, so sequences are binned by that cost in half octaves (all costs
+// below 8 in bin 0) and the bins emitted from the top.  Within a bin the
+// order is that of LDS atomics: an item is computed whole by one workgroup,
+// so the order changes only which workgroup takes it and when, never a bit
+// of the output.
+constexpr int kCostBins = 64;  // one wave's lanes
+__device__ inline int cost_bin(int64_t past, int q) {
+  const uint64_t c = 2ull * static_cast<uint64_t>(past) + static_cast<uint64_t>(q);  // >= 2
+  const int lg = 63 - __clzll(c);
+  const int k = 2 * lg + static_cast<int>((c >> (lg - 1)) & 1u) - 4;
+  return k < 0 ? 0 : k > kCostBins - 1 ? kCostBins - 1 : k;
+}
 
 // The plan.  Decode sequences (one new token) get their index d and the tile
 // offset of their first segment; each decode wave gets the segment and tile
@@ -71,15 +85,17 @@ constexpr int kPlanLdsSeqs = 1024;  // decode sequences whose record the plan ke
 __device__ void plan(const ScatterPlanParams& p, char* smem) {
   int3* scan_lds = reinterpret_cast<int3*>(smem);
   int4* seq_lds = reinterpret_cast<int4*>(smem + kPlanThreads * sizeof(int3));  // dec_seq records of the first kPlanLdsSeqs
+  int* bin_lds = reinterpret_cast<int*>(smem + kPlanThreads * sizeof(int3) + kPlanLdsSeqs * sizeof(int4));  // item count, then next slot, per cost bin
   const int tid = threadIdx.x;
   const int U = p.decode_units;
   int dec_base = 0, tile_base = 0, pf_base = 0;
+  int row_np = 0, row_bin = 0;  // this thread's row when the batch is one pass
   for (int start = 0; start < p.batch; start += kPlanThreads) {
     const int b = start + tid;
-    int nd = 0, nt = 0, np = 0, t0 = 0, L = 0;
+    int nd = 0, nt = 0, np = 0, t0 = 0, L = 0, q = 0;
     if (b < p.batch) {
       t0 = p.cum[b];
-      const int q = p.cum[b + 1] - t0;
+      q = p.cum[b + 1] - t0;
       L = p.past[b] + q;
       if (q == 1) {
         nd = 1;
@@ -96,10 +112,52 @@ __device__ void plan(const ScatterPlanParams& p, char* smem) {
       p.dec_seq[d] = rec;
       if (d < kPlanLdsSeqs) seq_lds[d] = rec;
     }
-    for (int t = 0; t < np; ++t) p.pf_items[pf_base + o.z + t] = make_int2(b, t);
+    row_np = np;
+    if (np != 0) row_bin = cost_bin(L - q, q);
     dec_base += tot.x;
     tile_base += tot.y;
     pf_base += tot.z;
+  }
+  if (pf_base != 0) {
+    // Longest first: count the items of each cost bin, turn the counts into
+    // first slots from the costliest bin down, then place the items.  When
+    // the batch is one pass each thread still holds its row; otherwise the
+    // rows are read again.
+    static_assert(kCostBins <= kPlanThreads, "one bin per thread");
+    const bool one_pass = p.batch <= kPlanThreads;
+    if (tid < kCostBins) bin_lds[tid] = 0;
+    __syncthreads();
+    auto each_row = [&](auto&& f) {
+      if (one_pass) {
+        if (row_np != 0) f(tid, row_np, row_bin);
+      } else {
+        for (int start = 0; start < p.batch; start += kPlanThreads) {
+          const int b = start + tid;
+          if (b < p.batch) {
+            const int q = p.cum[b + 1] - p.cum[b];
+            if (q > 1) f(b, ((q + p.prefill_positions - 1) / p.prefill_positions + 1) / 2, cost_bin(p.past[b], q));
+          }
+        }
+      }
+    };
+    each_row([&](int, int np, int k) { atomicAdd(&bin_lds[k], np); });
+    __syncthreads();
+    if (tid < kCostBins) {  // the first wave: exclusive scan over the bins, costliest first
+      const int kb = kCostBins - 1 - tid;
+      const int cnt = bin_lds[kb];
+      int incl = cnt;
+#pragma unroll
+      for (int off = 1; off < kCostBins; off <<= 1) {
+        const int up = __shfl_up(incl, off, kCostBins);
+        if (tid >= off) incl += up;
+      }
+      bin_lds[kb] = incl - cnt;
+    }
+    __syncthreads();
+    each_row([&](int b, int np, int k) {
+      const int at = atomicAdd(&bin_lds[k], np);
+      for (int t = 0; t < np; ++t) p.pf_items[at + t] = make_int2(b, t);
+    });
   }
   static_assert(kZeroPageBytes / 4 <= kPlanThreads, "zero page");
   if (tid < kZeroPageBytes / 4) p.zeros[tid] = 0;
@@ -362,7 +420,7 @@ __device__ void prologue_token(const ScatterPlanParams& p, int64_t t, int64_t sl
 // workgroup), or a scatter workgroup's staged sequence offsets and the
 // prologue's (cos, sin) table, overlaid, so that the scatter workgroups are
 // not held to the plan's LDS (more of them per compute unit)
-constexpr size_t kPlanSmem = kPlanThreads * sizeof(int3) + kPlanLdsSeqs * sizeof(int4);
+constexpr size_t kPlanSmem = kPlanThreads * sizeof(int3) + kPlanLdsSeqs * sizeof(int4) + kCostBins * sizeof(int);
 constexpr size_t kTokenSmem = kScatterLdsCum * sizeof(int) + kMaxRotaryPairs * sizeof(float2);
 constexpr size_t kScatterSmem = kPlanSmem > kTokenSmem ? kPlanSmem : kTokenSmem;
 

@@ -129,7 +129,7 @@ WorkspaceLayout layout(const Resolved& r) {
                             ((static_cast<int64_t>(r.MB) * r.bs + kDecodeTile - 1) / kDecodeTile);
   const int64_t resident = static_cast<int64_t>(device_cus()) * decode_wg_per_cu(r.D, hs, r.kq);
   w.decode_grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(resident, (max_tiles + 31) / 32)));
-  w.decode_waves = w.decode_grid * decode_wg_waves(r.D, r.kq != 0);
+  w.decode_waves = w.decode_grid * decode_wg_waves(r.D, r.kq, hs);
   const size_t W = static_cast<size_t>(w.decode_waves);
   size_t off = 0;
   w.ctrl = off;
@@ -332,7 +332,8 @@ pa_status enqueue(const pa_args* a, const Resolved& r, const WorkspaceLayout& w,
   const int pair =
       r.kq == 4 && cache_row_bytes(r.D, r.kq) < 128 && units % 2 == 0 && w.decode_waves % 2 == 0 ? 2 : 1;
   sp.decode_units = units / pair;
-  sp.decode_waves = w.decode_waves / pair;
+  const int split = decode_split(r.D, r.kq, decode_head_slots(r.G));
+  sp.decode_waves = w.decode_waves / (pair * split);
   sp.prefill_positions = prefill_positions(r.G);
   sp.kq = r.kq;
   sp.bf16 = a->dtype == PA_DTYPE_BF16 ? 1 : 0;
@@ -383,6 +384,7 @@ pa_status enqueue(const pa_args* a, const Resolved& r, const WorkspaceLayout& w,
   ap.decode_units = units;
   ap.decode_waves = w.decode_waves;
   ap.decode_pair = pair;
+  ap.decode_split = split;
   ap.prefill_positions = prefill_positions(r.G);
   ap.scale_log2 = r.scale * 1.4426950408889634f;
   ap.lse_out = a->lse;

@@ -740,11 +740,12 @@ constexpr int kComplete = 1 << 10; // the piece is the whole segment
 constexpr int kSecond = 1 << 11;   // partial goes to the wave's second slot
 
 template <int D, int HS, bool BF16, int KQ>
-__global__ __launch_bounds__(64 * decode_wg_waves(D, KQ != 0)) void decode_kernel(AttnParams p) {
+__global__ __launch_bounds__(64 * decode_wg_waves(D, KQ, HS)) void decode_kernel(AttnParams p) {
   using E = Elem<BF16>;
   constexpr bool QNT = KQ != 0;                   // the caches hold codes (INT8 or INT4)
   constexpr bool Q4 = KQ == 4;
-  constexpr int kDecodeWaves = decode_wg_waves(D, QNT);
+  constexpr int kDecodeWaves = decode_wg_waves(D, KQ, HS);
+  constexpr int SP = decode_split(D, KQ, HS);  // 2: waves 2v, 2v+1 halve pair v's tiles
   constexpr int ROW = 2 * D;                      // bytes of one key of one kv head (data type)
   constexpr int CPR = ROW / 16;                   // 16-byte chunks per row
   constexpr int ROWC = cache_row_bytes(D, KQ);    // bytes of a cached row (codes when quantized)
@@ -787,13 +788,22 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ != 0)) void decode_kerne
 
   // ---- this wave's share ---------------------------------------------------
   // paired waves (INT4 rows under a memory line): wave pair vw streams the
-  // tiles of unit pairs, wave 2vw taking units 2u, wave 2vw+1 units 2u+1
+  // tiles of unit pairs, wave 2vw taking units 2u, wave 2vw+1 units 2u+1.
+  // Split pairs (SP = 2, 16-bit caches with eight waves): the plan's record vw
+  // starts pair vw's tiles; wave 2vw takes their lower half, wave 2vw+1 the
+  // upper half (decode_wave_begin_sp).
   const int PF = p.decode_pair;
-  const int vw = w / PF, par = w % PF;
+  const int vw = w / (PF * SP), par = w % PF;
   const int* rec = p.dec_start + 8 * vw;
   const int rv = rec[lane & 7];
-  const int g1 = p.dec_start[8 * (vw + 1) + 3];
-  const int g0 = uniform(__builtin_amdgcn_readlane(rv, 3));
+  const int g_pair = uniform(__builtin_amdgcn_readlane(rv, 3));
+  const int g_next = p.dec_start[8 * (vw + 1) + 3];
+  int g0 = g_pair, g1 = g_next;
+  if constexpr (SP == 2) {
+    const int mid = g_pair + (g_next - g_pair) / 2;
+    if (w & 1) g0 = mid;
+    else g1 = mid;
+  }
   if (g0 >= g1) return;
   const int Bd = p.ws_ctrl[kCtrlDecodeSeqs];
   const int U = p.decode_units / PF;  // units (pairs) per sequence in the tile order
@@ -868,6 +878,21 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ != 0)) void decode_kerne
   int L_i = uniform(__builtin_amdgcn_readlane(rv, 6));
   int P_i = uniform(__builtin_amdgcn_readlane(rv, 7));
   int n_i = (L_i + kDecodeTile - 1) / kDecodeTile;
+  if constexpr (SP == 2) {
+    if (w & 1) {  // the upper half starts at g0: from the pair's sequence, forward to the one holding g0
+      while (g0 >= P_i + U * n_i) {  // (the last sequence ends at T > g0)
+        ++d_i;
+        const int4 sq = p.dec_seq[d_i];
+        b_i = uniform(sq.x);
+        t_i = uniform(sq.y);
+        L_i = uniform(sq.z);
+        P_i = uniform(sq.w);
+        n_i = (L_i + kDecodeTile - 1) / kDecodeTile;
+      }
+      u_i = (g0 - P_i) / n_i;
+      i_i = (g0 - P_i) % n_i;
+    }
+  }
   int kvh_i = (PF * u_i + par) / hcc, hc_i = (PF * u_i + par) % hcc;  // of the actual unit
   int pi = i_i / tpp, ip = i_i % tpp;  // page of the tile and tile within the page
   int g_i = g0;
@@ -1247,7 +1272,7 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ != 0)) void decode_kerne
 
 template <int D, int HS, bool BF16>
 void launch_decode_t(const AttnParams& p, int kq, dim3 g, hipStream_t s) {
-  const dim3 b(64 * decode_wg_waves(D, kq != 0));
+  const dim3 b(64 * decode_wg_waves(D, kq, HS));
   if (kq == 8) hipLaunchKernelGGL((decode_kernel<D, HS, BF16, 8>), g, b, 0, s, p);
   else if (kq == 4) hipLaunchKernelGGL((decode_kernel<D, HS, BF16, 4>), g, b, 0, s, p);
   else hipLaunchKernelGGL((decode_kernel<D, HS, BF16, 0>), g, b, 0, s, p);

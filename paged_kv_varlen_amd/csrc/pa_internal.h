@@ -26,15 +26,6 @@
 namespace pa {
 
 // ---- tiling constants -----------------------------------------------------
-// waves per decode workgroup: 4, or 2 at head_size 256 (so that a ring of
-// three or four 16-key tiles per wave still fits in LDS).  Quantized caches (INT8
-// or INT4: quant)
-// halve the tile bytes and add the code conversion to every tile, so twice
-// the waves share the LDS (two per SIMD below head_size 256) with rings of
-// two to four tiles: one wave converts while the other waits on its loads.
-__host__ __device__ constexpr int decode_wg_waves(int D, bool quant = false) {
-  return quant ? (D > 128 ? 4 : 8) : (D > 128 ? 2 : 4);
-}
 constexpr int kDecodeTile = 16;       // keys per decode tile
 constexpr int kDecodeUnitHeads = 16;  // query heads of one decode segment (MFMA N)
 constexpr int kDecodeWindow = 64;     // block-table entries a wave holds (one per lane)
@@ -86,17 +77,35 @@ __host__ __device__ constexpr int cache_row_bytes(int D, int kq) { return kq == 
 __host__ __device__ constexpr int decode_slot_bytes(int D, int hslots, int kq = 0) {
   return 2 * kDecodeTile * cache_row_bytes(D, kq) + decode_q_bytes(D, hslots) + (kq != 0 ? decode_scale_bytes(D) : 0);
 }
+// Waves per decode workgroup.  Eight (two per SIMD: one computes while the
+// other waits on its loads) whenever each still gets a ring of two tiles in
+// about 150 KB of LDS: quantized caches below head size 256 (half the tile
+// bytes, and a code conversion in every tile), 16-bit caches of head size 64,
+// and of 128 with up to four head slots.  Otherwise four (one per SIMD), or
+// two at head size 256 with 16-bit caches.
+__host__ __device__ constexpr int decode_wg_waves(int D, int kq, int hslots) {
+  return kq != 0 ? (D > 128 ? 4 : 8)
+                 : D > 128 ? 2 : (150 * 1024) / (8 * decode_slot_bytes(D, hslots, 0)) >= 2 ? 8 : 4;
+}
+// With eight waves of 16-bit caches the plan keeps one start per pair of waves
+// (the plan's cost grows with the starts): waves 2v and 2v+1 take the lower
+// and the upper half of pair v's tiles, and wave 2v+1 finds its own start
+// from pair v's.  Quantized caches keep one start per wave (INT4 pairs waves
+// for another purpose, see decode_pair).
+__host__ __device__ constexpr int decode_split(int D, int kq, int hslots) {
+  return kq == 0 && decode_wg_waves(D, kq, hslots) == 8 ? 2 : 1;
+}
 // ring depth: as many slots as fit the workgroup's waves in about 150 KB, at
 // most 4
 __host__ __device__ constexpr int decode_ring(int D, int hslots, int kq = 0) {
-  return (150 * 1024) / (decode_wg_waves(D, kq != 0) * decode_slot_bytes(D, hslots, kq)) > 4
+  return (150 * 1024) / (decode_wg_waves(D, kq, hslots) * decode_slot_bytes(D, hslots, kq)) > 4
              ? 4
-             : (150 * 1024) / (decode_wg_waves(D, kq != 0) * decode_slot_bytes(D, hslots, kq));
+             : (150 * 1024) / (decode_wg_waves(D, kq, hslots) * decode_slot_bytes(D, hslots, kq));
 }
 // per wave: the ring, a 16-byte piece record per slot, 512 bytes of
 // prefetched metadata
 __host__ __device__ constexpr int decode_lds_bytes(int D, int hslots, int kq = 0) {
-  return decode_wg_waves(D, kq != 0) * (decode_ring(D, hslots, kq) * (decode_slot_bytes(D, hslots, kq) + 16) + 512);
+  return decode_wg_waves(D, kq, hslots) * (decode_ring(D, hslots, kq) * (decode_slot_bytes(D, hslots, kq) + 16) + 512);
 }
 __host__ __device__ constexpr int decode_wg_per_cu(int D, int hslots, int kq = 0) {
   return (160 * 1024) / decode_lds_bytes(D, hslots, kq) > 0 ? (160 * 1024) / decode_lds_bytes(D, hslots, kq) : 1;
@@ -114,6 +123,22 @@ __host__ __device__ inline int decode_wave_of(int64_t g, int64_t T, int W) {
 }
 __host__ __device__ inline int64_t decode_wave_begin(int w, int64_t T, int W) {
   return div_floor(static_cast<int64_t>(w) * T, W);
+}
+// The same over W waves split in pairs (SP = 2, decode_split): pair v owns
+// [decode_wave_begin(v, T, W / 2), decode_wave_begin(v + 1, T, W / 2)), wave
+// 2v its lower half (rounded down), wave 2v+1 the rest.
+__host__ __device__ inline int64_t decode_split_mid(int v, int64_t T, int Wp) {
+  const int64_t b = decode_wave_begin(v, T, Wp);
+  return b + (decode_wave_begin(v + 1, T, Wp) - b) / 2;
+}
+__host__ __device__ inline int64_t decode_wave_begin_sp(int w, int64_t T, int W, int SP) {
+  if (SP == 1) return decode_wave_begin(w, T, W);
+  return (w & 1) ? decode_split_mid(w >> 1, T, W >> 1) : decode_wave_begin(w >> 1, T, W >> 1);
+}
+__host__ __device__ inline int decode_wave_of_sp(int64_t g, int64_t T, int W, int SP) {
+  if (SP == 1) return decode_wave_of(g, T, W);
+  const int v = decode_wave_of(g, T, W >> 1);
+  return 2 * v + (g >= decode_split_mid(v, T, W >> 1) ? 1 : 0);
 }
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
@@ -205,6 +230,7 @@ struct AttnParams {
   // 2: waves 2v and 2v+1 stream the same tiles of units 2u and 2u+1 (the plan
   // sees unit pairs and wave pairs); 1: one unit per wave
   int32_t decode_pair;
+  int32_t decode_split;        // 2: waves 2v and 2v+1 halve pair v's tiles (decode_split)
   int32_t prefill_positions;
   float scale_log2;            // scale * log2(e)
   float* lse_out;              // [N, H] natural-log lse, or null

@@ -37,10 +37,11 @@ __device__ inline void merge_segment(const AttnParams& p, int task, int T, int l
   // wave pairs; unit u's pieces are in the waves of its parity
   const int PF = p.decode_pair, par = u % PF;
   const int W = p.decode_waves / PF;
+  const int SP = p.decode_split;  // 2: waves halve the plan's pair ranges
   const int S = tile0 + (u / PF) * n;
-  const int wf = decode_wave_of(S, T, W), wl = decode_wave_of(S + n - 1, T, W);
+  const int wf = decode_wave_of_sp(S, T, W, SP), wl = decode_wave_of_sp(S + n - 1, T, W, SP);
   if (wf == wl) return;  // written whole by its wave
-  const int first_k = decode_wave_begin(wf, T, W) < S ? 1 : 0;
+  const int first_k = decode_wave_begin_sp(wf, T, W, SP) < S ? 1 : 0;
   const int hcc = decode_head_chunks(p.group);
   const int kvh = u / hcc, hc = u % hcc;
   const int nh = min(kDecodeUnitHeads, p.group - kDecodeUnitHeads * hc);
@@ -50,7 +51,7 @@ __device__ inline void merge_segment(const AttnParams& p, int task, int T, int l
   // (with at least as many tiles as waves every range is non-empty)
   const bool every_wave_holds = T >= W;
   auto holds = [&](int v) {
-    return every_wave_holds || v == wf || decode_wave_begin(v, T, W) < decode_wave_begin(v + 1, T, W);
+    return every_wave_holds || v == wf || decode_wave_begin_sp(v, T, W, SP) < decode_wave_begin_sp(v + 1, T, W, SP);
   };
   // partial slot of wave v's piece: the first piece in wf's second slot when
   // the segment starts inside wf's range, every other in the wave's first

@@ -260,7 +260,7 @@ __global__ __launch_bounds__(PrefillShape<D>::THREADS) void prefill_kernel(AttnP
     const int T = p.ws_ctrl[kCtrlDecodeTiles];
     const int nw = static_cast<int>(gridDim.x) * S::WAVES;
     for (int task = first; task < segments; task += nw)
-      merge_segment<D, BF16>(p, task, T, lane, task == first ? sq0 : p.dec_seq[task / U]);
+      merge_segment_any<D, BF16>(p, task, T, lane, task == first ? sq0 : p.dec_seq[task / U]);
   }
 
   const int nq = prefill_queue_count(p.kv_heads);

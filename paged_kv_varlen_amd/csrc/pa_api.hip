@@ -324,15 +324,12 @@ pa_status enqueue(const pa_args* a, const Resolved& r, const WorkspaceLayout& w,
   sp.max_blocks = r.MB;
   sp.block_size = r.bs;
   sp.row_elems = r.Hkv * r.D;
-  // INT4 rows under 128 bytes (head size 128: 64 bytes) are half a memory line:
-  // waves 2v and 2v+1 then stream the same tiles of units 2u and 2u+1 (adjacent
-  // kv heads, or head chunks of one kv head), so both halves of a line are read
-  // by one compute unit at nearly the same time; the plan sees the pairs
+  // paired waves (adjacent units) or split pairs: the plan keeps one start per
+  // pair of waves and sees the unit pairs
   const int units = r.Hkv * decode_head_chunks(r.G);
-  const int pair =
-      r.kq == 4 && cache_row_bytes(r.D, r.kq) < 128 && units % 2 == 0 && w.decode_waves % 2 == 0 ? 2 : 1;
+  const int pair = decode_pair_of(r.D, r.kq, decode_head_slots(r.G), units);
+  const int split = decode_split_of(r.D, r.kq, decode_head_slots(r.G), units);
   sp.decode_units = units / pair;
-  const int split = decode_split(r.D, r.kq, decode_head_slots(r.G));
   sp.decode_waves = w.decode_waves / (pair * split);
   sp.prefill_positions = prefill_positions(r.G);
   sp.kq = r.kq;

@@ -745,7 +745,6 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ, HS)) void decode_kernel
   constexpr bool QNT = KQ != 0;                   // the caches hold codes (INT8 or INT4)
   constexpr bool Q4 = KQ == 4;
   constexpr int kDecodeWaves = decode_wg_waves(D, KQ, HS);
-  constexpr int SP = decode_split(D, KQ, HS);  // 2: waves 2v, 2v+1 halve pair v's tiles
   constexpr int ROW = 2 * D;                      // bytes of one key of one kv head (data type)
   constexpr int CPR = ROW / 16;                   // 16-byte chunks per row
   constexpr int ROWC = cache_row_bytes(D, KQ);    // bytes of a cached row (codes when quantized)
@@ -787,19 +786,21 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ, HS)) void decode_kernel
   if (w >= W) return;
 
   // ---- this wave's share ---------------------------------------------------
-  // paired waves (INT4 rows under a memory line): wave pair vw streams the
-  // tiles of unit pairs, wave 2vw taking units 2u, wave 2vw+1 units 2u+1.
-  // Split pairs (SP = 2, 16-bit caches with eight waves): the plan's record vw
+  // Paired waves (PF = 2): wave pair vw streams the tiles of unit pairs, wave
+  // 2vw taking units 2u, wave 2vw+1 units 2u+1 (adjacent kv heads, read by
+  // one compute unit at nearly the same time).  Split pairs (SP = 2, eight
+  // waves of 16-bit caches when the units cannot pair): the plan's record vw
   // starts pair vw's tiles; wave 2vw takes their lower half, wave 2vw+1 the
   // upper half (decode_wave_begin_sp).
   const int PF = p.decode_pair;
+  const int SP = !QNT && kDecodeWaves == 8 ? p.decode_split : 1;  // (1 for every other shape)
   const int vw = w / (PF * SP), par = w % PF;
   const int* rec = p.dec_start + 8 * vw;
   const int rv = rec[lane & 7];
   const int g_pair = uniform(__builtin_amdgcn_readlane(rv, 3));
   const int g_next = p.dec_start[8 * (vw + 1) + 3];
   int g0 = g_pair, g1 = g_next;
-  if constexpr (SP == 2) {
+  if (SP == 2) {
     const int mid = g_pair + (g_next - g_pair) / 2;
     if (w & 1) g0 = mid;
     else g1 = mid;
@@ -878,7 +879,7 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ, HS)) void decode_kernel
   int L_i = uniform(__builtin_amdgcn_readlane(rv, 6));
   int P_i = uniform(__builtin_amdgcn_readlane(rv, 7));
   int n_i = (L_i + kDecodeTile - 1) / kDecodeTile;
-  if constexpr (SP == 2) {
+  if (SP == 2) {
     if (w & 1) {  // the upper half starts at g0: from the pair's sequence, forward to the one holding g0
       while (g0 >= P_i + U * n_i) {  // (the last sequence ends at T > g0)
         ++d_i;

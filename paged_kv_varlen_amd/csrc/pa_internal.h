@@ -87,13 +87,22 @@ __host__ __device__ constexpr int decode_wg_waves(int D, int kq, int hslots) {
   return kq != 0 ? (D > 128 ? 4 : 8)
                  : D > 128 ? 2 : (150 * 1024) / (8 * decode_slot_bytes(D, hslots, 0)) >= 2 ? 8 : 4;
 }
-// With eight waves of 16-bit caches the plan keeps one start per pair of waves
-// (the plan's cost grows with the starts): waves 2v and 2v+1 take the lower
-// and the upper half of pair v's tiles, and wave 2v+1 finds its own start
-// from pair v's.  Quantized caches keep one start per wave (INT4 pairs waves
-// for another purpose, see decode_pair).
-__host__ __device__ constexpr int decode_split(int D, int kq, int hslots) {
-  return kq == 0 && decode_wg_waves(D, kq, hslots) == 8 ? 2 : 1;
+// Waves 2v and 2v+1 share one of the plan's starts when the decode runs eight
+// waves per workgroup (the plan's cost grows with the starts) or INT4 rows are
+// under a memory line: they stream the same tiles of the adjacent units 2u
+// and 2u+1 (decode_pair = 2), so the rows of two kv heads, contiguous in every
+// cache slot, are read by one compute unit at nearly the same time.  With an
+// odd unit count, eight waves of 16-bit caches split each pair's tiles
+// instead (decode_split = 2): wave 2v takes the lower half, wave 2v+1 the
+// upper half and finds its own start from the pair's.
+__host__ __device__ constexpr int decode_pair_of(int D, int kq, int hslots, int units) {
+  return units % 2 == 0 && (kq == 8 || (kq == 4 && cache_row_bytes(D, kq) < 128) ||
+                            (kq == 0 && decode_wg_waves(D, kq, hslots) == 8))
+             ? 2
+             : 1;
+}
+__host__ __device__ constexpr int decode_split_of(int D, int kq, int hslots, int units) {
+  return kq == 0 && decode_wg_waves(D, kq, hslots) == 8 && decode_pair_of(D, kq, hslots, units) == 1 ? 2 : 1;
 }
 // ring depth: as many slots as fit the workgroup's waves in about 150 KB, at
 // most 4
@@ -124,7 +133,7 @@ __host__ __device__ inline int decode_wave_of(int64_t g, int64_t T, int W) {
 __host__ __device__ inline int64_t decode_wave_begin(int w, int64_t T, int W) {
   return div_floor(static_cast<int64_t>(w) * T, W);
 }
-// The same over W waves split in pairs (SP = 2, decode_split): pair v owns
+// The same over W waves split in pairs (SP = 2, decode_split_of): pair v owns
 // [decode_wave_begin(v, T, W / 2), decode_wave_begin(v + 1, T, W / 2)), wave
 // 2v its lower half (rounded down), wave 2v+1 the rest.
 __host__ __device__ inline int64_t decode_split_mid(int v, int64_t T, int Wp) {
@@ -230,7 +239,7 @@ struct AttnParams {
   // 2: waves 2v and 2v+1 stream the same tiles of units 2u and 2u+1 (the plan
   // sees unit pairs and wave pairs); 1: one unit per wave
   int32_t decode_pair;
-  int32_t decode_split;        // 2: waves 2v and 2v+1 halve pair v's tiles (decode_split)
+  int32_t decode_split;        // 2: waves 2v and 2v+1 halve pair v's tiles (decode_split_of)
   int32_t prefill_positions;
   float scale_log2;            // scale * log2(e)
   float* lse_out;              // [N, H] natural-log lse, or null

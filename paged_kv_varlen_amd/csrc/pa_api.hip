@@ -324,13 +324,13 @@ pa_status enqueue(const pa_args* a, const Resolved& r, const WorkspaceLayout& w,
   sp.max_blocks = r.MB;
   sp.block_size = r.bs;
   sp.row_elems = r.Hkv * r.D;
-  // paired waves (adjacent units) or split pairs: the plan keeps one start per
-  // pair of waves and sees the unit pairs
+  // unit groups or split pairs: the plan keeps one start per group (pair) of
+  // waves and sees the unit groups
   const int units = r.Hkv * decode_head_chunks(r.G);
-  const int pair = decode_pair_of(r.D, r.kq, decode_head_slots(r.G), units);
+  const int ugroup = decode_unit_group_of(r.D, r.kq, decode_head_slots(r.G), units);
   const int split = decode_split_of(r.D, r.kq, decode_head_slots(r.G), units);
-  sp.decode_units = units / pair;
-  sp.decode_waves = w.decode_waves / (pair * split);
+  sp.decode_units = units / ugroup;
+  sp.decode_waves = w.decode_waves / (ugroup * split);
   sp.prefill_positions = prefill_positions(r.G);
   sp.kq = r.kq;
   sp.bf16 = a->dtype == PA_DTYPE_BF16 ? 1 : 0;
@@ -380,7 +380,7 @@ pa_status enqueue(const pa_args* a, const Resolved& r, const WorkspaceLayout& w,
   ap.block_size = r.bs;
   ap.decode_units = units;
   ap.decode_waves = w.decode_waves;
-  ap.decode_pair = pair;
+  ap.decode_unit_group = ugroup;
   ap.decode_split = split;
   ap.prefill_positions = prefill_positions(r.G);
   ap.scale_log2 = r.scale * 1.4426950408889634f;

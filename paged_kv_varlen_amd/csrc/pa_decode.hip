@@ -786,13 +786,13 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ, HS)) void decode_kernel
   if (w >= W) return;
 
   // ---- this wave's share ---------------------------------------------------
-  // Paired waves (PF = 2): wave pair vw streams the tiles of unit pairs, wave
-  // 2vw taking units 2u, wave 2vw+1 units 2u+1 (adjacent kv heads, read by
-  // one compute unit at nearly the same time).  Split pairs (SP = 2, eight
-  // waves of 16-bit caches when the units cannot pair): the plan's record vw
-  // starts pair vw's tiles; wave 2vw takes their lower half, wave 2vw+1 the
-  // upper half (decode_wave_begin_sp).
-  const int PF = p.decode_pair;
+  // Unit groups (PF = 8, 4 or 2): wave group vw streams the tiles of unit
+  // groups, wave PF vw + par taking units PF u + par (consecutive kv heads,
+  // read by one compute unit at nearly the same time).  Split pairs (SP = 2,
+  // eight waves of 16-bit caches when the units cannot be grouped): the
+  // plan's record vw starts pair vw's tiles; wave 2vw takes their lower half,
+  // wave 2vw+1 the upper half (decode_wave_begin_sp).
+  const int PF = p.decode_unit_group;
   const int SP = !QNT && kDecodeWaves == 8 ? p.decode_split : 1;  // (1 for every other shape)
   const int vw = w / (PF * SP), par = w % PF;
   const int* rec = p.dec_start + 8 * vw;
@@ -807,7 +807,7 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ, HS)) void decode_kernel
   }
   if (g0 >= g1) return;
   const int Bd = p.ws_ctrl[kCtrlDecodeSeqs];
-  const int U = p.decode_units / PF;  // units (pairs) per sequence in the tile order
+  const int U = p.decode_units / PF;  // unit groups per sequence in the tile order
   const int hcc = decode_head_chunks(p.group);
   const int G = p.group;
   const int bs = p.block_size;

@@ -87,22 +87,26 @@ __host__ __device__ constexpr int decode_wg_waves(int D, int kq, int hslots) {
   return kq != 0 ? (D > 128 ? 4 : 8)
                  : D > 128 ? 2 : (150 * 1024) / (8 * decode_slot_bytes(D, hslots, 0)) >= 2 ? 8 : 4;
 }
-// Waves 2v and 2v+1 share one of the plan's starts when the decode runs eight
-// waves per workgroup (the plan's cost grows with the starts) or INT4 rows are
-// under a memory line: they stream the same tiles of the adjacent units 2u
-// and 2u+1 (decode_pair = 2), so the rows of two kv heads, contiguous in every
-// cache slot, are read by one compute unit at nearly the same time.  With an
-// odd unit count, eight waves of 16-bit caches split each pair's tiles
-// instead (decode_split = 2): wave 2v takes the lower half, wave 2v+1 the
-// upper half and finds its own start from the pair's.
-__host__ __device__ constexpr int decode_pair_of(int D, int kq, int hslots, int units) {
-  return units % 2 == 0 && (kq == 8 || (kq == 4 && cache_row_bytes(D, kq) < 128) ||
-                            (kq == 0 && decode_wg_waves(D, kq, hslots) == 8))
-             ? 2
-             : 1;
+// Unit groups: when a workgroup runs eight waves (every 16-bit decode with
+// eight waves, INT8 and INT4 caches below head size 256), waves PF v .. PF v +
+// PF - 1 share one of the plan's starts and stream the same tiles of the
+// consecutive units PF u .. PF u + PF - 1 (PF = 8, 4 or 2, the largest that
+// divides the unit count).  At PF = 8 a workgroup reads whole cache pages:
+// the rows of all kv heads of a slot are contiguous, and one compute unit
+// requests them at nearly the same time (for INT4 rows under a memory line,
+// both halves of every line).  The plan also computes PF times fewer starts.
+// With an odd unit count, eight waves of 16-bit caches split each pair of
+// waves' tiles instead (decode_split = 2): wave 2v takes the lower half, wave
+// 2v+1 the upper half and finds its own start from the pair's.
+__host__ __device__ constexpr int decode_unit_group_of(int D, int kq, int hslots, int units) {
+  return decode_wg_waves(D, kq, hslots) != 8 ? 1
+         : units % 8 == 0                    ? 8
+         : units % 4 == 0                    ? 4
+         : units % 2 == 0                    ? 2
+                                             : 1;
 }
 __host__ __device__ constexpr int decode_split_of(int D, int kq, int hslots, int units) {
-  return kq == 0 && decode_wg_waves(D, kq, hslots) == 8 && decode_pair_of(D, kq, hslots, units) == 1 ? 2 : 1;
+  return kq == 0 && decode_wg_waves(D, kq, hslots) == 8 && decode_unit_group_of(D, kq, hslots, units) == 1 ? 2 : 1;
 }
 // ring depth: as many slots as fit the workgroup's waves in about 150 KB, at
 // most 4
@@ -236,9 +240,10 @@ struct AttnParams {
   int32_t block_size;
   int32_t decode_units;        // units per sequence
   int32_t decode_waves;        // W
-  // 2: waves 2v and 2v+1 stream the same tiles of units 2u and 2u+1 (the plan
-  // sees unit pairs and wave pairs); 1: one unit per wave
-  int32_t decode_pair;
+  // PF = 8, 4 or 2: waves PF v .. PF v + PF - 1 stream the same tiles of units
+  // PF u .. PF u + PF - 1 (the plan sees unit groups and wave groups); 1: one
+  // unit per wave (decode_unit_group_of)
+  int32_t decode_unit_group;
   int32_t decode_split;        // 2: waves 2v and 2v+1 halve pair v's tiles (decode_split_of)
   int32_t prefill_positions;
   float scale_log2;            // scale * log2(e)

@@ -37,9 +37,9 @@ __device__ inline void merge_segment(const AttnParams& p, int task, int T, int l
   const int U = p.decode_units;
   const int u = task % U;
   const int n = (L + kDecodeTile - 1) / kDecodeTile;
-  // paired waves: the tile order and the wave ranges are over unit pairs and
-  // wave pairs; unit u's pieces are in the waves of its parity
-  const int PF = p.decode_pair, par = u % PF;
+  // unit groups: the tile order and the wave ranges are over unit groups and
+  // wave groups; unit u's pieces are in the waves of its place in the group
+  const int PF = p.decode_unit_group, par = u % PF;
   const int W = p.decode_waves / PF;
   const int SP = p.decode_split;  // 2: waves halve the plan's pair ranges
   const int S = tile0 + (u / PF) * n;

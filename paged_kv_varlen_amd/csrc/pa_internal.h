@@ -87,23 +87,22 @@ __host__ __device__ constexpr int decode_wg_waves(int D, int kq, int hslots) {
   return kq != 0 ? (D > 128 ? 4 : 8)
                  : D > 128 ? 2 : (150 * 1024) / (8 * decode_slot_bytes(D, hslots, 0)) >= 2 ? 8 : 4;
 }
-// Unit groups: when a workgroup runs eight waves (every 16-bit decode with
-// eight waves, INT8 and INT4 caches below head size 256), waves PF v .. PF v +
-// PF - 1 share one of the plan's starts and stream the same tiles of the
-// consecutive units PF u .. PF u + PF - 1 (PF = 8, 4 or 2, the largest that
-// divides the unit count).  At PF = 8 a workgroup reads whole cache pages:
-// the rows of all kv heads of a slot are contiguous, and one compute unit
-// requests them at nearly the same time (for INT4 rows under a memory line,
-// both halves of every line).  The plan also computes PF times fewer starts.
-// With an odd unit count, eight waves of 16-bit caches split each pair of
-// waves' tiles instead (decode_split = 2): wave 2v takes the lower half, wave
-// 2v+1 the upper half and finds its own start from the pair's.
+// Unit groups: waves PF v .. PF v + PF - 1 of a workgroup share one of the
+// plan's starts and stream the same tiles of the consecutive units PF u .. PF
+// u + PF - 1 (PF = 8, 4 or 2, the largest that divides both the unit count
+// and the workgroup's waves).  With all waves of a workgroup in one group it
+// reads whole cache pages at eight kv heads: the rows of all kv heads of a
+// slot are contiguous, and one compute unit requests them at nearly the same
+// time (for INT4 rows under a memory line, both halves of every line).  The
+// plan also computes PF times fewer starts.  With an odd unit count, eight
+// waves of 16-bit caches split each pair of waves' tiles instead
+// (decode_split = 2): wave 2v takes the lower half, wave 2v+1 the upper half
+// and finds its own start from the pair's.
 __host__ __device__ constexpr int decode_unit_group_of(int D, int kq, int hslots, int units) {
-  return decode_wg_waves(D, kq, hslots) != 8 ? 1
-         : units % 8 == 0                    ? 8
-         : units % 4 == 0                    ? 4
-         : units % 2 == 0                    ? 2
-                                             : 1;
+  return units % 8 == 0 && decode_wg_waves(D, kq, hslots) % 8 == 0   ? 8
+         : units % 4 == 0 && decode_wg_waves(D, kq, hslots) % 4 == 0 ? 4
+         : units % 2 == 0 && decode_wg_waves(D, kq, hslots) % 2 == 0 ? 2
+                                                                     : 1;
 }
 __host__ __device__ constexpr int decode_split_of(int D, int kq, int hslots, int units) {
   return kq == 0 && decode_wg_waves(D, kq, hslots) == 8 && decode_unit_group_of(D, kq, hslots, units) == 1 ? 2 : 1;

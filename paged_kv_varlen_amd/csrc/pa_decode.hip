@@ -520,8 +520,8 @@ struct CodeRegs<256> {
 
 // INT4 caches: XOR swizzle (16-byte chunks) of code row r for head sizes 128
 // and 256 (rows of 64 and 128 bytes), chosen like swz8 for the 4-byte K reads
-// and the byte reads of V; head size 64 (32-byte rows, 4-byte direct loads)
-// is not swizzled
+// (the transposing V reads take 32 contiguous bytes of each of 16 rows); head
+// size 64 (32-byte rows, 4-byte direct loads) is not swizzled
 template <int D>
 __device__ inline int swz4(int r) {
   if constexpr (D == 128) return (r >> 2) & 3;
@@ -529,206 +529,77 @@ __device__ inline int swz4(int r) {
   else return 0;
 }
 
-// INT4 caches: the tile's code bytes, converted in registers.  k[s]: the 8
-// codes of key n at d = 32 s + 8 g .. +7 (4 bytes, one ds_read_b32).  v[4 blk
-// + j]: the byte holding the code of key 4 g + j at d = 16 blk + n (its
-// nibble n & 1).  As for CodeRegs, four base addresses per lane serve every
-// block, and head size 256 reads in two parts.
+// INT4 caches: the tile's codes as operand bits, converted in registers.
+// k[s]: the 8 codes of key n at d = 32 s + 8 g .. +7 (4 bytes, one
+// ds_read_b32).  v[R]: the V^T operands of blocks 4R .. 4R+3 from one
+// transposing read (ds_read_b64_tr_b4).  That read takes, in each group of 16
+// lanes, one 8-byte row per lane (16 codes) and hands lane l code l of every
+// row, row r as code r of its result.  Lane r of group g supplies row r = the
+// 16 codes of key 4 g + (r & 3) at d = 16 (4R + (r >> 2)) .. +15, so lane (n,
+// g) receives codes 4j .. 4j+3 = keys 4 g .. 4 g + 3 of column d = 16 (4R +
+// j) + n: the A operand of block 4R + j as the 16x16x16 product reads it.
+// One address register per read (vt[R]).
 template <int D>
 struct CodeRegs4;
 template <>
 struct CodeRegs4<64> {
-  static constexpr int FIRST = 4;  // V blocks of read(); read_rest() has the others
   uint32_t k[2];
-  uint32_t v[16];
+  u32x2 v[1];
   template <int OFF>
-  __device__ void read(const uint32_t (&ka)[2], const uint32_t (&vb)[4]) {
+  __device__ void read(const uint32_t (&ka)[2], const uint32_t (&vt)[4]) {
     asm volatile(
-        "ds_read_b32 %0, %18 offset:%24\n\t"
-        "ds_read_b32 %1, %19 offset:%24\n\t"
-        "ds_read_u8 %2, %20 offset:%24+0\n\t"
-        "ds_read_u8 %3, %20 offset:%24+32\n\t"
-        "ds_read_u8 %4, %20 offset:%24+64\n\t"
-        "ds_read_u8 %5, %20 offset:%24+96\n\t"
-        "ds_read_u8 %6, %21 offset:%24+0\n\t"
-        "ds_read_u8 %7, %21 offset:%24+32\n\t"
-        "ds_read_u8 %8, %21 offset:%24+64\n\t"
-        "ds_read_u8 %9, %21 offset:%24+96\n\t"
-        "ds_read_u8 %10, %22 offset:%24+0\n\t"
-        "ds_read_u8 %11, %22 offset:%24+32\n\t"
-        "ds_read_u8 %12, %22 offset:%24+64\n\t"
-        "ds_read_u8 %13, %22 offset:%24+96\n\t"
-        "ds_read_u8 %14, %23 offset:%24+0\n\t"
-        "ds_read_u8 %15, %23 offset:%24+32\n\t"
-        "ds_read_u8 %16, %23 offset:%24+64\n\t"
-        "ds_read_u8 %17, %23 offset:%24+96\n\t"
+        "ds_read_b32 %0, %3 offset:%6\n\t"
+        "ds_read_b32 %1, %4 offset:%6\n\t"
+        "ds_read_b64_tr_b4 %2, %5 offset:%6\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
-          "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]),
-          "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15])
-        : "v"(ka[0]), "v"(ka[1]), "v"(vb[0]), "v"(vb[1]), "v"(vb[2]), "v"(vb[3]), "n"(OFF)
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(v[0])
+        : "v"(ka[0]), "v"(ka[1]), "v"(vt[0]), "n"(OFF)
         : "memory");
   }
-  template <int OFF>
-  __device__ void read_rest(const uint32_t (&)[2], const uint32_t (&)[4]) {}
 };
 template <>
 struct CodeRegs4<128> {
-  static constexpr int FIRST = 8;  // V blocks of read(); read_rest() has the others
   uint32_t k[4];
-  uint32_t v[32];
+  u32x2 v[2];
   template <int OFF>
-  __device__ void read(const uint32_t (&ka)[4], const uint32_t (&vb)[4]) {
+  __device__ void read(const uint32_t (&ka)[4], const uint32_t (&vt)[4]) {
     asm volatile(
-        "ds_read_b32 %0, %36 offset:%44\n\t"
-        "ds_read_b32 %1, %37 offset:%44\n\t"
-        "ds_read_b32 %2, %38 offset:%44\n\t"
-        "ds_read_b32 %3, %39 offset:%44\n\t"
-        "ds_read_u8 %4, %40 offset:%44+0\n\t"
-        "ds_read_u8 %5, %40 offset:%44+64\n\t"
-        "ds_read_u8 %6, %40 offset:%44+128\n\t"
-        "ds_read_u8 %7, %40 offset:%44+192\n\t"
-        "ds_read_u8 %8, %40 offset:%44+8\n\t"
-        "ds_read_u8 %9, %40 offset:%44+72\n\t"
-        "ds_read_u8 %10, %40 offset:%44+136\n\t"
-        "ds_read_u8 %11, %40 offset:%44+200\n\t"
-        "ds_read_u8 %12, %41 offset:%44+0\n\t"
-        "ds_read_u8 %13, %41 offset:%44+64\n\t"
-        "ds_read_u8 %14, %41 offset:%44+128\n\t"
-        "ds_read_u8 %15, %41 offset:%44+192\n\t"
-        "ds_read_u8 %16, %41 offset:%44+8\n\t"
-        "ds_read_u8 %17, %41 offset:%44+72\n\t"
-        "ds_read_u8 %18, %41 offset:%44+136\n\t"
-        "ds_read_u8 %19, %41 offset:%44+200\n\t"
-        "ds_read_u8 %20, %42 offset:%44+0\n\t"
-        "ds_read_u8 %21, %42 offset:%44+64\n\t"
-        "ds_read_u8 %22, %42 offset:%44+128\n\t"
-        "ds_read_u8 %23, %42 offset:%44+192\n\t"
-        "ds_read_u8 %24, %42 offset:%44+8\n\t"
-        "ds_read_u8 %25, %42 offset:%44+72\n\t"
-        "ds_read_u8 %26, %42 offset:%44+136\n\t"
-        "ds_read_u8 %27, %42 offset:%44+200\n\t"
-        "ds_read_u8 %28, %43 offset:%44+0\n\t"
-        "ds_read_u8 %29, %43 offset:%44+64\n\t"
-        "ds_read_u8 %30, %43 offset:%44+128\n\t"
-        "ds_read_u8 %31, %43 offset:%44+192\n\t"
-        "ds_read_u8 %32, %43 offset:%44+8\n\t"
-        "ds_read_u8 %33, %43 offset:%44+72\n\t"
-        "ds_read_u8 %34, %43 offset:%44+136\n\t"
-        "ds_read_u8 %35, %43 offset:%44+200\n\t"
+        "ds_read_b32 %0, %6 offset:%12\n\t"
+        "ds_read_b32 %1, %7 offset:%12\n\t"
+        "ds_read_b32 %2, %8 offset:%12\n\t"
+        "ds_read_b32 %3, %9 offset:%12\n\t"
+        "ds_read_b64_tr_b4 %4, %10 offset:%12\n\t"
+        "ds_read_b64_tr_b4 %5, %11 offset:%12\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]),
-          "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]),
-          "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15]), "=&v"(v[16]), "=&v"(v[17]), "=&v"(v[18]),
-          "=&v"(v[19]), "=&v"(v[20]), "=&v"(v[21]), "=&v"(v[22]), "=&v"(v[23]), "=&v"(v[24]), "=&v"(v[25]),
-          "=&v"(v[26]), "=&v"(v[27]), "=&v"(v[28]), "=&v"(v[29]), "=&v"(v[30]), "=&v"(v[31])
-        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(vb[0]), "v"(vb[1]), "v"(vb[2]), "v"(vb[3]), "n"(OFF)
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v[0]), "=&v"(v[1])
+        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(vt[0]), "v"(vt[1]), "n"(OFF)
         : "memory");
   }
-  template <int OFF>
-  __device__ void read_rest(const uint32_t (&)[4], const uint32_t (&)[4]) {}
 };
 template <>
 struct CodeRegs4<256> {
-  static constexpr int FIRST = 8;  // V blocks of read(); read_rest() has the others
   uint32_t k[8];
-  uint32_t v[64];
+  u32x2 v[4];
   template <int OFF>
-  __device__ void read(const uint32_t (&ka)[8], const uint32_t (&vb)[4]) {
+  __device__ void read(const uint32_t (&ka)[8], const uint32_t (&vt)[4]) {
     asm volatile(
-        "ds_read_b32 %0, %40 offset:%52\n\t"
-        "ds_read_b32 %1, %41 offset:%52\n\t"
-        "ds_read_b32 %2, %42 offset:%52\n\t"
-        "ds_read_b32 %3, %43 offset:%52\n\t"
-        "ds_read_b32 %4, %44 offset:%52\n\t"
-        "ds_read_b32 %5, %45 offset:%52\n\t"
-        "ds_read_b32 %6, %46 offset:%52\n\t"
-        "ds_read_b32 %7, %47 offset:%52\n\t"
-        "ds_read_u8 %8, %48 offset:%52+0\n\t"
-        "ds_read_u8 %9, %48 offset:%52+128\n\t"
-        "ds_read_u8 %10, %48 offset:%52+272\n\t"
-        "ds_read_u8 %11, %48 offset:%52+400\n\t"
-        "ds_read_u8 %12, %48 offset:%52+8\n\t"
-        "ds_read_u8 %13, %48 offset:%52+136\n\t"
-        "ds_read_u8 %14, %48 offset:%52+280\n\t"
-        "ds_read_u8 %15, %48 offset:%52+408\n\t"
-        "ds_read_u8 %16, %48 offset:%52+16\n\t"
-        "ds_read_u8 %17, %48 offset:%52+144\n\t"
-        "ds_read_u8 %18, %48 offset:%52+256\n\t"
-        "ds_read_u8 %19, %48 offset:%52+384\n\t"
-        "ds_read_u8 %20, %48 offset:%52+24\n\t"
-        "ds_read_u8 %21, %48 offset:%52+152\n\t"
-        "ds_read_u8 %22, %48 offset:%52+264\n\t"
-        "ds_read_u8 %23, %48 offset:%52+392\n\t"
-        "ds_read_u8 %24, %49 offset:%52+0\n\t"
-        "ds_read_u8 %25, %49 offset:%52+128\n\t"
-        "ds_read_u8 %26, %49 offset:%52+272\n\t"
-        "ds_read_u8 %27, %49 offset:%52+400\n\t"
-        "ds_read_u8 %28, %49 offset:%52+8\n\t"
-        "ds_read_u8 %29, %49 offset:%52+136\n\t"
-        "ds_read_u8 %30, %49 offset:%52+280\n\t"
-        "ds_read_u8 %31, %49 offset:%52+408\n\t"
-        "ds_read_u8 %32, %49 offset:%52+16\n\t"
-        "ds_read_u8 %33, %49 offset:%52+144\n\t"
-        "ds_read_u8 %34, %49 offset:%52+256\n\t"
-        "ds_read_u8 %35, %49 offset:%52+384\n\t"
-        "ds_read_u8 %36, %49 offset:%52+24\n\t"
-        "ds_read_u8 %37, %49 offset:%52+152\n\t"
-        "ds_read_u8 %38, %49 offset:%52+264\n\t"
-        "ds_read_u8 %39, %49 offset:%52+392\n\t"
+        "ds_read_b32 %0, %12 offset:%24\n\t"
+        "ds_read_b32 %1, %13 offset:%24\n\t"
+        "ds_read_b32 %2, %14 offset:%24\n\t"
+        "ds_read_b32 %3, %15 offset:%24\n\t"
+        "ds_read_b32 %4, %16 offset:%24\n\t"
+        "ds_read_b32 %5, %17 offset:%24\n\t"
+        "ds_read_b32 %6, %18 offset:%24\n\t"
+        "ds_read_b32 %7, %19 offset:%24\n\t"
+        "ds_read_b64_tr_b4 %8, %20 offset:%24\n\t"
+        "ds_read_b64_tr_b4 %9, %21 offset:%24\n\t"
+        "ds_read_b64_tr_b4 %10, %22 offset:%24\n\t"
+        "ds_read_b64_tr_b4 %11, %23 offset:%24\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]), "=&v"(k[6]), "=&v"(k[7]),
-          "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
-          "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]),
-          "=&v"(v[15]), "=&v"(v[16]), "=&v"(v[17]), "=&v"(v[18]), "=&v"(v[19]), "=&v"(v[20]), "=&v"(v[21]),
-          "=&v"(v[22]), "=&v"(v[23]), "=&v"(v[24]), "=&v"(v[25]), "=&v"(v[26]), "=&v"(v[27]), "=&v"(v[28]),
-          "=&v"(v[29]), "=&v"(v[30]), "=&v"(v[31])
+          "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
         : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(ka[4]), "v"(ka[5]), "v"(ka[6]), "v"(ka[7]),
-          "v"(vb[0]), "v"(vb[1]), "v"(vb[2]), "v"(vb[3]), "n"(OFF)
-        : "memory");
-  }
-  template <int OFF>
-  __device__ void read_rest(const uint32_t (&ka)[8], const uint32_t (&vb)[4]) {
-    asm volatile(
-        "ds_read_u8 %0, %34 offset:%36+0\n\t"
-        "ds_read_u8 %1, %34 offset:%36+128\n\t"
-        "ds_read_u8 %2, %34 offset:%36+272\n\t"
-        "ds_read_u8 %3, %34 offset:%36+400\n\t"
-        "ds_read_u8 %4, %34 offset:%36+8\n\t"
-        "ds_read_u8 %5, %34 offset:%36+136\n\t"
-        "ds_read_u8 %6, %34 offset:%36+280\n\t"
-        "ds_read_u8 %7, %34 offset:%36+408\n\t"
-        "ds_read_u8 %8, %34 offset:%36+16\n\t"
-        "ds_read_u8 %9, %34 offset:%36+144\n\t"
-        "ds_read_u8 %10, %34 offset:%36+256\n\t"
-        "ds_read_u8 %11, %34 offset:%36+384\n\t"
-        "ds_read_u8 %12, %34 offset:%36+24\n\t"
-        "ds_read_u8 %13, %34 offset:%36+152\n\t"
-        "ds_read_u8 %14, %34 offset:%36+264\n\t"
-        "ds_read_u8 %15, %34 offset:%36+392\n\t"
-        "ds_read_u8 %16, %35 offset:%36+0\n\t"
-        "ds_read_u8 %17, %35 offset:%36+128\n\t"
-        "ds_read_u8 %18, %35 offset:%36+272\n\t"
-        "ds_read_u8 %19, %35 offset:%36+400\n\t"
-        "ds_read_u8 %20, %35 offset:%36+8\n\t"
-        "ds_read_u8 %21, %35 offset:%36+136\n\t"
-        "ds_read_u8 %22, %35 offset:%36+280\n\t"
-        "ds_read_u8 %23, %35 offset:%36+408\n\t"
-        "ds_read_u8 %24, %35 offset:%36+16\n\t"
-        "ds_read_u8 %25, %35 offset:%36+144\n\t"
-        "ds_read_u8 %26, %35 offset:%36+256\n\t"
-        "ds_read_u8 %27, %35 offset:%36+384\n\t"
-        "ds_read_u8 %28, %35 offset:%36+24\n\t"
-        "ds_read_u8 %29, %35 offset:%36+152\n\t"
-        "ds_read_u8 %30, %35 offset:%36+264\n\t"
-        "ds_read_u8 %31, %35 offset:%36+392\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(v[32]), "=&v"(v[33]), "=&v"(v[34]), "=&v"(v[35]), "=&v"(v[36]), "=&v"(v[37]), "=&v"(v[38]),
-          "=&v"(v[39]), "=&v"(v[40]), "=&v"(v[41]), "=&v"(v[42]), "=&v"(v[43]), "=&v"(v[44]), "=&v"(v[45]),
-          "=&v"(v[46]), "=&v"(v[47]), "=&v"(v[48]), "=&v"(v[49]), "=&v"(v[50]), "=&v"(v[51]), "=&v"(v[52]),
-          "=&v"(v[53]), "=&v"(v[54]), "=&v"(v[55]), "=&v"(v[56]), "=&v"(v[57]), "=&v"(v[58]), "=&v"(v[59]),
-          "=&v"(v[60]), "=&v"(v[61]), "=&v"(v[62]), "=&v"(v[63])
-        : "v"(vb[0]), "v"(vb[1]), "v"(vb[2]), "v"(vb[3]), "n"(OFF)
+          "v"(vt[0]), "v"(vt[1]), "v"(vt[2]), "v"(vt[3]), "n"(OFF)
         : "memory");
   }
 };
@@ -844,12 +715,15 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ, HS)) void decode_kernel
     qa[s] = ring0 + 2 * TBC + (n < QB / ROW ? n : 0) * ROW + 16 * (4 * s + g);
   }
   if constexpr (Q4) {
-    // the byte of block blk and key 4g+j (CodeRegs4) is at vb[i] + a constant:
-    // D = 64: i = blk; 128: i = blk / 2; 256: i = blk / 4
+    // row of transposing read R (CodeRegs4): key 4g + (n & 3), codes of block
+    // 4R + (n >> 2), i.e. bytes 8 blk .. +7 of the key's row (chunk blk / 2,
+    // swizzled, half blk & 1)
+    const int key = 4 * g + (n & 3);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      vb[i] = ring0 + TBC + (n >> 1) + (D == 64 ? 128 * g + 8 * i : D == 128 ? 256 * g + 16 * (i ^ g)
-                                                                             : 512 * g + 32 * (i ^ g));
+    for (int R = 0; R < 4; ++R) {
+      const int blk = 4 * R + (n >> 2);
+      vb[R] = R < DB / 4 ? ring0 + TBC + key * ROWC + 16 * ((blk >> 1) ^ swz4<D>(key)) + 8 * (blk & 1) : 0u;
+    }
   } else if constexpr (QNT) {
     // byte j of block blk (key 4g+j, d = 16 blk + n) is at vb[i] + a constant
     // (CodeRegs): D = 64: i = blk; 128: i = blk / 2; 256: i = blk % 4
@@ -1116,21 +990,18 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ, HS)) void decode_kernel
     typename E::x4 vx[DB];
     if constexpr (Q4) {  // INT4 codes -> data type in registers (exact)
       CodeRegs4<D> cr;
-      const int sh = 4 * (n & 1);  // this lane's nibble of a V byte
-      auto v_block = [&](int blk) __attribute__((always_inline)) {
-        const uint32_t* b = &cr.v[4 * blk];  // keys j = 0..3, one byte each
-        const typename E::x2 a = E::from_nibble_bytes(__builtin_amdgcn_perm(b[1], b[0], 0x0c040c00u), sh);
-        const typename E::x2 c = E::from_nibble_bytes(__builtin_amdgcn_perm(b[3], b[2], 0x0c040c00u), sh);
-        vx[blk] = typename E::x4{a[0], a[1], c[0], c[1]};
-      };
       cr.template read<S * SLOT>(ka, vb);
 #pragma unroll
       for (int s = 0; s < KS; ++s) kx[s] = E::from_nibbles8(cr.k[s]);
+      // codes 8h .. 8h+7 of read R: blocks 4R + 2h and 4R + 2h + 1, keys 4g .. 4g+3 each
 #pragma unroll
-      for (int blk = 0; blk < CodeRegs4<D>::FIRST; ++blk) v_block(blk);
-      cr.template read_rest<S * SLOT>(ka, vb);
+      for (int R = 0; R < DB / 4; ++R)
 #pragma unroll
-      for (int blk = CodeRegs4<D>::FIRST; blk < DB; ++blk) v_block(blk);
+        for (int h = 0; h < 2; ++h) {
+          const typename E::x8 t = E::from_nibbles8(h == 0 ? cr.v[R].x : cr.v[R].y);
+          vx[4 * R + 2 * h] = typename E::x4{t[0], t[1], t[2], t[3]};
+          vx[4 * R + 2 * h + 1] = typename E::x4{t[4], t[5], t[6], t[7]};
+        }
     } else if constexpr (QNT) {  // INT8 codes -> data type in registers (exact)
       CodeRegs<D> cr;
       auto v_block = [&](int blk) __attribute__((always_inline)) {

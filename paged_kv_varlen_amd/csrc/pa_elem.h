@@ -78,11 +78,6 @@ struct Elem<false> {  // IEEE binary16
     const x2 bias = {static_cast<_Float16>(1032.f), static_cast<_Float16>(1032.f)};
     return __builtin_bit_cast(x2, h | 0x64006400u) - bias;
   }
-  // the codes in the nibbles at bit sh of the two bytes that sit (zero-extended)
-  // in the 16-bit halves of w
-  static __device__ inline x2 from_nibble_bytes(uint32_t w, int sh) {
-    return minus_1032(((w ^ 0x00880088u) >> sh) & 0x000F000Fu);
-  }
   // eight int4 codes (nibble e of w is code e) as values: the even codes (low
   // nibbles) and odd ones (high nibbles) of each byte are paired by v_perm_b32
   static __device__ inline x8 from_nibbles8(uint32_t w) {
@@ -140,14 +135,6 @@ struct Elem<true> {  // bfloat16: the upper half of a binary32
     const uint32_t u = w ^ 0x00800080u;  // code + 128 in bits 0..7 and 16..23
     return x2{static_cast<__bf16>(static_cast<float>(u & 0xffu) - 128.f),
               static_cast<__bf16>(static_cast<float>((u >> 16) & 0xffu) - 128.f)};
-  }
-  // the codes in the nibbles at bit sh of the two bytes that sit (zero-extended)
-  // in the 16-bit halves of w
-  static __device__ inline x2 from_nibble_bytes(uint32_t w, int sh) {
-    // (the builtin's result type is unsigned: the sign-extended field is read back as int)
-    const int c0 = static_cast<int>(__builtin_amdgcn_sbfe(w, sh, 4));
-    const int c1 = static_cast<int>(__builtin_amdgcn_sbfe(w, 16 + sh, 4));
-    return x2{static_cast<__bf16>(static_cast<float>(c0)), static_cast<__bf16>(static_cast<float>(c1))};
   }
   // eight int4 codes (nibble e of w is code e) as values
   static __device__ inline x8 from_nibbles8(uint32_t w) {

@@ -301,9 +301,9 @@ __device__ inline int swz(int k) {
 }
 
 // INT8 caches: XOR swizzle (in 16-byte chunks) of code row r (0..15) of a
-// tile, chosen so that the 8-byte K reads (16 keys, 16 lanes each) and the
-// byte reads of V (keys 4g+j of 16 lanes g, one 16-byte chunk each) touch
-// distinct LDS banks (every 256 bytes hold 256 / D rows)
+// tile, chosen so that the 8-byte K reads (16 keys, 16 lanes each) touch
+// distinct LDS banks (every 256 bytes hold 256 / D rows); the transposing V
+// reads take one whole chunk of each of 16 rows
 template <int D>
 __device__ inline int swz8(int r) {
   if constexpr (D == 64) return (r >> 2) & 3;
@@ -313,207 +313,82 @@ __device__ inline int swz8(int r) {
 
 // INT8 caches: the tile's codes as operand bits, converted in registers.
 // k[s]: the 8 codes of key n at d = 32 s + 8 g .. +7 (one ds_read_b64).
-// v[4 blk + j]: the code of key 4 g + j at d = 16 blk + n (ds_read_u8, one
-// register each: the 16-bit d16 loads do not keep the other half of their
-// register on parts with SRAM ECC).  Byte j of block blk sits at vb[.] + a
-// constant: with the swizzle above, four base addresses per lane serve every
-// block.  Head size 256 reads in two parts (read, then read_rest), each with
-// its own wait, to bound the registers in flight.
+// v[R]: the V^T operands of blocks 2R and 2R+1 from one transposing read
+// (ds_read_b64_tr_b8).  That read forms, in each group of 16 lanes, eight
+// 16-byte rows (row e: the 8 bytes of lane 2e, then those of lane 2e+1) and
+// hands lane l byte l of every row, row e as byte e of its result.  Row e of
+// group g is the 16 codes of key 4 g + (e & 3) at d = 16 (2R + (e >> 2)) ..
+// +15, so lane (n, g) receives keys 4 g .. 4 g + 3 of column d = 16 (2R + j)
+// + n as bytes 4j .. 4j+3: the A operands of blocks 2R and 2R+1 as the
+// 16x16x16 product reads them.  One address register per read (vt[R]).
 template <int D>
 struct CodeRegs;
 template <>
 struct CodeRegs<64> {
-  static constexpr int FIRST = 4;  // V blocks of read(); read_rest() has the others
   u32x2 k[2];
-  uint32_t v[16];
+  u32x2 v[2];
   template <int OFF>
-  __device__ void read(const uint32_t (&ka)[2], const uint32_t (&vb)[4]) {
+  __device__ void read(const uint32_t (&ka)[2], const uint32_t (&vt)[8]) {
     asm volatile(
-        "ds_read_b64 %0, %18 offset:%24\n\t"
-        "ds_read_b64 %1, %19 offset:%24\n\t"
-        "ds_read_u8 %2, %20 offset:%24+0\n\t"
-        "ds_read_u8 %3, %20 offset:%24+64\n\t"
-        "ds_read_u8 %4, %20 offset:%24+128\n\t"
-        "ds_read_u8 %5, %20 offset:%24+192\n\t"
-        "ds_read_u8 %6, %21 offset:%24+0\n\t"
-        "ds_read_u8 %7, %21 offset:%24+64\n\t"
-        "ds_read_u8 %8, %21 offset:%24+128\n\t"
-        "ds_read_u8 %9, %21 offset:%24+192\n\t"
-        "ds_read_u8 %10, %22 offset:%24+0\n\t"
-        "ds_read_u8 %11, %22 offset:%24+64\n\t"
-        "ds_read_u8 %12, %22 offset:%24+128\n\t"
-        "ds_read_u8 %13, %22 offset:%24+192\n\t"
-        "ds_read_u8 %14, %23 offset:%24+0\n\t"
-        "ds_read_u8 %15, %23 offset:%24+64\n\t"
-        "ds_read_u8 %16, %23 offset:%24+128\n\t"
-        "ds_read_u8 %17, %23 offset:%24+192\n\t"
+        "ds_read_b64 %0, %4 offset:%8\n\t"
+        "ds_read_b64 %1, %5 offset:%8\n\t"
+        "ds_read_b64_tr_b8 %2, %6 offset:%8\n\t"
+        "ds_read_b64_tr_b8 %3, %7 offset:%8\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
-          "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]),
-          "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15])
-        : "v"(ka[0]), "v"(ka[1]), "v"(vb[0]), "v"(vb[1]), "v"(vb[2]), "v"(vb[3]), "n"(OFF)
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(v[0]), "=&v"(v[1])
+        : "v"(ka[0]), "v"(ka[1]), "v"(vt[0]), "v"(vt[1]), "n"(OFF)
         : "memory");
   }
-  template <int OFF>
-  __device__ void read_rest(const uint32_t (&)[2], const uint32_t (&)[4]) {}
 };
 template <>
 struct CodeRegs<128> {
-  static constexpr int FIRST = 8;  // V blocks of read(); read_rest() has the others
   u32x2 k[4];
-  uint32_t v[32];
+  u32x2 v[4];
   template <int OFF>
-  __device__ void read(const uint32_t (&ka)[4], const uint32_t (&vb)[4]) {
+  __device__ void read(const uint32_t (&ka)[4], const uint32_t (&vt)[8]) {
     asm volatile(
-        "ds_read_b64 %0, %36 offset:%44\n\t"
-        "ds_read_b64 %1, %37 offset:%44\n\t"
-        "ds_read_b64 %2, %38 offset:%44\n\t"
-        "ds_read_b64 %3, %39 offset:%44\n\t"
-        "ds_read_u8 %4, %40 offset:%44+0\n\t"
-        "ds_read_u8 %5, %40 offset:%44+128\n\t"
-        "ds_read_u8 %6, %40 offset:%44+272\n\t"
-        "ds_read_u8 %7, %40 offset:%44+400\n\t"
-        "ds_read_u8 %8, %40 offset:%44+16\n\t"
-        "ds_read_u8 %9, %40 offset:%44+144\n\t"
-        "ds_read_u8 %10, %40 offset:%44+256\n\t"
-        "ds_read_u8 %11, %40 offset:%44+384\n\t"
-        "ds_read_u8 %12, %41 offset:%44+0\n\t"
-        "ds_read_u8 %13, %41 offset:%44+128\n\t"
-        "ds_read_u8 %14, %41 offset:%44+272\n\t"
-        "ds_read_u8 %15, %41 offset:%44+400\n\t"
-        "ds_read_u8 %16, %41 offset:%44+16\n\t"
-        "ds_read_u8 %17, %41 offset:%44+144\n\t"
-        "ds_read_u8 %18, %41 offset:%44+256\n\t"
-        "ds_read_u8 %19, %41 offset:%44+384\n\t"
-        "ds_read_u8 %20, %42 offset:%44+0\n\t"
-        "ds_read_u8 %21, %42 offset:%44+128\n\t"
-        "ds_read_u8 %22, %42 offset:%44+272\n\t"
-        "ds_read_u8 %23, %42 offset:%44+400\n\t"
-        "ds_read_u8 %24, %42 offset:%44+16\n\t"
-        "ds_read_u8 %25, %42 offset:%44+144\n\t"
-        "ds_read_u8 %26, %42 offset:%44+256\n\t"
-        "ds_read_u8 %27, %42 offset:%44+384\n\t"
-        "ds_read_u8 %28, %43 offset:%44+0\n\t"
-        "ds_read_u8 %29, %43 offset:%44+128\n\t"
-        "ds_read_u8 %30, %43 offset:%44+272\n\t"
-        "ds_read_u8 %31, %43 offset:%44+400\n\t"
-        "ds_read_u8 %32, %43 offset:%44+16\n\t"
-        "ds_read_u8 %33, %43 offset:%44+144\n\t"
-        "ds_read_u8 %34, %43 offset:%44+256\n\t"
-        "ds_read_u8 %35, %43 offset:%44+384\n\t"
+        "ds_read_b64 %0, %8 offset:%16\n\t"
+        "ds_read_b64 %1, %9 offset:%16\n\t"
+        "ds_read_b64 %2, %10 offset:%16\n\t"
+        "ds_read_b64 %3, %11 offset:%16\n\t"
+        "ds_read_b64_tr_b8 %4, %12 offset:%16\n\t"
+        "ds_read_b64_tr_b8 %5, %13 offset:%16\n\t"
+        "ds_read_b64_tr_b8 %6, %14 offset:%16\n\t"
+        "ds_read_b64_tr_b8 %7, %15 offset:%16\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]),
-          "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]),
-          "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15]), "=&v"(v[16]), "=&v"(v[17]), "=&v"(v[18]),
-          "=&v"(v[19]), "=&v"(v[20]), "=&v"(v[21]), "=&v"(v[22]), "=&v"(v[23]), "=&v"(v[24]), "=&v"(v[25]),
-          "=&v"(v[26]), "=&v"(v[27]), "=&v"(v[28]), "=&v"(v[29]), "=&v"(v[30]), "=&v"(v[31])
-        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(vb[0]), "v"(vb[1]), "v"(vb[2]), "v"(vb[3]), "n"(OFF)
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(vt[0]), "v"(vt[1]), "v"(vt[2]), "v"(vt[3]), "n"(OFF)
         : "memory");
   }
-  template <int OFF>
-  __device__ void read_rest(const uint32_t (&)[4], const uint32_t (&)[4]) {}
 };
 template <>
 struct CodeRegs<256> {
-  static constexpr int FIRST = 8;  // V blocks of read(); read_rest() has the others
   u32x2 k[8];
-  uint32_t v[64];
+  u32x2 v[8];
   template <int OFF>
-  __device__ void read(const uint32_t (&ka)[8], const uint32_t (&vb)[4]) {
+  __device__ void read(const uint32_t (&ka)[8], const uint32_t (&vt)[8]) {
     asm volatile(
-        "ds_read_b64 %0, %40 offset:%52\n\t"
-        "ds_read_b64 %1, %41 offset:%52\n\t"
-        "ds_read_b64 %2, %42 offset:%52\n\t"
-        "ds_read_b64 %3, %43 offset:%52\n\t"
-        "ds_read_b64 %4, %44 offset:%52\n\t"
-        "ds_read_b64 %5, %45 offset:%52\n\t"
-        "ds_read_b64 %6, %46 offset:%52\n\t"
-        "ds_read_b64 %7, %47 offset:%52\n\t"
-        "ds_read_u8 %8, %48 offset:%52+0\n\t"
-        "ds_read_u8 %9, %48 offset:%52+320\n\t"
-        "ds_read_u8 %10, %48 offset:%52+640\n\t"
-        "ds_read_u8 %11, %48 offset:%52+960\n\t"
-        "ds_read_u8 %12, %49 offset:%52+0\n\t"
-        "ds_read_u8 %13, %49 offset:%52+320\n\t"
-        "ds_read_u8 %14, %49 offset:%52+640\n\t"
-        "ds_read_u8 %15, %49 offset:%52+960\n\t"
-        "ds_read_u8 %16, %50 offset:%52+0\n\t"
-        "ds_read_u8 %17, %50 offset:%52+320\n\t"
-        "ds_read_u8 %18, %50 offset:%52+640\n\t"
-        "ds_read_u8 %19, %50 offset:%52+960\n\t"
-        "ds_read_u8 %20, %51 offset:%52+0\n\t"
-        "ds_read_u8 %21, %51 offset:%52+320\n\t"
-        "ds_read_u8 %22, %51 offset:%52+640\n\t"
-        "ds_read_u8 %23, %51 offset:%52+960\n\t"
-        "ds_read_u8 %24, %48 offset:%52+64\n\t"
-        "ds_read_u8 %25, %48 offset:%52+256\n\t"
-        "ds_read_u8 %26, %48 offset:%52+704\n\t"
-        "ds_read_u8 %27, %48 offset:%52+896\n\t"
-        "ds_read_u8 %28, %49 offset:%52+64\n\t"
-        "ds_read_u8 %29, %49 offset:%52+256\n\t"
-        "ds_read_u8 %30, %49 offset:%52+704\n\t"
-        "ds_read_u8 %31, %49 offset:%52+896\n\t"
-        "ds_read_u8 %32, %50 offset:%52+64\n\t"
-        "ds_read_u8 %33, %50 offset:%52+256\n\t"
-        "ds_read_u8 %34, %50 offset:%52+704\n\t"
-        "ds_read_u8 %35, %50 offset:%52+896\n\t"
-        "ds_read_u8 %36, %51 offset:%52+64\n\t"
-        "ds_read_u8 %37, %51 offset:%52+256\n\t"
-        "ds_read_u8 %38, %51 offset:%52+704\n\t"
-        "ds_read_u8 %39, %51 offset:%52+896\n\t"
+        "ds_read_b64 %0, %16 offset:%32\n\t"
+        "ds_read_b64 %1, %17 offset:%32\n\t"
+        "ds_read_b64 %2, %18 offset:%32\n\t"
+        "ds_read_b64 %3, %19 offset:%32\n\t"
+        "ds_read_b64 %4, %20 offset:%32\n\t"
+        "ds_read_b64 %5, %21 offset:%32\n\t"
+        "ds_read_b64 %6, %22 offset:%32\n\t"
+        "ds_read_b64 %7, %23 offset:%32\n\t"
+        "ds_read_b64_tr_b8 %8, %24 offset:%32\n\t"
+        "ds_read_b64_tr_b8 %9, %25 offset:%32\n\t"
+        "ds_read_b64_tr_b8 %10, %26 offset:%32\n\t"
+        "ds_read_b64_tr_b8 %11, %27 offset:%32\n\t"
+        "ds_read_b64_tr_b8 %12, %28 offset:%32\n\t"
+        "ds_read_b64_tr_b8 %13, %29 offset:%32\n\t"
+        "ds_read_b64_tr_b8 %14, %30 offset:%32\n\t"
+        "ds_read_b64_tr_b8 %15, %31 offset:%32\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]), "=&v"(k[6]), "=&v"(k[7]),
-          "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
-          "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]),
-          "=&v"(v[15]), "=&v"(v[16]), "=&v"(v[17]), "=&v"(v[18]), "=&v"(v[19]), "=&v"(v[20]), "=&v"(v[21]),
-          "=&v"(v[22]), "=&v"(v[23]), "=&v"(v[24]), "=&v"(v[25]), "=&v"(v[26]), "=&v"(v[27]), "=&v"(v[28]),
-          "=&v"(v[29]), "=&v"(v[30]), "=&v"(v[31])
+          "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
         : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(ka[4]), "v"(ka[5]), "v"(ka[6]), "v"(ka[7]),
-          "v"(vb[0]), "v"(vb[1]), "v"(vb[2]), "v"(vb[3]), "n"(OFF)
-        : "memory");
-  }
-  template <int OFF>
-  __device__ void read_rest(const uint32_t (&ka)[8], const uint32_t (&vb)[4]) {
-    asm volatile(
-        "ds_read_u8 %0, %32 offset:%36+128\n\t"
-        "ds_read_u8 %1, %32 offset:%36+448\n\t"
-        "ds_read_u8 %2, %32 offset:%36+512\n\t"
-        "ds_read_u8 %3, %32 offset:%36+832\n\t"
-        "ds_read_u8 %4, %33 offset:%36+128\n\t"
-        "ds_read_u8 %5, %33 offset:%36+448\n\t"
-        "ds_read_u8 %6, %33 offset:%36+512\n\t"
-        "ds_read_u8 %7, %33 offset:%36+832\n\t"
-        "ds_read_u8 %8, %34 offset:%36+128\n\t"
-        "ds_read_u8 %9, %34 offset:%36+448\n\t"
-        "ds_read_u8 %10, %34 offset:%36+512\n\t"
-        "ds_read_u8 %11, %34 offset:%36+832\n\t"
-        "ds_read_u8 %12, %35 offset:%36+128\n\t"
-        "ds_read_u8 %13, %35 offset:%36+448\n\t"
-        "ds_read_u8 %14, %35 offset:%36+512\n\t"
-        "ds_read_u8 %15, %35 offset:%36+832\n\t"
-        "ds_read_u8 %16, %32 offset:%36+192\n\t"
-        "ds_read_u8 %17, %32 offset:%36+384\n\t"
-        "ds_read_u8 %18, %32 offset:%36+576\n\t"
-        "ds_read_u8 %19, %32 offset:%36+768\n\t"
-        "ds_read_u8 %20, %33 offset:%36+192\n\t"
-        "ds_read_u8 %21, %33 offset:%36+384\n\t"
-        "ds_read_u8 %22, %33 offset:%36+576\n\t"
-        "ds_read_u8 %23, %33 offset:%36+768\n\t"
-        "ds_read_u8 %24, %34 offset:%36+192\n\t"
-        "ds_read_u8 %25, %34 offset:%36+384\n\t"
-        "ds_read_u8 %26, %34 offset:%36+576\n\t"
-        "ds_read_u8 %27, %34 offset:%36+768\n\t"
-        "ds_read_u8 %28, %35 offset:%36+192\n\t"
-        "ds_read_u8 %29, %35 offset:%36+384\n\t"
-        "ds_read_u8 %30, %35 offset:%36+576\n\t"
-        "ds_read_u8 %31, %35 offset:%36+768\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(v[32]), "=&v"(v[33]), "=&v"(v[34]), "=&v"(v[35]), "=&v"(v[36]), "=&v"(v[37]), "=&v"(v[38]),
-          "=&v"(v[39]), "=&v"(v[40]), "=&v"(v[41]), "=&v"(v[42]), "=&v"(v[43]), "=&v"(v[44]), "=&v"(v[45]),
-          "=&v"(v[46]), "=&v"(v[47]), "=&v"(v[48]), "=&v"(v[49]), "=&v"(v[50]), "=&v"(v[51]), "=&v"(v[52]),
-          "=&v"(v[53]), "=&v"(v[54]), "=&v"(v[55]), "=&v"(v[56]), "=&v"(v[57]), "=&v"(v[58]), "=&v"(v[59]),
-          "=&v"(v[60]), "=&v"(v[61]), "=&v"(v[62]), "=&v"(v[63])
-        : "v"(vb[0]), "v"(vb[1]), "v"(vb[2]), "v"(vb[3]), "n"(OFF)
+          "v"(vt[0]), "v"(vt[1]), "v"(vt[2]), "v"(vt[3]), "v"(vt[4]), "v"(vt[5]), "v"(vt[6]), "v"(vt[7]), "n"(OFF)
         : "memory");
   }
 };
@@ -546,7 +421,7 @@ struct CodeRegs4<64> {
   uint32_t k[2];
   u32x2 v[1];
   template <int OFF>
-  __device__ void read(const uint32_t (&ka)[2], const uint32_t (&vt)[4]) {
+  __device__ void read(const uint32_t (&ka)[2], const uint32_t (&vt)[8]) {
     asm volatile(
         "ds_read_b32 %0, %3 offset:%6\n\t"
         "ds_read_b32 %1, %4 offset:%6\n\t"
@@ -562,7 +437,7 @@ struct CodeRegs4<128> {
   uint32_t k[4];
   u32x2 v[2];
   template <int OFF>
-  __device__ void read(const uint32_t (&ka)[4], const uint32_t (&vt)[4]) {
+  __device__ void read(const uint32_t (&ka)[4], const uint32_t (&vt)[8]) {
     asm volatile(
         "ds_read_b32 %0, %6 offset:%12\n\t"
         "ds_read_b32 %1, %7 offset:%12\n\t"
@@ -581,7 +456,7 @@ struct CodeRegs4<256> {
   uint32_t k[8];
   u32x2 v[4];
   template <int OFF>
-  __device__ void read(const uint32_t (&ka)[8], const uint32_t (&vt)[4]) {
+  __device__ void read(const uint32_t (&ka)[8], const uint32_t (&vt)[8]) {
     asm volatile(
         "ds_read_b32 %0, %12 offset:%24\n\t"
         "ds_read_b32 %1, %13 offset:%24\n\t"
@@ -706,7 +581,7 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ, HS)) void decode_kernel
   // caches: addresses of the code reads (CodeRegs, CodeRegs4) in ka and vb
   const int n = lane & 15, g = lane >> 4;
   const uint32_t ring0 = uniform(static_cast<int>(lds_addr(&ring[wave][0][0])));
-  uint32_t ka[KS], va[QNT ? 1 : DB], vb[4], qa[KS];
+  uint32_t ka[KS], va[QNT ? 1 : DB], vb[8], qa[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     ka[s] = Q4    ? ring0 + n * ROWC + 16 * (s ^ swz4<D>(n)) + 4 * g
@@ -720,17 +595,19 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ, HS)) void decode_kernel
     // swizzled, half blk & 1)
     const int key = 4 * g + (n & 3);
 #pragma unroll
-    for (int R = 0; R < 4; ++R) {
+    for (int R = 0; R < 8; ++R) {
       const int blk = 4 * R + (n >> 2);
       vb[R] = R < DB / 4 ? ring0 + TBC + key * ROWC + 16 * ((blk >> 1) ^ swz4<D>(key)) + 8 * (blk & 1) : 0u;
     }
   } else if constexpr (QNT) {
-    // byte j of block blk (key 4g+j, d = 16 blk + n) is at vb[i] + a constant
-    // (CodeRegs): D = 64: i = blk; 128: i = blk / 2; 256: i = blk % 4
+    // half n & 1 of row n >> 1 of transposing read R (CodeRegs): key 4g + ((n
+    // >> 1) & 3), the 16 codes of block 2R + (n >> 3) (one swizzled chunk)
+    const int key = 4 * g + ((n >> 1) & 3);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      vb[i] = ring0 + TBC + n + (D == 64 ? 256 * g + 16 * (i ^ g) : D == 128 ? 512 * g + 32 * (i ^ g)
-                                                                              : 1024 * g + 16 * (i ^ g));
+    for (int R = 0; R < 8; ++R) {
+      const int blk = 2 * R + (n >> 3);
+      vb[R] = R < DB / 2 ? ring0 + TBC + key * ROWC + 16 * (blk ^ swz8<D>(key)) + 8 * (n & 1) : 0u;
+    }
   } else {
     const int kv = 4 * g + (n >> 2), cc = n & 3;
 #pragma unroll
@@ -1004,19 +881,16 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ, HS)) void decode_kernel
         }
     } else if constexpr (QNT) {  // INT8 codes -> data type in registers (exact)
       CodeRegs<D> cr;
-      auto v_block = [&](int blk) __attribute__((always_inline)) {
-        const typename E::x2 a = E::from_code_halves(cr.v[4 * blk] | (cr.v[4 * blk + 1] << 16));
-        const typename E::x2 b = E::from_code_halves(cr.v[4 * blk + 2] | (cr.v[4 * blk + 3] << 16));
-        vx[blk] = typename E::x4{a[0], a[1], b[0], b[1]};
-      };
       cr.template read<S * SLOT>(ka, vb);
 #pragma unroll
       for (int s = 0; s < KS; ++s) kx[s] = E::from_codes(cr.k[s].x, cr.k[s].y);
+      // bytes 0..3 of read R: block 2R, keys 4g .. 4g+3; bytes 4..7: block 2R+1
 #pragma unroll
-      for (int blk = 0; blk < CodeRegs<D>::FIRST; ++blk) v_block(blk);
-      cr.template read_rest<S * SLOT>(ka, vb);
-#pragma unroll
-      for (int blk = CodeRegs<D>::FIRST; blk < DB; ++blk) v_block(blk);
+      for (int R = 0; R < DB / 2; ++R) {
+        const typename E::x8 t = E::from_codes(cr.v[R].x, cr.v[R].y);
+        vx[2 * R] = typename E::x4{t[0], t[1], t[2], t[3]};
+        vx[2 * R + 1] = typename E::x4{t[4], t[5], t[6], t[7]};
+      }
     } else {
       TileRegs<D> tr;
       tr.template read<S * SLOT>(ka, va);

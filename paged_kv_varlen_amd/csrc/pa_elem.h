@@ -65,12 +65,6 @@ struct Elem<false> {  // IEEE binary16
     }
     return r;
   }
-  // two int8 codes, zero-extended into the 16-bit halves of w, as values
-  // (the same 1024 + u trick, the high byte added instead of placed)
-  static __device__ inline x2 from_code_halves(uint32_t w) {
-    const x2 bias = {static_cast<_Float16>(1152.f), static_cast<_Float16>(1152.f)};
-    return __builtin_bit_cast(x2, (w ^ 0x00800080u) + 0x64006400u) - bias;
-  }
   // int4 codes as values: a 4-bit two's complement code c, its top bit
   // flipped, is c + 8 in [0, 15]; placed under the exponent of 1024 it gives
   // the half 1024 + c + 8, and 1032 is subtracted (exact)
@@ -129,12 +123,6 @@ struct Elem<true> {  // bfloat16: the upper half of a binary32
     for (int e = 0; e < 8; ++e)
       r[e] = static_cast<__bf16>(static_cast<float>(static_cast<int8_t>((e < 4 ? w0 : w1) >> (8 * (e & 3)))));
     return r;
-  }
-  // two int8 codes, zero-extended into the 16-bit halves of w, as values
-  static __device__ inline x2 from_code_halves(uint32_t w) {
-    const uint32_t u = w ^ 0x00800080u;  // code + 128 in bits 0..7 and 16..23
-    return x2{static_cast<__bf16>(static_cast<float>(u & 0xffu) - 128.f),
-              static_cast<__bf16>(static_cast<float>((u >> 16) & 0xffu) - 128.f)};
   }
   // eight int4 codes (nibble e of w is code e) as values
   static __device__ inline x8 from_nibbles8(uint32_t w) {

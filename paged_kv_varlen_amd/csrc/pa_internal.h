@@ -6,8 +6,8 @@
 //                             (one workgroup per token) and, in its first
 //                             workgroup, builds the device work plan from
 //                             cum/past: the decode sequences with their tile
-//                             offsets, each decode wave's start, the prefill
-//                             items.
+//                             offsets, the start of each group of decode
+//                             waves, the prefill items.
 //   2. decode_kernel        - single-token sequences: every wave streams an
 //                             equal share of the 16-key tiles of all
 //                             (sequence, kv head) segments.

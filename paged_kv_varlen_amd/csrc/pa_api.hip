@@ -393,7 +393,12 @@ pa_status enqueue(const pa_args* a, const Resolved& r, const WorkspaceLayout& w,
   const int cus = device_cus();
   mark(PA_KERNEL_DECODE, 0);
   const bool bf16 = a->dtype == PA_DTYPE_BF16;
-  if (launch_decode(ap, r.D, decode_head_slots(r.G), bf16, r.kq, w.decode_grid, s) != hipSuccess)
+  // A call of one sequence whose query has more than one token (cum[1] = N
+  // by the contract) has no single-token row: its decode launch would find no
+  // tile, and is left out.
+  const bool no_decode_rows = r.B == 1 && r.N > 1;
+  if (!no_decode_rows &&
+      launch_decode(ap, r.D, decode_head_slots(r.G), bf16, r.kq, w.decode_grid, s) != hipSuccess)
     return PA_ERR_HIP;
   mark(PA_KERNEL_DECODE, 1);
   mark(PA_KERNEL_MERGE, 0);  // the merge of cut decode segments opens the prefill launch

@@ -590,10 +590,11 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ, HS)) void decode_kernel
     qa[s] = ring0 + 2 * TBC + (n < QB / ROW ? n : 0) * ROW + 16 * (4 * s + g);
   }
   if constexpr (Q4) {
-    // row of transposing read R (CodeRegs4): key 4g + (n & 3), codes of block
-    // 4R + (n >> 2), i.e. bytes 8 blk .. +7 of the key's row (chunk blk / 2,
-    // swizzled, half blk & 1)
-    const int key = 4 * g + (n & 3);
+    // row of transposing read R (CodeRegs4): key 4g + j with j = n & 3, its
+    // two bits swapped (the conversion takes the codes of a word in the order
+    // 0, 2, 1, 3, 4, 6, 5, 7), codes of block 4R + (n >> 2), i.e. bytes 8 blk
+    // .. +7 of the key's row (chunk blk / 2, swizzled, half blk & 1)
+    const int key = 4 * g + (((n & 1) << 1) | ((n >> 1) & 1));
 #pragma unroll
     for (int R = 0; R < 8; ++R) {
       const int blk = 4 * R + (n >> 2);
@@ -857,6 +858,14 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ, HS)) void decode_kernel
 #pragma unroll
           for (int k = 0; k < 4; ++k) vsc[4 * decltype(i)::value + k] = __builtin_bit_cast(f32x4_t, t[k]);
         });
+        if constexpr (Q4) {  // the d order of the INT4 K fragments: 0, 2, 1, 3, 4, 6, 5, 7
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            const u32x4 q = qv[s];
+            qv[s] = u32x4{__builtin_amdgcn_perm(q.y, q.x, 0x05040100u), __builtin_amdgcn_perm(q.y, q.x, 0x07060302u),
+                          __builtin_amdgcn_perm(q.w, q.z, 0x05040100u), __builtin_amdgcn_perm(q.w, q.z, 0x07060302u)};
+          }
+        }
       }
       // acc is rescaled by exp2(-inf) = 0 below, as every lane's max grows
       m = kNegInf;
@@ -868,14 +877,16 @@ __global__ __launch_bounds__(64 * decode_wg_waves(D, KQ, HS)) void decode_kernel
     if constexpr (Q4) {  // INT4 codes -> data type in registers (exact)
       CodeRegs4<D> cr;
       cr.template read<S * SLOT>(ka, vb);
+      // K fragments with their d in the order 0, 2, 1, 3, 4, 6, 5, 7 of each 8
+      // (the query operand is permuted alike once per piece)
 #pragma unroll
-      for (int s = 0; s < KS; ++s) kx[s] = E::from_nibbles8(cr.k[s]);
+      for (int s = 0; s < KS; ++s) kx[s] = E::from_nibbles8_swapped(cr.k[s]);
       // codes 8h .. 8h+7 of read R: blocks 4R + 2h and 4R + 2h + 1, keys 4g .. 4g+3 each
 #pragma unroll
       for (int R = 0; R < DB / 4; ++R)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const typename E::x8 t = E::from_nibbles8(h == 0 ? cr.v[R].x : cr.v[R].y);
+          const typename E::x8 t = E::from_nibbles8_swapped(h == 0 ? cr.v[R].x : cr.v[R].y);
           vx[4 * R + 2 * h] = typename E::x4{t[0], t[1], t[2], t[3]};
           vx[4 * R + 2 * h + 1] = typename E::x4{t[4], t[5], t[6], t[7]};
         }

@@ -88,6 +88,26 @@ struct Elem<false> {  // IEEE binary16
     }
     return r;
   }
+  // the same eight codes in the order 0, 2, 1, 3, 4, 6, 5, 7: v_perm_b32 places
+  // each low or high nibble (code + 8) straight under the exponent byte of
+  // 1024, so no OR is needed
+  static __device__ inline x8 from_nibbles8_swapped(uint32_t w) {
+    const uint32_t u = w ^ 0x88888888u;
+    const uint32_t lo = u & 0x0F0F0F0Fu, hi = (u >> 4) & 0x0F0F0F0Fu;
+    const uint32_t h[4] = {__builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u),   // codes 0, 2
+                           __builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u),   // codes 1, 3
+                           __builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u),   // codes 4, 6
+                           __builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u)};  // codes 5, 7
+    const x2 bias = {static_cast<_Float16>(1032.f), static_cast<_Float16>(1032.f)};
+    x8 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const x2 v = __builtin_bit_cast(x2, h[k]) - bias;
+      r[2 * k] = v[0];
+      r[2 * k + 1] = v[1];
+    }
+    return r;
+  }
 };
 
 template <>
@@ -130,6 +150,15 @@ struct Elem<true> {  // bfloat16: the upper half of a binary32
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       r[e] = static_cast<__bf16>(static_cast<float>(static_cast<int>(w << (28 - 4 * e)) >> 28));
+    return r;
+  }
+  // the same eight codes in the order 0, 2, 1, 3, 4, 6, 5, 7
+  static __device__ inline x8 from_nibbles8_swapped(uint32_t w) {
+    constexpr int kCode[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+    x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      r[e] = static_cast<__bf16>(static_cast<float>(static_cast<int>(w << (28 - 4 * kCode[e])) >> 28));
     return r;
   }
 };

@@ -157,6 +157,10 @@ SWEEP = [
     ([2, 1, 70], [0, 0, 0], 12, 4, 64, 16),      # G=3
     ([1, 9, 1], [100, 100, 5000], 64, 1, 128, 16),  # G=64
     ([1, 16, 1], [17, 3, 2000], 20, 4, 128, 48),  # G=5, block_size 48
+    # three kv heads: an odd unit count (16-bit: split pairs of waves; quantized:
+    # one plan start per wave)
+    ([1, 1, 40, 1, 3], [3000, 700, 50, 9000, 17], 3, 3, 128, 16),
+    ([1, 25, 1, 1], [1500, 40, 4000, 33], 12, 6, 64, 32),  # six kv heads: unit groups of two
 ]
 
 

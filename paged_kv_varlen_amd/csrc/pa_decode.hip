@@ -410,10 +410,12 @@ __device__ inline int swz4(int r) {
 // transposing read (ds_read_b64_tr_b4).  That read takes, in each group of 16
 // lanes, one 8-byte row per lane (16 codes) and hands lane l code l of every
 // row, row r as code r of its result.  Lane r of group g supplies row r = the
-// 16 codes of key 4 g + (r & 3) at d = 16 (4R + (r >> 2)) .. +15, so lane (n,
-// g) receives codes 4j .. 4j+3 = keys 4 g .. 4 g + 3 of column d = 16 (4R +
-// j) + n: the A operand of block 4R + j as the 16x16x16 product reads it.
-// One address register per read (vt[R]).
+// 16 codes of key 4 g + k(r) at d = 16 (4R + (r >> 2)) .. +15, k(r) being r &
+// 3 with its two bits swapped, so lane (n, g) receives in codes 4j .. 4j+3
+// keys 4 g + {0, 2, 1, 3} of column d = 16 (4R + j) + n; the conversion
+// (from_nibbles8_swapped) takes them in the order 0, 2, 1, 3, which gives keys
+// 4 g .. 4 g + 3 in order: the A operand of block 4R + j as the 16x16x16
+// product reads it.  One address register per read (vt[R]).
 template <int D>
 struct CodeRegs4;
 template <>

@@ -81,11 +81,17 @@ __host__ __device__ constexpr int decode_slot_bytes(int D, int hslots, int kq = 
 // other waits on its loads) whenever each still gets a ring of two tiles in
 // about 150 KB of LDS: quantized caches below head size 256 (half the tile
 // bytes, and a code conversion in every tile), 16-bit caches of head size 64,
-// and of 128 with up to four head slots.  Otherwise four (one per SIMD), or
-// two at head size 256 with 16-bit caches.
+// and of 128 with up to four head slots.  INT4 caches below head size 256,
+// whose tiles are a quarter of the 16-bit ones and whose time goes to the
+// per-tile chain of conversion and products, run twelve (three per SIMD)
+// where the ring keeps two tiles.  Otherwise four (one per SIMD), or two at
+// head size 256 with 16-bit caches.
 __host__ __device__ constexpr int decode_wg_waves(int D, int kq, int hslots) {
-  return kq != 0 ? (D > 128 ? 4 : 8)
-                 : D > 128 ? 2 : (150 * 1024) / (8 * decode_slot_bytes(D, hslots, 0)) >= 2 ? 8 : 4;
+  return kq == 4 && D <= 128 && (150 * 1024) / (12 * decode_slot_bytes(D, hslots, 4)) >= 2 ? 12
+         : kq != 0 ? (D > 128 ? 4 : 8)
+         : D > 128 ? 2
+         : (150 * 1024) / (8 * decode_slot_bytes(D, hslots, 0)) >= 2 ? 8
+                                                                      : 4;
 }
 // Unit groups: waves PF v .. PF v + PF - 1 of a workgroup share one of the
 // plan's starts and stream the same tiles of the consecutive units PF u .. PF

@@ -290,7 +290,7 @@ pa_status pa_paged_attention(const pa_args *args, void *stream);
  * contents there; the kernels clear what must start at zero.  Two calls
  * that may overlap on one GPU (different streams without ordering) race on
  * the scratch: the caller must order them. */
-#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+#define PA_NOALLOC_SCRATCH_BYTES (128u << 20)
 pa_status pa_paged_attention_noalloc(const pa_args *args, void *stream);
 
 /* Bytes of device workspace pa_paged_attention needs for these shapes (an

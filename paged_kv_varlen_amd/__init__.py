@@ -37,7 +37,7 @@ _CODE_DTYPES = {torch.int8: PA_KV_INT8, torch.uint8: PA_KV_INT4}  # cache dtype 
 _DTYPE_CODES = {torch.float16: PA_DTYPE_F16, torch.bfloat16: PA_DTYPE_BF16}
 ABI_VERSION = 5
 KERNELS = ("scatter_plan", "decode", "merge", "prefill")  # enum pa_kernel order
-NOALLOC_SCRATCH_BYTES = 64 << 20  # PA_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = 128 << 20  # PA_NOALLOC_SCRATCH_BYTES
 STATUS = {
     0: "PA_OK", 1: "PA_ERR_NULL_ARG", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED",
     4: "PA_ERR_WORKSPACE", 5: "PA_ERR_ALIGNMENT", 6: "PA_ERR_ABI", 7: "PA_ERR_METADATA",

@@ -232,7 +232,7 @@ def test_noalloc_scratch_limit_matches_header():
     (dict(kv_quant=1), NULL),
     (dict(num_tokens=0, batch_size=2), OK),              # nothing to do: no device work
     # shapes whose workspace exceeds the scratch: rejected before any device work
-    (dict(num_tokens=4_000_000, batch_size=4_000_000), WS),
+    (dict(num_tokens=8_000_000, batch_size=8_000_000), WS),
 ])
 def test_noalloc_host_validation(case, expect):
     a = args(**case)
